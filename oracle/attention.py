@@ -1,0 +1,68 @@
+"""Grouped-query decode attention over the active prefix of a KV cache.
+
+Test infrastructure only (see the package header).
+
+Follows the page "Fish Speech KV Cache 推理优化记录" (Fish Speech KV-cache
+optimisation notes):
+  * section 4 -- the cache is pre-allocated at full capacity (32768 slots in
+    the page's S2-Pro setup), 32 query heads share 8 KV heads, head dim 128;
+  * section 5 -- keep the capacity, read only K[:, :, :kv_len] and
+    V[:, :, :kv_len]; the KV heads are expanded with repeat_interleave by
+    n_head // n_kv_head along the head axis, so query head h reads KV head
+    h // G; attention is PyTorch scaled_dot_product_attention with the mask
+    narrowed to the prefix, i.e. softmax(q k^T / sqrt(D)) v over t < kv_len;
+  * section 5, table of kv_len: prefill T, first decode T + 1, i-th decode
+    (from 0) T + i + 1 -- the new token's K/V is already in the cache when the
+    decode query attends, so the query sees every position in [0, kv_len).
+
+The loop below never touches cache positions t >= kv_len[b].
+
+Pins (tests/test_oracle_attention.py): kv_len = 1 returns v_0; q = 0 returns
+the mean of the V prefix; equality with an explicit np.repeat expansion of the
+heads; torch's float64 scaled_dot_product_attention on the expanded heads;
+active-prefix equals full-cache-plus-mask within rtol 1e-5 / atol 1e-6 (the
+tolerance of the page's section 7 test); the kv_len schedule of section 5.
+"""
+
+import numpy as np
+
+
+def kv_len_schedule(prompt_len, decode_index=None):
+    """kv_len at prefill (decode_index None) or at the i-th decode (from 0)."""
+    if decode_index is None:
+        return prompt_len
+    return prompt_len + decode_index + 1
+
+
+def gqa_decode_attention(q, k_cache, v_cache, kv_len, scale=None):
+    """Decode attention for one query token per sequence.
+
+    q        : [B, Hq, D]
+    k_cache  : [B, Hkv, cap, D]   (only t < kv_len[b] is read)
+    v_cache  : [B, Hkv, cap, D]
+    kv_len   : [B] ints in [1, cap]
+    scale    : softmax scale, default 1/sqrt(D)
+    Returns float64 [B, Hq, D].
+    """
+    q = np.asarray(q)
+    B, Hq, D = q.shape
+    Hkv = k_cache.shape[1]
+    if Hq % Hkv:
+        raise ValueError("Hq must be a multiple of Hkv")
+    G = Hq // Hkv
+    if scale is None:
+        scale = 1.0 / np.sqrt(D)
+    out = np.zeros((B, Hq, D), np.float64)
+    for b in range(B):
+        L = int(kv_len[b])
+        if not 1 <= L <= k_cache.shape[2]:
+            raise ValueError(f"kv_len[{b}] = {L} outside [1, cap]")
+        for h in range(Hq):
+            kvh = h // G
+            K = np.asarray(k_cache[b, kvh, :L], np.float64)
+            V = np.asarray(v_cache[b, kvh, :L], np.float64)
+            s = (K @ np.asarray(q[b, h], np.float64)) * scale
+            p = np.exp(s - s.max())
+            p /= p.sum()
+            out[b, h] = p @ V
+    return out

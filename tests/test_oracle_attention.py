@@ -1,0 +1,100 @@
+"""Pins of the oracle's GQA decode attention: closed forms, an explicit
+repeat_interleave expansion, torch's float64 SDPA over the full cache with a
+narrowed mask, tail invariance, and the kv_len schedule of the page."""
+
+import os
+
+import numpy as np
+import torch
+
+from oracle import attention
+
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
+
+
+def _case(seed, B=3, Hq=8, Hkv=2, D=16, cap=40):
+    g = np.random.default_rng(seed)
+    q = g.standard_normal((B, Hq, D))
+    k = g.standard_normal((B, Hkv, cap, D))
+    v = g.standard_normal((B, Hkv, cap, D))
+    L = g.integers(1, cap + 1, size=B)
+    return q, k, v, L
+
+
+def test_kv_len_one_returns_first_value():
+    q, k, v, _ = _case(1)
+    out = attention.gqa_decode_attention(q, k, v, np.ones(3, int))
+    G = 8 // 2
+    for h in range(8):
+        assert np.array_equal(out[:, h], v[:, h // G, 0])
+
+
+def test_zero_query_gives_mean_of_prefix():
+    q, k, v, L = _case(2)
+    out = attention.gqa_decode_attention(np.zeros_like(q), k, v, L)
+    for b in range(3):
+        for h in range(8):
+            assert np.allclose(out[b, h], v[b, h // 4, :L[b]].mean(axis=0), rtol=1e-13, atol=1e-14)
+
+
+def test_gqa_equals_explicit_repeat_interleave():
+    q, k, v, L = _case(3)
+    G = 4
+    kr = np.repeat(k, G, axis=1)          # repeat_interleave along the head axis
+    vr = np.repeat(v, G, axis=1)
+    out = attention.gqa_decode_attention(q, k, v, L)
+    for b in range(3):
+        s = np.einsum("hd,htd->ht", q[b], kr[b, :, :L[b]]) / np.sqrt(16)
+        p = np.exp(s - s.max(axis=1, keepdims=True))
+        p /= p.sum(axis=1, keepdims=True)
+        ref = np.einsum("ht,htd->hd", p, vr[b, :, :L[b]])
+        assert np.allclose(out[b], ref, rtol=1e-12, atol=1e-13)
+
+
+def test_active_prefix_equals_full_cache_with_mask_sdpa():
+    """Section 7 of the KV-cache page: active-prefix output equals the full
+    cache with a narrowed mask, within rtol 1e-5 / atol 1e-6."""
+    q, k, v, L = _case(4, B=2, Hq=32, Hkv=8, D=128, cap=300)
+    out = attention.gqa_decode_attention(q, k, v, L)
+    kt = torch.from_numpy(k).repeat_interleave(4, dim=1)
+    vt = torch.from_numpy(v).repeat_interleave(4, dim=1)
+    qt = torch.from_numpy(q)[:, :, None, :]
+    mask = torch.arange(300)[None, None, None, :] < torch.from_numpy(L)[:, None, None, None]
+    ref = torch.nn.functional.scaled_dot_product_attention(qt, kt, vt, attn_mask=mask)
+    assert np.allclose(out, ref[:, :, 0].numpy(), rtol=1e-5, atol=1e-6)
+
+
+def test_tail_is_never_read():
+    q, k, v, L = _case(5)
+    k2, v2 = k.copy(), v.copy()
+    for b in range(3):
+        k2[b, :, L[b]:] = np.nan
+        v2[b, :, L[b]:] = np.inf
+    assert np.array_equal(attention.gqa_decode_attention(q, k, v, L),
+                          attention.gqa_decode_attention(q, k2, v2, L))
+
+
+def test_softmax_scale_default_is_inverse_sqrt_d():
+    q, k, v, L = _case(6, D=64)
+    a = attention.gqa_decode_attention(q, k, v, L)
+    b = attention.gqa_decode_attention(q, k, v, L, scale=1 / 8.0)
+    assert np.array_equal(a, b)
+
+
+def test_invalid_kv_len_rejected():
+    q, k, v, _ = _case(7)
+    for bad in (0, 41):
+        try:
+            attention.gqa_decode_attention(q, k, v, np.array([1, bad, 1]))
+        except ValueError:
+            continue
+        raise AssertionError("kv_len outside [1, cap] must be rejected")
+
+
+def test_golden_kv_len_schedule():
+    with open(os.path.join(GOLDEN, "kv_len_schedule.txt")) as f:
+        rows = [l.split() for l in f if l.strip() and not l.startswith("#")]
+    for phase, idx, kv in rows:
+        idx = int(idx)
+        got = attention.kv_len_schedule(234, None if idx < 0 else idx)
+        assert got == int(kv), (phase, idx)
