@@ -1,0 +1,280 @@
+// gqa_decode_attn: grouped-query decode attention over the active prefix of a
+// full-capacity KV cache, split over the sequence, then a log-sum-exp merge.
+//
+// What it computes follows the page "Fish Speech KV Cache 推理优化记录"
+// (Fish Speech KV-cache optimisation notes): section 4 (a cache pre-allocated
+// at full capacity, 32 query heads over 8 KV heads, head dim 128) and
+// section 5 (read only K/V[:, :, :kv_len], query head h uses KV head
+// h // (Hq/Hkv) as repeat_interleave would give, softmax(q k^T / sqrt(D)) v).
+// The page's own kernels broadcast K/V to the query heads instead of
+// repeating them ("native GQA via stride-0 K/V broadcast", section "What's
+// Open Source" of "How We Made Our Text-to-Speech API Free"); here the G
+// query heads of a KV head are simply the rows of one MFMA operand.
+//
+// MI355X design:
+//   * One workgroup per (sequence, KV head, chunk of positions).  K and V of
+//     the chunk are read exactly once, for all G query heads.  Positions at
+//     or beyond kv_len are never loaded.
+//   * Scores: bf16 MFMA 16x16x32 with the G query heads as A rows and 16
+//     positions as B columns (K rows go straight from HBM into the B operand,
+//     16 contiguous bytes per lane).
+//   * Softmax per head over the chunk in LDS (wave max/sum reductions); P*V
+//     on the VALU with V rows loaded 16 bytes per lane, reduced across lanes
+//     and waves; the chunk's (max, sum, acc) goes to the workspace.
+//   * A second small kernel merges the chunks of every (sequence, head).
+#include "common.h"
+#include "host_common.h"
+
+namespace fp8s {
+
+constexpr int kMaxChunk = 512;
+
+struct AttnArgs {
+    const uint16_t* q;
+    const uint16_t* k;
+    const uint16_t* v;
+    int64_t sb, sh, st;
+    const int32_t* kv_len;
+    int B, Hq, Hkv, n_split, chunk;
+    int64_t cap, hint;
+    float scale_log2;          // softmax scale * log2(e)
+    float* part;               // [B][Hq][n_split][D + 2]
+    uint16_t* out;
+    int32_t* err;
+};
+
+__device__ __forceinline__ bool kv_len_ok(int L, const AttnArgs& a) {
+    return L >= 1 && (int64_t)L <= a.cap && (int64_t)L <= a.hint;
+}
+
+template <int D, int G>
+__global__ __launch_bounds__(256) void attn_split_kernel(AttnArgs a) {
+    constexpr int NJ = D / 32;                 // MFMA K-steps over the head dim
+    constexpr int LPR = D / 8;                 // lanes per V row (8 bf16 each)
+    constexpr int TPL = 64 / LPR;              // V rows per wave load
+    __shared__ float s_p[G][kMaxChunk];        // scores, then probabilities
+    __shared__ float s_red[4][G][D];
+    __shared__ float s_ml[G][2];
+
+    const int sp = blockIdx.x % a.n_split;
+    const int bg = blockIdx.x / a.n_split;
+    const int g = bg % a.Hkv, b = bg / a.Hkv;
+    const int L = a.kv_len[b];
+    if (!kv_len_ok(L, a)) return;              // the merge writes zeros and reports
+    const int t_begin = sp * a.chunk;
+    if (t_begin >= L) return;                  // chunk entirely past the prefix
+    const int n_tok = min(a.chunk, L - t_begin);
+
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const uint16_t* kbase = a.k + (int64_t)b * a.sb + (int64_t)g * a.sh;
+    const uint16_t* vbase = a.v + (int64_t)b * a.sb + (int64_t)g * a.sh;
+
+    // Query heads of this KV head as MFMA A rows (rows >= G are zero).
+    v8bf qa[NJ];
+    {
+        const int h = lane & 15;
+#pragma unroll
+        for (int j = 0; j < NJ; ++j) {
+            uint4 w = make_uint4(0, 0, 0, 0);
+            if (h < G)
+                w = *reinterpret_cast<const uint4*>(a.q + ((int64_t)b * a.Hq + g * G + h) * D + 32 * j + 8 * (lane >> 4));
+            qa[j] = __builtin_bit_cast(v8bf, w);
+        }
+    }
+
+    // ---- scores: 16 positions per MFMA group, groups round-robin over waves
+    const int n_grp = (n_tok + 15) / 16;
+    for (int grp = wave; grp < n_grp; grp += 4) {
+        const int tl = grp * 16 + (lane & 15);             // position within the chunk
+        const bool live = tl < n_tok;
+        v4f acc = {0, 0, 0, 0};
+        uint4 kw[NJ];
+#pragma unroll
+        for (int j = 0; j < NJ; ++j) {
+            kw[j] = make_uint4(0, 0, 0, 0);
+            if (live)
+                kw[j] = *reinterpret_cast<const uint4*>(kbase + (int64_t)(t_begin + tl) * a.st + 32 * j + 8 * (lane >> 4));
+        }
+#pragma unroll
+        for (int j = 0; j < NJ; ++j)
+            acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(qa[j], __builtin_bit_cast(v8bf, kw[j]), acc, 0, 0, 0);
+        // lane holds S[head 4*(lane/16)+r][position tl]
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+            const int h = 4 * (lane >> 4) + r;
+            if (h < G && live) s_p[h][tl] = acc[r] * a.scale_log2;
+        }
+    }
+    __syncthreads();
+
+    // ---- softmax statistics per head (base-2 exponent of the scaled scores)
+    for (int h = wave; h < G; h += 4) {
+        float m = -INFINITY;
+        for (int t = lane; t < n_tok; t += 64) m = fmaxf(m, s_p[h][t]);
+        m = fmax_xor<64>(m);
+        float l = 0.0f;
+        for (int t = lane; t < n_tok; t += 64) {
+            const float p = exp2f(s_p[h][t] - m);
+            s_p[h][t] = p;
+            l += p;
+        }
+        l = fsum_xor<64>(l);
+        if (lane == 0) { s_ml[h][0] = m; s_ml[h][1] = l; }
+    }
+    __syncthreads();
+
+    // ---- P * V on the VALU: lane owns 8 consecutive d of one V row
+    float o[G][8];
+#pragma unroll
+    for (int h = 0; h < G; ++h)
+#pragma unroll
+        for (int i = 0; i < 8; ++i) o[h][i] = 0.0f;
+    const int dl = 8 * (lane % LPR);
+    const int slot = lane / LPR;
+    for (int t = wave * TPL + slot; t < n_tok; t += 4 * TPL) {
+        const uint4 w = *reinterpret_cast<const uint4*>(vbase + (int64_t)(t_begin + t) * a.st + dl);
+        const uint32_t ww[4] = {w.x, w.y, w.z, w.w};
+        float vf[8];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) { vf[2 * i] = bf16_to_f32(ww[i] & 0xFFFFu); vf[2 * i + 1] = bf16_to_f32(ww[i] >> 16); }
+#pragma unroll
+        for (int h = 0; h < G; ++h) {
+            const float p = s_p[h][t];
+#pragma unroll
+            for (int i = 0; i < 8; ++i) o[h][i] += p * vf[i];
+        }
+    }
+    // reduce the TPL row slots of the wave, then the 4 waves
+#pragma unroll
+    for (int h = 0; h < G; ++h)
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+            float v = o[h][i];
+            for (int off = LPR; off < 64; off <<= 1) v += __shfl_xor(v, off, kWave);
+            o[h][i] = v;
+        }
+    if (slot == 0) {
+#pragma unroll
+        for (int h = 0; h < G; ++h)
+#pragma unroll
+            for (int i = 0; i < 8; ++i) s_red[wave][h][dl + i] = o[h][i];
+    }
+    __syncthreads();
+    for (int e = threadIdx.x; e < G * D; e += 256) {
+        const int h = e / D, d = e % D;
+        const float acc = s_red[0][h][d] + s_red[1][h][d] + s_red[2][h][d] + s_red[3][h][d];
+        float* p = a.part + (((int64_t)b * a.Hq + g * G + h) * a.n_split + sp) * (D + 2);
+        p[2 + d] = acc;
+        if (d == 0) { p[0] = s_ml[h][0]; p[1] = s_ml[h][1]; }
+    }
+}
+
+// Merge the chunks of one (sequence, query head): out = sum_i 2^(m_i - M) acc_i
+// / sum_i 2^(m_i - M) l_i over the chunks that hold positions.
+template <int D>
+__global__ __launch_bounds__(D) void attn_merge_kernel(AttnArgs a) {
+    const int bh = blockIdx.x;
+    const int b = bh / a.Hq;
+    const int d = threadIdx.x;
+    const int L = a.kv_len[b];
+    uint16_t* o = a.out + (int64_t)bh * D;
+    if (!kv_len_ok(L, a)) {
+        o[d] = 0;
+        if (d == 0 && (bh % a.Hq) == 0) report_error(a.err, FP8S_DEV_KVLEN_RANGE);
+        return;
+    }
+    const int n = (L + a.chunk - 1) / a.chunk;
+    const float* p = a.part + (int64_t)bh * a.n_split * (D + 2);
+    float M = -INFINITY;
+    for (int i = 0; i < n; ++i) M = fmaxf(M, p[i * (D + 2)]);
+    float num = 0.0f, den = 0.0f;
+    for (int i = 0; i < n; ++i) {
+        const float w = exp2f(p[i * (D + 2)] - M);
+        den += w * p[i * (D + 2) + 1];
+        num += w * p[i * (D + 2) + 2 + d];
+    }
+    o[d] = (uint16_t)f32_to_bf16(num / den);
+}
+
+struct AttnPlan { int n_split, chunk; };
+
+static AttnPlan plan_attn(int64_t B, int32_t Hkv, int64_t hint) {
+    // Aim for >= 2048 workgroups so that all 256 CUs stay busy at small batch.
+    int64_t want = (2048 + B * Hkv - 1) / (B * Hkv);
+    if (want < 1) want = 1;
+    int64_t chunk = (hint + want - 1) / want;
+    chunk = (chunk + 15) / 16 * 16;
+    if (chunk < 16) chunk = 16;
+    if (chunk > kMaxChunk) chunk = kMaxChunk;
+    AttnPlan p;
+    p.chunk = (int)chunk;
+    p.n_split = (int)((hint + chunk - 1) / chunk);
+    return p;
+}
+
+template <int D, int G>
+static void launch_split(dim3 grid, hipStream_t st, const AttnArgs& a) {
+    hipLaunchKernelGGL((attn_split_kernel<D, G>), grid, dim3(256), 0, st, a);
+}
+
+}  // namespace fp8s
+
+using namespace fp8s;
+
+extern "C" size_t gqa_decode_attn_workspace_size(int64_t B, int32_t Hq, int32_t D, int64_t max_kv_len) {
+    if (B < 1 || Hq < 1 || D < 1 || max_kv_len < 1) return 0;
+    // The split count never exceeds ceil(max_kv_len / 16).
+    const int64_t max_split = (max_kv_len + 15) / 16;
+    return (size_t)B * Hq * max_split * (D + 2) * sizeof(float);
+}
+
+extern "C" int gqa_decode_attn(const uint16_t* q, const uint16_t* k_cache, const uint16_t* v_cache,
+                               int64_t stride_b, int64_t stride_h, int64_t stride_t, const int32_t* kv_len,
+                               int64_t B, int32_t Hq, int32_t Hkv, int32_t D, int64_t cap, int64_t hint,
+                               float softmax_scale, uint16_t* out, void* workspace, size_t workspace_bytes,
+                               int32_t* err_flag, void* stream) {
+    clear_error();
+    FP8S_REQUIRE(q && k_cache && v_cache && kv_len && out, FP8S_EINVAL, "gqa_decode_attn: null pointer");
+    FP8S_REQUIRE(B >= 1 && Hq >= 1 && Hkv >= 1 && cap >= 1 && hint >= 1, FP8S_EINVAL,
+                 "gqa_decode_attn: sizes must be positive");
+    FP8S_REQUIRE(Hq % Hkv == 0, FP8S_EINVAL, "gqa_decode_attn: Hq=%d is not a multiple of Hkv=%d", Hq, Hkv);
+    const int G = Hq / Hkv;
+    FP8S_REQUIRE(D == 64 || D == 128, FP8S_EUNSUPPORTED, "gqa_decode_attn: head dim %d (64 or 128 supported)", D);
+    FP8S_REQUIRE(G == 1 || G == 2 || G == 4 || G == 8, FP8S_EUNSUPPORTED,
+                 "gqa_decode_attn: group size %d (1, 2, 4 or 8 supported)", G);
+    FP8S_REQUIRE(stride_t >= D && stride_t % 8 == 0 && stride_h % 8 == 0 && stride_b % 8 == 0, FP8S_EINVAL,
+                 "gqa_decode_attn: strides must keep rows 16-byte aligned (multiples of 8) and stride_t >= D");
+    FP8S_REQUIRE(aligned16(q) && aligned16(k_cache) && aligned16(v_cache) && aligned16(out), FP8S_EINVAL,
+                 "gqa_decode_attn: q, caches and out must be 16-byte aligned");
+    FP8S_REQUIRE(B * Hkv <= (1ll << 24), FP8S_EUNSUPPORTED, "gqa_decode_attn: batch too large");
+    if (hint > cap) hint = cap;
+    const AttnPlan p = plan_attn(B, Hkv, hint);
+    const size_t need = (size_t)B * Hq * p.n_split * (D + 2) * sizeof(float);
+    FP8S_REQUIRE(workspace && aligned16(workspace), FP8S_EWORKSPACE, "gqa_decode_attn: workspace missing or unaligned");
+    FP8S_REQUIRE(workspace_bytes >= need, FP8S_EWORKSPACE, "gqa_decode_attn: workspace %zu < required %zu bytes",
+                 workspace_bytes, need);
+    AttnArgs a;
+    a.q = q; a.k = k_cache; a.v = v_cache;
+    a.sb = stride_b; a.sh = stride_h; a.st = stride_t;
+    a.kv_len = kv_len;
+    a.B = (int)B; a.Hq = Hq; a.Hkv = Hkv; a.n_split = p.n_split; a.chunk = p.chunk;
+    a.cap = cap; a.hint = hint;
+    a.scale_log2 = softmax_scale * 1.4426950408889634f;
+    a.part = static_cast<float*>(workspace);
+    a.out = out;
+    a.err = err_flag;
+    hipStream_t st = as_stream(stream);
+    const dim3 grid((unsigned)(B * Hkv * p.n_split));
+#define FP8S_ATTN_CASE(DD, GG) \
+    if (D == DD && G == GG) launch_split<DD, GG>(grid, st, a);
+    FP8S_ATTN_CASE(64, 1) FP8S_ATTN_CASE(64, 2) FP8S_ATTN_CASE(64, 4) FP8S_ATTN_CASE(64, 8)
+    FP8S_ATTN_CASE(128, 1) FP8S_ATTN_CASE(128, 2) FP8S_ATTN_CASE(128, 4) FP8S_ATTN_CASE(128, 8)
+#undef FP8S_ATTN_CASE
+    int rc = check_launch("gqa_decode_attn (split)");
+    if (rc) return rc;
+    if (D == 64)
+        hipLaunchKernelGGL(attn_merge_kernel<64>, dim3((unsigned)(B * Hq)), dim3(64), 0, st, a);
+    else
+        hipLaunchKernelGGL(attn_merge_kernel<128>, dim3((unsigned)(B * Hq)), dim3(128), 0, st, a);
+    return check_launch("gqa_decode_attn (merge)");
+}

@@ -1,0 +1,146 @@
+"""gqa_decode_attn on the GPU against the oracle: the tiny workload, the
+32/8/128 workload at B in {1, 16, 64} with ragged kv_len in 234..400 in a
+32768-slot cache, the long sweep up to 8192, garbage-tail invariance, closed
+forms, split invariance and invalid kv_len handling."""
+
+import numpy as np
+import pytest
+import torch
+
+from oracle import attention as oattn
+from fp8_transformer_step_amd import inputs, ops
+from _helpers import TOL_BF16_ATTN, f32, from_dev_bf16, log, max_rel_err, need_gpu, to_dev_bf16
+
+pytestmark = pytest.mark.gpu
+
+
+def _garbage_cache(B, Hkv, cap, D, seed):
+    """A cache of random bytes (NaN and Inf bf16 patterns included)."""
+    g = torch.Generator(device="cuda")
+    g.manual_seed(seed)
+    out = torch.empty((B, Hkv, cap, D), dtype=torch.int16, device="cuda")
+    for b in range(B):
+        out[b] = torch.randint(-32768, 32768, (Hkv, cap, D), dtype=torch.int32, device="cuda",
+                               generator=g).to(torch.int16)
+    return out.view(torch.bfloat16)
+
+
+def _make(workload, B, Hq, Hkv, D, cap, kv, seed=0, tail_seed=1, extra=0):
+    Lmax = int(kv.max())
+    qb, kb, vb = inputs.attention_prefix(workload, B, Hq, Hkv, D, Lmax, extra=extra)
+    kc = _garbage_cache(B, Hkv, cap, D, tail_seed)
+    vc = _garbage_cache(B, Hkv, cap, D, tail_seed + 7)
+    kd, vd = to_dev_bf16(kb), to_dev_bf16(vb)
+    for b in range(B):
+        L = int(kv[b])
+        kc[b, :, :L] = kd[b, :, :L]
+        vc[b, :, :L] = vd[b, :, :L]
+    return qb, kb, vb, kc, vc
+
+
+def _oracle(qb, kb, vb, kv):
+    return oattn.gqa_decode_attention(f32(qb), f32(kb), f32(vb), kv)
+
+
+def _run(qb, kc, vc, kv, hint, err=None):
+    out = ops.gqa_decode_attn(to_dev_bf16(qb), kc, vc, torch.from_numpy(kv).cuda(), hint, err=err)
+    torch.cuda.synchronize()
+    return out
+
+
+def test_tiny_workload():
+    need_gpu()
+    kv = np.array([37], np.int32)
+    qb, kb, vb, kc, vc = _make(inputs.W_TINY, 1, 4, 1, 64, 128, kv)
+    out = _run(qb, kc, vc, kv, 128)
+    assert max_rel_err(from_dev_bf16(out), _oracle(qb, kb, vb, kv)) <= TOL_BF16_ATTN
+
+
+@pytest.mark.parametrize("B", [1, 16, 64])
+def test_qwen_shape_short_context(B):
+    need_gpu()
+    kv = inputs.kv_lengths(inputs.W_ATTN, B, 234, 400, extra=B)
+    log(f"attn B={B} kv range {kv.min()}..{kv.max()}")
+    qb, kb, vb, kc, vc = _make(inputs.W_ATTN, B, 32, 8, 128, 32768, kv, extra=B)
+    err = torch.zeros(1, dtype=torch.int32, device="cuda")
+    out = _run(qb, kc, vc, kv, 400, err)
+    e = max_rel_err(from_dev_bf16(out), _oracle(qb, kb, vb, kv))
+    log(f"  max rel err {e:.3e}")
+    assert int(err.item()) == 0
+    assert e <= TOL_BF16_ATTN
+
+
+@pytest.mark.parametrize("B,lo,hi", [(16, 234, 8192), (4, 8192, 8192), (8, 1024, 4096)])
+def test_long_context_sweep(B, lo, hi):
+    need_gpu()
+    kv = inputs.kv_lengths(inputs.W_ATTN, B, lo, hi, extra=10 * B + hi)
+    log(f"attn long B={B} kv range {kv.min()}..{kv.max()}")
+    qb, kb, vb, kc, vc = _make(inputs.W_ATTN, B, 32, 8, 128, 32768, kv, extra=10 * B + hi)
+    out = _run(qb, kc, vc, kv, hi)
+    assert max_rel_err(from_dev_bf16(out), _oracle(qb, kb, vb, kv)) <= TOL_BF16_ATTN
+
+
+def test_garbage_tail_invariance_and_split_invariance():
+    need_gpu()
+    B = 16
+    kv = inputs.kv_lengths(inputs.W_ATTN, B, 234, 400, extra=99)
+    qb, kb, vb, kc, vc = _make(inputs.W_ATTN, B, 32, 8, 128, 4096, kv, tail_seed=5, extra=99)
+    base = _run(qb, kc, vc, kv, 400)
+    # a different garbage tail, and a zero tail: bit-identical output
+    _, _, _, kc2, vc2 = _make(inputs.W_ATTN, B, 32, 8, 128, 4096, kv, tail_seed=11, extra=99)
+    assert torch.equal(base, _run(qb, kc2, vc2, kv, 400))
+    kz, vz = torch.zeros_like(kc), torch.zeros_like(vc)
+    for b in range(B):
+        L = int(kv[b])
+        kz[b, :, :L] = kc[b, :, :L]
+        vz[b, :, :L] = vc[b, :, :L]
+    assert torch.equal(base, _run(qb, kz, vz, kv, 400))
+    # other split plans (the hint sets the chunking) stay within tolerance
+    ref = _oracle(qb, kb, vb, kv)
+    for hint in (401, 1000, 4096):
+        assert max_rel_err(from_dev_bf16(_run(qb, kc, vc, kv, hint)), ref) <= TOL_BF16_ATTN
+
+
+def test_closed_forms():
+    need_gpu()
+    B, cap = 4, 256
+    kv = np.array([1, 1, 1, 1], np.int32)
+    qb, kb, vb, kc, vc = _make(inputs.W_ATTN, B, 32, 8, 128, cap, kv, extra=5)
+    out = _run(qb, kc, vc, kv, cap)
+    # one position: the output is that position's V, exactly (bf16)
+    want = torch.from_numpy(np.repeat(vb[:, :, 0], 4, axis=1).view(np.int16)).cuda().view(torch.bfloat16)
+    assert torch.equal(out, want)
+    # zero query: the mean of the V prefix; kv_len = cap is valid
+    kv = np.array([cap, 17, 100, 255], np.int32)
+    qb, kb, vb, kc, vc = _make(inputs.W_ATTN, B, 32, 8, 128, cap, kv, extra=6)
+    qz = np.zeros_like(qb)
+    out = from_dev_bf16(_run(qz, kc, vc, kv, cap))
+    mean = np.stack([np.repeat(f32(vb)[b, :, :kv[b]].mean(axis=1), 4, axis=0) for b in range(B)])
+    assert max_rel_err(out, mean) <= TOL_BF16_ATTN
+
+
+def test_gqa_matches_explicit_head_repeat():
+    """Equality with attention over explicitly repeated KV heads (the
+    repeat_interleave reference of the KV-cache page)."""
+    need_gpu()
+    B = 2
+    kv = np.array([300, 391], np.int32)
+    qb, kb, vb, kc, vc = _make(inputs.W_ATTN, B, 32, 8, 128, 512, kv, extra=31)
+    out = from_dev_bf16(_run(qb, kc, vc, kv, 400))
+    kr, vr = np.repeat(f32(kb), 4, axis=1), np.repeat(f32(vb), 4, axis=1)
+    ref = oattn.gqa_decode_attention(f32(qb), kr, vr, kv)      # Hkv == Hq: one head each
+    assert max_rel_err(out, ref) <= TOL_BF16_ATTN
+
+
+def test_invalid_kv_len_sets_flag_and_zeroes():
+    need_gpu()
+    B, cap = 3, 64
+    kv = np.array([10, 10, 10], np.int32)
+    qb, kb, vb, kc, vc = _make(inputs.W_ATTN, B, 32, 8, 128, cap, kv, extra=41)
+    bad = np.array([10, 0, 65], np.int32)
+    err = torch.zeros(1, dtype=torch.int32, device="cuda")
+    out = _run(qb, kc, vc, bad, cap, err)
+    assert int(err.item()) == ops.DEV_KVLEN_RANGE
+    assert not out[1].float().abs().sum().item() and not out[2].float().abs().sum().item()
+    ref = _oracle(qb[:1], kb[:1], vb[:1], kv[:1])
+    assert max_rel_err(from_dev_bf16(out[:1]), ref) <= TOL_BF16_ATTN
