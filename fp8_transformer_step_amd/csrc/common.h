@@ -101,12 +101,20 @@ __device__ __forceinline__ v4f mfma_fp8(const v8i& a, const v8i& b, const v4f& c
 }
 
 // ---- cross-workgroup signalling ----------------------------------------------
-__device__ __forceinline__ int atomic_add_agent(int* p, int v) {
-    return __hip_atomic_fetch_add(p, v, __ATOMIC_ACQ_REL, __HIP_MEMORY_SCOPE_AGENT);
+// On gfx950 an agent-scope release writes the L2 back and an agent-scope
+// acquire invalidates it, so the kernels keep those to one per hand-off:
+// counters are bumped with relaxed or release atomics, waits spin on relaxed
+// loads and issue a single acquire fence once the wait is over.
+__device__ __forceinline__ int atomic_add_relaxed(int* p, int v) {
+    return __hip_atomic_fetch_add(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
-__device__ __forceinline__ int load_acquire_agent(const int* p) {
-    return __hip_atomic_load(p, __ATOMIC_ACQUIRE, __HIP_MEMORY_SCOPE_AGENT);
+__device__ __forceinline__ int atomic_add_release(int* p, int v) {
+    return __hip_atomic_fetch_add(p, v, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_AGENT);
 }
+__device__ __forceinline__ int load_relaxed_agent(const int* p) {
+    return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ void acquire_fence_agent() { __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent"); }
 __device__ __forceinline__ void store_relaxed_agent(int* p, int v) {
     __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }

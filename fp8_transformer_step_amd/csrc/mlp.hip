@@ -60,12 +60,13 @@ __device__ __forceinline__ int* amax_cnt(const MlpArgs& a) { return a.ctrl + kCt
 __device__ __forceinline__ int* h_done(const MlpArgs& a) { return a.ctrl + kCtrlHeader + a.KBH + a.KBI; }
 __device__ __forceinline__ int* down_cnt(const MlpArgs& a) { return a.ctrl + kCtrlHeader + a.KBH + 2 * a.KBI; }
 
-// Bounded wait of one thread until *flag >= target.  Returns false if the
-// kernel is aborting.
+// Bounded wait of one thread until *flag >= target, on relaxed loads (no
+// cache maintenance while spinning).  The caller issues one acquire fence
+// after its waits.  Returns false if the kernel is aborting.
 __device__ bool wait_geq(const MlpArgs& a, const int* flag, int target) {
     int spins = 0;
-    while (load_acquire_agent(flag) < target) {
-        if (load_acquire_agent(a.ctrl + 2)) return false;
+    while (load_relaxed_agent(flag) < target) {
+        if (load_relaxed_agent(a.ctrl + 2)) return false;
         if (++spins > kSpinLimit) {
             store_relaxed_agent(a.ctrl + 2, 1);
             report_error(a.err, FP8S_DEV_WAIT_TIMEOUT);
@@ -76,17 +77,23 @@ __device__ bool wait_geq(const MlpArgs& a, const int* flag, int target) {
     return true;
 }
 
-// Make this thread's global stores visible device-wide, then let thread 0
-// bump `counter` once all threads of the workgroup got here.  Returns the
-// counter's previous value to every thread.
+// Publish this workgroup's global stores and bump `counter`: every wave waits
+// until its own stores are acknowledged by L2, the workgroup meets, and
+// thread 0 performs one release (L2 write-back) fused with the increment.
+// Returns the counter's previous value to every thread.
 __device__ int publish(int* counter, int* s_bcast) {
-    __threadfence();
+    __builtin_amdgcn_s_waitcnt(0);
     __syncthreads();
-    if (threadIdx.x == 0) *s_bcast = atomic_add_agent(counter, 1);
+    if (threadIdx.x == 0) *s_bcast = atomic_add_release(counter, 1);
     __syncthreads();
-    int v = *s_bcast;
+    return *s_bcast;
+}
+
+// Thread 0 has finished its waits: make the published data visible to the
+// whole workgroup.
+__device__ __forceinline__ void acquire_and_sync() {
+    if (threadIdx.x == 0) acquire_fence_agent();
     __syncthreads();
-    return v;
 }
 
 // ---- fragment addressing ------------------------------------------------------
@@ -194,7 +201,7 @@ __device__ void gu_item(const MlpArgs& a, int item, float* lds, int* s_bcast) {
         for (int kb = 0; kb < a.KBH; ++kb)
             if (!wait_geq(a, xq_done(a) + kb, 1)) break;
     }
-    __syncthreads();
+    acquire_and_sync();
 
     for (int kb0 = lo; kb0 < hi; kb0 += PF) {
 #pragma unroll
@@ -280,7 +287,7 @@ __device__ void gu_item(const MlpArgs& a, int item, float* lds, int* s_bcast) {
             a.amax_part[((int64_t)kbi * 4 + sub) * rows + m] = fmaxf(amax_lds[m], amax_lds[MT * 16 + m]);
         publish(amax_cnt(a) + kbi, s_bcast);
         if (threadIdx.x == 0) wait_geq(a, amax_cnt(a) + kbi, 4);
-        __syncthreads();
+        acquire_and_sync();
         if (kh == 0) {
 #pragma unroll
             for (int mt = 0; mt < MT; ++mt)
@@ -354,7 +361,7 @@ __device__ void down_item(const MlpArgs& a, int item, int* s_bcast) {
         for (int kb = lo; kb < hi; ++kb)
             if (!wait_geq(a, h_done(a) + kb, 4)) break;
     }
-    __syncthreads();
+    acquire_and_sync();
 
     for (int kb0 = lo; kb0 < hi; kb0 += PF) {
 #pragma unroll
@@ -401,11 +408,11 @@ __device__ void down_item(const MlpArgs& a, int item, int* s_bcast) {
     const int prev = publish(down_cnt(a) + nt, s_bcast);
     if (prev != a.S - 1) return;
     // Last split of this tile: reduce in split order (deterministic).
-    __threadfence();
+    acquire_and_sync();
     const float* base = a.ypart + (int64_t)nt * a.S * a.M * kDownRows;
     for (int e = threadIdx.x; e < a.M * kDownRows; e += blockDim.x) {
         float sum = 0.0f;
-        for (int k = 0; k < a.S; ++k) sum += __builtin_nontemporal_load(base + (int64_t)k * a.M * kDownRows + e);
+        for (int k = 0; k < a.S; ++k) sum += base[(int64_t)k * a.M * kDownRows + e];
         const int m = e / kDownRows, n = nt * kDownRows + (e % kDownRows);
         a.y[(int64_t)m * a.H + n] = (uint16_t)f32_to_bf16(sum);
     }
@@ -416,7 +423,7 @@ __global__ __launch_bounds__(256, 2) void mlp_kernel(MlpArgs a) {
     extern __shared__ float lds[];
     __shared__ int s_ticket, s_bcast;
     for (;;) {
-        if (threadIdx.x == 0) s_ticket = atomic_add_agent(a.ctrl, 1);
+        if (threadIdx.x == 0) s_ticket = atomic_add_relaxed(a.ctrl, 1);
         __syncthreads();
         const int t = s_ticket;
         __syncthreads();
@@ -431,10 +438,9 @@ __global__ __launch_bounds__(256, 2) void mlp_kernel(MlpArgs a) {
         }
     }
     // Last workgroup out resets the control words for the next call.
-    if (threadIdx.x == 0) s_bcast = atomic_add_agent(a.ctrl + 1, 1);
+    if (threadIdx.x == 0) s_bcast = atomic_add_relaxed(a.ctrl + 1, 1);
     __syncthreads();
     if (s_bcast == (int)gridDim.x - 1) {
-        __threadfence();
         const int n = kCtrlHeader + a.KBH + 2 * a.KBI + a.NT;
         for (int i = threadIdx.x; i < n; i += blockDim.x) store_relaxed_agent(a.ctrl + i, 0);
     }
