@@ -7,7 +7,7 @@
 #include <stdint.h>
 #include <stdio.h>
 
-#include "../../include/fp8step.h"
+#include "fp8step.h"
 
 namespace fp8s {
 
