@@ -4,7 +4,7 @@
 One step = the two parts of a decode step's hot path for a batch of B = 64
 sequences, as a Qwen3-4B-sized layer computes them:
   * the FP8 SwiGLU MLP at M = 64 (hidden 2560, intermediate 9728, bsgemm
-    128x128 weight scales, activations quantised in-kernel), one launch;
+    128x128 weight scales, activations quantised on the GPU);
   * GQA decode attention (32 query / 8 KV heads, dim 128) over bf16 caches of
     32768 slots per sequence with ragged kv_len ~ U{234..400}.
 tokens/s = B / step time.  Inputs are resident in HBM before timing starts.
@@ -34,10 +34,42 @@ H, I = 2560, 9728                # Qwen3-4B MLP
 HQ, HKV, D, CAP = 32, 8, 128, 32768
 
 
+def _wscale_bytes(n, k, mode):
+    return (n // 128) * (k // 128) * 4 if mode == 0 else n * k // 32
+
+
+def _ascale_bytes(m, k, mode):
+    return m * (k // 128) * 4 if mode == 0 else m * k // 32
+
+
 def mlp_bytes(M, mode):
-    w = 3 * H * I
-    s = 3 * (H // 128) * (I // 128) * 4 if mode == 0 else 3 * H * I // 32
-    return w + s + 2 * M * H * 2
+    """Algorithmic bytes of one MLP call: FP8 weights + scales, x in, y out."""
+    return 3 * H * I + 3 * _wscale_bytes(I, H, mode) + 2 * M * H * 2
+
+
+def kernel_bytes(name, M, mode, kv_len=None, B=None):
+    """Algorithmic bytes per launch of each library kernel (what the step it
+    implements must read and write; workspace traffic that a fused design
+    would avoid, such as split partials, is not counted)."""
+    w_gu = 2 * I * H + 2 * _wscale_bytes(I, H, mode)
+    w_dn = H * I + _wscale_bytes(H, I, mode)
+    if name == "mlp_gu_small":
+        return w_gu + M * H * 2 + 2 * M * I * 4
+    if name == "mlp_gu":
+        return w_gu + M * H + _ascale_bytes(M, H, mode) + 2 * M * I * 4
+    if name == "mlp_down_small_fused":
+        return w_dn + 2 * M * I * 4 + M * H * 2
+    if name in ("mlp_down_small", "mlp_down"):
+        return w_dn + M * I + _ascale_bytes(M, I, mode) + M * H * 2
+    if name == "mlp_xq":
+        return M * H * 2 + M * H + _ascale_bytes(M, H, mode)
+    if name == "mlp_hq":
+        return 2 * M * I * 4 + M * I + _ascale_bytes(M, I, mode)
+    if name == "attn_split":
+        return int(np.sum(kv_len.astype(np.int64))) * HKV * D * 2 * 2 + B * HQ * D * 2 + 4 * B
+    if name == "attn_merge":
+        return B * HQ * D * 2 + 4 * B
+    return 0
 
 
 def attn_bytes(kv_len, B):
@@ -83,8 +115,7 @@ class Workload:
                 st["q"] = torch.randn((B, HQ, D), generator=g, device="cuda").to(torch.bfloat16)
                 st["o"] = torch.empty((B, HQ, D), dtype=torch.bfloat16, device="cuda")
                 st["kv"] = torch.from_numpy(kv_len).cuda()
-                st["aws"] = torch.empty(ops.attn_workspace_bytes(B, HQ, D, Lmax), dtype=torch.uint8,
-                                        device="cuda")
+                st["aws"] = ops.new_attn_workspace(B, HQ, D, Lmax)
                 st["hint"] = Lmax
             self.sets.append(st)
         self.err = torch.zeros(1, dtype=torch.int32, device="cuda")
@@ -99,32 +130,68 @@ class Workload:
                                  workspace=st["aws"], err=self.err)
 
 
-def time_parts(torch, wl, parts, steps, warmup):
-    """Run `steps` steps (each calls every part once on a rotating set);
-    returns per-part mean launch durations (ms, HIP events on the launch
-    stream) and the total ms per step."""
+def time_parts(torch, ops, wl, parts, steps, warmup):
+    """Two timed regions of `steps` steps each (every step calls every part
+    once on a rotating set), bracketed by synchronisation and HIP events:
+      1. clean: gives ms per step (the headline);
+      2. per kernel: the library records a HIP event pair around every kernel
+         it launches, on the launch stream (the events add small gaps between
+         launches, so this pass is not used for the headline).
+    Returns (ms per step, wall ms per step, {kernel: [ms, ...]})."""
     n = len(wl.sets)
     for i in range(warmup):
         for p in parts:
             p(i % n)
     torch.cuda.synchronize()
-    ev = [[(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in parts]
-          for _ in range(steps)]
     t0 = torch.cuda.Event(enable_timing=True)
     t1 = torch.cuda.Event(enable_timing=True)
-    torch.cuda.synchronize()
     wall0 = time.perf_counter()
     t0.record()
     for i in range(steps):
-        for j, p in enumerate(parts):
-            ev[i][j][0].record()
+        for p in parts:
             p(i % n)
-            ev[i][j][1].record()
     t1.record()
     torch.cuda.synchronize()
     wall = (time.perf_counter() - wall0) * 1e3 / steps
-    per = [float(np.mean([ev[i][j][0].elapsed_time(ev[i][j][1]) for i in range(steps)])) for j in range(len(parts))]
-    return per, t0.elapsed_time(t1) / steps, wall
+    ms_step = t0.elapsed_time(t1) / steps
+    ops.profile_start(steps * len(parts) * 8 + 64)
+    for i in range(steps):
+        for p in parts:
+            p(i % n)
+    torch.cuda.synchronize()
+    recs = ops.profile_stop()
+    per = {}
+    for name, ms in recs:
+        per.setdefault(name, []).append(ms)
+    return ms_step, wall, per
+
+
+def pmc_traffic(kernel):
+    """HBM bytes per launch of `kernel` from the committed profiler summary
+    (FETCH_SIZE and WRITE_SIZE runs scaled by a copy of known size), or None
+    when there is none or the kernel's source changed since it was taken."""
+    import hashlib
+    path = os.path.join(ROOT, "profiles", "pmc_traffic.json")
+    if not os.path.exists(path):
+        return None
+    rec = json.load(open(path)).get("kernels", {}).get(kernel)
+    if not rec:
+        return None
+    src = os.path.join(ROOT, rec["source"])
+    if not os.path.exists(src) or hashlib.sha256(open(src, "rb").read()).hexdigest() != rec["source_sha256"]:
+        return None
+    return rec["fetch_bytes"] + rec["write_bytes"]
+
+
+def kernel_table(per, steps, M, mode, kv_len=None, B=None):
+    """{kernel: {launches per step, mean us, GB/s, frac of peak}}."""
+    out = {}
+    for name, v in per.items():
+        us = float(np.mean(v)) * 1e3
+        nb = kernel_bytes(name, M, mode, kv_len, B)
+        gbs = nb / (us * 1e-6) / 1e9 if us > 0 else 0.0
+        out[name] = {"per_step": len(v) / steps, "us": us, "bytes": nb, "GB/s": gbs, "frac": gbs / PEAK_HBM_GBS}
+    return out
 
 
 def cpu_baseline(B, kv_len):
@@ -168,6 +235,9 @@ def main():
     ap.add_argument("--sets", type=int, default=4)
     ap.add_argument("--no-sweep", action="store_true")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="also run a plain 512 MiB device copy (3x) so that profiler byte counters can be "
+                         "scaled against a kernel of known traffic")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py measures one GPU only; --gpus {args.gpus} is not supported "
@@ -182,16 +252,21 @@ def main():
     kv_len = inputs.kv_lengths(inputs.W_ATTN, B, 234, 400)
     log(f"bench: building {args.sets} rotating sets (B={B})")
     wl = Workload(torch, ops, B, B, ops.MLP_BSGEMM, args.sets, kv_len)
-    (t_mlp, t_attn), ms_step, wall = time_parts(torch, wl, [wl.mlp, wl.attn], args.steps, args.warmup)
+    ms_step, wall, per = time_parts(torch, ops, wl, [wl.mlp, wl.attn], args.steps, args.warmup)
     torch.cuda.synchronize()
     if int(wl.err.item()) != 0:
         raise SystemExit(f"device error flag {int(wl.err.item())}")
+    ktab = kernel_table(per, args.steps, B, ops.MLP_BSGEMM, kv_len, B)
+    t_mlp = sum(v["us"] * v["per_step"] for k, v in ktab.items() if k.startswith("mlp"))
+    t_attn = sum(v["us"] * v["per_step"] for k, v in ktab.items() if k.startswith("attn"))
     b_mlp, b_attn = mlp_bytes(B, 0), attn_bytes(kv_len, B)
-    gbs_mlp = b_mlp / (t_mlp * 1e-3) / 1e9
-    gbs_attn = b_attn / (t_attn * 1e-3) / 1e9
-    log(f"step {ms_step * 1e3:.1f} us: mlp {t_mlp * 1e3:.1f} us {gbs_mlp:.0f} GB/s, "
-        f"attn {t_attn * 1e3:.1f} us {gbs_attn:.0f} GB/s")
-    dom = ("swiglu_mlp_fp8", b_mlp, t_mlp) if t_mlp >= t_attn else ("gqa_decode_attn", b_attn, t_attn)
+    gbs_mlp = b_mlp / (t_mlp * 1e-6) / 1e9
+    gbs_attn = b_attn / (t_attn * 1e-6) / 1e9
+    log(f"step {ms_step * 1e3:.1f} us: mlp kernels {t_mlp:.1f} us {gbs_mlp:.0f} GB/s, "
+        f"attn kernels {t_attn:.1f} us {gbs_attn:.0f} GB/s")
+    for k, v in sorted(ktab.items(), key=lambda kv: -kv[1]["us"] * kv[1]["per_step"]):
+        log(f"  {k:22s} {v['us']:7.1f} us  {v['GB/s']:6.0f} GB/s  ({100 * v['frac']:.1f}% of HBM peak)")
+    dom_name, dom = max(ktab.items(), key=lambda kv: kv[1]["us"] * kv[1]["per_step"])
     result = {
         "metric": METRIC,
         "value": B / (ms_step * 1e-3),
@@ -209,13 +284,12 @@ def main():
                                "bsgemm FP8 SwiGLU MLP (2560/9728, M=64) + GQA decode attention "
                                "(32/8 heads, dim 128, cache 32768, kv_len U[234,400])",
                    "batch": B, "hidden": H, "intermediate": I, "heads": [HQ, HKV, D], "cache": CAP},
-        "roofline": {"bound": "hbm", "kernel": dom[0], "achieved": dom[1] / (dom[2] * 1e-3) / 1e9,
-                     "peak": PEAK_HBM_GBS, "unit": "GB/s",
-                     "frac": dom[1] / (dom[2] * 1e-3) / 1e9 / PEAK_HBM_GBS, "traffic": None,
-                     "algorithmic_bytes": dom[1], "launch_us": dom[2] * 1e3},
-        "parts": {"mlp": {"us": t_mlp * 1e3, "bytes": b_mlp, "GB/s": gbs_mlp, "frac": gbs_mlp / PEAK_HBM_GBS},
-                  "attn": {"us": t_attn * 1e3, "bytes": b_attn, "GB/s": gbs_attn,
-                           "frac": gbs_attn / PEAK_HBM_GBS}},
+        "roofline": {"bound": "hbm", "kernel": dom_name, "achieved": dom["GB/s"], "peak": PEAK_HBM_GBS,
+                     "unit": "GB/s", "frac": dom["frac"], "traffic": pmc_traffic(dom_name),
+                     "algorithmic_bytes": dom["bytes"], "launch_us": dom["us"]},
+        "parts": {"mlp": {"us": t_mlp, "bytes": b_mlp, "GB/s": gbs_mlp, "frac": gbs_mlp / PEAK_HBM_GBS},
+                  "attn": {"us": t_attn, "bytes": b_attn, "GB/s": gbs_attn, "frac": gbs_attn / PEAK_HBM_GBS}},
+        "kernels": ktab,
         "wall_ms_per_step": wall,
     }
     del wl
@@ -226,23 +300,36 @@ def main():
         for mode, key in ((ops.MLP_BSGEMM, "mlp_bsgemm"), (ops.MLP_MXFP8, "mlp_mxfp8")):
             for M in (1, 8, 32, 64, 128):
                 w = Workload(torch, ops, 1, M, mode, args.sets, kv_len, with_attn=False)
-                (t,), _, _ = time_parts(torch, w, [w.mlp], 20, 5)
+                t, _, per = time_parts(torch, ops, w, [w.mlp], 20, 5)
                 gb = mlp_bytes(M, mode) / (t * 1e-3) / 1e9
-                sweep[key][M] = {"us": t * 1e3, "tokens/s": M / (t * 1e-3), "GB/s": gb, "frac": gb / PEAK_HBM_GBS}
-                log(f"{key} M={M}: {t * 1e3:.1f} us {gb:.0f} GB/s")
+                sweep[key][M] = {"us": t * 1e3, "tokens/s": M / (t * 1e-3), "GB/s": gb, "frac": gb / PEAK_HBM_GBS,
+                                 "kernels": kernel_table(per, 20, M, mode)}
+                log(f"{key} M={M}: {t * 1e3:.1f} us {gb:.0f} GB/s  " +
+                    " ".join(f"{k}={v['us']:.1f}" for k, v in sweep[key][M]["kernels"].items()))
                 del w
                 torch.cuda.empty_cache()
         for Bs, lo, hi in ((1, 234, 400), (16, 234, 400), (64, 234, 400), (64, 234, 8192)):
             kv = inputs.kv_lengths(inputs.W_ATTN, Bs, lo, hi, extra=Bs + hi)
             w = Workload(torch, ops, Bs, 1, 0, 2 if hi > 400 else args.sets, kv, with_mlp=False)
-            (t,), _, _ = time_parts(torch, w, [w.attn], 20, 5)
+            t, _, per = time_parts(torch, ops, w, [w.attn], 20, 5)
             gb = attn_bytes(kv, Bs) / (t * 1e-3) / 1e9
             sweep["attn"][f"B={Bs},kv=U[{lo},{hi}]"] = {"us": t * 1e3, "tokens/s": Bs / (t * 1e-3), "GB/s": gb,
-                                                        "frac": gb / PEAK_HBM_GBS}
+                                                        "frac": gb / PEAK_HBM_GBS,
+                                                        "kernels": kernel_table(per, 20, 1, 0, kv, Bs)}
             log(f"attn B={Bs} kv {lo}..{hi}: {t * 1e3:.1f} us {gb:.0f} GB/s")
             del w
             torch.cuda.empty_cache()
         result["sweep"] = sweep
+
+    if args.copy_calibration:
+        # a plain elementwise copy kernel: reads 512 MiB, writes 512 MiB
+        src = torch.ones(128 << 20, dtype=torch.float32, device="cuda")
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            torch.add(src, 0.0, out=dst)
+        torch.cuda.synchronize()
+        result["copy_calibration_bytes"] = {"read": 512 << 20, "write": 512 << 20}
+        del src, dst
 
     if not args.no_cpu_baseline:
         log("bench: timing the CPU oracle")

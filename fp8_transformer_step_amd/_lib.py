@@ -32,6 +32,10 @@ SIGNATURES = {
     "gqa_decode_attn_workspace_size": (c_sz, [c_i64, c_i32, c_i32, c_i64]),
     "gqa_decode_attn": (ctypes.c_int, [c_vp, c_vp, c_vp, c_i64, c_i64, c_i64, c_vp, c_i64, c_i32, c_i32, c_i32,
                                        c_i64, c_i64, ctypes.c_float, c_vp, c_vp, c_sz, c_vp, c_vp]),
+    "fp8s_profile_start": (ctypes.c_int, [ctypes.c_int]),
+    "fp8s_profile_stop": (ctypes.c_int, []),
+    "fp8s_profile_record": (ctypes.c_int, [ctypes.c_int, ctypes.c_char_p, ctypes.c_int,
+                                           ctypes.POINTER(ctypes.c_float)]),
     "fp8s_last_error": (ctypes.c_char_p, []),
 }
 

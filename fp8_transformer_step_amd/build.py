@@ -23,7 +23,7 @@ DEVICE = ["-x", "hip", "--offload-arch=" + ARCH,
           "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
           "-fno-gpu-rdc"]
 
-SOURCES = ["status.cpp", "quantize.hip", "mlp.hip", "attention.hip"]
+SOURCES = ["status.cpp", "profile.cpp", "quantize.hip", "mlp.hip", "attention.hip"]
 
 
 def _compile(src, verbose):

@@ -24,6 +24,7 @@
 //   * A second small kernel merges the chunks of every (sequence, head).
 #include "common.h"
 #include "host_common.h"
+#include "profile.h"
 
 namespace fp8s {
 
@@ -84,6 +85,7 @@ __global__ __launch_bounds__(256) void attn_split_kernel(AttnArgs a) {
 
     // ---- scores: 16 positions per MFMA group, groups round-robin over waves
     const int n_grp = (n_tok + 15) / 16;
+#pragma unroll 2
     for (int grp = wave; grp < n_grp; grp += 4) {
         const int tl = grp * 16 + (lane & 15);             // position within the chunk
         const bool live = tl < n_tok;
@@ -131,6 +133,7 @@ __global__ __launch_bounds__(256) void attn_split_kernel(AttnArgs a) {
         for (int i = 0; i < 8; ++i) o[h][i] = 0.0f;
     const int dl = 8 * (lane % LPR);
     const int slot = lane / LPR;
+#pragma unroll 4
     for (int t = wave * TPL + slot; t < n_tok; t += 4 * TPL) {
         const uint4 w = *reinterpret_cast<const uint4*>(vbase + (int64_t)(t_begin + t) * a.st + dl);
         const uint32_t ww[4] = {w.x, w.y, w.z, w.w};
@@ -214,7 +217,7 @@ static AttnPlan plan_attn(int64_t B, int32_t Hkv, int64_t hint) {
 
 template <int D, int G>
 static void launch_split(dim3 grid, hipStream_t st, const AttnArgs& a) {
-    hipLaunchKernelGGL((attn_split_kernel<D, G>), grid, dim3(256), 0, st, a);
+    FP8S_LAUNCH("attn_split", (attn_split_kernel<D, G>), grid, dim3(256), 0, st, a);
 }
 
 }  // namespace fp8s
@@ -273,8 +276,8 @@ extern "C" int gqa_decode_attn(const uint16_t* q, const uint16_t* k_cache, const
     int rc = check_launch("gqa_decode_attn (split)");
     if (rc) return rc;
     if (D == 64)
-        hipLaunchKernelGGL(attn_merge_kernel<64>, dim3((unsigned)(B * Hq)), dim3(64), 0, st, a);
+        FP8S_LAUNCH("attn_merge", attn_merge_kernel<64>, dim3((unsigned)(B * Hq)), dim3(64), 0, st, a);
     else
-        hipLaunchKernelGGL(attn_merge_kernel<128>, dim3((unsigned)(B * Hq)), dim3(128), 0, st, a);
+        FP8S_LAUNCH("attn_merge", attn_merge_kernel<128>, dim3((unsigned)(B * Hq)), dim3(128), 0, st, a);
     return check_launch("gqa_decode_attn (merge)");
 }

@@ -37,6 +37,7 @@
 // the MFMA).  No kernel waits on another workgroup, so none can hang.
 #include "common.h"
 #include "host_common.h"
+#include "profile.h"
 
 namespace fp8s {
 
@@ -744,22 +745,22 @@ template <int MODE>
 static void launch_mlp(const MlpPlan& p, hipStream_t st, const MlpArgs& a) {
     const dim3 blk(256), g_gu(a.I / kGuCols), g_xq(p.MT * p.KBH), g_hq(p.MT * p.KBI), g_dn(p.NT * p.S);
     if (a.M <= kTinyM) {
-        hipLaunchKernelGGL(gu_small_kernel<MODE>, g_gu, blk, 0, st, a);
-        hipLaunchKernelGGL((down_small_kernel<MODE, true>), g_dn, blk, 0, st, a);
+        FP8S_LAUNCH("mlp_gu_small", gu_small_kernel<MODE>, g_gu, blk, 0, st, a);
+        FP8S_LAUNCH("mlp_down_small_fused", (down_small_kernel<MODE, true>), g_dn, blk, 0, st, a);
         return;
     }
-    hipLaunchKernelGGL(xq_kernel<MODE>, g_xq, blk, 0, st, a);
+    FP8S_LAUNCH("mlp_xq", xq_kernel<MODE>, g_xq, blk, 0, st, a);
     switch (p.MT) {
     case 1:
-        hipLaunchKernelGGL((gu_kernel<1, MODE>), g_gu, blk, kLdsBytes, st, a);
-        hipLaunchKernelGGL(hq_kernel<MODE>, g_hq, blk, 0, st, a);
-        hipLaunchKernelGGL((down_small_kernel<MODE, false>), g_dn, blk, 0, st, a);
+        FP8S_LAUNCH("mlp_gu", (gu_kernel<1, MODE>), g_gu, blk, kLdsBytes, st, a);
+        FP8S_LAUNCH("mlp_hq", hq_kernel<MODE>, g_hq, blk, 0, st, a);
+        FP8S_LAUNCH("mlp_down_small", (down_small_kernel<MODE, false>), g_dn, blk, 0, st, a);
         break;
 #define FP8S_MT_CASE(N)                                                                \
     case N:                                                                            \
-        hipLaunchKernelGGL((gu_kernel<N, MODE>), g_gu, blk, kLdsBytes, st, a);         \
-        hipLaunchKernelGGL(hq_kernel<MODE>, g_hq, blk, 0, st, a);                       \
-        hipLaunchKernelGGL((down_kernel<N, MODE>), g_dn, blk, kLdsBytes, st, a);       \
+        FP8S_LAUNCH("mlp_gu", (gu_kernel<N, MODE>), g_gu, blk, kLdsBytes, st, a);      \
+        FP8S_LAUNCH("mlp_hq", hq_kernel<MODE>, g_hq, blk, 0, st, a);                    \
+        FP8S_LAUNCH("mlp_down", (down_kernel<N, MODE>), g_dn, blk, kLdsBytes, st, a);   \
         break;
         FP8S_MT_CASE(2) FP8S_MT_CASE(4) FP8S_MT_CASE(8)
 #undef FP8S_MT_CASE

@@ -10,6 +10,7 @@
 // stores (8 bytes per lane) -- HBM-bound, 3 bytes moved per element.
 #include "common.h"
 #include "host_common.h"
+#include "profile.h"
 
 namespace fp8s {
 
@@ -147,17 +148,17 @@ extern "C" int qlinear_quantize(const uint16_t* x, int64_t rows, int64_t cols, i
         const int64_t cbs = cols / 128;
         const int64_t nblk = (rows / 128) * cbs;
         FP8S_REQUIRE(nblk < (1ll << 31), FP8S_EUNSUPPORTED, "qlinear_quantize: matrix too large");
-        hipLaunchKernelGGL(quant_block128_kernel, dim3((unsigned)nblk), dim3(256), 0, st, x, ld_x, cbs, q,
-                           ld_q, reinterpret_cast<float*>(scale), ssr, ssc);
+        FP8S_LAUNCH("quantize_block128", quant_block128_kernel, dim3((unsigned)nblk), dim3(256), 0, st, x, ld_x, cbs, q,
+                    ld_q, reinterpret_cast<float*>(scale), ssr, ssc);
         return check_launch("qlinear_quantize");
     }
     const int64_t bpr = (cols + 2047) / 2048;
     FP8S_REQUIRE(rows * bpr < (1ll << 31), FP8S_EUNSUPPORTED, "qlinear_quantize: matrix too large");
     if (mode == FP8S_Q_ACT_1x128)
-        hipLaunchKernelGGL(quant_rows_kernel<128>, dim3((unsigned)(rows * bpr)), dim3(256), 0, st, x, ld_x,
-                           cols, bpr, q, ld_q, scale, ssr, ssc);
+        FP8S_LAUNCH("quantize_1x128", quant_rows_kernel<128>, dim3((unsigned)(rows * bpr)), dim3(256), 0, st, x, ld_x,
+                    cols, bpr, q, ld_q, scale, ssr, ssc);
     else
-        hipLaunchKernelGGL(quant_rows_kernel<32>, dim3((unsigned)(rows * bpr)), dim3(256), 0, st, x, ld_x,
-                           cols, bpr, q, ld_q, scale, ssr, ssc);
+        FP8S_LAUNCH("quantize_1x32", quant_rows_kernel<32>, dim3((unsigned)(rows * bpr)), dim3(256), 0, st, x, ld_x,
+                    cols, bpr, q, ld_q, scale, ssr, ssc);
     return check_launch("qlinear_quantize");
 }

@@ -123,6 +123,11 @@ def attn_workspace_bytes(B, Hq, D, max_kv_len):
     return int(_lib.load().gqa_decode_attn_workspace_size(B, Hq, D, max_kv_len))
 
 
+def new_attn_workspace(B, Hq, D, max_kv_len, device="cuda"):
+    """A zero-filled attention workspace (its split counters stay zeroed)."""
+    return torch.zeros(max(attn_workspace_bytes(B, Hq, D, max_kv_len), 16), dtype=torch.uint8, device=device)
+
+
 def gqa_decode_attn(q, k_cache, v_cache, kv_len, max_kv_len_hint, softmax_scale=None,
                     out=None, workspace=None, err=None):
     """Decode attention of q [B, Hq, D] over caches [B, Hkv, cap, D] (any
@@ -142,11 +147,31 @@ def gqa_decode_attn(q, k_cache, v_cache, kv_len, max_kv_len_hint, softmax_scale=
         out = torch.empty((B, Hq, D), dtype=torch.bfloat16, device=q.device)
     hint = min(int(max_kv_len_hint), cap)
     if workspace is None:
-        workspace = torch.empty(max(attn_workspace_bytes(B, Hq, D, hint), 16), dtype=torch.uint8,
-                                device=q.device)
+        workspace = new_attn_workspace(B, Hq, D, hint, q.device)
     _lib.check(_lib.load().gqa_decode_attn(
         _bits(q.contiguous()), _bits(k_cache), _bits(v_cache), k_cache.stride(0), k_cache.stride(1),
         k_cache.stride(2), kv_len.data_ptr(), B, Hq, Hkv, D, cap, hint, float(softmax_scale),
         _bits(out), workspace.data_ptr(), workspace.numel(),
         err.data_ptr() if err is not None else None, _stream()))
+    return out
+
+
+def profile_start(max_records=200000):
+    """Start recording per-kernel HIP events inside the library."""
+    _lib.check(_lib.load().fp8s_profile_start(int(max_records)))
+
+
+def profile_stop():
+    """Stop recording; returns [(kernel name, milliseconds), ...] in launch order."""
+    import ctypes
+    lib = _lib.load()
+    n = lib.fp8s_profile_stop()
+    if n < 0:
+        _lib.check(n)
+    out = []
+    buf = ctypes.create_string_buffer(64)
+    ms = ctypes.c_float()
+    for i in range(n):
+        _lib.check(lib.fp8s_profile_record(i, buf, 64, ctypes.byref(ms)))
+        out.append((buf.value.decode(), float(ms.value)))
     return out

@@ -166,6 +166,24 @@ int gqa_decode_attn(const uint16_t* q, const uint16_t* k_cache, const uint16_t* 
                     uint16_t* out, void* workspace, size_t workspace_bytes,
                     int32_t* err_flag, void* stream);
 
+/*
+ * Per-kernel timing, for benchmarks and tracing.  Between fp8s_profile_start
+ * and fp8s_profile_stop every kernel the library launches is given a start
+ * and a stop HIP event that the runtime stamps at the kernel's own begin and
+ * end (hipExtLaunchKernel), so a duration excludes launch gaps.  The events
+ * are created by fp8s_profile_start, up to max_records kernels; later
+ * launches are not recorded.
+ * fp8s_profile_stop waits for the events and returns the number of records
+ * (or a negative FP8S_E* code); fp8s_profile_record copies record i's kernel
+ * name (NUL-terminated, at most name_len bytes) and its duration in
+ * milliseconds.  Host-side state is process-global and not thread-safe:
+ * for single-threaded benchmark drivers.  Do not record while a stream is
+ * being captured into a graph.
+ */
+int fp8s_profile_start(int max_records);
+int fp8s_profile_stop(void);
+int fp8s_profile_record(int i, char* name, int name_len, float* ms);
+
 /* Message for the last non-OK return on the calling thread ("" if none). */
 const char* fp8s_last_error(void);
 
