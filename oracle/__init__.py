@@ -38,3 +38,14 @@ from .fp8 import (  # noqa: F401
 )
 from .mlp import linear_dequant, swiglu, swiglu_mlp  # noqa: F401
 from .attention import gqa_decode_attention, kv_len_schedule  # noqa: F401
+from .dual_ar import (  # noqa: F401
+    RMS_EPS,
+    round_bf16,
+    rmsnorm,
+    fp8_linear,
+    dequant_weight,
+    decoder_layer,
+    embed_sum,
+    greedy_code,
+    dual_ar_step,
+)
