@@ -34,9 +34,32 @@ tests/golden; scale round-trip of exactly representable blocks; the UE8M0
 closed form.
 """
 
+import os
+from concurrent.futures import ThreadPoolExecutor
+
 import numpy as np
 
 E4M3_MAX = 448.0
+_CHUNK = 1 << 20            # elementwise work is done in chunks of this size
+
+
+def _chunked(fn, v, out_dtype):
+    """Apply the elementwise function fn to v in chunks (on a few threads).
+
+    Purely a traversal order: every element is computed by the same fn as an
+    unchunked call would, so the result is identical; it only keeps the
+    float64 temporaries of large tensors in cache."""
+    flat = np.ascontiguousarray(v).reshape(-1)
+    if flat.size <= _CHUNK:
+        return fn(flat).reshape(np.shape(v))
+    out = np.empty(flat.size, dtype=out_dtype)
+    starts = range(0, flat.size, _CHUNK)
+
+    def run(i):
+        out[i:i + _CHUNK] = fn(flat[i:i + _CHUNK])
+    with ThreadPoolExecutor(max_workers=min(16, os.cpu_count() or 1)) as ex:
+        list(ex.map(run, starts))
+    return out.reshape(np.shape(v))
 _MIN_NORMAL_EXP = -6        # smallest normal exponent of E4M3
 _MANT_BITS = 3
 
@@ -49,6 +72,10 @@ def e4m3_encode(v):
     v = np.asarray(v, dtype=np.float64)
     if np.isinf(v).any():
         raise ValueError("e4m3_encode: infinities are not accepted")
+    return _chunked(_encode, v, np.uint8)
+
+
+def _encode(v):
     sign = np.signbit(v)
     a = np.abs(v)
     nan = np.isnan(a)
@@ -76,7 +103,11 @@ def e4m3_encode(v):
 
 def e4m3_decode(b):
     """Decode e4m3 bytes to float64 (exact).  0x7F/0xFF decode to NaN."""
-    b = np.asarray(b, dtype=np.uint8).astype(np.int64)
+    return _chunked(_decode, np.asarray(b, dtype=np.uint8), np.float64)
+
+
+def _decode(b):
+    b = b.astype(np.int64)
     s = np.where(b & 0x80, -1.0, 1.0)
     ef = (b >> 3) & 0xF
     m = b & 0x7
