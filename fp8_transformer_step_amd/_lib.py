@@ -22,6 +22,30 @@ class QWeightC(ctypes.Structure):
                 ("scale_stride_row", c_i64), ("scale_stride_colblk", c_i64)]
 
 
+class BlockWeightsC(ctypes.Structure):
+    """Mirror of fp8s_block_weights."""
+    _fields_ = [("qkv", QWeightC), ("o", QWeightC), ("gate", QWeightC), ("up", QWeightC), ("down", QWeightC),
+                ("norm_attn", c_vp), ("norm_mlp", c_vp)]
+
+
+class DualArModelC(ctypes.Structure):
+    """Mirror of fp8s_dual_ar_model (array fields are host pointers)."""
+    _fields_ = [("hidden", c_i64), ("inter", c_i64), ("codebook_size", c_i64),
+                ("n_heads", c_i32), ("n_kv_heads", c_i32), ("head_dim", c_i32),
+                ("n_codebooks", c_i32), ("n_slow_layers", c_i32), ("n_fast_layers", c_i32),
+                ("rms_eps", ctypes.c_float),
+                ("slow", ctypes.POINTER(BlockWeightsC)), ("fast", ctypes.POINTER(BlockWeightsC)),
+                ("slow_norm", c_vp), ("fast_norm", c_vp),
+                ("embed", ctypes.POINTER(c_vp)), ("heads", ctypes.POINTER(QWeightC))]
+
+
+class KvStateC(ctypes.Structure):
+    """Mirror of fp8s_kv_state (cache arrays are host pointers)."""
+    _fields_ = [("k_cache", ctypes.POINTER(c_vp)), ("v_cache", ctypes.POINTER(c_vp)),
+                ("stride_b", c_i64), ("stride_h", c_i64), ("stride_t", c_i64), ("cap", c_i64),
+                ("kv_len", c_vp), ("max_kv_len_hint", c_i64)]
+
+
 # name -> (restype, argtypes)
 SIGNATURES = {
     "qlinear_quantize": (ctypes.c_int, [c_vp, c_i64, c_i64, c_i64, ctypes.c_int, c_vp, c_i64, c_vp,
@@ -32,6 +56,18 @@ SIGNATURES = {
     "gqa_decode_attn_workspace_size": (c_sz, [c_i64, c_i32, c_i32, c_i64]),
     "gqa_decode_attn": (ctypes.c_int, [c_vp, c_vp, c_vp, c_i64, c_i64, c_i64, c_vp, c_i64, c_i32, c_i32, c_i32,
                                        c_i64, c_i64, ctypes.c_float, c_vp, c_vp, c_sz, c_vp, c_vp]),
+    "qlinear_fp8_workspace_size": (c_sz, [c_i64, c_i64, c_i64]),
+    "qlinear_fp8": (ctypes.c_int, [c_vp, c_i64, c_i64, c_i64, c_vp, ctypes.c_float, QWeightC, c_i64, c_vp, c_i64,
+                                   ctypes.c_int, c_vp, c_i64, c_vp, c_sz, c_vp]),
+    "qkv_proj_kv_append": (ctypes.c_int, [c_vp, c_i64, c_i64, c_i64, c_vp, ctypes.c_float, QWeightC, c_i32, c_i32,
+                                          c_i32, c_vp, c_vp, c_vp, c_i64, c_i64, c_i64, c_vp, c_i64, c_vp, c_sz,
+                                          c_vp, c_vp]),
+    "embed_sum_bf16": (ctypes.c_int, [ctypes.POINTER(c_vp), c_i32, c_i64, c_i64, c_vp, c_i64, c_i64, c_vp, c_vp,
+                                      c_vp, c_vp]),
+    "argmax_rows_f32": (ctypes.c_int, [c_vp, c_i64, c_i64, c_i64, c_vp, c_i64, c_vp]),
+    "dual_ar_decode_step_workspace_size": (c_sz, [ctypes.POINTER(DualArModelC), c_i64, c_i64]),
+    "dual_ar_decode_step": (ctypes.c_int, [ctypes.POINTER(DualArModelC), c_i64, c_vp, ctypes.POINTER(KvStateC), c_vp,
+                                           c_vp, c_vp, c_vp, c_vp, c_sz, c_vp, c_vp]),
     "fp8s_profile_start": (ctypes.c_int, [ctypes.c_int]),
     "fp8s_profile_stop": (ctypes.c_int, []),
     "fp8s_profile_record": (ctypes.c_int, [ctypes.c_int, ctypes.c_char_p, ctypes.c_int,

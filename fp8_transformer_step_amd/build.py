@@ -16,14 +16,14 @@ LIB = os.path.join(HERE, "libfp8step.so")
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 ARCH = "gfx950"
-COMMON = ["-O3", "-fPIC", "-std=c++17", "-Wall", "-Wno-unused-function",
+COMMON = ["-O3", "-fPIC", "-fvisibility=hidden", "-std=c++17", "-Wall", "-Wno-unused-function",
           "-I" + os.path.join(ROOT, "include")]
 # Device code: gfx950 only; packed fp32 VALU ops are disabled.
 DEVICE = ["-x", "hip", "--offload-arch=" + ARCH,
           "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
           "-fno-gpu-rdc"]
 
-SOURCES = ["status.cpp", "profile.cpp", "quantize.hip", "mlp.hip", "attention.hip"]
+SOURCES = ["status.cpp", "profile.cpp", "quantize.hip", "mlp.hip", "attention.hip", "qlinear.hip", "dual_ar.hip"]
 
 
 def _compile(src, verbose):

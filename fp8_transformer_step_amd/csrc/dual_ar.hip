@@ -1,0 +1,384 @@
+// The full batched Dual-AR decode step: the slow AR over its layers, then the
+// fast AR over the codebooks of the frame.
+//
+// What it computes follows the page "Fish Speech KV Cache 推理优化记录",
+// section 2 (a frame is one token per codebook of a 10-codebook RVQ; the slow
+// AR advances in time and predicts the semantic token, the fast AR fills in
+// the remaining codebook tokens of the frame one after another; the frame's
+// tokens are the context of the next step) and sections 4-5 (full-capacity
+// KV caches, the new token's K/V written first, attention over the prefix),
+// and the page "How Fish Audio Keeps a GPU Busy: Continuous Batching for
+// Streaming Speech", section "Where speech makes it harder" (slow AR semantic
+// code, fast AR the other nine).  Every projection is the FP8 GEMM of the
+// page "How We Made Our Text-to-Speech API Free".
+//
+// Everything runs on the caller's stream as a sequence of the library's
+// kernels; nothing synchronises, allocates or reads device memory from the
+// host, so the whole step can be captured into a HIP graph.
+#include <math.h>
+#include <string.h>
+
+#include <string>
+
+#include "common.h"
+#include "host_common.h"
+#include "internal.h"
+#include "profile.h"
+
+namespace fp8s {
+
+constexpr int kMaxTables = 16;
+
+struct EmbedArgs {
+    const uint16_t* t[kMaxTables];
+    int nt;
+    int64_t V, H, ldc;
+    const int32_t* codes;
+    const uint16_t* add;
+    uint16_t* out;
+    int32_t* err;
+};
+
+// One workgroup per row: out = bf16(add + sum_t table_t[code_t]) in fp32.
+__global__ __launch_bounds__(256) void embed_kernel(EmbedArgs a) {
+    __shared__ int s_code[kMaxTables];
+    const int64_t b = blockIdx.x;
+    if ((int)threadIdx.x < a.nt) {
+        int c = a.codes[b * a.ldc + threadIdx.x];
+        if (c < 0 || c >= a.V) {
+            report_error(a.err, FP8S_DEV_CODE_RANGE);
+            c = -1;
+        }
+        s_code[threadIdx.x] = c;
+    }
+    __syncthreads();
+    for (int64_t c8 = 8 * (int64_t)threadIdx.x; c8 < a.H; c8 += 8 * 256) {
+        float f[8] = {0, 0, 0, 0, 0, 0, 0, 0};
+        if (a.add) {
+            const uint4 v = *reinterpret_cast<const uint4*>(a.add + b * a.H + c8);
+            const uint32_t w[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+            for (int i = 0; i < 4; ++i) { f[2 * i] = bf16_to_f32(w[i] & 0xFFFFu); f[2 * i + 1] = bf16_to_f32(w[i] >> 16); }
+        }
+        for (int t = 0; t < a.nt; ++t) {
+            const int c = s_code[t];
+            if (c < 0) continue;
+            const uint4 v = *reinterpret_cast<const uint4*>(a.t[t] + (int64_t)c * a.H + c8);
+            const uint32_t w[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+            for (int i = 0; i < 4; ++i) { f[2 * i] += bf16_to_f32(w[i] & 0xFFFFu); f[2 * i + 1] += bf16_to_f32(w[i] >> 16); }
+        }
+        uint4 o;
+        o.x = f32_to_bf16(f[0]) | (f32_to_bf16(f[1]) << 16);
+        o.y = f32_to_bf16(f[2]) | (f32_to_bf16(f[3]) << 16);
+        o.z = f32_to_bf16(f[4]) | (f32_to_bf16(f[5]) << 16);
+        o.w = f32_to_bf16(f[6]) | (f32_to_bf16(f[7]) << 16);
+        *reinterpret_cast<uint4*>(a.out + b * a.H + c8) = o;
+    }
+}
+
+// (value, index) ordering of greedy decoding: larger value first, then the
+// lower index; NaN never wins (it is mapped to -inf with the sentinel index).
+__device__ __forceinline__ bool better(float v, int i, float bv, int bi) {
+    return v > bv || (v == bv && i < bi);
+}
+
+// One workgroup per row.
+__global__ __launch_bounds__(256) void argmax_kernel(const float* logits, int64_t N, int64_t ld, int32_t* codes,
+                                                     int64_t ldc) {
+    __shared__ float s_v[4];
+    __shared__ int s_i[4];
+    const int64_t b = blockIdx.x;
+    const float* r = logits + b * ld;
+    float bv = -INFINITY;
+    int bi = 0x7FFFFFFF;
+    for (int64_t n = threadIdx.x; n < N; n += 256) {
+        const float v = r[n];
+        if (v > bv) { bv = v; bi = (int)n; }      // increasing n: the first maximum stays
+    }
+#pragma unroll
+    for (int o = 1; o < kWave; o <<= 1) {
+        const float ov = __shfl_xor(bv, o, kWave);
+        const int oi = __shfl_xor(bi, o, kWave);
+        if (better(ov, oi, bv, bi)) { bv = ov; bi = oi; }
+    }
+    const int wave = threadIdx.x >> 6;
+    if ((threadIdx.x & 63) == 0) { s_v[wave] = bv; s_i[wave] = bi; }
+    __syncthreads();
+    if (threadIdx.x == 0) {
+        for (int w = 1; w < 4; ++w)
+            if (better(s_v[w], s_i[w], bv, bi)) { bv = s_v[w]; bi = s_i[w]; }
+        codes[b * ldc] = bi == 0x7FFFFFFF ? 0 : bi;
+    }
+}
+
+// One workgroup per row: out = bf16(x / sqrt(mean(x^2) + eps) * w).
+__global__ __launch_bounds__(256) void rmsnorm_kernel(const uint16_t* x, const uint16_t* w, int64_t H, float eps,
+                                                      uint16_t* out) {
+    __shared__ float s_ss[4];
+    const int64_t b = blockIdx.x;
+    const uint16_t* xr = x + b * H;
+    float ss = 0.0f;
+    for (int64_t c8 = 8 * (int64_t)threadIdx.x; c8 < H; c8 += 8 * 256) {
+        const uint4 v = *reinterpret_cast<const uint4*>(xr + c8);
+        const uint32_t u[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const float lo = bf16_to_f32(u[i] & 0xFFFFu), hi = bf16_to_f32(u[i] >> 16);
+            ss = fmaf(lo, lo, ss);
+            ss = fmaf(hi, hi, ss);
+        }
+    }
+    ss = fsum_xor<kWave>(ss);
+    if ((threadIdx.x & 63) == 0) s_ss[threadIdx.x >> 6] = ss;
+    __syncthreads();
+    const float inv = 1.0f / sqrtf((s_ss[0] + s_ss[1] + s_ss[2] + s_ss[3]) / (float)H + eps);
+    for (int64_t c8 = 8 * (int64_t)threadIdx.x; c8 < H; c8 += 8 * 256) {
+        const uint4 v = *reinterpret_cast<const uint4*>(xr + c8);
+        const uint4 g = *reinterpret_cast<const uint4*>(w + c8);
+        const uint32_t u[4] = {v.x, v.y, v.z, v.w}, gw[4] = {g.x, g.y, g.z, g.w};
+        uint32_t o[4];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const float lo = bf16_to_f32(u[i] & 0xFFFFu) * inv * bf16_to_f32(gw[i] & 0xFFFFu);
+            const float hi = bf16_to_f32(u[i] >> 16) * inv * bf16_to_f32(gw[i] >> 16);
+            o[i] = f32_to_bf16(lo) | (f32_to_bf16(hi) << 16);
+        }
+        *reinterpret_cast<uint4*>(out + b * H + c8) = make_uint4(o[0], o[1], o[2], o[3]);
+    }
+}
+
+// kv_len table of the fast AR: table[p * B + b] = p + 1.
+__global__ __launch_bounds__(256) void fill_steps_kernel(int32_t* table, int P, int B) {
+    const int i = blockIdx.x * 256 + threadIdx.x;
+    if (i < P * B) table[i] = i / B + 1;
+}
+
+// ---- host side ---------------------------------------------------------------
+static size_t align_up(size_t v, size_t a) { return (v + a - 1) / a * a; }
+
+// Re-raise the error of a nested call with the step's context in front.
+static int step_error(int rc, const char* where) {
+    const std::string inner = fp8s_last_error();
+    return set_error(rc, "dual_ar_decode_step: %s: %s", where, inner.c_str());
+}
+
+struct StepPlan {
+    int FS;                               // fast cache slots (C - 1)
+    size_t off_ql, ql_bytes, off_mlp, mlp_bytes, off_attn, attn_bytes;
+    size_t off_x[2], off_xmid, off_h, off_q, off_ao, off_logits, off_fk, off_fv, off_fsteps, total;
+};
+
+static int check_model(const fp8s_dual_ar_model* m, int64_t B, int64_t hint) {
+    FP8S_REQUIRE(m, FP8S_EINVAL, "dual_ar_decode_step: null model");
+    FP8S_REQUIRE(B >= 1 && B <= 128, FP8S_EUNSUPPORTED, "dual_ar_decode_step: B=%lld outside [1, 128]", (long long)B);
+    FP8S_REQUIRE(hint >= 1, FP8S_EINVAL, "dual_ar_decode_step: max_kv_len_hint must be >= 1");
+    FP8S_REQUIRE(m->hidden >= 128 && m->hidden % 128 == 0 && m->inter >= 128 && m->inter % 128 == 0, FP8S_EINVAL,
+                 "dual_ar_decode_step: hidden and inter must be positive multiples of 128");
+    FP8S_REQUIRE(m->n_heads >= 1 && m->n_kv_heads >= 1 && m->n_heads % m->n_kv_heads == 0, FP8S_EINVAL,
+                 "dual_ar_decode_step: n_heads must be a multiple of n_kv_heads");
+    FP8S_REQUIRE(m->head_dim == 64 || m->head_dim == 128, FP8S_EUNSUPPORTED,
+                 "dual_ar_decode_step: head_dim %d (64 or 128)", m->head_dim);
+    FP8S_REQUIRE(((int64_t)m->n_heads * m->head_dim) % 128 == 0, FP8S_EINVAL,
+                 "dual_ar_decode_step: n_heads * head_dim must be a multiple of 128");
+    FP8S_REQUIRE(m->n_codebooks >= 2 && m->n_codebooks <= kMaxTables, FP8S_EUNSUPPORTED,
+                 "dual_ar_decode_step: n_codebooks %d outside [2, %d]", m->n_codebooks, kMaxTables);
+    FP8S_REQUIRE(m->codebook_size >= 32 && m->codebook_size % 32 == 0 && m->codebook_size < (1ll << 31),
+                 FP8S_EINVAL, "dual_ar_decode_step: codebook_size must be a positive multiple of 32");
+    FP8S_REQUIRE(m->n_slow_layers >= 0 && m->n_fast_layers >= 0, FP8S_EINVAL,
+                 "dual_ar_decode_step: negative layer count");
+    FP8S_REQUIRE((m->n_slow_layers == 0 || m->slow) && (m->n_fast_layers == 0 || m->fast) && m->embed && m->heads &&
+                     m->slow_norm && m->fast_norm,
+                 FP8S_EINVAL, "dual_ar_decode_step: null weight array");
+    FP8S_REQUIRE(m->rms_eps >= 0.0f && isfinite(m->rms_eps), FP8S_EINVAL, "dual_ar_decode_step: bad rms_eps");
+    return FP8S_OK;
+}
+
+static StepPlan plan_step(const fp8s_dual_ar_model* m, int64_t B, int64_t hint) {
+    StepPlan p;
+    const int64_t H = m->hidden, A = (int64_t)m->n_heads * m->head_dim, V = m->codebook_size;
+    const int64_t NQKV = (int64_t)(m->n_heads + 2 * m->n_kv_heads) * m->head_dim;
+    p.FS = m->n_codebooks - 1;
+    size_t q1 = qlinear_fp8_workspace_size(B, NQKV, H), q2 = qlinear_fp8_workspace_size(B, H, A),
+           q3 = qlinear_fp8_workspace_size(B, V, H);
+    p.ql_bytes = q1 > q2 ? q1 : q2;
+    p.ql_bytes = p.ql_bytes > q3 ? p.ql_bytes : q3;
+    p.mlp_bytes = swiglu_mlp_fp8_workspace_size(B, H, m->inter, FP8S_MLP_BSGEMM);
+    const size_t a1 = gqa_decode_attn_workspace_size(B, m->n_heads, m->head_dim, hint);
+    const size_t a2 = gqa_decode_attn_workspace_size(B, m->n_heads, m->head_dim, p.FS);
+    p.attn_bytes = a1 > a2 ? a1 : a2;
+    const size_t act = (size_t)B * H * 2, fcache = (size_t)m->n_fast_layers * B * m->n_kv_heads * p.FS * m->head_dim * 2;
+    size_t o = 0;
+    p.off_ql = o; o = align_up(o + p.ql_bytes, 256);
+    p.off_mlp = o; o = align_up(o + p.mlp_bytes, 256);
+    p.off_attn = o; o = align_up(o + p.attn_bytes, 256);
+    p.off_x[0] = o; o = align_up(o + act, 256);
+    p.off_x[1] = o; o = align_up(o + act, 256);
+    p.off_xmid = o; o = align_up(o + act, 256);
+    p.off_h = o; o = align_up(o + act, 256);
+    p.off_q = o; o = align_up(o + (size_t)B * A * 2, 256);
+    p.off_ao = o; o = align_up(o + (size_t)B * A * 2, 256);
+    p.off_logits = o; o = align_up(o + (size_t)B * V * 4, 256);
+    p.off_fk = o; o = align_up(o + fcache, 256);
+    p.off_fv = o; o = align_up(o + fcache, 256);
+    p.off_fsteps = o; o = align_up(o + (size_t)p.FS * B * 4, 256);
+    p.total = o;
+    return p;
+}
+
+struct StepCtx {
+    const fp8s_dual_ar_model* m;
+    int64_t B;
+    uint8_t* ws;
+    const StepPlan* p;
+    int32_t* err;
+    void* stream;
+};
+
+// One pre-norm block: xout = x + O(attn(qkv(norm(x)))), then += MLP(norm(.)).
+static int run_block(const StepCtx& c, const fp8s_block_weights& L, const uint16_t* xin, uint16_t* xout,
+                     uint16_t* kc, uint16_t* vc, int64_t sb, int64_t sh, int64_t stt, int64_t cap,
+                     const int32_t* kv_len, int64_t hint) {
+    const fp8s_dual_ar_model* m = c.m;
+    const int64_t H = m->hidden, A = (int64_t)m->n_heads * m->head_dim;
+    uint16_t* q = reinterpret_cast<uint16_t*>(c.ws + c.p->off_q);
+    uint16_t* ao = reinterpret_cast<uint16_t*>(c.ws + c.p->off_ao);
+    uint16_t* xmid = reinterpret_cast<uint16_t*>(c.ws + c.p->off_xmid);
+    void* qlw = c.ws + c.p->off_ql;
+    int rc = qkv_proj_kv_append(xin, c.B, H, H, L.norm_attn, m->rms_eps, L.qkv, m->n_heads, m->n_kv_heads,
+                                m->head_dim, q, kc, vc, sb, sh, stt, kv_len, cap, qlw, c.p->ql_bytes, c.err, c.stream);
+    if (rc) return step_error(rc, "qkv projection");
+    rc = gqa_decode_attn(q, kc, vc, sb, sh, stt, kv_len, c.B, m->n_heads, m->n_kv_heads, m->head_dim, cap, hint,
+                         1.0f / sqrtf((float)m->head_dim), ao, c.ws + c.p->off_attn, c.p->attn_bytes, c.err, c.stream);
+    if (rc) return step_error(rc, "attention");
+    rc = qlinear_fp8(ao, c.B, A, A, nullptr, 0.0f, L.o, H, xin, H, FP8S_OUT_BF16, xmid, H, qlw, c.p->ql_bytes,
+                     c.stream);
+    if (rc) return step_error(rc, "output projection");
+    rc = swiglu_mlp_fp8_ex(xmid, c.B, H, m->inter, FP8S_MLP_BSGEMM, L.gate, L.up, L.down, L.norm_mlp, m->rms_eps,
+                           xmid, xout, c.ws + c.p->off_mlp, c.p->mlp_bytes, c.stream);
+    if (rc) return step_error(rc, "mlp");
+    return FP8S_OK;
+}
+
+// logits = head . (norm ? RMSNorm(z) : z); codes[:, col] = argmax.
+static int run_head(const StepCtx& c, const fp8s_qweight& head, const uint16_t* z, const uint16_t* norm_w,
+                    float* logits, int32_t* codes, int col) {
+    const fp8s_dual_ar_model* m = c.m;
+    int rc = qlinear_fp8(z, c.B, m->hidden, m->hidden, norm_w, m->rms_eps, head, m->codebook_size, nullptr, 0,
+                         FP8S_OUT_F32, logits, m->codebook_size, c.ws + c.p->off_ql, c.p->ql_bytes, c.stream);
+    if (rc) return step_error(rc, "codebook head");
+    rc = argmax_rows_f32(logits, c.B, m->codebook_size, m->codebook_size, codes + col, m->n_codebooks, c.stream);
+    if (rc) return step_error(rc, "argmax");
+    return FP8S_OK;
+}
+
+}  // namespace fp8s
+
+using namespace fp8s;
+
+extern "C" int embed_sum_bf16(const uint16_t* const* tables, int32_t n_tables, int64_t V, int64_t H,
+                              const int32_t* codes, int64_t ld_codes, int64_t B, const uint16_t* add, uint16_t* out,
+                              int32_t* err_flag, void* stream) {
+    clear_error();
+    FP8S_REQUIRE(tables && codes && out, FP8S_EINVAL, "embed_sum_bf16: null pointer");
+    FP8S_REQUIRE(n_tables >= 1 && n_tables <= kMaxTables, FP8S_EUNSUPPORTED, "embed_sum_bf16: n_tables %d outside [1, %d]",
+                 n_tables, kMaxTables);
+    FP8S_REQUIRE(V >= 1 && V < (1ll << 31) && H >= 8 && H % 8 == 0 && B >= 1 && B < (1ll << 31), FP8S_EINVAL,
+                 "embed_sum_bf16: bad sizes (H must be a positive multiple of 8)");
+    FP8S_REQUIRE(ld_codes >= n_tables, FP8S_EINVAL, "embed_sum_bf16: ld_codes < n_tables");
+    FP8S_REQUIRE(aligned16(out) && (!add || aligned16(add)), FP8S_EINVAL, "embed_sum_bf16: out/add must be 16-byte aligned");
+    EmbedArgs a{};
+    for (int t = 0; t < n_tables; ++t) {
+        FP8S_REQUIRE(tables[t] && aligned16(tables[t]), FP8S_EINVAL, "embed_sum_bf16: table %d null or unaligned", t);
+        a.t[t] = tables[t];
+    }
+    a.nt = n_tables; a.V = V; a.H = H; a.ldc = ld_codes; a.codes = codes; a.add = add; a.out = out; a.err = err_flag;
+    FP8S_LAUNCH("embed_sum", embed_kernel, dim3((unsigned)B), dim3(256), 0, as_stream(stream), a);
+    return check_launch("embed_sum_bf16");
+}
+
+extern "C" int argmax_rows_f32(const float* logits, int64_t B, int64_t N, int64_t ld_logits, int32_t* codes,
+                               int64_t ld_codes, void* stream) {
+    clear_error();
+    FP8S_REQUIRE(logits && codes, FP8S_EINVAL, "argmax_rows_f32: null pointer");
+    FP8S_REQUIRE(B >= 1 && B < (1ll << 31) && N >= 1 && N < (1ll << 31) && ld_logits >= N && ld_codes >= 1,
+                 FP8S_EINVAL, "argmax_rows_f32: bad sizes");
+    FP8S_LAUNCH("argmax", argmax_kernel, dim3((unsigned)B), dim3(256), 0, as_stream(stream), logits, N, ld_logits,
+                codes, ld_codes);
+    return check_launch("argmax_rows_f32");
+}
+
+extern "C" size_t dual_ar_decode_step_workspace_size(const fp8s_dual_ar_model* model, int64_t B,
+                                                     int64_t max_kv_len_hint) {
+    if (check_model(model, B, max_kv_len_hint)) return 0;
+    return plan_step(model, B, max_kv_len_hint).total;
+}
+
+extern "C" int dual_ar_decode_step(const fp8s_dual_ar_model* m, int64_t B, const int32_t* prev_codes,
+                                   const fp8s_kv_state* kv, int32_t* codes, uint16_t* slow_taps, uint16_t* fast_taps,
+                                   float* logits_tap, void* workspace, size_t workspace_bytes, int32_t* err_flag,
+                                   void* stream) {
+    clear_error();
+    FP8S_REQUIRE(kv, FP8S_EINVAL, "dual_ar_decode_step: null kv state");
+    int rc = check_model(m, B, kv->max_kv_len_hint);
+    if (rc) return rc;
+    FP8S_REQUIRE(prev_codes && codes, FP8S_EINVAL, "dual_ar_decode_step: null codes");
+    FP8S_REQUIRE(m->n_slow_layers == 0 || (kv->k_cache && kv->v_cache && kv->kv_len), FP8S_EINVAL,
+                 "dual_ar_decode_step: null cache array or kv_len");
+    for (int l = 0; l < m->n_slow_layers; ++l)
+        FP8S_REQUIRE(kv->k_cache[l] && kv->v_cache[l], FP8S_EINVAL, "dual_ar_decode_step: null cache of layer %d", l);
+    FP8S_REQUIRE(!slow_taps || aligned16(slow_taps), FP8S_EINVAL, "dual_ar_decode_step: slow_taps unaligned");
+    FP8S_REQUIRE(!fast_taps || aligned16(fast_taps), FP8S_EINVAL, "dual_ar_decode_step: fast_taps unaligned");
+    const StepPlan p = plan_step(m, B, kv->max_kv_len_hint);
+    FP8S_REQUIRE(workspace && aligned16(workspace), FP8S_EWORKSPACE, "dual_ar_decode_step: workspace missing or unaligned");
+    FP8S_REQUIRE(workspace_bytes >= p.total, FP8S_EWORKSPACE, "dual_ar_decode_step: workspace %zu < required %zu bytes",
+                 workspace_bytes, p.total);
+    uint8_t* ws = static_cast<uint8_t*>(workspace);
+    const StepCtx c{m, B, ws, &p, err_flag, stream};
+    const int64_t H = m->hidden, BH = B * H, V = m->codebook_size;
+    const int C = m->n_codebooks, L = m->n_slow_layers, F = m->n_fast_layers;
+    uint16_t* xbuf[2] = {reinterpret_cast<uint16_t*>(ws + p.off_x[0]), reinterpret_cast<uint16_t*>(ws + p.off_x[1])};
+    uint16_t* h = reinterpret_cast<uint16_t*>(ws + p.off_h);
+    auto slow_x = [&](int l) { return slow_taps ? slow_taps + (int64_t)l * BH : xbuf[l & 1]; };
+    auto fast_x = [&](int step, int f) {
+        return fast_taps ? fast_taps + ((int64_t)step * (F + 1) + f) * BH : xbuf[f & 1];
+    };
+    auto logits = [&](int cb) {
+        return logits_tap ? logits_tap + (int64_t)cb * B * V : reinterpret_cast<float*>(ws + p.off_logits);
+    };
+    hipStream_t st = as_stream(stream);
+
+    // ---- slow AR
+    rc = embed_sum_bf16(m->embed, C, V, H, prev_codes, C, B, nullptr, slow_x(0), err_flag, stream);
+    if (rc) return step_error(rc, "slow input embedding");
+    for (int l = 0; l < L; ++l) {
+        rc = run_block(c, m->slow[l], slow_x(l), slow_x(l + 1), kv->k_cache[l], kv->v_cache[l], kv->stride_b,
+                       kv->stride_h, kv->stride_t, kv->cap, kv->kv_len, kv->max_kv_len_hint);
+        if (rc) return rc;
+    }
+    FP8S_LAUNCH("rmsnorm", rmsnorm_kernel, dim3((unsigned)B), dim3(256), 0, st, slow_x(L), m->slow_norm, H,
+                m->rms_eps, h);
+    if ((rc = check_launch("dual_ar_decode_step: slow norm"))) return rc;
+    if ((rc = run_head(c, m->heads[0], h, nullptr, logits(0), codes, 0))) return rc;
+
+    // ---- fast AR over the remaining codebooks
+    int32_t* steps = reinterpret_cast<int32_t*>(ws + p.off_fsteps);
+    FP8S_LAUNCH("fill_steps", fill_steps_kernel, dim3((unsigned)((p.FS * B + 255) / 256)), dim3(256), 0, st, steps,
+                p.FS, (int)B);
+    if ((rc = check_launch("dual_ar_decode_step: fast steps"))) return rc;
+    const int64_t fsh = (int64_t)p.FS * m->head_dim, fsb = (int64_t)m->n_kv_heads * fsh;
+    for (int s = 0; s < C - 1; ++s) {
+        rc = embed_sum_bf16(&m->embed[s], 1, V, H, codes + s, C, B, s == 0 ? h : nullptr, fast_x(s, 0), err_flag,
+                            stream);
+        if (rc) return step_error(rc, "fast input embedding");
+        for (int f = 0; f < F; ++f) {
+            uint16_t* fk = reinterpret_cast<uint16_t*>(ws + p.off_fk) + (int64_t)f * B * fsb;
+            uint16_t* fv = reinterpret_cast<uint16_t*>(ws + p.off_fv) + (int64_t)f * B * fsb;
+            rc = run_block(c, m->fast[f], fast_x(s, f), fast_x(s, f + 1), fk, fv, fsb, fsh, m->head_dim, p.FS,
+                           steps + (int64_t)s * B, s + 1);
+            if (rc) return rc;
+        }
+        if ((rc = run_head(c, m->heads[s + 1], fast_x(s, F), m->fast_norm, logits(s + 1), codes, s + 1))) return rc;
+    }
+    return FP8S_OK;
+}

@@ -1,0 +1,339 @@
+// Building blocks of the FP8 MFMA GEMM tiles shared by the MLP and the
+// generic FP8 linear: operand fragments in the 16x16x128 FP8 MFMA layout,
+// direct-to-LDS weight staging, the activation register ring, the MFMA loop
+// with bsgemm or MX scales, the cross-wave reduction, and the 1x128 / 1x32
+// activation quantiser writing operand-ordered fragments.
+#pragma once
+
+#include "common.h"
+#include "fp8step.h"
+
+namespace fp8s {
+
+constexpr int kLdsBytes = 81920;   // LDS-staged items: two workgroups per CU
+constexpr int kFrag = 2048;        // one 16 x 128 e4m3 MFMA operand fragment
+constexpr int kScratch = 64;       // LDS bytes kept for ints ahead of the reduction scratch
+
+// ---- fragments -------------------------------------------------------------------
+// Activation fragment (mt, kb) of a [16*MT, 128*KB] e4m3 matrix: 64 lanes x 32
+// bytes in the MFMA operand order, lane = row%16 + 16*frag_lane_group(k),
+// byte = frag_byte(k) for k the column within the 128-wide block.
+__device__ __forceinline__ int64_t frag_off(int mt, int kb, int KB) { return ((int64_t)mt * KB + kb) * kFrag; }
+
+__device__ __forceinline__ v8i load_frag(const uint8_t* base, int lane) {
+    const uint4* p = reinterpret_cast<const uint4*>(base + lane * 32);
+    uint4 lo = p[0], hi = p[1];
+    v8i r;
+    r[0] = lo.x; r[1] = lo.y; r[2] = lo.z; r[3] = lo.w;
+    r[4] = hi.x; r[5] = hi.y; r[6] = hi.z; r[7] = hi.w;
+    return r;
+}
+
+typedef __attribute__((address_space(3))) void lds_void;
+
+// Stream weight fragment (rows n0..n0+15, K block kb) of W [N, K] into LDS at
+// byte offset `dst`: the first 1 KiB holds every lane's operand bytes 0..15
+// (K = kb*128 + 16g ..), the second its bytes 16..31 (K = kb*128 + 64 + 16g ..).
+__device__ __forceinline__ void stage_w(const uint8_t* w, int64_t ld, int n0, int kb, uint8_t* lds, int dst,
+                                        int lane) {
+    const uint8_t* src = w + (int64_t)(n0 + (lane & 15)) * ld + kb * 128 + 16 * (lane >> 4);
+    __builtin_amdgcn_global_load_lds(src, (lds_void*)(lds + dst), 16, 0, 0);
+    __builtin_amdgcn_global_load_lds(src + 64, (lds_void*)(lds + dst + 1024), 16, 0, 0);
+}
+
+__device__ __forceinline__ v8i lds_frag(const uint8_t* lds, int off, int lane) {
+    uint4 lo = *reinterpret_cast<const uint4*>(lds + off + lane * 16);
+    uint4 hi = *reinterpret_cast<const uint4*>(lds + off + 1024 + lane * 16);
+    v8i r;
+    r[0] = lo.x; r[1] = lo.y; r[2] = lo.z; r[3] = lo.w;
+    r[4] = hi.x; r[5] = hi.y; r[6] = hi.z; r[7] = hi.w;
+    return r;
+}
+
+// An operand fragment stored lane-contiguous (64 lanes x 32 bytes) in LDS.
+__device__ __forceinline__ v8i lds_frag32(const uint8_t* frag, int lane) {
+    const uint4 lo = *reinterpret_cast<const uint4*>(frag + lane * 32);
+    const uint4 hi = *reinterpret_cast<const uint4*>(frag + lane * 32 + 16);
+    v8i r;
+    r[0] = lo.x; r[1] = lo.y; r[2] = lo.z; r[3] = lo.w;
+    r[4] = hi.x; r[5] = hi.y; r[6] = hi.z; r[7] = hi.w;
+    return r;
+}
+
+// bsgemm weight scale of the 128x128 block holding (row n0, K block kb).
+__device__ __forceinline__ float wscale_bs(const void* s, int64_t sr, int64_t sc, int n0, int kb) {
+    return reinterpret_cast<const float*>(s)[(int64_t)(n0 >> 7) * sr + (int64_t)kb * sc];
+}
+// MX weight exponent of (row n0 + lane%16, group kb*4 + lane/16).
+__device__ __forceinline__ int wscale_mx(const void* s, int64_t sr, int64_t sc, int n0, int kb, int lane) {
+    return reinterpret_cast<const uint8_t*>(s)[(int64_t)(n0 + (lane & 15)) * sr + (int64_t)(kb * 4 + (lane >> 4)) * sc];
+}
+
+// Wave layout of a GEMM item: WM waves split the M tiles, WK waves the K range.
+template <int MT>
+struct WaveSplit {
+    static constexpr int WM = (MT % 4 == 0) ? 4 : ((MT % 2 == 0) ? 2 : 1);
+    static constexpr int WK = 4 / WM;
+    static constexpr int MTS = MT / WM;        // M tiles per wave
+};
+
+// One stage of activation operands for the MTS tiles of a wave at block kb.
+template <int MTS, int MODE>
+struct AStage {
+    v8i a[MTS];
+    float4 s[MTS];     // bsgemm: fp32 scales of rows 4*(lane/16) + r
+    int e[MTS];        // MX: exponent byte of this lane's (row, group)
+};
+
+template <int MTS, int MODE>
+__device__ __forceinline__ void load_astage(AStage<MTS, MODE>& st, const uint8_t* q, const void* sc, int KB,
+                                            int mt0, int kb, int lane) {
+#pragma unroll
+    for (int i = 0; i < MTS; ++i) {
+        st.a[i] = load_frag(q + frag_off(mt0 + i, kb, KB), lane);
+        if (MODE == FP8S_MLP_BSGEMM)
+            st.s[i] = *reinterpret_cast<const float4*>(reinterpret_cast<const float*>(sc) +
+                                                       ((int64_t)(mt0 + i) * KB + kb) * 16 + 4 * (lane >> 4));
+        else
+            st.e[i] = reinterpret_cast<const uint8_t*>(sc)[((int64_t)(mt0 + i) * KB + kb) * 64 + lane];
+    }
+}
+
+// acc[i] += A_i * B over one 128-K block (bsgemm scales applied outside the MFMA).
+template <int MTS, int MODE>
+__device__ __forceinline__ void mma_block(v4f* acc, const AStage<MTS, MODE>& st, const v8i& b, float sw, int ew) {
+#pragma unroll
+    for (int i = 0; i < MTS; ++i) {
+        if (MODE == FP8S_MLP_BSGEMM) {
+            const v4f z = {0, 0, 0, 0};
+            const v4f t = mfma_fp8(st.a[i], b, z, kUnitScale, kUnitScale);
+            acc[i][0] += t[0] * (st.s[i].x * sw);
+            acc[i][1] += t[1] * (st.s[i].y * sw);
+            acc[i][2] += t[2] * (st.s[i].z * sw);
+            acc[i][3] += t[3] * (st.s[i].w * sw);
+        } else {
+            acc[i] = mfma_fp8(st.a[i], b, acc[i], st.e[i], ew);
+        }
+    }
+}
+
+// The MFMA loop of a wave: NB weight tiles (LDS fragments at b_off(j, kb)),
+// K blocks [lo, hi), activation stages in a register ring of depth R.
+template <int MTS, int NB, int MODE, typename BOff, typename WScale>
+__device__ __forceinline__ void gemm_loop(v4f (&acc)[NB][MTS], const uint8_t* lds, BOff b_off, WScale wsc,
+                                          const uint8_t* q, const void* sc, int KB, int mt0, int lo, int hi,
+                                          int lane) {
+    constexpr int R = MTS == 1 ? 8 : 3;
+    AStage<MTS, MODE> st[R];
+#pragma unroll
+    for (int u = 0; u < R; ++u)
+        if (lo + u < hi) load_astage<MTS, MODE>(st[u], q, sc, KB, mt0, lo + u, lane);
+    for (int kb0 = lo; kb0 < hi; kb0 += R) {
+#pragma unroll
+        for (int u = 0; u < R; ++u) {
+            const int kb = kb0 + u;
+            if (kb < hi) {
+#pragma unroll
+                for (int j = 0; j < NB; ++j) {
+                    const v8i b = lds_frag(lds, b_off(j, kb), lane);
+                    float sw = 0.0f;
+                    int ew = kUnitScale;
+                    wsc(j, kb, sw, ew);
+                    mma_block<MTS, MODE>(acc[j], st[u], b, sw, ew);
+                }
+                if (kb + R < hi) load_astage<MTS, MODE>(st[u], q, sc, KB, mt0, kb + R, lane);
+            }
+        }
+    }
+}
+
+// Sum the WK partial accumulators of the waves that share M tiles; the wave
+// with wk == 0 ends up with the total.  Uses LDS scratch after the weights.
+template <int MTS, int NB, int WK>
+__device__ __forceinline__ void reduce_wk(v4f (&acc)[NB][MTS], uint8_t* lds, int wm, int wk, int lane) {
+    __syncthreads();                           // everyone is done reading weights
+    if (WK == 1) return;
+    float* red = reinterpret_cast<float*>(lds + kScratch);
+    constexpr int per = NB * MTS * 4 * 64;     // floats per wave
+    if (wk > 0) {
+#pragma unroll
+        for (int j = 0; j < NB; ++j)
+#pragma unroll
+            for (int i = 0; i < MTS; ++i)
+#pragma unroll
+                for (int r = 0; r < 4; ++r) red[(wm * WK + wk) * per + ((j * MTS + i) * 4 + r) * 64 + lane] = acc[j][i][r];
+    }
+    __syncthreads();
+    if (wk == 0) {
+#pragma unroll
+        for (int k = 1; k < WK; ++k)
+#pragma unroll
+            for (int j = 0; j < NB; ++j)
+#pragma unroll
+                for (int i = 0; i < MTS; ++i)
+#pragma unroll
+                    for (int r = 0; r < 4; ++r) acc[j][i][r] += red[(wm * WK + k) * per + ((j * MTS + i) * 4 + r) * 64 + lane];
+    }
+}
+
+
+// bsgemm 1x128: the group is the whole 128-block of the row, spread over the
+// four lanes with the same row (lane bits 4 and 5).
+__device__ __forceinline__ void quant_frag_bs(const float (&v)[32], v8i& q, float4& srow, int lane) {
+    float am = 0.0f;
+#pragma unroll
+    for (int i = 0; i < 32; ++i) am = fmaxf(am, fabsf(v[i]));
+    am = fmaxf(am, __shfl_xor(am, 16, kWave));
+    am = fmaxf(am, __shfl_xor(am, 32, kWave));
+    const float s = bs_scale(am);
+#pragma unroll
+    for (int i = 0; i < 8; ++i) q[i] = (int)e4m3x4(v[4 * i] / s, v[4 * i + 1] / s, v[4 * i + 2] / s, v[4 * i + 3] / s);
+    // scales of the rows this lane accumulates (4*(lane/16) + r)
+    const int r0 = 4 * (lane >> 4);
+    srow.x = __shfl(s, r0 + 0, kWave);
+    srow.y = __shfl(s, r0 + 1, kWave);
+    srow.z = __shfl(s, r0 + 2, kWave);
+    srow.w = __shfl(s, r0 + 3, kWave);
+}
+
+// MX 1x32: the low half of lane g belongs to group g/2, the high half to
+// group 2 + g/2; each group is split over lanes g and g^1 (lane bit 4).  The
+// MFMA takes from lane (row, g) the exponent of group g.
+__device__ __forceinline__ void quant_frag_mx(const float (&v)[32], v8i& q, int& e, int lane) {
+    float lo = 0.0f, hi = 0.0f;
+#pragma unroll
+    for (int i = 0; i < 16; ++i) { lo = fmaxf(lo, fabsf(v[i])); hi = fmaxf(hi, fabsf(v[16 + i])); }
+    lo = fmaxf(lo, __shfl_xor(lo, 16, kWave));
+    hi = fmaxf(hi, __shfl_xor(hi, 16, kWave));
+    const int elo = mx_exponent(__float_as_uint(lo)), ehi = mx_exponent(__float_as_uint(hi));
+    const float mlo = mx_inv_scale(elo), mhi = mx_inv_scale(ehi);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        q[i] = (int)e4m3x4(v[4 * i] * mlo, v[4 * i + 1] * mlo, v[4 * i + 2] * mlo, v[4 * i + 3] * mlo);
+        q[4 + i] = (int)e4m3x4(v[16 + 4 * i] * mhi, v[17 + 4 * i] * mhi, v[18 + 4 * i] * mhi, v[19 + 4 * i] * mhi);
+    }
+    const int g = lane >> 4, src = (lane & 15) + 32 * (g & 1);
+    const int slo = __shfl(elo, src, kWave), shi = __shfl(ehi, src, kWave);
+    e = g < 2 ? slo : shi;
+}
+
+
+
+// Weight operand straight into registers: row n0 + lane%16, K bytes
+// kb*128 + [16g, +16) and kb*128 + [64+16g, +16), g = lane/16.
+__device__ __forceinline__ v8i load_w(const uint8_t* w, int64_t ld, int n0, int kb, int lane) {
+    const uint8_t* row = w + (int64_t)(n0 + (lane & 15)) * ld + kb * 128 + 16 * (lane >> 4);
+    const uint4 lo = *reinterpret_cast<const uint4*>(row);
+    const uint4 hi = *reinterpret_cast<const uint4*>(row + 64);
+    v8i r;
+    r[0] = lo.x; r[1] = lo.y; r[2] = lo.z; r[3] = lo.w;
+    r[4] = hi.x; r[5] = hi.y; r[6] = hi.z; r[7] = hi.w;
+    return r;
+}
+
+// Quantise 8 consecutive columns (8j .. 8j+7 of a 128-block) of one row held
+// by a thread whose 16-lane group owns the row, and store them in MFMA operand
+// order.  bsgemm: 1x128 groups (the 16 lanes), fp32 s = amax / 448, q =
+// e4m3(v / s).  MX: 1x32 groups (4 lanes), E = floor(log2 amax) - 8 + 127,
+// q = e4m3(v * 2^(127 - E)).  frag: the (mt, kb) fragment; sc: its 16 fp32
+// scales (bsgemm) or 64 exponent bytes (MX, scale lane order).
+template <int MODE>
+__device__ __forceinline__ void quant_chunk(const float (&f)[8], uint8_t* frag, void* sc, int row, int j,
+                                            bool valid = true) {
+    float am = 0.0f;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) am = fmaxf(am, fabsf(f[i]));
+    uint32_t q0, q1;
+    if (MODE == FP8S_MLP_BSGEMM) {
+        am = fmax_xor<16>(am);
+        const float s = bs_scale(am);
+        q0 = e4m3x4(f[0] / s, f[1] / s, f[2] / s, f[3] / s);
+        q1 = e4m3x4(f[4] / s, f[5] / s, f[6] / s, f[7] / s);
+        if (valid && j == 0) reinterpret_cast<float*>(sc)[row] = s;
+    } else {
+        am = fmax_xor<4>(am);
+        const int E = mx_exponent(__float_as_uint(am));
+        const float mul = mx_inv_scale(E);
+        q0 = e4m3x4(f[0] * mul, f[1] * mul, f[2] * mul, f[3] * mul);
+        q1 = e4m3x4(f[4] * mul, f[5] * mul, f[6] * mul, f[7] * mul);
+        if (valid && (j & 3) == 0) reinterpret_cast<uint8_t*>(sc)[row + 16 * (j >> 2)] = (uint8_t)E;
+    }
+    const int lane = row + 16 * frag_lane_group(8 * j);
+    if (valid) *reinterpret_cast<uint2*>(frag + lane * 32 + frag_byte(8 * j)) = make_uint2(q0, q1);
+}
+
+template <int MODE>
+__device__ __forceinline__ void* scale_slot(void* base, int mt, int kb, int KB) {
+    return MODE == FP8S_MLP_BSGEMM ? (void*)(reinterpret_cast<float*>(base) + ((int64_t)mt * KB + kb) * 16)
+                                   : (void*)(reinterpret_cast<uint8_t*>(base) + ((int64_t)mt * KB + kb) * 64);
+}
+
+
+// Device-coherent store of a split partial (no cache write-back needed later).
+__device__ __forceinline__ void store_partial(float* p, float v) {
+    __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+// ---- activation quantisation, optionally behind an RMSNorm ----------------------
+// One workgroup per (16-row tile mt, 128-column block kb) of x [M, K] bf16; the
+// 16 threads of a row own 8 columns each and write them into the operand
+// fragment (mt, kb) with the block's scales (rows >= M are zero).  With
+// norm_w set the row is first normalised, bf16(x * rsqrt(mean(x^2) + eps) *
+// w): the same 16 threads read the whole row for its sum of squares (L2
+// resident after the first block of the row).
+struct ActQuantArgs {
+    const uint16_t* x;
+    int64_t ld_x;
+    int M, K, KB;
+    const uint16_t* norm_w;
+    float eps;
+    uint8_t* qx;
+    void* sx;
+};
+
+__device__ __forceinline__ void unpack_bf16x8(const uint4& v, float (&f)[8]) {
+    const uint32_t w[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        f[2 * i] = bf16_to_f32(w[i] & 0xFFFFu);
+        f[2 * i + 1] = bf16_to_f32(w[i] >> 16);
+    }
+}
+
+// 1 / sqrt(mean(x^2) + eps) of row xr [K] (bf16), summed by the 16 lanes of a
+// row group, lane j taking the 8-column chunks j, j + 16, ...
+__device__ __forceinline__ float row_inv_rms(const uint16_t* xr, int K, float eps, int j, bool valid) {
+    float ss = 0.0f;
+    if (valid) {
+        for (int c = 8 * j; c < K; c += 128) {
+            float f[8];
+            unpack_bf16x8(*reinterpret_cast<const uint4*>(xr + c), f);
+#pragma unroll
+            for (int i = 0; i < 8; ++i) ss = fmaf(f[i], f[i], ss);
+        }
+    }
+    ss = fsum_xor<16>(ss);
+    return 1.0f / sqrtf(ss / (float)K + eps);
+}
+
+template <int MODE>
+__global__ __launch_bounds__(256) void act_quant_kernel(ActQuantArgs a) {
+    const int mt = blockIdx.x / a.KB, kb = blockIdx.x % a.KB;
+    const int row = threadIdx.x >> 4, j = threadIdx.x & 15, m = mt * 16 + row;
+    const bool valid = m < a.M;
+    const uint16_t* xr = a.x + (int64_t)(valid ? m : 0) * a.ld_x;
+    float f[8];
+    uint4 v = make_uint4(0, 0, 0, 0);
+    if (valid) v = *reinterpret_cast<const uint4*>(xr + kb * 128 + 8 * j);
+    unpack_bf16x8(v, f);
+    if (a.norm_w) {
+        const float inv = row_inv_rms(xr, a.K, a.eps, j, valid);
+        float w[8];
+        unpack_bf16x8(*reinterpret_cast<const uint4*>(a.norm_w + kb * 128 + 8 * j), w);
+#pragma unroll
+        for (int i = 0; i < 8; ++i) f[i] = bf16_to_f32(f32_to_bf16(f[i] * inv * w[i]));
+    }
+    quant_chunk<MODE>(f, a.qx + frag_off(mt, kb, a.KB), scale_slot<MODE>(a.sx, mt, kb, a.KB), row, j);
+}
+
+}  // namespace fp8s

@@ -36,20 +36,18 @@
 // fp32 block scales applied per 128-K block; MXFP8: the UE8M0 exponents go to
 // the MFMA).  No kernel waits on another workgroup, so none can hang.
 #include "common.h"
+#include "gemm_tiles.h"
 #include "host_common.h"
 #include "profile.h"
 
 namespace fp8s {
 
 constexpr int kGuCols = 16;        // I columns per gate/up item (16 gate + 16 up rows)
-constexpr int kLdsBytes = 81920;   // LDS-staged items: two workgroups per CU
-constexpr int kFrag = 2048;        // one 16 x 128 e4m3 MFMA operand fragment
 constexpr int kMaxKbGu = kLdsBytes / (2 * kFrag);        // 20: hidden <= 2560
 constexpr int kWaveKb = (kMaxKbGu + 3) / 4;               // K blocks per wave in gu_small
 constexpr int kSmallDownCols = 64;                        // down_small: 4 tiles x 4 K blocks
 constexpr int kSmallDownKb = 4;
 constexpr int kCtrlWords = 4096;   // fixed-size control region at workspace offset 0
-constexpr int kScratch = 64;       // LDS bytes kept for ints ahead of the reduction scratch
 
 // DOWN items of the LDS path: NB 16-column tiles, K range bounded by LDS.
 constexpr int kDownNb = 2;
@@ -68,275 +66,10 @@ struct MlpArgs {
     float* ypart;                  // [NT][S][M][cols per tile] split partials
     int* cnt;                      // [NT] split counters (zero between calls)
     int NT, S;
+    const uint16_t* norm_w;        // optional RMSNorm weight [H] in front of the MLP
+    float eps;
+    const uint16_t* res;           // optional residual [M, H] added to y
 };
-
-// ---- fragments -------------------------------------------------------------------
-// Activation fragment (mt, kb) of a [16*MT, 128*KB] e4m3 matrix: 64 lanes x 32
-// bytes in the MFMA operand order, lane = row%16 + 16*frag_lane_group(k),
-// byte = frag_byte(k) for k the column within the 128-wide block.
-__device__ __forceinline__ int64_t frag_off(int mt, int kb, int KB) { return ((int64_t)mt * KB + kb) * kFrag; }
-
-__device__ __forceinline__ v8i load_frag(const uint8_t* base, int lane) {
-    const uint4* p = reinterpret_cast<const uint4*>(base + lane * 32);
-    uint4 lo = p[0], hi = p[1];
-    v8i r;
-    r[0] = lo.x; r[1] = lo.y; r[2] = lo.z; r[3] = lo.w;
-    r[4] = hi.x; r[5] = hi.y; r[6] = hi.z; r[7] = hi.w;
-    return r;
-}
-
-typedef __attribute__((address_space(3))) void lds_void;
-
-// Stream weight fragment (rows n0..n0+15, K block kb) of W [N, K] into LDS at
-// byte offset `dst`: the first 1 KiB holds every lane's operand bytes 0..15
-// (K = kb*128 + 16g ..), the second its bytes 16..31 (K = kb*128 + 64 + 16g ..).
-__device__ __forceinline__ void stage_w(const uint8_t* w, int64_t ld, int n0, int kb, uint8_t* lds, int dst,
-                                        int lane) {
-    const uint8_t* src = w + (int64_t)(n0 + (lane & 15)) * ld + kb * 128 + 16 * (lane >> 4);
-    __builtin_amdgcn_global_load_lds(src, (lds_void*)(lds + dst), 16, 0, 0);
-    __builtin_amdgcn_global_load_lds(src + 64, (lds_void*)(lds + dst + 1024), 16, 0, 0);
-}
-
-__device__ __forceinline__ v8i lds_frag(const uint8_t* lds, int off, int lane) {
-    uint4 lo = *reinterpret_cast<const uint4*>(lds + off + lane * 16);
-    uint4 hi = *reinterpret_cast<const uint4*>(lds + off + 1024 + lane * 16);
-    v8i r;
-    r[0] = lo.x; r[1] = lo.y; r[2] = lo.z; r[3] = lo.w;
-    r[4] = hi.x; r[5] = hi.y; r[6] = hi.z; r[7] = hi.w;
-    return r;
-}
-
-// An operand fragment stored lane-contiguous (64 lanes x 32 bytes) in LDS.
-__device__ __forceinline__ v8i lds_frag32(const uint8_t* frag, int lane) {
-    const uint4 lo = *reinterpret_cast<const uint4*>(frag + lane * 32);
-    const uint4 hi = *reinterpret_cast<const uint4*>(frag + lane * 32 + 16);
-    v8i r;
-    r[0] = lo.x; r[1] = lo.y; r[2] = lo.z; r[3] = lo.w;
-    r[4] = hi.x; r[5] = hi.y; r[6] = hi.z; r[7] = hi.w;
-    return r;
-}
-
-// bsgemm weight scale of the 128x128 block holding (row n0, K block kb).
-__device__ __forceinline__ float wscale_bs(const void* s, int64_t sr, int64_t sc, int n0, int kb) {
-    return reinterpret_cast<const float*>(s)[(int64_t)(n0 >> 7) * sr + (int64_t)kb * sc];
-}
-// MX weight exponent of (row n0 + lane%16, group kb*4 + lane/16).
-__device__ __forceinline__ int wscale_mx(const void* s, int64_t sr, int64_t sc, int n0, int kb, int lane) {
-    return reinterpret_cast<const uint8_t*>(s)[(int64_t)(n0 + (lane & 15)) * sr + (int64_t)(kb * 4 + (lane >> 4)) * sc];
-}
-
-// Wave layout of a GEMM item: WM waves split the M tiles, WK waves the K range.
-template <int MT>
-struct WaveSplit {
-    static constexpr int WM = (MT % 4 == 0) ? 4 : ((MT % 2 == 0) ? 2 : 1);
-    static constexpr int WK = 4 / WM;
-    static constexpr int MTS = MT / WM;        // M tiles per wave
-};
-
-// One stage of activation operands for the MTS tiles of a wave at block kb.
-template <int MTS, int MODE>
-struct AStage {
-    v8i a[MTS];
-    float4 s[MTS];     // bsgemm: fp32 scales of rows 4*(lane/16) + r
-    int e[MTS];        // MX: exponent byte of this lane's (row, group)
-};
-
-template <int MTS, int MODE>
-__device__ __forceinline__ void load_astage(AStage<MTS, MODE>& st, const uint8_t* q, const void* sc, int KB,
-                                            int mt0, int kb, int lane) {
-#pragma unroll
-    for (int i = 0; i < MTS; ++i) {
-        st.a[i] = load_frag(q + frag_off(mt0 + i, kb, KB), lane);
-        if (MODE == FP8S_MLP_BSGEMM)
-            st.s[i] = *reinterpret_cast<const float4*>(reinterpret_cast<const float*>(sc) +
-                                                       ((int64_t)(mt0 + i) * KB + kb) * 16 + 4 * (lane >> 4));
-        else
-            st.e[i] = reinterpret_cast<const uint8_t*>(sc)[((int64_t)(mt0 + i) * KB + kb) * 64 + lane];
-    }
-}
-
-// acc[i] += A_i * B over one 128-K block (bsgemm scales applied outside the MFMA).
-template <int MTS, int MODE>
-__device__ __forceinline__ void mma_block(v4f* acc, const AStage<MTS, MODE>& st, const v8i& b, float sw, int ew) {
-#pragma unroll
-    for (int i = 0; i < MTS; ++i) {
-        if (MODE == FP8S_MLP_BSGEMM) {
-            const v4f z = {0, 0, 0, 0};
-            const v4f t = mfma_fp8(st.a[i], b, z, kUnitScale, kUnitScale);
-            acc[i][0] += t[0] * (st.s[i].x * sw);
-            acc[i][1] += t[1] * (st.s[i].y * sw);
-            acc[i][2] += t[2] * (st.s[i].z * sw);
-            acc[i][3] += t[3] * (st.s[i].w * sw);
-        } else {
-            acc[i] = mfma_fp8(st.a[i], b, acc[i], st.e[i], ew);
-        }
-    }
-}
-
-// The MFMA loop of a wave: NB weight tiles (LDS fragments at b_off(j, kb)),
-// K blocks [lo, hi), activation stages in a register ring of depth R.
-template <int MTS, int NB, int MODE, typename BOff, typename WScale>
-__device__ __forceinline__ void gemm_loop(v4f (&acc)[NB][MTS], const uint8_t* lds, BOff b_off, WScale wsc,
-                                          const uint8_t* q, const void* sc, int KB, int mt0, int lo, int hi,
-                                          int lane) {
-    constexpr int R = MTS == 1 ? 8 : 3;
-    AStage<MTS, MODE> st[R];
-#pragma unroll
-    for (int u = 0; u < R; ++u)
-        if (lo + u < hi) load_astage<MTS, MODE>(st[u], q, sc, KB, mt0, lo + u, lane);
-    for (int kb0 = lo; kb0 < hi; kb0 += R) {
-#pragma unroll
-        for (int u = 0; u < R; ++u) {
-            const int kb = kb0 + u;
-            if (kb < hi) {
-#pragma unroll
-                for (int j = 0; j < NB; ++j) {
-                    const v8i b = lds_frag(lds, b_off(j, kb), lane);
-                    float sw = 0.0f;
-                    int ew = kUnitScale;
-                    wsc(j, kb, sw, ew);
-                    mma_block<MTS, MODE>(acc[j], st[u], b, sw, ew);
-                }
-                if (kb + R < hi) load_astage<MTS, MODE>(st[u], q, sc, KB, mt0, kb + R, lane);
-            }
-        }
-    }
-}
-
-// Sum the WK partial accumulators of the waves that share M tiles; the wave
-// with wk == 0 ends up with the total.  Uses LDS scratch after the weights.
-template <int MTS, int NB, int WK>
-__device__ __forceinline__ void reduce_wk(v4f (&acc)[NB][MTS], uint8_t* lds, int wm, int wk, int lane) {
-    __syncthreads();                           // everyone is done reading weights
-    if (WK == 1) return;
-    float* red = reinterpret_cast<float*>(lds + kScratch);
-    constexpr int per = NB * MTS * 4 * 64;     // floats per wave
-    if (wk > 0) {
-#pragma unroll
-        for (int j = 0; j < NB; ++j)
-#pragma unroll
-            for (int i = 0; i < MTS; ++i)
-#pragma unroll
-                for (int r = 0; r < 4; ++r) red[(wm * WK + wk) * per + ((j * MTS + i) * 4 + r) * 64 + lane] = acc[j][i][r];
-    }
-    __syncthreads();
-    if (wk == 0) {
-#pragma unroll
-        for (int k = 1; k < WK; ++k)
-#pragma unroll
-            for (int j = 0; j < NB; ++j)
-#pragma unroll
-                for (int i = 0; i < MTS; ++i)
-#pragma unroll
-                    for (int r = 0; r < 4; ++r) acc[j][i][r] += red[(wm * WK + k) * per + ((j * MTS + i) * 4 + r) * 64 + lane];
-    }
-}
-
-
-// bsgemm 1x128: the group is the whole 128-block of the row, spread over the
-// four lanes with the same row (lane bits 4 and 5).
-__device__ __forceinline__ void quant_frag_bs(const float (&v)[32], v8i& q, float4& srow, int lane) {
-    float am = 0.0f;
-#pragma unroll
-    for (int i = 0; i < 32; ++i) am = fmaxf(am, fabsf(v[i]));
-    am = fmaxf(am, __shfl_xor(am, 16, kWave));
-    am = fmaxf(am, __shfl_xor(am, 32, kWave));
-    const float s = bs_scale(am);
-#pragma unroll
-    for (int i = 0; i < 8; ++i) q[i] = (int)e4m3x4(v[4 * i] / s, v[4 * i + 1] / s, v[4 * i + 2] / s, v[4 * i + 3] / s);
-    // scales of the rows this lane accumulates (4*(lane/16) + r)
-    const int r0 = 4 * (lane >> 4);
-    srow.x = __shfl(s, r0 + 0, kWave);
-    srow.y = __shfl(s, r0 + 1, kWave);
-    srow.z = __shfl(s, r0 + 2, kWave);
-    srow.w = __shfl(s, r0 + 3, kWave);
-}
-
-// MX 1x32: the low half of lane g belongs to group g/2, the high half to
-// group 2 + g/2; each group is split over lanes g and g^1 (lane bit 4).  The
-// MFMA takes from lane (row, g) the exponent of group g.
-__device__ __forceinline__ void quant_frag_mx(const float (&v)[32], v8i& q, int& e, int lane) {
-    float lo = 0.0f, hi = 0.0f;
-#pragma unroll
-    for (int i = 0; i < 16; ++i) { lo = fmaxf(lo, fabsf(v[i])); hi = fmaxf(hi, fabsf(v[16 + i])); }
-    lo = fmaxf(lo, __shfl_xor(lo, 16, kWave));
-    hi = fmaxf(hi, __shfl_xor(hi, 16, kWave));
-    const int elo = mx_exponent(__float_as_uint(lo)), ehi = mx_exponent(__float_as_uint(hi));
-    const float mlo = mx_inv_scale(elo), mhi = mx_inv_scale(ehi);
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-        q[i] = (int)e4m3x4(v[4 * i] * mlo, v[4 * i + 1] * mlo, v[4 * i + 2] * mlo, v[4 * i + 3] * mlo);
-        q[4 + i] = (int)e4m3x4(v[16 + 4 * i] * mhi, v[17 + 4 * i] * mhi, v[18 + 4 * i] * mhi, v[19 + 4 * i] * mhi);
-    }
-    const int g = lane >> 4, src = (lane & 15) + 32 * (g & 1);
-    const int slo = __shfl(elo, src, kWave), shi = __shfl(ehi, src, kWave);
-    e = g < 2 ? slo : shi;
-}
-
-
-
-// Weight operand straight into registers: row n0 + lane%16, K bytes
-// kb*128 + [16g, +16) and kb*128 + [64+16g, +16), g = lane/16.
-__device__ __forceinline__ v8i load_w(const uint8_t* w, int64_t ld, int n0, int kb, int lane) {
-    const uint8_t* row = w + (int64_t)(n0 + (lane & 15)) * ld + kb * 128 + 16 * (lane >> 4);
-    const uint4 lo = *reinterpret_cast<const uint4*>(row);
-    const uint4 hi = *reinterpret_cast<const uint4*>(row + 64);
-    v8i r;
-    r[0] = lo.x; r[1] = lo.y; r[2] = lo.z; r[3] = lo.w;
-    r[4] = hi.x; r[5] = hi.y; r[6] = hi.z; r[7] = hi.w;
-    return r;
-}
-
-// Quantise 8 consecutive columns (8j .. 8j+7 of a 128-block) of one row held
-// by a thread whose 16-lane group owns the row, and store them in MFMA operand
-// order.  bsgemm: 1x128 groups (the 16 lanes), fp32 s = amax / 448, q =
-// e4m3(v / s).  MX: 1x32 groups (4 lanes), E = floor(log2 amax) - 8 + 127,
-// q = e4m3(v * 2^(127 - E)).  frag: the (mt, kb) fragment; sc: its 16 fp32
-// scales (bsgemm) or 64 exponent bytes (MX, scale lane order).
-template <int MODE>
-__device__ __forceinline__ void quant_chunk(const float (&f)[8], uint8_t* frag, void* sc, int row, int j,
-                                            bool valid = true) {
-    float am = 0.0f;
-#pragma unroll
-    for (int i = 0; i < 8; ++i) am = fmaxf(am, fabsf(f[i]));
-    uint32_t q0, q1;
-    if (MODE == FP8S_MLP_BSGEMM) {
-        am = fmax_xor<16>(am);
-        const float s = bs_scale(am);
-        q0 = e4m3x4(f[0] / s, f[1] / s, f[2] / s, f[3] / s);
-        q1 = e4m3x4(f[4] / s, f[5] / s, f[6] / s, f[7] / s);
-        if (valid && j == 0) reinterpret_cast<float*>(sc)[row] = s;
-    } else {
-        am = fmax_xor<4>(am);
-        const int E = mx_exponent(__float_as_uint(am));
-        const float mul = mx_inv_scale(E);
-        q0 = e4m3x4(f[0] * mul, f[1] * mul, f[2] * mul, f[3] * mul);
-        q1 = e4m3x4(f[4] * mul, f[5] * mul, f[6] * mul, f[7] * mul);
-        if (valid && (j & 3) == 0) reinterpret_cast<uint8_t*>(sc)[row + 16 * (j >> 2)] = (uint8_t)E;
-    }
-    const int lane = row + 16 * frag_lane_group(8 * j);
-    if (valid) *reinterpret_cast<uint2*>(frag + lane * 32 + frag_byte(8 * j)) = make_uint2(q0, q1);
-}
-
-template <int MODE>
-__device__ __forceinline__ void* scale_slot(void* base, int mt, int kb, int KB) {
-    return MODE == FP8S_MLP_BSGEMM ? (void*)(reinterpret_cast<float*>(base) + ((int64_t)mt * KB + kb) * 16)
-                                   : (void*)(reinterpret_cast<uint8_t*>(base) + ((int64_t)mt * KB + kb) * 64);
-}
-
-// ---- xq: x [M, H] bf16 -> q_x fragments (one workgroup per (M tile, K block))
-template <int MODE>
-__global__ __launch_bounds__(256) void xq_kernel(MlpArgs a) {
-    const int mt = blockIdx.x / a.KBH, kb = blockIdx.x % a.KBH;
-    const int row = threadIdx.x >> 4, j = threadIdx.x & 15, m = mt * 16 + row;
-    float f[8];
-    uint4 v = make_uint4(0, 0, 0, 0);
-    if (m < a.M) v = *reinterpret_cast<const uint4*>(a.x + (int64_t)m * a.H + kb * 128 + 8 * j);
-    const uint32_t w[4] = {v.x, v.y, v.z, v.w};
-#pragma unroll
-    for (int i = 0; i < 4; ++i) { f[2 * i] = bf16_to_f32(w[i] & 0xFFFFu); f[2 * i + 1] = bf16_to_f32(w[i] >> 16); }
-    quant_chunk<MODE>(f, a.qx + frag_off(mt, kb, a.KBH), scale_slot<MODE>(a.sx, mt, kb, a.KBH), row, j);
-}
 
 // ---- hq: h = silu(g) * u -> q_h fragments (one workgroup per (M tile, K block))
 template <int MODE>
@@ -523,9 +256,6 @@ __global__ __launch_bounds__(256, 2) void gu_kernel(MlpArgs a) {
 // thread waits for its partial stores to complete, one thread bumps the tile
 // counter, and the last split of the tile sums the S partials in split order
 // (deterministic) into bf16 y and re-arms the counter.
-__device__ __forceinline__ void store_partial(float* p, float v) {
-    __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-}
 template <int COLS>
 __device__ __forceinline__ void finish_split(const MlpArgs& a, int nt, int s, int n0, int* s_prev) {
     __builtin_amdgcn_s_waitcnt(0);             // this thread's partial stores are complete
@@ -539,6 +269,7 @@ __device__ __forceinline__ void finish_split(const MlpArgs& a, int nt, int s, in
         for (int k = 0; k < a.S; ++k)
             sum += __hip_atomic_load(base + (int64_t)k * a.M * COLS + e, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
         const int m = e / COLS, n = n0 + (e % COLS);
+        if (a.res) sum += bf16_to_f32(a.res[(int64_t)m * a.H + n]);
         a.y[(int64_t)m * a.H + n] = (uint16_t)f32_to_bf16(sum);
     }
     if (threadIdx.x == 0) store_relaxed_agent(a.cnt + nt, 0);
@@ -739,17 +470,19 @@ static MlpPlan plan_mlp(int64_t M, int64_t H, int64_t I, int mode) {
 }
 
 // M <= 4  : gu_small (x quantised in-kernel) -> down_small<fused SwiGLU+quant>
+//           (with an RMSNorm in front, the M <= 16 chain instead)
 // M <= 16 : xq -> gu<1> -> hq -> down_small
 // M >  16 : xq -> gu<MT> -> hq -> down<MT>
 template <int MODE>
 static void launch_mlp(const MlpPlan& p, hipStream_t st, const MlpArgs& a) {
     const dim3 blk(256), g_gu(a.I / kGuCols), g_xq(p.MT * p.KBH), g_hq(p.MT * p.KBI), g_dn(p.NT * p.S);
-    if (a.M <= kTinyM) {
+    if (a.M <= kTinyM && !a.norm_w) {
         FP8S_LAUNCH("mlp_gu_small", gu_small_kernel<MODE>, g_gu, blk, 0, st, a);
         FP8S_LAUNCH("mlp_down_small_fused", (down_small_kernel<MODE, true>), g_dn, blk, 0, st, a);
         return;
     }
-    FP8S_LAUNCH("mlp_xq", xq_kernel<MODE>, g_xq, blk, 0, st, a);
+    const ActQuantArgs xa{a.x, a.H, a.M, a.H, a.KBH, a.norm_w, a.eps, a.qx, a.sx};
+    FP8S_LAUNCH("mlp_xq", act_quant_kernel<MODE>, g_xq, blk, 0, st, xa);
     switch (p.MT) {
     case 1:
         FP8S_LAUNCH("mlp_gu", (gu_kernel<1, MODE>), g_gu, blk, kLdsBytes, st, a);
@@ -787,11 +520,11 @@ extern "C" size_t swiglu_mlp_fp8_workspace_size(int64_t M, int64_t hidden, int64
     return plan_mlp(M, hidden, inter, mode).total;
 }
 
-extern "C" int swiglu_mlp_fp8(const uint16_t* x, int64_t M, int64_t H, int64_t I, int mode,
-                              fp8s_qweight gate, fp8s_qweight up, fp8s_qweight down, uint16_t* y,
-                              void* workspace, size_t workspace_bytes, int32_t* err_flag, void* stream) {
-    clear_error();
-    (void)err_flag;   // no device-side error conditions remain in this path
+namespace fp8s {
+int swiglu_mlp_fp8_ex(const uint16_t* x, int64_t M, int64_t H, int64_t I, int mode, fp8s_qweight gate,
+                      fp8s_qweight up, fp8s_qweight down, const uint16_t* norm_w, float eps,
+                      const uint16_t* residual, uint16_t* y, void* workspace, size_t workspace_bytes,
+                      void* stream) {
     FP8S_REQUIRE(x && y, FP8S_EINVAL, "swiglu_mlp_fp8: null x or y");
     FP8S_REQUIRE(mode == FP8S_MLP_BSGEMM || mode == FP8S_MLP_MXFP8, FP8S_EINVAL, "swiglu_mlp_fp8: unknown mode %d",
                  mode);
@@ -803,6 +536,8 @@ extern "C" int swiglu_mlp_fp8(const uint16_t* x, int64_t M, int64_t H, int64_t I
                  "swiglu_mlp_fp8: hidden=%lld > %d (a gate/up tile must fit in LDS)", (long long)H, 128 * kMaxKbGu);
     FP8S_REQUIRE(I <= (1 << 20), FP8S_EUNSUPPORTED, "swiglu_mlp_fp8: inter too large");
     FP8S_REQUIRE(aligned16(x) && aligned16(y), FP8S_EINVAL, "swiglu_mlp_fp8: x and y must be 16-byte aligned");
+    FP8S_REQUIRE(!norm_w || aligned16(norm_w), FP8S_EINVAL, "swiglu_mlp_fp8: norm weight must be 16-byte aligned");
+    FP8S_REQUIRE(!norm_w || eps >= 0.0f, FP8S_EINVAL, "swiglu_mlp_fp8: eps must be >= 0");
     int rc;
     if ((rc = check_qweight(gate, H, mode, "gate")) || (rc = check_qweight(up, H, mode, "up")) ||
         (rc = check_qweight(down, I, mode, "down")))
@@ -826,10 +561,21 @@ extern "C" int swiglu_mlp_fp8(const uint16_t* x, int64_t M, int64_t H, int64_t I
     a.ypart = reinterpret_cast<float*>(ws + p.off_ypart);
     a.cnt = reinterpret_cast<int*>(ws + p.off_ctrl);
     a.NT = p.NT; a.S = p.S;
+    a.norm_w = norm_w; a.eps = eps; a.res = residual;
     hipStream_t st = as_stream(stream);
     if (mode == FP8S_MLP_BSGEMM)
         launch_mlp<FP8S_MLP_BSGEMM>(p, st, a);
     else
         launch_mlp<FP8S_MLP_MXFP8>(p, st, a);
     return check_launch("swiglu_mlp_fp8");
+}
+}  // namespace fp8s
+
+extern "C" int swiglu_mlp_fp8(const uint16_t* x, int64_t M, int64_t H, int64_t I, int mode,
+                              fp8s_qweight gate, fp8s_qweight up, fp8s_qweight down, uint16_t* y,
+                              void* workspace, size_t workspace_bytes, int32_t* err_flag, void* stream) {
+    clear_error();
+    (void)err_flag;   // no device-side error conditions remain in this path
+    return swiglu_mlp_fp8_ex(x, M, H, I, mode, gate, up, down, nullptr, 0.0f, nullptr, y, workspace,
+                             workspace_bytes, stream);
 }

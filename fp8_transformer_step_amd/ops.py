@@ -16,7 +16,8 @@ from . import _lib
 # Quantisation and MLP modes (include/fp8step.h).
 Q_ACT_1x128, Q_WGT_128x128, Q_MX_1x32 = 0, 1, 2
 MLP_BSGEMM, MLP_MXFP8 = 0, 1
-DEV_KVLEN_RANGE, DEV_WAIT_TIMEOUT = 1, 2
+DEV_KVLEN_RANGE, DEV_WAIT_TIMEOUT, DEV_CODE_RANGE = 1, 2, 3
+OUT_BF16, OUT_F32 = 0, 1
 
 
 def _stream():
@@ -154,6 +155,158 @@ def gqa_decode_attn(q, k_cache, v_cache, kv_len, max_kv_len_hint, softmax_scale=
         _bits(out), workspace.data_ptr(), workspace.numel(),
         err.data_ptr() if err is not None else None, _stream()))
     return out
+
+
+def _opt_ptr(t):
+    return t.data_ptr() if t is not None else None
+
+
+def qlinear_workspace_bytes(M, N, K):
+    return int(_lib.load().qlinear_fp8_workspace_size(M, N, K))
+
+
+def new_qlinear_workspace(M, N, K, device="cuda"):
+    """A zero-filled workspace (the library keeps its control words zeroed)."""
+    n = qlinear_workspace_bytes(M, N, K)
+    if n == 0:
+        raise ValueError("unsupported qlinear shape")
+    return torch.zeros(n, dtype=torch.uint8, device=device)
+
+
+def qlinear_fp8(x, w, norm_w=None, eps=1e-6, residual=None, out_dtype=OUT_BF16, y=None, workspace=None):
+    """y = [residual +] quant(norm(x)) . W^T for x [M, K] bf16 and a bsgemm
+    QWeight W [N, K]; y is bf16 or fp32 [M, N]."""
+    _require_cuda(x, norm_w, residual)
+    if x.dim() != 2 or x.stride(1) != 1:
+        raise ValueError("x must be 2-D with unit column stride")
+    M, K = x.shape
+    N = w.w.shape[0]
+    if y is None:
+        y = torch.empty((M, N), dtype=torch.bfloat16 if out_dtype == OUT_BF16 else torch.float32, device=x.device)
+    if workspace is None:
+        workspace = new_qlinear_workspace(M, N, K, x.device)
+    _lib.check(_lib.load().qlinear_fp8(
+        _bits(x), M, K, x.stride(0), _opt_ptr(norm_w), float(eps), w.as_c(), N,
+        _opt_ptr(residual), residual.stride(0) if residual is not None else 0, out_dtype,
+        y.data_ptr(), y.stride(0), workspace.data_ptr(), workspace.numel(), _stream()))
+    return y
+
+
+def qkv_proj_kv_append(x, w_qkv, Hq, Hkv, D, k_cache, v_cache, kv_len, norm_w=None, eps=1e-6,
+                       q_out=None, workspace=None, err=None):
+    """q = query part of quant(norm(x)) . W_qkv^T ([M, Hq*D] bf16); the key and
+    value parts are written into the caches [B, Hkv, cap, D] at kv_len - 1."""
+    _require_cuda(x, k_cache, v_cache, kv_len)
+    if k_cache.stride() != v_cache.stride() or k_cache.shape != v_cache.shape or k_cache.stride(3) != 1:
+        raise ValueError("k_cache and v_cache must share shape and strides, D contiguous")
+    M, K = x.shape
+    N = (Hq + 2 * Hkv) * D
+    if q_out is None:
+        q_out = torch.empty((M, Hq * D), dtype=torch.bfloat16, device=x.device)
+    if workspace is None:
+        workspace = new_qlinear_workspace(M, N, K, x.device)
+    _lib.check(_lib.load().qkv_proj_kv_append(
+        _bits(x), M, K, x.stride(0), _opt_ptr(norm_w), float(eps), w_qkv.as_c(), Hq, Hkv, D, _bits(q_out),
+        _bits(k_cache), _bits(v_cache), k_cache.stride(0), k_cache.stride(1), k_cache.stride(2),
+        kv_len.data_ptr(), k_cache.shape[2], workspace.data_ptr(), workspace.numel(), _opt_ptr(err), _stream()))
+    return q_out
+
+
+def embed_sum(tables, codes, add=None, out=None, err=None):
+    """out[b] = bf16(add[b] + sum_c tables[c][codes[b, c]]); codes int32 [B, >= len(tables)]."""
+    import ctypes
+    _require_cuda(codes, add, *tables)
+    B = codes.shape[0]
+    V, H = tables[0].shape
+    if out is None:
+        out = torch.empty((B, H), dtype=torch.bfloat16, device=codes.device)
+    arr = (ctypes.c_void_p * len(tables))(*[t.data_ptr() for t in tables])
+    _lib.check(_lib.load().embed_sum_bf16(arr, len(tables), V, H, codes.data_ptr(), codes.stride(0), B,
+                                          _opt_ptr(add), _bits(out), _opt_ptr(err), _stream()))
+    return out
+
+
+def argmax_rows(logits, codes=None):
+    """Greedy codes of fp32 logits [B, N] (ties to the lowest index); int32 [B]
+    or into column 0 of the given int32 codes view."""
+    _require_cuda(logits)
+    B, N = logits.shape
+    if codes is None:
+        codes = torch.empty((B, 1), dtype=torch.int32, device=logits.device)
+    _lib.check(_lib.load().argmax_rows_f32(logits.data_ptr(), B, N, logits.stride(0), codes.data_ptr(),
+                                           codes.stride(0), _stream()))
+    return codes
+
+
+class DualArModel:
+    """Device weights of a Dual-AR model and the C structs that describe them.
+
+    slow / fast: lists of dicts with QWeight 'qkv', 'o', 'gate', 'up', 'down'
+    and bf16 tensors 'norm_attn', 'norm_mlp'; embed: list of bf16 [V, H];
+    heads: list of QWeight [V, H]."""
+
+    def __init__(self, slow, fast, slow_norm, fast_norm, embed, heads, n_heads, n_kv_heads, head_dim,
+                 inter, rms_eps=1e-6):
+        import ctypes
+        self.slow, self.fast, self.embed, self.heads = slow, fast, embed, heads
+        self.slow_norm, self.fast_norm = slow_norm, fast_norm
+        V, H = embed[0].shape
+
+        def block(d):
+            return _lib.BlockWeightsC(d["qkv"].as_c(), d["o"].as_c(), d["gate"].as_c(), d["up"].as_c(),
+                                      d["down"].as_c(), d["norm_attn"].data_ptr(), d["norm_mlp"].data_ptr())
+        self._slow_c = (_lib.BlockWeightsC * max(len(slow), 1))(*[block(d) for d in slow])
+        self._fast_c = (_lib.BlockWeightsC * max(len(fast), 1))(*[block(d) for d in fast])
+        self._embed_c = (ctypes.c_void_p * len(embed))(*[t.data_ptr() for t in embed])
+        self._heads_c = (_lib.QWeightC * len(heads))(*[h.as_c() for h in heads])
+        self.c = _lib.DualArModelC(H, inter, V, n_heads, n_kv_heads, head_dim, len(embed), len(slow), len(fast),
+                                   float(rms_eps), self._slow_c, self._fast_c, slow_norm.data_ptr(),
+                                   fast_norm.data_ptr(), self._embed_c, self._heads_c)
+
+    def workspace_bytes(self, B, max_kv_len_hint):
+        import ctypes
+        return int(_lib.load().dual_ar_decode_step_workspace_size(ctypes.byref(self.c), B, max_kv_len_hint))
+
+    def new_workspace(self, B, max_kv_len_hint, device="cuda"):
+        n = self.workspace_bytes(B, max_kv_len_hint)
+        if n == 0:
+            raise ValueError("unsupported Dual-AR configuration")
+        return torch.zeros(n, dtype=torch.uint8, device=device)
+
+
+class KvState:
+    """Per-slow-layer K/V caches (each [B, Hkv, cap, D], shared strides) and kv_len."""
+
+    def __init__(self, k_caches, v_caches, kv_len, max_kv_len_hint):
+        import ctypes
+        k0 = k_caches[0]
+        for t in list(k_caches) + list(v_caches):
+            if t.stride() != k0.stride() or t.shape != k0.shape or t.stride(3) != 1:
+                raise ValueError("all caches must share shape and strides, D contiguous")
+        if kv_len.dtype != torch.int32:
+            raise TypeError("kv_len must be int32")
+        self.k_caches, self.v_caches, self.kv_len = k_caches, v_caches, kv_len
+        self._k = (ctypes.c_void_p * len(k_caches))(*[t.data_ptr() for t in k_caches])
+        self._v = (ctypes.c_void_p * len(v_caches))(*[t.data_ptr() for t in v_caches])
+        self.c = _lib.KvStateC(self._k, self._v, k0.stride(0), k0.stride(1), k0.stride(2), k0.shape[2],
+                               kv_len.data_ptr(), int(max_kv_len_hint))
+
+
+def dual_ar_decode_step(model, kv, prev_codes, codes=None, slow_taps=None, fast_taps=None, logits_tap=None,
+                        workspace=None, err=None):
+    """One batched Dual-AR decode step; returns the frame's codes int32 [B, C]."""
+    import ctypes
+    _require_cuda(prev_codes, slow_taps, fast_taps, logits_tap)
+    B, C = prev_codes.shape
+    if codes is None:
+        codes = torch.empty((B, C), dtype=torch.int32, device=prev_codes.device)
+    if workspace is None:
+        workspace = model.new_workspace(B, kv.c.max_kv_len_hint, prev_codes.device)
+    _lib.check(_lib.load().dual_ar_decode_step(
+        ctypes.byref(model.c), B, prev_codes.data_ptr(), ctypes.byref(kv.c), codes.data_ptr(),
+        _opt_ptr(slow_taps), _opt_ptr(fast_taps), _opt_ptr(logits_tap), workspace.data_ptr(), workspace.numel(),
+        _opt_ptr(err), _stream()))
+    return codes
 
 
 def profile_start(max_records=200000):

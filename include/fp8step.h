@@ -8,7 +8,10 @@
  *         "FP8 Quantization Strategy", "Kernel Benchmark Results",
  *         "What's Open Source".
  *   [KV]  "Fish Speech KV Cache 推理优化记录" (Fish Speech KV-cache
- *         optimisation notes) -- sections 4 and 5.
+ *         optimisation notes) -- sections 2 (the Dual-AR model), 4 and 5.
+ *   [CB]  "How Fish Audio Keeps a GPU Busy: Continuous Batching for Streaming
+ *         Speech" -- section "Where speech makes it harder" (slow AR semantic
+ *         code, fast AR fills in the other nine codebook tokens).
  *
  * General conventions
  *   - Every pointer argument is a DEVICE pointer owned by the caller unless
@@ -35,6 +38,13 @@
 #include <stddef.h>
 #include <stdint.h>
 
+/* Exported entry points (the library is built with hidden visibility). */
+#if defined(__GNUC__)
+#define FP8S_API __attribute__((visibility("default")))
+#else
+#define FP8S_API
+#endif
+
 #ifdef __cplusplus
 extern "C" {
 #endif
@@ -50,7 +60,14 @@ enum fp8s_status {
 /* Device error codes written to err_flag. */
 enum fp8s_device_error {
     FP8S_DEV_KVLEN_RANGE = 1, /* kv_len[b] outside [1, min(cap, hint)]         */
-    FP8S_DEV_WAIT_TIMEOUT = 2 /* a cross-workgroup wait in a fused kernel gave up */
+    FP8S_DEV_WAIT_TIMEOUT = 2,/* a cross-workgroup wait in a fused kernel gave up */
+    FP8S_DEV_CODE_RANGE = 3   /* a codebook index outside [0, codebook_size)   */
+};
+
+/* Output types of qlinear_fp8. */
+enum fp8s_out_dtype {
+    FP8S_OUT_BF16 = 0,
+    FP8S_OUT_F32 = 1
 };
 
 /* Quantisation modes ([TTS] "FP8 Quantization Strategy"). */
@@ -91,7 +108,7 @@ enum fp8s_mlp_mode {
  *   (128 or 32) and, in mode 1, rows a multiple of 128 (else FP8S_EINVAL).
  *   Bit-exact with the CPU oracle.
  */
-int qlinear_quantize(const uint16_t* x, int64_t rows, int64_t cols, int64_t ld_x,
+FP8S_API int qlinear_quantize(const uint16_t* x, int64_t rows, int64_t cols, int64_t ld_x,
                      int mode, uint8_t* q, int64_t ld_q, void* scale,
                      int64_t scale_stride_row, int64_t scale_stride_colblk,
                      void* stream);
@@ -111,8 +128,10 @@ typedef struct fp8s_qweight {
  * swiglu_mlp_fp8 -- y = down( quant( silu(x Wg^T) * (x Wu^T) ) ) at decode
  * shape, with the activation quantisation of x fused into the gate/up GEMM
  * and the SwiGLU fused into the down projection's activation quantisation
- * ([TTS] "Why cuBLAS Wasn't Enough", "Kernel Benchmark Results").  One
- * kernel launch; no bf16 intermediate reaches memory.
+ * ([TTS] "Why cuBLAS Wasn't Enough", "Kernel Benchmark Results").  A chain
+ * of two (M <= 4) to four streaming kernels on `stream`; the gate and up
+ * projections cross memory once in fp32, h = silu(g) * u is never written
+ * in bf16 (only as the e4m3 operand of the down GEMM when M > 4).
  *
  *   x     [M, hidden] bf16, contiguous.  1 <= M <= 128.
  *   gate, up  : W [inter, hidden];  down : W [hidden, inter].
@@ -129,8 +148,8 @@ typedef struct fp8s_qweight {
  *   err_flag  optional device int (see conventions).
  *   Accuracy: fp32 accumulation; max|y - y_oracle| <= 2e-2 * max|y_oracle|.
  */
-size_t swiglu_mlp_fp8_workspace_size(int64_t M, int64_t hidden, int64_t inter, int mode);
-int swiglu_mlp_fp8(const uint16_t* x, int64_t M, int64_t hidden, int64_t inter, int mode,
+FP8S_API size_t swiglu_mlp_fp8_workspace_size(int64_t M, int64_t hidden, int64_t inter, int mode);
+FP8S_API int swiglu_mlp_fp8(const uint16_t* x, int64_t M, int64_t hidden, int64_t inter, int mode,
                    fp8s_qweight gate, fp8s_qweight up, fp8s_qweight down,
                    uint16_t* y, void* workspace, size_t workspace_bytes,
                    int32_t* err_flag, void* stream);
@@ -158,13 +177,153 @@ int swiglu_mlp_fp8(const uint16_t* x, int64_t M, int64_t hidden, int64_t inter, 
  *   Accuracy: fp32 softmax and accumulation; max|out - oracle| <= 5e-3 *
  *   max|oracle|.
  */
-size_t gqa_decode_attn_workspace_size(int64_t B, int32_t Hq, int32_t D, int64_t max_kv_len);
-int gqa_decode_attn(const uint16_t* q, const uint16_t* k_cache, const uint16_t* v_cache,
+FP8S_API size_t gqa_decode_attn_workspace_size(int64_t B, int32_t Hq, int32_t D, int64_t max_kv_len);
+FP8S_API int gqa_decode_attn(const uint16_t* q, const uint16_t* k_cache, const uint16_t* v_cache,
                     int64_t stride_b, int64_t stride_h, int64_t stride_t,
                     const int32_t* kv_len, int64_t B, int32_t Hq, int32_t Hkv, int32_t D,
                     int64_t cap, int64_t max_kv_len_hint, float softmax_scale,
                     uint16_t* out, void* workspace, size_t workspace_bytes,
                     int32_t* err_flag, void* stream);
+
+/*
+ * qlinear_fp8 -- y = [residual +] dequant(quant(norm(x))) . dequant(W)^T, the
+ * FP8 projections of a decode block other than the MLP ([TTS] "FP8
+ * Quantization Strategy", "Kernel Benchmark Results").
+ *
+ *   x        [M, K] bf16, row stride ld_x (multiple of 8); 1 <= M <= 128.
+ *   norm_w   optional bf16 [K] RMSNorm weight: x is first replaced by
+ *            bf16(x / sqrt(mean_k(x^2) + eps) * norm_w) row by row.
+ *   w        W [N, K] e4m3 with 128x128 fp32 block scales (bsgemm).
+ *            K multiple of 128, N multiple of 32.
+ *   The activation is quantised in 1x128 groups (qlinear_quantize mode 0).
+ *   residual optional bf16 [M, N] (row stride ld_res) added before rounding;
+ *            only with out_dtype FP8S_OUT_BF16.
+ *   y        [M, N] out, row stride ld_y: bf16 (FP8S_OUT_BF16) or fp32.
+ *   workspace  at least qlinear_fp8_workspace_size(M, N, K) bytes; its first
+ *            16 KiB are control words: zero-fill once, every call leaves them
+ *            at zero (reusable for any shape it is large enough for).  Calls
+ *            sharing a workspace must not overlap in time.
+ *   Accuracy: fp32 accumulation; max|y - y_oracle| <= 2e-2 * max|y_oracle|.
+ */
+FP8S_API size_t qlinear_fp8_workspace_size(int64_t M, int64_t N, int64_t K);
+FP8S_API int qlinear_fp8(const uint16_t* x, int64_t M, int64_t K, int64_t ld_x,
+                const uint16_t* norm_w, float eps, fp8s_qweight w, int64_t N,
+                const uint16_t* residual, int64_t ld_res, int out_dtype,
+                void* y, int64_t ld_y, void* workspace, size_t workspace_bytes,
+                void* stream);
+
+/*
+ * qkv_proj_kv_append -- the QKV projection of a decode block with the K/V
+ * append fused into its epilogue ([KV] section 5: the full-capacity cache is
+ * updated at the new token's position, then attention reads the prefix).
+ * Computes qkv = dequant(quant(norm(x))) . dequant(W_qkv)^T (as qlinear_fp8)
+ * with output columns [Hq*D query | Hkv*D key | Hkv*D value] (head-major,
+ * D contiguous) and writes, rounded to bf16:
+ *   q_out[m, :]                                   <- query columns ([M, Hq*D])
+ *   k_cache[m*stride_b + g*stride_h + t*stride_t + d] <- key column g*D + d
+ *   v_cache[...same...]                           <- value column g*D + d
+ * with t = kv_len[m] - 1 (kv_len counts the new token).  A kv_len outside
+ * [1, cap] writes nothing to the caches for that row and sets
+ * FP8S_DEV_KVLEN_RANGE in err_flag.  D must be 64 or 128, Hq a multiple of
+ * Hkv.  workspace: qlinear_fp8_workspace_size(M, (Hq + 2*Hkv)*D, K).
+ */
+FP8S_API int qkv_proj_kv_append(const uint16_t* x, int64_t M, int64_t K, int64_t ld_x,
+                       const uint16_t* norm_w, float eps, fp8s_qweight w_qkv,
+                       int32_t Hq, int32_t Hkv, int32_t D, uint16_t* q_out,
+                       uint16_t* k_cache, uint16_t* v_cache,
+                       int64_t stride_b, int64_t stride_h, int64_t stride_t,
+                       const int32_t* kv_len, int64_t cap,
+                       void* workspace, size_t workspace_bytes,
+                       int32_t* err_flag, void* stream);
+
+/*
+ * embed_sum_bf16 -- out[b, :] = bf16( add[b, :] + sum_{c < n_tables}
+ * tables[c][codes[b * ld_codes + c], :] ), summed in fp32 in table order: the
+ * input of a Dual-AR step is the embedding of the previous frame's codes
+ * ([KV] section 2: a frame's tokens become the next step's context).
+ *   tables   HOST array of n_tables (1..16) device pointers, bf16 [V, H].
+ *   codes    device int32, row stride ld_codes.
+ *   add      optional bf16 [B, H] (row stride H).   out  bf16 [B, H].
+ *   H must be a multiple of 8.  A code outside [0, V) contributes nothing and
+ *   sets FP8S_DEV_CODE_RANGE in err_flag.
+ */
+FP8S_API int embed_sum_bf16(const uint16_t* const* tables, int32_t n_tables, int64_t V, int64_t H,
+                   const int32_t* codes, int64_t ld_codes, int64_t B, const uint16_t* add,
+                   uint16_t* out, int32_t* err_flag, void* stream);
+
+/*
+ * argmax_rows_f32 -- codes[b * ld_codes] = argmax_n logits[b * ld_logits + n]
+ * over n < N (greedy decoding of a codebook head); ties go to the lowest
+ * index, NaN entries are never chosen (all-NaN rows give 0).  Bit-exact.
+ */
+FP8S_API int argmax_rows_f32(const float* logits, int64_t B, int64_t N, int64_t ld_logits,
+                    int32_t* codes, int64_t ld_codes, void* stream);
+
+/*
+ * The full batched Dual-AR decode step ([KV] section 2, [CB], [TTS]).
+ *
+ * Slow AR: x = embed_sum(E, prev_codes); for each slow layer (pre-norm block)
+ *   x = x + O( attn( qkv_proj_kv_append( RMSNorm_attn(x) ) ) )
+ *   x = x + MLP( RMSNorm_mlp(x) )             (bsgemm SwiGLU MLP)
+ * h = RMSNorm_slow(x); code 0 = argmax(head_0 . h).
+ * Fast AR (its own layers and a cache of n_codebooks - 1 slots in the
+ * workspace): micro-step p = 0 .. C-2 takes z = bf16(h + E_0[code_0]) for
+ * p = 0 and z = E_p[code_p] after that, runs the fast layers with
+ * kv_len = p + 1, and sets code p+1 = argmax(head_{p+1} . RMSNorm_fast(z)).
+ * No rotary embedding; softmax scale 1/sqrt(D); all activations bf16, every
+ * projection an FP8 bsgemm GEMM (128x128 weight blocks, 1x128 activation
+ * groups).
+ */
+typedef struct fp8s_block_weights {
+    fp8s_qweight qkv;             /* [(Hq + 2*Hkv)*D, hidden]              */
+    fp8s_qweight o;               /* [hidden, Hq*D]                         */
+    fp8s_qweight gate, up;        /* [inter, hidden]                        */
+    fp8s_qweight down;            /* [hidden, inter]                        */
+    const uint16_t* norm_attn;    /* bf16 [hidden]                          */
+    const uint16_t* norm_mlp;     /* bf16 [hidden]                          */
+} fp8s_block_weights;
+
+typedef struct fp8s_dual_ar_model {
+    int64_t hidden, inter, codebook_size;
+    int32_t n_heads, n_kv_heads, head_dim;
+    int32_t n_codebooks;                 /* C, 2..16                         */
+    int32_t n_slow_layers, n_fast_layers;
+    float rms_eps;
+    const fp8s_block_weights* slow;      /* HOST array [n_slow_layers]      */
+    const fp8s_block_weights* fast;      /* HOST array [n_fast_layers]      */
+    const uint16_t* slow_norm;           /* bf16 [hidden]                    */
+    const uint16_t* fast_norm;           /* bf16 [hidden]                    */
+    const uint16_t* const* embed;        /* HOST array [C] of bf16 [V, hidden] */
+    const fp8s_qweight* heads;           /* HOST array [C] of [V, hidden]    */
+} fp8s_dual_ar_model;
+
+typedef struct fp8s_kv_state {
+    uint16_t* const* k_cache;            /* HOST array [n_slow_layers] of   */
+    uint16_t* const* v_cache;            /*   device bf16 caches (strides)  */
+    int64_t stride_b, stride_h, stride_t, cap;
+    const int32_t* kv_len;               /* device [B], counts this token    */
+    int64_t max_kv_len_hint;             /* host bound of kv_len             */
+} fp8s_kv_state;
+
+/*
+ *   prev_codes  device int32 [B, C]; codes  device int32 [B, C] out.
+ *   slow_taps   optional bf16 [n_slow_layers + 1][B][hidden]: the input of
+ *               each slow layer and, last, the output of the last one.
+ *   fast_taps   optional bf16 [C - 1][n_fast_layers + 1][B][hidden]: per
+ *               micro-step, the input of each fast layer and the output.
+ *   logits_tap  optional fp32 [C][B][codebook_size]: every head's logits.
+ *   workspace   dual_ar_decode_step_workspace_size(model, B, hint) bytes,
+ *               zero-filled once before first use (control words).
+ *   err_flag    kv_len or code range errors (see above).
+ *   Constraints: 1 <= B <= 128; hidden, inter, Hq*D multiples of 128;
+ *   codebook_size a multiple of 32; D 64 or 128.
+ */
+FP8S_API size_t dual_ar_decode_step_workspace_size(const fp8s_dual_ar_model* model, int64_t B,
+                                          int64_t max_kv_len_hint);
+FP8S_API int dual_ar_decode_step(const fp8s_dual_ar_model* model, int64_t B, const int32_t* prev_codes,
+                        const fp8s_kv_state* kv, int32_t* codes, uint16_t* slow_taps,
+                        uint16_t* fast_taps, float* logits_tap, void* workspace,
+                        size_t workspace_bytes, int32_t* err_flag, void* stream);
 
 /*
  * Per-kernel timing, for benchmarks and tracing.  Between fp8s_profile_start
@@ -180,12 +339,12 @@ int gqa_decode_attn(const uint16_t* q, const uint16_t* k_cache, const uint16_t* 
  * for single-threaded benchmark drivers.  Do not record while a stream is
  * being captured into a graph.
  */
-int fp8s_profile_start(int max_records);
-int fp8s_profile_stop(void);
-int fp8s_profile_record(int i, char* name, int name_len, float* ms);
+FP8S_API int fp8s_profile_start(int max_records);
+FP8S_API int fp8s_profile_stop(void);
+FP8S_API int fp8s_profile_record(int i, char* name, int name_len, float* ms);
 
 /* Message for the last non-OK return on the calling thread ("" if none). */
-const char* fp8s_last_error(void);
+FP8S_API const char* fp8s_last_error(void);
 
 #ifdef __cplusplus
 }

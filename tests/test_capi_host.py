@@ -96,3 +96,86 @@ def test_attention_argument_checks():
 def test_mlp_workspace_is_small(M, H, I):
     n = _lib.load().swiglu_mlp_fp8_workspace_size(M, H, I, 0)
     assert 0 < n < 32 * 2 ** 20
+
+
+def test_qlinear_argument_checks():
+    lib = _lib.load()
+    ws = lib.qlinear_fp8_workspace_size(64, 6144, 2560)
+    assert ws > 0
+    assert lib.qlinear_fp8_workspace_size(129, 6144, 2560) == 0
+    assert lib.qlinear_fp8_workspace_size(64, 6100, 2560) == 0
+    assert lib.qlinear_fp8_workspace_size(64, 6144, 2500) == 0
+    w = _lib.QWeightC(FAKE, 2560, FAKE, 20, 1)
+    call = lambda M, K, N, out, wsb, res=None, norm=None, ldx=2560: lib.qlinear_fp8(
+        FAKE, M, K, ldx, norm, ctypes.c_float(1e-6), w, N, res, N, out, FAKE, N, FAKE, wsb, None)
+    assert call(0, 2560, 6144, 0, ws) == EINVAL
+    assert call(129, 2560, 6144, 0, ws) == EUNSUPPORTED
+    assert call(64, 2500, 6144, 0, ws) == EINVAL              # K % 128
+    assert call(64, 2560, 6100, 0, ws) == EINVAL              # N % 32
+    assert call(64, 2560, 6144, 2, ws) == EINVAL              # out dtype
+    assert call(64, 2560, 6144, 1, ws, res=FAKE) == EINVAL    # residual needs bf16 output
+    assert call(64, 2560, 6144, 0, ws, norm=FAKE + 2) == EINVAL
+    assert call(64, 2560, 6144, 0, ws, ldx=2564) == EINVAL    # ld_x % 8
+    assert call(64, 2560, 6144, 0, ws - 1) == EWORKSPACE
+
+
+def test_qkv_append_argument_checks():
+    lib = _lib.load()
+    w = _lib.QWeightC(FAKE, 2560, FAKE, 20, 1)
+    ws = lib.qlinear_fp8_workspace_size(64, 6144, 2560)
+    call = lambda Hq, Hkv, D, kvl=FAKE, cap=32768: lib.qkv_proj_kv_append(
+        FAKE, 64, 2560, 2560, None, ctypes.c_float(1e-6), w, Hq, Hkv, D, FAKE, FAKE, FAKE,
+        8 * 32768 * 128, 32768 * 128, 128, kvl, cap, FAKE, ws, None, None)
+    assert call(32, 6, 128) == EINVAL                         # Hq % Hkv
+    assert call(32, 8, 96) == EUNSUPPORTED                    # head dim
+    assert call(32, 8, 128, kvl=None) == EINVAL
+    assert call(32, 8, 128, cap=0) == EINVAL
+    assert call(64, 16, 128) == EWORKSPACE                    # N = 12288 needs a larger workspace
+
+
+def test_embed_and_argmax_argument_checks():
+    lib = _lib.load()
+    tabs = (ctypes.c_void_p * 2)(FAKE, FAKE)
+    assert lib.embed_sum_bf16(tabs, 0, 4096, 2560, FAKE, 10, 64, None, FAKE, None, None) == EUNSUPPORTED
+    assert lib.embed_sum_bf16(tabs, 17, 4096, 2560, FAKE, 17, 64, None, FAKE, None, None) == EUNSUPPORTED
+    assert lib.embed_sum_bf16(tabs, 2, 4096, 2564, FAKE, 10, 64, None, FAKE, None, None) == EINVAL
+    assert lib.embed_sum_bf16(tabs, 2, 4096, 2560, FAKE, 1, 64, None, FAKE, None, None) == EINVAL
+    assert lib.embed_sum_bf16(tabs, 2, 4096, 2560, None, 10, 64, None, FAKE, None, None) == EINVAL
+    assert lib.argmax_rows_f32(FAKE, 64, 4096, 4000, FAKE, 10, None) == EINVAL
+    assert lib.argmax_rows_f32(None, 64, 4096, 4096, FAKE, 10, None) == EINVAL
+
+
+def _model(**kw):
+    f = dict(hidden=2560, inter=9728, codebook_size=4096, n_heads=32, n_kv_heads=8, head_dim=128,
+             n_codebooks=10, n_slow_layers=2, n_fast_layers=1, rms_eps=1e-6)
+    f.update(kw)
+    blk = _lib.BlockWeightsC(_qw(), _qw(), _qw(), _qw(), _qw(), FAKE, FAKE)
+    slow = (_lib.BlockWeightsC * 2)(blk, blk)
+    fast = (_lib.BlockWeightsC * 1)(blk)
+    emb = (ctypes.c_void_p * 16)(*([FAKE] * 16))
+    heads = (_lib.QWeightC * 16)(*([_qw()] * 16))
+    m = _lib.DualArModelC(f["hidden"], f["inter"], f["codebook_size"], f["n_heads"], f["n_kv_heads"],
+                          f["head_dim"], f["n_codebooks"], f["n_slow_layers"], f["n_fast_layers"],
+                          f["rms_eps"], slow, fast, FAKE, FAKE, emb, heads)
+    m._keep = (slow, fast, emb, heads)
+    return m
+
+
+def test_dual_ar_step_argument_checks():
+    lib = _lib.load()
+    m = _model()
+    ws = lib.dual_ar_decode_step_workspace_size(ctypes.byref(m), 64, 4096)
+    assert ws > 0
+    assert lib.dual_ar_decode_step_workspace_size(ctypes.byref(m), 129, 4096) == 0
+    for bad in (dict(n_codebooks=1), dict(n_codebooks=17), dict(head_dim=96), dict(codebook_size=4004),
+                dict(n_kv_heads=6), dict(hidden=2500)):
+        assert lib.dual_ar_decode_step_workspace_size(ctypes.byref(_model(**bad)), 64, 4096) == 0, bad
+    caches = (ctypes.c_void_p * 2)(FAKE, FAKE)
+    kv = _lib.KvStateC(caches, caches, 8 * 32768 * 128, 32768 * 128, 128, 32768, FAKE, 4096)
+    call = lambda mm, B, wsb, prev=FAKE: lib.dual_ar_decode_step(
+        ctypes.byref(mm), B, prev, ctypes.byref(kv), FAKE, None, None, None, FAKE, wsb, None, None)
+    assert call(m, 0, ws) == EUNSUPPORTED
+    assert call(m, 64, ws, prev=None) == EINVAL
+    assert call(_model(n_codebooks=1), 64, ws) == EUNSUPPORTED
+    assert call(m, 64, ws - 1) == EWORKSPACE
+    assert "workspace" in lib.fp8s_last_error().decode()

@@ -1,0 +1,168 @@
+"""The full Dual-AR decode step on the GPU against the oracle, teacher forced:
+every layer's (and every micro-step's) output is compared with the oracle
+applied to the GPU's own input of that layer, so FP8 re-quantisation flips
+and argmax near-ties cannot compound.  The codes must be the exact argmax of
+the GPU's logits, and those logits must match the oracle's.
+
+A small model with the same structure is checked on every layer, row and
+micro-step; the full model (36 slow layers, 4 fast layers, batch 64, caches
+of 32768 slots, kv_len up to 4096) on sampled layers and rows."""
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from fp8_transformer_step_amd import model, ops
+from _helpers import TOL_FP8_PATH, f32, log, max_rel_err, need_gpu
+
+pytestmark = pytest.mark.gpu
+
+
+def _np(t):
+    return t.float().cpu().numpy().astype(np.float64)
+
+
+def _oracle_block(d):
+    p = {k: oracle.dequant_weight(f32(d[k]))[2] for k in ("qkv", "o", "gate", "up", "down")}
+    p["norm_attn"] = f32(d["norm_attn"]).astype(np.float64)
+    p["norm_mlp"] = f32(d["norm_mlp"]).astype(np.float64)
+    return p
+
+
+def _prefix_cache(host, s, rows):
+    """The oracle's copy of physical set s for the given rows (initial content)."""
+    c = host.cfg
+    Lmax = int(max(host.kv_len[b] for b in rows))
+    k = np.zeros((len(rows), c.n_kv_heads, Lmax, c.head_dim), np.float32)
+    v = np.zeros_like(k)
+    for i, b in enumerate(rows):
+        kp, vp = host.kv_prefix(s, b)
+        k[i, :, :kp.shape[1]] = f32(kp)
+        v[i, :, :vp.shape[1]] = f32(vp)
+    return k, v
+
+
+def _ulp_close(got, want):
+    ulp = np.ldexp(1.0, np.frexp(np.maximum(np.abs(want), 1e-30))[1] - 8)
+    return bool(np.all(np.abs(got - want) <= ulp))
+
+
+def _run_step(host):
+    c = host.cfg
+    dm = model.device_model(host)
+    kv, ks, vs = model.device_kv(host)
+    k0 = [k.clone() for k in ks]
+    v0 = [v.clone() for v in vs]
+    B, H, C, V = c.batch, c.hidden, c.n_codebooks, c.codebook_size
+    slow_taps = torch.empty((c.n_slow_layers + 1, B, H), dtype=torch.bfloat16, device="cuda")
+    fast_taps = torch.empty((C - 1, c.n_fast_layers + 1, B, H), dtype=torch.bfloat16, device="cuda")
+    logits = torch.empty((C, B, V), dtype=torch.float32, device="cuda")
+    err = torch.zeros(1, dtype=torch.int32, device="cuda")
+    log(f"dual-AR step B={B} L={c.n_slow_layers} F={c.n_fast_layers} H={H} V={V}")
+    codes = ops.dual_ar_decode_step(dm, kv, torch.from_numpy(host.prev_codes).cuda(), slow_taps=slow_taps,
+                                    fast_taps=fast_taps, logits_tap=logits, err=err)
+    torch.cuda.synchronize()
+    assert int(err.item()) == 0
+    out = {"codes": codes.cpu().numpy(), "slow": _np(slow_taps), "fast": _np(fast_taps),
+           "logits": logits.cpu().numpy().astype(np.float64), "ks": ks, "vs": vs, "k0": k0, "v0": v0}
+    # the codes are the exact greedy decisions on the GPU's logits
+    np.testing.assert_array_equal(out["codes"], np.argmax(out["logits"], axis=2).T)
+    # a second call on the same inputs gives the same codes (deterministic reductions)
+    codes2 = ops.dual_ar_decode_step(dm, kv, torch.from_numpy(host.prev_codes).cuda())
+    torch.cuda.synchronize()
+    np.testing.assert_array_equal(codes2.cpu().numpy(), out["codes"])
+    return out
+
+
+def test_small_model_every_layer_teacher_forced():
+    need_gpu()
+    host = model.HostModel(model.TINY)
+    c = host.cfg
+    g = _run_step(host)
+    C, F, L = c.n_codebooks, c.n_fast_layers, c.n_slow_layers
+    om = {"slow": [_oracle_block(d) for d in host.slow], "fast": [_oracle_block(d) for d in host.fast],
+          "slow_norm": f32(host.slow_norm).astype(np.float64), "fast_norm": f32(host.fast_norm).astype(np.float64),
+          "embed": [f32(t) for t in host.embed], "heads": [oracle.dequant_weight(f32(h))[2] for h in host.heads],
+          "n_heads": c.n_heads, "n_kv_heads": c.n_kv_heads, "head_dim": c.head_dim, "eps": c.rms_eps}
+    rows = list(range(c.batch))
+    caches = [_prefix_cache(host, l % c.kv_sets, rows) for l in range(L)]
+    force = {"slow_x": list(g["slow"]), "codes": g["codes"], "fast_x": [list(g["fast"][p]) for p in range(C - 1)]}
+    r = oracle.dual_ar_step(om, host.prev_codes, [k for k, _ in caches], [v for _, v in caches], host.kv_len,
+                            force=force)
+    assert _ulp_close(g["slow"][0], r["slow_x"][0])
+    for l in range(L):
+        e = max_rel_err(g["slow"][l + 1], r["slow_x"][l + 1])
+        log(f"  slow layer {l}: {e:.3e}")
+        assert e <= TOL_FP8_PATH
+    for cb in range(C):
+        e = max_rel_err(g["logits"][cb], r["logits"][cb])
+        log(f"  head {cb}: {e:.3e}, codes equal to the oracle's argmax: "
+            f"{np.mean(g['codes'][:, cb] == r['codes'][:, cb]):.2f}")
+        assert e <= TOL_FP8_PATH
+    for p in range(C - 1):
+        assert max_rel_err(g["fast"][p][0], r["fast_x"][p][0]) <= 2 ** -7
+        for f in range(F):
+            e = max_rel_err(g["fast"][p][f + 1], r["fast_x"][p][f + 1])
+            assert e <= TOL_FP8_PATH, (p, f, e)
+    # caches: the last layer on each set left its K/V at kv_len - 1, nothing else changed
+    for s in range(c.kv_sets):
+        last = max(l for l in range(L) if l % c.kv_sets == s)
+        kk, vv = r["slow_kv"][last]
+        kg, vg = g["ks"][s], g["vs"][s]
+        for b in rows:
+            t = int(host.kv_len[b]) - 1
+            assert max_rel_err(_np(kg[b, :, t]), kk[b]) <= TOL_FP8_PATH
+            assert max_rel_err(_np(vg[b, :, t]), vv[b]) <= TOL_FP8_PATH
+            keep = torch.arange(c.cap, device="cuda") != t
+            assert torch.equal(kg[b][:, keep].view(torch.int16), g["k0"][s][b][:, keep].view(torch.int16))
+            assert torch.equal(vg[b][:, keep].view(torch.int16), g["v0"][s][b][:, keep].view(torch.int16))
+
+
+@pytest.mark.timeout(900)
+def test_full_model_sampled_layers_teacher_forced():
+    need_gpu()
+    host = model.HostModel(model.FULL)
+    c = host.cfg
+    g = _run_step(host)
+    C, F, L = c.n_codebooks, c.n_fast_layers, c.n_slow_layers
+    rows = sorted({0, 13, 29, 47, c.batch - 1, int(np.argmax(host.kv_len)), int(np.argmin(host.kv_len))})
+    log(f"  sampled rows {rows}, kv_len {[int(host.kv_len[b]) for b in rows]}")
+    D = c.head_dim
+    for l in (0, 17, L - 1):
+        p = _oracle_block(host.slow[l])
+        k, v = _prefix_cache(host, l % c.kv_sets, rows)
+        out, it = oracle.decoder_layer(g["slow"][l][rows], p, k, v, host.kv_len[rows], c.n_heads, c.n_kv_heads, D,
+                                       c.rms_eps)
+        e = max_rel_err(g["slow"][l + 1][rows], out)
+        log(f"  slow layer {l}: {e:.3e}")
+        assert e <= TOL_FP8_PATH
+        if l == L - 1:           # the last layer on its set: its K/V row is what the cache holds now
+            s = l % c.kv_sets
+            for i, b in enumerate(rows):
+                t = int(host.kv_len[b]) - 1
+                assert max_rel_err(_np(g["ks"][s][b, :, t]), it["k"][i]) <= TOL_FP8_PATH
+                assert max_rel_err(_np(g["vs"][s][b, :, t]), it["v"][i]) <= TOL_FP8_PATH
+    heads = [oracle.dequant_weight(f32(h))[2] for h in host.heads]
+    h = oracle.rmsnorm(g["slow"][L][rows], f32(host.slow_norm))
+    lg, _ = oracle.greedy_code(h, heads[0])
+    e = max_rel_err(g["logits"][0][rows], lg)
+    log(f"  head 0: {e:.3e}")
+    assert e <= TOL_FP8_PATH
+    fast = [_oracle_block(d) for d in host.fast]
+    fk = [np.zeros((len(rows), c.n_kv_heads, C - 1, D)) for _ in range(F)]
+    fv = [np.zeros((len(rows), c.n_kv_heads, C - 1, D)) for _ in range(F)]
+    for p in range(C - 1):
+        z = oracle.embed_sum([f32(host.embed[p])], g["codes"][rows, p:p + 1], add=h if p == 0 else None)
+        assert max_rel_err(g["fast"][p][0][rows], z) <= 2 ** -7
+        steps = np.full(len(rows), p + 1)
+        for f in range(F):
+            out, _ = oracle.decoder_layer(g["fast"][p][f][rows], fast[f], fk[f], fv[f], steps, c.n_heads,
+                                          c.n_kv_heads, D, c.rms_eps)
+            e = max_rel_err(g["fast"][p][f + 1][rows], out)
+            assert e <= TOL_FP8_PATH, (p, f, e)
+        zn = oracle.rmsnorm(g["fast"][p][F][rows], f32(host.fast_norm))
+        lg, _ = oracle.greedy_code(zn, heads[p + 1])
+        e = max_rel_err(g["logits"][p + 1][rows], lg)
+        log(f"  micro-step {p}: head {p + 1} {e:.3e}")
+        assert e <= TOL_FP8_PATH

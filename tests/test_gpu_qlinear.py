@@ -1,0 +1,202 @@
+"""The block's other FP8 projections and the codebook glue on the GPU against
+the oracle: qlinear_fp8 (plain, RMSNorm in front, residual, fp32 logits) at
+the Qwen3-4B projection shapes and ragged small ones, an exact small-integer
+case with the scale-stride contract, the QKV projection with its K/V append,
+the embedding sum and the greedy argmax."""
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from fp8_transformer_step_amd import inputs, ops
+from _helpers import TOL_FP8_PATH, f32, from_dev_bf16, log, max_rel_err, need_gpu, to_dev_bf16
+
+pytestmark = pytest.mark.gpu
+W = inputs.W_STEP
+
+
+def _weight(bits):
+    """GPU-quantised weight and the oracle's own dequantised copy (the bytes
+    and scales are checked equal first)."""
+    qw = ops.quantize_weight(to_dev_bf16(bits), ops.MLP_BSGEMM)
+    q, s, d = oracle.dequant_weight(f32(bits))
+    torch.cuda.synchronize()
+    assert np.array_equal(qw.w.cpu().numpy(), q)
+    assert np.array_equal(qw.scale.cpu().numpy(), s)
+    return qw, d
+
+
+@pytest.mark.parametrize("M,N,K,norm,res,out", [
+    (1, 6144, 2560, True, False, ops.OUT_BF16),       # QKV shape
+    (64, 6144, 2560, True, False, ops.OUT_BF16),
+    (64, 2560, 4096, False, True, ops.OUT_BF16),      # output projection + residual
+    (128, 2560, 4096, False, True, ops.OUT_BF16),
+    (64, 4096, 2560, True, False, ops.OUT_F32),       # codebook head, fp32 logits
+    (5, 128, 384, True, True, ops.OUT_BF16),          # ragged M, small N and K
+    (37, 384, 640, False, False, ops.OUT_F32),
+    (17, 128, 128, True, False, ops.OUT_F32),
+])
+def test_qlinear_matches_oracle(M, N, K, norm, res, out):
+    need_gpu()
+    e = 7 * M + N + K
+    log(f"qlinear M={M} N={N} K={K} norm={norm} res={res} out={out}")
+    xb = inputs.normal_bf16(W, inputs.T_X, (M, K), 1.0, extra=e)
+    qw, d = _weight(inputs.normal_bf16(W, inputs.T_WO, (N, K), 0.02, extra=e))
+    nw = inputs.norm_weight(W, e, K) if norm else None
+    rb = inputs.normal_bf16(W, inputs.T_V, (M, N), 1.0, extra=e) if res else None
+    y = ops.qlinear_fp8(to_dev_bf16(xb), qw, norm_w=to_dev_bf16(nw) if norm else None,
+                        residual=to_dev_bf16(rb) if res else None, out_dtype=out)
+    torch.cuda.synchronize()
+    x = f32(xb).astype(np.float64)
+    if norm:
+        x = oracle.rmsnorm(x, f32(nw))
+    ref = oracle.fp8_linear(x, d)
+    if res:
+        ref = ref + f32(rb)
+    got = from_dev_bf16(y) if out == ops.OUT_BF16 else y.cpu().numpy().astype(np.float64)
+    err = max_rel_err(got, ref)
+    log(f"  max rel err {err:.3e}")
+    assert err <= TOL_FP8_PATH
+
+
+def _exact_operands(M, N, K, rs):
+    """Small integers with one 448 per group: every scale is a power of two
+    and every fp32 partial sum is exact."""
+    x = rs.integers(-8, 9, (M, K)).astype(np.float32)
+    x[:, 5::128] = 448.0                                   # s_x = 1 for every 1x128 group
+    w = rs.integers(-8, 9, (N, K)).astype(np.float32)
+    for nb in range(N // 128):
+        for kb in range(K // 128):
+            k = (nb + 2 * kb) % 3 - 1                       # s_w = 2^k, not symmetric in (nb, kb)
+            blk = w[nb * 128:(nb + 1) * 128, kb * 128:(kb + 1) * 128]
+            blk[0, 77] = 448.0
+            blk *= np.float32(2.0 ** k)
+    return x, w
+
+
+def test_qlinear_exact_small_integers_and_scale_strides():
+    need_gpu()
+    rs = np.random.default_rng(11)
+    M, N, K = 16, 512, 512
+    x, w = _exact_operands(M, N, K, rs)
+    xb, wb = inputs.f32_to_bf16_bits(x), inputs.f32_to_bf16_bits(w)
+    qw, d = _weight(wb)
+    ref = oracle.fp8_linear(f32(xb), d)
+    y = ops.qlinear_fp8(to_dev_bf16(xb), qw, out_dtype=ops.OUT_F32)
+    torch.cuda.synchronize()
+    np.testing.assert_array_equal(y.cpu().numpy().astype(np.float64), ref)
+    # the same scales read through swapped strides give a large error
+    swapped = ops.QWeight(qw.w, qw.scale.t())
+    y2 = ops.qlinear_fp8(to_dev_bf16(xb), swapped, out_dtype=ops.OUT_F32)
+    torch.cuda.synchronize()
+    assert max_rel_err(y2.cpu().numpy(), ref) > 0.2
+
+
+def _qkv_case(layout, kv_len, Hq=4, Hkv=2, D=64, H=256, cap=64, seed=0):
+    B = len(kv_len)
+    xb = inputs.normal_bf16(W, inputs.T_X, (B, H), 1.0, extra=500 + seed)
+    wb = inputs.normal_bf16(W, inputs.T_WQKV, ((Hq + 2 * Hkv) * D, H), 0.02, extra=500 + seed)
+    nw = inputs.norm_weight(W, 500 + seed, H)
+    qw, d = _weight(wb)
+    g = torch.Generator(device="cuda")
+    g.manual_seed(seed)
+    if layout == "bhtd":
+        shape = (B, Hkv, cap, D)
+    else:                                                     # [B, cap, Hkv, D] storage
+        shape = (B, cap, Hkv, D)
+    kc = torch.randint(-32768, 32768, shape, dtype=torch.int16, device="cuda", generator=g).view(torch.bfloat16)
+    vc = torch.randint(-32768, 32768, shape, dtype=torch.int16, device="cuda", generator=g).view(torch.bfloat16)
+    if layout != "bhtd":
+        kc, vc = kc.permute(0, 2, 1, 3), vc.permute(0, 2, 1, 3)
+    k0, v0 = kc.clone(), vc.clone()
+    kvl = torch.tensor(kv_len, dtype=torch.int32, device="cuda")
+    err = torch.zeros(1, dtype=torch.int32, device="cuda")
+    q = ops.qkv_proj_kv_append(to_dev_bf16(xb), qw, Hq, Hkv, D, kc, vc, kvl, norm_w=to_dev_bf16(nw), err=err)
+    torch.cuda.synchronize()
+    ref = oracle.fp8_linear(oracle.rmsnorm(f32(xb).astype(np.float64), f32(nw)), d)
+    return q, kc, vc, k0, v0, ref, int(err.item())
+
+
+@pytest.mark.parametrize("layout", ["bhtd", "bthd"])
+def test_qkv_append_writes_the_new_rows_only(layout):
+    need_gpu()
+    Hq, Hkv, D = 4, 2, 64
+    kv_len = [1, 17, 64, 33, 2]
+    log(f"qkv append layout={layout}")
+    q, kc, vc, k0, v0, ref, err = _qkv_case(layout, kv_len)
+    assert err == 0
+    assert max_rel_err(from_dev_bf16(q), ref[:, :Hq * D]) <= TOL_FP8_PATH
+    kref = ref[:, Hq * D:(Hq + Hkv) * D].reshape(-1, Hkv, D)
+    vref = ref[:, (Hq + Hkv) * D:].reshape(-1, Hkv, D)
+    kb = kc.view(torch.int16).cpu().numpy()
+    vb = vc.view(torch.int16).cpu().numpy()
+    k0b = k0.view(torch.int16).cpu().numpy()
+    v0b = v0.view(torch.int16).cpu().numpy()
+    for b, L in enumerate(kv_len):
+        t = L - 1
+        got_k = from_dev_bf16(kc[b, :, t])
+        got_v = from_dev_bf16(vc[b, :, t])
+        assert max_rel_err(got_k, kref[b]) <= TOL_FP8_PATH
+        assert max_rel_err(got_v, vref[b]) <= TOL_FP8_PATH
+        keep = np.arange(kb.shape[2]) != t
+        assert np.array_equal(kb[b][:, keep], k0b[b][:, keep])
+        assert np.array_equal(vb[b][:, keep], v0b[b][:, keep])
+
+
+def test_qkv_append_out_of_range_sets_the_flag_and_writes_nothing():
+    need_gpu()
+    q, kc, vc, k0, v0, ref, err = _qkv_case("bhtd", [0, 65, 3], seed=1)
+    assert err == ops.DEV_KVLEN_RANGE
+    assert torch.equal(kc[:2].view(torch.int16), k0[:2].view(torch.int16))
+    assert torch.equal(vc[:2].view(torch.int16), v0[:2].view(torch.int16))
+    assert max_rel_err(from_dev_bf16(q), ref[:, :256]) <= TOL_FP8_PATH
+
+
+def test_embed_sum_matches_oracle():
+    need_gpu()
+    C, V, H, B = 10, 512, 384, 7
+    tabs = [inputs.normal_bf16(W, inputs.T_EMB, (V, H), 0.02, extra=c) for c in range(C)]
+    codes = inputs.prev_codes(W, B, C, V)
+    add = inputs.normal_bf16(W, inputs.T_X, (B, H), 1.0, extra=77)
+    dev_tabs = [to_dev_bf16(t) for t in tabs]
+    err = torch.zeros(1, dtype=torch.int32, device="cuda")
+    dcodes = torch.from_numpy(codes).cuda()
+    out = ops.embed_sum(dev_tabs, dcodes, err=err)
+    out_add = ops.embed_sum(dev_tabs[:1], dcodes, add=to_dev_bf16(add), err=err)
+    torch.cuda.synchronize()
+    assert int(err.item()) == 0
+    ref = oracle.embed_sum([f32(t) for t in tabs], codes)
+    ref_add = oracle.embed_sum([f32(tabs[0])], codes[:, :1], add=f32(add))
+    for got, want in ((from_dev_bf16(out), ref), (from_dev_bf16(out_add), ref_add)):
+        ulp = np.ldexp(1.0, np.frexp(np.maximum(np.abs(want), 1e-30))[1] - 8)
+        assert np.all(np.abs(got - want) <= ulp)             # at most one bf16 step (fp32 summation)
+        assert np.mean(got == want) > 0.999
+    # a code out of range contributes nothing and raises the flag
+    bad = codes.copy()
+    bad[2, 4] = V
+    out_bad = ops.embed_sum(dev_tabs, torch.from_numpy(bad).cuda(), err=err)
+    torch.cuda.synchronize()
+    assert int(err.item()) == ops.DEV_CODE_RANGE
+    keep = [c for c in range(C) if c != 4]
+    want = oracle.embed_sum([f32(tabs[c]) for c in keep], codes[2:3, keep])
+    assert np.abs(from_dev_bf16(out_bad[2:3]) - want).max() <= np.abs(want).max() * 2 ** -7
+
+
+def test_argmax_is_exact_with_ties_nan_and_inf():
+    need_gpu()
+    rs = np.random.default_rng(12)
+    B, N = 9, 4096
+    lg = rs.standard_normal((B, N)).astype(np.float32)
+    lg[1, [100, 3000]] = 50.0                       # tie -> lowest index
+    lg[2, rs.integers(0, N, 40)] = np.nan
+    lg[2, 999] = 20.0
+    lg[3, :] = -np.inf
+    lg[4, :] = np.nan
+    lg[5, N - 1] = 30.0
+    lg[6, :] = 1.5                                   # all equal -> 0
+    lg[7, ::2] = np.nan
+    want = np.argmax(np.where(np.isnan(lg), -np.inf, lg), axis=1)
+    codes = ops.argmax_rows(torch.from_numpy(lg).cuda())
+    torch.cuda.synchronize()
+    np.testing.assert_array_equal(codes[:, 0].cpu().numpy(), want)
