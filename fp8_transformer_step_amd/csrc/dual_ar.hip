@@ -235,15 +235,15 @@ struct StepCtx {
     void* stream;
 };
 
-// One pre-norm block: xout = x + O(attn(qkv(norm(x)))), then += MLP(norm(.)).
-static int run_block(const StepCtx& c, const fp8s_block_weights& L, const uint16_t* xin, uint16_t* xout,
-                     uint16_t* kc, uint16_t* vc, int64_t sb, int64_t sh, int64_t stt, int64_t cap,
+// One pre-norm block: xmid = x + O(attn(qkv(norm(x)))), xout = xmid +
+// MLP(norm(xmid)).
+static int run_block(const StepCtx& c, const fp8s_block_weights& L, const uint16_t* xin, uint16_t* xmid,
+                     uint16_t* xout, uint16_t* kc, uint16_t* vc, int64_t sb, int64_t sh, int64_t stt, int64_t cap,
                      const int32_t* kv_len, int64_t hint) {
     const fp8s_dual_ar_model* m = c.m;
     const int64_t H = m->hidden, A = (int64_t)m->n_heads * m->head_dim;
     uint16_t* q = reinterpret_cast<uint16_t*>(c.ws + c.p->off_q);
     uint16_t* ao = reinterpret_cast<uint16_t*>(c.ws + c.p->off_ao);
-    uint16_t* xmid = reinterpret_cast<uint16_t*>(c.ws + c.p->off_xmid);
     void* qlw = c.ws + c.p->off_ql;
     int rc = qkv_proj_kv_append(xin, c.B, H, H, L.norm_attn, m->rms_eps, L.qkv, m->n_heads, m->n_kv_heads,
                                 m->head_dim, q, kc, vc, sb, sh, stt, kv_len, cap, qlw, c.p->ql_bytes, c.err, c.stream);
@@ -339,9 +339,17 @@ extern "C" int dual_ar_decode_step(const fp8s_dual_ar_model* m, int64_t B, const
     const int C = m->n_codebooks, L = m->n_slow_layers, F = m->n_fast_layers;
     uint16_t* xbuf[2] = {reinterpret_cast<uint16_t*>(ws + p.off_x[0]), reinterpret_cast<uint16_t*>(ws + p.off_x[1])};
     uint16_t* h = reinterpret_cast<uint16_t*>(ws + p.off_h);
-    auto slow_x = [&](int l) { return slow_taps ? slow_taps + (int64_t)l * BH : xbuf[l & 1]; };
+    uint16_t* xmid = reinterpret_cast<uint16_t*>(ws + p.off_xmid);
+    // Residual stream at the half-block boundaries: entry 2l is the input of
+    // layer l, 2l + 1 the stream after its attention half (taps, or the
+    // workspace buffers when no taps are requested).
+    auto slow_x = [&](int l) { return slow_taps ? slow_taps + (int64_t)(2 * l) * BH : xbuf[l & 1]; };
+    auto slow_mid = [&](int l) { return slow_taps ? slow_taps + (int64_t)(2 * l + 1) * BH : xmid; };
     auto fast_x = [&](int step, int f) {
-        return fast_taps ? fast_taps + ((int64_t)step * (F + 1) + f) * BH : xbuf[f & 1];
+        return fast_taps ? fast_taps + ((int64_t)step * (2 * F + 1) + 2 * f) * BH : xbuf[f & 1];
+    };
+    auto fast_mid = [&](int step, int f) {
+        return fast_taps ? fast_taps + ((int64_t)step * (2 * F + 1) + 2 * f + 1) * BH : xmid;
     };
     auto logits = [&](int cb) {
         return logits_tap ? logits_tap + (int64_t)cb * B * V : reinterpret_cast<float*>(ws + p.off_logits);
@@ -352,7 +360,7 @@ extern "C" int dual_ar_decode_step(const fp8s_dual_ar_model* m, int64_t B, const
     rc = embed_sum_bf16(m->embed, C, V, H, prev_codes, C, B, nullptr, slow_x(0), err_flag, stream);
     if (rc) return step_error(rc, "slow input embedding");
     for (int l = 0; l < L; ++l) {
-        rc = run_block(c, m->slow[l], slow_x(l), slow_x(l + 1), kv->k_cache[l], kv->v_cache[l], kv->stride_b,
+        rc = run_block(c, m->slow[l], slow_x(l), slow_mid(l), slow_x(l + 1), kv->k_cache[l], kv->v_cache[l], kv->stride_b,
                        kv->stride_h, kv->stride_t, kv->cap, kv->kv_len, kv->max_kv_len_hint);
         if (rc) return rc;
     }
@@ -374,7 +382,7 @@ extern "C" int dual_ar_decode_step(const fp8s_dual_ar_model* m, int64_t B, const
         for (int f = 0; f < F; ++f) {
             uint16_t* fk = reinterpret_cast<uint16_t*>(ws + p.off_fk) + (int64_t)f * B * fsb;
             uint16_t* fv = reinterpret_cast<uint16_t*>(ws + p.off_fv) + (int64_t)f * B * fsb;
-            rc = run_block(c, m->fast[f], fast_x(s, f), fast_x(s, f + 1), fk, fv, fsb, fsh, m->head_dim, p.FS,
+            rc = run_block(c, m->fast[f], fast_x(s, f), fast_mid(s, f), fast_x(s, f + 1), fk, fv, fsb, fsh, m->head_dim, p.FS,
                            steps + (int64_t)s * B, s + 1);
             if (rc) return rc;
         }

@@ -307,10 +307,12 @@ typedef struct fp8s_kv_state {
 
 /*
  *   prev_codes  device int32 [B, C]; codes  device int32 [B, C] out.
- *   slow_taps   optional bf16 [n_slow_layers + 1][B][hidden]: the input of
- *               each slow layer and, last, the output of the last one.
- *   fast_taps   optional bf16 [C - 1][n_fast_layers + 1][B][hidden]: per
- *               micro-step, the input of each fast layer and the output.
+ *   slow_taps   optional bf16 [2 * n_slow_layers + 1][B][hidden]: the
+ *               residual stream at every half-block boundary -- entry 2l is
+ *               the input of slow layer l, 2l + 1 the stream after its
+ *               attention half, the last entry the output of the last layer.
+ *   fast_taps   optional bf16 [C - 1][2 * n_fast_layers + 1][B][hidden]: the
+ *               same for the fast layers, per micro-step.
  *   logits_tap  optional fp32 [C][B][codebook_size]: every head's logits.
  *   workspace   dual_ar_decode_step_workspace_size(model, B, hint) bytes,
  *               zero-filled once before first use (control words).

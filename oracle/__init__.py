@@ -44,6 +44,8 @@ from .dual_ar import (  # noqa: F401
     rmsnorm,
     fp8_linear,
     dequant_weight,
+    attention_block,
+    mlp_block,
     decoder_layer,
     embed_sum,
     greedy_code,

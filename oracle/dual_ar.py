@@ -98,16 +98,15 @@ def dequant_weight(w_bf16_values):
     return q, s, dequant_block_fp32(q, s, 128, 128)
 
 
-def decoder_layer(x, p, k_cache, v_cache, kv_len, n_heads, n_kv_heads, head_dim, eps=RMS_EPS):
-    """One pre-norm block at decode.
+def attention_block(x, p, k_cache, v_cache, kv_len, n_heads, n_kv_heads, head_dim, eps=RMS_EPS):
+    """First half of a pre-norm block: x + O(attn(qkv(RMSNorm(x)))).
 
     x        : [B, H] bf16 values
-    p        : dict with dequantised weights 'qkv' [(Hq+2Hkv)D, H], 'o' [H, Hq D],
-               'gate', 'up' [I, H], 'down' [H, I] and bf16 norm weights
-               'norm_attn', 'norm_mlp' [H]
+    p        : dict with dequantised 'qkv' [(Hq+2Hkv)D, H], 'o' [H, Hq D] and
+               the bf16 RMSNorm weight 'norm_attn' [H]
     k_cache, v_cache : [B, Hkv, slots, D] arrays, written at kv_len[b] - 1
                (the new token) and read over [0, kv_len[b])
-    Returns (x_out, dict of the intermediates).
+    Returns (x_mid, dict of the intermediates).
     """
     x = np.asarray(x, np.float64)
     B = x.shape[0]
@@ -125,10 +124,24 @@ def decoder_layer(x, p, k_cache, v_cache, kv_len, n_heads, n_kv_heads, head_dim,
         v_cache[b, :, t, :] = v[b]
     attn = round_bf16(gqa_decode_attention(q, k_cache, v_cache, kv_len)).reshape(B, Hq * D)
     x_mid = round_bf16(x + fp8_linear(attn, p["o"]))
+    return x_mid, {"xn": xn, "q": q, "k": k, "v": v, "attn": attn}
+
+
+def mlp_block(x_mid, p, eps=RMS_EPS):
+    """Second half of a pre-norm block: x_mid + MLP(RMSNorm(x_mid)), with the
+    dequantised 'gate', 'up' [I, H], 'down' [H, I] and 'norm_mlp' [H] of p."""
+    x_mid = np.asarray(x_mid, np.float64)
     xn2 = rmsnorm(x_mid, p["norm_mlp"], eps)
     y = swiglu_mlp(xn2, p["gate"], p["up"], p["down"], MODE_BSGEMM)["y"]
-    out = round_bf16(x_mid + y)
-    return out, {"xn": xn, "q": q, "k": k, "v": v, "attn": attn, "x_mid": x_mid, "xn2": xn2, "y": y}
+    return round_bf16(x_mid + y), {"xn2": xn2, "y": y}
+
+
+def decoder_layer(x, p, k_cache, v_cache, kv_len, n_heads, n_kv_heads, head_dim, eps=RMS_EPS):
+    """One pre-norm block at decode: the attention half, then the MLP half.
+    Returns (x_out, dict of the intermediates, x_mid included)."""
+    x_mid, it = attention_block(x, p, k_cache, v_cache, kv_len, n_heads, n_kv_heads, head_dim, eps)
+    out, it2 = mlp_block(x_mid, p, eps)
+    return out, {**it, "x_mid": x_mid, **it2}
 
 
 def embed_sum(tables, codes, add=None):
@@ -151,7 +164,7 @@ def dual_ar_step(model, prev_codes, slow_k, slow_v, kv_len, force=None):
     """One batched Dual-AR decode step.
 
     model : dict with
-        'slow', 'fast' : lists of layer dicts (see decoder_layer)
+        'slow', 'fast' : lists of layer dicts (see attention_block, mlp_block)
         'slow_norm', 'fast_norm' : bf16 [H] final norm weights
         'embed' : list of C bf16 tables [V, H];  'heads' : list of C
                   dequantised FP8 heads [V, H]
@@ -161,13 +174,17 @@ def dual_ar_step(model, prev_codes, slow_k, slow_v, kv_len, force=None):
         caller's copies; row kv_len-1 is overwritten with the new K/V)
     kv_len : int [B], includes this step's token
     force  : optional teacher forcing, a dict with
-        'slow_x' : [L+1][B, H]  input of slow layer l (and x after the last)
-        'codes'  : [B, C]       the codes fed onward
-        'fast_x' : [C-1][F+1][B, H] input of fast layer f at micro-step p
-      Each layer then starts from the forced input instead of the oracle's own
-      previous output, and each micro-step embeds the forced code.
-    Returns a dict with slow_x [L+1], h, logits [C], codes [B, C], fast_x
-    [C-1][F+1] (each entry the oracle's output given its (forced) input), and
+        'slow_x' : [2L+1][B, H]  the residual stream at every half-block
+                   boundary: entry 2l is the input of slow layer l, 2l+1 its
+                   stream after the attention half, 2L the last output
+        'codes'  : [B, C]        the codes fed onward
+        'fast_x' : [C-1][2F+1][B, H] the same for the fast layers, per
+                   micro-step
+      Each half-block then starts from the forced input instead of the
+      oracle's own previous output, and each micro-step embeds the forced code
+      (FP8 re-quantisation flips and argmax near-ties cannot compound).
+    Returns a dict with slow_x [2L+1], h, logits [C], codes [B, C], fast_x
+    [C-1][2F+1] (each entry the oracle's output given its (forced) input), and
     the K/V rows written per layer ('slow_kv', 'fast_kv').
     """
     Hq, Hkv, D = model["n_heads"], model["n_kv_heads"], model["head_dim"]
@@ -175,15 +192,22 @@ def dual_ar_step(model, prev_codes, slow_k, slow_v, kv_len, force=None):
     C = len(model["embed"])
     B = prev_codes.shape[0]
     L, F = len(model["slow"]), len(model["fast"])
+
+    def stream_in(own, forced, i):
+        return own[i] if forced is None else np.asarray(forced[i], np.float64)
+
+    def run_layers(xs, forced, layers, ks, vs, lens, kv_out):
+        for l, p in enumerate(layers):
+            x_mid, it = attention_block(stream_in(xs, forced, 2 * l), p, ks[l], vs[l], lens, Hq, Hkv, D, eps)
+            xs.append(x_mid)
+            out, _ = mlp_block(stream_in(xs, forced, 2 * l + 1), p, eps)
+            xs.append(out)
+            kv_out.append((it["k"], it["v"]))
+
     slow_x = [embed_sum(model["embed"], prev_codes)]
     slow_kv = []
-    for l in range(L):
-        xin = slow_x[l] if force is None else np.asarray(force["slow_x"][l], np.float64)
-        xo, inter = decoder_layer(xin, model["slow"][l], slow_k[l], slow_v[l], kv_len, Hq, Hkv, D, eps)
-        slow_x.append(xo)
-        slow_kv.append((inter["k"], inter["v"]))
-    x_last = slow_x[L] if force is None else np.asarray(force["slow_x"][L], np.float64)
-    h = rmsnorm(x_last, model["slow_norm"], eps)
+    run_layers(slow_x, None if force is None else force["slow_x"], model["slow"], slow_k, slow_v, kv_len, slow_kv)
+    h = rmsnorm(stream_in(slow_x, None if force is None else force["slow_x"], 2 * L), model["slow_norm"], eps)
     logits = [None] * C
     codes = np.zeros((B, C), np.int32)
     logits[0], codes[:, 0] = greedy_code(h, model["heads"][0])
@@ -194,17 +218,11 @@ def dual_ar_step(model, prev_codes, slow_k, slow_v, kv_len, force=None):
     fv = [np.zeros((B, Hkv, slots, D)) for _ in range(F)]
     fast_x, fast_kv = [], []
     for p in range(C - 1):
-        z = embed_sum([model["embed"][p]], fed[:, p:p + 1], add=h if p == 0 else None)
-        xs = [z]
+        xs = [embed_sum([model["embed"][p]], fed[:, p:p + 1], add=h if p == 0 else None)]
         kvs = []
-        step_len = np.full(B, p + 1, np.int32)
-        for f in range(F):
-            zin = xs[f] if force is None else np.asarray(force["fast_x"][p][f], np.float64)
-            zo, inter = decoder_layer(zin, model["fast"][f], fk[f], fv[f], step_len, Hq, Hkv, D, eps)
-            xs.append(zo)
-            kvs.append((inter["k"], inter["v"]))
-        z_last = xs[F] if force is None else np.asarray(force["fast_x"][p][F], np.float64)
-        zn = rmsnorm(z_last, model["fast_norm"], eps)
+        forced = None if force is None else force["fast_x"][p]
+        run_layers(xs, forced, model["fast"], fk, fv, np.full(B, p + 1, np.int32), kvs)
+        zn = rmsnorm(stream_in(xs, forced, 2 * F), model["fast_norm"], eps)
         logits[p + 1], codes[:, p + 1] = greedy_code(zn, model["heads"][p + 1])
         if force is None:
             fed = codes

@@ -1,7 +1,8 @@
 """The full Dual-AR decode step on the GPU against the oracle, teacher forced:
-every layer's (and every micro-step's) output is compared with the oracle
-applied to the GPU's own input of that layer, so FP8 re-quantisation flips
-and argmax near-ties cannot compound.  The codes must be the exact argmax of
+the output of every half-block (attention half, MLP half) of every layer and
+micro-step is compared with the oracle applied to the GPU's own input of that
+half-block, so FP8 re-quantisation flips and argmax near-ties cannot
+compound.  The codes must be the exact argmax of
 the GPU's logits, and those logits must match the oracle's.
 
 A small model with the same structure is checked on every layer, row and
@@ -55,8 +56,8 @@ def _run_step(host):
     k0 = [k.clone() for k in ks]
     v0 = [v.clone() for v in vs]
     B, H, C, V = c.batch, c.hidden, c.n_codebooks, c.codebook_size
-    slow_taps = torch.empty((c.n_slow_layers + 1, B, H), dtype=torch.bfloat16, device="cuda")
-    fast_taps = torch.empty((C - 1, c.n_fast_layers + 1, B, H), dtype=torch.bfloat16, device="cuda")
+    slow_taps = torch.empty((2 * c.n_slow_layers + 1, B, H), dtype=torch.bfloat16, device="cuda")
+    fast_taps = torch.empty((C - 1, 2 * c.n_fast_layers + 1, B, H), dtype=torch.bfloat16, device="cuda")
     logits = torch.empty((C, B, V), dtype=torch.float32, device="cuda")
     err = torch.zeros(1, dtype=torch.int32, device="cuda")
     log(f"dual-AR step B={B} L={c.n_slow_layers} F={c.n_fast_layers} H={H} V={V}")
@@ -91,9 +92,9 @@ def test_small_model_every_layer_teacher_forced():
     r = oracle.dual_ar_step(om, host.prev_codes, [k for k, _ in caches], [v for _, v in caches], host.kv_len,
                             force=force)
     assert _ulp_close(g["slow"][0], r["slow_x"][0])
-    for l in range(L):
-        e = max_rel_err(g["slow"][l + 1], r["slow_x"][l + 1])
-        log(f"  slow layer {l}: {e:.3e}")
+    for i in range(1, 2 * L + 1):
+        e = max_rel_err(g["slow"][i], r["slow_x"][i])
+        log(f"  slow layer {(i - 1) // 2} {'attention' if i % 2 else 'mlp'} half: {e:.3e}")
         assert e <= TOL_FP8_PATH
     for cb in range(C):
         e = max_rel_err(g["logits"][cb], r["logits"][cb])
@@ -102,9 +103,9 @@ def test_small_model_every_layer_teacher_forced():
         assert e <= TOL_FP8_PATH
     for p in range(C - 1):
         assert max_rel_err(g["fast"][p][0], r["fast_x"][p][0]) <= 2 ** -7
-        for f in range(F):
-            e = max_rel_err(g["fast"][p][f + 1], r["fast_x"][p][f + 1])
-            assert e <= TOL_FP8_PATH, (p, f, e)
+        for i in range(1, 2 * F + 1):
+            e = max_rel_err(g["fast"][p][i], r["fast_x"][p][i])
+            assert e <= TOL_FP8_PATH, (p, i, e)
     # caches: the last layer on each set left its K/V at kv_len - 1, nothing else changed
     for s in range(c.kv_sets):
         last = max(l for l in range(L) if l % c.kv_sets == s)
@@ -132,11 +133,13 @@ def test_full_model_sampled_layers_teacher_forced():
     for l in (0, 17, L - 1):
         p = _oracle_block(host.slow[l])
         k, v = _prefix_cache(host, l % c.kv_sets, rows)
-        out, it = oracle.decoder_layer(g["slow"][l][rows], p, k, v, host.kv_len[rows], c.n_heads, c.n_kv_heads, D,
-                                       c.rms_eps)
-        e = max_rel_err(g["slow"][l + 1][rows], out)
-        log(f"  slow layer {l}: {e:.3e}")
-        assert e <= TOL_FP8_PATH
+        mid, it = oracle.attention_block(g["slow"][2 * l][rows], p, k, v, host.kv_len[rows], c.n_heads,
+                                         c.n_kv_heads, D, c.rms_eps)
+        out, _ = oracle.mlp_block(g["slow"][2 * l + 1][rows], p, c.rms_eps)
+        e1 = max_rel_err(g["slow"][2 * l + 1][rows], mid)
+        e2 = max_rel_err(g["slow"][2 * l + 2][rows], out)
+        log(f"  slow layer {l}: attention half {e1:.3e}, mlp half {e2:.3e}")
+        assert e1 <= TOL_FP8_PATH and e2 <= TOL_FP8_PATH
         if l == L - 1:           # the last layer on its set: its K/V row is what the cache holds now
             s = l % c.kv_sets
             for i, b in enumerate(rows):
@@ -144,7 +147,7 @@ def test_full_model_sampled_layers_teacher_forced():
                 assert max_rel_err(_np(g["ks"][s][b, :, t]), it["k"][i]) <= TOL_FP8_PATH
                 assert max_rel_err(_np(g["vs"][s][b, :, t]), it["v"][i]) <= TOL_FP8_PATH
     heads = [oracle.dequant_weight(f32(h))[2] for h in host.heads]
-    h = oracle.rmsnorm(g["slow"][L][rows], f32(host.slow_norm))
+    h = oracle.rmsnorm(g["slow"][2 * L][rows], f32(host.slow_norm))
     lg, _ = oracle.greedy_code(h, heads[0])
     e = max_rel_err(g["logits"][0][rows], lg)
     log(f"  head 0: {e:.3e}")
@@ -157,11 +160,13 @@ def test_full_model_sampled_layers_teacher_forced():
         assert max_rel_err(g["fast"][p][0][rows], z) <= 2 ** -7
         steps = np.full(len(rows), p + 1)
         for f in range(F):
-            out, _ = oracle.decoder_layer(g["fast"][p][f][rows], fast[f], fk[f], fv[f], steps, c.n_heads,
-                                          c.n_kv_heads, D, c.rms_eps)
-            e = max_rel_err(g["fast"][p][f + 1][rows], out)
-            assert e <= TOL_FP8_PATH, (p, f, e)
-        zn = oracle.rmsnorm(g["fast"][p][F][rows], f32(host.fast_norm))
+            mid, _ = oracle.attention_block(g["fast"][p][2 * f][rows], fast[f], fk[f], fv[f], steps, c.n_heads,
+                                            c.n_kv_heads, D, c.rms_eps)
+            out, _ = oracle.mlp_block(g["fast"][p][2 * f + 1][rows], fast[f], c.rms_eps)
+            e1 = max_rel_err(g["fast"][p][2 * f + 1][rows], mid)
+            e2 = max_rel_err(g["fast"][p][2 * f + 2][rows], out)
+            assert e1 <= TOL_FP8_PATH and e2 <= TOL_FP8_PATH, (p, f, e1, e2)
+        zn = oracle.rmsnorm(g["fast"][p][2 * F][rows], f32(host.fast_norm))
         lg, _ = oracle.greedy_code(zn, heads[p + 1])
         e = max_rel_err(g["logits"][p + 1][rows], lg)
         log(f"  micro-step {p}: head {p + 1} {e:.3e}")
