@@ -1,19 +1,21 @@
 #!/usr/bin/env python3
 """Decode-step hot-path benchmark on one MI355X (gfx950).
 
-One step = the two parts of a decode step's hot path for a batch of B = 64
-sequences, as a Qwen3-4B-sized layer computes them:
-  * the FP8 SwiGLU MLP at M = 64 (hidden 2560, intermediate 9728, bsgemm
-    128x128 weight scales, activations quantised on the GPU);
-  * GQA decode attention (32 query / 8 KV heads, dim 128) over bf16 caches of
-    32768 slots per sequence with ragged kv_len ~ U{234..400}.
-tokens/s = B / step time.  Inputs are resident in HBM before timing starts.
-Four independent weight/cache sets are rotated (reuse distance > 600 MB) so
-the 256 MB Infinity Cache cannot serve repeats.
+One step = one full batched Dual-AR decode step (dual_ar_decode_step): the
+slow AR's 36 Qwen3-4B-sized layers (RMSNorm, FP8 QKV projection with the K/V
+append, GQA decode attention over the active prefix, FP8 output projection,
+FP8 SwiGLU MLP) for a batch of 64 sequences with kv_len ~ U{234..4096} in
+caches of 32768 slots, then the 4-layer fast AR over the remaining 9
+codebooks of 4096 entries and the 10 greedy codebook heads.  tokens/s =
+64 / step time (each step decodes one frame per sequence).  Every input is
+resident in HBM before timing starts; the 36 layers' 3.6 GB of FP8 weights
+are all distinct and the KV prefixes (about 568 MB per layer) rotate over 4
+physical cache sets, so the 256 MB Infinity Cache cannot serve repeats.
 
-Prints ONE JSON line.  Extra keys: per-kernel HBM rates, the M sweep of the
-MLP (bsgemm and MXFP8) and the B sweep of attention, and the CPU oracle timed
-on the host cores as a reported baseline.
+Prints ONE JSON line.  Extra keys: the per-kernel table of the step (time,
+algorithmic bytes, HBM rate), the M sweep of the MLP alone (bsgemm and
+MXFP8, M = 1..128) and the batch / context sweep of attention alone, and the
+CPU oracle timed on the host cores on a bounded sample of the step.
 """
 
 import argparse
@@ -168,17 +170,16 @@ def time_parts(torch, ops, wl, parts, steps, warmup):
 
 def pmc_traffic(kernel):
     """HBM bytes per launch of `kernel` from the committed profiler summary
-    (FETCH_SIZE and WRITE_SIZE runs scaled by a copy of known size), or None
-    when there is none or the kernel's source changed since it was taken."""
-    import hashlib
+    (FETCH_SIZE and WRITE_SIZE runs of this bench, scaled by a copy of known
+    size), or None when there is none or any kernel source changed since it
+    was taken."""
+    from fp8_transformer_step_amd import profiling
     path = os.path.join(ROOT, "profiles", "pmc_traffic.json")
     if not os.path.exists(path):
         return None
-    rec = json.load(open(path)).get("kernels", {}).get(kernel)
-    if not rec:
-        return None
-    src = os.path.join(ROOT, rec["source"])
-    if not os.path.exists(src) or hashlib.sha256(open(src, "rb").read()).hexdigest() != rec["source_sha256"]:
+    d = json.load(open(path))
+    rec = d.get("kernels", {}).get(kernel)
+    if not rec or d.get("sources_sha256") != profiling.sources_sha256():
         return None
     return rec["fetch_bytes"] + rec["write_bytes"]
 
@@ -194,45 +195,163 @@ def kernel_table(per, steps, M, mode, kv_len=None, B=None):
     return out
 
 
-def cpu_baseline(B, kv_len):
-    """The oracle as it stands, on the host cores: one step at B = 64 (MLP at
-    M = 64 plus attention), weights dequantised once outside the timing,
-    median of 3."""
-    from oracle import attention as oattn
-    from oracle import fp8, mlp as omlp
-    from fp8_transformer_step_amd import inputs
+def step_launch_plan(cfg, kv_len):
+    """(library kernel name, algorithmic bytes) of every launch of one
+    dual_ar_decode_step, in launch order.  Algorithmic bytes are what the
+    operation must move: weights and their scales, the activations it reads
+    and writes, the K/V prefix; workspace traffic of split partials and the
+    L2-resident re-reads of a row for its RMS are not counted."""
+    c = cfg
+    B, H, I, V, C = c.batch, c.hidden, c.inter, c.codebook_size, c.n_codebooks
+    A, NQKV, KVD = c.n_heads * c.head_dim, (c.n_heads + 2 * c.n_kv_heads) * c.head_dim, c.n_kv_heads * c.head_dim
+
+    def ws(n, k):
+        return (n // 128) * (k // 128) * 4
+
+    def asc(k):
+        return B * (k // 128) * 4
+
+    def act_quant(name, K, norm):
+        return (name, B * K * 2 + (K * 2 if norm else 0) + B * K + asc(K))
+
+    down = "mlp_down_small" if B <= 16 else "mlp_down"
+
+    def block(kv_bytes):
+        return [act_quant("ql_act_quant", H, True),
+                ("qlinear", NQKV * H + ws(NQKV, H) + B * H + asc(H) + B * NQKV * 2),
+                ("attn_split", kv_bytes + B * A * 2 + 4 * B),
+                ("attn_merge", B * A * 2 + 4 * B),
+                act_quant("ql_act_quant", A, False),
+                ("qlinear", H * A + ws(H, A) + B * A + asc(A) + 2 * B * H * 2),
+                act_quant("mlp_xq", H, True),
+                ("mlp_gu", 2 * I * H + 2 * ws(I, H) + B * H + asc(H) + 2 * B * I * 4),
+                ("mlp_hq", 2 * B * I * 4 + B * I + asc(I)),
+                (down, H * I + ws(H, I) + B * I + asc(I) + 2 * B * H * 2)]
+
+    def head(norm):
+        return [act_quant("ql_act_quant", H, norm),
+                ("qlinear", V * H + ws(V, H) + B * H + asc(H) + B * V * 4),
+                ("argmax", B * V * 4 + 4 * B)]
+
+    out = [("embed_sum", B * C * H * 2 + B * H * 2 + 4 * B * C)]
+    slow_kv = int(np.sum(kv_len, dtype=np.int64)) * KVD * 2 * 2
+    for _ in range(c.n_slow_layers):
+        out += block(slow_kv)
+    out.append(("rmsnorm", 2 * B * H * 2 + H * 2))
+    out += head(False)
+    out.append(("fill_steps", (C - 1) * B * 4))
+    for p in range(C - 1):
+        out.append(("embed_sum", B * H * 2 * (3 if p == 0 else 2) + 4 * B))
+        for _ in range(c.n_fast_layers):
+            out += block((p + 1) * B * KVD * 2 * 2)
+        out += head(True)
+    return out
+
+
+def time_step(torch, ops, dm, kv, prev, steps, warmup, workspace, err):
+    """ms per step over `steps` back-to-back steps (HIP events on the stream,
+    bracketed by synchronisation), the wall clock per step, and the library's
+    per-launch records of a second pass of `steps` steps."""
+    codes = torch.empty(prev.shape, dtype=torch.int32, device="cuda")
+    for _ in range(warmup):
+        ops.dual_ar_decode_step(dm, kv, prev, codes=codes, workspace=workspace, err=err)
+    torch.cuda.synchronize()
+    t0 = torch.cuda.Event(enable_timing=True)
+    t1 = torch.cuda.Event(enable_timing=True)
+    wall0 = time.perf_counter()
+    t0.record()
+    for _ in range(steps):
+        ops.dual_ar_decode_step(dm, kv, prev, codes=codes, workspace=workspace, err=err)
+    t1.record()
+    torch.cuda.synchronize()
+    wall = (time.perf_counter() - wall0) * 1e3 / steps
+    ms = t0.elapsed_time(t1) / steps
+    ops.profile_start(steps * 4096 + 64)
+    for _ in range(steps):
+        ops.dual_ar_decode_step(dm, kv, prev, codes=codes, workspace=workspace, err=err)
+    torch.cuda.synchronize()
+    return ms, wall, ops.profile_stop()
+
+
+def step_kernel_table(recs, plan, steps):
+    """{kernel: launches per step, us per step, us per launch, algorithmic
+    bytes per step and per launch, GB/s, fraction of peak}; checks that the
+    recorded launch sequence is the planned one."""
+    n = len(plan)
+    if len(recs) != n * steps:
+        raise SystemExit(f"recorded {len(recs)} launches, expected {n} x {steps}")
+    tab = {}
+    for i, (name, ms) in enumerate(recs):
+        pname, nbytes = plan[i % n]
+        if name != pname:
+            raise SystemExit(f"launch {i % n} of the step is {name}, expected {pname}")
+        t = tab.setdefault(name, {"launches": 0, "us": 0.0, "bytes": 0})
+        t["launches"] += 1
+        t["us"] += ms * 1e3
+        t["bytes"] += nbytes
+    out = {}
+    for name, t in tab.items():
+        us, nb, k = t["us"] / steps, t["bytes"] / steps, t["launches"] / steps
+        gbs = nb / (us * 1e-6) / 1e9 if us > 0 else 0.0
+        out[name] = {"per_step": k, "us_per_step": us, "us_per_launch": us / k, "bytes_per_step": int(nb),
+                     "bytes_per_launch": nb / k, "GB/s": gbs, "frac": gbs / PEAK_HBM_GBS}
+    return out
+
+
+def cpu_baseline(host):
+    """The oracle as it stands, on the host cores, on a bounded sample of the
+    step: one slow layer (full batch, the first cache set's prefixes), one
+    fast-AR layer at its first micro-step and one codebook head, timed once
+    each with their weights dequantised outside the timing, and scaled to a
+    full step (36 slow + 9 x 4 fast layer evaluations + 10 heads)."""
+    import oracle
+    f32 = __import__("fp8_transformer_step_amd.inputs", fromlist=["x"]).bf16_bits_to_f32
     try:
         import threadpoolctl
         blas = max((p.get("num_threads", 1) for p in threadpoolctl.threadpool_info()), default=1)
     except Exception:
         blas = 1
-    f32 = inputs.bf16_bits_to_f32
-    wbits = inputs.mlp_weights(inputs.W_BSGEMM, H, I)
-    deq = [fp8.dequant_block_fp32(*fp8.quant_weight_128x128(f32(b)), 128, 128) for b in wbits]
-    xb = f32(inputs.mlp_activations(inputs.W_BSGEMM, B, H))
-    Lmax = int(kv_len.max())
-    qb, kb, vb = inputs.attention_prefix(inputs.W_ATTN, B, HQ, HKV, D, Lmax)
-    q, k, v = f32(qb), f32(kb), f32(vb)
-    times = []
-    for _ in range(3):
-        t = time.perf_counter()
-        omlp.swiglu_mlp(xb, *deq, omlp.MODE_BSGEMM)
-        oattn.gqa_decode_attention(q, k, v, kv_len)
-        times.append(time.perf_counter() - t)
-    t = float(np.median(times))
-    return {"value": B / t, "unit": "tokens/s", "cores": int(blas), "kind": "oracle",
-            "sample": f"one full step at B={B} (MLP M={B} + attention), median of 3 runs, "
-                      f"float64 NumPy, weights dequantised once outside the timing; "
-                      f"{t:.3f} s per step; host affinity {len(os.sched_getaffinity(0))} cores"}
+    c = host.cfg
+
+    def block(d):
+        p = {k: oracle.dequant_weight(f32(d[k]))[2] for k in ("qkv", "o", "gate", "up", "down")}
+        p["norm_attn"], p["norm_mlp"] = f32(d["norm_attn"]), f32(d["norm_mlp"])
+        return p
+    ps, pf = block(host.slow[0]), block(host.fast[0])
+    head = oracle.dequant_weight(f32(host.heads[1]))[2]
+    Lmax = int(host.kv_len.max())
+    k = np.zeros((c.batch, c.n_kv_heads, Lmax, c.head_dim), np.float32)
+    v = np.zeros_like(k)
+    for b in range(c.batch):
+        kp, vp = host.kv_prefix(0, b)
+        k[b, :, :kp.shape[1]], v[b, :, :vp.shape[1]] = f32(kp), f32(vp)
+    fk = np.zeros((c.batch, c.n_kv_heads, c.n_codebooks - 1, c.head_dim))
+    fv = np.zeros_like(fk)
+    t0 = time.perf_counter()
+    x = oracle.embed_sum([f32(t) for t in host.embed], host.prev_codes)
+    t1 = time.perf_counter()
+    x1, _ = oracle.decoder_layer(x, ps, k, v, host.kv_len, c.n_heads, c.n_kv_heads, c.head_dim, c.rms_eps)
+    t2 = time.perf_counter()
+    z, _ = oracle.decoder_layer(x1, pf, fk, fv, np.ones(c.batch, np.int32), c.n_heads, c.n_kv_heads,
+                                c.head_dim, c.rms_eps)
+    t3 = time.perf_counter()
+    oracle.greedy_code(oracle.rmsnorm(z, f32(host.fast_norm)), head)
+    t4 = time.perf_counter()
+    L, F, C = c.n_slow_layers, c.n_fast_layers, c.n_codebooks
+    est = (t1 - t0) + L * (t2 - t1) + (C - 1) * F * (t3 - t2) + C * (t4 - t3)
+    return {"value": c.batch / est, "unit": "tokens/s", "cores": int(blas), "kind": "oracle",
+            "sample": f"one slow layer ({t2 - t1:.2f} s), one fast layer ({t3 - t2:.2f} s) and one head "
+                      f"({t4 - t3:.2f} s) at batch {c.batch}, float64 NumPy, weights dequantised outside the "
+                      f"timing, scaled to a full step of {L} + {(C - 1) * F} layer evaluations and {C} heads "
+                      f"= {est:.1f} s; host affinity {len(os.sched_getaffinity(0))} cores"}
 
 
 def main():
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=50)
-    ap.add_argument("--warmup", type=int, default=10)
-    ap.add_argument("--batch", type=int, default=64)
-    ap.add_argument("--sets", type=int, default=4)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--sets", type=int, default=4, help="rotating weight/cache sets of the sweeps")
     ap.add_argument("--no-sweep", action="store_true")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--copy-calibration", action="store_true",
@@ -245,28 +364,38 @@ def main():
         sys.exit(2)
 
     import torch
-    from fp8_transformer_step_amd import inputs, ops
+    from fp8_transformer_step_amd import inputs, model, ops
 
     torch.cuda.set_device(0)
-    B = args.batch
-    kv_len = inputs.kv_lengths(inputs.W_ATTN, B, 234, 400)
-    log(f"bench: building {args.sets} rotating sets (B={B})")
-    wl = Workload(torch, ops, B, B, ops.MLP_BSGEMM, args.sets, kv_len)
-    ms_step, wall, per = time_parts(torch, ops, wl, [wl.mlp, wl.attn], args.steps, args.warmup)
+    cfg = model.FULL
+    log("bench: generating the seeded model and caches")
+    host = model.HostModel(cfg)
+    dm = model.device_model(host)
+    kv, _, _ = model.device_kv(host)
+    prev = torch.from_numpy(host.prev_codes).cuda()
+    err = torch.zeros(1, dtype=torch.int32, device="cuda")
+    workspace = dm.new_workspace(cfg.batch, kv.c.max_kv_len_hint)
     torch.cuda.synchronize()
-    if int(wl.err.item()) != 0:
-        raise SystemExit(f"device error flag {int(wl.err.item())}")
-    ktab = kernel_table(per, args.steps, B, ops.MLP_BSGEMM, kv_len, B)
-    t_mlp = sum(v["us"] * v["per_step"] for k, v in ktab.items() if k.startswith("mlp"))
-    t_attn = sum(v["us"] * v["per_step"] for k, v in ktab.items() if k.startswith("attn"))
-    b_mlp, b_attn = mlp_bytes(B, 0), attn_bytes(kv_len, B)
-    gbs_mlp = b_mlp / (t_mlp * 1e-6) / 1e9
-    gbs_attn = b_attn / (t_attn * 1e-6) / 1e9
-    log(f"step {ms_step * 1e3:.1f} us: mlp kernels {t_mlp:.1f} us {gbs_mlp:.0f} GB/s, "
-        f"attn kernels {t_attn:.1f} us {gbs_attn:.0f} GB/s")
-    for k, v in sorted(ktab.items(), key=lambda kv: -kv[1]["us"] * kv[1]["per_step"]):
-        log(f"  {k:22s} {v['us']:7.1f} us  {v['GB/s']:6.0f} GB/s  ({100 * v['frac']:.1f}% of HBM peak)")
-    dom_name, dom = max(ktab.items(), key=lambda kv: kv[1]["us"] * kv[1]["per_step"])
+    log(f"bench: timing {args.steps} steps after {args.warmup} warm-up steps")
+    ms_step, wall, recs = time_step(torch, ops, dm, kv, prev, args.steps, args.warmup, workspace, err)
+    if int(err.item()) != 0:
+        raise SystemExit(f"device error flag {int(err.item())}")
+    plan = step_launch_plan(cfg, host.kv_len)
+    ktab = step_kernel_table(recs, plan, args.steps)
+    B = cfg.batch
+    log(f"step {ms_step:.3f} ms ({B / (ms_step * 1e-3):.0f} tokens/s), {len(plan)} launches")
+    for k, v in sorted(ktab.items(), key=lambda kv_: -kv_[1]["us_per_step"]):
+        log(f"  {k:16s} {v['per_step']:5.0f} x {v['us_per_launch']:7.1f} us = {v['us_per_step']:8.1f} us/step "
+            f"{v['GB/s']:6.0f} GB/s ({100 * v['frac']:.1f}% of HBM peak)")
+    dom_name, dom = max(ktab.items(), key=lambda kv_: kv_[1]["us_per_step"])
+    groups = {"attention": ("attn_",), "mlp": ("mlp_",), "projections": ("ql_act_quant", "qlinear")}
+    parts = {}
+    for gname, prefixes in groups.items():
+        us = sum(v["us_per_step"] for k, v in ktab.items() if k.startswith(prefixes))
+        nb = sum(v["bytes_per_step"] for k, v in ktab.items() if k.startswith(prefixes))
+        gbs = nb / (us * 1e-6) / 1e9
+        parts[gname] = {"us_per_step": us, "bytes_per_step": nb, "GB/s": gbs, "frac": gbs / PEAK_HBM_GBS}
+    traffic = pmc_traffic(dom_name)
     result = {
         "metric": METRIC,
         "value": B / (ms_step * 1e-3),
@@ -278,24 +407,30 @@ def main():
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "fp8e4m3 MLP, bf16 attention (fp32 accumulate)",
-        "data": "synthetic (seeded, random-init weights N(0,0.02), q/K/V N(0,1))",
-        "config": {"workload": "decode-step hot path, one Qwen3-4B-shaped layer at batch 64: "
-                               "bsgemm FP8 SwiGLU MLP (2560/9728, M=64) + GQA decode attention "
-                               "(32/8 heads, dim 128, cache 32768, kv_len U[234,400])",
-                   "batch": B, "hidden": H, "intermediate": I, "heads": [HQ, HKV, D], "cache": CAP},
+        "dtype": "fp8e4m3 GEMMs (128x128 block / 1x128 group fp32 scales), bf16 activations and attention, "
+                 "fp32 accumulate",
+        "data": "synthetic: seeded random-init weights N(0,0.02) (windows of one seeded pool), K/V prefixes "
+                "N(0,1), random previous codes; no trained weights or datasets",
+        "config": {"workload": "full batched Dual-AR decode step: 36 slow layers (hidden 2560, intermediate "
+                               "9728, 32/8 heads of dim 128) + 4-layer fast AR over 10 codebooks of 4096, "
+                               "batch 64, kv_len U[234,4096] in 32768-slot caches (4 physical K/V sets)",
+                   "batch": B, "hidden": cfg.hidden, "intermediate": cfg.inter,
+                   "heads": [cfg.n_heads, cfg.n_kv_heads, cfg.head_dim], "cache": cfg.cap,
+                   "slow_layers": cfg.n_slow_layers, "fast_layers": cfg.n_fast_layers,
+                   "codebooks": [cfg.n_codebooks, cfg.codebook_size], "kv_len": [cfg.kv_lo, cfg.kv_hi]},
         "roofline": {"bound": "hbm", "kernel": dom_name, "achieved": dom["GB/s"], "peak": PEAK_HBM_GBS,
-                     "unit": "GB/s", "frac": dom["frac"], "traffic": pmc_traffic(dom_name),
-                     "algorithmic_bytes": dom["bytes"], "launch_us": dom["us"]},
-        "parts": {"mlp": {"us": t_mlp, "bytes": b_mlp, "GB/s": gbs_mlp, "frac": gbs_mlp / PEAK_HBM_GBS},
-                  "attn": {"us": t_attn, "bytes": b_attn, "GB/s": gbs_attn, "frac": gbs_attn / PEAK_HBM_GBS}},
+                     "unit": "GB/s", "frac": dom["frac"], "traffic": traffic,
+                     "algorithmic_bytes": dom["bytes_per_launch"], "launch_us": dom["us_per_launch"],
+                     "launches_per_step": dom["per_step"]},
+        "parts": parts,
         "kernels": ktab,
         "wall_ms_per_step": wall,
     }
-    del wl
+    del dm, kv, workspace, prev
     torch.cuda.empty_cache()
 
     if not args.no_sweep:
+        kv_len = inputs.kv_lengths(inputs.W_ATTN, 64, 234, 400)
         sweep = {"mlp_bsgemm": {}, "mlp_mxfp8": {}, "attn": {}}
         for mode, key in ((ops.MLP_BSGEMM, "mlp_bsgemm"), (ops.MLP_MXFP8, "mlp_mxfp8")):
             for M in (1, 8, 32, 64, 128):
@@ -333,7 +468,7 @@ def main():
 
     if not args.no_cpu_baseline:
         log("bench: timing the CPU oracle")
-        result["cpu_baseline"] = cpu_baseline(B, kv_len)
+        result["cpu_baseline"] = cpu_baseline(host)
     print(json.dumps(result), flush=True)
 
 

@@ -99,50 +99,83 @@ __device__ __forceinline__ void load_astage(AStage<MTS, MODE>& st, const uint8_t
     }
 }
 
-// acc[i] += A_i * B over one 128-K block (bsgemm scales applied outside the MFMA).
+// acc[i] += A_i * B over one 128-K block (bsgemm scales applied outside the
+// MFMA); nothing is added when `live` is false (a block past the end of the
+// range, computed on a clamped index so that the loop body has no branches).
 template <int MTS, int MODE>
-__device__ __forceinline__ void mma_block(v4f* acc, const AStage<MTS, MODE>& st, const v8i& b, float sw, int ew) {
+__device__ __forceinline__ void mma_block(v4f* acc, const AStage<MTS, MODE>& st, const v8i& b, float sw, int ew,
+                                          bool live) {
 #pragma unroll
     for (int i = 0; i < MTS; ++i) {
         if (MODE == FP8S_MLP_BSGEMM) {
             const v4f z = {0, 0, 0, 0};
+            // (t * s_x) * s_w, with both products hanging off the MFMA result:
+            // a product of the two scales alone would be computed (and waited
+            // for) as soon as the scales arrive, stalling the prefetch ring.
             const v4f t = mfma_fp8(st.a[i], b, z, kUnitScale, kUnitScale);
-            acc[i][0] += t[0] * (st.s[i].x * sw);
-            acc[i][1] += t[1] * (st.s[i].y * sw);
-            acc[i][2] += t[2] * (st.s[i].z * sw);
-            acc[i][3] += t[3] * (st.s[i].w * sw);
+            const float p0 = (t[0] * st.s[i].x) * sw, p1 = (t[1] * st.s[i].y) * sw;
+            const float p2 = (t[2] * st.s[i].z) * sw, p3 = (t[3] * st.s[i].w) * sw;
+            acc[i][0] += live ? p0 : 0.0f;
+            acc[i][1] += live ? p1 : 0.0f;
+            acc[i][2] += live ? p2 : 0.0f;
+            acc[i][3] += live ? p3 : 0.0f;
         } else {
-            acc[i] = mfma_fp8(st.a[i], b, acc[i], st.e[i], ew);
+            const v4f t = mfma_fp8(st.a[i], b, acc[i], st.e[i], ew);
+            acc[i] = live ? t : acc[i];
         }
     }
 }
 
+// Weight scales of one K block for the NB tiles of an item.
+template <int NB>
+struct WStage {
+    float sw[NB];      // bsgemm: fp32 block scale
+    int ew[NB];        // MX: this lane's UE8M0 exponent byte
+};
+
 // The MFMA loop of a wave: NB weight tiles (LDS fragments at b_off(j, kb)),
-// K blocks [lo, hi), activation stages in a register ring of depth R.
+// K blocks [lo, hi).  The activation operands of a K block and the weight
+// scales wsc(j, kb) are loaded R blocks ahead into a register ring, all
+// loads of a block issued together, so each block waits only for its own
+// (oldest) loads.
 template <int MTS, int NB, int MODE, typename BOff, typename WScale>
 __device__ __forceinline__ void gemm_loop(v4f (&acc)[NB][MTS], const uint8_t* lds, BOff b_off, WScale wsc,
                                           const uint8_t* q, const void* sc, int KB, int mt0, int lo, int hi,
                                           int lane) {
     constexpr int R = MTS == 1 ? 8 : 3;
+    if (lo >= hi) return;                      // this wave has no K blocks
+    const int last = hi - 1;
     AStage<MTS, MODE> st[R];
+    WStage<NB> ws[R];
+    auto load = [&](int u, int kb) {
+        load_astage<MTS, MODE>(st[u], q, sc, KB, mt0, kb, lane);
 #pragma unroll
-    for (int u = 0; u < R; ++u)
-        if (lo + u < hi) load_astage<MTS, MODE>(st[u], q, sc, KB, mt0, lo + u, lane);
+        for (int j = 0; j < NB; ++j) {
+            ws[u].sw[j] = 0.0f;
+            ws[u].ew[j] = kUnitScale;
+            wsc(j, kb, ws[u].sw[j], ws[u].ew[j]);
+        }
+    };
+    // Loads past the end re-read the last block (cache hits) and are never
+    // consumed; the body below is branch-free so the waits stay per block.
+#pragma unroll
+    for (int u = 0; u < R; ++u) load(u, min(lo + u, last));
     for (int kb0 = lo; kb0 < hi; kb0 += R) {
 #pragma unroll
         for (int u = 0; u < R; ++u) {
             const int kb = kb0 + u;
-            if (kb < hi) {
+            const bool live = kb < hi;
+            const int kbc = live ? kb : last;
 #pragma unroll
-                for (int j = 0; j < NB; ++j) {
-                    const v8i b = lds_frag(lds, b_off(j, kb), lane);
-                    float sw = 0.0f;
-                    int ew = kUnitScale;
-                    wsc(j, kb, sw, ew);
-                    mma_block<MTS, MODE>(acc[j], st[u], b, sw, ew);
-                }
-                if (kb + R < hi) load_astage<MTS, MODE>(st[u], q, sc, KB, mt0, kb + R, lane);
+            for (int j = 0; j < NB; ++j) {
+                const v8i b = lds_frag(lds, b_off(j, kbc), lane);
+                mma_block<MTS, MODE>(acc[j], st[u], b, ws[u].sw[j], ws[u].ew[j], live);
             }
+            // keep the refill after this block's math and before the next
+            // block's: the scheduler may not move arithmetic on fresh loads up
+            __builtin_amdgcn_sched_barrier(0);
+            load(u, min(kb + R, last));
+            __builtin_amdgcn_sched_barrier(0);
         }
     }
 }
@@ -268,6 +301,45 @@ __device__ __forceinline__ void* scale_slot(void* base, int mt, int kb, int KB) 
                                    : (void*)(reinterpret_cast<uint8_t*>(base) + ((int64_t)mt * KB + kb) * 64);
 }
 
+
+// Sum of the S split partials of one output tile, in split order (so the
+// result does not depend on which split finished last), for the ITEMS outputs
+// e = threadIdx.x + 256 * i (i < ITEMS, e < n) of this thread.  The partials
+// of other workgroups are read with device-coherent loads; the loads of four
+// splits are all issued before any is consumed, so a thread pays one memory
+// round trip per four splits rather than one per partial.
+template <int ITEMS>
+__device__ __forceinline__ void sum_partials(const float* base, int64_t stride, int S, int n, float (&out)[ITEMS]) {
+#pragma unroll
+    for (int i = 0; i < ITEMS; ++i) out[i] = 0.0f;
+    int k = 0;
+    for (; k + 4 <= S; k += 4) {
+        float v[4][ITEMS];
+#pragma unroll
+        for (int u = 0; u < 4; ++u)
+#pragma unroll
+            for (int i = 0; i < ITEMS; ++i) {
+                const int e = threadIdx.x + 256 * i;
+                v[u][i] = e < n ? __hip_atomic_load(base + (k + u) * stride + e, __ATOMIC_RELAXED,
+                                                     __HIP_MEMORY_SCOPE_AGENT)
+                                : 0.0f;
+            }
+#pragma unroll
+        for (int u = 0; u < 4; ++u)
+#pragma unroll
+            for (int i = 0; i < ITEMS; ++i) out[i] += v[u][i];
+    }
+    for (; k < S; ++k) {
+        float v[ITEMS];
+#pragma unroll
+        for (int i = 0; i < ITEMS; ++i) {
+            const int e = threadIdx.x + 256 * i;
+            v[i] = e < n ? __hip_atomic_load(base + k * stride + e, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) : 0.0f;
+        }
+#pragma unroll
+        for (int i = 0; i < ITEMS; ++i) out[i] += v[i];
+    }
+}
 
 // Device-coherent store of a split partial (no cache write-back needed later).
 __device__ __forceinline__ void store_partial(float* p, float v) {

@@ -256,21 +256,25 @@ __global__ __launch_bounds__(256, 2) void gu_kernel(MlpArgs a) {
 // thread waits for its partial stores to complete, one thread bumps the tile
 // counter, and the last split of the tile sums the S partials in split order
 // (deterministic) into bf16 y and re-arms the counter.
-template <int COLS>
+template <int COLS, int MAXM>
 __device__ __forceinline__ void finish_split(const MlpArgs& a, int nt, int s, int n0, int* s_prev) {
     __builtin_amdgcn_s_waitcnt(0);             // this thread's partial stores are complete
     __syncthreads();
     if (threadIdx.x == 0) *s_prev = atomic_add_relaxed(a.cnt + nt, 1);
     __syncthreads();
     if (*s_prev != a.S - 1) return;
-    const float* base = a.ypart + (int64_t)nt * a.S * a.M * COLS;
-    for (int e = threadIdx.x; e < a.M * COLS; e += blockDim.x) {
-        float sum = 0.0f;
-        for (int k = 0; k < a.S; ++k)
-            sum += __hip_atomic_load(base + (int64_t)k * a.M * COLS + e, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-        const int m = e / COLS, n = n0 + (e % COLS);
-        if (a.res) sum += bf16_to_f32(a.res[(int64_t)m * a.H + n]);
-        a.y[(int64_t)m * a.H + n] = (uint16_t)f32_to_bf16(sum);
+    constexpr int kItems = (MAXM * COLS + 255) / 256;
+    const int n = a.M * COLS;
+    float sum[kItems];
+    sum_partials<kItems>(a.ypart + (int64_t)nt * a.S * a.M * COLS, (int64_t)a.M * COLS, a.S, n, sum);
+#pragma unroll
+    for (int i = 0; i < kItems; ++i) {
+        const int e = threadIdx.x + 256 * i;
+        if (e >= n) continue;
+        const int m = e / COLS, col = n0 + (e % COLS);
+        float v = sum[i];
+        if (a.res) v += bf16_to_f32(a.res[(int64_t)m * a.H + col]);
+        a.y[(int64_t)m * a.H + col] = (uint16_t)f32_to_bf16(v);
     }
     if (threadIdx.x == 0) store_relaxed_agent(a.cnt + nt, 0);
 }
@@ -375,7 +379,7 @@ __global__ __launch_bounds__(256) void down_small_kernel(MlpArgs a) {
                                   acc[t][r] + red[0][t][r][lane] + red[1][t][r][lane] + red[2][t][r][lane]);
             }
     }
-    finish_split<kSmallDownCols>(a, nt, s, n0, &s_prev);
+    finish_split<kSmallDownCols, 16>(a, nt, s, n0, &s_prev);
 }
 
 // ---- down (M > 16): 32 columns x one K split staged in LDS ---------------------
@@ -425,7 +429,7 @@ __global__ __launch_bounds__(256, 2) void down_kernel(MlpArgs a) {
                     if (m < a.M) store_partial(&part[(int64_t)m * COLS + 16 * j + (lane & 15)], acc[j][i][r]);
                 }
     }
-    finish_split<COLS>(a, nt, s, n0, reinterpret_cast<int*>(lds));
+    finish_split<COLS, 16 * MT>(a, nt, s, n0, reinterpret_cast<int*>(lds));
 }
 
 // ---- host side ---------------------------------------------------------------

@@ -126,12 +126,13 @@ __global__ __launch_bounds__(256, 2) void qlinear_kernel(QlArgs a) {
     if (threadIdx.x == 0) *s_prev = atomic_add_relaxed(a.cnt + nt, 1);
     __syncthreads();
     if (*s_prev != a.S - 1) return;
-    const float* base = a.part + (int64_t)nt * a.S * a.M * kQlCols;
-    for (int e = threadIdx.x; e < a.M * kQlCols; e += blockDim.x) {
-        float sum = 0.0f;
-        for (int k = 0; k < a.S; ++k)
-            sum += __hip_atomic_load(base + (int64_t)k * a.M * kQlCols + e, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-        ql_epilogue(a, e / kQlCols, n0 + e % kQlCols, sum);
+    constexpr int kItems = MT * 16 * kQlCols / 256;
+    float sum[kItems];
+    sum_partials<kItems>(a.part + (int64_t)nt * a.S * a.M * kQlCols, (int64_t)a.M * kQlCols, a.S, a.M * kQlCols, sum);
+#pragma unroll
+    for (int i = 0; i < kItems; ++i) {
+        const int e = threadIdx.x + 256 * i;
+        if (e < a.M * kQlCols) ql_epilogue(a, e / kQlCols, n0 + e % kQlCols, sum[i]);
     }
     if (threadIdx.x == 0) store_relaxed_agent(a.cnt + nt, 0);
 }

@@ -7,8 +7,8 @@
       one WRITE_SIZE run (KiB per dispatch), each scaled so that the same
       counter reads the known traffic of the calibration copy in the same run
       (an elementwise copy of 128 Mi fp32: 512 MiB read, 512 MiB written).
-      Records the sha256 of each kernel's source so that stale numbers are
-      ignored by bench.py.
+      Records the sha256 of the kernel sources (csrc/) so that bench.py
+      ignores the numbers once any kernel has changed.
 """
 
 import argparse
@@ -22,29 +22,47 @@ import statistics
 
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 
-# rocprof kernel name (function name) -> (library kernel name, source file)
+# rocprof kernel name (function name) -> library kernel name.  act_quant_kernel
+# serves both the MLP's x quantisation (mlp_xq) and the other projections'
+# (ql_act_quant); the profiler cannot tell the two apart.
 KERNELS = [
-    (r"gu_small_kernel", "mlp_gu_small", "mlp.hip"),
-    (r"down_small_kernel<[^>]*true", "mlp_down_small_fused", "mlp.hip"),
-    (r"down_small_kernel", "mlp_down_small", "mlp.hip"),
-    (r"\bgu_kernel", "mlp_gu", "mlp.hip"),
-    (r"\bdown_kernel", "mlp_down", "mlp.hip"),
-    (r"xq_kernel", "mlp_xq", "mlp.hip"),
-    (r"hq_kernel", "mlp_hq", "mlp.hip"),
-    (r"attn_split_kernel", "attn_split", "attention.hip"),
-    (r"attn_merge_kernel", "attn_merge", "attention.hip"),
-    (r"quant_block128_kernel", "quantize_block128", "quantize.hip"),
-    (r"quant_rows_kernel<128>", "quantize_1x128", "quantize.hip"),
-    (r"quant_rows_kernel<32>", "quantize_1x32", "quantize.hip"),
+    (r"gu_small_kernel", "mlp_gu_small"),
+    (r"down_small_kernel<[^>]*true", "mlp_down_small_fused"),
+    (r"down_small_kernel", "mlp_down_small"),
+    (r"\bgu_kernel", "mlp_gu"),
+    (r"\bdown_kernel", "mlp_down"),
+    (r"act_quant_kernel", "act_quant"),
+    (r"hq_kernel", "mlp_hq"),
+    (r"attn_split_kernel", "attn_split"),
+    (r"attn_merge_kernel", "attn_merge"),
+    (r"qlinear_kernel", "qlinear"),
+    (r"embed_kernel", "embed_sum"),
+    (r"argmax_kernel", "argmax"),
+    (r"rmsnorm_kernel", "rmsnorm"),
+    (r"fill_steps_kernel", "fill_steps"),
+    (r"quant_block128_kernel", "quantize_block128"),
+    (r"quant_rows_kernel<128>", "quantize_1x128"),
+    (r"quant_rows_kernel<32>", "quantize_1x32"),
 ]
 CALIB_BYTES = 512 << 20
 
 
 def lib_kernel(name):
-    for pat, lib, src in KERNELS:
+    for pat, lib in KERNELS:
         if "fp8s::" in name and re.search(pat, name):
-            return lib, "fp8_transformer_step_amd/csrc/" + src
-    return None, None
+            return lib
+    return None
+
+
+def sources_sha256():
+    """sha256 over every kernel source file of the library (sorted by name)."""
+    h = hashlib.sha256()
+    csrc = os.path.join(ROOT, "fp8_transformer_step_amd", "csrc")
+    for f in sorted(os.listdir(csrc)):
+        if f.endswith((".hip", ".h", ".cpp")):
+            h.update(f.encode())
+            h.update(open(os.path.join(csrc, f), "rb").read())
+    return h.hexdigest()
 
 
 def _csv(path_or_dir, suffix):
@@ -62,7 +80,7 @@ def stats(csv_path, out_md, command):
              "| library kernel | rocprof name | calls | avg us | min us | max us |",
              "|---|---|---|---|---|---|"]
     for r in rows:
-        lib, _ = lib_kernel(r["Name"])
+        lib = lib_kernel(r["Name"])
         if not lib:
             continue
         short = r["Name"].split("(")[0].replace("void ", "")
@@ -77,9 +95,9 @@ def _counter_means(run_dir):
     for r in rows:
         v = float(r["Counter_Value"]) * 1024.0      # KiB -> bytes
         name = r["Kernel_Name"]
-        lib, src = lib_kernel(name)
+        lib = lib_kernel(name)
         if lib:
-            per.setdefault((lib, src), []).append(v)
+            per.setdefault(lib, []).append(v)
         elif "add" in name.lower() and int(r.get("Grid_Size", 0) or 0) >= (1 << 20):
             calib.append(v)
     if not calib:
@@ -96,12 +114,10 @@ def pmc(fetch_dir, write_dir, out_json, command):
                            "known_read_bytes": CALIB_BYTES, "known_write_bytes": CALIB_BYTES,
                            "fetch_size_bytes": fcal, "write_size_bytes": wcal,
                            "fetch_scale": fs, "write_scale": ws},
+           "sources_sha256": sources_sha256(),
            "kernels": {}}
-    for (lib, src), fv in fetch.items():
-        wv = write.get((lib, src), 0.0)
-        sha = hashlib.sha256(open(os.path.join(ROOT, src), "rb").read()).hexdigest()
-        out["kernels"][lib] = {"fetch_bytes": fv * fs, "write_bytes": wv * ws, "source": src,
-                               "source_sha256": sha}
+    for lib, fv in fetch.items():
+        out["kernels"][lib] = {"fetch_bytes": fv * fs, "write_bytes": write.get(lib, 0.0) * ws}
     json.dump(out, open(out_json, "w"), indent=1)
 
 
