@@ -84,6 +84,31 @@ __device__ __forceinline__ float fsum_xor(float v) {
     return v;
 }
 
+// All-reduce over each row of 16 lanes with DPP moves (VALU, no LDS round
+// trip): swap within pairs, then within quads, then mirror the half-rows
+// (lane i <-> 7 - i joins the two quads) and the rows (i <-> 15 - i joins the
+// two halves).
+template <int CTRL>
+__device__ __forceinline__ float dpp_f32(float v) {
+    return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), CTRL, 0xF, 0xF, false));
+}
+constexpr int kDppXor1 = 0xB1;        // quad_perm [1, 0, 3, 2]
+constexpr int kDppXor2 = 0x4E;        // quad_perm [2, 3, 0, 1]
+constexpr int kDppHalfMirror = 0x141; // row_half_mirror
+constexpr int kDppMirror = 0x140;     // row_mirror
+__device__ __forceinline__ float max16(float v) {
+    v = fmaxf(v, dpp_f32<kDppXor1>(v));
+    v = fmaxf(v, dpp_f32<kDppXor2>(v));
+    v = fmaxf(v, dpp_f32<kDppHalfMirror>(v));
+    return fmaxf(v, dpp_f32<kDppMirror>(v));
+}
+__device__ __forceinline__ float sum16(float v) {
+    v += dpp_f32<kDppXor1>(v);
+    v += dpp_f32<kDppXor2>(v);
+    v += dpp_f32<kDppHalfMirror>(v);
+    return v + dpp_f32<kDppMirror>(v);
+}
+
 // ---- MFMA --------------------------------------------------------------------
 // D(16x16 fp32) += A(16x128 e4m3) * B(128x16 e4m3) with per-lane UE8M0 scales.
 // Operand layout (gfx950, 8-bit elements, measured with a lane probe): lane l
