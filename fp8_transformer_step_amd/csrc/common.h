@@ -102,6 +102,10 @@ __device__ __forceinline__ float max16(float v) {
     v = fmaxf(v, dpp_f32<kDppHalfMirror>(v));
     return fmaxf(v, dpp_f32<kDppMirror>(v));
 }
+__device__ __forceinline__ float max4(float v) {
+    v = fmaxf(v, dpp_f32<kDppXor1>(v));
+    return fmaxf(v, dpp_f32<kDppXor2>(v));
+}
 __device__ __forceinline__ float sum16(float v) {
     v += dpp_f32<kDppXor1>(v);
     v += dpp_f32<kDppXor2>(v);

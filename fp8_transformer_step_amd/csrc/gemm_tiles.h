@@ -278,13 +278,13 @@ __device__ __forceinline__ void quant_chunk(const float (&f)[8], uint8_t* frag, 
     for (int i = 0; i < 8; ++i) am = fmaxf(am, fabsf(f[i]));
     uint32_t q0, q1;
     if (MODE == FP8S_MLP_BSGEMM) {
-        am = fmax_xor<16>(am);
+        am = max16(am);
         const float s = bs_scale(am);
         q0 = e4m3x4(f[0] / s, f[1] / s, f[2] / s, f[3] / s);
         q1 = e4m3x4(f[4] / s, f[5] / s, f[6] / s, f[7] / s);
         if (valid && j == 0) reinterpret_cast<float*>(sc)[row] = s;
     } else {
-        am = fmax_xor<4>(am);
+        am = max4(am);
         const int E = mx_exponent(__float_as_uint(am));
         const float mul = mx_inv_scale(E);
         q0 = e4m3x4(f[0] * mul, f[1] * mul, f[2] * mul, f[3] * mul);
@@ -375,17 +375,31 @@ __device__ __forceinline__ void unpack_bf16x8(const uint4& v, float (&f)[8]) {
 // 1 / sqrt(mean(x^2) + eps) of row xr [K] (bf16), summed by the 16 lanes of a
 // row group, lane j taking the 8-column chunks j, j + 16, ...
 __device__ __forceinline__ float row_inv_rms(const uint16_t* xr, int K, float eps, int j, bool valid) {
-    float ss = 0.0f;
+    // four chunks in flight per step, four independent partial sums
+    float ss[4] = {0.0f, 0.0f, 0.0f, 0.0f};
     if (valid) {
-        for (int c = 8 * j; c < K; c += 128) {
+        int c = 8 * j;
+        for (; c + 384 < K; c += 512) {
+            uint4 v[4];
+#pragma unroll
+            for (int u = 0; u < 4; ++u) v[u] = *reinterpret_cast<const uint4*>(xr + c + 128 * u);
+#pragma unroll
+            for (int u = 0; u < 4; ++u) {
+                float f[8];
+                unpack_bf16x8(v[u], f);
+#pragma unroll
+                for (int i = 0; i < 8; ++i) ss[u] = fmaf(f[i], f[i], ss[u]);
+            }
+        }
+        for (; c < K; c += 128) {
             float f[8];
             unpack_bf16x8(*reinterpret_cast<const uint4*>(xr + c), f);
 #pragma unroll
-            for (int i = 0; i < 8; ++i) ss = fmaf(f[i], f[i], ss);
+            for (int i = 0; i < 8; ++i) ss[0] = fmaf(f[i], f[i], ss[0]);
         }
     }
-    ss = fsum_xor<16>(ss);
-    return 1.0f / sqrtf(ss / (float)K + eps);
+    const float t = sum16((ss[0] + ss[1]) + (ss[2] + ss[3]));
+    return 1.0f / sqrtf(t / (float)K + eps);
 }
 
 template <int MODE>
