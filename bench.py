@@ -216,11 +216,12 @@ def step_launch_plan(cfg, kv_len):
 
     down = "mlp_down_small" if B <= 16 else "mlp_down"
 
-    def block(kv_bytes):
+    def block(kv_bytes, single):
+        attn = ([("attn_single", kv_bytes + 2 * B * A * 2 + 4 * B)] if single else
+                [("attn_split", kv_bytes + B * A * 2 + 4 * B), ("attn_merge", B * A * 2 + 4 * B)])
         return [act_quant("ql_act_quant", H, True),
-                ("qlinear", NQKV * H + ws(NQKV, H) + B * H + asc(H) + B * NQKV * 2),
-                ("attn_split", kv_bytes + B * A * 2 + 4 * B),
-                ("attn_merge", B * A * 2 + 4 * B),
+                ("qlinear", NQKV * H + ws(NQKV, H) + B * H + asc(H) + B * NQKV * 2)] + attn + [
+
                 act_quant("ql_act_quant", A, False),
                 ("qlinear", H * A + ws(H, A) + B * A + asc(A) + 2 * B * H * 2),
                 act_quant("mlp_xq", H, True),
@@ -235,15 +236,17 @@ def step_launch_plan(cfg, kv_len):
 
     out = [("embed_sum", B * C * H * 2 + B * H * 2 + 4 * B * C)]
     slow_kv = int(np.sum(kv_len, dtype=np.int64)) * KVD * 2 * 2
+    # the slow AR's prefixes are split over chunks and merged; the fast AR's
+    # few-slot caches are one chunk, written by the split kernel itself
     for _ in range(c.n_slow_layers):
-        out += block(slow_kv)
+        out += block(slow_kv, False)
     out.append(("rmsnorm", 2 * B * H * 2 + H * 2))
     out += head(False)
     out.append(("fill_steps", (C - 1) * B * 4))
     for p in range(C - 1):
         out.append(("embed_sum", B * H * 2 * (3 if p == 0 else 2) + 4 * B))
         for _ in range(c.n_fast_layers):
-            out += block((p + 1) * B * KVD * 2 * 2)
+            out += block((p + 1) * B * KVD * 2 * 2, True)
         out += head(True)
     return out
 

@@ -48,7 +48,10 @@ __device__ __forceinline__ bool kv_len_ok(int L, const AttnArgs& a) {
     return L >= 1 && (int64_t)L <= a.cap && (int64_t)L <= a.hint;
 }
 
-template <int D, int G>
+// SINGLE: the whole prefix is one chunk (n_split == 1), so the kernel
+// normalises and writes the bf16 output itself (and handles an invalid
+// kv_len the way the merge does); no merge launch follows.
+template <int D, int G, bool SINGLE>
 __global__ __launch_bounds__(256) void attn_split_kernel(AttnArgs a) {
     constexpr int NJ = D / 32;                 // MFMA K-steps over the head dim
     constexpr int LPR = D / 8;                 // lanes per V row (8 bf16 each)
@@ -61,7 +64,14 @@ __global__ __launch_bounds__(256) void attn_split_kernel(AttnArgs a) {
     const int bg = blockIdx.x / a.n_split;
     const int g = bg % a.Hkv, b = bg / a.Hkv;
     const int L = a.kv_len[b];
-    if (!kv_len_ok(L, a)) return;              // the merge writes zeros and reports
+    if (!kv_len_ok(L, a)) {                    // the merge writes zeros and reports
+        if (SINGLE) {
+            for (int e = threadIdx.x; e < G * D; e += 256)
+                a.out[((int64_t)b * a.Hq + g * G) * D + e] = 0;
+            if (threadIdx.x == 0 && g == 0) report_error(a.err, FP8S_DEV_KVLEN_RANGE);
+        }
+        return;
+    }
     const int t_begin = sp * a.chunk;
     if (t_begin >= L) return;                  // chunk entirely past the prefix
     const int n_tok = min(a.chunk, L - t_begin);
@@ -166,9 +176,13 @@ __global__ __launch_bounds__(256) void attn_split_kernel(AttnArgs a) {
     for (int e = threadIdx.x; e < G * D; e += 256) {
         const int h = e / D, d = e % D;
         const float acc = s_red[0][h][d] + s_red[1][h][d] + s_red[2][h][d] + s_red[3][h][d];
-        float* p = a.part + (((int64_t)b * a.Hq + g * G + h) * a.n_split + sp) * (D + 2);
-        p[2 + d] = acc;
-        if (d == 0) { p[0] = s_ml[h][0]; p[1] = s_ml[h][1]; }
+        if (SINGLE) {
+            a.out[((int64_t)b * a.Hq + g * G + h) * D + d] = (uint16_t)f32_to_bf16(acc / s_ml[h][1]);
+        } else {
+            float* p = a.part + (((int64_t)b * a.Hq + g * G + h) * a.n_split + sp) * (D + 2);
+            p[2 + d] = acc;
+            if (d == 0) { p[0] = s_ml[h][0]; p[1] = s_ml[h][1]; }
+        }
     }
 }
 
@@ -217,7 +231,10 @@ static AttnPlan plan_attn(int64_t B, int32_t Hkv, int64_t hint) {
 
 template <int D, int G>
 static void launch_split(dim3 grid, hipStream_t st, const AttnArgs& a) {
-    FP8S_LAUNCH("attn_split", (attn_split_kernel<D, G>), grid, dim3(256), 0, st, a);
+    if (a.n_split == 1)
+        FP8S_LAUNCH("attn_single", (attn_split_kernel<D, G, true>), grid, dim3(256), 0, st, a);
+    else
+        FP8S_LAUNCH("attn_split", (attn_split_kernel<D, G, false>), grid, dim3(256), 0, st, a);
 }
 
 }  // namespace fp8s
@@ -275,6 +292,7 @@ extern "C" int gqa_decode_attn(const uint16_t* q, const uint16_t* k_cache, const
 #undef FP8S_ATTN_CASE
     int rc = check_launch("gqa_decode_attn (split)");
     if (rc) return rc;
+    if (p.n_split == 1) return FP8S_OK;        // the split kernel wrote the output
     if (D == 64)
         FP8S_LAUNCH("attn_merge", attn_merge_kernel<64>, dim3((unsigned)(B * Hq)), dim3(64), 0, st, a);
     else

@@ -138,12 +138,19 @@ struct WStage {
 // scales wsc(j, kb) are loaded R blocks ahead into a register ring, all
 // loads of a block issued together, so each block waits only for its own
 // (oldest) loads.
-template <int MTS, int NB, int MODE, typename BOff, typename WScale>
+//
+// `ready()` is called once the ring's first loads are issued and before any
+// weight fragment is read from LDS: the caller waits there for its weight
+// staging, so the activation loads overlap the weight stream.
+template <int MTS, int NB, int MODE, typename BOff, typename WScale, typename Ready>
 __device__ __forceinline__ void gemm_loop(v4f (&acc)[NB][MTS], const uint8_t* lds, BOff b_off, WScale wsc,
                                           const uint8_t* q, const void* sc, int KB, int mt0, int lo, int hi,
-                                          int lane) {
+                                          int lane, Ready ready) {
     constexpr int R = MTS == 1 ? 8 : 3;
-    if (lo >= hi) return;                      // this wave has no K blocks
+    if (lo >= hi) {                            // this wave has no K blocks
+        ready();
+        return;
+    }
     const int last = hi - 1;
     AStage<MTS, MODE> st[R];
     WStage<NB> ws[R];
@@ -160,6 +167,7 @@ __device__ __forceinline__ void gemm_loop(v4f (&acc)[NB][MTS], const uint8_t* ld
     // consumed; the body below is branch-free so the waits stay per block.
 #pragma unroll
     for (int u = 0; u < R; ++u) load(u, min(lo + u, last));
+    ready();
     for (int kb0 = lo; kb0 < hi; kb0 += R) {
 #pragma unroll
         for (int u = 0; u < R; ++u) {

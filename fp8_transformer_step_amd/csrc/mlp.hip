@@ -218,8 +218,6 @@ __global__ __launch_bounds__(256, 2) void gu_kernel(MlpArgs a) {
         const int kb = up ? f - a.KBH : f;
         stage_w(up ? a.wu : a.wg, up ? a.ldu : a.ldg, n0, kb, lds, f * kFrag, lane);
     }
-    __builtin_amdgcn_s_waitcnt(0);
-    __syncthreads();
 
     v4f acc[2][MTS];
 #pragma unroll
@@ -234,7 +232,10 @@ __global__ __launch_bounds__(256, 2) void gu_kernel(MlpArgs a) {
         else
             ew = j ? wscale_mx(a.su, a.su_r, a.su_c, n0, kb, lane) : wscale_mx(a.sg, a.sg_r, a.sg_c, n0, kb, lane);
     };
-    gemm_loop<MTS, 2, MODE>(acc, lds, b_off, wsc, a.qx, a.sx, a.KBH, wm * MTS, lo, hi, lane);
+    gemm_loop<MTS, 2, MODE>(acc, lds, b_off, wsc, a.qx, a.sx, a.KBH, wm * MTS, lo, hi, lane, [] {
+        __builtin_amdgcn_s_waitcnt(0);       // this thread's weight fragments are in LDS
+        __syncthreads();                     // and everyone's
+    });
     reduce_wk<MTS, 2, WK>(acc, lds, wm, wk, lane);
     if (wk == 0) {
 #pragma unroll
@@ -398,8 +399,6 @@ __global__ __launch_bounds__(256, 2) void down_kernel(MlpArgs a) {
         const int j = f / nkb, kb = klo + f % nkb;
         stage_w(a.wd, a.ldd, n0 + 16 * j, kb, lds, f * kFrag, lane);
     }
-    __builtin_amdgcn_s_waitcnt(0);
-    __syncthreads();
 
     v4f acc[NB][MTS];
 #pragma unroll
@@ -414,7 +413,10 @@ __global__ __launch_bounds__(256, 2) void down_kernel(MlpArgs a) {
         else
             ew = wscale_mx(a.sd, a.sd_r, a.sd_c, n0 + 16 * j, kb, lane);
     };
-    gemm_loop<MTS, NB, MODE>(acc, lds, b_off, wsc, a.qh, a.sh, a.KBI, wm * MTS, lo, hi, lane);
+    gemm_loop<MTS, NB, MODE>(acc, lds, b_off, wsc, a.qh, a.sh, a.KBI, wm * MTS, lo, hi, lane, [] {
+        __builtin_amdgcn_s_waitcnt(0);       // this thread's weight fragments are in LDS
+        __syncthreads();                     // and everyone's
+    });
     reduce_wk<MTS, NB, WK>(acc, lds, wm, wk, lane);
     constexpr int COLS = 16 * NB;
     float* part = a.ypart + ((int64_t)nt * a.S + s) * a.M * COLS;

@@ -89,8 +89,6 @@ __global__ __launch_bounds__(256, 2) void qlinear_kernel(QlArgs a) {
         const int j = f / nkb, kb = klo + f % nkb;
         stage_w(a.w, a.ldw, n0 + 16 * j, kb, lds, f * kFrag, lane);
     }
-    __builtin_amdgcn_s_waitcnt(0);
-    __syncthreads();
 
     v4f acc[NB][MTS];
 #pragma unroll
@@ -103,7 +101,10 @@ __global__ __launch_bounds__(256, 2) void qlinear_kernel(QlArgs a) {
         (void)ew;
         sw = wscale_bs(a.sw, a.sw_r, a.sw_c, n0 + 16 * j, kb);
     };
-    gemm_loop<MTS, NB, FP8S_MLP_BSGEMM>(acc, lds, b_off, wsc, a.qx, a.sx, a.KB, wm * MTS, lo, hi, lane);
+    gemm_loop<MTS, NB, FP8S_MLP_BSGEMM>(acc, lds, b_off, wsc, a.qx, a.sx, a.KB, wm * MTS, lo, hi, lane, [] {
+        __builtin_amdgcn_s_waitcnt(0);       // this thread's weight fragments are in LDS
+        __syncthreads();                     // and everyone's
+    });
     reduce_wk<MTS, NB, WK>(acc, lds, wm, wk, lane);
 
     float* part = a.part + ((int64_t)nt * a.S + s) * a.M * kQlCols;

@@ -33,6 +33,7 @@ KERNELS = [
     (r"\bdown_kernel", "mlp_down"),
     (r"act_quant_kernel", "act_quant"),
     (r"hq_kernel", "mlp_hq"),
+    (r"attn_split_kernel<[^>]*true", "attn_single"),
     (r"attn_split_kernel", "attn_split"),
     (r"attn_merge_kernel", "attn_merge"),
     (r"qlinear_kernel", "qlinear"),

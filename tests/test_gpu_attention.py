@@ -132,15 +132,30 @@ def test_gqa_matches_explicit_head_repeat():
     assert max_rel_err(out, ref) <= TOL_BF16_ATTN
 
 
-def test_invalid_kv_len_sets_flag_and_zeroes():
+@pytest.mark.parametrize("hint", [64, 16])
+def test_invalid_kv_len_sets_flag_and_zeroes(hint):
+    """hint 64 splits the prefix and merges; hint 16 is a single chunk whose
+    kernel writes the output itself."""
     need_gpu()
     B, cap = 3, 64
     kv = np.array([10, 10, 10], np.int32)
     qb, kb, vb, kc, vc = _make(inputs.W_ATTN, B, 32, 8, 128, cap, kv, extra=41)
     bad = np.array([10, 0, 65], np.int32)
     err = torch.zeros(1, dtype=torch.int32, device="cuda")
-    out = _run(qb, kc, vc, bad, cap, err)
+    out = _run(qb, kc, vc, bad, hint, err)
     assert int(err.item()) == ops.DEV_KVLEN_RANGE
     assert not out[1].float().abs().sum().item() and not out[2].float().abs().sum().item()
     ref = _oracle(qb[:1], kb[:1], vb[:1], kv[:1])
     assert max_rel_err(from_dev_bf16(out[:1]), ref) <= TOL_BF16_ATTN
+
+
+@pytest.mark.parametrize("G", [4, 2])
+def test_single_chunk_short_prefix(G):
+    """Prefixes of at most 16 positions (the fast AR's few-slot cache): one
+    chunk, no merge, output written by the split kernel."""
+    need_gpu()
+    B, Hkv, cap = 64, 8, 16
+    kv = (np.arange(B) % 9 + 1).astype(np.int32)
+    qb, kb, vb, kc, vc = _make(inputs.W_ATTN, B, Hkv * G, Hkv, 128, cap, kv, extra=50 + G)
+    out = from_dev_bf16(_run(qb, kc, vc, kv, 9))
+    assert max_rel_err(out, _oracle(qb, kb, vb, kv)) <= TOL_BF16_ATTN
