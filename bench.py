@@ -216,13 +216,17 @@ def step_launch_plan(cfg, kv_len):
 
     down = "mlp_down_small" if B <= 16 else "mlp_down"
 
-    def block(kv_bytes, single):
-        attn = ([("attn_single", kv_bytes + 2 * B * A * 2 + 4 * B)] if single else
-                [("attn_split", kv_bytes + B * A * 2 + 4 * B), ("attn_merge", B * A * 2 + 4 * B)])
-        return [act_quant("ql_act_quant", H, True),
-                ("qlinear", NQKV * H + ws(NQKV, H) + B * H + asc(H) + B * NQKV * 2)] + attn + [
+    # the attention quantises its output into the output projection's operand
+    # itself when each KV head's query group spans whole 128-column groups
+    fused = (c.n_heads // c.n_kv_heads) * c.head_dim % 128 == 0
+    oq = B * A + asc(A) if fused else 0
 
-                act_quant("ql_act_quant", A, False),
+    def block(kv_bytes, single):
+        attn = ([("attn_single", kv_bytes + 2 * B * A * 2 + 4 * B + oq)] if single else
+                [("attn_split", kv_bytes + B * A * 2 + 4 * B), ("attn_merge", B * A * 2 + 4 * B + oq)])
+        return [act_quant("ql_act_quant", H, True),
+                ("qlinear", NQKV * H + ws(NQKV, H) + B * H + asc(H) + B * NQKV * 2)] + attn + (
+                [] if fused else [act_quant("ql_act_quant", A, False)]) + [
                 ("qlinear", H * A + ws(H, A) + B * A + asc(A) + 2 * B * H * 2),
                 act_quant("mlp_xq", H, True),
                 ("mlp_gu", 2 * I * H + 2 * ws(I, H) + B * H + asc(H) + 2 * B * I * 4),

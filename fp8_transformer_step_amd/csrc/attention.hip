@@ -24,6 +24,7 @@
 //   * A second small kernel merges the chunks of every (sequence, head).
 #include "common.h"
 #include "host_common.h"
+#include "internal.h"
 #include "profile.h"
 
 namespace fp8s {
@@ -42,7 +43,28 @@ struct AttnArgs {
     float* part;               // [B][Hq][n_split][D + 2]
     uint16_t* out;
     int32_t* err;
+    uint8_t* qo;               // optional: the output quantised as the next GEMM's operand
+    float* so;                 //   (1x128 groups = one head of D = 128, fp32 scales)
+    int qo_KB;                 //   K blocks of that operand (Hq * D / 128)
 };
+
+// Quantise one 128-column group kb of output row b (held by one wave: column
+// lane in v0, column lane + 64 in v1) the way the projection that follows
+// quantises its input: s = amax / 448, e4m3(v / s), stored in MFMA operand
+// order with its scale.  The values are the bf16-rounded outputs, so the
+// bytes equal those of quantising the bf16 output afterwards.
+__device__ __forceinline__ void quant_out_wave(const AttnArgs& a, int b, int kb, float v0, float v1, int lane) {
+    float m = max16(fmaxf(fabsf(v0), fabsf(v1)));
+    m = fmaxf(m, __shfl_xor(m, 16, kWave));
+    m = fmaxf(m, __shfl_xor(m, 32, kWave));
+    const float s = bs_scale(m);
+    const int mt = b >> 4, row = b & 15;
+    uint8_t* frag = a.qo + ((int64_t)mt * a.qo_KB + kb) * 2048;
+    const int c1 = lane + 64;
+    frag[(row + 16 * frag_lane_group(lane)) * 32 + frag_byte(lane)] = (uint8_t)(e4m3x2(v0 / s, 0.0f) & 0xFFu);
+    frag[(row + 16 * frag_lane_group(c1)) * 32 + frag_byte(c1)] = (uint8_t)(e4m3x2(v1 / s, 0.0f) & 0xFFu);
+    if (lane == 0) a.so[((int64_t)mt * a.qo_KB + kb) * 16 + row] = s;
+}
 
 __device__ __forceinline__ bool kv_len_ok(int L, const AttnArgs& a) {
     return L >= 1 && (int64_t)L <= a.cap && (int64_t)L <= a.hint;
@@ -69,6 +91,10 @@ __global__ __launch_bounds__(256) void attn_split_kernel(AttnArgs a) {
             for (int e = threadIdx.x; e < G * D; e += 256)
                 a.out[((int64_t)b * a.Hq + g * G) * D + e] = 0;
             if (threadIdx.x == 0 && g == 0) report_error(a.err, FP8S_DEV_KVLEN_RANGE);
+            if constexpr ((G * D) % 128 == 0)
+                if (a.qo)
+                    for (int w = threadIdx.x >> 6; w < G * D / 128; w += 4)
+                        quant_out_wave(a, b, g * G * D / 128 + w, 0.0f, 0.0f, threadIdx.x & 63);
         }
         return;
     }
@@ -177,40 +203,74 @@ __global__ __launch_bounds__(256) void attn_split_kernel(AttnArgs a) {
         const int h = e / D, d = e % D;
         const float acc = s_red[0][h][d] + s_red[1][h][d] + s_red[2][h][d] + s_red[3][h][d];
         if (SINGLE) {
-            a.out[((int64_t)b * a.Hq + g * G + h) * D + d] = (uint16_t)f32_to_bf16(acc / s_ml[h][1]);
+            const uint32_t bits = f32_to_bf16(acc / s_ml[h][1]);
+            a.out[((int64_t)b * a.Hq + g * G + h) * D + d] = (uint16_t)bits;
+            s_red[0][h][d] = bf16_to_f32(bits);      // s_red[0] is no longer read below
         } else {
             float* p = a.part + (((int64_t)b * a.Hq + g * G + h) * a.n_split + sp) * (D + 2);
             p[2 + d] = acc;
             if (d == 0) { p[0] = s_ml[h][0]; p[1] = s_ml[h][1]; }
         }
     }
+    if constexpr (SINGLE && (G * D) % 128 == 0) {
+        if (a.qo) {                              // the G heads' outputs are G*D/128 whole groups
+            __syncthreads();
+            const float* ov = &s_red[0][0][0];
+            for (int w = wave; w < G * D / 128; w += 4)
+                quant_out_wave(a, b, g * G * D / 128 + w, ov[128 * w + lane], ov[128 * w + 64 + lane], lane);
+        }
+    }
 }
 
 // Merge the chunks of one (sequence, query head): out = sum_i 2^(m_i - M) acc_i
-// / sum_i 2^(m_i - M) l_i over the chunks that hold positions.
+// / sum_i 2^(m_i - M) l_i over the chunks that hold positions.  One wave per
+// (sequence, 128 output columns): column lane and lane + 64 of the group, each
+// of them in one head (D is 64 or 128).  Lane i holds chunk i's statistics;
+// its weight reaches the other lanes by readlane while every lane streams
+// its own column of the chunk accumulators.
 template <int D>
-__global__ __launch_bounds__(D) void attn_merge_kernel(AttnArgs a) {
-    const int bh = blockIdx.x;
-    const int b = bh / a.Hq;
-    const int d = threadIdx.x;
+__global__ __launch_bounds__(256) void attn_merge_kernel(AttnArgs a) {
+    const int lane = threadIdx.x & 63;
+    const int segs = a.Hq * D / 64;              // 64-column segments of an output row
+    const int pairs = (segs + 1) / 2;
+    const int wid = blockIdx.x * 4 + __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    if (wid >= a.B * pairs) return;
+    const int b = wid / pairs, pr = wid % pairs;
     const int L = a.kv_len[b];
-    uint16_t* o = a.out + (int64_t)bh * D;
-    if (!kv_len_ok(L, a)) {
-        o[d] = 0;
-        if (d == 0 && (bh % a.Hq) == 0) report_error(a.err, FP8S_DEV_KVLEN_RANGE);
-        return;
+    const bool ok = kv_len_ok(L, a);
+    if (!ok && pr == 0 && lane == 0) report_error(a.err, FP8S_DEV_KVLEN_RANGE);
+    const int n = ok ? (L + a.chunk - 1) / a.chunk : 0;
+    float val[2] = {0.0f, 0.0f};
+#pragma unroll
+    for (int e = 0; e < 2; ++e) {
+        const int seg = 2 * pr + e;
+        if (seg >= segs) break;
+        const int head = seg * 64 / D, d = seg * 64 % D + lane;
+        const float* p = a.part + ((int64_t)b * a.Hq + head) * a.n_split * (D + 2);
+        if (n > 0) {
+            float M = -INFINITY;
+            for (int i = lane; i < n; i += 64) M = fmaxf(M, p[(int64_t)i * (D + 2)]);
+            M = fmax_xor<64>(M);
+            float den = 0.0f, num = 0.0f;
+            for (int c0 = 0; c0 < n; c0 += 64) {
+                const int i = c0 + lane;
+                float w = 0.0f;
+                if (i < n) {
+                    w = exp2f(p[(int64_t)i * (D + 2)] - M);
+                    den += w * p[(int64_t)i * (D + 2) + 1];
+                }
+                const int cnt = min(64, n - c0);
+                const float* col = p + (int64_t)c0 * (D + 2) + 2 + d;
+#pragma unroll 4
+                for (int j = 0; j < cnt; ++j)
+                    num += __int_as_float(__builtin_amdgcn_readlane(__float_as_int(w), j)) * col[(int64_t)j * (D + 2)];
+            }
+            den = fsum_xor<64>(den);
+            val[e] = bf16_to_f32(f32_to_bf16(num / den));
+        }
+        a.out[((int64_t)b * a.Hq + head) * D + d] = (uint16_t)f32_to_bf16(val[e]);
     }
-    const int n = (L + a.chunk - 1) / a.chunk;
-    const float* p = a.part + (int64_t)bh * a.n_split * (D + 2);
-    float M = -INFINITY;
-    for (int i = 0; i < n; ++i) M = fmaxf(M, p[i * (D + 2)]);
-    float num = 0.0f, den = 0.0f;
-    for (int i = 0; i < n; ++i) {
-        const float w = exp2f(p[i * (D + 2)] - M);
-        den += w * p[i * (D + 2) + 1];
-        num += w * p[i * (D + 2) + 2 + d];
-    }
-    o[d] = (uint16_t)f32_to_bf16(num / den);
+    if (a.qo) quant_out_wave(a, b, pr, val[0], val[1], lane);
 }
 
 struct AttnPlan { int n_split, chunk; };
@@ -237,6 +297,65 @@ static void launch_split(dim3 grid, hipStream_t st, const AttnArgs& a) {
         FP8S_LAUNCH("attn_split", (attn_split_kernel<D, G, false>), grid, dim3(256), 0, st, a);
 }
 
+// The attention with, optionally (qo non-null), its output also quantised
+// in bsgemm 1x128 groups into a GEMM operand: fragments qo[mt][kb] of 16 rows
+// x 128 bytes in MFMA operand order and scales so[mt][kb][16], kb < qo_KB =
+// Hq * D / 128, for the rows b < B.
+int gqa_decode_attn_ex(const uint16_t* q, const uint16_t* k_cache, const uint16_t* v_cache, int64_t stride_b,
+                       int64_t stride_h, int64_t stride_t, const int32_t* kv_len, int64_t B, int32_t Hq, int32_t Hkv,
+                       int32_t D, int64_t cap, int64_t hint, float softmax_scale, uint16_t* out, uint8_t* qo, float* so,
+                       void* workspace, size_t workspace_bytes, int32_t* err_flag, void* stream) {
+    FP8S_REQUIRE(q && k_cache && v_cache && kv_len && out, FP8S_EINVAL, "gqa_decode_attn: null pointer");
+    FP8S_REQUIRE(B >= 1 && Hq >= 1 && Hkv >= 1 && cap >= 1 && hint >= 1, FP8S_EINVAL,
+                 "gqa_decode_attn: sizes must be positive");
+    FP8S_REQUIRE(Hq % Hkv == 0, FP8S_EINVAL, "gqa_decode_attn: Hq=%d is not a multiple of Hkv=%d", Hq, Hkv);
+    const int G = Hq / Hkv;
+    FP8S_REQUIRE(D == 64 || D == 128, FP8S_EUNSUPPORTED, "gqa_decode_attn: head dim %d (64 or 128 supported)", D);
+    FP8S_REQUIRE(G == 1 || G == 2 || G == 4 || G == 8, FP8S_EUNSUPPORTED,
+                 "gqa_decode_attn: group size %d (1, 2, 4 or 8 supported)", G);
+    FP8S_REQUIRE(stride_t >= D && stride_t % 8 == 0 && stride_h % 8 == 0 && stride_b % 8 == 0, FP8S_EINVAL,
+                 "gqa_decode_attn: strides must keep rows 16-byte aligned (multiples of 8) and stride_t >= D");
+    FP8S_REQUIRE(aligned16(q) && aligned16(k_cache) && aligned16(v_cache) && aligned16(out), FP8S_EINVAL,
+                 "gqa_decode_attn: q, caches and out must be 16-byte aligned");
+    FP8S_REQUIRE(B * Hkv <= (1ll << 24), FP8S_EUNSUPPORTED, "gqa_decode_attn: batch too large");
+    FP8S_REQUIRE(!qo || (so && (G * D) % 128 == 0), FP8S_EUNSUPPORTED,
+                 "gqa_decode_attn: a quantised output needs whole 128-column groups per KV head");
+    if (hint > cap) hint = cap;
+    const AttnPlan p = plan_attn(B, Hkv, hint);
+    const size_t need = (size_t)B * Hq * p.n_split * (D + 2) * sizeof(float);
+    FP8S_REQUIRE(workspace && aligned16(workspace), FP8S_EWORKSPACE, "gqa_decode_attn: workspace missing or unaligned");
+    FP8S_REQUIRE(workspace_bytes >= need, FP8S_EWORKSPACE, "gqa_decode_attn: workspace %zu < required %zu bytes",
+                 workspace_bytes, need);
+    AttnArgs a;
+    a.q = q; a.k = k_cache; a.v = v_cache;
+    a.sb = stride_b; a.sh = stride_h; a.st = stride_t;
+    a.kv_len = kv_len;
+    a.B = (int)B; a.Hq = Hq; a.Hkv = Hkv; a.n_split = p.n_split; a.chunk = p.chunk;
+    a.cap = cap; a.hint = hint;
+    a.scale_log2 = softmax_scale * 1.4426950408889634f;
+    a.part = static_cast<float*>(workspace);
+    a.out = out;
+    a.err = err_flag;
+    a.qo = qo; a.so = so; a.qo_KB = Hq * D / 128;
+    hipStream_t st = as_stream(stream);
+    const dim3 grid((unsigned)(B * Hkv * p.n_split));
+#define FP8S_ATTN_CASE(DD, GG) \
+    if (D == DD && G == GG) launch_split<DD, GG>(grid, st, a);
+    FP8S_ATTN_CASE(64, 1) FP8S_ATTN_CASE(64, 2) FP8S_ATTN_CASE(64, 4) FP8S_ATTN_CASE(64, 8)
+    FP8S_ATTN_CASE(128, 1) FP8S_ATTN_CASE(128, 2) FP8S_ATTN_CASE(128, 4) FP8S_ATTN_CASE(128, 8)
+#undef FP8S_ATTN_CASE
+    int rc = check_launch("gqa_decode_attn (split)");
+    if (rc) return rc;
+    if (p.n_split == 1) return FP8S_OK;        // the split kernel wrote the output
+    const int64_t waves = B * ((Hq * D / 64 + 1) / 2);
+    const dim3 mgrid((unsigned)((waves + 3) / 4));
+    if (D == 64)
+        FP8S_LAUNCH("attn_merge", attn_merge_kernel<64>, mgrid, dim3(256), 0, st, a);
+    else
+        FP8S_LAUNCH("attn_merge", attn_merge_kernel<128>, mgrid, dim3(256), 0, st, a);
+    return check_launch("gqa_decode_attn (merge)");
+}
+
 }  // namespace fp8s
 
 using namespace fp8s;
@@ -254,48 +373,6 @@ extern "C" int gqa_decode_attn(const uint16_t* q, const uint16_t* k_cache, const
                                float softmax_scale, uint16_t* out, void* workspace, size_t workspace_bytes,
                                int32_t* err_flag, void* stream) {
     clear_error();
-    FP8S_REQUIRE(q && k_cache && v_cache && kv_len && out, FP8S_EINVAL, "gqa_decode_attn: null pointer");
-    FP8S_REQUIRE(B >= 1 && Hq >= 1 && Hkv >= 1 && cap >= 1 && hint >= 1, FP8S_EINVAL,
-                 "gqa_decode_attn: sizes must be positive");
-    FP8S_REQUIRE(Hq % Hkv == 0, FP8S_EINVAL, "gqa_decode_attn: Hq=%d is not a multiple of Hkv=%d", Hq, Hkv);
-    const int G = Hq / Hkv;
-    FP8S_REQUIRE(D == 64 || D == 128, FP8S_EUNSUPPORTED, "gqa_decode_attn: head dim %d (64 or 128 supported)", D);
-    FP8S_REQUIRE(G == 1 || G == 2 || G == 4 || G == 8, FP8S_EUNSUPPORTED,
-                 "gqa_decode_attn: group size %d (1, 2, 4 or 8 supported)", G);
-    FP8S_REQUIRE(stride_t >= D && stride_t % 8 == 0 && stride_h % 8 == 0 && stride_b % 8 == 0, FP8S_EINVAL,
-                 "gqa_decode_attn: strides must keep rows 16-byte aligned (multiples of 8) and stride_t >= D");
-    FP8S_REQUIRE(aligned16(q) && aligned16(k_cache) && aligned16(v_cache) && aligned16(out), FP8S_EINVAL,
-                 "gqa_decode_attn: q, caches and out must be 16-byte aligned");
-    FP8S_REQUIRE(B * Hkv <= (1ll << 24), FP8S_EUNSUPPORTED, "gqa_decode_attn: batch too large");
-    if (hint > cap) hint = cap;
-    const AttnPlan p = plan_attn(B, Hkv, hint);
-    const size_t need = (size_t)B * Hq * p.n_split * (D + 2) * sizeof(float);
-    FP8S_REQUIRE(workspace && aligned16(workspace), FP8S_EWORKSPACE, "gqa_decode_attn: workspace missing or unaligned");
-    FP8S_REQUIRE(workspace_bytes >= need, FP8S_EWORKSPACE, "gqa_decode_attn: workspace %zu < required %zu bytes",
-                 workspace_bytes, need);
-    AttnArgs a;
-    a.q = q; a.k = k_cache; a.v = v_cache;
-    a.sb = stride_b; a.sh = stride_h; a.st = stride_t;
-    a.kv_len = kv_len;
-    a.B = (int)B; a.Hq = Hq; a.Hkv = Hkv; a.n_split = p.n_split; a.chunk = p.chunk;
-    a.cap = cap; a.hint = hint;
-    a.scale_log2 = softmax_scale * 1.4426950408889634f;
-    a.part = static_cast<float*>(workspace);
-    a.out = out;
-    a.err = err_flag;
-    hipStream_t st = as_stream(stream);
-    const dim3 grid((unsigned)(B * Hkv * p.n_split));
-#define FP8S_ATTN_CASE(DD, GG) \
-    if (D == DD && G == GG) launch_split<DD, GG>(grid, st, a);
-    FP8S_ATTN_CASE(64, 1) FP8S_ATTN_CASE(64, 2) FP8S_ATTN_CASE(64, 4) FP8S_ATTN_CASE(64, 8)
-    FP8S_ATTN_CASE(128, 1) FP8S_ATTN_CASE(128, 2) FP8S_ATTN_CASE(128, 4) FP8S_ATTN_CASE(128, 8)
-#undef FP8S_ATTN_CASE
-    int rc = check_launch("gqa_decode_attn (split)");
-    if (rc) return rc;
-    if (p.n_split == 1) return FP8S_OK;        // the split kernel wrote the output
-    if (D == 64)
-        FP8S_LAUNCH("attn_merge", attn_merge_kernel<64>, dim3((unsigned)(B * Hq)), dim3(64), 0, st, a);
-    else
-        FP8S_LAUNCH("attn_merge", attn_merge_kernel<128>, dim3((unsigned)(B * Hq)), dim3(128), 0, st, a);
-    return check_launch("gqa_decode_attn (merge)");
+    return gqa_decode_attn_ex(q, k_cache, v_cache, stride_b, stride_h, stride_t, kv_len, B, Hq, Hkv, D, cap, hint,
+                              softmax_scale, out, nullptr, nullptr, workspace, workspace_bytes, err_flag, stream);
 }

@@ -248,11 +248,20 @@ static int run_block(const StepCtx& c, const fp8s_block_weights& L, const uint16
     int rc = qkv_proj_kv_append(xin, c.B, H, H, L.norm_attn, m->rms_eps, L.qkv, m->n_heads, m->n_kv_heads,
                                 m->head_dim, q, kc, vc, sb, sh, stt, kv_len, cap, qlw, c.p->ql_bytes, c.err, c.stream);
     if (rc) return step_error(rc, "qkv projection");
-    rc = gqa_decode_attn(q, kc, vc, sb, sh, stt, kv_len, c.B, m->n_heads, m->n_kv_heads, m->head_dim, cap, hint,
-                         1.0f / sqrtf((float)m->head_dim), ao, c.ws + c.p->off_attn, c.p->attn_bytes, c.err, c.stream);
+    // The attention quantises its own output straight into the output
+    // projection's operand when every KV head's query group covers whole
+    // 128-column quantisation groups; otherwise the projection quantises it.
+    const bool fuse = (m->n_heads / m->n_kv_heads) * m->head_dim % 128 == 0;
+    uint8_t* qo = nullptr;
+    float* so = nullptr;
+    if (fuse && (rc = qlinear_operand(c.B, H, A, qlw, c.p->ql_bytes, &qo, &so))) return step_error(rc, "attention");
+    rc = gqa_decode_attn_ex(q, kc, vc, sb, sh, stt, kv_len, c.B, m->n_heads, m->n_kv_heads, m->head_dim, cap, hint,
+                            1.0f / sqrtf((float)m->head_dim), ao, qo, so, c.ws + c.p->off_attn, c.p->attn_bytes, c.err,
+                            c.stream);
     if (rc) return step_error(rc, "attention");
-    rc = qlinear_fp8(ao, c.B, A, A, nullptr, 0.0f, L.o, H, xin, H, FP8S_OUT_BF16, xmid, H, qlw, c.p->ql_bytes,
-                     c.stream);
+    rc = fuse ? qlinear_fp8_prequant(c.B, A, L.o, H, xin, H, xmid, H, qlw, c.p->ql_bytes, c.stream)
+              : qlinear_fp8(ao, c.B, A, A, nullptr, 0.0f, L.o, H, xin, H, FP8S_OUT_BF16, xmid, H, qlw, c.p->ql_bytes,
+                            c.stream);
     if (rc) return step_error(rc, "output projection");
     rc = swiglu_mlp_fp8_ex(xmid, c.B, H, m->inter, FP8S_MLP_BSGEMM, L.gate, L.up, L.down, L.norm_mlp, m->rms_eps,
                            xmid, xout, c.ws + c.p->off_mlp, c.p->mlp_bytes, c.stream);

@@ -19,6 +19,7 @@
 #include "common.h"
 #include "gemm_tiles.h"
 #include "host_common.h"
+#include "internal.h"
 #include "profile.h"
 
 namespace fp8s {
@@ -210,8 +211,10 @@ static void ql_launch(const QlPlan& p, QlArgs& a, const uint16_t* x, int64_t ld_
     a.sx = reinterpret_cast<const float*>(ws + p.off_sx);
     a.part = reinterpret_cast<float*>(ws + p.off_part);
     a.cnt = reinterpret_cast<int*>(ws + p.off_ctrl);
-    const ActQuantArgs xa{x, ld_x, a.M, (int)K, p.KB, norm_w, eps, ws + p.off_qx, ws + p.off_sx};
-    FP8S_LAUNCH("ql_act_quant", act_quant_kernel<FP8S_MLP_BSGEMM>, dim3(p.MT * p.KB), dim3(256), 0, st, xa);
+    if (x) {                                   // else the operand is already in place
+        const ActQuantArgs xa{x, ld_x, a.M, (int)K, p.KB, norm_w, eps, ws + p.off_qx, ws + p.off_sx};
+        FP8S_LAUNCH("ql_act_quant", act_quant_kernel<FP8S_MLP_BSGEMM>, dim3(p.MT * p.KB), dim3(256), 0, st, xa);
+    }
     const dim3 grid(p.NT * p.S), blk(256);
     switch (p.MT) {
     case 1: FP8S_LAUNCH("qlinear", qlinear_kernel<1>, grid, blk, p.lds, st, a); break;
@@ -225,6 +228,37 @@ static void ql_weight(QlArgs& a, const fp8s_qweight& w) {
     a.w = w.w; a.ldw = w.ld_w;
     a.sw = reinterpret_cast<const float*>(w.scale);
     a.sw_r = w.scale_stride_row; a.sw_c = w.scale_stride_colblk;
+}
+
+int qlinear_operand(int64_t M, int64_t N, int64_t K, void* workspace, size_t workspace_bytes, uint8_t** qx,
+                    float** sx) {
+    FP8S_REQUIRE(ql_shape_ok(M, N, K), FP8S_EINVAL, "qlinear_operand: unsupported shape");
+    const QlPlan p = plan_ql(M, N, K);
+    FP8S_REQUIRE(workspace && aligned16(workspace) && workspace_bytes >= p.total, FP8S_EWORKSPACE,
+                 "qlinear_operand: workspace missing, unaligned or too small");
+    *qx = static_cast<uint8_t*>(workspace) + p.off_qx;
+    *sx = reinterpret_cast<float*>(static_cast<uint8_t*>(workspace) + p.off_sx);
+    return FP8S_OK;
+}
+
+int qlinear_fp8_prequant(int64_t M, int64_t K, fp8s_qweight w, int64_t N, const uint16_t* residual, int64_t ld_res,
+                         uint16_t* y, int64_t ld_y, void* workspace, size_t workspace_bytes, void* stream) {
+    // The checks of qlinear_fp8 with a stand-in activation pointer (never read).
+    alignas(16) static const uint16_t kNoX[8] = {};
+    QlPlan p;
+    int rc = ql_check_common("qlinear_fp8_prequant", kNoX, M, K, K, nullptr, 0.0f, w, N, workspace, workspace_bytes,
+                             &p);
+    if (rc) return rc;
+    FP8S_REQUIRE(y && ld_y >= N, FP8S_EINVAL, "qlinear_fp8_prequant: null y or ld_y < N");
+    FP8S_REQUIRE(!residual || ld_res >= N, FP8S_EINVAL, "qlinear_fp8_prequant: ld_res < N");
+    QlArgs a{};
+    a.M = (int)M; a.N = (int)N;
+    ql_weight(a, w);
+    a.epi = EPI_BF16;
+    a.y = y; a.ldy = ld_y;
+    a.res = residual; a.ld_res = ld_res;
+    ql_launch(p, a, nullptr, 0, K, nullptr, 0.0f, workspace, as_stream(stream));
+    return check_launch("qlinear_fp8_prequant");
 }
 
 }  // namespace fp8s
