@@ -82,8 +82,13 @@ __global__ __launch_bounds__(256) void attn_split_kernel(AttnArgs a) {
     __shared__ float s_red[4][G][D];
     __shared__ float s_ml[G][2];
 
-    const int sp = blockIdx.x % a.n_split;
-    const int bg = blockIdx.x / a.n_split;
+    // Chunk-major order: consecutive workgroups (which the dispatcher deals
+    // round-robin to the 8 XCDs) belong to different (sequence, KV head)
+    // pairs, so every XCD gets a fair share of long and short prefixes.  With
+    // the chunk index fastest, chunk i of every sequence would land on one
+    // XCD and the XCD holding the first chunks would carry most of the work.
+    const int bg = blockIdx.x % (a.B * a.Hkv);
+    const int sp = blockIdx.x / (a.B * a.Hkv);
     const int g = bg % a.Hkv, b = bg / a.Hkv;
     const int L = a.kv_len[b];
     if (!kv_len_ok(L, a)) {                    // the merge writes zeros and reports
