@@ -29,7 +29,7 @@
 
 namespace fp8s {
 
-constexpr int kMaxChunk = 512;
+constexpr int kMaxChunk = 1024;
 
 struct AttnArgs {
     const uint16_t* q;
@@ -229,12 +229,15 @@ __global__ __launch_bounds__(256) void attn_split_kernel(AttnArgs a) {
 
 // Merge the chunks of one (sequence, query head): out = sum_i 2^(m_i - M) acc_i
 // / sum_i 2^(m_i - M) l_i over the chunks that hold positions.  One wave per
-// (sequence, 128 output columns): column lane and lane + 64 of the group, each
-// of them in one head (D is 64 or 128).  Lane i holds chunk i's statistics;
-// its weight reaches the other lanes by readlane while every lane streams
-// its own column of the chunk accumulators.
+// (sequence, 128 output columns): value A is column lane of the group, value
+// B column lane + 64 (one head for D = 128, two heads for D = 64).  Lane i
+// holds chunk i's statistics and its weight reaches the other lanes by
+// readlane; the accumulators of the first kU chunks are loaded together with
+// the statistics, so the common case costs one memory round trip.
 template <int D>
 __global__ __launch_bounds__(256) void attn_merge_kernel(AttnArgs a) {
+    constexpr int kU = 8;
+    constexpr int RS = D + 2;                    // floats per (head, chunk) record
     const int lane = threadIdx.x & 63;
     const int segs = a.Hq * D / 64;              // 64-column segments of an output row
     const int pairs = (segs + 1) / 2;
@@ -245,37 +248,63 @@ __global__ __launch_bounds__(256) void attn_merge_kernel(AttnArgs a) {
     const bool ok = kv_len_ok(L, a);
     if (!ok && pr == 0 && lane == 0) report_error(a.err, FP8S_DEV_KVLEN_RANGE);
     const int n = ok ? (L + a.chunk - 1) / a.chunk : 0;
-    float val[2] = {0.0f, 0.0f};
+    const bool hasB = 2 * pr + 1 < segs;
+    const int hA = 128 * pr / D, dA = 128 * pr % D + lane;
+    const int hB = hasB ? (128 * pr + 64) / D : hA, dB = hasB ? (128 * pr + 64) % D + lane : dA;
+    const float* pA = a.part + ((int64_t)b * a.Hq + hA) * a.n_split * RS;
+    const float* pB = a.part + ((int64_t)b * a.Hq + hB) * a.n_split * RS;
+    float cA[kU], cB[kU];
 #pragma unroll
-    for (int e = 0; e < 2; ++e) {
-        const int seg = 2 * pr + e;
-        if (seg >= segs) break;
-        const int head = seg * 64 / D, d = seg * 64 % D + lane;
-        const float* p = a.part + ((int64_t)b * a.Hq + head) * a.n_split * (D + 2);
-        if (n > 0) {
-            float M = -INFINITY;
-            for (int i = lane; i < n; i += 64) M = fmaxf(M, p[(int64_t)i * (D + 2)]);
-            M = fmax_xor<64>(M);
-            float den = 0.0f, num = 0.0f;
-            for (int c0 = 0; c0 < n; c0 += 64) {
-                const int i = c0 + lane;
-                float w = 0.0f;
-                if (i < n) {
-                    w = exp2f(p[(int64_t)i * (D + 2)] - M);
-                    den += w * p[(int64_t)i * (D + 2) + 1];
-                }
-                const int cnt = min(64, n - c0);
-                const float* col = p + (int64_t)c0 * (D + 2) + 2 + d;
-#pragma unroll 4
-                for (int j = 0; j < cnt; ++j)
-                    num += __int_as_float(__builtin_amdgcn_readlane(__float_as_int(w), j)) * col[(int64_t)j * (D + 2)];
-            }
-            den = fsum_xor<64>(den);
-            val[e] = bf16_to_f32(f32_to_bf16(num / den));
-        }
-        a.out[((int64_t)b * a.Hq + head) * D + d] = (uint16_t)f32_to_bf16(val[e]);
+    for (int j = 0; j < kU; ++j) {
+        cA[j] = j < n ? pA[j * RS + 2 + dA] : 0.0f;
+        cB[j] = j < n ? pB[j * RS + 2 + dB] : 0.0f;
     }
-    if (a.qo) quant_out_wave(a, b, pr, val[0], val[1], lane);
+    // statistics of head A (and of head B when it differs)
+    const float mA = lane < n ? pA[lane * RS] : -INFINITY, lA = lane < n ? pA[lane * RS + 1] : 0.0f;
+    float mB = mA, lB = lA;
+    if (D != 128) {
+        mB = lane < n ? pB[lane * RS] : -INFINITY;
+        lB = lane < n ? pB[lane * RS + 1] : 0.0f;
+    }
+    float MA = mA, MB = mB;
+    for (int i = lane + 64; i < n; i += 64) {
+        MA = fmaxf(MA, pA[(int64_t)i * RS]);
+        MB = fmaxf(MB, pB[(int64_t)i * RS]);
+    }
+    MA = fmax_xor<64>(MA);
+    MB = D == 128 ? MA : fmax_xor<64>(MB);
+    const float wA = lane < n ? exp2f(mA - MA) : 0.0f;
+    const float wB = D == 128 ? wA : (lane < n ? exp2f(mB - MB) : 0.0f);
+    float denA = wA * lA, denB = wB * lB;
+    for (int i = lane + 64; i < n; i += 64) {
+        denA += exp2f(pA[(int64_t)i * RS] - MA) * pA[(int64_t)i * RS + 1];
+        denB += exp2f(pB[(int64_t)i * RS] - MB) * pB[(int64_t)i * RS + 1];
+    }
+    denA = fsum_xor<64>(denA);
+    denB = D == 128 ? denA : fsum_xor<64>(denB);
+    float numA = 0.0f, numB = 0.0f;
+#pragma unroll
+    for (int j = 0; j < kU; ++j) {               // chunks j >= n carry zero weight and zero values
+        numA += __int_as_float(__builtin_amdgcn_readlane(__float_as_int(wA), j)) * cA[j];
+        numB += __int_as_float(__builtin_amdgcn_readlane(__float_as_int(wB), j)) * cB[j];
+    }
+    for (int j = kU; j < n; ++j) {
+        float wjA, wjB;
+        if (j < 64) {
+            wjA = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(wA), j));
+            wjB = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(wB), j));
+        } else {
+            wjA = exp2f(pA[(int64_t)j * RS] - MA);
+            wjB = exp2f(pB[(int64_t)j * RS] - MB);
+        }
+        numA += wjA * pA[(int64_t)j * RS + 2 + dA];
+        numB += wjB * pB[(int64_t)j * RS + 2 + dB];
+    }
+    const float vA = n > 0 ? bf16_to_f32(f32_to_bf16(numA / denA)) : 0.0f;
+    const float vB = n > 0 ? bf16_to_f32(f32_to_bf16(numB / denB)) : 0.0f;
+    a.out[((int64_t)b * a.Hq + hA) * D + dA] = (uint16_t)f32_to_bf16(vA);
+    if (hasB) a.out[((int64_t)b * a.Hq + hB) * D + dB] = (uint16_t)f32_to_bf16(vB);
+    if (a.qo) quant_out_wave(a, b, pr, vA, vB, lane);
 }
 
 struct AttnPlan { int n_split, chunk; };
