@@ -221,37 +221,41 @@ def step_launch_plan(cfg, kv_len):
     fused = (c.n_heads // c.n_kv_heads) * c.head_dim % 128 == 0
     oq = B * A + asc(A) if fused else 0
 
+    # the row finisher: residual (+ deferred partials) -> residual stream out,
+    # RMSNorm, 1x128 quantisation of the next projection's operand
+    def finish(with_residual):
+        return ("row_finish", B * H * 2 + (B * H * 2 if with_residual else 0) + H * 2 + B * H + asc(H))
+
     def block(kv_bytes, single):
         attn = ([("attn_single", kv_bytes + 2 * B * A * 2 + 4 * B + oq)] if single else
                 [("attn_split", kv_bytes + B * A * 2 + 4 * B), ("attn_merge", B * A * 2 + 4 * B + oq)])
-        return [act_quant("ql_act_quant", H, True),
-                ("qlinear", NQKV * H + ws(NQKV, H) + B * H + asc(H) + B * NQKV * 2)] + attn + (
+        return [("qlinear", NQKV * H + ws(NQKV, H) + B * H + asc(H) + B * NQKV * 2)] + attn + (
                 [] if fused else [act_quant("ql_act_quant", A, False)]) + [
-                ("qlinear", H * A + ws(H, A) + B * A + asc(A) + 2 * B * H * 2),
-                act_quant("mlp_xq", H, True),
+                ("qlinear", H * A + ws(H, A) + B * A + asc(A)),
+                finish(True),
                 ("mlp_gu", 2 * I * H + 2 * ws(I, H) + B * H + asc(H) + 2 * B * I * 4),
                 ("mlp_hq", 2 * B * I * 4 + B * I + asc(I)),
-                (down, H * I + ws(H, I) + B * I + asc(I) + 2 * B * H * 2)]
+                (down, H * I + ws(H, I) + B * I + asc(I)),
+                finish(True)]
 
-    def head(norm):
-        return [act_quant("ql_act_quant", H, norm),
-                ("qlinear", V * H + ws(V, H) + B * H + asc(H) + B * V * 4),
+    def head():
+        return [("qlinear", V * H + ws(V, H) + B * H + asc(H) + B * V * 4),
                 ("argmax", B * V * 4 + 4 * B)]
 
-    out = [("embed_sum", B * C * H * 2 + B * H * 2 + 4 * B * C)]
+    out = [("embed_sum", B * C * H * 2 + B * H * 2 + 4 * B * C), finish(False)]
     slow_kv = int(np.sum(kv_len, dtype=np.int64)) * KVD * 2 * 2
     # the slow AR's prefixes are split over chunks and merged; the fast AR's
     # few-slot caches are one chunk, written by the split kernel itself
     for _ in range(c.n_slow_layers):
         out += block(slow_kv, False)
-    out.append(("rmsnorm", 2 * B * H * 2 + H * 2))
-    out += head(False)
+    out += head()
     out.append(("fill_steps", (C - 1) * B * 4))
     for p in range(C - 1):
         out.append(("embed_sum", B * H * 2 * (3 if p == 0 else 2) + 4 * B))
+        out.append(finish(False))
         for _ in range(c.n_fast_layers):
             out += block((p + 1) * B * KVD * 2 * 2, True)
-        out += head(True)
+        out += head()
     return out
 
 

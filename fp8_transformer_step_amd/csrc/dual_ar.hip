@@ -21,6 +21,7 @@
 #include <string>
 
 #include "common.h"
+#include "gemm_tiles.h"
 #include "host_common.h"
 #include "internal.h"
 #include "profile.h"
@@ -112,39 +113,102 @@ __global__ __launch_bounds__(256) void argmax_kernel(const float* logits, int64_
     }
 }
 
-// One workgroup per row: out = bf16(x / sqrt(mean(x^2) + eps) * w).
-__global__ __launch_bounds__(256) void rmsnorm_kernel(const uint16_t* x, const uint16_t* w, int64_t H, float eps,
-                                                      uint16_t* out) {
+// ---- row finisher -------------------------------------------------------------
+// One workgroup per row m, 8 columns per thread and chunk.  With the split
+// partials of a deferred projection: x = bf16(sum_s part_s + base), the
+// projection's reduction in split order plus its residual, written to xout
+// (the residual stream); without: x = base.  Then the operand of the next
+// projection: y = bf16(x / sqrt(mean(x^2) + eps) * w) (the RMSNorm in front
+// of it, written to xn when asked), quantised in 1x128 groups into MFMA
+// operand fragments.  The 16 chunks of a quantisation group belong to the
+// 16 lanes of one DPP row.
+constexpr int kFinishChunks = 2;          // chunks per thread: H <= 4096
+constexpr int kFinishBatch = 8;           // split partials loaded at once
+
+struct FinishArgs {
+    const float* part;                    // split partials (SplitPartials layout) or null
+    int S, cols;
+    const uint16_t* base;                 // residual, or the row itself when part is null
+    uint16_t* xout;                       // x (with partials; may be null)
+    const uint16_t* norm_w;
+    float eps;
+    uint16_t* xn;                         // optional normalised row
+    uint8_t* qx;                          // operand fragments [mt][kb] and fp32 scales [mt][kb][16]
+    float* sx;
+    int M, H, KB;
+};
+
+__global__ __launch_bounds__(256) void finish_kernel(FinishArgs a) {
     __shared__ float s_ss[4];
-    const int64_t b = blockIdx.x;
-    const uint16_t* xr = x + b * H;
-    float ss = 0.0f;
-    for (int64_t c8 = 8 * (int64_t)threadIdx.x; c8 < H; c8 += 8 * 256) {
-        const uint4 v = *reinterpret_cast<const uint4*>(xr + c8);
-        const uint32_t u[4] = {v.x, v.y, v.z, v.w};
+    const int m = blockIdx.x, t = threadIdx.x;
+    const int nch = a.H / 8;
+    float x[kFinishChunks][8];
+    uint4 wn[kFinishChunks];                  // the norm weights, requested with the row
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            const float lo = bf16_to_f32(u[i] & 0xFFFFu), hi = bf16_to_f32(u[i] >> 16);
-            ss = fmaf(lo, lo, ss);
-            ss = fmaf(hi, hi, ss);
+    for (int p = 0; p < kFinishChunks; ++p)
+        wn[p] = *reinterpret_cast<const uint4*>(a.norm_w + 8 * min(t + 256 * p, nch - 1));
+    float ss = 0.0f;
+#pragma unroll
+    for (int p = 0; p < kFinishChunks; ++p) {
+        const int c = t + 256 * p;
+        if (c >= nch) continue;
+        float v[8];
+        unpack_bf16x8(*reinterpret_cast<const uint4*>(a.base + (int64_t)m * a.H + 8 * c), v);
+        if (a.part) {
+            const int n = 8 * c;
+            const float* ps = a.part + ((int64_t)(n / a.cols) * a.S * a.M + m) * a.cols + n % a.cols;
+            // the loads of kFinishBatch splits are issued together, then
+            // added in split order
+            float acc[8] = {0, 0, 0, 0, 0, 0, 0, 0};
+            const int64_t ss_ = (int64_t)a.M * a.cols;
+            for (int s0 = 0; s0 < a.S; s0 += kFinishBatch) {
+                float4 pv[kFinishBatch][2];
+#pragma unroll
+                for (int u = 0; u < kFinishBatch; ++u) {
+                    const float* q = ps + (int64_t)min(s0 + u, a.S - 1) * ss_;
+                    pv[u][0] = *reinterpret_cast<const float4*>(q);
+                    pv[u][1] = *reinterpret_cast<const float4*>(q + 4);
+                }
+#pragma unroll
+                for (int u = 0; u < kFinishBatch; ++u) {
+                    if (s0 + u >= a.S) break;
+                    acc[0] += pv[u][0].x; acc[1] += pv[u][0].y; acc[2] += pv[u][0].z; acc[3] += pv[u][0].w;
+                    acc[4] += pv[u][1].x; acc[5] += pv[u][1].y; acc[6] += pv[u][1].z; acc[7] += pv[u][1].w;
+                }
+            }
+            uint32_t o[4];
+#pragma unroll
+            for (int i = 0; i < 8; ++i) v[i] = bf16_to_f32(f32_to_bf16(acc[i] + v[i]));
+#pragma unroll
+            for (int i = 0; i < 4; ++i) o[i] = f32_to_bf16(v[2 * i]) | (f32_to_bf16(v[2 * i + 1]) << 16);
+            if (a.xout) *reinterpret_cast<uint4*>(a.xout + (int64_t)m * a.H + n) = make_uint4(o[0], o[1], o[2], o[3]);
+        }
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+            ss = fmaf(v[i], v[i], ss);
+            x[p][i] = v[i];
         }
     }
     ss = fsum_xor<kWave>(ss);
-    if ((threadIdx.x & 63) == 0) s_ss[threadIdx.x >> 6] = ss;
+    if ((t & 63) == 0) s_ss[t >> 6] = ss;
     __syncthreads();
-    const float inv = 1.0f / sqrtf((s_ss[0] + s_ss[1] + s_ss[2] + s_ss[3]) / (float)H + eps);
-    for (int64_t c8 = 8 * (int64_t)threadIdx.x; c8 < H; c8 += 8 * 256) {
-        const uint4 v = *reinterpret_cast<const uint4*>(xr + c8);
-        const uint4 g = *reinterpret_cast<const uint4*>(w + c8);
-        const uint32_t u[4] = {v.x, v.y, v.z, v.w}, gw[4] = {g.x, g.y, g.z, g.w};
-        uint32_t o[4];
+    const float inv = 1.0f / sqrtf((s_ss[0] + s_ss[1] + s_ss[2] + s_ss[3]) / (float)a.H + a.eps);
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            const float lo = bf16_to_f32(u[i] & 0xFFFFu) * inv * bf16_to_f32(gw[i] & 0xFFFFu);
-            const float hi = bf16_to_f32(u[i] >> 16) * inv * bf16_to_f32(gw[i] >> 16);
-            o[i] = f32_to_bf16(lo) | (f32_to_bf16(hi) << 16);
+    for (int p = 0; p < kFinishChunks; ++p) {
+        const int c = t + 256 * p;
+        if (c >= nch) continue;
+        float w[8], f[8];
+        unpack_bf16x8(wn[p], w);
+#pragma unroll
+        for (int i = 0; i < 8; ++i) f[i] = bf16_to_f32(f32_to_bf16(x[p][i] * inv * w[i]));
+        if (a.xn) {
+            uint32_t o[4];
+#pragma unroll
+            for (int i = 0; i < 4; ++i) o[i] = f32_to_bf16(f[2 * i]) | (f32_to_bf16(f[2 * i + 1]) << 16);
+            *reinterpret_cast<uint4*>(a.xn + (int64_t)m * a.H + 8 * c) = make_uint4(o[0], o[1], o[2], o[3]);
         }
-        *reinterpret_cast<uint4*>(out + b * H + c8) = make_uint4(o[0], o[1], o[2], o[3]);
+        quant_chunk<FP8S_MLP_BSGEMM>(f, a.qx + frag_off(m >> 4, c >> 4, a.KB),
+                                     scale_slot<FP8S_MLP_BSGEMM>(a.sx, m >> 4, c >> 4, a.KB), m & 15, c & 15);
     }
 }
 
@@ -177,6 +241,8 @@ static int check_model(const fp8s_dual_ar_model* m, int64_t B, int64_t hint) {
                  "dual_ar_decode_step: hidden and inter must be positive multiples of 128");
     FP8S_REQUIRE(m->n_heads >= 1 && m->n_kv_heads >= 1 && m->n_heads % m->n_kv_heads == 0, FP8S_EINVAL,
                  "dual_ar_decode_step: n_heads must be a multiple of n_kv_heads");
+    FP8S_REQUIRE(m->hidden <= 8 * 256 * kFinishChunks, FP8S_EUNSUPPORTED, "dual_ar_decode_step: hidden %lld > %d",
+                 (long long)m->hidden, 8 * 256 * kFinishChunks);
     FP8S_REQUIRE(m->head_dim == 64 || m->head_dim == 128, FP8S_EUNSUPPORTED,
                  "dual_ar_decode_step: head_dim %d (64 or 128)", m->head_dim);
     FP8S_REQUIRE(((int64_t)m->n_heads * m->head_dim) % 128 == 0, FP8S_EINVAL,
@@ -235,18 +301,48 @@ struct StepCtx {
     void* stream;
 };
 
+// The operand of the next projection from the row stream: x = base (+ the
+// split partials of a deferred projection, written to xout), RMSNorm with
+// norm_w, 1x128 quantisation into qx / sx (and the normalised rows into xn).
+static int finish_rows(const StepCtx& c, const SplitPartials* part, const uint16_t* base, uint16_t* xout,
+                       const uint16_t* norm_w, uint16_t* xn, uint8_t* qx, void* sx, const char* where) {
+    FinishArgs a;
+    a.part = part ? part->part : nullptr;
+    a.S = part ? part->S : 0;
+    a.cols = part ? part->cols : 8;
+    a.base = base; a.xout = xout; a.norm_w = norm_w; a.eps = c.m->rms_eps; a.xn = xn;
+    a.qx = qx; a.sx = static_cast<float*>(sx);
+    a.M = (int)c.B; a.H = (int)c.m->hidden; a.KB = (int)(c.m->hidden / 128);
+    FP8S_LAUNCH("row_finish", finish_kernel, dim3((unsigned)c.B), dim3(256), 0, as_stream(c.stream), a);
+    const int rc = check_launch("row finish");
+    return rc ? step_error(rc, where) : FP8S_OK;
+}
+
+// The operand of the QKV and head projections (K = hidden) in the qlinear
+// workspace, and the MLP's in its workspace.
+static int ql_operand(const StepCtx& c, uint8_t** qx, float** sx) {
+    const fp8s_dual_ar_model* m = c.m;
+    const int64_t NQKV = (int64_t)(m->n_heads + 2 * m->n_kv_heads) * m->head_dim;
+    return qlinear_operand(c.B, NQKV, m->hidden, c.ws + c.p->off_ql, c.p->ql_bytes, qx, sx);
+}
+
 // One pre-norm block: xmid = x + O(attn(qkv(norm(x)))), xout = xmid +
-// MLP(norm(xmid)).
+// MLP(norm(xmid)).  On entry the qlinear workspace holds the quantised
+// norm_attn(xin); on return it holds the quantised next_norm(xout) (and xn,
+// when not null, the normalised rows).  The output and down projections
+// leave split partials that the row finisher reduces together with the
+// residual and the next RMSNorm.
 static int run_block(const StepCtx& c, const fp8s_block_weights& L, const uint16_t* xin, uint16_t* xmid,
-                     uint16_t* xout, uint16_t* kc, uint16_t* vc, int64_t sb, int64_t sh, int64_t stt, int64_t cap,
-                     const int32_t* kv_len, int64_t hint) {
+                     uint16_t* xout, const uint16_t* next_norm, uint16_t* xn, uint16_t* kc, uint16_t* vc, int64_t sb,
+                     int64_t sh, int64_t stt, int64_t cap, const int32_t* kv_len, int64_t hint) {
     const fp8s_dual_ar_model* m = c.m;
     const int64_t H = m->hidden, A = (int64_t)m->n_heads * m->head_dim;
     uint16_t* q = reinterpret_cast<uint16_t*>(c.ws + c.p->off_q);
     uint16_t* ao = reinterpret_cast<uint16_t*>(c.ws + c.p->off_ao);
     void* qlw = c.ws + c.p->off_ql;
-    int rc = qkv_proj_kv_append(xin, c.B, H, H, L.norm_attn, m->rms_eps, L.qkv, m->n_heads, m->n_kv_heads,
-                                m->head_dim, q, kc, vc, sb, sh, stt, kv_len, cap, qlw, c.p->ql_bytes, c.err, c.stream);
+    void* mlpw = c.ws + c.p->off_mlp;
+    int rc = qkv_proj_kv_append_ex(nullptr, c.B, H, H, nullptr, 0.0f, L.qkv, m->n_heads, m->n_kv_heads, m->head_dim,
+                                   q, kc, vc, sb, sh, stt, kv_len, cap, qlw, c.p->ql_bytes, c.err, c.stream);
     if (rc) return step_error(rc, "qkv projection");
     // The attention quantises its own output straight into the output
     // projection's operand when every KV head's query group covers whole
@@ -254,27 +350,37 @@ static int run_block(const StepCtx& c, const fp8s_block_weights& L, const uint16
     const bool fuse = (m->n_heads / m->n_kv_heads) * m->head_dim % 128 == 0;
     uint8_t* qo = nullptr;
     float* so = nullptr;
-    if (fuse && (rc = qlinear_operand(c.B, H, A, qlw, c.p->ql_bytes, &qo, &so))) return step_error(rc, "attention");
+    if ((rc = qlinear_operand(c.B, H, A, qlw, c.p->ql_bytes, &qo, &so))) return step_error(rc, "attention");
     rc = gqa_decode_attn_ex(q, kc, vc, sb, sh, stt, kv_len, c.B, m->n_heads, m->n_kv_heads, m->head_dim, cap, hint,
-                            1.0f / sqrtf((float)m->head_dim), ao, qo, so, c.ws + c.p->off_attn, c.p->attn_bytes, c.err,
-                            c.stream);
+                            1.0f / sqrtf((float)m->head_dim), ao, fuse ? qo : nullptr, fuse ? so : nullptr,
+                            c.ws + c.p->off_attn, c.p->attn_bytes, c.err, c.stream);
     if (rc) return step_error(rc, "attention");
-    rc = fuse ? qlinear_fp8_prequant(c.B, A, L.o, H, xin, H, xmid, H, qlw, c.p->ql_bytes, c.stream)
-              : qlinear_fp8(ao, c.B, A, A, nullptr, 0.0f, L.o, H, xin, H, FP8S_OUT_BF16, xmid, H, qlw, c.p->ql_bytes,
-                            c.stream);
-    if (rc) return step_error(rc, "output projection");
-    rc = swiglu_mlp_fp8_ex(xmid, c.B, H, m->inter, FP8S_MLP_BSGEMM, L.gate, L.up, L.down, L.norm_mlp, m->rms_eps,
-                           xmid, xout, c.ws + c.p->off_mlp, c.p->mlp_bytes, c.stream);
+    if (!fuse) {                               // quantise ao into the same operand buffer
+        if ((rc = qlinear_quantize_operand(ao, c.B, A, qo, so, c.stream))) return step_error(rc, "attention");
+    }
+    SplitPartials po;
+    if ((rc = qlinear_fp8_partials(c.B, A, L.o, H, qlw, c.p->ql_bytes, c.stream, &po)))
+        return step_error(rc, "output projection");
+    uint8_t* mq;
+    void* ms;
+    if ((rc = mlp_operand(c.B, H, m->inter, FP8S_MLP_BSGEMM, mlpw, c.p->mlp_bytes, &mq, &ms))) return step_error(rc, "mlp");
+    if ((rc = finish_rows(c, &po, xin, xmid, L.norm_mlp, nullptr, mq, ms, "output projection"))) return rc;
+    SplitPartials pd;
+    rc = swiglu_mlp_fp8_ex(nullptr, c.B, H, m->inter, FP8S_MLP_BSGEMM, L.gate, L.up, L.down, nullptr, 0.0f, nullptr,
+                           nullptr, mlpw, c.p->mlp_bytes, c.stream, &pd);
     if (rc) return step_error(rc, "mlp");
-    return FP8S_OK;
+    uint8_t* nq;
+    float* ns;
+    if ((rc = ql_operand(c, &nq, &ns))) return step_error(rc, "mlp");
+    return finish_rows(c, &pd, xmid, xout, next_norm, xn, nq, ns, "mlp");
 }
 
-// logits = head . (norm ? RMSNorm(z) : z); codes[:, col] = argmax.
-static int run_head(const StepCtx& c, const fp8s_qweight& head, const uint16_t* z, const uint16_t* norm_w,
-                    float* logits, int32_t* codes, int col) {
+// logits = head . z with z already quantised in the qlinear workspace;
+// codes[:, col] = argmax.
+static int run_head(const StepCtx& c, const fp8s_qweight& head, float* logits, int32_t* codes, int col) {
     const fp8s_dual_ar_model* m = c.m;
-    int rc = qlinear_fp8(z, c.B, m->hidden, m->hidden, norm_w, m->rms_eps, head, m->codebook_size, nullptr, 0,
-                         FP8S_OUT_F32, logits, m->codebook_size, c.ws + c.p->off_ql, c.p->ql_bytes, c.stream);
+    int rc = qlinear_fp8_ex(nullptr, c.B, m->hidden, m->hidden, nullptr, 0.0f, head, m->codebook_size, nullptr, 0,
+                            FP8S_OUT_F32, logits, m->codebook_size, c.ws + c.p->off_ql, c.p->ql_bytes, c.stream);
     if (rc) return step_error(rc, "codebook head");
     rc = argmax_rows_f32(logits, c.B, m->codebook_size, m->codebook_size, codes + col, m->n_codebooks, c.stream);
     if (rc) return step_error(rc, "argmax");
@@ -364,19 +470,25 @@ extern "C" int dual_ar_decode_step(const fp8s_dual_ar_model* m, int64_t B, const
         return logits_tap ? logits_tap + (int64_t)cb * B * V : reinterpret_cast<float*>(ws + p.off_logits);
     };
     hipStream_t st = as_stream(stream);
+    uint8_t* oq;
+    float* os;
+    if ((rc = ql_operand(c, &oq, &os))) return step_error(rc, "workspace");
 
     // ---- slow AR
     rc = embed_sum_bf16(m->embed, C, V, H, prev_codes, C, B, nullptr, slow_x(0), err_flag, stream);
     if (rc) return step_error(rc, "slow input embedding");
+    // operand of layer 0's QKV projection (or, with no layers, of the head)
+    rc = finish_rows(c, nullptr, slow_x(0), nullptr, L > 0 ? m->slow[0].norm_attn : m->slow_norm, L > 0 ? nullptr : h,
+                     oq, os, "slow input norm");
+    if (rc) return rc;
     for (int l = 0; l < L; ++l) {
-        rc = run_block(c, m->slow[l], slow_x(l), slow_mid(l), slow_x(l + 1), kv->k_cache[l], kv->v_cache[l], kv->stride_b,
-                       kv->stride_h, kv->stride_t, kv->cap, kv->kv_len, kv->max_kv_len_hint);
+        const bool last = l == L - 1;
+        rc = run_block(c, m->slow[l], slow_x(l), slow_mid(l), slow_x(l + 1), last ? m->slow_norm : m->slow[l + 1].norm_attn,
+                       last ? h : nullptr, kv->k_cache[l], kv->v_cache[l], kv->stride_b, kv->stride_h, kv->stride_t,
+                       kv->cap, kv->kv_len, kv->max_kv_len_hint);
         if (rc) return rc;
     }
-    FP8S_LAUNCH("rmsnorm", rmsnorm_kernel, dim3((unsigned)B), dim3(256), 0, st, slow_x(L), m->slow_norm, H,
-                m->rms_eps, h);
-    if ((rc = check_launch("dual_ar_decode_step: slow norm"))) return rc;
-    if ((rc = run_head(c, m->heads[0], h, nullptr, logits(0), codes, 0))) return rc;
+    if ((rc = run_head(c, m->heads[0], logits(0), codes, 0))) return rc;
 
     // ---- fast AR over the remaining codebooks
     int32_t* steps = reinterpret_cast<int32_t*>(ws + p.off_fsteps);
@@ -388,14 +500,18 @@ extern "C" int dual_ar_decode_step(const fp8s_dual_ar_model* m, int64_t B, const
         rc = embed_sum_bf16(&m->embed[s], 1, V, H, codes + s, C, B, s == 0 ? h : nullptr, fast_x(s, 0), err_flag,
                             stream);
         if (rc) return step_error(rc, "fast input embedding");
+        rc = finish_rows(c, nullptr, fast_x(s, 0), nullptr, F > 0 ? m->fast[0].norm_attn : m->fast_norm, nullptr, oq, os,
+                         "fast input norm");
+        if (rc) return rc;
         for (int f = 0; f < F; ++f) {
             uint16_t* fk = reinterpret_cast<uint16_t*>(ws + p.off_fk) + (int64_t)f * B * fsb;
             uint16_t* fv = reinterpret_cast<uint16_t*>(ws + p.off_fv) + (int64_t)f * B * fsb;
-            rc = run_block(c, m->fast[f], fast_x(s, f), fast_mid(s, f), fast_x(s, f + 1), fk, fv, fsb, fsh, m->head_dim, p.FS,
-                           steps + (int64_t)s * B, s + 1);
+            rc = run_block(c, m->fast[f], fast_x(s, f), fast_mid(s, f), fast_x(s, f + 1),
+                           f + 1 < F ? m->fast[f + 1].norm_attn : m->fast_norm, nullptr, fk, fv, fsb, fsh, m->head_dim,
+                           p.FS, steps + (int64_t)s * B, s + 1);
             if (rc) return rc;
         }
-        if ((rc = run_head(c, m->heads[s + 1], fast_x(s, F), m->fast_norm, logits(s + 1), codes, s + 1))) return rc;
+        if ((rc = run_head(c, m->heads[s + 1], logits(s + 1), codes, s + 1))) return rc;
     }
     return FP8S_OK;
 }

@@ -9,12 +9,28 @@
 
 namespace fp8s {
 
+// Split-K partials left in a workspace by a deferred GEMM: element (m, n) of
+// split s at part[((n / cols * S + s) * M + m) * cols + n % cols]; the sum
+// over s in split order is the product.
+struct SplitPartials {
+    const float* part;
+    int S, cols;
+};
+
 // swiglu_mlp_fp8 with an optional RMSNorm of x in front (norm_w, eps) and an
 // optional residual added to y before its bf16 rounding; either may be null.
+// x == nullptr: the quantised x is already in the workspace (mlp_operand).
+// partials != nullptr: y is not written; the down projection's split
+// partials stay in the workspace, described in *partials.
 int swiglu_mlp_fp8_ex(const uint16_t* x, int64_t M, int64_t H, int64_t I, int mode, fp8s_qweight gate,
                       fp8s_qweight up, fp8s_qweight down, const uint16_t* norm_w, float eps,
                       const uint16_t* residual, uint16_t* y, void* workspace, size_t workspace_bytes,
-                      void* stream);
+                      void* stream, SplitPartials* partials);
+
+// Where swiglu_mlp_fp8 keeps its quantised x (fragments [mt][kb] of 16 rows x
+// 128 bytes, then the mode's scales) inside a workspace.
+int mlp_operand(int64_t M, int64_t H, int64_t I, int mode, void* workspace, size_t workspace_bytes, uint8_t** qx,
+                void** sx);
 
 // gqa_decode_attn that can also write its output quantised (bsgemm 1x128
 // groups, the operand layout of qlinear_fp8_prequant) into qo / so; the
@@ -30,9 +46,24 @@ int gqa_decode_attn_ex(const uint16_t* q, const uint16_t* k_cache, const uint16_
 int qlinear_operand(int64_t M, int64_t N, int64_t K, void* workspace, size_t workspace_bytes, uint8_t** qx,
                     float** sx);
 
-// qlinear_fp8 (bf16 output, optional residual) whose activation operand is
-// already quantised in the workspace (qlinear_operand), so no quantiser runs.
-int qlinear_fp8_prequant(int64_t M, int64_t K, fp8s_qweight w, int64_t N, const uint16_t* residual, int64_t ld_res,
-                         uint16_t* y, int64_t ld_y, void* workspace, size_t workspace_bytes, void* stream);
+// qlinear_fp8 and qkv_proj_kv_append; x == nullptr means the activation
+// operand is already quantised in the workspace (qlinear_operand).
+int qlinear_fp8_ex(const uint16_t* x, int64_t M, int64_t K, int64_t ld_x, const uint16_t* norm_w, float eps,
+                   fp8s_qweight w, int64_t N, const uint16_t* residual, int64_t ld_res, int out_dtype, void* y,
+                   int64_t ld_y, void* workspace, size_t workspace_bytes, void* stream);
+int qkv_proj_kv_append_ex(const uint16_t* x, int64_t M, int64_t K, int64_t ld_x, const uint16_t* norm_w, float eps,
+                          fp8s_qweight w_qkv, int32_t Hq, int32_t Hkv, int32_t D, uint16_t* q_out,
+                          uint16_t* k_cache, uint16_t* v_cache, int64_t stride_b, int64_t stride_h,
+                          int64_t stride_t, const int32_t* kv_len, int64_t cap, void* workspace,
+                          size_t workspace_bytes, int32_t* err_flag, void* stream);
+
+// x [M, K] bf16 (contiguous rows) quantised in 1x128 groups into the operand
+// layout of qlinear_operand.
+int qlinear_quantize_operand(const uint16_t* x, int64_t M, int64_t K, uint8_t* qx, float* sx, void* stream);
+
+// The product of a pre-quantised operand and w, left as split partials in
+// the workspace (no reduction, no epilogue): the next kernel finishes it.
+int qlinear_fp8_partials(int64_t M, int64_t K, fp8s_qweight w, int64_t N, void* workspace, size_t workspace_bytes,
+                         void* stream, SplitPartials* out);
 
 }  // namespace fp8s

@@ -38,6 +38,7 @@
 #include "common.h"
 #include "gemm_tiles.h"
 #include "host_common.h"
+#include "internal.h"
 #include "profile.h"
 
 namespace fp8s {
@@ -69,6 +70,7 @@ struct MlpArgs {
     const uint16_t* norm_w;        // optional RMSNorm weight [H] in front of the MLP
     float eps;
     const uint16_t* res;           // optional residual [M, H] added to y
+    bool defer;                    // leave the down projection's split partials for the next kernel
 };
 
 // ---- hq: h = silu(g) * u -> q_h fragments (one workgroup per (M tile, K block))
@@ -259,6 +261,7 @@ __global__ __launch_bounds__(256, 2) void gu_kernel(MlpArgs a) {
 // (deterministic) into bf16 y and re-arms the counter.
 template <int COLS, int MAXM>
 __device__ __forceinline__ void finish_split(const MlpArgs& a, int nt, int s, int n0, int* s_prev) {
+    if (a.defer) return;                       // the next kernel reduces the partials
     __builtin_amdgcn_s_waitcnt(0);             // this thread's partial stores are complete
     __syncthreads();
     if (threadIdx.x == 0) *s_prev = atomic_add_relaxed(a.cnt + nt, 1);
@@ -479,16 +482,19 @@ static MlpPlan plan_mlp(int64_t M, int64_t H, int64_t I, int mode) {
 //           (with an RMSNorm in front, the M <= 16 chain instead)
 // M <= 16 : xq -> gu<1> -> hq -> down_small
 // M >  16 : xq -> gu<MT> -> hq -> down<MT>
+// prequant: the quantised x is already in the workspace (no xq launch).
 template <int MODE>
-static void launch_mlp(const MlpPlan& p, hipStream_t st, const MlpArgs& a) {
+static void launch_mlp(const MlpPlan& p, hipStream_t st, const MlpArgs& a, bool prequant) {
     const dim3 blk(256), g_gu(a.I / kGuCols), g_xq(p.MT * p.KBH), g_hq(p.MT * p.KBI), g_dn(p.NT * p.S);
-    if (a.M <= kTinyM && !a.norm_w) {
+    if (a.M <= kTinyM && !a.norm_w && !prequant) {
         FP8S_LAUNCH("mlp_gu_small", gu_small_kernel<MODE>, g_gu, blk, 0, st, a);
         FP8S_LAUNCH("mlp_down_small_fused", (down_small_kernel<MODE, true>), g_dn, blk, 0, st, a);
         return;
     }
-    const ActQuantArgs xa{a.x, a.H, a.M, a.H, a.KBH, a.norm_w, a.eps, a.qx, a.sx};
-    FP8S_LAUNCH("mlp_xq", act_quant_kernel<MODE>, g_xq, blk, 0, st, xa);
+    if (!prequant) {
+        const ActQuantArgs xa{a.x, a.H, a.M, a.H, a.KBH, a.norm_w, a.eps, a.qx, a.sx};
+        FP8S_LAUNCH("mlp_xq", act_quant_kernel<MODE>, g_xq, blk, 0, st, xa);
+    }
     switch (p.MT) {
     case 1:
         FP8S_LAUNCH("mlp_gu", (gu_kernel<1, MODE>), g_gu, blk, kLdsBytes, st, a);
@@ -527,10 +533,26 @@ extern "C" size_t swiglu_mlp_fp8_workspace_size(int64_t M, int64_t hidden, int64
 }
 
 namespace fp8s {
+int mlp_operand(int64_t M, int64_t H, int64_t I, int mode, void* workspace, size_t workspace_bytes, uint8_t** qx,
+                void** sx) {
+    FP8S_REQUIRE(M >= 1 && M <= 128 && H >= 128 && I >= 128 && H % 128 == 0 && I % 128 == 0 && H <= 128 * kMaxKbGu,
+                 FP8S_EINVAL, "mlp_operand: unsupported shape");
+    const MlpPlan p = plan_mlp(M, H, I, mode);
+    FP8S_REQUIRE(workspace && aligned16(workspace) && workspace_bytes >= p.total, FP8S_EWORKSPACE,
+                 "mlp_operand: workspace missing, unaligned or too small");
+    *qx = static_cast<uint8_t*>(workspace) + p.off_qx;
+    *sx = static_cast<uint8_t*>(workspace) + p.off_sx;
+    return FP8S_OK;
+}
+
 int swiglu_mlp_fp8_ex(const uint16_t* x, int64_t M, int64_t H, int64_t I, int mode, fp8s_qweight gate,
                       fp8s_qweight up, fp8s_qweight down, const uint16_t* norm_w, float eps,
                       const uint16_t* residual, uint16_t* y, void* workspace, size_t workspace_bytes,
-                      void* stream) {
+                      void* stream, SplitPartials* partials) {
+    const bool prequant = x == nullptr;
+    alignas(16) static const uint16_t kNoRow[8] = {};
+    if (prequant) x = kNoRow;                  // never read
+    if (partials) y = const_cast<uint16_t*>(kNoRow);
     FP8S_REQUIRE(x && y, FP8S_EINVAL, "swiglu_mlp_fp8: null x or y");
     FP8S_REQUIRE(mode == FP8S_MLP_BSGEMM || mode == FP8S_MLP_MXFP8, FP8S_EINVAL, "swiglu_mlp_fp8: unknown mode %d",
                  mode);
@@ -568,11 +590,17 @@ int swiglu_mlp_fp8_ex(const uint16_t* x, int64_t M, int64_t H, int64_t I, int mo
     a.cnt = reinterpret_cast<int*>(ws + p.off_ctrl);
     a.NT = p.NT; a.S = p.S;
     a.norm_w = norm_w; a.eps = eps; a.res = residual;
+    a.defer = partials != nullptr;
     hipStream_t st = as_stream(stream);
     if (mode == FP8S_MLP_BSGEMM)
-        launch_mlp<FP8S_MLP_BSGEMM>(p, st, a);
+        launch_mlp<FP8S_MLP_BSGEMM>(p, st, a, prequant);
     else
-        launch_mlp<FP8S_MLP_MXFP8>(p, st, a);
+        launch_mlp<FP8S_MLP_MXFP8>(p, st, a, prequant);
+    if (partials) {
+        partials->part = a.ypart;
+        partials->S = p.S;
+        partials->cols = p.MT == 1 ? kSmallDownCols : 16 * kDownNb;
+    }
     return check_launch("swiglu_mlp_fp8");
 }
 }  // namespace fp8s
@@ -582,6 +610,7 @@ extern "C" int swiglu_mlp_fp8(const uint16_t* x, int64_t M, int64_t H, int64_t I
                               void* workspace, size_t workspace_bytes, int32_t* err_flag, void* stream) {
     clear_error();
     (void)err_flag;   // no device-side error conditions remain in this path
+    FP8S_REQUIRE(x, FP8S_EINVAL, "swiglu_mlp_fp8: null x or y");
     return swiglu_mlp_fp8_ex(x, M, H, I, mode, gate, up, down, nullptr, 0.0f, nullptr, y, workspace,
-                             workspace_bytes, stream);
+                             workspace_bytes, stream, nullptr);
 }

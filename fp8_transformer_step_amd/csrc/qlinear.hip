@@ -30,7 +30,9 @@ constexpr int kQlMaxKb = kLdsBytes / (kQlNb * kFrag);      // K blocks per split
 constexpr int kQlTargetItems = 512;
 constexpr int kQlCtrlWords = 4096;                         // control region at workspace offset 0
 
-enum { EPI_BF16 = 0, EPI_F32 = 1, EPI_QKV = 2 };
+// EPI_PARTIAL: the split partials are left in the workspace for the next
+// kernel to reduce (no hand-off, no epilogue).
+enum { EPI_BF16 = 0, EPI_F32 = 1, EPI_QKV = 2, EPI_PARTIAL = 3 };
 
 struct QlArgs {
     int M, N, KB, NT, S;
@@ -120,6 +122,7 @@ __global__ __launch_bounds__(256, 2) void qlinear_kernel(QlArgs a) {
                     if (m < a.M) store_partial(&part[(int64_t)m * kQlCols + 16 * j + (lane & 15)], acc[j][i][r]);
                 }
     }
+    if (a.epi == EPI_PARTIAL) return;
     // Split hand-off: partial stores complete, one counter bump per workgroup;
     // the last split of the tile reduces in split order and re-arms the counter.
     __builtin_amdgcn_s_waitcnt(0);
@@ -241,41 +244,17 @@ int qlinear_operand(int64_t M, int64_t N, int64_t K, void* workspace, size_t wor
     return FP8S_OK;
 }
 
-int qlinear_fp8_prequant(int64_t M, int64_t K, fp8s_qweight w, int64_t N, const uint16_t* residual, int64_t ld_res,
-                         uint16_t* y, int64_t ld_y, void* workspace, size_t workspace_bytes, void* stream) {
-    // The checks of qlinear_fp8 with a stand-in activation pointer (never read).
-    alignas(16) static const uint16_t kNoX[8] = {};
+// The checks of the public entry points; x == nullptr means the activation
+// operand is already quantised in the workspace (a stand-in pointer passes
+// the x checks and is never read).
+alignas(16) static const uint16_t kNoX[8] = {};
+
+int qlinear_fp8_ex(const uint16_t* x, int64_t M, int64_t K, int64_t ld_x, const uint16_t* norm_w, float eps,
+                   fp8s_qweight w, int64_t N, const uint16_t* residual, int64_t ld_res, int out_dtype, void* y,
+                   int64_t ld_y, void* workspace, size_t workspace_bytes, void* stream) {
     QlPlan p;
-    int rc = ql_check_common("qlinear_fp8_prequant", kNoX, M, K, K, nullptr, 0.0f, w, N, workspace, workspace_bytes,
-                             &p);
-    if (rc) return rc;
-    FP8S_REQUIRE(y && ld_y >= N, FP8S_EINVAL, "qlinear_fp8_prequant: null y or ld_y < N");
-    FP8S_REQUIRE(!residual || ld_res >= N, FP8S_EINVAL, "qlinear_fp8_prequant: ld_res < N");
-    QlArgs a{};
-    a.M = (int)M; a.N = (int)N;
-    ql_weight(a, w);
-    a.epi = EPI_BF16;
-    a.y = y; a.ldy = ld_y;
-    a.res = residual; a.ld_res = ld_res;
-    ql_launch(p, a, nullptr, 0, K, nullptr, 0.0f, workspace, as_stream(stream));
-    return check_launch("qlinear_fp8_prequant");
-}
-
-}  // namespace fp8s
-
-using namespace fp8s;
-
-extern "C" size_t qlinear_fp8_workspace_size(int64_t M, int64_t N, int64_t K) {
-    if (!ql_shape_ok(M, N, K)) return 0;
-    return plan_ql(M, N, K).total;
-}
-
-extern "C" int qlinear_fp8(const uint16_t* x, int64_t M, int64_t K, int64_t ld_x, const uint16_t* norm_w, float eps,
-                           fp8s_qweight w, int64_t N, const uint16_t* residual, int64_t ld_res, int out_dtype,
-                           void* y, int64_t ld_y, void* workspace, size_t workspace_bytes, void* stream) {
-    clear_error();
-    QlPlan p;
-    int rc = ql_check_common("qlinear_fp8", x, M, K, ld_x, norm_w, eps, w, N, workspace, workspace_bytes, &p);
+    int rc = ql_check_common("qlinear_fp8", x ? x : kNoX, M, K, x ? ld_x : K, norm_w, eps, w, N, workspace,
+                             workspace_bytes, &p);
     if (rc) return rc;
     FP8S_REQUIRE(y, FP8S_EINVAL, "qlinear_fp8: null y");
     FP8S_REQUIRE(out_dtype == FP8S_OUT_BF16 || out_dtype == FP8S_OUT_F32, FP8S_EINVAL,
@@ -294,18 +273,44 @@ extern "C" int qlinear_fp8(const uint16_t* x, int64_t M, int64_t K, int64_t ld_x
     return check_launch("qlinear_fp8");
 }
 
-extern "C" int qkv_proj_kv_append(const uint16_t* x, int64_t M, int64_t K, int64_t ld_x, const uint16_t* norm_w,
-                                  float eps, fp8s_qweight w_qkv, int32_t Hq, int32_t Hkv, int32_t D,
-                                  uint16_t* q_out, uint16_t* k_cache, uint16_t* v_cache, int64_t stride_b,
-                                  int64_t stride_h, int64_t stride_t, const int32_t* kv_len, int64_t cap,
-                                  void* workspace, size_t workspace_bytes, int32_t* err_flag, void* stream) {
-    clear_error();
+int qlinear_fp8_partials(int64_t M, int64_t K, fp8s_qweight w, int64_t N, void* workspace, size_t workspace_bytes,
+                         void* stream, SplitPartials* out) {
+    QlPlan p;
+    int rc = ql_check_common("qlinear_fp8_partials", kNoX, M, K, K, nullptr, 0.0f, w, N, workspace, workspace_bytes,
+                             &p);
+    if (rc) return rc;
+    FP8S_REQUIRE(out, FP8S_EINVAL, "qlinear_fp8_partials: null output description");
+    QlArgs a{};
+    a.M = (int)M; a.N = (int)N;
+    ql_weight(a, w);
+    a.epi = EPI_PARTIAL;
+    ql_launch(p, a, nullptr, 0, K, nullptr, 0.0f, workspace, as_stream(stream));
+    out->part = reinterpret_cast<const float*>(static_cast<const uint8_t*>(workspace) + p.off_part);
+    out->S = p.S;
+    out->cols = kQlCols;
+    return check_launch("qlinear_fp8_partials");
+}
+
+int qlinear_quantize_operand(const uint16_t* x, int64_t M, int64_t K, uint8_t* qx, float* sx, void* stream) {
+    FP8S_REQUIRE(x && qx && sx && M >= 1 && M <= 128 && K >= 128 && K % 128 == 0 && aligned16(x), FP8S_EINVAL,
+                 "qlinear_quantize_operand: bad arguments");
+    const int KB = (int)(K / 128), mt = (int)((M + 15) / 16);
+    const ActQuantArgs xa{x, K, (int)M, (int)K, KB, nullptr, 0.0f, qx, sx};
+    FP8S_LAUNCH("ql_act_quant", act_quant_kernel<FP8S_MLP_BSGEMM>, dim3(mt * KB), dim3(256), 0, as_stream(stream), xa);
+    return check_launch("qlinear_quantize_operand");
+}
+
+int qkv_proj_kv_append_ex(const uint16_t* x, int64_t M, int64_t K, int64_t ld_x, const uint16_t* norm_w, float eps,
+                          fp8s_qweight w_qkv, int32_t Hq, int32_t Hkv, int32_t D, uint16_t* q_out,
+                          uint16_t* k_cache, uint16_t* v_cache, int64_t stride_b, int64_t stride_h,
+                          int64_t stride_t, const int32_t* kv_len, int64_t cap, void* workspace,
+                          size_t workspace_bytes, int32_t* err_flag, void* stream) {
     FP8S_REQUIRE(Hq >= 1 && Hkv >= 1 && Hq % Hkv == 0, FP8S_EINVAL, "qkv_proj_kv_append: Hq must be a multiple of Hkv");
     FP8S_REQUIRE(D == 64 || D == 128, FP8S_EUNSUPPORTED, "qkv_proj_kv_append: head_dim %d (64 or 128)", D);
     const int64_t N = (int64_t)(Hq + 2 * Hkv) * D;
     QlPlan p;
-    int rc = ql_check_common("qkv_proj_kv_append", x, M, K, ld_x, norm_w, eps, w_qkv, N, workspace, workspace_bytes,
-                             &p);
+    int rc = ql_check_common("qkv_proj_kv_append", x ? x : kNoX, M, K, x ? ld_x : K, norm_w, eps, w_qkv, N,
+                             workspace, workspace_bytes, &p);
     if (rc) return rc;
     FP8S_REQUIRE(q_out && k_cache && v_cache && kv_len, FP8S_EINVAL, "qkv_proj_kv_append: null output or kv_len");
     FP8S_REQUIRE(cap >= 1 && stride_t >= D && stride_h >= 1 && stride_b >= 1, FP8S_EINVAL,
@@ -319,4 +324,33 @@ extern "C" int qkv_proj_kv_append(const uint16_t* x, int64_t M, int64_t K, int64
     a.kv_len = kv_len; a.cap = cap; a.err = err_flag;
     ql_launch(p, a, x, ld_x, K, norm_w, eps, workspace, as_stream(stream));
     return check_launch("qkv_proj_kv_append");
+}
+
+}  // namespace fp8s
+
+using namespace fp8s;
+
+extern "C" size_t qlinear_fp8_workspace_size(int64_t M, int64_t N, int64_t K) {
+    if (!ql_shape_ok(M, N, K)) return 0;
+    return plan_ql(M, N, K).total;
+}
+
+extern "C" int qlinear_fp8(const uint16_t* x, int64_t M, int64_t K, int64_t ld_x, const uint16_t* norm_w, float eps,
+                           fp8s_qweight w, int64_t N, const uint16_t* residual, int64_t ld_res, int out_dtype,
+                           void* y, int64_t ld_y, void* workspace, size_t workspace_bytes, void* stream) {
+    clear_error();
+    FP8S_REQUIRE(x, FP8S_EINVAL, "qlinear_fp8: null x");
+    return qlinear_fp8_ex(x, M, K, ld_x, norm_w, eps, w, N, residual, ld_res, out_dtype, y, ld_y, workspace,
+                          workspace_bytes, stream);
+}
+
+extern "C" int qkv_proj_kv_append(const uint16_t* x, int64_t M, int64_t K, int64_t ld_x, const uint16_t* norm_w,
+                                  float eps, fp8s_qweight w_qkv, int32_t Hq, int32_t Hkv, int32_t D,
+                                  uint16_t* q_out, uint16_t* k_cache, uint16_t* v_cache, int64_t stride_b,
+                                  int64_t stride_h, int64_t stride_t, const int32_t* kv_len, int64_t cap,
+                                  void* workspace, size_t workspace_bytes, int32_t* err_flag, void* stream) {
+    clear_error();
+    FP8S_REQUIRE(x, FP8S_EINVAL, "qkv_proj_kv_append: null x");
+    return qkv_proj_kv_append_ex(x, M, K, ld_x, norm_w, eps, w_qkv, Hq, Hkv, D, q_out, k_cache, v_cache, stride_b,
+                                 stride_h, stride_t, kv_len, cap, workspace, workspace_bytes, err_flag, stream);
 }

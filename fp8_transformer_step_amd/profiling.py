@@ -39,7 +39,7 @@ KERNELS = [
     (r"qlinear_kernel", "qlinear"),
     (r"embed_kernel", "embed_sum"),
     (r"argmax_kernel", "argmax"),
-    (r"rmsnorm_kernel", "rmsnorm"),
+    (r"finish_kernel", "row_finish"),
     (r"fill_steps_kernel", "fill_steps"),
     (r"quant_block128_kernel", "quantize_block128"),
     (r"quant_rows_kernel<128>", "quantize_1x128"),
