@@ -122,7 +122,8 @@ __global__ __launch_bounds__(256) void argmax_kernel(const float* logits, int64_
 // of it, written to xn when asked), quantised in 1x128 groups into MFMA
 // operand fragments.  The 16 chunks of a quantisation group belong to the
 // 16 lanes of one DPP row.
-constexpr int kFinishChunks = 2;          // chunks per thread: H <= 4096
+constexpr int kFinishThreads = 512;
+constexpr int kFinishChunks = 1;          // chunks per thread: H <= 4096
 constexpr int kFinishBatch = 8;           // split partials loaded at once
 
 struct FinishArgs {
@@ -138,19 +139,20 @@ struct FinishArgs {
     int M, H, KB;
 };
 
-__global__ __launch_bounds__(256) void finish_kernel(FinishArgs a) {
-    __shared__ float s_ss[4];
+__global__ __launch_bounds__(kFinishThreads) void finish_kernel(FinishArgs a) {
+    constexpr int NW = kFinishThreads / 64;
+    __shared__ float s_ss[NW];
     const int m = blockIdx.x, t = threadIdx.x;
     const int nch = a.H / 8;
     float x[kFinishChunks][8];
     uint4 wn[kFinishChunks];                  // the norm weights, requested with the row
 #pragma unroll
     for (int p = 0; p < kFinishChunks; ++p)
-        wn[p] = *reinterpret_cast<const uint4*>(a.norm_w + 8 * min(t + 256 * p, nch - 1));
+        wn[p] = *reinterpret_cast<const uint4*>(a.norm_w + 8 * min(t + kFinishThreads * p, nch - 1));
     float ss = 0.0f;
 #pragma unroll
     for (int p = 0; p < kFinishChunks; ++p) {
-        const int c = t + 256 * p;
+        const int c = t + kFinishThreads * p;
         if (c >= nch) continue;
         float v[8];
         unpack_bf16x8(*reinterpret_cast<const uint4*>(a.base + (int64_t)m * a.H + 8 * c), v);
@@ -192,10 +194,13 @@ __global__ __launch_bounds__(256) void finish_kernel(FinishArgs a) {
     ss = fsum_xor<kWave>(ss);
     if ((t & 63) == 0) s_ss[t >> 6] = ss;
     __syncthreads();
-    const float inv = 1.0f / sqrtf((s_ss[0] + s_ss[1] + s_ss[2] + s_ss[3]) / (float)a.H + a.eps);
+    float tot = 0.0f;
+#pragma unroll
+    for (int w = 0; w < NW; ++w) tot += s_ss[w];
+    const float inv = 1.0f / sqrtf(tot / (float)a.H + a.eps);
 #pragma unroll
     for (int p = 0; p < kFinishChunks; ++p) {
-        const int c = t + 256 * p;
+        const int c = t + kFinishThreads * p;
         if (c >= nch) continue;
         float w[8], f[8];
         unpack_bf16x8(wn[p], w);
@@ -241,8 +246,8 @@ static int check_model(const fp8s_dual_ar_model* m, int64_t B, int64_t hint) {
                  "dual_ar_decode_step: hidden and inter must be positive multiples of 128");
     FP8S_REQUIRE(m->n_heads >= 1 && m->n_kv_heads >= 1 && m->n_heads % m->n_kv_heads == 0, FP8S_EINVAL,
                  "dual_ar_decode_step: n_heads must be a multiple of n_kv_heads");
-    FP8S_REQUIRE(m->hidden <= 8 * 256 * kFinishChunks, FP8S_EUNSUPPORTED, "dual_ar_decode_step: hidden %lld > %d",
-                 (long long)m->hidden, 8 * 256 * kFinishChunks);
+    FP8S_REQUIRE(m->hidden <= 8 * kFinishThreads * kFinishChunks, FP8S_EUNSUPPORTED,
+                 "dual_ar_decode_step: hidden %lld > %d", (long long)m->hidden, 8 * kFinishThreads * kFinishChunks);
     FP8S_REQUIRE(m->head_dim == 64 || m->head_dim == 128, FP8S_EUNSUPPORTED,
                  "dual_ar_decode_step: head_dim %d (64 or 128)", m->head_dim);
     FP8S_REQUIRE(((int64_t)m->n_heads * m->head_dim) % 128 == 0, FP8S_EINVAL,
@@ -313,7 +318,7 @@ static int finish_rows(const StepCtx& c, const SplitPartials* part, const uint16
     a.base = base; a.xout = xout; a.norm_w = norm_w; a.eps = c.m->rms_eps; a.xn = xn;
     a.qx = qx; a.sx = static_cast<float*>(sx);
     a.M = (int)c.B; a.H = (int)c.m->hidden; a.KB = (int)(c.m->hidden / 128);
-    FP8S_LAUNCH("row_finish", finish_kernel, dim3((unsigned)c.B), dim3(256), 0, as_stream(c.stream), a);
+    FP8S_LAUNCH("row_finish", finish_kernel, dim3((unsigned)c.B), dim3(kFinishThreads), 0, as_stream(c.stream), a);
     const int rc = check_launch("row finish");
     return rc ? step_error(rc, where) : FP8S_OK;
 }
