@@ -76,9 +76,19 @@ def _run_step(host):
     return out
 
 
-def test_small_model_every_layer_teacher_forced():
+@pytest.mark.parametrize("batch,n_heads", [(5, 4), (24, 8), (100, 8)])
+def test_small_model_every_layer_teacher_forced(batch, n_heads):
+    """Batch 5, 24 and 100 take the one-, two- and eight-tile (16 rows per
+    tile) variants of every projection and of the split-partial finisher.
+
+    The larger batches use 8 query heads: with 4 heads of 64 the output
+    projection contracts over only 256 values, so one e4m3 rounding flip of
+    an attention output moves a residual entry by about 2 % of the tensor's
+    maximum, and at batch 24 one sequence sits at the 2e-2 bound (the same
+    sequence with the projection's operand quantised separately gives the
+    same bytes, so the flip is the rounding, not the kernels)."""
     need_gpu()
-    host = model.HostModel(model.TINY)
+    host = model.HostModel(model.scaled(model.TINY, batch=batch, n_heads=n_heads))
     c = host.cfg
     g = _run_step(host)
     C, F, L = c.n_codebooks, c.n_fast_layers, c.n_slow_layers
