@@ -12,8 +12,10 @@
 // operand order) -> qlinear (split-K tiles of 32 output columns, weights
 // staged in LDS by direct-to-LDS loads, FP8 MFMA 16x16x128, fp32 partials;
 // the last split of a tile sums the partials in split order and runs the
-// epilogue).  At decode sizes (M <= 128) the weight stream is the whole cost,
-// so the split count is chosen for about 512 workgroups in flight.
+// epilogue; an unsplit tile runs it straight from registers).  At decode
+// sizes (M <= 128) the weight stream is the whole cost; the K range of an
+// item is as long as its LDS slice allows (20 blocks), because every split
+// adds a partial round trip that costs more than the parallelism it buys.
 #include <math.h>
 
 #include "common.h"
@@ -27,7 +29,7 @@ namespace fp8s {
 constexpr int kQlNb = 2;                                   // 16-column tiles per item
 constexpr int kQlCols = 16 * kQlNb;
 constexpr int kQlMaxKb = kLdsBytes / (kQlNb * kFrag);      // K blocks per split (LDS bound)
-constexpr int kQlTargetItems = 512;
+constexpr int kQlTargetItems = 64;     // more splits only when the columns alone give fewer items
 constexpr int kQlCtrlWords = 4096;                         // control region at workspace offset 0
 
 // EPI_PARTIAL: the split partials are left in the workspace for the next
@@ -110,6 +112,20 @@ __global__ __launch_bounds__(256, 2) void qlinear_kernel(QlArgs a) {
     });
     reduce_wk<MTS, NB, WK>(acc, lds, wm, wk, lane);
 
+    if (a.S == 1 && a.epi != EPI_PARTIAL) {   // the whole K range: the epilogue straight from registers
+        if (wk == 0) {
+#pragma unroll
+            for (int j = 0; j < NB; ++j)
+#pragma unroll
+                for (int i = 0; i < MTS; ++i)
+#pragma unroll
+                    for (int r = 0; r < 4; ++r) {
+                        const int m = (wm * MTS + i) * 16 + 4 * (lane >> 4) + r;
+                        if (m < a.M) ql_epilogue(a, m, n0 + 16 * j + (lane & 15), acc[j][i][r]);
+                    }
+        }
+        return;
+    }
     float* part = a.part + ((int64_t)nt * a.S + s) * a.M * kQlCols;
     if (wk == 0) {
 #pragma unroll
