@@ -109,16 +109,15 @@ __device__ __forceinline__ void mma_block(v4f* acc, const AStage<MTS, MODE>& st,
     for (int i = 0; i < MTS; ++i) {
         if (MODE == FP8S_MLP_BSGEMM) {
             const v4f z = {0, 0, 0, 0};
-            // (t * s_x) * s_w, with both products hanging off the MFMA result:
-            // a product of the two scales alone would be computed (and waited
-            // for) as soon as the scales arrive, stalling the prefetch ring.
+            // acc += t * (s_x * s_w): the scale product is formed inside this
+            // block's math (the loop fences it off from the prefetch), one FMA
+            // per output after the MFMA.
             const v4f t = mfma_fp8(st.a[i], b, z, kUnitScale, kUnitScale);
-            const float p0 = (t[0] * st.s[i].x) * sw, p1 = (t[1] * st.s[i].y) * sw;
-            const float p2 = (t[2] * st.s[i].z) * sw, p3 = (t[3] * st.s[i].w) * sw;
-            acc[i][0] += live ? p0 : 0.0f;
-            acc[i][1] += live ? p1 : 0.0f;
-            acc[i][2] += live ? p2 : 0.0f;
-            acc[i][3] += live ? p3 : 0.0f;
+            const float swl = live ? sw : 0.0f;
+            acc[i][0] = fmaf(t[0], st.s[i].x * swl, acc[i][0]);
+            acc[i][1] = fmaf(t[1], st.s[i].y * swl, acc[i][1]);
+            acc[i][2] = fmaf(t[2], st.s[i].z * swl, acc[i][2]);
+            acc[i][3] = fmaf(t[3], st.s[i].w * swl, acc[i][3]);
         } else {
             const v4f t = mfma_fp8(st.a[i], b, acc[i], st.e[i], ew);
             acc[i] = live ? t : acc[i];
