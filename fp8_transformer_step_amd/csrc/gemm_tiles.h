@@ -60,9 +60,10 @@ __device__ __forceinline__ v8i lds_frag32(const uint8_t* frag, int lane) {
     return r;
 }
 
-// bsgemm weight scale of the 128x128 block holding (row n0, K block kb).
+// bsgemm weight scale of the 128x128 block holding (row n0, K block kb).  The
+// per-block step kb * sc stays 32-bit: a scale matrix never nears 2^31 entries.
 __device__ __forceinline__ float wscale_bs(const void* s, int64_t sr, int64_t sc, int n0, int kb) {
-    return reinterpret_cast<const float*>(s)[(int64_t)(n0 >> 7) * sr + (int64_t)kb * sc];
+    return (reinterpret_cast<const float*>(s) + (int64_t)(n0 >> 7) * sr)[kb * (int)sc];
 }
 // MX weight exponent of (row n0 + lane%16, group kb*4 + lane/16).
 __device__ __forceinline__ int wscale_mx(const void* s, int64_t sr, int64_t sc, int n0, int kb, int lane) {
@@ -85,42 +86,39 @@ struct AStage {
     int e[MTS];        // MX: exponent byte of this lane's (row, group)
 };
 
+// Operand offsets are 32-bit: an operand holds at most 128 rows of K <= 2^20.
 template <int MTS, int MODE>
 __device__ __forceinline__ void load_astage(AStage<MTS, MODE>& st, const uint8_t* q, const void* sc, int KB,
                                             int mt0, int kb, int lane) {
 #pragma unroll
     for (int i = 0; i < MTS; ++i) {
-        st.a[i] = load_frag(q + frag_off(mt0 + i, kb, KB), lane);
+        const int blk = (mt0 + i) * KB + kb;
+        st.a[i] = load_frag(q + (uint32_t)blk * kFrag, lane);
         if (MODE == FP8S_MLP_BSGEMM)
-            st.s[i] = *reinterpret_cast<const float4*>(reinterpret_cast<const float*>(sc) +
-                                                       ((int64_t)(mt0 + i) * KB + kb) * 16 + 4 * (lane >> 4));
+            st.s[i] = *reinterpret_cast<const float4*>(reinterpret_cast<const float*>(sc) + (uint32_t)blk * 16 +
+                                                       4 * (lane >> 4));
         else
-            st.e[i] = reinterpret_cast<const uint8_t*>(sc)[((int64_t)(mt0 + i) * KB + kb) * 64 + lane];
+            st.e[i] = reinterpret_cast<const uint8_t*>(sc)[(uint32_t)blk * 64 + lane];
     }
 }
 
-// acc[i] += A_i * B over one 128-K block (bsgemm scales applied outside the
-// MFMA); nothing is added when `live` is false (a block past the end of the
-// range, computed on a clamped index so that the loop body has no branches).
+// acc[i] += A_i * B over one 128-K block.  bsgemm: acc += t * (s_x * s_w),
+// the scale product formed inside this block's math (the loop fences it off
+// from the prefetch), one FMA per output after the MFMA; MX: the UE8M0
+// scales go to the MFMA.
 template <int MTS, int MODE>
-__device__ __forceinline__ void mma_block(v4f* acc, const AStage<MTS, MODE>& st, const v8i& b, float sw, int ew,
-                                          bool live) {
+__device__ __forceinline__ void mma_block(v4f* acc, const AStage<MTS, MODE>& st, const v8i& b, float sw, int ew) {
 #pragma unroll
     for (int i = 0; i < MTS; ++i) {
         if (MODE == FP8S_MLP_BSGEMM) {
             const v4f z = {0, 0, 0, 0};
-            // acc += t * (s_x * s_w): the scale product is formed inside this
-            // block's math (the loop fences it off from the prefetch), one FMA
-            // per output after the MFMA.
             const v4f t = mfma_fp8(st.a[i], b, z, kUnitScale, kUnitScale);
-            const float swl = live ? sw : 0.0f;
-            acc[i][0] = fmaf(t[0], st.s[i].x * swl, acc[i][0]);
-            acc[i][1] = fmaf(t[1], st.s[i].y * swl, acc[i][1]);
-            acc[i][2] = fmaf(t[2], st.s[i].z * swl, acc[i][2]);
-            acc[i][3] = fmaf(t[3], st.s[i].w * swl, acc[i][3]);
+            acc[i][0] = fmaf(t[0], st.s[i].x * sw, acc[i][0]);
+            acc[i][1] = fmaf(t[1], st.s[i].y * sw, acc[i][1]);
+            acc[i][2] = fmaf(t[2], st.s[i].z * sw, acc[i][2]);
+            acc[i][3] = fmaf(t[3], st.s[i].w * sw, acc[i][3]);
         } else {
-            const v4f t = mfma_fp8(st.a[i], b, acc[i], st.e[i], ew);
-            acc[i] = live ? t : acc[i];
+            acc[i] = mfma_fp8(st.a[i], b, acc[i], st.e[i], ew);
         }
     }
 }
@@ -136,7 +134,9 @@ struct WStage {
 // K blocks [lo, hi).  The activation operands of a K block and the weight
 // scales wsc(j, kb) are loaded R blocks ahead into a register ring, all
 // loads of a block issued together, so each block waits only for its own
-// (oldest) loads.
+// (oldest) loads; the weight fragments of the next block are read from LDS
+// while this block's MFMAs run.  Full rounds of R blocks run branch-free
+// (the waits stay per block); the last partial round runs without refills.
 //
 // `ready()` is called once the ring's first loads are issued and before any
 // weight fragment is read from LDS: the caller waits there for its weight
@@ -162,29 +162,38 @@ __device__ __forceinline__ void gemm_loop(v4f (&acc)[NB][MTS], const uint8_t* ld
             wsc(j, kb, ws[u].sw[j], ws[u].ew[j]);
         }
     };
-    // Loads past the end re-read the last block (cache hits) and are never
-    // consumed; the body below is branch-free so the waits stay per block.
+    // Ring slots past the end re-read the last block (cache hits) and are
+    // never consumed.
 #pragma unroll
     for (int u = 0; u < R; ++u) load(u, min(lo + u, last));
     ready();
-    for (int kb0 = lo; kb0 < hi; kb0 += R) {
+    v8i bcur[NB];
+#pragma unroll
+    for (int j = 0; j < NB; ++j) bcur[j] = lds_frag(lds, b_off(j, lo), lane);
+    auto block = [&](int u, int kb) {
+        v8i bnext[NB];
+#pragma unroll
+        for (int j = 0; j < NB; ++j) bnext[j] = lds_frag(lds, b_off(j, min(kb + 1, last)), lane);
+#pragma unroll
+        for (int j = 0; j < NB; ++j) mma_block<MTS, MODE>(acc[j], st[u], bcur[j], ws[u].sw[j], ws[u].ew[j]);
+#pragma unroll
+        for (int j = 0; j < NB; ++j) bcur[j] = bnext[j];
+    };
+    int kb0 = lo;
+    for (; kb0 + R <= hi; kb0 += R) {
 #pragma unroll
         for (int u = 0; u < R; ++u) {
-            const int kb = kb0 + u;
-            const bool live = kb < hi;
-            const int kbc = live ? kb : last;
-#pragma unroll
-            for (int j = 0; j < NB; ++j) {
-                const v8i b = lds_frag(lds, b_off(j, kbc), lane);
-                mma_block<MTS, MODE>(acc[j], st[u], b, ws[u].sw[j], ws[u].ew[j], live);
-            }
+            block(u, kb0 + u);
             // keep the refill after this block's math and before the next
             // block's: the scheduler may not move arithmetic on fresh loads up
             __builtin_amdgcn_sched_barrier(0);
-            load(u, min(kb + R, last));
+            load(u, min(kb0 + u + R, last));
             __builtin_amdgcn_sched_barrier(0);
         }
     }
+#pragma unroll
+    for (int u = 0; u < R; ++u)
+        if (kb0 + u < hi) block(u, kb0 + u);
 }
 
 // Sum the WK partial accumulators of the waves that share M tiles; the wave
