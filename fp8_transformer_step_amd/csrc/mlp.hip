@@ -48,7 +48,8 @@ constexpr int kMaxKbGu = kLdsBytes / (2 * kFrag);        // 20: hidden <= 2560
 constexpr int kWaveKb = (kMaxKbGu + 3) / 4;               // K blocks per wave in gu_small
 constexpr int kSmallDownCols = 64;                        // down_small: 4 tiles x 4 K blocks
 constexpr int kSmallDownKb = 4;
-constexpr int kCtrlWords = 4096;   // fixed-size control region at workspace offset 0
+constexpr int kCtrlWords = 4096;
+constexpr int kGuFullItems = 512;  // gu items over the whole hidden dim: two per CU, 256 CUs (a multiple of 8)   // fixed-size control region at workspace offset 0
 
 // DOWN items of the LDS path: NB 16-column tiles, K range bounded by LDS.
 constexpr int kDownNb = 2;
@@ -63,6 +64,8 @@ struct MlpArgs {
     const uint8_t* wd; int64_t ldd; const void* sd; int64_t sd_r, sd_c;
     uint8_t* qx; void* sx;         // [MT][KBH] fragments of 16 rows x 128 K, and scales
     float* gbuf; float* ubuf;      // gate and up projections, fp32 [M][I]
+    int GF, GQ;                    // gu: items over the whole hidden dim; tiles split in K quarters
+    float* gtail;                  // [2][4][M][16*GQ] K-quarter partials of the split tiles (g, u)
     uint8_t* qh; void* sh;         // [MT][KBI] fragments of the quantised h, and scales
     float* ypart;                  // [NT][S][M][cols per tile] split partials
     int* cnt;                      // [NT] split counters (zero between calls)
@@ -73,6 +76,11 @@ struct MlpArgs {
     bool defer;                    // leave the down projection's split partials for the next kernel
 };
 
+__device__ __forceinline__ void load8(const float* p, float (&v)[8]) {
+    const float4 a = *reinterpret_cast<const float4*>(p), b = *reinterpret_cast<const float4*>(p + 4);
+    v[0] = a.x; v[1] = a.y; v[2] = a.z; v[3] = a.w; v[4] = b.x; v[5] = b.y; v[6] = b.z; v[7] = b.w;
+}
+
 // ---- hq: h = silu(g) * u -> q_h fragments (one workgroup per (M tile, K block))
 template <int MODE>
 __global__ __launch_bounds__(256) void hq_kernel(MlpArgs a) {
@@ -82,11 +90,27 @@ __global__ __launch_bounds__(256) void hq_kernel(MlpArgs a) {
 #pragma unroll
     for (int i = 0; i < 8; ++i) f[i] = 0.0f;
     if (m < a.M) {
-        const int64_t o = (int64_t)m * a.I + kb * 128 + 8 * j;
-        const float4 g0 = *reinterpret_cast<const float4*>(a.gbuf + o), g1 = *reinterpret_cast<const float4*>(a.gbuf + o + 4);
-        const float4 u0 = *reinterpret_cast<const float4*>(a.ubuf + o), u1 = *reinterpret_cast<const float4*>(a.ubuf + o + 4);
-        const float g[8] = {g0.x, g0.y, g0.z, g0.w, g1.x, g1.y, g1.z, g1.w};
-        const float u[8] = {u0.x, u0.y, u0.z, u0.w, u1.x, u1.y, u1.z, u1.w};
+        const int c = kb * 128 + 8 * j;
+        float g[8], u[8];
+        if (c < 16 * a.GF) {
+            const int64_t o = (int64_t)m * a.I + c;
+            load8(a.gbuf + o, g);
+            load8(a.ubuf + o, u);
+        } else {                               // a K-split tile: its quarters in order
+            const int64_t ld = 16 * (int64_t)a.GQ, o = (int64_t)m * ld + c - 16 * a.GF;
+            float t[8];
+            load8(a.gtail + o, g);
+            load8(a.gtail + 4 * a.M * ld + o, u);
+#pragma unroll
+            for (int q = 1; q < 4; ++q) {
+                load8(a.gtail + q * a.M * ld + o, t);
+#pragma unroll
+                for (int i = 0; i < 8; ++i) g[i] += t[i];
+                load8(a.gtail + (4 + q) * a.M * ld + o, t);
+#pragma unroll
+                for (int i = 0; i < 8; ++i) u[i] += t[i];
+            }
+        }
 #pragma unroll
         for (int i = 0; i < 8; ++i) f[i] = g[i] * __builtin_amdgcn_rcpf(1.0f + __expf(-g[i])) * u[i];
     }
@@ -206,6 +230,10 @@ __global__ __launch_bounds__(256) void gu_small_kernel(MlpArgs a) {
 }
 
 // ---- gu (M > 16): the weight slice in LDS, waves split M tiles and K -----------
+// The first GF items take 16 columns of gate and up over the whole hidden
+// dimension, two per CU; the GQ tiles left over are split into four K
+// quarters, so that the short items of that last round spread over the CUs
+// freed first.  A quarter writes its partial to gtail; hq sums the quarters.
 template <int MT, int MODE>
 __global__ __launch_bounds__(256, 2) void gu_kernel(MlpArgs a) {
     extern __shared__ __attribute__((aligned(1024))) uint8_t lds[];
@@ -213,11 +241,19 @@ __global__ __launch_bounds__(256, 2) void gu_kernel(MlpArgs a) {
     constexpr int MTS = WS::MTS, WK = WS::WK;
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
     const int wm = wave / WK, wk = wave % WK;
-    const int n0 = blockIdx.x * kGuCols;
+    int tile = blockIdx.x, q = -1, klo = 0, khi = a.KBH;
+    if (tile >= a.GF) {
+        const int t = tile - a.GF;
+        q = t / a.GQ;
+        tile = a.GF + t % a.GQ;
+        klo = q * a.KBH / 4;
+        khi = (q + 1) * a.KBH / 4;
+    }
+    const int n0 = tile * kGuCols, nkb = khi - klo;
 
-    for (int f = wave; f < 2 * a.KBH; f += 4) {
-        const bool up = f >= a.KBH;
-        const int kb = up ? f - a.KBH : f;
+    for (int f = wave; f < 2 * nkb; f += 4) {
+        const bool up = f >= nkb;
+        const int kb = klo + (up ? f - nkb : f);
         stage_w(up ? a.wu : a.wg, up ? a.ldu : a.ldg, n0, kb, lds, f * kFrag, lane);
     }
 
@@ -226,8 +262,8 @@ __global__ __launch_bounds__(256, 2) void gu_kernel(MlpArgs a) {
     for (int j = 0; j < 2; ++j)
 #pragma unroll
         for (int i = 0; i < MTS; ++i) acc[j][i] = v4f{0, 0, 0, 0};
-    const int lo = wk * a.KBH / WK, hi = (wk + 1) * a.KBH / WK;
-    auto b_off = [&](int j, int kb) { return (j * a.KBH + kb) * kFrag; };
+    const int lo = klo + wk * nkb / WK, hi = klo + (wk + 1) * nkb / WK;
+    auto b_off = [&](int j, int kb) { return (j * nkb + kb - klo) * kFrag; };
     auto wsc = [&](int j, int kb, float& sw, int& ew) {
         if (MODE == FP8S_MLP_BSGEMM)
             sw = j ? wscale_bs(a.su, a.su_r, a.su_c, n0, kb) : wscale_bs(a.sg, a.sg_r, a.sg_c, n0, kb);
@@ -245,9 +281,14 @@ __global__ __launch_bounds__(256, 2) void gu_kernel(MlpArgs a) {
 #pragma unroll
             for (int r = 0; r < 4; ++r) {
                 const int m = (wm * MTS + i) * 16 + 4 * (lane >> 4) + r;
-                if (m < a.M) {
+                if (m >= a.M) continue;
+                if (q < 0) {
                     a.gbuf[(int64_t)m * a.I + n0 + (lane & 15)] = acc[0][i][r];
                     a.ubuf[(int64_t)m * a.I + n0 + (lane & 15)] = acc[1][i][r];
+                } else {
+                    const int64_t ld = 16 * (int64_t)a.GQ, o = (int64_t)m * ld + n0 - 16 * a.GF + (lane & 15);
+                    a.gtail[(int64_t)q * a.M * ld + o] = acc[0][i][r];
+                    a.gtail[(int64_t)(4 + q) * a.M * ld + o] = acc[1][i][r];
                 }
             }
     }
@@ -439,8 +480,8 @@ __global__ __launch_bounds__(256, 2) void down_kernel(MlpArgs a) {
 
 // ---- host side ---------------------------------------------------------------
 struct MlpPlan {
-    int MT, KBH, KBI, NT, S;
-    size_t off_ctrl, off_qx, off_sx, off_g, off_u, off_qh, off_sh, off_ypart, total;
+    int MT, KBH, KBI, NT, S, GF, GQ;
+    size_t off_ctrl, off_qx, off_sx, off_g, off_u, off_gtail, off_qh, off_sh, off_ypart, total;
 };
 
 static size_t align_up(size_t v, size_t a) { return (v + a - 1) / a * a; }
@@ -460,6 +501,12 @@ static MlpPlan plan_mlp(int64_t M, int64_t H, int64_t I, int mode) {
         p.NT = (int)(H / (16 * kDownNb));
         p.S = (p.KBI + kDownMaxKb - 1) / kDownMaxKb;
     }
+    // gu: two whole-hidden items per CU (256 CUs) in the first round, the
+    // rest as K quarters (a multiple of 8 tiles, so no 128-column group of h
+    // mixes the two).
+    const int tiles = (int)(I / kGuCols);
+    p.GF = tiles <= kGuFullItems ? tiles : kGuFullItems;
+    p.GQ = tiles - p.GF;
     const size_t rows = 16 * (size_t)p.MT;
     const size_t cols = p.MT == 1 ? kSmallDownCols : 16 * kDownNb;
     // The control words sit at offset 0 in a region whose size does not
@@ -471,6 +518,7 @@ static MlpPlan plan_mlp(int64_t M, int64_t H, int64_t I, int mode) {
     p.off_sx = o; o = align_up(o + (mode == FP8S_MLP_BSGEMM ? rows * p.KBH * 4 : (size_t)p.MT * p.KBH * 64), 256);
     p.off_g = o; o = align_up(o + (size_t)M * I * 4, 256);
     p.off_u = o; o = align_up(o + (size_t)M * I * 4, 256);
+    p.off_gtail = o; o = align_up(o + (size_t)8 * M * p.GQ * kGuCols * 4, 256);
     p.off_qh = o; o = align_up(o + rows * I, 256);
     p.off_sh = o; o = align_up(o + (mode == FP8S_MLP_BSGEMM ? rows * p.KBI * 4 : (size_t)p.MT * p.KBI * 64), 256);
     p.off_ypart = o; o = align_up(o + (size_t)p.NT * p.S * M * cols * 4, 256);
@@ -485,7 +533,7 @@ static MlpPlan plan_mlp(int64_t M, int64_t H, int64_t I, int mode) {
 // prequant: the quantised x is already in the workspace (no xq launch).
 template <int MODE>
 static void launch_mlp(const MlpPlan& p, hipStream_t st, const MlpArgs& a, bool prequant) {
-    const dim3 blk(256), g_gu(a.I / kGuCols), g_xq(p.MT * p.KBH), g_hq(p.MT * p.KBI), g_dn(p.NT * p.S);
+    const dim3 blk(256), g_gu(a.I / kGuCols), g_gul(a.GF + 4 * a.GQ), g_xq(p.MT * p.KBH), g_hq(p.MT * p.KBI), g_dn(p.NT * p.S);
     if (a.M <= kTinyM && !a.norm_w && !prequant) {
         FP8S_LAUNCH("mlp_gu_small", gu_small_kernel<MODE>, g_gu, blk, 0, st, a);
         FP8S_LAUNCH("mlp_down_small_fused", (down_small_kernel<MODE, true>), g_dn, blk, 0, st, a);
@@ -497,13 +545,13 @@ static void launch_mlp(const MlpPlan& p, hipStream_t st, const MlpArgs& a, bool 
     }
     switch (p.MT) {
     case 1:
-        FP8S_LAUNCH("mlp_gu", (gu_kernel<1, MODE>), g_gu, blk, kLdsBytes, st, a);
+        FP8S_LAUNCH("mlp_gu", (gu_kernel<1, MODE>), g_gul, blk, kLdsBytes, st, a);
         FP8S_LAUNCH("mlp_hq", hq_kernel<MODE>, g_hq, blk, 0, st, a);
         FP8S_LAUNCH("mlp_down_small", (down_small_kernel<MODE, false>), g_dn, blk, 0, st, a);
         break;
 #define FP8S_MT_CASE(N)                                                                \
     case N:                                                                            \
-        FP8S_LAUNCH("mlp_gu", (gu_kernel<N, MODE>), g_gu, blk, kLdsBytes, st, a);      \
+        FP8S_LAUNCH("mlp_gu", (gu_kernel<N, MODE>), g_gul, blk, kLdsBytes, st, a);     \
         FP8S_LAUNCH("mlp_hq", hq_kernel<MODE>, g_hq, blk, 0, st, a);                    \
         FP8S_LAUNCH("mlp_down", (down_kernel<N, MODE>), g_dn, blk, kLdsBytes, st, a);   \
         break;
@@ -585,6 +633,8 @@ int swiglu_mlp_fp8_ex(const uint16_t* x, int64_t M, int64_t H, int64_t I, int mo
     a.qx = ws + p.off_qx; a.sx = ws + p.off_sx;
     a.gbuf = reinterpret_cast<float*>(ws + p.off_g);
     a.ubuf = reinterpret_cast<float*>(ws + p.off_u);
+    a.GF = p.GF; a.GQ = p.GQ;
+    a.gtail = reinterpret_cast<float*>(ws + p.off_gtail);
     a.qh = ws + p.off_qh; a.sh = ws + p.off_sh;
     a.ypart = reinterpret_cast<float*>(ws + p.off_ypart);
     a.cnt = reinterpret_cast<int*>(ws + p.off_ctrl);
