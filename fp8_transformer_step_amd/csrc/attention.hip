@@ -46,7 +46,22 @@ struct AttnArgs {
     uint8_t* qo;               // optional: the output quantised as the next GEMM's operand
     float* so;                 //   (1x128 groups = one head of D = 128, fp32 scales)
     int qo_KB;                 //   K blocks of that operand (Hq * D / 128)
+    // MXFP8 caches: e4m3 K/V bytes (strides sb, sh, st in bytes) and one UE8M0
+    // exponent per 32 consecutive d (byte strides esb, esh, est per row)
+    const uint8_t* kq; const uint8_t* ke; const uint8_t* vq; const uint8_t* ve;
+    int64_t esb, esh, est;
 };
+
+// UE8M0 byte -> 2^(E - 127) (E = 0 is the subnormal 2^-127).
+__device__ __forceinline__ float ue8m0_f32(uint32_t E) { return __uint_as_float(E ? E << 23 : 0x00400000u); }
+// Two OCP e4m3 bytes (bytes 0-1 or 2-3 of dw) times X, as a bf16 pair.  An
+// e4m3 value times a power of two has at most four significant bits, so the
+// product and its bf16 truncation are exact.
+template <bool HI>
+__device__ __forceinline__ uint32_t fp8x2_bf16x2(uint32_t dw, float X) {
+    const auto f = __builtin_amdgcn_cvt_pk_f32_fp8((int)dw, HI);
+    return (__float_as_uint(f[0] * X) >> 16) | (__float_as_uint(f[1] * X) & 0xFFFF0000u);
+}
 
 // Quantise one 128-column group kb of output row b (held by one wave: column
 // lane in v0, column lane + 64 in v1) the way the projection that follows
@@ -73,7 +88,12 @@ __device__ __forceinline__ bool kv_len_ok(int L, const AttnArgs& a) {
 // SINGLE: the whole prefix is one chunk (n_split == 1), so the kernel
 // normalises and writes the bf16 output itself (and handles an invalid
 // kv_len the way the merge does); no merge launch follows.
-template <int D, int G, bool SINGLE>
+// MX: the caches are MXFP8 (see AttnArgs); K and V are dequantised exactly
+// on load and the math is that of the bf16 path.  Lane group j4 = lane/16 of
+// the score MFMA then takes the D/4 consecutive d from j4*D/4, one scale
+// group, and the query operand is permuted the same way (the dot product
+// does not depend on the order of d).
+template <int D, int G, bool SINGLE, bool MX = false>
 __global__ __launch_bounds__(256) void attn_split_kernel(AttnArgs a) {
     constexpr int NJ = D / 32;                 // MFMA K-steps over the head dim
     constexpr int LPR = D / 8;                 // lanes per V row (8 bf16 each)
@@ -118,8 +138,9 @@ __global__ __launch_bounds__(256) void attn_split_kernel(AttnArgs a) {
 #pragma unroll
         for (int j = 0; j < NJ; ++j) {
             uint4 w = make_uint4(0, 0, 0, 0);
+            const int d0 = MX ? (lane >> 4) * (D / 4) + 8 * j : 32 * j + 8 * (lane >> 4);
             if (h < G)
-                w = *reinterpret_cast<const uint4*>(a.q + ((int64_t)b * a.Hq + g * G + h) * D + 32 * j + 8 * (lane >> 4));
+                w = *reinterpret_cast<const uint4*>(a.q + ((int64_t)b * a.Hq + g * G + h) * D + d0);
             qa[j] = __builtin_bit_cast(v8bf, w);
         }
     }
@@ -132,11 +153,32 @@ __global__ __launch_bounds__(256) void attn_split_kernel(AttnArgs a) {
         const bool live = tl < n_tok;
         v4f acc = {0, 0, 0, 0};
         uint4 kw[NJ];
+        if constexpr (MX) {
+            constexpr int QB = D / 4;            // bytes of the row per lane group: NJ pieces of 8
+            uint4 raw[QB / 16];
+            float X = 0.0f;
 #pragma unroll
-        for (int j = 0; j < NJ; ++j) {
-            kw[j] = make_uint4(0, 0, 0, 0);
-            if (live)
-                kw[j] = *reinterpret_cast<const uint4*>(kbase + (int64_t)(t_begin + tl) * a.st + 32 * j + 8 * (lane >> 4));
+            for (int i = 0; i < QB / 16; ++i) raw[i] = make_uint4(0, 0, 0, 0);
+            if (live) {
+                const int64_t t = t_begin + tl;
+                const uint8_t* src = a.kq + (int64_t)b * a.sb + (int64_t)g * a.sh + t * a.st + (lane >> 4) * QB;
+#pragma unroll
+                for (int i = 0; i < QB / 16; ++i) raw[i] = reinterpret_cast<const uint4*>(src)[i];
+                X = ue8m0_f32(a.ke[(int64_t)b * a.esb + (int64_t)g * a.esh + t * a.est + (lane >> 4) * QB / 32]);
+            }
+#pragma unroll
+            for (int j = 0; j < NJ; ++j) {
+                const uint32_t w0 = j & 1 ? raw[j / 2].z : raw[j / 2].x, w1 = j & 1 ? raw[j / 2].w : raw[j / 2].y;
+                kw[j] = make_uint4(fp8x2_bf16x2<false>(w0, X), fp8x2_bf16x2<true>(w0, X),
+                                   fp8x2_bf16x2<false>(w1, X), fp8x2_bf16x2<true>(w1, X));
+            }
+        } else {
+#pragma unroll
+            for (int j = 0; j < NJ; ++j) {
+                kw[j] = make_uint4(0, 0, 0, 0);
+                if (live)
+                    kw[j] = *reinterpret_cast<const uint4*>(kbase + (int64_t)(t_begin + tl) * a.st + 32 * j + 8 * (lane >> 4));
+            }
         }
 #pragma unroll
         for (int j = 0; j < NJ; ++j)
@@ -176,11 +218,24 @@ __global__ __launch_bounds__(256) void attn_split_kernel(AttnArgs a) {
     const int slot = lane / LPR;
 #pragma unroll 4
     for (int t = wave * TPL + slot; t < n_tok; t += 4 * TPL) {
-        const uint4 w = *reinterpret_cast<const uint4*>(vbase + (int64_t)(t_begin + t) * a.st + dl);
-        const uint32_t ww[4] = {w.x, w.y, w.z, w.w};
         float vf[8];
+        if constexpr (MX) {
+            const int64_t row = (int64_t)(t_begin + t);
+            const uint2 w = *reinterpret_cast<const uint2*>(a.vq + (int64_t)b * a.sb + (int64_t)g * a.sh + row * a.st + dl);
+            const float X = ue8m0_f32(a.ve[(int64_t)b * a.esb + (int64_t)g * a.esh + row * a.est + dl / 32]);
+            const uint32_t ww[2] = {w.x, w.y};
 #pragma unroll
-        for (int i = 0; i < 4; ++i) { vf[2 * i] = bf16_to_f32(ww[i] & 0xFFFFu); vf[2 * i + 1] = bf16_to_f32(ww[i] >> 16); }
+            for (int i = 0; i < 2; ++i) {
+                const auto lo = __builtin_amdgcn_cvt_pk_f32_fp8((int)ww[i], false);
+                const auto hi = __builtin_amdgcn_cvt_pk_f32_fp8((int)ww[i], true);
+                vf[4 * i] = lo[0] * X; vf[4 * i + 1] = lo[1] * X; vf[4 * i + 2] = hi[0] * X; vf[4 * i + 3] = hi[1] * X;
+            }
+        } else {
+            const uint4 w = *reinterpret_cast<const uint4*>(vbase + (int64_t)(t_begin + t) * a.st + dl);
+            const uint32_t ww[4] = {w.x, w.y, w.z, w.w};
+#pragma unroll
+            for (int i = 0; i < 4; ++i) { vf[2 * i] = bf16_to_f32(ww[i] & 0xFFFFu); vf[2 * i + 1] = bf16_to_f32(ww[i] >> 16); }
+        }
 #pragma unroll
         for (int h = 0; h < G; ++h) {
             const float p = s_p[h][t];
@@ -308,6 +363,8 @@ __global__ __launch_bounds__(256) void attn_merge_kernel(AttnArgs a) {
 }
 
 struct AttnPlan { int n_split, chunk; };
+template <bool MX>
+static int attn_launch(const AttnArgs& a, int D, int G, hipStream_t st);
 
 static AttnPlan plan_attn(int64_t B, int32_t Hkv, int64_t hint) {
     // Aim for >= 2048 workgroups so that all 256 CUs stay busy at small batch.
@@ -323,12 +380,42 @@ static AttnPlan plan_attn(int64_t B, int32_t Hkv, int64_t hint) {
     return p;
 }
 
-template <int D, int G>
-static void launch_split(dim3 grid, hipStream_t st, const AttnArgs& a) {
-    if (a.n_split == 1)
-        FP8S_LAUNCH("attn_single", (attn_split_kernel<D, G, true>), grid, dim3(256), 0, st, a);
+template <int D, int G, bool MX>
+static void launch_split(dim3 grid, hipStream_t st, const AttnArgs& a);
+
+// The split kernel (and the merge when there are several chunks).
+template <bool MX>
+static int attn_launch(const AttnArgs& a, int D, int G, hipStream_t st) {
+    const dim3 grid((unsigned)(a.B * a.Hkv * a.n_split));
+#define FP8S_ATTN_CASE(DD, GG) \
+    if (D == DD && G == GG) launch_split<DD, GG, MX>(grid, st, a);
+    FP8S_ATTN_CASE(64, 1) FP8S_ATTN_CASE(64, 2) FP8S_ATTN_CASE(64, 4) FP8S_ATTN_CASE(64, 8)
+    FP8S_ATTN_CASE(128, 1) FP8S_ATTN_CASE(128, 2) FP8S_ATTN_CASE(128, 4) FP8S_ATTN_CASE(128, 8)
+#undef FP8S_ATTN_CASE
+    int rc = check_launch("gqa_decode_attn (split)");
+    if (rc) return rc;
+    if (a.n_split == 1) return FP8S_OK;        // the split kernel wrote the output
+    const int64_t waves = (int64_t)a.B * ((a.Hq * D / 64 + 1) / 2);
+    const dim3 mgrid((unsigned)((waves + 3) / 4));
+    if (D == 64)
+        FP8S_LAUNCH("attn_merge", attn_merge_kernel<64>, mgrid, dim3(256), 0, st, a);
     else
+        FP8S_LAUNCH("attn_merge", attn_merge_kernel<128>, mgrid, dim3(256), 0, st, a);
+    return check_launch("gqa_decode_attn (merge)");
+}
+
+template <int D, int G, bool MX>
+static void launch_split(dim3 grid, hipStream_t st, const AttnArgs& a) {
+    if (MX) {
+        if (a.n_split == 1)
+            FP8S_LAUNCH("attn_single_mx", (attn_split_kernel<D, G, true, true>), grid, dim3(256), 0, st, a);
+        else
+            FP8S_LAUNCH("attn_split_mx", (attn_split_kernel<D, G, false, true>), grid, dim3(256), 0, st, a);
+    } else if (a.n_split == 1) {
+        FP8S_LAUNCH("attn_single", (attn_split_kernel<D, G, true>), grid, dim3(256), 0, st, a);
+    } else {
         FP8S_LAUNCH("attn_split", (attn_split_kernel<D, G, false>), grid, dim3(256), 0, st, a);
+    }
 }
 
 // The attention with, optionally (qo non-null), its output also quantised
@@ -371,23 +458,55 @@ int gqa_decode_attn_ex(const uint16_t* q, const uint16_t* k_cache, const uint16_
     a.out = out;
     a.err = err_flag;
     a.qo = qo; a.so = so; a.qo_KB = Hq * D / 128;
-    hipStream_t st = as_stream(stream);
-    const dim3 grid((unsigned)(B * Hkv * p.n_split));
-#define FP8S_ATTN_CASE(DD, GG) \
-    if (D == DD && G == GG) launch_split<DD, GG>(grid, st, a);
-    FP8S_ATTN_CASE(64, 1) FP8S_ATTN_CASE(64, 2) FP8S_ATTN_CASE(64, 4) FP8S_ATTN_CASE(64, 8)
-    FP8S_ATTN_CASE(128, 1) FP8S_ATTN_CASE(128, 2) FP8S_ATTN_CASE(128, 4) FP8S_ATTN_CASE(128, 8)
-#undef FP8S_ATTN_CASE
-    int rc = check_launch("gqa_decode_attn (split)");
-    if (rc) return rc;
-    if (p.n_split == 1) return FP8S_OK;        // the split kernel wrote the output
-    const int64_t waves = B * ((Hq * D / 64 + 1) / 2);
-    const dim3 mgrid((unsigned)((waves + 3) / 4));
-    if (D == 64)
-        FP8S_LAUNCH("attn_merge", attn_merge_kernel<64>, mgrid, dim3(256), 0, st, a);
-    else
-        FP8S_LAUNCH("attn_merge", attn_merge_kernel<128>, mgrid, dim3(256), 0, st, a);
-    return check_launch("gqa_decode_attn (merge)");
+    a.kq = a.ke = a.vq = a.ve = nullptr;
+    a.esb = a.esh = a.est = 0;
+    return attn_launch<false>(a, D, G, as_stream(stream));
+}
+
+// MXFP8 caches (kq/ke, vq/ve): the checks and layout rules of the bf16 path,
+// with byte strides; the query, output and workspace are as there.
+static int gqa_decode_attn_mxkv_ex(const uint16_t* q, const uint8_t* kq, const uint8_t* ke, const uint8_t* vq,
+                            const uint8_t* ve, int64_t stride_b, int64_t stride_h, int64_t stride_t, int64_t sstride_b,
+                            int64_t sstride_h, int64_t sstride_t, const int32_t* kv_len, int64_t B, int32_t Hq,
+                            int32_t Hkv, int32_t D, int64_t cap, int64_t hint, float softmax_scale, uint16_t* out,
+                            void* workspace, size_t workspace_bytes, int32_t* err_flag, void* stream) {
+    FP8S_REQUIRE(q && kq && ke && vq && ve && kv_len && out, FP8S_EINVAL, "gqa_decode_attn_mxkv: null pointer");
+    FP8S_REQUIRE(B >= 1 && Hq >= 1 && Hkv >= 1 && cap >= 1 && hint >= 1, FP8S_EINVAL,
+                 "gqa_decode_attn_mxkv: sizes must be positive");
+    FP8S_REQUIRE(Hq % Hkv == 0, FP8S_EINVAL, "gqa_decode_attn_mxkv: Hq=%d is not a multiple of Hkv=%d", Hq, Hkv);
+    const int G = Hq / Hkv;
+    FP8S_REQUIRE(D == 64 || D == 128, FP8S_EUNSUPPORTED, "gqa_decode_attn_mxkv: head dim %d (64 or 128 supported)",
+                 D);
+    FP8S_REQUIRE(G == 1 || G == 2 || G == 4 || G == 8, FP8S_EUNSUPPORTED,
+                 "gqa_decode_attn_mxkv: group size %d (1, 2, 4 or 8 supported)", G);
+    FP8S_REQUIRE(stride_t >= D && stride_t % 16 == 0 && stride_h % 16 == 0 && stride_b % 16 == 0, FP8S_EINVAL,
+                 "gqa_decode_attn_mxkv: e4m3 byte strides must be multiples of 16 with stride_t >= D");
+    FP8S_REQUIRE(sstride_t >= D / 32 && sstride_b >= 0 && sstride_h >= 0, FP8S_EINVAL,
+                 "gqa_decode_attn_mxkv: scale strides must be non-negative with sstride_t >= D/32");
+    FP8S_REQUIRE(aligned16(q) && aligned16(kq) && aligned16(vq) && aligned16(out), FP8S_EINVAL,
+                 "gqa_decode_attn_mxkv: q, caches and out must be 16-byte aligned");
+    FP8S_REQUIRE(B * Hkv <= (1ll << 24), FP8S_EUNSUPPORTED, "gqa_decode_attn_mxkv: batch too large");
+    if (hint > cap) hint = cap;
+    const AttnPlan p = plan_attn(B, Hkv, hint);
+    const size_t need = (size_t)B * Hq * p.n_split * (D + 2) * sizeof(float);
+    FP8S_REQUIRE(workspace && aligned16(workspace), FP8S_EWORKSPACE,
+                 "gqa_decode_attn_mxkv: workspace missing or unaligned");
+    FP8S_REQUIRE(workspace_bytes >= need, FP8S_EWORKSPACE, "gqa_decode_attn_mxkv: workspace %zu < required %zu bytes",
+                 workspace_bytes, need);
+    AttnArgs a;
+    a.q = q; a.k = a.v = nullptr;
+    a.kq = kq; a.ke = ke; a.vq = vq; a.ve = ve;
+    a.sb = stride_b; a.sh = stride_h; a.st = stride_t;
+    a.esb = sstride_b; a.esh = sstride_h; a.est = sstride_t;
+    a.kv_len = kv_len;
+    a.B = (int)B; a.Hq = Hq; a.Hkv = Hkv; a.n_split = p.n_split; a.chunk = p.chunk;
+    a.cap = cap; a.hint = hint;
+    a.scale_log2 = softmax_scale * 1.4426950408889634f;
+    a.part = static_cast<float*>(workspace);
+    a.out = out;
+    a.err = err_flag;
+    a.qo = nullptr; a.so = nullptr; a.qo_KB = Hq * D / 128;
+    return attn_launch<true>(a, D, G, as_stream(stream));
 }
 
 }  // namespace fp8s
@@ -399,6 +518,18 @@ extern "C" size_t gqa_decode_attn_workspace_size(int64_t B, int32_t Hq, int32_t 
     // The split count never exceeds ceil(max_kv_len / 16).
     const int64_t max_split = (max_kv_len + 15) / 16;
     return (size_t)B * Hq * max_split * (D + 2) * sizeof(float);
+}
+
+extern "C" int gqa_decode_attn_mxkv(const uint16_t* q, const uint8_t* k_q, const uint8_t* k_e, const uint8_t* v_q,
+                                    const uint8_t* v_e, int64_t stride_b, int64_t stride_h, int64_t stride_t,
+                                    int64_t sstride_b, int64_t sstride_h, int64_t sstride_t, const int32_t* kv_len,
+                                    int64_t B, int32_t Hq, int32_t Hkv, int32_t D, int64_t cap, int64_t hint,
+                                    float softmax_scale, uint16_t* out, void* workspace, size_t workspace_bytes,
+                                    int32_t* err_flag, void* stream) {
+    clear_error();
+    return gqa_decode_attn_mxkv_ex(q, k_q, k_e, v_q, v_e, stride_b, stride_h, stride_t, sstride_b, sstride_h,
+                                   sstride_t, kv_len, B, Hq, Hkv, D, cap, hint, softmax_scale, out, workspace,
+                                   workspace_bytes, err_flag, stream);
 }
 
 extern "C" int gqa_decode_attn(const uint16_t* q, const uint16_t* k_cache, const uint16_t* v_cache,

@@ -157,6 +157,54 @@ def gqa_decode_attn(q, k_cache, v_cache, kv_len, max_kv_len_hint, softmax_scale=
     return out
 
 
+@dataclass
+class MxKvCache:
+    """An MXFP8 KV cache: e4m3 bytes q [B, Hkv, cap, D] and UE8M0 exponents
+    e [B, Hkv, cap, D/32] (one per 32 consecutive d)."""
+    q: torch.Tensor
+    e: torch.Tensor
+
+
+def quantize_kv_mx(cache_bf16):
+    """Quantise a bf16 cache [B, Hkv, cap, D] (contiguous) row by row in 1x32
+    groups (qlinear_quantize mode 2, row-major exponents)."""
+    if not cache_bf16.is_contiguous():
+        raise ValueError("the cache must be contiguous")
+    B, Hkv, cap, D = cache_bf16.shape
+    rows = cache_bf16.view(B * Hkv * cap, D)
+    e = torch.empty((B * Hkv * cap, D // 32), dtype=torch.uint8, device=cache_bf16.device)
+    q, e = qlinear_quantize(rows, Q_MX_1x32, scale=e)
+    return MxKvCache(q.view(B, Hkv, cap, D), e.view(B, Hkv, cap, D // 32))
+
+
+def gqa_decode_attn_mxkv(q, k, v, kv_len, max_kv_len_hint, softmax_scale=None,
+                         out=None, workspace=None, err=None):
+    """Decode attention of q [B, Hq, D] over MXFP8 caches k, v (MxKvCache)."""
+    _require_cuda(q, k.q, k.e, v.q, v.e, kv_len)
+    if kv_len.dtype != torch.int32:
+        raise TypeError("kv_len must be int32")
+    if k.q.stride() != v.q.stride() or k.e.stride() != v.e.stride() or k.q.shape != v.q.shape:
+        raise ValueError("k and v must share shapes and strides")
+    B, Hq, D = q.shape
+    _, Hkv, cap, _ = k.q.shape
+    if k.q.stride(3) != 1 or k.e.stride(3) != 1:
+        raise ValueError("the head dimension must be contiguous")
+    if softmax_scale is None:
+        softmax_scale = 1.0 / math.sqrt(D)
+    if out is None:
+        out = torch.empty((B, Hq, D), dtype=torch.bfloat16, device=q.device)
+    hint = min(int(max_kv_len_hint), cap)
+    if workspace is None:
+        workspace = new_attn_workspace(B, Hq, D, hint, q.device)
+    _lib.check(_lib.load().gqa_decode_attn_mxkv(
+        _bits(q.contiguous()), k.q.data_ptr(), k.e.data_ptr(), v.q.data_ptr(), v.e.data_ptr(),
+        k.q.stride(0), k.q.stride(1), k.q.stride(2), k.e.stride(0), k.e.stride(1), k.e.stride(2),
+        kv_len.data_ptr(), B, Hq, Hkv, D, cap, hint, float(softmax_scale),
+        _bits(out), workspace.data_ptr(), workspace.numel(),
+        err.data_ptr() if err is not None else None, _stream()))
+    return out
+
+
 def _opt_ptr(t):
     return t.data_ptr() if t is not None else None
 

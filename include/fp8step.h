@@ -186,6 +186,36 @@ FP8S_API int gqa_decode_attn(const uint16_t* q, const uint16_t* k_cache, const u
                     int32_t* err_flag, void* stream);
 
 /*
+ * gqa_decode_attn_mxkv -- gqa_decode_attn over MXFP8 KV caches: the pages'
+ * FP8/MX decode-attention variant ([TTS] "What's Open Source": MXFP8
+ * FlashAttention; "FP8 Quantization Strategy": 1x32 groups with OCP UE8M0
+ * shared exponents).  Each cache row of D values is stored as D e4m3 bytes
+ * and D/32 UE8M0 exponents, one per 32 consecutive d (the row quantised as
+ * qlinear_quantize mode 2 does), so K[b,g,t,d] = e4m3(k_q) * 2^(E - 127).
+ * The output is that of gqa_decode_attn on the dequantised caches; K and V
+ * are dequantised exactly on load and the math is the bf16 path's.
+ *
+ *   k_q, v_q   e4m3 bytes, element (b, g, t, d) at
+ *              b * stride_b + g * stride_h + t * stride_t + d; the byte
+ *              strides are multiples of 16, stride_t >= D, 16-byte aligned.
+ *   k_e, v_e   UE8M0 bytes, exponent (b, g, t, d/32) at
+ *              b * sstride_b + g * sstride_h + t * sstride_t + d/32.
+ *   Everything else (q, kv_len, hint, scale, out, workspace, err_flag, the
+ *   supported D and group sizes, the error behaviour) as gqa_decode_attn;
+ *   the workspace is sized by gqa_decode_attn_workspace_size.
+ *   Accuracy: max|out - oracle| <= 5e-3 * max|oracle|, oracle = exact
+ *   attention over the dequantised caches.
+ */
+FP8S_API int gqa_decode_attn_mxkv(const uint16_t* q, const uint8_t* k_q, const uint8_t* k_e,
+                    const uint8_t* v_q, const uint8_t* v_e,
+                    int64_t stride_b, int64_t stride_h, int64_t stride_t,
+                    int64_t sstride_b, int64_t sstride_h, int64_t sstride_t,
+                    const int32_t* kv_len, int64_t B, int32_t Hq, int32_t Hkv, int32_t D,
+                    int64_t cap, int64_t max_kv_len_hint, float softmax_scale,
+                    uint16_t* out, void* workspace, size_t workspace_bytes,
+                    int32_t* err_flag, void* stream);
+
+/*
  * qlinear_fp8 -- y = [residual +] dequant(quant(norm(x))) . dequant(W)^T, the
  * FP8 projections of a decode block other than the MLP ([TTS] "FP8
  * Quantization Strategy", "Kernel Benchmark Results").

@@ -17,14 +17,25 @@ optimisation notes):
 
 The loop below never touches cache positions t >= kv_len[b].
 
+The MXFP8-cache variant (gqa_decode_attention_mxkv) is the pages' FP8/MX
+decode attention (page "How We Made Our Text-to-Speech API Free", sections
+"What's Open Source" and "FP8 Quantization Strategy"): each cache row is held
+as e4m3 codes with one OCP UE8M0 exponent per 32 consecutive d, and the
+attention is the one above over the dequantised rows.
+
 Pins (tests/test_oracle_attention.py): kv_len = 1 returns v_0; q = 0 returns
 the mean of the V prefix; equality with an explicit np.repeat expansion of the
 heads; torch's float64 scaled_dot_product_attention on the expanded heads;
 active-prefix equals full-cache-plus-mask within rtol 1e-5 / atol 1e-6 (the
 tolerance of the page's section 7 test); the kv_len schedule of section 5.
+MXFP8 variant: on caches built from MX-representable rows (so that the OCP
+rule gives back the codes and exponents they were built from) it equals the
+plain attention over those rows, and kv_len = 1 returns the dequantised v_0.
 """
 
 import numpy as np
+
+from . import fp8
 
 
 def kv_len_schedule(prompt_len, decode_index=None):
@@ -66,3 +77,21 @@ def gqa_decode_attention(q, k_cache, v_cache, kv_len, scale=None):
             p /= p.sum()
             out[b, h] = p @ V
     return out
+
+
+def dequant_mx_rows(codes, exps):
+    """Exact float64 values of MX rows: codes [..., D] uint8 (OCP e4m3) and
+    exps [..., D/32] uint8 (UE8M0, one per 32 consecutive entries)."""
+    codes = np.asarray(codes)
+    D = codes.shape[-1]
+    flat = fp8.dequant_mx_1x32(codes.reshape(-1, D), np.asarray(exps).reshape(-1, D // 32))
+    return flat.reshape(codes.shape)
+
+
+def gqa_decode_attention_mxkv(q, k_codes, k_exps, v_codes, v_exps, kv_len, scale=None):
+    """gqa_decode_attention over MXFP8 caches: k_codes, v_codes [B, Hkv, T, D]
+    e4m3 bytes, k_exps, v_exps [B, Hkv, T, D/32] UE8M0 bytes.  Only rows
+    t < kv_len[b] enter the result (the dequantisation is elementwise)."""
+    k = dequant_mx_rows(k_codes, k_exps)
+    v = dequant_mx_rows(v_codes, v_exps)
+    return gqa_decode_attention(q, k, v, kv_len, scale)

@@ -92,6 +92,21 @@ def test_attention_argument_checks():
     assert call(32, 8, 128, 128, 16) == EWORKSPACE
 
 
+def test_attention_mxkv_argument_checks():
+    lib = _lib.load()
+    ws = lib.gqa_decode_attn_workspace_size(2, 32, 128, 400)
+    call = lambda Hq, Hkv, D, st, sst, wsb: lib.gqa_decode_attn_mxkv(
+        FAKE, FAKE, FAKE, FAKE, FAKE, 8 * 32768 * 128, 32768 * 128, st, 8 * 32768 * 4, 32768 * 4, sst, FAKE,
+        2, Hq, Hkv, D, 32768, 400, ctypes.c_float(0.088), FAKE, FAKE, wsb, None, None)
+    assert call(32, 6, 128, 128, 4, ws) == EINVAL           # Hq % Hkv
+    assert call(32, 8, 96, 128, 4, ws) == EUNSUPPORTED      # head dim
+    assert call(32, 8, 128, 120, 4, ws) == EINVAL           # byte stride not a multiple of 16
+    assert call(32, 8, 128, 128, 3, ws) == EINVAL           # fewer than D/32 exponents per row
+    assert call(32, 8, 128, 128, 4, 16) == EWORKSPACE
+    assert lib.gqa_decode_attn_mxkv(FAKE, None, FAKE, FAKE, FAKE, 0, 0, 128, 0, 0, 4, FAKE, 2, 32, 8, 128,
+                                    32768, 400, ctypes.c_float(0.088), FAKE, FAKE, ws, None, None) == EINVAL
+
+
 @pytest.mark.parametrize("M,H,I", [(1, 2560, 9728), (128, 2560, 9728), (1, 256, 1024)])
 def test_mlp_workspace_is_small(M, H, I):
     n = _lib.load().swiglu_mlp_fp8_workspace_size(M, H, I, 0)

@@ -7,7 +7,7 @@ import os
 import numpy as np
 import torch
 
-from oracle import attention
+from oracle import attention, fp8
 
 GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
 
@@ -98,3 +98,45 @@ def test_golden_kv_len_schedule():
         idx = int(idx)
         got = attention.kv_len_schedule(234, None if idx < 0 else idx)
         assert got == int(kv), (phase, idx)
+
+
+def _mx_representable(g, shape):
+    """Rows of 32-groups built from e4m3 codes and UE8M0 exponents such that
+    every group holds a code of the top binade (256..448), so the OCP rule
+    returns the very exponent, and dividing by it the very codes."""
+    D = shape[-1]
+    n_groups = int(np.prod(shape[:-1])) * (D // 32)
+    codes = g.integers(0, 256, size=(n_groups, 32)).astype(np.uint8)
+    codes[(codes & 0x7F) == 0x7F] &= 0xF7                    # no NaN codes
+    top = g.integers(0x78, 0x7F, size=n_groups).astype(np.uint8) | (g.integers(0, 2, size=n_groups) << 7).astype(np.uint8)
+    codes[np.arange(n_groups), g.integers(0, 32, size=n_groups)] = top
+    exps = g.integers(110, 140, size=n_groups).astype(np.uint8)
+    vals = fp8.e4m3_decode(codes) * np.ldexp(1.0, exps.astype(np.int64) - 127)[:, None]
+    return (vals.reshape(shape), codes.reshape(shape),
+            exps.reshape(tuple(shape[:-1]) + (D // 32,)))
+
+
+def test_mxkv_equals_plain_attention_on_representable_rows():
+    g = np.random.default_rng(11)
+    B, Hq, Hkv, D, T = 2, 8, 2, 64, 50
+    q = g.standard_normal((B, Hq, D))
+    kval, kc, ke = _mx_representable(g, (B, Hkv, T, D))
+    vval, vc, ve = _mx_representable(g, (B, Hkv, T, D))
+    # the OCP quantiser gives back the codes and exponents the rows came from
+    qk, ek = fp8.quant_mx_1x32(kval.reshape(-1, D).astype(np.float32))
+    assert np.array_equal(qk, kc.reshape(-1, D)) and np.array_equal(ek, ke.reshape(-1, D // 32))
+    L = np.array([50, 13])
+    out = attention.gqa_decode_attention_mxkv(q, kc, ke, vc, ve, L)
+    ref = attention.gqa_decode_attention(q, kval, vval, L)
+    assert np.allclose(out, ref, rtol=1e-12, atol=0)
+
+
+def test_mxkv_kv_len_one_returns_dequantised_first_value():
+    g = np.random.default_rng(12)
+    B, Hq, Hkv, D, T = 2, 4, 1, 64, 9
+    q = g.standard_normal((B, Hq, D))
+    _, kc, ke = _mx_representable(g, (B, Hkv, T, D))
+    vval, vc, ve = _mx_representable(g, (B, Hkv, T, D))
+    out = attention.gqa_decode_attention_mxkv(q, kc, ke, vc, ve, np.ones(B, int))
+    for h in range(Hq):
+        assert np.array_equal(out[:, h], vval[:, 0, 0])
