@@ -69,13 +69,16 @@ def kernel_bytes(name, M, mode, kv_len=None, B=None):
         return 2 * M * I * 4 + M * I + _ascale_bytes(M, I, mode)
     if name == "attn_split":
         return int(np.sum(kv_len.astype(np.int64))) * HKV * D * 2 * 2 + B * HQ * D * 2 + 4 * B
+    if name == "attn_split_mx":
+        return int(np.sum(kv_len.astype(np.int64))) * HKV * (D + D // 32) * 2 + B * HQ * D * 2 + 4 * B
     if name == "attn_merge":
         return B * HQ * D * 2 + 4 * B
     return 0
 
 
-def attn_bytes(kv_len, B):
-    return int(np.sum(kv_len.astype(np.int64))) * HKV * D * 2 * 2 + 2 * B * HQ * D * 2 + 4 * B
+def attn_bytes(kv_len, B, mx=False):
+    row = D + D // 32 if mx else 2 * D         # bytes per cached row: e4m3 + UE8M0, or bf16
+    return int(np.sum(kv_len.astype(np.int64))) * HKV * row * 2 + 2 * B * HQ * D * 2 + 4 * B
 
 
 def log(msg):
@@ -85,8 +88,9 @@ def log(msg):
 class Workload:
     """Rotating sets of GPU-resident weights, activations and KV caches."""
 
-    def __init__(self, torch, ops, B, M, mode, n_sets, kv_len, with_attn=True, with_mlp=True):
+    def __init__(self, torch, ops, B, M, mode, n_sets, kv_len, with_attn=True, with_mlp=True, mx_kv=False):
         self.torch, self.ops = torch, ops
+        self.mx_kv = mx_kv
         self.B, self.M, self.mode = B, M, mode
         self.sets = []
         g = torch.Generator(device="cuda")
@@ -113,6 +117,8 @@ class Workload:
                 vc = torch.empty((B, HKV, CAP, D), dtype=torch.bfloat16, device="cuda")
                 kc[:, :, :Lmax] = torch.randn((B, HKV, Lmax, D), generator=g, device="cuda").to(torch.bfloat16)
                 vc[:, :, :Lmax] = torch.randn((B, HKV, Lmax, D), generator=g, device="cuda").to(torch.bfloat16)
+                if mx_kv:                               # MXFP8 caches, quantised from the bf16 ones
+                    kc, vc = ops.quantize_kv_mx(kc), ops.quantize_kv_mx(vc)
                 st["k"], st["v"] = kc, vc
                 st["q"] = torch.randn((B, HQ, D), generator=g, device="cuda").to(torch.bfloat16)
                 st["o"] = torch.empty((B, HQ, D), dtype=torch.bfloat16, device="cuda")
@@ -128,8 +134,8 @@ class Workload:
 
     def attn(self, s):
         st = self.sets[s]
-        self.ops.gqa_decode_attn(st["q"], st["k"], st["v"], st["kv"], st["hint"], out=st["o"],
-                                 workspace=st["aws"], err=self.err)
+        fn = self.ops.gqa_decode_attn_mxkv if self.mx_kv else self.ops.gqa_decode_attn
+        fn(st["q"], st["k"], st["v"], st["kv"], st["hint"], out=st["o"], workspace=st["aws"], err=self.err)
 
 
 def time_parts(torch, ops, wl, parts, steps, warmup):
@@ -454,15 +460,18 @@ def main():
                     " ".join(f"{k}={v['us']:.1f}" for k, v in sweep[key][M]["kernels"].items()))
                 del w
                 torch.cuda.empty_cache()
-        for Bs, lo, hi in ((1, 234, 400), (16, 234, 400), (64, 234, 400), (64, 234, 8192)):
+        sweep["attn_mxkv"] = {}
+        for Bs, lo, hi, mx in ((1, 234, 400, False), (16, 234, 400, False), (64, 234, 400, False),
+                               (64, 234, 4096, False), (64, 234, 8192, False),
+                               (64, 234, 4096, True), (64, 234, 8192, True)):
             kv = inputs.kv_lengths(inputs.W_ATTN, Bs, lo, hi, extra=Bs + hi)
-            w = Workload(torch, ops, Bs, 1, 0, 2 if hi > 400 else args.sets, kv, with_mlp=False)
+            w = Workload(torch, ops, Bs, 1, 0, 2 if hi > 400 else args.sets, kv, with_mlp=False, mx_kv=mx)
             t, _, per = time_parts(torch, ops, w, [w.attn], 20, 5)
-            gb = attn_bytes(kv, Bs) / (t * 1e-3) / 1e9
-            sweep["attn"][f"B={Bs},kv=U[{lo},{hi}]"] = {"us": t * 1e3, "tokens/s": Bs / (t * 1e-3), "GB/s": gb,
-                                                        "frac": gb / PEAK_HBM_GBS,
-                                                        "kernels": kernel_table(per, 20, 1, 0, kv, Bs)}
-            log(f"attn B={Bs} kv {lo}..{hi}: {t * 1e3:.1f} us {gb:.0f} GB/s")
+            gb = attn_bytes(kv, Bs, mx) / (t * 1e-3) / 1e9
+            sweep["attn_mxkv" if mx else "attn"][f"B={Bs},kv=U[{lo},{hi}]"] = {
+                "us": t * 1e3, "tokens/s": Bs / (t * 1e-3), "GB/s": gb, "frac": gb / PEAK_HBM_GBS,
+                "kernels": kernel_table(per, 20, 1, 0, kv, Bs)}
+            log(f"attn{' mxkv' if mx else ''} B={Bs} kv {lo}..{hi}: {t * 1e3:.1f} us {gb:.0f} GB/s")
             del w
             torch.cuda.empty_cache()
         result["sweep"] = sweep

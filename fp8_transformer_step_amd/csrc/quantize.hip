@@ -59,16 +59,24 @@ __device__ __forceinline__ uint32_t amax8_bits(uint4 v) {
 }
 
 // Row groups (1 x GROUP): each lane owns 8 consecutive elements, GROUP/8
-// lanes own a group.  Blocks are laid out row-major over (row, 2048-column
-// chunk); a group never straddles two blocks because cols % GROUP == 0.
+// lanes own a group.  Rows wider than 2048: blocks laid out row-major over
+// (row, 2048-column chunk).  Narrower rows: 2^lpr_log2 lanes per row (a power
+// of two >= cols/8) and 256 >> lpr_log2 rows per block.  A group never
+// straddles two blocks or two rows because cols % GROUP == 0.
 template <int GROUP>
 __global__ __launch_bounds__(256) void quant_rows_kernel(
-    const uint16_t* __restrict__ x, int64_t ld_x, int64_t cols, int64_t blocks_per_row,
-    uint8_t* __restrict__ q, int64_t ld_q, void* __restrict__ scale, int64_t ssr, int64_t ssc) {
+    const uint16_t* __restrict__ x, int64_t ld_x, int64_t rows, int64_t cols, int64_t blocks_per_row,
+    int lpr_log2, uint8_t* __restrict__ q, int64_t ld_q, void* __restrict__ scale, int64_t ssr, int64_t ssc) {
     constexpr int LANES = GROUP / 8;
-    const int64_t row = blockIdx.x / blocks_per_row;
-    const int64_t col0 = (blockIdx.x % blocks_per_row) * 2048 + 8 * (int64_t)threadIdx.x;
-    const bool valid = col0 < cols;
+    int64_t row, col0;
+    if (lpr_log2) {
+        row = (int64_t)blockIdx.x * (256 >> lpr_log2) + (threadIdx.x >> lpr_log2);
+        col0 = 8 * (int64_t)(threadIdx.x & ((1 << lpr_log2) - 1));
+    } else {
+        row = blockIdx.x / blocks_per_row;
+        col0 = (blockIdx.x % blocks_per_row) * 2048 + 8 * (int64_t)threadIdx.x;
+    }
+    const bool valid = row < rows && col0 < cols;
     uint4 v = make_uint4(0, 0, 0, 0);
     if (valid) v = *reinterpret_cast<const uint4*>(x + row * ld_x + col0);
     uint32_t amax = umax_xor<LANES>(amax8_bits(v));
@@ -153,12 +161,16 @@ extern "C" int qlinear_quantize(const uint16_t* x, int64_t rows, int64_t cols, i
         return check_launch("qlinear_quantize");
     }
     const int64_t bpr = (cols + 2047) / 2048;
-    FP8S_REQUIRE(rows * bpr < (1ll << 31), FP8S_EUNSUPPORTED, "qlinear_quantize: matrix too large");
+    int lpr_log2 = 0;                          // rows of at most 2048: several per block
+    if (cols < 2048)
+        while ((8ll << lpr_log2) < cols) ++lpr_log2;
+    const int64_t nblk = lpr_log2 ? (rows + (256 >> lpr_log2) - 1) / (256 >> lpr_log2) : rows * bpr;
+    FP8S_REQUIRE(nblk < (1ll << 24), FP8S_EUNSUPPORTED, "qlinear_quantize: matrix too large");
     if (mode == FP8S_Q_ACT_1x128)
-        FP8S_LAUNCH("quantize_1x128", quant_rows_kernel<128>, dim3((unsigned)(rows * bpr)), dim3(256), 0, st, x, ld_x,
-                    cols, bpr, q, ld_q, scale, ssr, ssc);
+        FP8S_LAUNCH("quantize_1x128", quant_rows_kernel<128>, dim3((unsigned)nblk), dim3(256), 0, st, x, ld_x, rows,
+                    cols, bpr, lpr_log2, q, ld_q, scale, ssr, ssc);
     else
-        FP8S_LAUNCH("quantize_1x32", quant_rows_kernel<32>, dim3((unsigned)(rows * bpr)), dim3(256), 0, st, x, ld_x,
-                    cols, bpr, q, ld_q, scale, ssr, ssc);
+        FP8S_LAUNCH("quantize_1x32", quant_rows_kernel<32>, dim3((unsigned)nblk), dim3(256), 0, st, x, ld_x, rows,
+                    cols, bpr, lpr_log2, q, ld_q, scale, ssr, ssc);
     return check_launch("qlinear_quantize");
 }
