@@ -290,6 +290,36 @@ def time_step(torch, ops, dm, kv, prev, steps, warmup, workspace, err):
     return ms, wall, ops.profile_stop()
 
 
+def time_step_graph(torch, ops, dm, kv, prev, steps, warmup, workspace, err):
+    """ms per step when the step is captured once into a HIP graph and
+    replayed (every kernel of every step still runs; the host launches one
+    graph per step instead of each kernel)."""
+    codes = torch.empty(prev.shape, dtype=torch.int32, device="cuda")
+
+    def step():
+        ops.dual_ar_decode_step(dm, kv, prev, codes=codes, workspace=workspace, err=err)
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        step()
+    torch.cuda.current_stream().wait_stream(side)
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        step()
+    for _ in range(warmup):
+        graph.replay()
+    torch.cuda.synchronize()
+    t0 = torch.cuda.Event(enable_timing=True)
+    t1 = torch.cuda.Event(enable_timing=True)
+    t0.record()
+    for _ in range(steps):
+        graph.replay()
+    t1.record()
+    torch.cuda.synchronize()
+    del graph
+    return t0.elapsed_time(t1) / steps
+
+
 def step_kernel_table(recs, plan, steps):
     """{kernel: launches per step, us per step, us per launch, algorithmic
     bytes per step and per launch, GB/s, fraction of peak}; checks that the
@@ -395,6 +425,8 @@ def main():
     torch.cuda.synchronize()
     log(f"bench: timing {args.steps} steps after {args.warmup} warm-up steps")
     ms_step, wall, recs = time_step(torch, ops, dm, kv, prev, args.steps, args.warmup, workspace, err)
+    ms_graph = time_step_graph(torch, ops, dm, kv, prev, args.steps, args.warmup, workspace, err)
+    log(f"step as a replayed HIP graph: {ms_graph:.3f} ms (eager {ms_step:.3f} ms)")
     if int(err.item()) != 0:
         raise SystemExit(f"device error flag {int(err.item())}")
     plan = step_launch_plan(cfg, host.kv_len)
@@ -442,6 +474,8 @@ def main():
         "parts": parts,
         "kernels": ktab,
         "wall_ms_per_step": wall,
+        "ms_per_step_eager": ms_step,
+        "ms_per_step_graph": ms_graph,
     }
     del dm, kv, workspace, prev
     torch.cuda.empty_cache()
