@@ -22,6 +22,8 @@
 //     on the VALU with V rows loaded 16 bytes per lane, reduced across lanes
 //     and waves; the chunk's (max, sum, acc) goes to the workspace.
 //   * A second small kernel merges the chunks of every (sequence, head).
+#include <algorithm>
+
 #include "common.h"
 #include "host_common.h"
 #include "internal.h"
@@ -30,6 +32,7 @@
 namespace fp8s {
 
 constexpr int kMaxChunk = 1024;
+constexpr int kBalMaxB = 1024;            // batches up to this size use the balanced split
 
 struct AttnArgs {
     const uint16_t* q;
@@ -50,6 +53,10 @@ struct AttnArgs {
     // exponent per 32 consecutive d (byte strides esb, esh, est per row)
     const uint8_t* kq; const uint8_t* ke; const uint8_t* vq; const uint8_t* ve;
     int64_t esb, esh, est;
+    // balanced split (bal): the workgroups the CUs hold per KV head, and the
+    // (first record, record count) of every sequence, written for the merge
+    int bal, bal_slots, bal_W;
+    int2* seq_rec;
 };
 
 // UE8M0 byte -> 2^(E - 127) (E = 0 is the subnormal 2^-127).
@@ -93,39 +100,18 @@ __device__ __forceinline__ bool kv_len_ok(int L, const AttnArgs& a) {
 // the score MFMA then takes the D/4 consecutive d from j4*D/4, one scale
 // group, and the query operand is permuted the same way (the dot product
 // does not depend on the order of d).
+// One piece: positions [t_begin, t_begin + n_tok) of (sequence b, KV head g),
+// n_tok <= kMaxChunk.  Not SINGLE: the piece's (max, sum, accumulator) of
+// query head g*G + h go to rec + h * rec_hs.
 template <int D, int G, bool SINGLE, bool MX>
-__device__ __forceinline__ void attn_split_body(const AttnArgs& a) {
+__device__ __forceinline__ void attn_piece(const AttnArgs& a, int b, int g, int t_begin, int n_tok, float* rec,
+                                           int64_t rec_hs) {
     constexpr int NJ = D / 32;                 // MFMA K-steps over the head dim
     constexpr int LPR = D / 8;                 // lanes per V row (8 bf16 each)
     constexpr int TPL = 64 / LPR;              // V rows per wave load
     __shared__ float s_p[G][kMaxChunk];        // scores, then probabilities
     __shared__ float s_red[4][G][D];
     __shared__ float s_ml[G][2];
-
-    // Chunk-major order: consecutive workgroups (which the dispatcher deals
-    // round-robin to the 8 XCDs) belong to different (sequence, KV head)
-    // pairs, so every XCD gets a fair share of long and short prefixes.  With
-    // the chunk index fastest, chunk i of every sequence would land on one
-    // XCD and the XCD holding the first chunks would carry most of the work.
-    const int bg = blockIdx.x % (a.B * a.Hkv);
-    const int sp = blockIdx.x / (a.B * a.Hkv);
-    const int g = bg % a.Hkv, b = bg / a.Hkv;
-    const int L = a.kv_len[b];
-    if (!kv_len_ok(L, a)) {                    // the merge writes zeros and reports
-        if (SINGLE) {
-            for (int e = threadIdx.x; e < G * D; e += 256)
-                a.out[((int64_t)b * a.Hq + g * G) * D + e] = 0;
-            if (threadIdx.x == 0 && g == 0) report_error(a.err, FP8S_DEV_KVLEN_RANGE);
-            if constexpr ((G * D) % 128 == 0)
-                if (a.qo)
-                    for (int w = threadIdx.x >> 6; w < G * D / 128; w += 4)
-                        quant_out_wave(a, b, g * G * D / 128 + w, 0.0f, 0.0f, threadIdx.x & 63);
-        }
-        return;
-    }
-    const int t_begin = sp * a.chunk;
-    if (t_begin >= L) return;                  // chunk entirely past the prefix
-    const int n_tok = min(a.chunk, L - t_begin);
 
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
     const uint16_t* kbase = a.k + (int64_t)b * a.sb + (int64_t)g * a.sh;
@@ -267,7 +253,7 @@ __device__ __forceinline__ void attn_split_body(const AttnArgs& a) {
             a.out[((int64_t)b * a.Hq + g * G + h) * D + d] = (uint16_t)bits;
             s_red[0][h][d] = bf16_to_f32(bits);      // s_red[0] is no longer read below
         } else {
-            float* p = a.part + (((int64_t)b * a.Hq + g * G + h) * a.n_split + sp) * (D + 2);
+            float* p = rec + h * rec_hs;
             p[2 + d] = acc;
             if (d == 0) { p[0] = s_ml[h][0]; p[1] = s_ml[h][1]; }
         }
@@ -282,9 +268,112 @@ __device__ __forceinline__ void attn_split_body(const AttnArgs& a) {
     }
 }
 
+// Chunked split: one workgroup per (sequence, KV head, chunk of a.chunk
+// positions), the chunk's record at part[b][h][chunk].  Chunk-major order:
+// consecutive workgroups (which the dispatcher deals round-robin to the 8
+// XCDs) belong to different (sequence, KV head) pairs, so every XCD gets a
+// fair share of long and short prefixes.
+template <int D, int G, bool SINGLE, bool MX>
+__device__ __forceinline__ void attn_split_body(const AttnArgs& a) {
+    const int bg = blockIdx.x % (a.B * a.Hkv);
+    const int sp = blockIdx.x / (a.B * a.Hkv);
+    const int g = bg % a.Hkv, b = bg / a.Hkv;
+    const int L = a.kv_len[b];
+    if (!kv_len_ok(L, a)) {                    // the merge writes zeros and reports
+        if (SINGLE) {
+            for (int e = threadIdx.x; e < G * D; e += 256)
+                a.out[((int64_t)b * a.Hq + g * G) * D + e] = 0;
+            if (threadIdx.x == 0 && g == 0) report_error(a.err, FP8S_DEV_KVLEN_RANGE);
+            if constexpr ((G * D) % 128 == 0)
+                if (a.qo)
+                    for (int w = threadIdx.x >> 6; w < G * D / 128; w += 4)
+                        quant_out_wave(a, b, g * G * D / 128 + w, 0.0f, 0.0f, threadIdx.x & 63);
+        }
+        return;
+    }
+    const int t_begin = sp * a.chunk;
+    if (t_begin >= L) return;                  // chunk entirely past the prefix
+    attn_piece<D, G, SINGLE, MX>(a, b, g, t_begin, min(a.chunk, L - t_begin),
+                                 a.part + (((int64_t)b * a.Hq + g * G) * a.n_split + sp) * (D + 2),
+                                 (int64_t)a.n_split * (D + 2));
+}
+
+// Balanced split: the valid prefixes of all sequences, concatenated in
+// sequence order (T positions per KV head), are cut into W equal ranges,
+// W = max(workgroups the CUs hold per KV head, ceil(T / kMaxChunk)); the
+// workgroup (w, g) attends its range in pieces, one per sequence it
+// touches.  Piece (w, b) writes record w + b (distinct: along the
+// concatenation one of w and b grows at every cut), so the records of
+// sequence b are the contiguous run from w_first(b) + b.  Every workgroup
+// gets the same number of positions whatever the mix of prefix lengths.
+// Workgroup 0 also leaves (first record, record count) of every sequence
+// for the merge.
+__device__ __forceinline__ int bal_owner(int64_t x, int64_t T, int W) { return (int)(((x + 1) * W - 1) / T); }
+
+template <int D, int G, bool MX>
+__device__ __forceinline__ void attn_bal_body(const AttnArgs& a) {
+    __shared__ int s_pre[kBalMaxB + 1];        // s_pre[b] = valid positions of sequences < b (< 2^31)
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    if (wave == 0) {
+        int carry = 0;
+        if (lane == 0) s_pre[0] = 0;
+        for (int base = 0; base < a.B; base += 64) {
+            const int b = base + lane;
+            int L = 0;
+            if (b < a.B) {
+                const int l = a.kv_len[b];
+                L = kv_len_ok(l, a) ? l : 0;
+            }
+            int incl = L;                      // inclusive scan over the wave
+#pragma unroll
+            for (int o = 1; o < 64; o <<= 1) {
+                const int y = __shfl_up(incl, o, kWave);
+                if (lane >= o) incl += y;
+            }
+            if (b < a.B) s_pre[b + 1] = carry + incl;
+            carry += __shfl(incl, 63, kWave);
+        }
+    }
+    __syncthreads();
+    const int64_t T = s_pre[a.B];
+    const int W = (int)max((int64_t)a.bal_slots, (T + kMaxChunk - 1) / kMaxChunk);
+    if (blockIdx.x == 0) {
+        for (int b = threadIdx.x; b < a.B; b += 256) {
+            const int64_t p0 = s_pre[b], Lb = s_pre[b + 1] - p0;
+            int2 r = make_int2(0, 0);
+            if (Lb > 0) {
+                const int w0 = bal_owner(p0, T, W), w1 = bal_owner(p0 + Lb - 1, T, W);
+                r = make_int2(w0 + b, w1 - w0 + 1);
+            }
+            a.seq_rec[b] = r;
+        }
+    }
+    const int w = blockIdx.x / a.Hkv, g = blockIdx.x % a.Hkv;
+    if (w >= W || T == 0) return;
+    const int64_t R0 = (int64_t)w * T / W, R1 = (int64_t)(w + 1) * T / W;
+    int lo = 0, hi = a.B;                      // first sequence with s_pre[b + 1] > R0
+    while (lo < hi) {
+        const int mid = (lo + hi) / 2;
+        if (s_pre[mid + 1] > R0) hi = mid; else lo = mid + 1;
+    }
+    for (int b = lo; b < a.B && s_pre[b] < R1; ++b) {
+        const int64_t p0 = s_pre[b], p1 = s_pre[b + 1];
+        const int64_t s0 = max(R0, p0), s1 = min(R1, p1);
+        if (s1 <= s0) continue;
+        __syncthreads();                       // the previous piece is done with LDS
+        attn_piece<D, G, false, MX>(a, b, g, (int)(s0 - p0), (int)(s1 - s0),
+                                    a.part + ((int64_t)(w + b) * a.Hq + g * G) * (D + 2), D + 2);
+    }
+}
+
 template <int D, int G, bool SINGLE>
 __global__ __launch_bounds__(256) void attn_split_kernel(AttnArgs a) {
     attn_split_body<D, G, SINGLE, false>(a);
+}
+
+template <int D, int G>
+__global__ __launch_bounds__(256) void attn_bal_kernel(AttnArgs a) {
+    attn_bal_body<D, G, false>(a);
 }
 
 // The MXFP8-cache kernel holds five workgroups per CU only when capped at
@@ -293,6 +382,11 @@ __global__ __launch_bounds__(256) void attn_split_kernel(AttnArgs a) {
 template <int D, int G, bool SINGLE>
 __global__ __launch_bounds__(256, 5) void attn_split_mx_kernel(AttnArgs a) {
     attn_split_body<D, G, SINGLE, true>(a);
+}
+
+template <int D, int G>
+__global__ __launch_bounds__(256, 5) void attn_bal_mx_kernel(AttnArgs a) {
+    attn_bal_body<D, G, true>(a);
 }
 
 // Merge the chunks of one (sequence, query head): out = sum_i 2^(m_i - M) acc_i
@@ -315,29 +409,42 @@ __global__ __launch_bounds__(256) void attn_merge_kernel(AttnArgs a) {
     const int L = a.kv_len[b];
     const bool ok = kv_len_ok(L, a);
     if (!ok && pr == 0 && lane == 0) report_error(a.err, FP8S_DEV_KVLEN_RANGE);
-    const int n = ok ? (L + a.chunk - 1) / a.chunk : 0;
     const bool hasB = 2 * pr + 1 < segs;
     const int hA = 128 * pr / D, dA = 128 * pr % D + lane;
     const int hB = hasB ? (128 * pr + 64) / D : hA, dB = hasB ? (128 * pr + 64) % D + lane : dA;
-    const float* pA = a.part + ((int64_t)b * a.Hq + hA) * a.n_split * RS;
-    const float* pB = a.part + ((int64_t)b * a.Hq + hB) * a.n_split * RS;
+    // record j of (b, h): part[b][h][j] (chunked) or part[first + j][h] (balanced)
+    int n;
+    int64_t cs;
+    const float *pA, *pB;
+    if (a.bal) {
+        const int2 r = a.seq_rec[b];
+        n = ok ? r.y : 0;
+        cs = (int64_t)a.Hq * RS;
+        pA = a.part + ((int64_t)r.x * a.Hq + hA) * RS;
+        pB = a.part + ((int64_t)r.x * a.Hq + hB) * RS;
+    } else {
+        n = ok ? (L + a.chunk - 1) / a.chunk : 0;
+        cs = RS;
+        pA = a.part + ((int64_t)b * a.Hq + hA) * a.n_split * RS;
+        pB = a.part + ((int64_t)b * a.Hq + hB) * a.n_split * RS;
+    }
     float cA[kU], cB[kU];
 #pragma unroll
     for (int j = 0; j < kU; ++j) {
-        cA[j] = j < n ? pA[j * RS + 2 + dA] : 0.0f;
-        cB[j] = j < n ? pB[j * RS + 2 + dB] : 0.0f;
+        cA[j] = j < n ? pA[j * cs + 2 + dA] : 0.0f;
+        cB[j] = j < n ? pB[j * cs + 2 + dB] : 0.0f;
     }
     // statistics of head A (and of head B when it differs)
-    const float mA = lane < n ? pA[lane * RS] : -INFINITY, lA = lane < n ? pA[lane * RS + 1] : 0.0f;
+    const float mA = lane < n ? pA[lane * cs] : -INFINITY, lA = lane < n ? pA[lane * cs + 1] : 0.0f;
     float mB = mA, lB = lA;
     if (D != 128) {
-        mB = lane < n ? pB[lane * RS] : -INFINITY;
-        lB = lane < n ? pB[lane * RS + 1] : 0.0f;
+        mB = lane < n ? pB[lane * cs] : -INFINITY;
+        lB = lane < n ? pB[lane * cs + 1] : 0.0f;
     }
     float MA = mA, MB = mB;
     for (int i = lane + 64; i < n; i += 64) {
-        MA = fmaxf(MA, pA[(int64_t)i * RS]);
-        MB = fmaxf(MB, pB[(int64_t)i * RS]);
+        MA = fmaxf(MA, pA[i * cs]);
+        MB = fmaxf(MB, pB[i * cs]);
     }
     MA = fmax_xor<64>(MA);
     MB = D == 128 ? MA : fmax_xor<64>(MB);
@@ -345,8 +452,8 @@ __global__ __launch_bounds__(256) void attn_merge_kernel(AttnArgs a) {
     const float wB = D == 128 ? wA : (lane < n ? exp2f(mB - MB) : 0.0f);
     float denA = wA * lA, denB = wB * lB;
     for (int i = lane + 64; i < n; i += 64) {
-        denA += exp2f(pA[(int64_t)i * RS] - MA) * pA[(int64_t)i * RS + 1];
-        denB += exp2f(pB[(int64_t)i * RS] - MB) * pB[(int64_t)i * RS + 1];
+        denA += exp2f(pA[i * cs] - MA) * pA[i * cs + 1];
+        denB += exp2f(pB[i * cs] - MB) * pB[i * cs + 1];
     }
     denA = fsum_xor<64>(denA);
     denB = D == 128 ? denA : fsum_xor<64>(denB);
@@ -362,11 +469,11 @@ __global__ __launch_bounds__(256) void attn_merge_kernel(AttnArgs a) {
             wjA = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(wA), j));
             wjB = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(wB), j));
         } else {
-            wjA = exp2f(pA[(int64_t)j * RS] - MA);
-            wjB = exp2f(pB[(int64_t)j * RS] - MB);
+            wjA = exp2f(pA[j * cs] - MA);
+            wjB = exp2f(pB[j * cs] - MB);
         }
-        numA += wjA * pA[(int64_t)j * RS + 2 + dA];
-        numB += wjB * pB[(int64_t)j * RS + 2 + dB];
+        numA += wjA * pA[j * cs + 2 + dA];
+        numB += wjB * pB[j * cs + 2 + dB];
     }
     const float vA = n > 0 ? bf16_to_f32(f32_to_bf16(numA / denA)) : 0.0f;
     const float vB = n > 0 ? bf16_to_f32(f32_to_bf16(numB / denB)) : 0.0f;
@@ -375,11 +482,19 @@ __global__ __launch_bounds__(256) void attn_merge_kernel(AttnArgs a) {
     if (a.qo) quant_out_wave(a, b, pr, vA, vB, lane);
 }
 
-struct AttnPlan { int n_split, chunk; };
+// Chunked split: n_split chunks of `chunk` positions per (sequence, KV head).
+// Balanced split (bal, 16 <= B <= kBalMaxB with more than one chunk): at
+// most bal_W equal ranges per KV head (bal_W bounds the device's choice),
+// the records after a table of B (first record, count) pairs.
+struct AttnPlan { int n_split, chunk, bal, bal_W; size_t off_part, need; };
+constexpr int kBalSlotsMax = 2048;        // workgroups the CUs hold at once, all KV heads together, at most
+constexpr int kBalMinB = 16;
 template <bool MX>
 static int attn_launch(const AttnArgs& a, int D, int G, hipStream_t st);
 
-static AttnPlan plan_attn(int64_t B, int32_t Hkv, int64_t hint) {
+static size_t align256(size_t v) { return (v + 255) / 256 * 256; }
+
+static AttnPlan plan_attn(int64_t B, int32_t Hq, int32_t Hkv, int32_t D, int64_t hint) {
     // Aim for >= 2048 workgroups so that all 256 CUs stay busy at small batch.
     int64_t want = (2048 + B * Hkv - 1) / (B * Hkv);
     if (want < 1) want = 1;
@@ -390,11 +505,32 @@ static AttnPlan plan_attn(int64_t B, int32_t Hkv, int64_t hint) {
     AttnPlan p;
     p.chunk = (int)chunk;
     p.n_split = (int)((hint + chunk - 1) / chunk);
+    p.bal = p.n_split > 1 && B >= kBalMinB && B <= kBalMaxB && B * hint < (1ll << 31);
+    const size_t rs = (size_t)(D + 2) * sizeof(float);
+    if (p.bal) {
+        const int64_t by_len = (B * hint + kMaxChunk - 1) / kMaxChunk;
+        p.bal_W = (int)std::max<int64_t>(std::max(1, kBalSlotsMax / Hkv), by_len);
+        p.off_part = align256((size_t)B * sizeof(int2));
+        p.need = p.off_part + (size_t)(p.bal_W + B) * Hq * rs;
+    } else {
+        p.bal_W = 0;
+        p.off_part = 0;
+        p.need = (size_t)B * Hq * p.n_split * rs;
+    }
     return p;
 }
 
 template <int D, int G, bool MX>
 static void launch_split(dim3 grid, hipStream_t st, const AttnArgs& a);
+
+static void set_split_layout(AttnArgs& a, const AttnPlan& p, void* workspace) {
+    uint8_t* ws = static_cast<uint8_t*>(workspace);
+    a.bal = p.bal;
+    a.bal_W = p.bal_W;
+    a.bal_slots = 0;
+    a.seq_rec = p.bal ? reinterpret_cast<int2*>(ws) : nullptr;
+    a.part = reinterpret_cast<float*>(ws + p.off_part);
+}
 
 // The split kernel (and the merge when there are several chunks).
 template <bool MX>
@@ -417,8 +553,39 @@ static int attn_launch(const AttnArgs& a, int D, int G, hipStream_t st) {
     return check_launch("gqa_decode_attn (merge)");
 }
 
+// Workgroups of a balanced-split kernel that all CUs hold at once, per KV
+// head (queried once per device; at most kBalSlotsMax in all).
+template <typename K>
+static int bal_slots(K kernel, int Hkv) {
+    static int slots[64];
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return std::max(1, 1024 / Hkv);
+    if (!slots[dev]) {
+        int per_cu = 0, cus = 0;
+        if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, kernel, 256, 0) != hipSuccess ||
+            hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || per_cu < 1 ||
+            cus < 1)
+            return std::max(1, 1024 / Hkv);
+        slots[dev] = std::min(per_cu * cus, kBalSlotsMax);
+    }
+    return std::max(1, slots[dev] / Hkv);
+}
+
 template <int D, int G, bool MX>
 static void launch_split(dim3 grid, hipStream_t st, const AttnArgs& a) {
+    if (a.bal) {
+        AttnArgs b = a;
+        if (MX) {
+            b.bal_slots = std::min(bal_slots(attn_bal_mx_kernel<D, G>, a.Hkv), a.bal_W);
+            FP8S_LAUNCH("attn_split_mx", (attn_bal_mx_kernel<D, G>), dim3((unsigned)(a.bal_W * a.Hkv)), dim3(256), 0,
+                        st, b);
+        } else {
+            b.bal_slots = std::min(bal_slots(attn_bal_kernel<D, G>, a.Hkv), a.bal_W);
+            FP8S_LAUNCH("attn_split", (attn_bal_kernel<D, G>), dim3((unsigned)(a.bal_W * a.Hkv)), dim3(256), 0, st,
+                        b);
+        }
+        return;
+    }
     if (MX) {
         if (a.n_split == 1)
             FP8S_LAUNCH("attn_single_mx", (attn_split_mx_kernel<D, G, true>), grid, dim3(256), 0, st, a);
@@ -455,8 +622,8 @@ int gqa_decode_attn_ex(const uint16_t* q, const uint16_t* k_cache, const uint16_
     FP8S_REQUIRE(!qo || (so && (G * D) % 128 == 0), FP8S_EUNSUPPORTED,
                  "gqa_decode_attn: a quantised output needs whole 128-column groups per KV head");
     if (hint > cap) hint = cap;
-    const AttnPlan p = plan_attn(B, Hkv, hint);
-    const size_t need = (size_t)B * Hq * p.n_split * (D + 2) * sizeof(float);
+    const AttnPlan p = plan_attn(B, Hq, Hkv, D, hint);
+    const size_t need = p.need;
     FP8S_REQUIRE(workspace && aligned16(workspace), FP8S_EWORKSPACE, "gqa_decode_attn: workspace missing or unaligned");
     FP8S_REQUIRE(workspace_bytes >= need, FP8S_EWORKSPACE, "gqa_decode_attn: workspace %zu < required %zu bytes",
                  workspace_bytes, need);
@@ -467,7 +634,7 @@ int gqa_decode_attn_ex(const uint16_t* q, const uint16_t* k_cache, const uint16_
     a.B = (int)B; a.Hq = Hq; a.Hkv = Hkv; a.n_split = p.n_split; a.chunk = p.chunk;
     a.cap = cap; a.hint = hint;
     a.scale_log2 = softmax_scale * 1.4426950408889634f;
-    a.part = static_cast<float*>(workspace);
+    set_split_layout(a, p, workspace);
     a.out = out;
     a.err = err_flag;
     a.qo = qo; a.so = so; a.qo_KB = Hq * D / 128;
@@ -500,8 +667,8 @@ static int gqa_decode_attn_mxkv_ex(const uint16_t* q, const uint8_t* kq, const u
                  "gqa_decode_attn_mxkv: q, caches and out must be 16-byte aligned");
     FP8S_REQUIRE(B * Hkv <= (1ll << 24), FP8S_EUNSUPPORTED, "gqa_decode_attn_mxkv: batch too large");
     if (hint > cap) hint = cap;
-    const AttnPlan p = plan_attn(B, Hkv, hint);
-    const size_t need = (size_t)B * Hq * p.n_split * (D + 2) * sizeof(float);
+    const AttnPlan p = plan_attn(B, Hq, Hkv, D, hint);
+    const size_t need = p.need;
     FP8S_REQUIRE(workspace && aligned16(workspace), FP8S_EWORKSPACE,
                  "gqa_decode_attn_mxkv: workspace missing or unaligned");
     FP8S_REQUIRE(workspace_bytes >= need, FP8S_EWORKSPACE, "gqa_decode_attn_mxkv: workspace %zu < required %zu bytes",
@@ -515,7 +682,7 @@ static int gqa_decode_attn_mxkv_ex(const uint16_t* q, const uint8_t* kq, const u
     a.B = (int)B; a.Hq = Hq; a.Hkv = Hkv; a.n_split = p.n_split; a.chunk = p.chunk;
     a.cap = cap; a.hint = hint;
     a.scale_log2 = softmax_scale * 1.4426950408889634f;
-    a.part = static_cast<float*>(workspace);
+    set_split_layout(a, p, workspace);
     a.out = out;
     a.err = err_flag;
     a.qo = nullptr; a.so = nullptr; a.qo_KB = Hq * D / 128;
@@ -530,7 +697,12 @@ extern "C" size_t gqa_decode_attn_workspace_size(int64_t B, int32_t Hq, int32_t 
     if (B < 1 || Hq < 1 || D < 1 || max_kv_len < 1) return 0;
     // The split count never exceeds ceil(max_kv_len / 16).
     const int64_t max_split = (max_kv_len + 15) / 16;
-    return (size_t)B * Hq * max_split * (D + 2) * sizeof(float);
+    size_t n = (size_t)B * Hq * max_split * (D + 2) * sizeof(float);
+    if (B >= kBalMinB && B <= kBalMaxB) {        // the balanced split with one KV head (its largest form)
+        const AttnPlan p = plan_attn(B, Hq, 1, D, max_kv_len);
+        if (p.bal) n = std::max(n, p.need);
+    }
+    return n;
 }
 
 extern "C" int gqa_decode_attn_mxkv(const uint16_t* q, const uint8_t* k_q, const uint8_t* k_e, const uint8_t* v_q,
