@@ -159,3 +159,39 @@ def test_single_chunk_short_prefix(G):
     qb, kb, vb, kc, vc = _make(inputs.W_ATTN, B, Hkv * G, Hkv, 128, cap, kv, extra=50 + G)
     out = from_dev_bf16(_run(qb, kc, vc, kv, 9))
     assert max_rel_err(out, _oracle(qb, kb, vb, kv)) <= TOL_BF16_ATTN
+
+
+def test_balanced_split_mixed_and_invalid_lengths():
+    """Batches of 16+ take the balanced split: equal position ranges over the
+    concatenated prefixes.  Mix one-position prefixes, the full capacity and
+    invalid lengths (zero output, error flag) in one batch."""
+    need_gpu()
+    B, cap = 32, 1024
+    kv = inputs.kv_lengths(inputs.W_ATTN, B, 1, cap, extra=201)
+    kv[:4] = [1, cap, 1, 2]
+    qb, kb, vb, kc, vc = _make(inputs.W_ATTN, B, 32, 8, 128, cap, kv, extra=201)
+    bad = kv.copy()
+    bad[5], bad[17] = 0, cap + 1
+    err = torch.zeros(1, dtype=torch.int32, device="cuda")
+    out = _run(qb, kc, vc, bad, cap, err)
+    assert int(err.item()) == ops.DEV_KVLEN_RANGE
+    assert not out[5].float().abs().sum().item() and not out[17].float().abs().sum().item()
+    keep = [b for b in range(B) if b not in (5, 17)]
+    ref = _oracle(qb[keep], kb[keep], vb[keep], kv[keep])
+    assert max_rel_err(from_dev_bf16(out[keep]), ref) <= TOL_BF16_ATTN
+
+
+@pytest.mark.parametrize("case", ["short_many", "one_long"])
+def test_balanced_split_pieces_across_many_sequences(case):
+    """Ranges that span many sequences (tiny prefixes) and more ranges than
+    positions (every prefix one position)."""
+    need_gpu()
+    B, cap = (64, 64) if case == "short_many" else (20, 2048)
+    if case == "short_many":
+        kv = np.ones(B, np.int32)
+    else:
+        kv = (np.arange(B) % 3 + 1).astype(np.int32)
+        kv[13] = cap
+    qb, kb, vb, kc, vc = _make(inputs.W_ATTN, B, 32, 8, 128, cap, kv, extra=202)
+    out = _run(qb, kc, vc, kv, cap)
+    assert max_rel_err(from_dev_bf16(out), _oracle(qb, kb, vb, kv)) <= TOL_BF16_ATTN

@@ -130,3 +130,15 @@ def test_invalid_kv_len_sets_flag_and_zeroes(hint):
     assert int(err.item()) == ops.DEV_KVLEN_RANGE
     assert not out[1].float().abs().sum().item() and not out[2].float().abs().sum().item()
     assert max_rel_err(from_dev_bf16(out[:1]), _oracle(qb[:1], kb[:1], vb[:1], kv[:1])) <= TOL_BF16_ATTN
+
+
+def test_balanced_split_mixed_lengths():
+    """The balanced split (16+ sequences) over MXFP8 caches, tiny and
+    full-capacity prefixes mixed."""
+    need_gpu()
+    B, cap = 24, 1024
+    kv = inputs.kv_lengths(inputs.W_ATTN, B, 1, cap, extra=203)
+    kv[:3] = [1, cap, 3]
+    qb, kb, vb, kc, vc = _make(inputs.W_ATTN, B, 32, 8, 128, cap, kv, extra=203)
+    out = _run(qb, kc, vc, kv, cap)
+    assert max_rel_err(from_dev_bf16(out), _oracle(qb, kb, vb, kv)) <= TOL_BF16_ATTN
