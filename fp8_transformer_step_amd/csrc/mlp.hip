@@ -53,7 +53,12 @@ constexpr int kGuFullItems = 512;  // gu items over the whole hidden dim: two pe
 
 // DOWN items of the LDS path: NB 16-column tiles, K range bounded by LDS.
 constexpr int kDownNb = 2;
-constexpr int kDownMaxKb = kLdsBytes / (kDownNb * kFrag);
+// K blocks per down item: 76 blocks (inter 9728) in 6 splits of at most 13,
+// 480 items of 52 KB, three to a CU.  Measured at M = 64 against 20 (4
+// splits, 320 items), 16, 12, 11 and 10 blocks: 10.6 against 13.7, 11.7,
+// 14.1, 14.2 and 13.6 us.
+constexpr int kDownMaxKb = 13;
+constexpr int kDownLds = kDownNb * kDownMaxKb * kFrag;   // the item's slice (also holds the reduction scratch)
 
 struct MlpArgs {
     const uint16_t* x;
@@ -553,7 +558,7 @@ static void launch_mlp(const MlpPlan& p, hipStream_t st, const MlpArgs& a, bool 
     case N:                                                                            \
         FP8S_LAUNCH("mlp_gu", (gu_kernel<N, MODE>), g_gul, blk, kLdsBytes, st, a);     \
         FP8S_LAUNCH("mlp_hq", hq_kernel<MODE>, g_hq, blk, 0, st, a);                    \
-        FP8S_LAUNCH("mlp_down", (down_kernel<N, MODE>), g_dn, blk, kLdsBytes, st, a);   \
+        FP8S_LAUNCH("mlp_down", (down_kernel<N, MODE>), g_dn, blk, kDownLds, st, a);    \
         break;
         FP8S_MT_CASE(2) FP8S_MT_CASE(4) FP8S_MT_CASE(8)
 #undef FP8S_MT_CASE
