@@ -35,6 +35,10 @@ KERNELS = [
     (r"hq_kernel", "mlp_hq"),
     (r"attn_split_kernel<[^>]*true", "attn_single"),
     (r"attn_split_kernel", "attn_split"),
+    (r"attn_bal_kernel", "attn_split"),
+    (r"attn_split_mx_kernel<[^>]*true", "attn_single_mx"),
+    (r"attn_split_mx_kernel", "attn_split_mx"),
+    (r"attn_bal_mx_kernel", "attn_split_mx"),
     (r"attn_merge_kernel", "attn_merge"),
     (r"qlinear_kernel", "qlinear"),
     (r"embed_kernel", "embed_sum"),
