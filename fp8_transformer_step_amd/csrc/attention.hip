@@ -299,15 +299,16 @@ __device__ __forceinline__ void attn_split_body(const AttnArgs& a) {
 }
 
 // Balanced split: the valid prefixes of all sequences, concatenated in
-// sequence order (T positions per KV head), are cut into W equal ranges,
-// W = max(workgroups the CUs hold per KV head, ceil(T / kMaxChunk)); the
-// workgroup (w, g) attends its range in pieces, one per sequence it
-// touches.  Piece (w, b) writes record w + b (distinct: along the
-// concatenation one of w and b grows at every cut), so the records of
-// sequence b are the contiguous run from w_first(b) + b.  Every workgroup
-// gets the same number of positions whatever the mix of prefix lengths.
-// Workgroup 0 also leaves (first record, record count) of every sequence
-// for the merge.
+// sequence order (T positions per KV head), are cut into W = S * K equal
+// ranges of at most kMaxChunk positions, S the workgroups the CUs hold per KV
+// head and K = ceil(T / (S * kMaxChunk)); workgroup (w, g) takes ranges
+// w*K .. w*K + K - 1 and attends each in pieces, one per sequence it
+// touches.  Piece (v, b) of range v writes record v + b (distinct: along the
+// concatenation one of v and b grows at every cut), so the records of
+// sequence b are the contiguous run from v_first(b) + b.  Every workgroup
+// gets the same number of positions whatever the mix of prefix lengths, in
+// one round.  Workgroup 0 also leaves (first record, record count) of every
+// sequence for the merge.
 __device__ __forceinline__ int bal_owner(int64_t x, int64_t T, int W) { return (int)(((x + 1) * W - 1) / T); }
 
 template <int D, int G, bool MX>
@@ -336,7 +337,9 @@ __device__ __forceinline__ void attn_bal_body(const AttnArgs& a) {
     }
     __syncthreads();
     const int64_t T = s_pre[a.B];
-    const int W = (int)max((int64_t)a.bal_slots, (T + kMaxChunk - 1) / kMaxChunk);
+    const int64_t per_wg = (int64_t)a.bal_slots * kMaxChunk;
+    const int K = (int)max((int64_t)1, (T + per_wg - 1) / per_wg);
+    const int W = a.bal_slots * K;
     if (blockIdx.x == 0) {
         for (int b = threadIdx.x; b < a.B; b += 256) {
             const int64_t p0 = s_pre[b], Lb = s_pre[b + 1] - p0;
@@ -348,21 +351,23 @@ __device__ __forceinline__ void attn_bal_body(const AttnArgs& a) {
             a.seq_rec[b] = r;
         }
     }
-    const int w = blockIdx.x / a.Hkv, g = blockIdx.x % a.Hkv;
-    if (w >= W || T == 0) return;
-    const int64_t R0 = (int64_t)w * T / W, R1 = (int64_t)(w + 1) * T / W;
-    int lo = 0, hi = a.B;                      // first sequence with s_pre[b + 1] > R0
-    while (lo < hi) {
-        const int mid = (lo + hi) / 2;
-        if (s_pre[mid + 1] > R0) hi = mid; else lo = mid + 1;
-    }
-    for (int b = lo; b < a.B && s_pre[b] < R1; ++b) {
-        const int64_t p0 = s_pre[b], p1 = s_pre[b + 1];
-        const int64_t s0 = max(R0, p0), s1 = min(R1, p1);
-        if (s1 <= s0) continue;
-        __syncthreads();                       // the previous piece is done with LDS
-        attn_piece<D, G, false, MX>(a, b, g, (int)(s0 - p0), (int)(s1 - s0),
-                                    a.part + ((int64_t)(w + b) * a.Hq + g * G) * (D + 2), D + 2);
+    const int wg = blockIdx.x / a.Hkv, g = blockIdx.x % a.Hkv;
+    if (wg >= a.bal_slots || T == 0) return;
+    for (int v = wg * K; v < wg * K + K; ++v) {
+        const int64_t R0 = (int64_t)v * T / W, R1 = (int64_t)(v + 1) * T / W;
+        int lo = 0, hi = a.B;                  // first sequence with s_pre[b + 1] > R0
+        while (lo < hi) {
+            const int mid = (lo + hi) / 2;
+            if (s_pre[mid + 1] > R0) hi = mid; else lo = mid + 1;
+        }
+        for (int b = lo; b < a.B && s_pre[b] < R1; ++b) {
+            const int64_t p0 = s_pre[b], p1 = s_pre[b + 1];
+            const int64_t s0 = max(R0, p0), s1 = min(R1, p1);
+            if (s1 <= s0) continue;
+            __syncthreads();                   // the previous piece is done with LDS
+            attn_piece<D, G, false, MX>(a, b, g, (int)(s0 - p0), (int)(s1 - s0),
+                                        a.part + ((int64_t)(v + b) * a.Hq + g * G) * (D + 2), D + 2);
+        }
     }
 }
 
@@ -508,8 +513,10 @@ static AttnPlan plan_attn(int64_t B, int32_t Hq, int32_t Hkv, int32_t D, int64_t
     p.bal = p.n_split > 1 && B >= kBalMinB && B <= kBalMaxB && B * hint < (1ll << 31);
     const size_t rs = (size_t)(D + 2) * sizeof(float);
     if (p.bal) {
+        // ranges W = S * ceil(T / (S * kMaxChunk)) < S + T / kMaxChunk, with
+        // S <= kBalSlotsMax / Hkv and T <= B * hint: records < bal_W + B
         const int64_t by_len = (B * hint + kMaxChunk - 1) / kMaxChunk;
-        p.bal_W = (int)std::max<int64_t>(std::max(1, kBalSlotsMax / Hkv), by_len);
+        p.bal_W = (int)(std::max(1, kBalSlotsMax / Hkv) + by_len);
         p.off_part = align256((size_t)B * sizeof(int2));
         p.need = p.off_part + (size_t)(p.bal_W + B) * Hq * rs;
     } else {
@@ -576,13 +583,13 @@ static void launch_split(dim3 grid, hipStream_t st, const AttnArgs& a) {
     if (a.bal) {
         AttnArgs b = a;
         if (MX) {
-            b.bal_slots = std::min(bal_slots(attn_bal_mx_kernel<D, G>, a.Hkv), a.bal_W);
-            FP8S_LAUNCH("attn_split_mx", (attn_bal_mx_kernel<D, G>), dim3((unsigned)(a.bal_W * a.Hkv)), dim3(256), 0,
-                        st, b);
+            b.bal_slots = bal_slots(attn_bal_mx_kernel<D, G>, a.Hkv);
+            FP8S_LAUNCH("attn_split_mx", (attn_bal_mx_kernel<D, G>), dim3((unsigned)(b.bal_slots * a.Hkv)),
+                        dim3(256), 0, st, b);
         } else {
-            b.bal_slots = std::min(bal_slots(attn_bal_kernel<D, G>, a.Hkv), a.bal_W);
-            FP8S_LAUNCH("attn_split", (attn_bal_kernel<D, G>), dim3((unsigned)(a.bal_W * a.Hkv)), dim3(256), 0, st,
-                        b);
+            b.bal_slots = bal_slots(attn_bal_kernel<D, G>, a.Hkv);
+            FP8S_LAUNCH("attn_split", (attn_bal_kernel<D, G>), dim3((unsigned)(b.bal_slots * a.Hkv)), dim3(256), 0,
+                        st, b);
         }
         return;
     }
