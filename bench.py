@@ -290,6 +290,25 @@ def time_step(torch, ops, dm, kv, prev, steps, warmup, workspace, err):
     return ms, wall, ops.profile_stop()
 
 
+def mlp_sweep(torch, ops, inputs, n_sets):
+    """The MLP alone at M in {1, 8, 32, 64, 128}, bsgemm and MXFP8, on
+    rotating weight sets."""
+    kv_len = inputs.kv_lengths(inputs.W_ATTN, 64, 234, 400)
+    sweep = {"mlp_bsgemm": {}, "mlp_mxfp8": {}}
+    for mode, key in ((ops.MLP_BSGEMM, "mlp_bsgemm"), (ops.MLP_MXFP8, "mlp_mxfp8")):
+        for M in (1, 8, 32, 64, 128):
+            w = Workload(torch, ops, 1, M, mode, n_sets, kv_len, with_attn=False)
+            t, _, per = time_parts(torch, ops, w, [w.mlp], 20, 5)
+            gb = mlp_bytes(M, mode) / (t * 1e-3) / 1e9
+            sweep[key][M] = {"us": t * 1e3, "tokens/s": M / (t * 1e-3), "GB/s": gb, "frac": gb / PEAK_HBM_GBS,
+                             "kernels": kernel_table(per, 20, M, mode)}
+            log(f"{key} M={M}: {t * 1e3:.1f} us {gb:.0f} GB/s  " +
+                " ".join(f"{k}={v['us']:.1f}" for k, v in sweep[key][M]["kernels"].items()))
+            del w
+            torch.cuda.empty_cache()
+    return sweep
+
+
 def time_step_graph(torch, ops, dm, kv, prev, steps, warmup, workspace, err):
     """ms per step when the step is captured once into a HIP graph and
     replayed (every kernel of every step still runs; the host launches one
@@ -400,6 +419,9 @@ def main():
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--sets", type=int, default=4, help="rotating weight/cache sets of the sweeps")
     ap.add_argument("--no-sweep", action="store_true")
+    ap.add_argument("--mlp-only", action="store_true",
+                    help="only the MLP at M in {1, 8, 32, 64, 128} (both paths), for counter runs; prints that "
+                         "sweep as JSON")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="also run a plain 512 MiB device copy (3x) so that profiler byte counters can be "
@@ -414,6 +436,9 @@ def main():
     from fp8_transformer_step_amd import inputs, model, ops
 
     torch.cuda.set_device(0)
+    if args.mlp_only:
+        print(json.dumps({"mlp_sweep": mlp_sweep(torch, ops, inputs, args.sets)}), flush=True)
+        return
     cfg = model.FULL
     log("bench: generating the seeded model and caches")
     host = model.HostModel(cfg)
@@ -481,19 +506,7 @@ def main():
     torch.cuda.empty_cache()
 
     if not args.no_sweep:
-        kv_len = inputs.kv_lengths(inputs.W_ATTN, 64, 234, 400)
-        sweep = {"mlp_bsgemm": {}, "mlp_mxfp8": {}, "attn": {}}
-        for mode, key in ((ops.MLP_BSGEMM, "mlp_bsgemm"), (ops.MLP_MXFP8, "mlp_mxfp8")):
-            for M in (1, 8, 32, 64, 128):
-                w = Workload(torch, ops, 1, M, mode, args.sets, kv_len, with_attn=False)
-                t, _, per = time_parts(torch, ops, w, [w.mlp], 20, 5)
-                gb = mlp_bytes(M, mode) / (t * 1e-3) / 1e9
-                sweep[key][M] = {"us": t * 1e3, "tokens/s": M / (t * 1e-3), "GB/s": gb, "frac": gb / PEAK_HBM_GBS,
-                                 "kernels": kernel_table(per, 20, M, mode)}
-                log(f"{key} M={M}: {t * 1e3:.1f} us {gb:.0f} GB/s  " +
-                    " ".join(f"{k}={v['us']:.1f}" for k, v in sweep[key][M]["kernels"].items()))
-                del w
-                torch.cuda.empty_cache()
+        sweep = mlp_sweep(torch, ops, inputs, args.sets) | {"attn": {}}
         sweep["attn_mxkv"] = {}
         for Bs, lo, hi, mx in ((1, 234, 400, False), (16, 234, 400, False), (64, 234, 400, False),
                                (64, 234, 4096, False), (64, 234, 8192, False),

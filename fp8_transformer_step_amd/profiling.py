@@ -9,6 +9,13 @@
       (an elementwise copy of 128 Mi fp32: 512 MiB read, 512 MiB written).
       Records the sha256 of the kernel sources (csrc/) so that bench.py
       ignores the numbers once any kernel has changed.
+  python -m fp8_transformer_step_amd.profiling counters <kernel_stats.csv> <pass dir>... <out.md> --command "<cmd>"
+      Per rocprof kernel (template arguments included): calls, average us,
+      MFMA busy (SQ_VALU_MFMA_BUSY_CYCLES, summed over the SIMDs, over the
+      average duration x 2.4 GHz x 1024 SIMDs), FP8 MFMA rate
+      (SQ_INSTS_VALU_MFMA_MOPS_F8 x 512 flop over the average duration) and
+      LDS bank conflicts (SQ_LDS_BANK_CONFLICT over the conflict-free LDS
+      cycles), from counter passes of the same command.
 """
 
 import argparse
@@ -126,6 +133,54 @@ def pmc(fetch_dir, write_dir, out_json, command):
     json.dump(out, open(out_json, "w"), indent=1)
 
 
+SIMDS = 1024                      # 256 CUs x 4 SIMDs
+CLOCK_HZ = 2.4e9                  # peak engine clock
+
+
+def _per_kernel_counters(dirs):
+    """{rocprof kernel name: {counter: mean value per dispatch}} over passes."""
+    out = {}
+    for d in dirs:
+        acc = {}
+        for r in csv.DictReader(open(_csv(d, "counter_collection.csv"))):
+            name = r["Kernel_Name"]
+            if not lib_kernel(name):
+                continue
+            key = (name.split("(")[0].replace("void ", ""), r["Counter_Name"])
+            acc.setdefault(key, []).append(float(r["Counter_Value"]))
+        for (name, ctr), v in acc.items():
+            out.setdefault(name, {})[ctr] = statistics.mean(v)
+    return out
+
+
+def counters(stats_csv, dirs, out_md, command):
+    dur = {}
+    for r in csv.DictReader(open(_csv(stats_csv, "kernel_stats.csv"))):
+        if lib_kernel(r["Name"]):
+            dur[r["Name"].split("(")[0].replace("void ", "")] = (int(r["Calls"]), float(r["AverageNs"]) / 1e3)
+    ctr = _per_kernel_counters(dirs)
+    lines = ["# rocprofv3 counters: MFMA use and LDS bank conflicts\n", f"Command:\n\n```\n{command}\n```\n",
+             "MFMA busy = SQ_VALU_MFMA_BUSY_CYCLES (summed over SIMDs) / (average duration x 2.4 GHz x 1024 "
+             "SIMDs); FP8 rate = SQ_INSTS_VALU_MFMA_MOPS_F8 x 512 / average duration (dense FP8 peak "
+             "5000 TFLOP/s); LDS conflicts = SQ_LDS_BANK_CONFLICT / (SQ_LDS_IDX_ACTIVE - "
+             "SQ_LDS_BANK_CONFLICT).  (GRBM_GUI_ACTIVE, also collected, spans the counter window of all "
+             "XCDs, not the kernel.)\n",
+             "| rocprof kernel | calls | avg us | MFMA busy % | FP8 TFLOP/s | % of FP8 peak | LDS conflict % |",
+             "|---|---|---|---|---|---|---|"]
+    for name, c in sorted(ctr.items()):
+        calls, us = dur.get(name, (0, 0.0))
+        busy = c.get("SQ_VALU_MFMA_BUSY_CYCLES")
+        mops = c.get("SQ_INSTS_VALU_MFMA_MOPS_F8")
+        conf, idx = c.get("SQ_LDS_BANK_CONFLICT"), c.get("SQ_LDS_IDX_ACTIVE")
+        f_busy = f"{100 * busy / (us * 1e-6 * CLOCK_HZ * SIMDS):.1f}" if busy is not None and us > 0 else "-"
+        tf = mops * 512 / (us * 1e-6) / 1e12 if mops is not None and us > 0 else None
+        f_tf = f"{tf:.0f}" if tf is not None else "-"
+        f_pk = f"{100 * tf / 5000:.1f}" if tf is not None else "-"
+        f_lds = f"{100 * conf / max(idx - conf, 1):.2f}" if conf is not None and idx else "-"
+        lines.append(f"| `{name}` | {calls} | {us:.1f} | {f_busy} | {f_tf} | {f_pk} | {f_lds} |")
+    open(out_md, "w").write("\n".join(lines) + "\n")
+
+
 def main():
     ap = argparse.ArgumentParser()
     sub = ap.add_subparsers(dest="cmd", required=True)
@@ -138,11 +193,17 @@ def main():
     b.add_argument("write_dir")
     b.add_argument("out")
     b.add_argument("--command", required=True)
+    c = sub.add_parser("counters")
+    c.add_argument("stats")
+    c.add_argument("dirs", nargs="+", help="counter pass directories, then the output .md")
+    c.add_argument("--command", required=True)
     args = ap.parse_args()
     if args.cmd == "stats":
         stats(args.csv, args.out, args.command)
-    else:
+    elif args.cmd == "pmc":
         pmc(args.fetch_dir, args.write_dir, args.out, args.command)
+    else:
+        counters(args.stats, args.dirs[:-1], args.dirs[-1], args.command)
 
 
 if __name__ == "__main__":
