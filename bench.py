@@ -67,9 +67,9 @@ def kernel_bytes(name, M, mode, kv_len=None, B=None):
         return M * H * 2 + M * H + _ascale_bytes(M, H, mode)
     if name == "mlp_hq":
         return 2 * M * I * 4 + M * I + _ascale_bytes(M, I, mode)
-    if name == "attn_split":
+    if name in ("attn_split", "attn_split_paged"):      # paged: the block table (4 B per page) is not counted
         return int(np.sum(kv_len.astype(np.int64))) * HKV * D * 2 * 2 + B * HQ * D * 2 + 4 * B
-    if name == "attn_split_mx":
+    if name in ("attn_split_mx", "attn_split_mx_paged"):
         return int(np.sum(kv_len.astype(np.int64))) * HKV * (D + D // 32) * 2 + B * HQ * D * 2 + 4 * B
     if name == "attn_merge":
         return B * HQ * D * 2 + 4 * B
@@ -88,9 +88,11 @@ def log(msg):
 class Workload:
     """Rotating sets of GPU-resident weights, activations and KV caches."""
 
-    def __init__(self, torch, ops, B, M, mode, n_sets, kv_len, with_attn=True, with_mlp=True, mx_kv=False):
+    def __init__(self, torch, ops, B, M, mode, n_sets, kv_len, with_attn=True, with_mlp=True, mx_kv=False,
+                 page=0):
         self.torch, self.ops = torch, ops
         self.mx_kv = mx_kv
+        self.page = page
         self.B, self.M, self.mode = B, M, mode
         self.sets = []
         g = torch.Generator(device="cuda")
@@ -117,6 +119,20 @@ class Workload:
                 vc = torch.empty((B, HKV, CAP, D), dtype=torch.bfloat16, device="cuda")
                 kc[:, :, :Lmax] = torch.randn((B, HKV, Lmax, D), generator=g, device="cuda").to(torch.bfloat16)
                 vc[:, :, :Lmax] = torch.randn((B, HKV, Lmax, D), generator=g, device="cuda").to(torch.bfloat16)
+                if page:                                # the prefixes on shuffled pages of a pool
+                    mp = (Lmax + page - 1) // page
+                    from fp8_transformer_step_amd import inputs
+                    table = inputs.page_table(inputs.W_ATTN, B, mp, B * mp, extra=s)
+                    idx = torch.from_numpy(table.reshape(-1).astype(np.int64)).cuda()
+                    pools = []
+                    for c in (kc, vc):
+                        pool = torch.empty((B * mp, HKV, page, D), dtype=torch.bfloat16, device="cuda")
+                        pool[idx] = c[:, :, :mp * page].reshape(B, HKV, mp, page, D).transpose(1, 2).reshape(
+                            B * mp, HKV, page, D)
+                        pools.append(pool)
+                    del kc, vc
+                    kc, vc = pools
+                    st["bt"] = torch.from_numpy(table).cuda()
                 if mx_kv:                               # MXFP8 caches, quantised from the bf16 ones
                     kc, vc = ops.quantize_kv_mx(kc), ops.quantize_kv_mx(vc)
                 st["k"], st["v"] = kc, vc
@@ -134,6 +150,11 @@ class Workload:
 
     def attn(self, s):
         st = self.sets[s]
+        if self.page:
+            fn = self.ops.gqa_decode_attn_paged_mxkv if self.mx_kv else self.ops.gqa_decode_attn_paged
+            fn(st["q"], st["k"], st["v"], st["bt"], st["kv"], st["hint"], out=st["o"], workspace=st["aws"],
+               err=self.err)
+            return
         fn = self.ops.gqa_decode_attn_mxkv if self.mx_kv else self.ops.gqa_decode_attn
         fn(st["q"], st["k"], st["v"], st["kv"], st["hint"], out=st["o"], workspace=st["aws"], err=self.err)
 
@@ -506,19 +527,22 @@ def main():
     torch.cuda.empty_cache()
 
     if not args.no_sweep:
-        sweep = mlp_sweep(torch, ops, inputs, args.sets) | {"attn": {}}
-        sweep["attn_mxkv"] = {}
-        for Bs, lo, hi, mx in ((1, 234, 400, False), (16, 234, 400, False), (64, 234, 400, False),
-                               (64, 234, 4096, False), (64, 234, 8192, False),
-                               (64, 234, 4096, True), (64, 234, 8192, True)):
+        sweep = mlp_sweep(torch, ops, inputs, args.sets) | {"attn": {}, "attn_mxkv": {}, "attn_paged": {}}
+        for Bs, lo, hi, mx, page in ((1, 234, 400, False, 0), (16, 234, 400, False, 0), (64, 234, 400, False, 0),
+                                     (64, 234, 4096, False, 0), (64, 234, 8192, False, 0),
+                                     (64, 234, 4096, True, 0), (64, 234, 8192, True, 0),
+                                     (64, 234, 4096, False, 16), (64, 234, 4096, True, 16)):
             kv = inputs.kv_lengths(inputs.W_ATTN, Bs, lo, hi, extra=Bs + hi)
-            w = Workload(torch, ops, Bs, 1, 0, 2 if hi > 400 else args.sets, kv, with_mlp=False, mx_kv=mx)
+            w = Workload(torch, ops, Bs, 1, 0, 2 if hi > 400 else args.sets, kv, with_mlp=False, mx_kv=mx,
+                         page=page)
             t, _, per = time_parts(torch, ops, w, [w.attn], 20, 5)
             gb = attn_bytes(kv, Bs, mx) / (t * 1e-3) / 1e9
-            sweep["attn_mxkv" if mx else "attn"][f"B={Bs},kv=U[{lo},{hi}]"] = {
+            key = f"B={Bs},kv=U[{lo},{hi}]" + (f",page={page},{'mxfp8' if mx else 'bf16'}" if page else "")
+            sweep["attn_paged" if page else "attn_mxkv" if mx else "attn"][key] = {
                 "us": t * 1e3, "tokens/s": Bs / (t * 1e-3), "GB/s": gb, "frac": gb / PEAK_HBM_GBS,
                 "kernels": kernel_table(per, 20, 1, 0, kv, Bs)}
-            log(f"attn{' mxkv' if mx else ''} B={Bs} kv {lo}..{hi}: {t * 1e3:.1f} us {gb:.0f} GB/s")
+            log(f"attn{' mxkv' if mx else ''}{f' paged {page}' if page else ''} B={Bs} kv {lo}..{hi}: "
+                f"{t * 1e3:.1f} us {gb:.0f} GB/s")
             del w
             torch.cuda.empty_cache()
         result["sweep"] = sweep

@@ -59,6 +59,12 @@ SIGNATURES = {
     "gqa_decode_attn_mxkv": (ctypes.c_int, [c_vp, c_vp, c_vp, c_vp, c_vp, c_i64, c_i64, c_i64, c_i64, c_i64, c_i64,
                                             c_vp, c_i64, c_i32, c_i32, c_i32, c_i64, c_i64, ctypes.c_float, c_vp,
                                             c_vp, c_sz, c_vp, c_vp]),
+    "gqa_decode_attn_paged": (ctypes.c_int, [c_vp, c_vp, c_vp, c_i64, c_i64, c_i64, c_i64, c_i32, c_vp, c_i64,
+                                             c_i64, c_vp, c_i64, c_i32, c_i32, c_i32, c_i64, ctypes.c_float, c_vp,
+                                             c_vp, c_sz, c_vp, c_vp]),
+    "gqa_decode_attn_paged_mxkv": (ctypes.c_int, [c_vp, c_vp, c_vp, c_vp, c_vp, c_i64, c_i64, c_i64, c_i64, c_i64,
+                                                  c_i64, c_i64, c_i32, c_vp, c_i64, c_i64, c_vp, c_i64, c_i32, c_i32,
+                                                  c_i32, c_i64, ctypes.c_float, c_vp, c_vp, c_sz, c_vp, c_vp]),
     "qlinear_fp8_workspace_size": (c_sz, [c_i64, c_i64, c_i64]),
     "qlinear_fp8": (ctypes.c_int, [c_vp, c_i64, c_i64, c_i64, c_vp, ctypes.c_float, QWeightC, c_i64, c_vp, c_i64,
                                    ctypes.c_int, c_vp, c_i64, c_vp, c_sz, c_vp]),

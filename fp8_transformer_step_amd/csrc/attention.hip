@@ -22,6 +22,12 @@
 //     on the VALU with V rows loaded 16 bytes per lane, reduced across lanes
 //     and waves; the chunk's (max, sum, acc) goes to the workspace.
 //   * A second small kernel merges the chunks of every (sequence, head).
+//   * Paged caches (the pages' "paged decode" variant, same section of "How
+//     We Made Our Text-to-Speech API Free"): position t of sequence b lives
+//     in slot t % P of pool page block_table[b][t / P].  A piece first reads
+//     the page ids its positions span into LDS (at most kMaxChunk / 16 + 1 of
+//     them), checks them against the pool, then runs the same loops with the
+//     row address taken from that table.
 #include <algorithm>
 
 #include "common.h"
@@ -33,6 +39,7 @@ namespace fp8s {
 
 constexpr int kMaxChunk = 1024;
 constexpr int kBalMaxB = 1024;            // batches up to this size use the balanced split
+constexpr int kMinPage = 16;              // smallest page of a paged cache (positions)
 
 struct AttnArgs {
     const uint16_t* q;
@@ -57,6 +64,11 @@ struct AttnArgs {
     // (first record, record count) of every sequence, written for the merge
     int bal, bal_slots, bal_W;
     int2* seq_rec;
+    // paged caches (bt non-null): sb (esb) is the pool's page stride, the
+    // pages of sequence b are bt[b * bt_stride + i], valid ids 0 .. n_pages-1
+    const int32_t* bt;
+    int64_t bt_stride, n_pages;
+    int page_log2;
 };
 
 // UE8M0 byte -> 2^(E - 127) (E = 0 is the subnormal 2^-127).
@@ -100,10 +112,24 @@ __device__ __forceinline__ bool kv_len_ok(int L, const AttnArgs& a) {
 // the score MFMA then takes the D/4 consecutive d from j4*D/4, one scale
 // group, and the query operand is permuted the same way (the dot product
 // does not depend on the order of d).
+// The G query heads of (sequence b, KV head g) written as zeros (an invalid
+// kv_len or page id), with their quantised copy when one is asked for.
+template <int D, int G>
+__device__ __forceinline__ void zero_heads(const AttnArgs& a, int b, int g) {
+    for (int e = threadIdx.x; e < G * D; e += 256) a.out[((int64_t)b * a.Hq + g * G) * D + e] = 0;
+    if constexpr ((G * D) % 128 == 0)
+        if (a.qo)
+            for (int w = threadIdx.x >> 6; w < G * D / 128; w += 4)
+                quant_out_wave(a, b, g * G * D / 128 + w, 0.0f, 0.0f, threadIdx.x & 63);
+}
+
 // One piece: positions [t_begin, t_begin + n_tok) of (sequence b, KV head g),
 // n_tok <= kMaxChunk.  Not SINGLE: the piece's (max, sum, accumulator) of
-// query head g*G + h go to rec + h * rec_hs.
-template <int D, int G, bool SINGLE, bool MX>
+// query head g*G + h go to rec + h * rec_hs.  PAGED: a page id outside the
+// pool stops the piece before any cache read; it reports the error and
+// writes zeros (SINGLE) or records whose sum is -1, which the merge turns
+// into a zero output.
+template <int D, int G, bool SINGLE, bool MX, bool PAGED>
 __device__ __forceinline__ void attn_piece(const AttnArgs& a, int b, int g, int t_begin, int n_tok, float* rec,
                                            int64_t rec_hs) {
     constexpr int NJ = D / 32;                 // MFMA K-steps over the head dim
@@ -112,10 +138,49 @@ __device__ __forceinline__ void attn_piece(const AttnArgs& a, int b, int g, int 
     __shared__ float s_p[G][kMaxChunk];        // scores, then probabilities
     __shared__ float s_red[4][G][D];
     __shared__ float s_ml[G][2];
+    __shared__ int s_pg[PAGED ? kMaxChunk / kMinPage + 1 : 1];
 
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-    const uint16_t* kbase = a.k + (int64_t)b * a.sb + (int64_t)g * a.sh;
-    const uint16_t* vbase = a.v + (int64_t)b * a.sb + (int64_t)g * a.sh;
+    // Row t of the piece's KV head starts at element (byte) row(t) of the
+    // cache base, its exponents at erow(t) of the exponent base.
+    const int64_t bofs = PAGED ? 0 : (int64_t)b * a.sb, ebofs = PAGED ? 0 : (int64_t)b * a.esb;
+    const int pfirst = PAGED ? t_begin >> a.page_log2 : 0;
+    const int64_t pmask = PAGED ? (1ll << a.page_log2) - 1 : 0;
+    auto row = [&](int64_t t) -> int64_t {
+        if constexpr (PAGED) return (int64_t)s_pg[(int)(t >> a.page_log2) - pfirst] * a.sb + (t & pmask) * a.st;
+        else return t * a.st;
+    };
+    auto erow = [&](int64_t t) -> int64_t {
+        if constexpr (PAGED) return (int64_t)s_pg[(int)(t >> a.page_log2) - pfirst] * a.esb + (t & pmask) * a.est;
+        else return t * a.est;
+    };
+    if constexpr (PAGED) {
+        const int np = ((t_begin + n_tok - 1) >> a.page_log2) - pfirst + 1;
+        int bad = 0;
+        for (int i = threadIdx.x; i < np; i += 256) {
+            const int pg = a.bt[(int64_t)b * a.bt_stride + pfirst + i];
+            bad |= pg < 0 || (int64_t)pg >= a.n_pages;
+            s_pg[i] = pg;
+        }
+        if (__syncthreads_or(bad)) {
+            if (threadIdx.x == 0) report_error(a.err, FP8S_DEV_PAGE_RANGE);
+            if (SINGLE) {
+                zero_heads<D, G>(a, b, g);
+            } else {
+                for (int h = threadIdx.x; h < G; h += 256) {
+                    rec[h * rec_hs] = -INFINITY;
+                    rec[h * rec_hs + 1] = -1.0f;
+                }
+            }
+            return;
+        }
+    }
+    const uint16_t* kbase = MX ? nullptr : a.k + bofs + (int64_t)g * a.sh;
+    const uint16_t* vbase = MX ? nullptr : a.v + bofs + (int64_t)g * a.sh;
+    const uint8_t* kqbase = MX ? a.kq + bofs + (int64_t)g * a.sh : nullptr;
+    const uint8_t* vqbase = MX ? a.vq + bofs + (int64_t)g * a.sh : nullptr;
+    const uint8_t* kebase = MX ? a.ke + ebofs + (int64_t)g * a.esh : nullptr;
+    const uint8_t* vebase = MX ? a.ve + ebofs + (int64_t)g * a.esh : nullptr;
 
     // Query heads of this KV head as MFMA A rows (rows >= G are zero).
     v8bf qa[NJ];
@@ -147,10 +212,10 @@ __device__ __forceinline__ void attn_piece(const AttnArgs& a, int b, int g, int 
             for (int i = 0; i < QB / 16; ++i) raw[i] = make_uint4(0, 0, 0, 0);
             if (live) {
                 const int64_t t = t_begin + tl;
-                const uint8_t* src = a.kq + (int64_t)b * a.sb + (int64_t)g * a.sh + t * a.st + (lane >> 4) * QB;
+                const uint8_t* src = kqbase + row(t) + (lane >> 4) * QB;
 #pragma unroll
                 for (int i = 0; i < QB / 16; ++i) raw[i] = reinterpret_cast<const uint4*>(src)[i];
-                X = ue8m0_f32(a.ke[(int64_t)b * a.esb + (int64_t)g * a.esh + t * a.est + (lane >> 4) * QB / 32]);
+                X = ue8m0_f32(kebase[erow(t) + (lane >> 4) * QB / 32]);
             }
 #pragma unroll
             for (int j = 0; j < NJ; ++j) {
@@ -163,7 +228,7 @@ __device__ __forceinline__ void attn_piece(const AttnArgs& a, int b, int g, int 
             for (int j = 0; j < NJ; ++j) {
                 kw[j] = make_uint4(0, 0, 0, 0);
                 if (live)
-                    kw[j] = *reinterpret_cast<const uint4*>(kbase + (int64_t)(t_begin + tl) * a.st + 32 * j + 8 * (lane >> 4));
+                    kw[j] = *reinterpret_cast<const uint4*>(kbase + row(t_begin + tl) + 32 * j + 8 * (lane >> 4));
             }
         }
 #pragma unroll
@@ -206,9 +271,9 @@ __device__ __forceinline__ void attn_piece(const AttnArgs& a, int b, int g, int 
     for (int t = wave * TPL + slot; t < n_tok; t += 4 * TPL) {
         float vf[8];
         if constexpr (MX) {
-            const int64_t row = (int64_t)(t_begin + t);
-            const uint2 w = *reinterpret_cast<const uint2*>(a.vq + (int64_t)b * a.sb + (int64_t)g * a.sh + row * a.st + dl);
-            const float X = ue8m0_f32(a.ve[(int64_t)b * a.esb + (int64_t)g * a.esh + row * a.est + dl / 32]);
+            const int64_t tt = (int64_t)(t_begin + t);
+            const uint2 w = *reinterpret_cast<const uint2*>(vqbase + row(tt) + dl);
+            const float X = ue8m0_f32(vebase[erow(tt) + dl / 32]);
             const uint32_t ww[2] = {w.x, w.y};
 #pragma unroll
             for (int i = 0; i < 2; ++i) {
@@ -217,7 +282,7 @@ __device__ __forceinline__ void attn_piece(const AttnArgs& a, int b, int g, int 
                 vf[4 * i] = lo[0] * X; vf[4 * i + 1] = lo[1] * X; vf[4 * i + 2] = hi[0] * X; vf[4 * i + 3] = hi[1] * X;
             }
         } else {
-            const uint4 w = *reinterpret_cast<const uint4*>(vbase + (int64_t)(t_begin + t) * a.st + dl);
+            const uint4 w = *reinterpret_cast<const uint4*>(vbase + row(t_begin + t) + dl);
             const uint32_t ww[4] = {w.x, w.y, w.z, w.w};
 #pragma unroll
             for (int i = 0; i < 4; ++i) { vf[2 * i] = bf16_to_f32(ww[i] & 0xFFFFu); vf[2 * i + 1] = bf16_to_f32(ww[i] >> 16); }
@@ -273,7 +338,7 @@ __device__ __forceinline__ void attn_piece(const AttnArgs& a, int b, int g, int 
 // consecutive workgroups (which the dispatcher deals round-robin to the 8
 // XCDs) belong to different (sequence, KV head) pairs, so every XCD gets a
 // fair share of long and short prefixes.
-template <int D, int G, bool SINGLE, bool MX>
+template <int D, int G, bool SINGLE, bool MX, bool PAGED>
 __device__ __forceinline__ void attn_split_body(const AttnArgs& a) {
     const int bg = blockIdx.x % (a.B * a.Hkv);
     const int sp = blockIdx.x / (a.B * a.Hkv);
@@ -281,19 +346,14 @@ __device__ __forceinline__ void attn_split_body(const AttnArgs& a) {
     const int L = a.kv_len[b];
     if (!kv_len_ok(L, a)) {                    // the merge writes zeros and reports
         if (SINGLE) {
-            for (int e = threadIdx.x; e < G * D; e += 256)
-                a.out[((int64_t)b * a.Hq + g * G) * D + e] = 0;
+            zero_heads<D, G>(a, b, g);
             if (threadIdx.x == 0 && g == 0) report_error(a.err, FP8S_DEV_KVLEN_RANGE);
-            if constexpr ((G * D) % 128 == 0)
-                if (a.qo)
-                    for (int w = threadIdx.x >> 6; w < G * D / 128; w += 4)
-                        quant_out_wave(a, b, g * G * D / 128 + w, 0.0f, 0.0f, threadIdx.x & 63);
         }
         return;
     }
     const int t_begin = sp * a.chunk;
     if (t_begin >= L) return;                  // chunk entirely past the prefix
-    attn_piece<D, G, SINGLE, MX>(a, b, g, t_begin, min(a.chunk, L - t_begin),
+    attn_piece<D, G, SINGLE, MX, PAGED>(a, b, g, t_begin, min(a.chunk, L - t_begin),
                                  a.part + (((int64_t)b * a.Hq + g * G) * a.n_split + sp) * (D + 2),
                                  (int64_t)a.n_split * (D + 2));
 }
@@ -311,7 +371,7 @@ __device__ __forceinline__ void attn_split_body(const AttnArgs& a) {
 // sequence for the merge.
 __device__ __forceinline__ int bal_owner(int64_t x, int64_t T, int W) { return (int)(((x + 1) * W - 1) / T); }
 
-template <int D, int G, bool MX>
+template <int D, int G, bool MX, bool PAGED>
 __device__ __forceinline__ void attn_bal_body(const AttnArgs& a) {
     __shared__ int s_pre[kBalMaxB + 1];        // s_pre[b] = valid positions of sequences < b (< 2^31)
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
@@ -365,33 +425,33 @@ __device__ __forceinline__ void attn_bal_body(const AttnArgs& a) {
             const int64_t s0 = max(R0, p0), s1 = min(R1, p1);
             if (s1 <= s0) continue;
             __syncthreads();                   // the previous piece is done with LDS
-            attn_piece<D, G, false, MX>(a, b, g, (int)(s0 - p0), (int)(s1 - s0),
+            attn_piece<D, G, false, MX, PAGED>(a, b, g, (int)(s0 - p0), (int)(s1 - s0),
                                         a.part + ((int64_t)(v + b) * a.Hq + g * G) * (D + 2), D + 2);
         }
     }
 }
 
-template <int D, int G, bool SINGLE>
+template <int D, int G, bool SINGLE, bool PAGED>
 __global__ __launch_bounds__(256) void attn_split_kernel(AttnArgs a) {
-    attn_split_body<D, G, SINGLE, false>(a);
+    attn_split_body<D, G, SINGLE, false, PAGED>(a);
 }
 
-template <int D, int G>
+template <int D, int G, bool PAGED>
 __global__ __launch_bounds__(256) void attn_bal_kernel(AttnArgs a) {
-    attn_bal_body<D, G, false>(a);
+    attn_bal_body<D, G, false, PAGED>(a);
 }
 
 // The MXFP8-cache kernel holds five workgroups per CU only when capped at
 // 102 registers (measured faster: 85 against 90 us at B = 64, kv up to
 // 4096); the bf16 kernel is faster uncapped.
-template <int D, int G, bool SINGLE>
+template <int D, int G, bool SINGLE, bool PAGED>
 __global__ __launch_bounds__(256, 5) void attn_split_mx_kernel(AttnArgs a) {
-    attn_split_body<D, G, SINGLE, true>(a);
+    attn_split_body<D, G, SINGLE, true, PAGED>(a);
 }
 
-template <int D, int G>
+template <int D, int G, bool PAGED>
 __global__ __launch_bounds__(256, 5) void attn_bal_mx_kernel(AttnArgs a) {
-    attn_bal_body<D, G, true>(a);
+    attn_bal_body<D, G, true, PAGED>(a);
 }
 
 // Merge the chunks of one (sequence, query head): out = sum_i 2^(m_i - M) acc_i
@@ -400,7 +460,9 @@ __global__ __launch_bounds__(256, 5) void attn_bal_mx_kernel(AttnArgs a) {
 // B column lane + 64 (one head for D = 128, two heads for D = 64).  Lane i
 // holds chunk i's statistics and its weight reaches the other lanes by
 // readlane; the accumulators of the first kU chunks are loaded together with
-// the statistics, so the common case costs one memory round trip.
+// the statistics, so the common case costs one memory round trip.  A record
+// whose sum is negative comes from a piece that met an invalid page id: the
+// head's output is then zero.
 template <int D>
 __global__ __launch_bounds__(256) void attn_merge_kernel(AttnArgs a) {
     constexpr int kU = 8;
@@ -453,6 +515,13 @@ __global__ __launch_bounds__(256) void attn_merge_kernel(AttnArgs a) {
     }
     MA = fmax_xor<64>(MA);
     MB = D == 128 ? MA : fmax_xor<64>(MB);
+    bool poisonA = lA < 0.0f, poisonB = lB < 0.0f;
+    for (int i = lane + 64; i < n; i += 64) {
+        poisonA |= pA[i * cs + 1] < 0.0f;
+        poisonB |= pB[i * cs + 1] < 0.0f;
+    }
+    poisonA = __any(poisonA);
+    poisonB = D == 128 ? poisonA : (bool)__any(poisonB);
     const float wA = lane < n ? exp2f(mA - MA) : 0.0f;
     const float wB = D == 128 ? wA : (lane < n ? exp2f(mB - MB) : 0.0f);
     float denA = wA * lA, denB = wB * lB;
@@ -480,8 +549,8 @@ __global__ __launch_bounds__(256) void attn_merge_kernel(AttnArgs a) {
         numA += wjA * pA[j * cs + 2 + dA];
         numB += wjB * pB[j * cs + 2 + dB];
     }
-    const float vA = n > 0 ? bf16_to_f32(f32_to_bf16(numA / denA)) : 0.0f;
-    const float vB = n > 0 ? bf16_to_f32(f32_to_bf16(numB / denB)) : 0.0f;
+    const float vA = n > 0 && !poisonA ? bf16_to_f32(f32_to_bf16(numA / denA)) : 0.0f;
+    const float vB = n > 0 && !poisonB ? bf16_to_f32(f32_to_bf16(numB / denB)) : 0.0f;
     a.out[((int64_t)b * a.Hq + hA) * D + dA] = (uint16_t)f32_to_bf16(vA);
     if (hasB) a.out[((int64_t)b * a.Hq + hB) * D + dB] = (uint16_t)f32_to_bf16(vB);
     if (a.qo) quant_out_wave(a, b, pr, vA, vB, lane);
@@ -578,31 +647,77 @@ static int bal_slots(K kernel, int Hkv) {
     return std::max(1, slots[dev] / Hkv);
 }
 
-template <int D, int G, bool MX>
-static void launch_split(dim3 grid, hipStream_t st, const AttnArgs& a) {
+// Profiler names of the split kernels: [MX][PAGED][single | split].
+static const char* const kSplitNames[2][2][2] = {
+    {{"attn_split", "attn_single"}, {"attn_split_paged", "attn_single_paged"}},
+    {{"attn_split_mx", "attn_single_mx"}, {"attn_split_mx_paged", "attn_single_mx_paged"}}};
+
+template <int D, int G, bool MX, bool PAGED>
+static void launch_split_t(dim3 grid, hipStream_t st, const AttnArgs& a) {
+    const char* const* names = kSplitNames[MX][PAGED];
     if (a.bal) {
         AttnArgs b = a;
         if (MX) {
-            b.bal_slots = bal_slots(attn_bal_mx_kernel<D, G>, a.Hkv);
-            FP8S_LAUNCH("attn_split_mx", (attn_bal_mx_kernel<D, G>), dim3((unsigned)(b.bal_slots * a.Hkv)),
+            b.bal_slots = bal_slots(attn_bal_mx_kernel<D, G, PAGED>, a.Hkv);
+            FP8S_LAUNCH(names[0], (attn_bal_mx_kernel<D, G, PAGED>), dim3((unsigned)(b.bal_slots * a.Hkv)),
                         dim3(256), 0, st, b);
         } else {
-            b.bal_slots = bal_slots(attn_bal_kernel<D, G>, a.Hkv);
-            FP8S_LAUNCH("attn_split", (attn_bal_kernel<D, G>), dim3((unsigned)(b.bal_slots * a.Hkv)), dim3(256), 0,
-                        st, b);
+            b.bal_slots = bal_slots(attn_bal_kernel<D, G, PAGED>, a.Hkv);
+            FP8S_LAUNCH(names[0], (attn_bal_kernel<D, G, PAGED>), dim3((unsigned)(b.bal_slots * a.Hkv)),
+                        dim3(256), 0, st, b);
         }
         return;
     }
     if (MX) {
         if (a.n_split == 1)
-            FP8S_LAUNCH("attn_single_mx", (attn_split_mx_kernel<D, G, true>), grid, dim3(256), 0, st, a);
+            FP8S_LAUNCH(names[1], (attn_split_mx_kernel<D, G, true, PAGED>), grid, dim3(256), 0, st, a);
         else
-            FP8S_LAUNCH("attn_split_mx", (attn_split_mx_kernel<D, G, false>), grid, dim3(256), 0, st, a);
+            FP8S_LAUNCH(names[0], (attn_split_mx_kernel<D, G, false, PAGED>), grid, dim3(256), 0, st, a);
     } else if (a.n_split == 1) {
-        FP8S_LAUNCH("attn_single", (attn_split_kernel<D, G, true>), grid, dim3(256), 0, st, a);
+        FP8S_LAUNCH(names[1], (attn_split_kernel<D, G, true, PAGED>), grid, dim3(256), 0, st, a);
     } else {
-        FP8S_LAUNCH("attn_split", (attn_split_kernel<D, G, false>), grid, dim3(256), 0, st, a);
+        FP8S_LAUNCH(names[0], (attn_split_kernel<D, G, false, PAGED>), grid, dim3(256), 0, st, a);
     }
+}
+
+template <int D, int G, bool MX>
+static void launch_split(dim3 grid, hipStream_t st, const AttnArgs& a) {
+    if (a.bt)
+        launch_split_t<D, G, MX, true>(grid, st, a);
+    else
+        launch_split_t<D, G, MX, false>(grid, st, a);
+}
+
+// Paged-cache arguments: block_table non-null, bt_stride >= max_pages >= 1,
+// 1 <= num_pages < 2^31, page_size a power of two from kMinPage to 2^20.
+static int check_paged(const char* fn, const int32_t* block_table, int64_t bt_stride, int64_t num_pages,
+                       int32_t page_size, int64_t max_pages, int64_t B, PagedSpec* spec, int64_t* cap) {
+    FP8S_REQUIRE(block_table, FP8S_EINVAL, "%s: null block table", fn);
+    FP8S_REQUIRE(page_size >= kMinPage && page_size <= (1 << 20) && (page_size & (page_size - 1)) == 0,
+                 FP8S_EUNSUPPORTED, "%s: page size %d (a power of two from %d to 2^20 supported)", fn, page_size,
+                 kMinPage);
+    FP8S_REQUIRE(num_pages >= 1 && num_pages < (1ll << 31), FP8S_EINVAL, "%s: num_pages %lld outside [1, 2^31)", fn,
+                 (long long)num_pages);
+    FP8S_REQUIRE(max_pages >= 1 && bt_stride >= max_pages, FP8S_EINVAL,
+                 "%s: need 1 <= max_pages_per_seq <= block-table row stride", fn);
+    FP8S_REQUIRE(max_pages <= (1ll << 31) / page_size, FP8S_EUNSUPPORTED,
+                 "%s: max_pages_per_seq * page_size must stay below 2^31", fn);
+    FP8S_REQUIRE(bt_stride <= (1ll << 40) / B, FP8S_EINVAL, "%s: block-table row stride too large", fn);
+    int lg = 0;
+    while ((1 << lg) < page_size) ++lg;
+    spec->block_table = block_table;
+    spec->bt_stride = bt_stride;
+    spec->num_pages = num_pages;
+    spec->page_log2 = lg;
+    *cap = max_pages * page_size;
+    return FP8S_OK;
+}
+
+static void set_paged(AttnArgs& a, const PagedSpec* paged) {
+    a.bt = paged ? paged->block_table : nullptr;
+    a.bt_stride = paged ? paged->bt_stride : 0;
+    a.n_pages = paged ? paged->num_pages : 0;
+    a.page_log2 = paged ? paged->page_log2 : 0;
 }
 
 // The attention with, optionally (qo non-null), its output also quantised
@@ -612,7 +727,8 @@ static void launch_split(dim3 grid, hipStream_t st, const AttnArgs& a) {
 int gqa_decode_attn_ex(const uint16_t* q, const uint16_t* k_cache, const uint16_t* v_cache, int64_t stride_b,
                        int64_t stride_h, int64_t stride_t, const int32_t* kv_len, int64_t B, int32_t Hq, int32_t Hkv,
                        int32_t D, int64_t cap, int64_t hint, float softmax_scale, uint16_t* out, uint8_t* qo, float* so,
-                       void* workspace, size_t workspace_bytes, int32_t* err_flag, void* stream) {
+                       void* workspace, size_t workspace_bytes, int32_t* err_flag, void* stream,
+                       const PagedSpec* paged) {
     FP8S_REQUIRE(q && k_cache && v_cache && kv_len && out, FP8S_EINVAL, "gqa_decode_attn: null pointer");
     FP8S_REQUIRE(B >= 1 && Hq >= 1 && Hkv >= 1 && cap >= 1 && hint >= 1, FP8S_EINVAL,
                  "gqa_decode_attn: sizes must be positive");
@@ -647,6 +763,7 @@ int gqa_decode_attn_ex(const uint16_t* q, const uint16_t* k_cache, const uint16_
     a.qo = qo; a.so = so; a.qo_KB = Hq * D / 128;
     a.kq = a.ke = a.vq = a.ve = nullptr;
     a.esb = a.esh = a.est = 0;
+    set_paged(a, paged);
     return attn_launch<false>(a, D, G, as_stream(stream));
 }
 
@@ -656,7 +773,8 @@ static int gqa_decode_attn_mxkv_ex(const uint16_t* q, const uint8_t* kq, const u
                             const uint8_t* ve, int64_t stride_b, int64_t stride_h, int64_t stride_t, int64_t sstride_b,
                             int64_t sstride_h, int64_t sstride_t, const int32_t* kv_len, int64_t B, int32_t Hq,
                             int32_t Hkv, int32_t D, int64_t cap, int64_t hint, float softmax_scale, uint16_t* out,
-                            void* workspace, size_t workspace_bytes, int32_t* err_flag, void* stream) {
+                            void* workspace, size_t workspace_bytes, int32_t* err_flag, void* stream,
+                            const PagedSpec* paged = nullptr) {
     FP8S_REQUIRE(q && kq && ke && vq && ve && kv_len && out, FP8S_EINVAL, "gqa_decode_attn_mxkv: null pointer");
     FP8S_REQUIRE(B >= 1 && Hq >= 1 && Hkv >= 1 && cap >= 1 && hint >= 1, FP8S_EINVAL,
                  "gqa_decode_attn_mxkv: sizes must be positive");
@@ -693,6 +811,7 @@ static int gqa_decode_attn_mxkv_ex(const uint16_t* q, const uint8_t* kq, const u
     a.out = out;
     a.err = err_flag;
     a.qo = nullptr; a.so = nullptr; a.qo_KB = Hq * D / 128;
+    set_paged(a, paged);
     return attn_launch<true>(a, D, G, as_stream(stream));
 }
 
@@ -732,4 +851,42 @@ extern "C" int gqa_decode_attn(const uint16_t* q, const uint16_t* k_cache, const
     clear_error();
     return gqa_decode_attn_ex(q, k_cache, v_cache, stride_b, stride_h, stride_t, kv_len, B, Hq, Hkv, D, cap, hint,
                               softmax_scale, out, nullptr, nullptr, workspace, workspace_bytes, err_flag, stream);
+}
+
+extern "C" int gqa_decode_attn_paged(const uint16_t* q, const uint16_t* k_pool, const uint16_t* v_pool,
+                                     int64_t stride_page, int64_t stride_h, int64_t stride_t, int64_t num_pages,
+                                     int32_t page_size, const int32_t* block_table, int64_t bt_stride,
+                                     int64_t max_pages_per_seq, const int32_t* kv_len, int64_t B, int32_t Hq,
+                                     int32_t Hkv, int32_t D, int64_t hint, float softmax_scale, uint16_t* out,
+                                     void* workspace, size_t workspace_bytes, int32_t* err_flag, void* stream) {
+    clear_error();
+    FP8S_REQUIRE(B >= 1, FP8S_EINVAL, "gqa_decode_attn_paged: sizes must be positive");
+    PagedSpec spec;
+    int64_t cap = 0;
+    const int rc = check_paged("gqa_decode_attn_paged", block_table, bt_stride, num_pages, page_size,
+                               max_pages_per_seq, B, &spec, &cap);
+    if (rc) return rc;
+    return gqa_decode_attn_ex(q, k_pool, v_pool, stride_page, stride_h, stride_t, kv_len, B, Hq, Hkv, D, cap, hint,
+                              softmax_scale, out, nullptr, nullptr, workspace, workspace_bytes, err_flag, stream,
+                              &spec);
+}
+
+extern "C" int gqa_decode_attn_paged_mxkv(const uint16_t* q, const uint8_t* k_q, const uint8_t* k_e,
+                                          const uint8_t* v_q, const uint8_t* v_e, int64_t stride_page,
+                                          int64_t stride_h, int64_t stride_t, int64_t sstride_page, int64_t sstride_h,
+                                          int64_t sstride_t, int64_t num_pages, int32_t page_size,
+                                          const int32_t* block_table, int64_t bt_stride, int64_t max_pages_per_seq,
+                                          const int32_t* kv_len, int64_t B, int32_t Hq, int32_t Hkv, int32_t D,
+                                          int64_t hint, float softmax_scale, uint16_t* out, void* workspace,
+                                          size_t workspace_bytes, int32_t* err_flag, void* stream) {
+    clear_error();
+    FP8S_REQUIRE(B >= 1, FP8S_EINVAL, "gqa_decode_attn_paged_mxkv: sizes must be positive");
+    PagedSpec spec;
+    int64_t cap = 0;
+    const int rc = check_paged("gqa_decode_attn_paged_mxkv", block_table, bt_stride, num_pages, page_size,
+                               max_pages_per_seq, B, &spec, &cap);
+    if (rc) return rc;
+    return gqa_decode_attn_mxkv_ex(q, k_q, k_e, v_q, v_e, stride_page, stride_h, stride_t, sstride_page, sstride_h,
+                                   sstride_t, kv_len, B, Hq, Hkv, D, cap, hint, softmax_scale, out, workspace,
+                                   workspace_bytes, err_flag, stream, &spec);
 }

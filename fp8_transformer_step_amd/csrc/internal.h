@@ -35,10 +35,18 @@ int mlp_operand(int64_t M, int64_t H, int64_t I, int mode, void* workspace, size
 // gqa_decode_attn that can also write its output quantised (bsgemm 1x128
 // groups, the operand layout of qlinear_fp8_prequant) into qo / so; the
 // quantised copy needs Hq/Hkv * D to be a multiple of 128.
+// paged (optional): the caches are page pools; stride_b is then the page
+// stride and cap = max_pages * page_size.
+struct PagedSpec {
+    const int32_t* block_table;
+    int64_t bt_stride, num_pages;
+    int page_log2;
+};
 int gqa_decode_attn_ex(const uint16_t* q, const uint16_t* k_cache, const uint16_t* v_cache, int64_t stride_b,
                        int64_t stride_h, int64_t stride_t, const int32_t* kv_len, int64_t B, int32_t Hq, int32_t Hkv,
                        int32_t D, int64_t cap, int64_t hint, float softmax_scale, uint16_t* out, uint8_t* qo, float* so,
-                       void* workspace, size_t workspace_bytes, int32_t* err_flag, void* stream);
+                       void* workspace, size_t workspace_bytes, int32_t* err_flag, void* stream,
+                       const PagedSpec* paged = nullptr);
 
 // Where qlinear_fp8 keeps its quantised activation operand inside a
 // workspace for an (M, N, K) product: fragments of 16 rows x 128 bytes in

@@ -22,7 +22,7 @@ W_TINY, W_BSGEMM, W_MXFP8, W_ATTN, W_STEP = 0, 1, 2, 3, 4
 
 # Tensor ids used in the seed formula.
 T_X, T_WG, T_WU, T_WD, T_Q, T_K, T_V, T_KVLEN, T_MASK = range(9)
-T_WQKV, T_WO, T_NORM, T_EMB, T_HEAD, T_CODES, T_POOL_W, T_POOL_KV = range(9, 17)
+T_WQKV, T_WO, T_NORM, T_EMB, T_HEAD, T_CODES, T_POOL_W, T_POOL_KV, T_PAGES = range(9, 18)
 
 
 def f32_to_bf16_bits(x):
@@ -78,6 +78,15 @@ def attention_prefix(workload, B, Hq, Hkv, D, max_len, extra=0):
     return (normal_bf16(workload, T_Q, (B, Hq, D), 1.0, extra),
             normal_bf16(workload, T_K, (B, Hkv, max_len, D), 1.0, extra),
             normal_bf16(workload, T_V, (B, Hkv, max_len, D), 1.0, extra))
+
+
+def page_table(workload, B, max_pages, n_pages, extra=0):
+    """A block table int32 [B, max_pages] of distinct page ids: the first
+    B * max_pages entries of a seeded permutation of range(n_pages)."""
+    if n_pages < B * max_pages:
+        raise ValueError("pool smaller than the table")
+    perm = rng(workload, T_PAGES, extra).permutation(n_pages)
+    return perm[:B * max_pages].reshape(B, max_pages).astype(np.int32)
 
 
 # ---- the full Dual-AR decode step ---------------------------------------------

@@ -16,7 +16,7 @@ from . import _lib
 # Quantisation and MLP modes (include/fp8step.h).
 Q_ACT_1x128, Q_WGT_128x128, Q_MX_1x32 = 0, 1, 2
 MLP_BSGEMM, MLP_MXFP8 = 0, 1
-DEV_KVLEN_RANGE, DEV_WAIT_TIMEOUT, DEV_CODE_RANGE = 1, 2, 3
+DEV_KVLEN_RANGE, DEV_WAIT_TIMEOUT, DEV_CODE_RANGE, DEV_PAGE_RANGE = 1, 2, 3, 4
 OUT_BF16, OUT_F32 = 0, 1
 
 
@@ -201,6 +201,76 @@ def gqa_decode_attn_mxkv(q, k, v, kv_len, max_kv_len_hint, softmax_scale=None,
         k.q.stride(0), k.q.stride(1), k.q.stride(2), k.e.stride(0), k.e.stride(1), k.e.stride(2),
         kv_len.data_ptr(), B, Hq, Hkv, D, cap, hint, float(softmax_scale),
         _bits(out), workspace.data_ptr(), workspace.numel(),
+        err.data_ptr() if err is not None else None, _stream()))
+    return out
+
+
+def _check_block_table(block_table, B):
+    if block_table.dtype != torch.int32 or block_table.dim() != 2 or block_table.shape[0] != B:
+        raise ValueError("block_table must be int32 [B, max_pages_per_seq]")
+    if block_table.stride(1) != 1:
+        raise ValueError("block_table rows must be contiguous")
+
+
+def gqa_decode_attn_paged(q, k_pool, v_pool, block_table, kv_len, max_kv_len_hint, softmax_scale=None,
+                          out=None, workspace=None, err=None):
+    """Decode attention of q [B, Hq, D] over paged bf16 caches: k_pool,
+    v_pool are indexed (page, kv head, slot, d) (any strides with unit stride
+    along d; a [pages, slot, head, d] pool is passed as .permute(0, 2, 1, 3));
+    position t of sequence b is slot t % P of page block_table[b, t // P]."""
+    _require_cuda(q, k_pool, v_pool, block_table, kv_len)
+    if kv_len.dtype != torch.int32:
+        raise TypeError("kv_len must be int32")
+    if k_pool.stride() != v_pool.stride() or k_pool.shape != v_pool.shape:
+        raise ValueError("k_pool and v_pool must share shape and strides")
+    B, Hq, D = q.shape
+    n_pages, Hkv, P, _ = k_pool.shape
+    if k_pool.stride(3) != 1:
+        raise ValueError("the head dimension must be contiguous")
+    _check_block_table(block_table, B)
+    max_pages = block_table.shape[1]
+    if softmax_scale is None:
+        softmax_scale = 1.0 / math.sqrt(D)
+    if out is None:
+        out = torch.empty((B, Hq, D), dtype=torch.bfloat16, device=q.device)
+    hint = min(int(max_kv_len_hint), max_pages * P)
+    if workspace is None:
+        workspace = new_attn_workspace(B, Hq, D, hint, q.device)
+    _lib.check(_lib.load().gqa_decode_attn_paged(
+        _bits(q.contiguous()), _bits(k_pool), _bits(v_pool), k_pool.stride(0), k_pool.stride(1), k_pool.stride(2),
+        n_pages, P, block_table.data_ptr(), block_table.stride(0), max_pages, kv_len.data_ptr(), B, Hq, Hkv, D,
+        hint, float(softmax_scale), _bits(out), workspace.data_ptr(), workspace.numel(),
+        err.data_ptr() if err is not None else None, _stream()))
+    return out
+
+
+def gqa_decode_attn_paged_mxkv(q, k, v, block_table, kv_len, max_kv_len_hint, softmax_scale=None,
+                               out=None, workspace=None, err=None):
+    """gqa_decode_attn_paged over MXFP8 page pools k, v (MxKvCache whose q
+    is [pages, Hkv, P, D] e4m3 and e [pages, Hkv, P, D/32] UE8M0)."""
+    _require_cuda(q, k.q, k.e, v.q, v.e, block_table, kv_len)
+    if kv_len.dtype != torch.int32:
+        raise TypeError("kv_len must be int32")
+    if k.q.stride() != v.q.stride() or k.e.stride() != v.e.stride() or k.q.shape != v.q.shape:
+        raise ValueError("k and v must share shapes and strides")
+    B, Hq, D = q.shape
+    n_pages, Hkv, P, _ = k.q.shape
+    if k.q.stride(3) != 1 or k.e.stride(3) != 1:
+        raise ValueError("the head dimension must be contiguous")
+    _check_block_table(block_table, B)
+    max_pages = block_table.shape[1]
+    if softmax_scale is None:
+        softmax_scale = 1.0 / math.sqrt(D)
+    if out is None:
+        out = torch.empty((B, Hq, D), dtype=torch.bfloat16, device=q.device)
+    hint = min(int(max_kv_len_hint), max_pages * P)
+    if workspace is None:
+        workspace = new_attn_workspace(B, Hq, D, hint, q.device)
+    _lib.check(_lib.load().gqa_decode_attn_paged_mxkv(
+        _bits(q.contiguous()), k.q.data_ptr(), k.e.data_ptr(), v.q.data_ptr(), v.e.data_ptr(),
+        k.q.stride(0), k.q.stride(1), k.q.stride(2), k.e.stride(0), k.e.stride(1), k.e.stride(2),
+        n_pages, P, block_table.data_ptr(), block_table.stride(0), max_pages, kv_len.data_ptr(), B, Hq, Hkv, D,
+        hint, float(softmax_scale), _bits(out), workspace.data_ptr(), workspace.numel(),
         err.data_ptr() if err is not None else None, _stream()))
     return out
 

@@ -61,7 +61,8 @@ enum fp8s_status {
 enum fp8s_device_error {
     FP8S_DEV_KVLEN_RANGE = 1, /* kv_len[b] outside [1, min(cap, hint)]         */
     FP8S_DEV_WAIT_TIMEOUT = 2,/* a cross-workgroup wait in a fused kernel gave up */
-    FP8S_DEV_CODE_RANGE = 3   /* a codebook index outside [0, codebook_size)   */
+    FP8S_DEV_CODE_RANGE = 3,  /* a codebook index outside [0, codebook_size)   */
+    FP8S_DEV_PAGE_RANGE = 4   /* a block-table page id outside [0, num_pages)  */
 };
 
 /* Output types of qlinear_fp8. */
@@ -169,7 +170,8 @@ FP8S_API int swiglu_mlp_fp8(const uint16_t* x, int64_t M, int64_t hidden, int64_
  *            (no device read, no synchronisation).
  *   softmax_scale    normally 1/sqrt(D).
  *   out      [B, Hq, D] bf16 contiguous.
- *   D must be 64 or 128; Hq must be a multiple of Hkv with Hq/Hkv <= 16.
+ *   D must be 64 or 128; Hq must be a multiple of Hkv with Hq/Hkv one of
+ *   1, 2, 4, 8.
  *   workspace  at least gqa_decode_attn_workspace_size(...) bytes (no
  *            initialisation needed).
  *   A kv_len outside the valid range writes zeros for that sequence and
@@ -212,6 +214,65 @@ FP8S_API int gqa_decode_attn_mxkv(const uint16_t* q, const uint8_t* k_q, const u
                     int64_t sstride_b, int64_t sstride_h, int64_t sstride_t,
                     const int32_t* kv_len, int64_t B, int32_t Hq, int32_t Hkv, int32_t D,
                     int64_t cap, int64_t max_kv_len_hint, float softmax_scale,
+                    uint16_t* out, void* workspace, size_t workspace_bytes,
+                    int32_t* err_flag, void* stream);
+
+/*
+ * gqa_decode_attn_paged -- gqa_decode_attn over a paged KV cache, the pages'
+ * paged decode attention ([TTS] "What's Open Source": paged decode with
+ * native GQA through a stride-0 K/V broadcast; here too the KV heads are
+ * never replicated).  The caches are pools of num_pages pages of page_size
+ * positions; position t of sequence b is slot t % page_size of page
+ * block_table[b * bt_stride + t / page_size].
+ *
+ *   k_pool, v_pool  bf16, element (page p, g, slot s, d) at
+ *              p * stride_page + g * stride_h + s * stride_t + d (d
+ *              contiguous; strides multiples of 8, stride_t >= D).  Both
+ *              [num_pages, Hkv, page_size, D] and [num_pages, page_size,
+ *              Hkv, D] pools are expressed by these strides.
+ *   page_size  a power of two, 16 .. 2^20.
+ *   block_table  device int32; row b holds the page ids of sequence b.
+ *              Entries t / page_size for t < kv_len[b] are read, the rest
+ *              never.  bt_stride >= max_pages_per_seq >= 1.
+ *   kv_len     valid 1 .. min(max_pages_per_seq * page_size, hint).
+ *   Everything else (q, hint, scale, out, err_flag, D, group sizes) as
+ *   gqa_decode_attn; the workspace is gqa_decode_attn_workspace_size(B, Hq,
+ *   D, max_pages_per_seq * page_size) bytes.
+ *   A read page id outside [0, num_pages) writes zeros for the query heads
+ *   whose positions it holds (all heads of the sequence when every KV head
+ *   reads it, as it always is), reads nothing from the pool for that part,
+ *   and sets FP8S_DEV_PAGE_RANGE in err_flag.  An invalid kv_len behaves as
+ *   in gqa_decode_attn.
+ *   The output is bit-identical to gqa_decode_attn on the contiguous caches
+ *   those pages describe (same batch, heads and hint).
+ *   Accuracy: max|out - oracle| <= 5e-3 * max|oracle|.
+ */
+FP8S_API int gqa_decode_attn_paged(const uint16_t* q, const uint16_t* k_pool, const uint16_t* v_pool,
+                    int64_t stride_page, int64_t stride_h, int64_t stride_t,
+                    int64_t num_pages, int32_t page_size,
+                    const int32_t* block_table, int64_t bt_stride, int64_t max_pages_per_seq,
+                    const int32_t* kv_len, int64_t B, int32_t Hq, int32_t Hkv, int32_t D,
+                    int64_t max_kv_len_hint, float softmax_scale,
+                    uint16_t* out, void* workspace, size_t workspace_bytes,
+                    int32_t* err_flag, void* stream);
+
+/*
+ * gqa_decode_attn_paged_mxkv -- gqa_decode_attn_paged over MXFP8 page pools
+ * (the row format of gqa_decode_attn_mxkv): e4m3 bytes at p * stride_page +
+ * g * stride_h + s * stride_t + d (byte strides, multiples of 16, stride_t >=
+ * D) and UE8M0 exponents at p * sstride_page + g * sstride_h + s * sstride_t
+ * + d/32.  The block table, page rules, errors and workspace are those of
+ * gqa_decode_attn_paged; the output is bit-identical to gqa_decode_attn_mxkv
+ * on the contiguous caches the pages describe.
+ */
+FP8S_API int gqa_decode_attn_paged_mxkv(const uint16_t* q, const uint8_t* k_q, const uint8_t* k_e,
+                    const uint8_t* v_q, const uint8_t* v_e,
+                    int64_t stride_page, int64_t stride_h, int64_t stride_t,
+                    int64_t sstride_page, int64_t sstride_h, int64_t sstride_t,
+                    int64_t num_pages, int32_t page_size,
+                    const int32_t* block_table, int64_t bt_stride, int64_t max_pages_per_seq,
+                    const int32_t* kv_len, int64_t B, int32_t Hq, int32_t Hkv, int32_t D,
+                    int64_t max_kv_len_hint, float softmax_scale,
                     uint16_t* out, void* workspace, size_t workspace_bytes,
                     int32_t* err_flag, void* stream);
 

@@ -23,6 +23,13 @@ decode attention (page "How We Made Our Text-to-Speech API Free", sections
 as e4m3 codes with one OCP UE8M0 exponent per 32 consecutive d, and the
 attention is the one above over the dequantised rows.
 
+The paged variants (gqa_decode_attention_paged, ..._paged_mxkv) are the
+pages' paged decode attention (same section "What's Open Source"): the cache
+rows live in a pool of fixed-size pages, and position t of sequence b is slot
+t % P of page block_table[b][t // P].  The pages give no page size or pool
+layout; the pool here is [pages, Hkv, P, D] and the attention is the one
+above over the rows the table names.
+
 Pins (tests/test_oracle_attention.py): kv_len = 1 returns v_0; q = 0 returns
 the mean of the V prefix; equality with an explicit np.repeat expansion of the
 heads; torch's float64 scaled_dot_product_attention on the expanded heads;
@@ -31,6 +38,10 @@ tolerance of the page's section 7 test); the kv_len schedule of section 5.
 MXFP8 variant: on caches built from MX-representable rows (so that the OCP
 rule gives back the codes and exponents they were built from) it equals the
 plain attention over those rows, and kv_len = 1 returns the dequantised v_0.
+Paged variants: a contiguous cache scattered over shuffled pages gives the
+contiguous result exactly; pages the table does not name (NaN-filled) never
+enter; kv_len = 1 returns slot 0 of the first named page; a brute-force
+scalar loop on a tiny pool; an out-of-pool page id is refused.
 """
 
 import numpy as np
@@ -95,3 +106,41 @@ def gqa_decode_attention_mxkv(q, k_codes, k_exps, v_codes, v_exps, kv_len, scale
     k = dequant_mx_rows(k_codes, k_exps)
     v = dequant_mx_rows(v_codes, v_exps)
     return gqa_decode_attention(q, k, v, kv_len, scale)
+
+
+def gather_paged(pool, block_table, kv_len, page_size):
+    """The contiguous cache [B, Hkv, max(kv_len), ...] that a paged pool
+    [pages, Hkv, P, ...] describes: row t < kv_len[b] of sequence b is slot
+    t % P of page block_table[b][t // P].  Rows past kv_len[b] stay zero; no
+    other page is read.  A named page outside the pool raises ValueError."""
+    pool = np.asarray(pool)
+    P = int(page_size)
+    if pool.shape[2] != P:
+        raise ValueError("pool slot axis must equal page_size")
+    B = len(kv_len)
+    Lmax = int(max(int(x) for x in kv_len))
+    out = np.zeros((B, pool.shape[1], Lmax) + pool.shape[3:], pool.dtype)
+    for b in range(B):
+        L = int(kv_len[b])
+        for i in range((L + P - 1) // P):
+            pg = int(block_table[b][i])
+            if not 0 <= pg < pool.shape[0]:
+                raise ValueError(f"block_table[{b}][{i}] = {pg} outside the pool")
+            n = min(P, L - i * P)
+            out[b, :, i * P:i * P + n] = pool[pg, :, :n]
+    return out
+
+
+def gqa_decode_attention_paged(q, k_pool, v_pool, block_table, kv_len, page_size, scale=None):
+    """gqa_decode_attention over paged caches k_pool, v_pool [pages, Hkv, P, D]."""
+    k = gather_paged(k_pool, block_table, kv_len, page_size)
+    v = gather_paged(v_pool, block_table, kv_len, page_size)
+    return gqa_decode_attention(q, k, v, kv_len, scale)
+
+
+def gqa_decode_attention_paged_mxkv(q, k_codes, k_exps, v_codes, v_exps, block_table, kv_len, page_size,
+                                    scale=None):
+    """gqa_decode_attention_mxkv over paged MXFP8 pools: codes [pages, Hkv,
+    P, D], exponents [pages, Hkv, P, D/32]."""
+    g = lambda pool: gather_paged(pool, block_table, kv_len, page_size)
+    return gqa_decode_attention_mxkv(q, g(k_codes), g(k_exps), g(v_codes), g(v_exps), kv_len, scale)

@@ -107,6 +107,27 @@ def test_attention_mxkv_argument_checks():
                                     32768, 400, ctypes.c_float(0.088), FAKE, FAKE, ws, None, None) == EINVAL
 
 
+def test_attention_paged_argument_checks():
+    lib = _lib.load()
+    ws = lib.gqa_decode_attn_workspace_size(2, 32, 128, 4096)
+    bf = lambda P, npg, bts, mp, wsb=ws, bt=FAKE, st=128: lib.gqa_decode_attn_paged(
+        FAKE, FAKE, FAKE, 8 * P * 128, P * 128, st, npg, P, bt, bts, mp, FAKE, 2, 32, 8, 128, 4096,
+        ctypes.c_float(0.088), FAKE, FAKE, wsb, None, None)
+    assert bf(8, 100, 256, 256) == EUNSUPPORTED             # page below 16 positions
+    assert bf(48, 100, 256, 256) == EUNSUPPORTED            # not a power of two
+    assert bf(16, 0, 256, 256) == EINVAL                    # empty pool
+    assert bf(16, 100, 255, 256) == EINVAL                  # table row shorter than max pages
+    assert bf(16, 100, 256, 0) == EINVAL
+    assert bf(16, 100, 256, 256, bt=None) == EINVAL         # no block table
+    assert bf(16, 100, 256, 256, st=132) == EINVAL          # slot stride not a multiple of 8
+    assert bf(16, 100, 256, 256, wsb=16) == EWORKSPACE
+    mx = lambda P, sst: lib.gqa_decode_attn_paged_mxkv(
+        FAKE, FAKE, FAKE, FAKE, FAKE, 8 * P * 128, P * 128, 128, 8 * P * 4, P * 4, sst, 100, P, FAKE, 256, 256,
+        FAKE, 2, 32, 8, 128, 4096, ctypes.c_float(0.088), FAKE, FAKE, ws, None, None)
+    assert mx(24, 4) == EUNSUPPORTED
+    assert mx(16, 3) == EINVAL                              # fewer than D/32 exponents per row
+
+
 @pytest.mark.parametrize("M,H,I", [(1, 2560, 9728), (128, 2560, 9728), (1, 256, 1024)])
 def test_mlp_workspace_is_small(M, H, I):
     n = _lib.load().swiglu_mlp_fp8_workspace_size(M, H, I, 0)

@@ -140,3 +140,92 @@ def test_mxkv_kv_len_one_returns_dequantised_first_value():
     out = attention.gqa_decode_attention_mxkv(q, kc, ke, vc, ve, np.ones(B, int))
     for h in range(Hq):
         assert np.array_equal(out[:, h], vval[:, 0, 0])
+
+
+def _scatter_pages(g, cache, P, spare=3):
+    """A pool [pages, Hkv, P, D] holding a contiguous cache [B, Hkv, cap, D]
+    (cap a multiple of P) on shuffled pages, plus `spare` NaN pages no
+    sequence names, and the block table [B, cap / P]."""
+    B, Hkv, cap, D = cache.shape
+    n = B * cap // P
+    order = g.permutation(n + spare)
+    pool = np.full((n + spare, Hkv, P, D), np.nan)
+    table = np.zeros((B, cap // P), np.int64)
+    for b in range(B):
+        for i in range(cap // P):
+            pg = order[b * (cap // P) + i]
+            table[b, i] = pg
+            pool[pg] = cache[b, :, i * P:(i + 1) * P]
+    return pool, table
+
+
+def test_paged_equals_contiguous_on_shuffled_pages():
+    g = np.random.default_rng(21)
+    q, k, v, L = _case(21, cap=48)
+    for P in (1, 4, 16):
+        kp, table = _scatter_pages(g, k, P)
+        vp = np.zeros_like(kp)
+        for b in range(3):
+            for i in range(48 // P):
+                vp[table[b, i]] = v[b, :, i * P:(i + 1) * P]
+        out = attention.gqa_decode_attention_paged(q, kp, vp, table, L, P)
+        assert np.isfinite(out).all()
+        assert np.array_equal(out, attention.gqa_decode_attention(q, k, v, L)), P
+
+
+def test_paged_kv_len_one_returns_first_slot_of_first_page():
+    g = np.random.default_rng(22)
+    q = g.standard_normal((2, 4, 8))
+    pool_k, pool_v = g.standard_normal((2, 5, 2, 4, 8))
+    table = np.array([[3, 0], [1, 4]])
+    out = attention.gqa_decode_attention_paged(q, pool_k, pool_v, table, [1, 1], 4)
+    for b in range(2):
+        for h in range(4):
+            assert np.array_equal(out[b, h], pool_v[table[b, 0], h // 2, 0])
+
+
+def test_paged_brute_force_scalar_loop():
+    """Tiny pool, every value from direct indexing and math.exp."""
+    import math
+    g = np.random.default_rng(23)
+    B, Hq, Hkv, D, P, n_pages = 2, 4, 2, 3, 2, 7
+    q = g.standard_normal((B, Hq, D))
+    pk, pv = g.standard_normal((2, n_pages, Hkv, P, D))
+    table = [[5, 2, 6], [0, 3, 1]]
+    L = [5, 3]
+    out = attention.gqa_decode_attention_paged(q, pk, pv, table, L, P, scale=0.7)
+    for b in range(B):
+        for h in range(Hq):
+            kvh = h // (Hq // Hkv)
+            rows = [(table[b][t // P], t % P) for t in range(L[b])]
+            s = [0.7 * sum(q[b, h, d] * pk[pg, kvh, sl, d] for d in range(D)) for pg, sl in rows]
+            w = [math.exp(x - max(s)) for x in s]
+            ref = [sum(w[i] * pv[pg, kvh, sl, d] for i, (pg, sl) in enumerate(rows)) / sum(w) for d in range(D)]
+            assert np.allclose(out[b, h], ref, rtol=1e-12, atol=1e-14)
+
+
+def test_paged_out_of_pool_page_rejected():
+    g = np.random.default_rng(24)
+    q = g.standard_normal((1, 2, 8))
+    pool = g.standard_normal((3, 1, 4, 8))
+    for bad in (3, -1):
+        try:
+            attention.gqa_decode_attention_paged(q, pool, pool, [[0, bad]], [6], 4)
+        except ValueError:
+            continue
+        raise AssertionError(f"page id {bad} accepted")
+    # the same entry past kv_len is never read
+    attention.gqa_decode_attention_paged(q, pool, pool, [[0, 99]], [4], 4)
+
+
+def test_paged_mxkv_equals_paged_plain_on_dequantised_pool():
+    g = np.random.default_rng(25)
+    B, Hq, Hkv, D, P = 2, 8, 2, 64, 16
+    q = g.standard_normal((B, Hq, D))
+    kval, kc, ke = _mx_representable(g, (6, Hkv, P, D))
+    vval, vc, ve = _mx_representable(g, (6, Hkv, P, D))
+    table = np.array([[4, 1, 5], [0, 2, 3]])
+    L = [40, 17]
+    out = attention.gqa_decode_attention_paged_mxkv(q, kc, ke, vc, ve, table, L, P)
+    ref = attention.gqa_decode_attention_paged(q, kval, vval, table, L, P)
+    assert np.allclose(out, ref, rtol=1e-12, atol=0)
