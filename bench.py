@@ -288,8 +288,9 @@ def step_launch_plan(cfg, kv_len):
 
 def time_step(torch, ops, dm, kv, prev, steps, warmup, workspace, err):
     """ms per step over `steps` back-to-back steps (HIP events on the stream,
-    bracketed by synchronisation), the wall clock per step, and the library's
-    per-launch records of a second pass of `steps` steps."""
+    bracketed by synchronisation), the wall clock per step, the library's
+    per-launch records of a second pass of `steps` steps, and the ms of each
+    step of a third pass with an event between steps."""
     codes = torch.empty(prev.shape, dtype=torch.int32, device="cuda")
     for _ in range(warmup):
         ops.dual_ar_decode_step(dm, kv, prev, codes=codes, workspace=workspace, err=err)
@@ -308,7 +309,21 @@ def time_step(torch, ops, dm, kv, prev, steps, warmup, workspace, err):
     for _ in range(steps):
         ops.dual_ar_decode_step(dm, kv, prev, codes=codes, workspace=workspace, err=err)
     torch.cuda.synchronize()
-    return ms, wall, ops.profile_stop()
+    recs = ops.profile_stop()
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(steps + 1)]
+    ev[0].record()
+    for i in range(steps):
+        ops.dual_ar_decode_step(dm, kv, prev, codes=codes, workspace=workspace, err=err)
+        ev[i + 1].record()
+    torch.cuda.synchronize()
+    per_step = [ev[i].elapsed_time(ev[i + 1]) for i in range(steps)]
+    return ms, wall, recs, per_step
+
+
+def percentiles(v):
+    """p10, median and p90 of a list of per-step times."""
+    a = np.asarray(v, np.float64)
+    return {"p10": float(np.percentile(a, 10)), "p50": float(np.median(a)), "p90": float(np.percentile(a, 90))}
 
 
 def mlp_sweep(torch, ops, inputs, n_sets):
@@ -470,7 +485,7 @@ def main():
     workspace = dm.new_workspace(cfg.batch, kv.c.max_kv_len_hint)
     torch.cuda.synchronize()
     log(f"bench: timing {args.steps} steps after {args.warmup} warm-up steps")
-    ms_step, wall, recs = time_step(torch, ops, dm, kv, prev, args.steps, args.warmup, workspace, err)
+    ms_step, wall, recs, per_step = time_step(torch, ops, dm, kv, prev, args.steps, args.warmup, workspace, err)
     ms_graph = time_step_graph(torch, ops, dm, kv, prev, args.steps, args.warmup, workspace, err)
     log(f"step as a replayed HIP graph: {ms_graph:.3f} ms (eager {ms_step:.3f} ms)")
     if int(err.item()) != 0:
@@ -522,6 +537,7 @@ def main():
         "wall_ms_per_step": wall,
         "ms_per_step_eager": ms_step,
         "ms_per_step_graph": ms_graph,
+        "ms_per_step_dist": percentiles(per_step),
     }
     del dm, kv, workspace, prev
     torch.cuda.empty_cache()

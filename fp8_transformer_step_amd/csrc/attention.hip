@@ -443,14 +443,16 @@ __global__ __launch_bounds__(256) void attn_bal_kernel(AttnArgs a) {
 
 // The MXFP8-cache kernel holds five workgroups per CU only when capped at
 // 102 registers (measured faster: 85 against 90 us at B = 64, kv up to
-// 4096); the bf16 kernel is faster uncapped.
+// 4096); the bf16 kernel is faster uncapped.  The paged balanced MXFP8
+// kernel spills under that cap and is capped at 128 registers instead
+// (97.5 against 105.8 us with 16-position pages).
 template <int D, int G, bool SINGLE, bool PAGED>
 __global__ __launch_bounds__(256, 5) void attn_split_mx_kernel(AttnArgs a) {
     attn_split_body<D, G, SINGLE, true, PAGED>(a);
 }
 
 template <int D, int G, bool PAGED>
-__global__ __launch_bounds__(256, 5) void attn_bal_mx_kernel(AttnArgs a) {
+__global__ __launch_bounds__(256, PAGED ? 4 : 5) void attn_bal_mx_kernel(AttnArgs a) {
     attn_bal_body<D, G, true, PAGED>(a);
 }
 
