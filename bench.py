@@ -320,6 +320,38 @@ def time_step(torch, ops, dm, kv, prev, steps, warmup, workspace, err):
     return ms, wall, recs, per_step
 
 
+def token_selection_timing(torch, ops):
+    """sample_top_k_top_p on the heads' logits (B = 64, V = 4096, the pages'
+    temperature 0.8 / top_p 0.8 / top_k 30, and top_k off) and the window
+    shift (64 x 16 frames x 10 codebooks): us per call over 50 calls."""
+    g = torch.Generator(device="cuda")
+    g.manual_seed(7)
+    logits = torch.randn((64, 4096), generator=g, device="cuda") * 3.0
+    u = torch.rand(64, generator=g, device="cuda")
+    codes = torch.empty(64, dtype=torch.int32, device="cuda")
+    prev = torch.zeros((64, 16, 10), dtype=torch.int32, device="cuda")
+    nxt = torch.ones((64, 10), dtype=torch.int32, device="cuda")
+    out = {}
+    cases = {"sample B=64,V=4096,T=0.8,top_k=30,top_p=0.8":
+             lambda: ops.sample_top_k_top_p(logits, u, 0.8, 30, 0.8, codes=codes),
+             "sample B=64,V=4096,T=1.0,top_k=0,top_p=0.95":
+             lambda: ops.sample_top_k_top_p(logits, u, 1.0, 0, 0.95, codes=codes),
+             "window_shift bs=64,W=16,cw=10": lambda: ops.prev_tokens_shift_inplace(prev, nxt)}
+    for name, fn in cases.items():
+        for _ in range(5):
+            fn()
+        torch.cuda.synchronize()
+        t0, t1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        t0.record()
+        for _ in range(50):
+            fn()
+        t1.record()
+        torch.cuda.synchronize()
+        out[name] = {"us": t0.elapsed_time(t1) / 50 * 1e3}
+        log(f"{name}: {out[name]['us']:.1f} us")
+    return out
+
+
 def percentiles(v):
     """p10, median and p90 of a list of per-step times."""
     a = np.asarray(v, np.float64)
@@ -561,6 +593,7 @@ def main():
                 f"{t * 1e3:.1f} us {gb:.0f} GB/s")
             del w
             torch.cuda.empty_cache()
+        sweep["sampling"] = token_selection_timing(torch, ops)
         result["sweep"] = sweep
 
     if args.copy_calibration:

@@ -23,7 +23,8 @@ DEVICE = ["-x", "hip", "--offload-arch=" + ARCH,
           "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
           "-fno-gpu-rdc"]
 
-SOURCES = ["status.cpp", "profile.cpp", "quantize.hip", "mlp.hip", "attention.hip", "qlinear.hip", "dual_ar.hip"]
+SOURCES = ["status.cpp", "profile.cpp", "quantize.hip", "mlp.hip", "attention.hip", "qlinear.hip", "dual_ar.hip",
+           "sampling.hip"]
 
 
 def _compile(src, verbose):

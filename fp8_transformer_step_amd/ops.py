@@ -275,6 +275,39 @@ def gqa_decode_attn_paged_mxkv(q, k, v, block_table, kv_len, max_kv_len_hint, so
     return out
 
 
+def sample_top_k_top_p(logits, uniforms, temperature=0.8, top_k=30, top_p=0.8, codes=None):
+    """One token per row of fp32 logits [B, V] (unit stride along V) with
+    the caller's uniforms [B] fp32 in [0, 1); returns int32 codes [B]."""
+    _require_cuda(logits, uniforms)
+    if logits.dtype != torch.float32 or logits.dim() != 2 or logits.stride(1) != 1:
+        raise ValueError("logits must be float32 [B, V] with unit stride along V")
+    B, V = logits.shape
+    if uniforms.dtype != torch.float32 or uniforms.shape != (B,) or not uniforms.is_contiguous():
+        raise ValueError("uniforms must be contiguous float32 [B]")
+    if codes is None:
+        codes = torch.empty(B, dtype=torch.int32, device=logits.device)
+    _lib.check(_lib.load().sample_top_k_top_p(
+        logits.data_ptr(), B, V, logits.stride(0), float(temperature), int(top_k), float(top_p),
+        uniforms.data_ptr(), codes.data_ptr(), codes.stride(0), _stream()))
+    return codes
+
+
+def prev_tokens_shift_inplace(prev, next_tokens):
+    """prev int32 [bs, W, cw] <- its frames 1..W-1 then next_tokens int32
+    [bs, cw], in place.  The contract is strict: no dtype conversion, no
+    reshaping or broadcasting (a mismatch raises)."""
+    _require_cuda(prev, next_tokens)
+    if prev.dtype != torch.int32 or next_tokens.dtype != torch.int32:
+        raise TypeError("prev and next_tokens must be int32")
+    if prev.dim() != 3 or next_tokens.dim() != 2 or tuple(next_tokens.shape) != (prev.shape[0], prev.shape[2]):
+        raise ValueError("shapes must be prev [bs, W, cw] and next_tokens [bs, cw]")
+    if not prev.is_contiguous() or not next_tokens.is_contiguous():
+        raise ValueError("prev and next_tokens must be contiguous")
+    bs, W, cw = prev.shape
+    _lib.check(_lib.load().prev_tokens_shift_inplace(prev.data_ptr(), next_tokens.data_ptr(), bs, W, cw, _stream()))
+    return prev
+
+
 def _opt_ptr(t):
     return t.data_ptr() if t is not None else None
 

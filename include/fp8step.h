@@ -351,6 +351,41 @@ FP8S_API int argmax_rows_f32(const float* logits, int64_t B, int64_t N, int64_t 
                     int32_t* codes, int64_t ld_codes, void* stream);
 
 /*
+ * sample_top_k_top_p -- one token per row drawn from fp32 logits with
+ * temperature, top-k and top-p ([KV] section 6: the benchmark generation
+ * samples with temperature 0.8, top_p 0.8, top_k 30 under a fixed seed;
+ * section 7: top_k = 1 is the deterministic configuration).  Per row b:
+ * entries are ranked by (logit descending, index ascending), NaN last and
+ * never drawn; the first min(top_k, V) ranked entries are kept (top_k <= 0
+ * keeps all); masses p_r = exp((l_r - l_0) / temperature); the shortest
+ * ranked prefix of n entries whose mass reaches top_p times the top-k mass
+ * is kept; codes[b * ld_codes] = index of the first ranked entry r < n whose
+ * cumulative mass exceeds uniforms[b] times the mass of the n kept.
+ *   logits   [B, V] fp32, row stride ld_logits >= V; 1 <= V <= 8192.
+ *   uniforms device fp32 [B], the caller's random numbers in [0, 1) (values
+ *            below 0 or NaN act as 0, values >= 1 draw the last kept entry).
+ *   temperature > 0 and finite; 0 < top_p <= 1.
+ *   A row of NaN only gives index 0.  Masses and sums are fp32 (an entry
+ *   whose cumulative-mass boundary lies within fp32 rounding of u or of the
+ *   top-p cut may differ from an exact evaluation by one rank).
+ */
+FP8S_API int sample_top_k_top_p(const float* logits, int64_t B, int64_t V, int64_t ld_logits,
+                    float temperature, int32_t top_k, float top_p,
+                    const float* uniforms, int32_t* codes, int64_t ld_codes, void* stream);
+
+/*
+ * prev_tokens_shift_inplace -- advance the Dual-AR window of previous tokens
+ * by one frame ([TTS] "Continuous Batching for Autoregressive TTS", DualAR
+ * batching constraints: prev int32 [bs, W, cw], next_tokens int32 [bs, cw],
+ * a strict shape and dtype contract): prev[b, w, c] <- prev[b, w + 1, c] for
+ * w < W - 1, then prev[b, W - 1, c] <- next_tokens[b, c].  Both buffers are
+ * contiguous int32 of exactly those shapes; nothing is converted or
+ * broadcast.  Bit-exact.
+ */
+FP8S_API int prev_tokens_shift_inplace(int32_t* prev, const int32_t* next_tokens, int64_t bs, int64_t W,
+                    int64_t cw, void* stream);
+
+/*
  * The full batched Dual-AR decode step ([KV] section 2, [CB], [TTS]).
  *
  * Slow AR: x = embed_sum(E, prev_codes); for each slow layer (pre-norm block)

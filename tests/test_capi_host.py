@@ -128,6 +128,22 @@ def test_attention_paged_argument_checks():
     assert mx(16, 3) == EINVAL                              # fewer than D/32 exponents per row
 
 
+def test_sampling_and_window_argument_checks():
+    lib = _lib.load()
+    f = ctypes.c_float
+    smp = lambda V, ld, T, k, p, lg=FAKE: lib.sample_top_k_top_p(lg, 4, V, ld, f(T), k, f(p), FAKE, FAKE, 1, None)
+    assert smp(8193, 8193, 0.8, 30, 0.8) == EUNSUPPORTED    # above the largest vocabulary
+    assert smp(4096, 4000, 0.8, 30, 0.8) == EINVAL          # row stride below V
+    assert smp(4096, 4096, 0.0, 30, 0.8) == EINVAL          # temperature
+    assert smp(4096, 4096, float("inf"), 30, 0.8) == EINVAL
+    assert smp(4096, 4096, 0.8, 30, 0.0) == EINVAL          # top_p
+    assert smp(4096, 4096, 0.8, 30, 1.5) == EINVAL
+    assert smp(4096, 4096, 0.8, 30, 0.8, lg=None) == EINVAL
+    assert lib.prev_tokens_shift_inplace(None, FAKE, 2, 4, 10, None) == EINVAL
+    assert lib.prev_tokens_shift_inplace(FAKE, FAKE, 2, 0, 10, None) == EINVAL
+    assert lib.prev_tokens_shift_inplace(FAKE, FAKE, 0, 4, 10, None) == EINVAL
+
+
 @pytest.mark.parametrize("M,H,I", [(1, 2560, 9728), (128, 2560, 9728), (1, 256, 1024)])
 def test_mlp_workspace_is_small(M, H, I):
     n = _lib.load().swiglu_mlp_fp8_workspace_size(M, H, I, 0)
