@@ -320,6 +320,32 @@ def time_step(torch, ops, dm, kv, prev, steps, warmup, workspace, err):
     return ms, wall, recs, per_step
 
 
+def bucket_curve(torch, dm, kv, max_b):
+    """The step replayed from one captured graph per batch bucket (the same
+    model and caches, the first B rows): ms per step and tokens/s per
+    bucket, 10 replays each after 2."""
+    from fp8_transformer_step_amd import graphs
+    sg = graphs.StepGraphs(dm, kv, buckets=[b for b in (1, 8, 16, 24, 32, 48, 64) if b <= max_b])
+    out = {}
+    for B in sg.buckets:
+        for _ in range(2):
+            sg.replay(B)
+        torch.cuda.synchronize()
+        t0, t1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        t0.record()
+        for _ in range(10):
+            sg.replay(B)
+        t1.record()
+        torch.cuda.synchronize()
+        ms = t0.elapsed_time(t1) / 10
+        out[f"B={B}"] = {"ms_per_step": ms, "tokens/s": B / (ms * 1e-3)}
+        log(f"graph bucket B={B}: {ms:.3f} ms/step, {B / (ms * 1e-3):.0f} tokens/s")
+    if int(sg.err.item()) != 0:
+        raise SystemExit(f"device error flag {int(sg.err.item())} in the bucket graphs")
+    del sg
+    return out
+
+
 def token_selection_timing(torch, ops):
     """sample_top_k_top_p on the heads' logits (B = 64, V = 4096, the pages'
     temperature 0.8 / top_p 0.8 / top_k 30, and top_k off) and the window
@@ -571,6 +597,8 @@ def main():
         "ms_per_step_graph": ms_graph,
         "ms_per_step_dist": percentiles(per_step),
     }
+    if not args.no_sweep:
+        result["step_buckets"] = bucket_curve(torch, dm, kv, B)
     del dm, kv, workspace, prev
     torch.cuda.empty_cache()
 

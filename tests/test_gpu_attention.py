@@ -132,15 +132,15 @@ def test_gqa_matches_explicit_head_repeat():
     assert max_rel_err(out, ref) <= TOL_BF16_ATTN
 
 
-@pytest.mark.parametrize("hint", [64, 16])
+@pytest.mark.parametrize("hint", [256, 16])
 def test_invalid_kv_len_sets_flag_and_zeroes(hint):
-    """hint 64 splits the prefix and merges; hint 16 is a single chunk whose
-    kernel writes the output itself."""
+    """hint 256 splits the prefix (64-position chunks) and merges; hint 16 is
+    a single chunk whose kernel writes the output itself."""
     need_gpu()
-    B, cap = 3, 64
+    B, cap = 3, 256
     kv = np.array([10, 10, 10], np.int32)
     qb, kb, vb, kc, vc = _make(inputs.W_ATTN, B, 32, 8, 128, cap, kv, extra=41)
-    bad = np.array([10, 0, 65], np.int32)
+    bad = np.array([10, 0, 257], np.int32)
     err = torch.zeros(1, dtype=torch.int32, device="cuda")
     out = _run(qb, kc, vc, bad, hint, err)
     assert int(err.item()) == ops.DEV_KVLEN_RANGE

@@ -1,0 +1,44 @@
+"""The decode step captured once per batch bucket (graphs.StepGraphs): every
+bucket's replay equals the eager step at that batch bit for bit (codes,
+logits of the eager call, caches), a batch between buckets runs on the next
+bucket up and returns its first rows, and replays of different buckets
+interleave without disturbing each other."""
+
+import pytest
+import torch
+
+from fp8_transformer_step_amd import graphs, model, ops
+from _helpers import need_gpu
+
+pytestmark = pytest.mark.gpu
+
+
+def test_bucket_replays_match_eager_steps():
+    need_gpu()
+    host = model.HostModel(model.scaled(model.TINY, batch=24, n_heads=8))
+    c = host.cfg
+    dm = model.device_model(host)
+    kv, ks, vs = model.device_kv(host)
+    prev_all = torch.from_numpy(host.prev_codes).cuda()
+    sg = graphs.StepGraphs(dm, kv, buckets=(1, 3, 8, 24, 64))
+    assert sg.buckets == [1, 3, 8, 24]                 # 64 is above the KV state's rows
+    eager = {}
+    for B in sg.buckets:
+        ws = dm.new_workspace(B, kv.c.max_kv_len_hint)
+        err = torch.zeros(1, dtype=torch.int32, device="cuda")
+        eager[B] = ops.dual_ar_decode_step(dm, kv, prev_all[:B].contiguous(), workspace=ws, err=err).clone()
+        torch.cuda.synchronize()
+        assert int(err.item()) == 0
+    k_ref = [k.view(torch.int16).clone() for k in ks]
+    for rep in range(2):
+        for b in (1, 2, 3, 5, 8, 17, 24):
+            B = sg.bucket_for(b)
+            sg.graphs[B]["prev"].copy_(prev_all[:B])       # the bucket's full input, as in the eager run
+            out = sg.step(prev_all[:b]).clone()
+            torch.cuda.synchronize()
+            assert torch.equal(out, eager[B][:b]), (rep, b, B)
+    assert int(sg.err.item()) == 0
+    for s in range(c.kv_sets):                          # replays rewrite the same cache slots
+        assert torch.equal(ks[s].view(torch.int16), k_ref[s])
+    with pytest.raises(ValueError):
+        sg.bucket_for(25)
