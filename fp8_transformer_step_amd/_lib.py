@@ -65,6 +65,11 @@ SIGNATURES = {
     "gqa_decode_attn_paged_mxkv": (ctypes.c_int, [c_vp, c_vp, c_vp, c_vp, c_vp, c_i64, c_i64, c_i64, c_i64, c_i64,
                                                   c_i64, c_i64, c_i32, c_vp, c_i64, c_i64, c_vp, c_i64, c_i32, c_i32,
                                                   c_i32, c_i64, ctypes.c_float, c_vp, c_vp, c_sz, c_vp, c_vp]),
+    "fp8_gemm_mx": (ctypes.c_int, [c_vp, c_i64, c_vp, c_i64, c_i64, c_vp, c_i64, c_vp, c_i64, c_i64, c_i64, c_i64,
+                                   c_i64, c_vp, c_i64, c_vp]),
+    "fp8_mx_packed_bytes": (c_sz, [c_i64, c_i64]),
+    "fp8_pack_mx": (ctypes.c_int, [c_vp, c_i64, c_vp, c_i64, c_i64, c_i64, c_i64, c_vp, c_sz, c_vp]),
+    "fp8_gemm_mx_packed": (ctypes.c_int, [c_vp, c_vp, c_i64, c_i64, c_i64, c_vp, c_i64, c_vp]),
     "sample_top_k_top_p": (ctypes.c_int, [c_vp, c_i64, c_i64, c_i64, ctypes.c_float, c_i32, ctypes.c_float, c_vp,
                                           c_vp, c_i64, c_vp]),
     "prev_tokens_shift_inplace": (ctypes.c_int, [c_vp, c_vp, c_i64, c_i64, c_i64, c_vp]),

@@ -1,0 +1,346 @@
+// fp8_gemm_mx: C = dequant(A) . dequant(B)^T for large M (prefill / extend),
+// both operands e4m3 with one OCP UE8M0 exponent per 32 consecutive K.
+//
+// What it computes follows the page "How We Made Our Text-to-Speech API
+// Free", sections "FP8 Quantization Strategy" (the mxfp8 path: 1x32 groups
+// with OCP UE8M0 shared exponents, scales read with K-major strides) and
+// "Kernel Benchmark Results" (the MXFP8 GEMM on square shapes from 1024^3 to
+// 16384^3 and the MLP at M up to 4096): fp32 accumulation of
+// sum_k (qa[m,k] 2^(Ea[m,k/32]-127)) (qb[n,k] 2^(Eb[n,k/32]-127)), rounded
+// once to bf16.
+//
+// MI355X design: the product is MFMA-bound at these sizes.
+//   * Workgroup tile 128 x 128 (four waves, 2 x 2, of 64 x 64 = 4 x 4
+//     16x16x128 scaled MFMAs per K block of 128); the UE8M0 exponents go
+//     straight into the MFMA's scale operands, so the inner loop is LDS
+//     reads and MFMAs only.
+//   * A and B fragments (16 rows x 128 K = 2 KiB each, 16 per K block) go
+//     global -> registers -> LDS in the MFMA operand order, double-buffered:
+//     the loads of K block kb+2 are issued right after block kb+1 is
+//     written to LDS and stay in flight while block kb+1 is multiplied.
+//     The barrier is the plain s_barrier after an LDS-only wait (a fenced
+//     barrier would also drain those loads).  Direct global->LDS loads were
+//     not used: the compiler drains every such load before the first LDS
+//     read that follows, which serialises the stages.
+//   * Tiles are dealt to the 8 XCDs in contiguous runs, and within a run
+//     walked in groups of 8 tile rows, so each XCD's L2 holds the A rows and
+//     B columns its tiles share.
+#include <algorithm>
+
+#include "common.h"
+#include "gemm_tiles.h"
+#include "host_common.h"
+#include "internal.h"
+#include "profile.h"
+
+namespace fp8s {
+
+constexpr int kGlBM = 128, kGlBN = 128;
+constexpr int kGlStage = 16 * kFrag;          // 8 A + 8 B fragments
+constexpr int kGlGroupM = 8;
+
+struct GemmLargeArgs {
+    const uint8_t* a; int64_t lda;
+    const uint8_t* ae; int64_t ae_r, ae_g;
+    const uint8_t* b; int64_t ldb;
+    const uint8_t* be; int64_t be_r, be_g;
+    int M, N, KB;                             // KB = K / 128
+    int tiles_m, tiles_n;
+    uint16_t* c; int64_t ldc;
+};
+
+// One lane's 32 operand bytes: 16 at p and 16 at p + hi (a row-major row:
+// p = row start + K block + 16 * lane group, hi = 64; a packed fragment:
+// p = fragment + 16 * lane, hi = 1024).
+__device__ __forceinline__ v8i ld_row32(const uint8_t* p, int hi_off) {
+    const uint4 lo = *reinterpret_cast<const uint4*>(p);
+    const uint4 hi = *reinterpret_cast<const uint4*>(p + hi_off);
+    v8i r;
+    r[0] = lo.x; r[1] = lo.y; r[2] = lo.z; r[3] = lo.w;
+    r[4] = hi.x; r[5] = hi.y; r[6] = hi.z; r[7] = hi.w;
+    return r;
+}
+// ... stored as that lane's part of an LDS fragment read back by lds_frag.
+__device__ __forceinline__ void st_frag(uint8_t* frag, const v8i& r, int lane) {
+    *reinterpret_cast<uint4*>(frag + lane * 16) = make_uint4(r[0], r[1], r[2], r[3]);
+    *reinterpret_cast<uint4*>(frag + 1024 + lane * 16) = make_uint4(r[4], r[5], r[6], r[7]);
+}
+
+// PACKED: A and B come in the packed operand layout of fp8_pack_mx
+// (fragments and exponents in MFMA lane order, so every load is one
+// contiguous KiB and each lane's four exponents of an operand are one dword).
+template <bool PACKED>
+__global__ __launch_bounds__(256, 2) void gemm_large_mx_kernel(GemmLargeArgs a) {
+    __shared__ __attribute__((aligned(1024))) uint8_t smem[2 * kGlStage];
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const int wm = wave >> 1, wn = wave & 1;
+
+    // tile order: contiguous runs per XCD, grouped rows inside a run
+    const int n_tiles = a.tiles_m * a.tiles_n;
+    int t = blockIdx.x;
+    if (n_tiles % 8 == 0) t = (t % 8) * (n_tiles / 8) + t / 8;
+    const int per_group = kGlGroupM * a.tiles_n;
+    const int grp = t / per_group, first_m = grp * kGlGroupM;
+    const int gm = min(a.tiles_m - first_m, kGlGroupM);
+    const int tm = first_m + (t % per_group) % gm, tn = (t % per_group) / gm;
+    const int m0 = tm * kGlBM, n0 = tn * kGlBN;
+    const int g4 = lane >> 4;
+
+    // The 4 fragments this wave moves per K block: A rows m0 + 16w and
+    // m0 + 16(w + 4), B rows n0 + 16w and n0 + 16(w + 4) (w = wave, slots w,
+    // w + 4, 8 + w, 12 + w of the stage); its lane reads 16 bytes at K = 16g
+    // and 16 at K = 64 + 16g of one row (rows past M repeat row M - 1).
+    const int rl = lane & 15;
+    const uint8_t *pa0, *pa1, *pb0, *pb1;
+    if (PACKED) {                              // fragment (16-row block, kb) at (block * KB + kb) * 2 KiB
+        pa0 = a.a + (int64_t)((m0 / 16 + wave) * a.KB) * kFrag + lane * 16;
+        pa1 = a.a + (int64_t)((m0 / 16 + wave + 4) * a.KB) * kFrag + lane * 16;
+        pb0 = a.b + (int64_t)((n0 / 16 + wave) * a.KB) * kFrag + lane * 16;
+        pb1 = a.b + (int64_t)((n0 / 16 + wave + 4) * a.KB) * kFrag + lane * 16;
+    } else {
+        pa0 = a.a + (int64_t)min(m0 + 16 * wave + rl, a.M - 1) * a.lda + 16 * g4;
+        pa1 = a.a + (int64_t)min(m0 + 16 * (wave + 4) + rl, a.M - 1) * a.lda + 16 * g4;
+        pb0 = a.b + (int64_t)(n0 + 16 * wave + rl) * a.ldb + 16 * g4;
+        pb1 = a.b + (int64_t)(n0 + 16 * (wave + 4) + rl) * a.ldb + 16 * g4;
+    }
+    constexpr int kStep = PACKED ? kFrag : 128;       // bytes per K block
+    constexpr int kHi = PACKED ? 1024 : 64;           // offset of the lane's second 16 bytes
+    v8i ga0, ga1, gb0, gb1;
+    auto gload = [&](int kb) {
+        const int ko = kb * kStep;
+        ga0 = ld_row32(pa0 + ko, kHi); ga1 = ld_row32(pa1 + ko, kHi);
+        gb0 = ld_row32(pb0 + ko, kHi); gb1 = ld_row32(pb1 + ko, kHi);
+    };
+    auto swrite = [&](uint8_t* s) {
+        st_frag(s + wave * kFrag, ga0, lane);
+        st_frag(s + (wave + 4) * kFrag, ga1, lane);
+        st_frag(s + (8 + wave) * kFrag, gb0, lane);
+        st_frag(s + (12 + wave) * kFrag, gb1, lane);
+    };
+    // exponents of this lane's 4 A rows (e[0..3]) and 4 B rows (e[4..7]):
+    // 32-bit row offsets fixed here, one add per load in the loop (the host
+    // keeps every exponent offset below 2^31)
+    const int ra = m0 + 64 * wm + rl, rb = n0 + 64 * wn + rl;
+    uint32_t offa[4], offb[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        offa[i] = (uint32_t)min(ra + 16 * i, a.M - 1) * (uint32_t)a.ae_r;
+        offb[i] = (uint32_t)(rb + 16 * i) * (uint32_t)a.be_r;
+    }
+    const uint32_t aeg = (uint32_t)a.ae_g, beg = (uint32_t)a.be_g;
+    // packed: the four exponents of a 64-row group are one dword per lane at
+    // ((group * KB + kb) * 64 + lane) * 4
+    const uint32_t* pea = reinterpret_cast<const uint32_t*>(a.ae) + (uint32_t)((m0 / 64 + wm) * a.KB) * 64 + lane;
+    const uint32_t* peb = reinterpret_cast<const uint32_t*>(a.be) + (uint32_t)((n0 / 64 + wn) * a.KB) * 64 + lane;
+    auto exps = [&](int kb) {
+        v8i e;
+        if (PACKED) {
+            const uint32_t wa = pea[kb * 64], wb = peb[kb * 64];
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                e[i] = (wa >> (8 * i)) & 0xFF;
+                e[4 + i] = (wb >> (8 * i)) & 0xFF;
+            }
+            return e;
+        }
+        const uint32_t g = (uint32_t)(kb * 4 + g4);
+        const uint32_t ga = g * aeg, gb = g * beg;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            e[i] = a.ae[offa[i] + ga];
+            e[4 + i] = a.be[offb[i] + gb];
+        }
+        return e;
+    };
+    v4f acc[4][4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int j = 0; j < 4; ++j) acc[i][j] = v4f{0, 0, 0, 0};
+    auto compute = [&](const uint8_t* s, const v8i& e) {
+        v8i af[4];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) af[i] = lds_frag(s, (4 * wm + i) * kFrag, lane);
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            const v8i bf = lds_frag(s, (8 + 4 * wn + j) * kFrag, lane);
+#pragma unroll
+            for (int i = 0; i < 4; ++i) acc[i][j] = mfma_fp8(af[i], bf, acc[i][j], e[i], e[4 + j]);
+        }
+    };
+    // LDS writes of this wave complete, then every wave meets: the stage just
+    // written is readable and the one just read may be overwritten.  The
+    // barrier carries no fence (a fence would also wait for the global loads
+    // of the next K block); the empty asm statements keep the compiler from
+    // moving memory accesses across it.
+    auto lds_sync = [] {
+        __builtin_amdgcn_s_waitcnt(0xC07F);   // lgkmcnt(0); vmcnt and expcnt untouched
+        asm volatile("" ::: "memory");
+        __builtin_amdgcn_s_barrier();
+        asm volatile("" ::: "memory");
+    };
+
+    const int KB = a.KB;
+    gload(0);
+    v8i e_cur = exps(0), e_next = e_cur;
+    swrite(smem);
+    if (KB > 1) {
+        gload(1);
+        e_next = exps(1);
+    }
+    lds_sync();
+    for (int kb = 0; kb < KB; ++kb) {
+        uint8_t* cur = smem + (kb & 1) * kGlStage;
+        uint8_t* nxt = smem + ((kb + 1) & 1) * kGlStage;
+        compute(cur, e_cur);
+        if (kb + 1 < KB) {
+            swrite(nxt);                       // block kb + 1, loaded during block kb
+            e_cur = e_next;
+            if (kb + 2 < KB) {
+                gload(kb + 2);
+                e_next = exps(kb + 2);
+            }
+        }
+        lds_sync();
+    }
+
+    // lane holds D[4 * (lane / 16) + r][lane % 16] of every 16 x 16 tile
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
+#pragma unroll
+            for (int q = 0; q < 4; ++q) {
+                const int row = m0 + 64 * wm + 16 * i + 4 * g4 + q;
+                const int col = n0 + 64 * wn + 16 * j + (lane & 15);
+                if (row < a.M) a.c[(int64_t)row * a.ldc + col] = (uint16_t)f32_to_bf16(acc[i][j][q]);
+            }
+}
+
+// fp8_pack_mx: an MXFP8 matrix [R, K] (codes row-major, exponents strided)
+// in the packed operand layout: R padded to a multiple of 128 (padding rows:
+// code 0, exponent 127); fragment (16-row block rb, K block kb) = 2 KiB at
+// (rb * KB + kb) * 2048, lane l = r + 16 g holding bytes K = 16g .. 16g+15 of
+// row 16 rb + r at l * 16 and K = 64 + 16g .. at 1024 + l * 16; then the
+// exponents, 256 bytes per (64-row group G, kb) at R_pad * K + (G * KB + kb)
+// * 256, lane l's dword holding (row 64 G + 16 i + r, group 4 kb + g) in
+// byte i.  One thread per 16 packed bytes of fragments, then per dword of
+// exponents.
+struct PackArgs {
+    const uint8_t* q; int64_t ldq;
+    const uint8_t* e; int64_t er, eg;
+    int R, KB, Rp;
+    uint8_t* out;
+};
+
+__global__ __launch_bounds__(256) void pack_mx_kernel(PackArgs a) {
+    const int64_t n_chunks = (int64_t)(a.Rp / 16) * a.KB * 128;   // 16-byte chunks: 128 per 2 KiB fragment
+    const int64_t n_words = (int64_t)(a.Rp / 64) * a.KB * 64;
+    const int64_t t = (int64_t)blockIdx.x * 256 + threadIdx.x;
+    if (t < n_chunks) {
+        const int64_t frag = t / 128;
+        const int c = (int)(t % 128), half = c / 64, l = c % 64;
+        const int rb = (int)(frag / a.KB), kb = (int)(frag % a.KB);
+        const int row = 16 * rb + (l & 15);
+        uint4 v = make_uint4(0, 0, 0, 0);
+        if (row < a.R)
+            v = *reinterpret_cast<const uint4*>(a.q + (int64_t)row * a.ldq + kb * 128 + 64 * half + 16 * (l >> 4));
+        *reinterpret_cast<uint4*>(a.out + frag * kFrag + half * 1024 + l * 16) = v;
+    } else if (t < n_chunks + n_words) {
+        const int64_t w = t - n_chunks;
+        const int l = (int)(w % 64);
+        const int64_t gk = w / 64;
+        const int G = (int)(gk / a.KB), kb = (int)(gk % a.KB);
+        uint32_t word = 0;
+        for (int i = 0; i < 4; ++i) {
+            const int row = 64 * G + 16 * i + (l & 15);
+            const uint32_t E = row < a.R ? a.e[(int64_t)row * a.er + (int64_t)(4 * kb + (l >> 4)) * a.eg] : 127u;
+            word |= E << (8 * i);
+        }
+        reinterpret_cast<uint32_t*>(a.out + (int64_t)a.Rp * a.KB * 128)[w] = word;
+    }
+}
+
+}  // namespace fp8s
+
+using namespace fp8s;
+
+extern "C" size_t fp8_mx_packed_bytes(int64_t R, int64_t K) {
+    if (R < 1 || K < 128 || K % 128 || R >= (1ll << 30) || K >= (1ll << 30)) return 0;
+    const int64_t Rp = (R + 127) / 128 * 128;
+    return (size_t)(Rp * K + Rp * (K / 32));
+}
+
+extern "C" int fp8_pack_mx(const uint8_t* q, int64_t ldq, const uint8_t* e, int64_t e_row, int64_t e_grp, int64_t R,
+                           int64_t K, void* packed, size_t packed_bytes, void* stream) {
+    clear_error();
+    FP8S_REQUIRE(q && e && packed, FP8S_EINVAL, "fp8_pack_mx: null pointer");
+    FP8S_REQUIRE(R >= 1 && K >= 128 && K % 128 == 0 && R < (1ll << 30) && K < (1ll << 30), FP8S_EINVAL,
+                 "fp8_pack_mx: need R >= 1 and K a positive multiple of 128");
+    FP8S_REQUIRE(ldq >= K && ldq % 16 == 0 && aligned16(q) && aligned16(packed), FP8S_EINVAL,
+                 "fp8_pack_mx: codes and output must be 16-byte aligned with ldq >= K, ldq % 16 == 0");
+    FP8S_REQUIRE(e_row >= 0 && e_grp >= 0, FP8S_EINVAL, "fp8_pack_mx: exponent strides must be non-negative");
+    FP8S_REQUIRE(packed_bytes >= fp8_mx_packed_bytes(R, K), FP8S_EWORKSPACE, "fp8_pack_mx: output %zu < %zu bytes",
+                 packed_bytes, fp8_mx_packed_bytes(R, K));
+    PackArgs p;
+    p.q = q; p.ldq = ldq; p.e = e; p.er = e_row; p.eg = e_grp;
+    p.R = (int)R; p.KB = (int)(K / 128); p.Rp = (int)((R + 127) / 128 * 128);
+    p.out = static_cast<uint8_t*>(packed);
+    const int64_t n = (int64_t)(p.Rp / 16) * p.KB * 128 + (int64_t)(p.Rp / 64) * p.KB * 64;
+    FP8S_REQUIRE((n + 255) / 256 < (1ll << 31), FP8S_EUNSUPPORTED, "fp8_pack_mx: too large");
+    FP8S_LAUNCH("pack_mx", pack_mx_kernel, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, as_stream(stream), p);
+    return check_launch("fp8_pack_mx");
+}
+
+extern "C" int fp8_gemm_mx_packed(const void* a_packed, const void* b_packed, int64_t M, int64_t N, int64_t K,
+                                  uint16_t* c, int64_t ldc, void* stream) {
+    clear_error();
+    FP8S_REQUIRE(a_packed && b_packed && c, FP8S_EINVAL, "fp8_gemm_mx_packed: null pointer");
+    FP8S_REQUIRE(M >= 1 && N >= 1 && K >= 128, FP8S_EINVAL, "fp8_gemm_mx_packed: sizes must be positive");
+    FP8S_REQUIRE(N % 128 == 0 && K % 128 == 0 && M < (1ll << 30) && N < (1ll << 30) && K < (1ll << 30),
+                 FP8S_EUNSUPPORTED, "fp8_gemm_mx_packed: N and K must be multiples of 128");
+    FP8S_REQUIRE(ldc >= N && ldc % 8 == 0 && aligned16(a_packed) && aligned16(b_packed) && aligned16(c), FP8S_EINVAL,
+                 "fp8_gemm_mx_packed: C must be 16-byte aligned with ldc >= N, ldc % 8 == 0; packed operands 16-byte aligned");
+    const int64_t Mp = (M + 127) / 128 * 128, tiles_m = Mp / kGlBM, tiles_n = N / kGlBN;
+    FP8S_REQUIRE(tiles_m * tiles_n < (1ll << 31), FP8S_EUNSUPPORTED, "fp8_gemm_mx_packed: too many tiles");
+    GemmLargeArgs g;
+    g.a = static_cast<const uint8_t*>(a_packed); g.lda = 0;
+    g.ae = g.a + Mp * K; g.ae_r = g.ae_g = 0;
+    g.b = static_cast<const uint8_t*>(b_packed); g.ldb = 0;
+    g.be = g.b + N * K; g.be_r = g.be_g = 0;
+    g.M = (int)M; g.N = (int)N; g.KB = (int)(K / 128);
+    g.tiles_m = (int)tiles_m; g.tiles_n = (int)tiles_n;
+    g.c = c; g.ldc = ldc;
+    FP8S_LAUNCH("gemm_large_mx", gemm_large_mx_kernel<true>, dim3((unsigned)(tiles_m * tiles_n)), dim3(256), 0,
+                as_stream(stream), g);
+    return check_launch("fp8_gemm_mx_packed");
+}
+
+extern "C" int fp8_gemm_mx(const uint8_t* a, int64_t lda, const uint8_t* a_e, int64_t ae_row, int64_t ae_grp,
+                           const uint8_t* b, int64_t ldb, const uint8_t* b_e, int64_t be_row, int64_t be_grp,
+                           int64_t M, int64_t N, int64_t K, uint16_t* c, int64_t ldc, void* stream) {
+    clear_error();
+    FP8S_REQUIRE(a && a_e && b && b_e && c, FP8S_EINVAL, "fp8_gemm_mx: null pointer");
+    FP8S_REQUIRE(M >= 1 && N >= 1 && K >= 1, FP8S_EINVAL, "fp8_gemm_mx: sizes must be positive");
+    FP8S_REQUIRE(N % 128 == 0 && K % 128 == 0, FP8S_EUNSUPPORTED, "fp8_gemm_mx: N and K must be multiples of 128");
+    FP8S_REQUIRE(M < (1ll << 30) && N < (1ll << 30) && K < (1ll << 30), FP8S_EUNSUPPORTED, "fp8_gemm_mx: too large");
+    FP8S_REQUIRE(lda >= K && ldb >= K && lda % 16 == 0 && ldb % 16 == 0 && ldc >= N && ldc % 8 == 0, FP8S_EINVAL,
+                 "fp8_gemm_mx: leading dimensions must cover the rows and keep them 16-byte aligned");
+    FP8S_REQUIRE(aligned16(a) && aligned16(b) && aligned16(c), FP8S_EINVAL, "fp8_gemm_mx: A, B and C must be 16-byte aligned");
+    FP8S_REQUIRE(ae_row >= 0 && ae_grp >= 0 && be_row >= 0 && be_grp >= 0, FP8S_EINVAL,
+                 "fp8_gemm_mx: exponent strides must be non-negative");
+    FP8S_REQUIRE((M - 1) * ae_row + (K / 32 - 1) * ae_grp < (1ll << 31) &&
+                     (N - 1) * be_row + (K / 32 - 1) * be_grp < (1ll << 31),
+                 FP8S_EUNSUPPORTED, "fp8_gemm_mx: exponent matrices must span less than 2^31 bytes");
+    const int64_t tiles_m = (M + kGlBM - 1) / kGlBM, tiles_n = N / kGlBN;
+    FP8S_REQUIRE(tiles_m * tiles_n < (1ll << 31), FP8S_EUNSUPPORTED, "fp8_gemm_mx: too many tiles");
+    GemmLargeArgs g;
+    g.a = a; g.lda = lda; g.ae = a_e; g.ae_r = ae_row; g.ae_g = ae_grp;
+    g.b = b; g.ldb = ldb; g.be = b_e; g.be_r = be_row; g.be_g = be_grp;
+    g.M = (int)M; g.N = (int)N; g.KB = (int)(K / 128);
+    g.tiles_m = (int)tiles_m; g.tiles_n = (int)tiles_n;
+    g.c = c; g.ldc = ldc;
+    FP8S_LAUNCH("gemm_large_mx", gemm_large_mx_kernel<false>, dim3((unsigned)(tiles_m * tiles_n)), dim3(256), 0,
+                as_stream(stream), g);
+    return check_launch("fp8_gemm_mx");
+}

@@ -275,6 +275,65 @@ def gqa_decode_attn_paged_mxkv(q, k, v, block_table, kv_len, max_kv_len_hint, so
     return out
 
 
+def fp8_gemm_mx(qa, ea, qb, eb, c=None):
+    """C bf16 [M, N] = dequant(qa, ea) . dequant(qb, eb)^T for MXFP8
+    operands: qa uint8 [M, K], ea uint8 [M, K/32] (any strides), qb uint8
+    [N, K], eb uint8 [N, K/32]."""
+    _require_cuda(qa, ea, qb, eb)
+    for t in (qa, ea, qb, eb):
+        if t.dtype != torch.uint8 or t.dim() != 2:
+            raise TypeError("operands and exponents must be 2-D uint8")
+    M, K = qa.shape
+    N = qb.shape[0]
+    if qb.shape[1] != K or tuple(ea.shape) != (M, K // 32) or tuple(eb.shape) != (N, K // 32):
+        raise ValueError("shapes must be qa [M, K], ea [M, K/32], qb [N, K], eb [N, K/32]")
+    if qa.stride(1) != 1 or qb.stride(1) != 1:
+        raise ValueError("operand rows must be contiguous")
+    if c is None:
+        c = torch.empty((M, N), dtype=torch.bfloat16, device=qa.device)
+    _lib.check(_lib.load().fp8_gemm_mx(
+        qa.data_ptr(), qa.stride(0), ea.data_ptr(), ea.stride(0), ea.stride(1),
+        qb.data_ptr(), qb.stride(0), eb.data_ptr(), eb.stride(0), eb.stride(1),
+        M, N, K, _bits(c), c.stride(0), _stream()))
+    return c
+
+
+@dataclass
+class PackedMx:
+    """An MXFP8 operand [rows, K] in the packed layout of fp8_pack_mx."""
+    data: torch.Tensor
+    rows: int
+    K: int
+
+
+def fp8_pack_mx(q, e):
+    """Pack codes q uint8 [R, K] and exponents e uint8 [R, K/32] (any
+    strides) for fp8_gemm_mx_packed."""
+    _require_cuda(q, e)
+    R, K = q.shape
+    if q.dtype != torch.uint8 or e.dtype != torch.uint8 or tuple(e.shape) != (R, K // 32) or q.stride(1) != 1:
+        raise ValueError("need q uint8 [R, K] with contiguous rows and e uint8 [R, K/32]")
+    n = int(_lib.load().fp8_mx_packed_bytes(R, K))
+    if n == 0:
+        raise ValueError("K must be a positive multiple of 128")
+    out = torch.empty(n, dtype=torch.uint8, device=q.device)
+    _lib.check(_lib.load().fp8_pack_mx(q.data_ptr(), q.stride(0), e.data_ptr(), e.stride(0), e.stride(1), R, K,
+                                       out.data_ptr(), n, _stream()))
+    return PackedMx(out, R, K)
+
+
+def fp8_gemm_mx_packed(pa, pb, c=None):
+    """C bf16 [M, N] = dequant(A) . dequant(B)^T from packed operands."""
+    if pa.K != pb.K:
+        raise ValueError("operands must share K")
+    M, N, K = pa.rows, pb.rows, pa.K
+    if c is None:
+        c = torch.empty((M, N), dtype=torch.bfloat16, device=pa.data.device)
+    _lib.check(_lib.load().fp8_gemm_mx_packed(pa.data.data_ptr(), pb.data.data_ptr(), M, N, K, _bits(c),
+                                              c.stride(0), _stream()))
+    return c
+
+
 def sample_top_k_top_p(logits, uniforms, temperature=0.8, top_k=30, top_p=0.8, codes=None):
     """One token per row of fp32 logits [B, V] (unit stride along V) with
     the caller's uniforms [B] fp32 in [0, 1); returns int32 codes [B]."""

@@ -351,6 +351,53 @@ FP8S_API int argmax_rows_f32(const float* logits, int64_t B, int64_t N, int64_t 
                     int32_t* codes, int64_t ld_codes, void* stream);
 
 /*
+ * fp8_gemm_mx -- C = dequant(A) . dequant(B)^T for prefill / extend shapes
+ * (large M), both operands MXFP8: e4m3 codes with one OCP UE8M0 exponent per
+ * 32 consecutive K ([TTS] "FP8 Quantization Strategy", the mxfp8 path;
+ * "Kernel Benchmark Results", the MXFP8 GEMM on square shapes 1024^3 ..
+ * 16384^3 and the MLP at M up to 4096):
+ *   C[m, n] = bf16( sum_k qa[m,k] 2^(Ea[m,k/32]-127) * qb[n,k] 2^(Eb[n,k/32]-127) )
+ * accumulated in fp32.
+ *   a        e4m3 [M, K], row stride lda (multiple of 16, >= K).
+ *   a_e      UE8M0 [M, K/32]: exponent (m, g) at m * ae_row + g * ae_grp
+ *            (qlinear_quantize mode 2 writes either layout; K-major is
+ *            ae_row = 1, ae_grp = M).
+ *   b, b_e   the same for B [N, K] (a weight quantised as mode 2).
+ *   c        bf16 [M, N], row stride ldc (multiple of 8, >= N).
+ *   M >= 1 (any); N and K multiples of 128.  No workspace; nothing is
+ *   allocated.  Accuracy: fp32 accumulation, one bf16 rounding;
+ *   max|C - oracle| <= 2e-2 * max|oracle| (exact when every partial sum is).
+ */
+FP8S_API int fp8_gemm_mx(const uint8_t* a, int64_t lda, const uint8_t* a_e, int64_t ae_row, int64_t ae_grp,
+                    const uint8_t* b, int64_t ldb, const uint8_t* b_e, int64_t be_row, int64_t be_grp,
+                    int64_t M, int64_t N, int64_t K, uint16_t* c, int64_t ldc, void* stream);
+
+/*
+ * fp8_pack_mx / fp8_gemm_mx_packed -- the same product with both operands in
+ * a packed layout that makes every operand load of the GEMM one contiguous
+ * KiB (the row-major layout reads 64 bytes from each of 16 rows per load).
+ * Pack a weight once at load time and an activation once per product.
+ *   fp8_mx_packed_bytes(R, K): bytes of a packed [R, K] operand (0 if K is
+ *   not a positive multiple of 128).
+ *   fp8_pack_mx: q e4m3 [R, K] (row stride ldq, multiple of 16) and its
+ *   UE8M0 exponents (strides e_row, e_grp, as fp8_gemm_mx) -> packed:
+ *     R_pad = R rounded up to 128; fragment (16-row block rb, K block kb) is
+ *     2 KiB at (rb * K/128 + kb) * 2048: lane l = r + 16 g holds bytes
+ *     K = 16g .. 16g+15 of row 16 rb + r at l * 16 and K = 64 + 16g .. at
+ *     1024 + l * 16; padding rows are code 0.  Then the exponents: 256
+ *     bytes per (64-row group G, kb) at R_pad * K + (G * K/128 + kb) * 256,
+ *     byte i of lane l's dword = exponent (row 64 G + 16 i + r, group
+ *     4 kb + g), 127 for padding rows.
+ *   fp8_gemm_mx_packed: C [M, N] bf16 from packed A (R = M) and packed B
+ *   (R = N, N a multiple of 128); same result as fp8_gemm_mx, bit for bit.
+ */
+FP8S_API size_t fp8_mx_packed_bytes(int64_t R, int64_t K);
+FP8S_API int fp8_pack_mx(const uint8_t* q, int64_t ldq, const uint8_t* e, int64_t e_row, int64_t e_grp,
+                    int64_t R, int64_t K, void* packed, size_t packed_bytes, void* stream);
+FP8S_API int fp8_gemm_mx_packed(const void* a_packed, const void* b_packed, int64_t M, int64_t N, int64_t K,
+                    uint16_t* c, int64_t ldc, void* stream);
+
+/*
  * sample_top_k_top_p -- one token per row drawn from fp32 logits with
  * temperature, top-k and top-p ([KV] section 6: the benchmark generation
  * samples with temperature 0.8, top_p 0.8, top_k 30 under a fixed seed;
