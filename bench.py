@@ -346,6 +346,54 @@ def bucket_curve(torch, dm, kv, max_b):
     return out
 
 
+PEAK_FP8_TFLOPS = 5000.0                # dense FP8 MFMA peak of the chip
+
+
+def prefill_gemm_sweep(torch, ops):
+    """fp8_gemm_mx_packed (and the row-major fp8_gemm_mx) on the pages'
+    square shapes and on the MLP's prefill shapes at M = 4096, operands
+    quantised from seeded bf16 and packed outside the timed loop (packing
+    the activation is timed on its own): TFLOP/s and fraction of the dense
+    FP8 peak."""
+    g = torch.Generator(device="cuda")
+    g.manual_seed(11)
+    out = {}
+    for M, N, K in ((1024, 1024, 1024), (4096, 4096, 4096), (8192, 8192, 8192), (16384, 16384, 16384),
+                    (4096, 19456, 2560), (4096, 2560, 9728)):
+        a = torch.randn((M, K), generator=g, device="cuda").to(torch.bfloat16)
+        b = (torch.randn((N, K), generator=g, device="cuda") * 0.02).to(torch.bfloat16)
+        qa, ea = ops.qlinear_quantize(a, ops.Q_MX_1x32)
+        qb, eb = ops.qlinear_quantize(b, ops.Q_MX_1x32)
+        del a, b
+        pa, pb = ops.fp8_pack_mx(qa, ea), ops.fp8_pack_mx(qb, eb)
+        c = torch.empty((M, N), dtype=torch.bfloat16, device="cuda")
+        n = max(3, min(30, int(2e12 / (2 * M * N * K))))
+        res = {}
+        for name, fn in (("packed", lambda: ops.fp8_gemm_mx_packed(pa, pb, c)),
+                         ("row_major", lambda: ops.fp8_gemm_mx(qa, ea, qb, eb, c)),
+                         ("pack_activation", lambda: ops.fp8_pack_mx(qa, ea))):
+            for _ in range(2):
+                fn()
+            torch.cuda.synchronize()
+            t0, t1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            t0.record()
+            for _ in range(n):
+                fn()
+            t1.record()
+            torch.cuda.synchronize()
+            us = t0.elapsed_time(t1) / n * 1e3
+            res[name] = {"us": us}
+            if name != "pack_activation":
+                tf = 2 * M * N * K / (us * 1e-6) / 1e12
+                res[name].update({"TFLOP/s": tf, "frac": tf / PEAK_FP8_TFLOPS})
+        out[f"{M}x{N}x{K}"] = res
+        log(f"gemm mx {M}x{N}x{K}: packed {res['packed']['us']:.1f} us {res['packed']['TFLOP/s']:.0f} TFLOP/s, "
+            f"row-major {res['row_major']['TFLOP/s']:.0f}, pack A {res['pack_activation']['us']:.1f} us")
+        del qa, ea, qb, eb, pa, pb, c
+        torch.cuda.empty_cache()
+    return out
+
+
 def token_selection_timing(torch, ops):
     """sample_top_k_top_p on the heads' logits (B = 64, V = 4096, the pages'
     temperature 0.8 / top_p 0.8 / top_k 30, and top_k off) and the window
@@ -622,6 +670,7 @@ def main():
             del w
             torch.cuda.empty_cache()
         sweep["sampling"] = token_selection_timing(torch, ops)
+        sweep["gemm_mx_prefill"] = prefill_gemm_sweep(torch, ops)
         result["sweep"] = sweep
 
     if args.copy_calibration:

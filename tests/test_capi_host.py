@@ -128,6 +128,23 @@ def test_attention_paged_argument_checks():
     assert mx(16, 3) == EINVAL                              # fewer than D/32 exponents per row
 
 
+def test_gemm_mx_argument_checks():
+    lib = _lib.load()
+    g = lambda M, N, K, lda=4096, ldc=4096, a=FAKE: lib.fp8_gemm_mx(a, lda, FAKE, 1, M, FAKE, 4096, FAKE, 1, N, M, N,
+                                                                    K, FAKE, ldc, None)
+    assert g(256, 4000, 4096) == EUNSUPPORTED               # N % 128
+    assert g(256, 4096, 4000, lda=4000) == EUNSUPPORTED     # K % 128
+    assert g(256, 4096, 4096, lda=4100) == EINVAL           # lda % 16
+    assert g(256, 4096, 4096, ldc=4000) == EINVAL           # ldc < N
+    assert g(256, 4096, 4096, a=None) == EINVAL
+    assert lib.fp8_mx_packed_bytes(200, 384) == 256 * 384 + 256 * 12
+    assert lib.fp8_mx_packed_bytes(200, 100) == 0
+    assert lib.fp8_pack_mx(FAKE, 384, FAKE, 1, 200, 200, 384, FAKE, 16, None) == EWORKSPACE
+    assert lib.fp8_pack_mx(FAKE, 380, FAKE, 1, 200, 200, 384, FAKE, 1 << 20, None) == EINVAL
+    assert lib.fp8_gemm_mx_packed(FAKE, FAKE, 256, 4000, 4096, FAKE, 4096, None) == EUNSUPPORTED
+    assert lib.fp8_gemm_mx_packed(None, FAKE, 256, 4096, 4096, FAKE, 4096, None) == EINVAL
+
+
 def test_sampling_and_window_argument_checks():
     lib = _lib.load()
     f = ctypes.c_float
