@@ -30,6 +30,13 @@ t % P of page block_table[b][t // P].  The pages give no page size or pool
 layout; the pool here is [pages, Hkv, P, D] and the attention is the one
 above over the rows the table names.
 
+The extend / prefill variant (extend_attention) is the pages' prefill and
+paged-prefill ("extend") attention (page "How We Made Our Text-to-Speech API
+Free", section "What's Open Source"; the KV-cache page's section 5 table:
+prefill writes T positions, kv_len = T): the T new tokens of a sequence are
+the last T of its kv_len cached positions, and the new token at position p
+attends causally to positions 0 .. p.  Prefill is T = kv_len.
+
 Pins (tests/test_oracle_attention.py): kv_len = 1 returns v_0; q = 0 returns
 the mean of the V prefix; equality with an explicit np.repeat expansion of the
 heads; torch's float64 scaled_dot_product_attention on the expanded heads;
@@ -42,6 +49,11 @@ Paged variants: a contiguous cache scattered over shuffled pages gives the
 contiguous result exactly; pages the table does not name (NaN-filled) never
 enter; kv_len = 1 returns slot 0 of the first named page; a brute-force
 scalar loop on a tiny pool; an out-of-pool page id is refused.
+Extend: one new token per sequence equals the decode attention exactly; a
+prefill equals torch's float64 causal scaled_dot_product_attention on the
+repeat_interleave'd heads; an extend equals the last rows of the prefill of
+the whole sequence exactly; a brute-force scalar loop on a tiny case; cache
+positions at or past kv_len (NaN-filled) never enter.
 """
 
 import numpy as np
@@ -144,3 +156,39 @@ def gqa_decode_attention_paged_mxkv(q, k_codes, k_exps, v_codes, v_exps, block_t
     P, D], exponents [pages, Hkv, P, D/32]."""
     g = lambda pool: gather_paged(pool, block_table, kv_len, page_size)
     return gqa_decode_attention_mxkv(q, g(k_codes), g(k_exps), g(v_codes), g(v_exps), kv_len, scale)
+
+def extend_attention(q, k_cache, v_cache, q_start, kv_len, scale=None):
+    """Causal attention of the new tokens of every sequence over its cache.
+
+    q        : [total, Hq, D]; sequence b owns rows q_start[b] .. q_start[b+1]-1,
+               T_b = q_start[b+1] - q_start[b] new tokens (T_b may be 0)
+    k_cache  : [B, Hkv, cap, D]; the new tokens are the last T_b of the
+    v_cache    kv_len[b] valid positions (only t < kv_len[b] is read)
+    Token t of sequence b sits at position p = kv_len[b] - T_b + t and
+    attends to positions 0 .. p.  Returns float64 [total, Hq, D].
+    """
+    q = np.asarray(q)
+    total, Hq, D = q.shape
+    B, Hkv = k_cache.shape[0], k_cache.shape[1]
+    if Hq % Hkv:
+        raise ValueError("Hq must be a multiple of Hkv")
+    G = Hq // Hkv
+    if scale is None:
+        scale = 1.0 / np.sqrt(D)
+    out = np.zeros((total, Hq, D), np.float64)
+    for b in range(B):
+        q0, q1 = int(q_start[b]), int(q_start[b + 1])
+        T, L = q1 - q0, int(kv_len[b])
+        if not 0 <= T <= L <= k_cache.shape[2]:
+            raise ValueError(f"sequence {b}: need 0 <= T <= kv_len <= cap")
+        for t in range(T):
+            p = L - T + t
+            for h in range(Hq):
+                kvh = h // G
+                K = np.asarray(k_cache[b, kvh, :p + 1], np.float64)
+                V = np.asarray(v_cache[b, kvh, :p + 1], np.float64)
+                s = (K @ np.asarray(q[q0 + t, h], np.float64)) * scale
+                w = np.exp(s - s.max())
+                w /= w.sum()
+                out[q0 + t, h] = w @ V
+    return out

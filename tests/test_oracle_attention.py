@@ -229,3 +229,74 @@ def test_paged_mxkv_equals_paged_plain_on_dequantised_pool():
     out = attention.gqa_decode_attention_paged_mxkv(q, kc, ke, vc, ve, table, L, P)
     ref = attention.gqa_decode_attention_paged(q, kval, vval, table, L, P)
     assert np.allclose(out, ref, rtol=1e-12, atol=0)
+
+
+def _extend_case(seed, T, L, Hq=8, Hkv=2, D=16, cap=48):
+    """Queries for T[b] new tokens and caches with kv_len L[b] (NaN past it)."""
+    g = np.random.default_rng(seed)
+    B = len(T)
+    q_start = np.concatenate([[0], np.cumsum(T)]).astype(np.int64)
+    q = g.standard_normal((int(q_start[-1]), Hq, D))
+    k = g.standard_normal((B, Hkv, cap, D))
+    v = g.standard_normal((B, Hkv, cap, D))
+    for b in range(B):
+        k[b, :, L[b]:] = np.nan
+        v[b, :, L[b]:] = np.nan
+    return q, k, v, q_start
+
+
+def test_extend_one_token_equals_decode():
+    L = [30, 1, 48]
+    q, k, v, qs = _extend_case(31, [1, 1, 1], L)
+    out = attention.extend_attention(q, k, v, qs, L)
+    assert np.array_equal(out, attention.gqa_decode_attention(q, k, v, np.array(L)))
+
+
+def test_prefill_equals_torch_causal_sdpa():
+    T = [20, 7]
+    q, k, v, qs = _extend_case(32, T, T)
+    out = attention.extend_attention(q, k, v, qs, T)
+    for b in range(2):
+        qt = torch.from_numpy(q[qs[b]:qs[b + 1]]).transpose(0, 1)                 # [Hq, T, D]
+        kt = torch.from_numpy(k[b, :, :T[b]]).repeat_interleave(4, dim=0)
+        vt = torch.from_numpy(v[b, :, :T[b]]).repeat_interleave(4, dim=0)
+        ref = torch.nn.functional.scaled_dot_product_attention(qt, kt, vt, is_causal=True)
+        assert np.allclose(out[qs[b]:qs[b + 1]], ref.transpose(0, 1).numpy(), rtol=1e-12, atol=1e-13)
+
+
+def test_extend_equals_last_rows_of_full_prefill():
+    L = [40, 25]
+    T = [9, 25]
+    qfull, k, v, qs_full = _extend_case(33, L, L)
+    full = attention.extend_attention(qfull, k, v, qs_full, L)
+    rows = np.concatenate([np.arange(qs_full[b + 1] - T[b], qs_full[b + 1]) for b in range(2)])
+    qs = np.concatenate([[0], np.cumsum(T)])
+    out = attention.extend_attention(qfull[rows], k, v, qs, L)
+    assert np.array_equal(out, full[rows])
+
+
+def test_extend_brute_force_scalar_loop():
+    import math
+    T, L = [3, 2], [5, 2]
+    q, k, v, qs = _extend_case(34, T, L, Hq=2, Hkv=1, D=3, cap=6)
+    out = attention.extend_attention(q, k, v, qs, L, scale=0.6)
+    for b in range(2):
+        for t in range(T[b]):
+            p = L[b] - T[b] + t
+            for h in range(2):
+                qv = q[qs[b] + t, h]
+                s = [0.6 * sum(qv[d] * k[b, 0, j, d] for d in range(3)) for j in range(p + 1)]
+                w = [math.exp(x - max(s)) for x in s]
+                ref = [sum(w[j] * v[b, 0, j, d] for j in range(p + 1)) / sum(w) for d in range(3)]
+                assert np.allclose(out[qs[b] + t, h], ref, rtol=1e-12, atol=1e-14)
+
+
+def test_extend_rejects_bad_lengths_and_allows_empty():
+    q, k, v, qs = _extend_case(35, [2, 0], [3, 4])
+    out = attention.extend_attention(q, k, v, qs, [3, 4])
+    assert out.shape == (2, 8, 16) and np.isfinite(out).all()
+    try:
+        attention.extend_attention(q, k, v, qs, [1, 4])          # T > kv_len
+    except ValueError:
+        return
+    raise AssertionError("T > kv_len accepted")
