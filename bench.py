@@ -394,6 +394,42 @@ def prefill_gemm_sweep(torch, ops):
     return out
 
 
+def extend_attn_sweep(torch, ops):
+    """extend_attn (prefill / extend) at 32/8/128: a 4096-token prefill, 16
+    sequences extending by 256 tokens after 1792 cached, 64 sequences by 16
+    after 4080.  TFLOP/s counts 4 Hq D flop per (new token, attended
+    position) against the bf16 MFMA peak; GB/s counts the K/V prefix once."""
+    g = torch.Generator(device="cuda")
+    g.manual_seed(13)
+    Hq, Hkv, D = 32, 8, 128
+    out = {}
+    for B, T, L in ((1, 4096, 4096), (16, 256, 2048), (64, 16, 4096)):
+        k = torch.randn((B, Hkv, L, D), generator=g, device="cuda").to(torch.bfloat16)
+        v = torch.randn((B, Hkv, L, D), generator=g, device="cuda").to(torch.bfloat16)
+        q = torch.randn((B * T, Hq, D), generator=g, device="cuda").to(torch.bfloat16)
+        qs = torch.arange(0, B * T + 1, T, dtype=torch.int32, device="cuda")
+        kv = torch.full((B,), L, dtype=torch.int32, device="cuda")
+        o = torch.empty_like(q)
+        for _ in range(3):
+            ops.extend_attn(q, qs, k, v, kv, T, out=o)
+        torch.cuda.synchronize()
+        t0, t1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        t0.record()
+        for _ in range(10):
+            ops.extend_attn(q, qs, k, v, kv, T, out=o)
+        t1.record()
+        torch.cuda.synchronize()
+        us = t0.elapsed_time(t1) / 10 * 1e3
+        pos = B * (T * (L - T) + T * (T + 1) // 2)
+        tf = 4 * Hq * D * pos / (us * 1e-6) / 1e12
+        gbs = B * L * Hkv * D * 2 * 2 / (us * 1e-6) / 1e9
+        out[f"B={B},new={T},kv_len={L}"] = {"us": us, "TFLOP/s": tf, "frac_bf16_mfma": tf / 2500.0, "GB/s": gbs}
+        log(f"extend B={B} new={T} kv_len={L}: {us:.1f} us {tf:.0f} TFLOP/s {gbs:.0f} GB/s")
+        del k, v, q, o
+        torch.cuda.empty_cache()
+    return out
+
+
 def token_selection_timing(torch, ops):
     """sample_top_k_top_p on the heads' logits (B = 64, V = 4096, the pages'
     temperature 0.8 / top_p 0.8 / top_k 30, and top_k off) and the window
@@ -671,6 +707,7 @@ def main():
             torch.cuda.empty_cache()
         sweep["sampling"] = token_selection_timing(torch, ops)
         sweep["gemm_mx_prefill"] = prefill_gemm_sweep(torch, ops)
+        sweep["extend_attn"] = extend_attn_sweep(torch, ops)
         result["sweep"] = sweep
 
     if args.copy_calibration:

@@ -298,6 +298,30 @@ def fp8_gemm_mx(qa, ea, qb, eb, c=None):
     return c
 
 
+def extend_attn(q, q_start, k_cache, v_cache, kv_len, max_new_hint, softmax_scale=None, out=None, err=None):
+    """Causal attention of new tokens q [total, Hq, D] (sequence b owns rows
+    q_start[b] .. q_start[b+1]-1, int32 [B+1] on the device) over caches
+    [B, Hkv, cap, D] holding them as the last rows of kv_len[b]."""
+    _require_cuda(q, q_start, k_cache, v_cache, kv_len)
+    if q_start.dtype != torch.int32 or kv_len.dtype != torch.int32:
+        raise TypeError("q_start and kv_len must be int32")
+    if k_cache.stride() != v_cache.stride() or k_cache.shape != v_cache.shape or k_cache.stride(3) != 1:
+        raise ValueError("k_cache and v_cache must share shape and strides, D contiguous")
+    total, Hq, D = q.shape
+    B, Hkv, cap, _ = k_cache.shape
+    if q_start.shape != (B + 1,) or kv_len.shape != (B,):
+        raise ValueError("q_start must be [B + 1] and kv_len [B]")
+    if softmax_scale is None:
+        softmax_scale = 1.0 / math.sqrt(D)
+    if out is None:
+        out = torch.empty_like(q)
+    _lib.check(_lib.load().extend_attn(
+        _bits(q.contiguous()), q_start.data_ptr(), total, _bits(k_cache), _bits(v_cache), k_cache.stride(0),
+        k_cache.stride(1), k_cache.stride(2), kv_len.data_ptr(), B, Hq, Hkv, D, cap, int(max_new_hint),
+        float(softmax_scale), _bits(out), err.data_ptr() if err is not None else None, _stream()))
+    return out
+
+
 @dataclass
 class PackedMx:
     """An MXFP8 operand [rows, K] in the packed layout of fp8_pack_mx."""

@@ -277,6 +277,36 @@ FP8S_API int gqa_decode_attn_paged_mxkv(const uint16_t* q, const uint8_t* k_q, c
                     int32_t* err_flag, void* stream);
 
 /*
+ * extend_attn -- causal attention of the new tokens of every sequence over
+ * its KV cache: prefill (every cached position is new) and extend (new
+ * tokens after a cached prefix) ([TTS] "What's Open Source": contiguous
+ * prefill and paged-prefill "extend" attention; [KV] section 5 for the
+ * cache and head mapping).  Sequence b has T_b = q_start[b+1] - q_start[b]
+ * new tokens, already written as the last T_b of its kv_len[b] cache
+ * positions; new token t (position p = kv_len[b] - T_b + t) attends to
+ * positions 0 .. p with query head h on KV head h / (Hq / Hkv):
+ *     out[q_start[b] + t, h] = sum_{j <= p} softmax_j(scale q . K[b,g,j]) V[b,g,j]
+ *   q        [total_tokens, Hq, D] bf16 contiguous; out the same shape.
+ *   q_start  device int32 [B + 1], non-decreasing from 0 to <= total_tokens.
+ *   k_cache, v_cache  as gqa_decode_attn (strided, D contiguous).
+ *   kv_len   device int32 [B]; needs T_b <= kv_len[b] <= cap.
+ *   max_new_hint  host bound on T_b (sizes the grid; rows past it are not
+ *            written).  D must be 128; Hq / Hkv one of 1, 2, 4, 8.
+ *   A sequence with T_b > kv_len[b], kv_len outside [1, cap] or T_b above
+ *   the hint has its rows written as zeros and sets FP8S_DEV_KVLEN_RANGE; a
+ *   q_start row range outside [0, total_tokens] writes nothing and sets it.
+ *   Positions >= kv_len[b] are never read.  Accuracy: bf16 MFMA products,
+ *   fp32 softmax and accumulation (probabilities rounded to bf16 before the
+ *   P V product); max|out - oracle| <= 5e-3 * max|oracle|.
+ */
+FP8S_API int extend_attn(const uint16_t* q, const int32_t* q_start, int64_t total_tokens,
+                    const uint16_t* k_cache, const uint16_t* v_cache,
+                    int64_t stride_b, int64_t stride_h, int64_t stride_t,
+                    const int32_t* kv_len, int64_t B, int32_t Hq, int32_t Hkv, int32_t D,
+                    int64_t cap, int64_t max_new_hint, float softmax_scale,
+                    uint16_t* out, int32_t* err_flag, void* stream);
+
+/*
  * qlinear_fp8 -- y = [residual +] dequant(quant(norm(x))) . dequant(W)^T, the
  * FP8 projections of a decode block other than the MLP ([TTS] "FP8
  * Quantization Strategy", "Kernel Benchmark Results").

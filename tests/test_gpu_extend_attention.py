@@ -1,0 +1,120 @@
+"""extend_attn (prefill / extend attention) on the GPU against the oracle:
+whole prefills and extends at the 32/8/128 shape with a garbage cache tail,
+one new token per sequence (the decode case), a long prefill checked on
+sampled rows (each sampled row is the oracle's one-token case at its
+position), group sizes 1, 2 and 8, an empty sequence between others,
+tail invariance and invalid lengths."""
+
+import numpy as np
+import pytest
+import torch
+
+from oracle import attention as oattn
+from fp8_transformer_step_amd import inputs, ops
+from _helpers import TOL_BF16_ATTN, f32, from_dev_bf16, log, max_rel_err, need_gpu, to_dev_bf16
+
+pytestmark = pytest.mark.gpu
+
+
+def _garbage(shape, seed):
+    g = torch.Generator(device="cuda")
+    g.manual_seed(seed)
+    return torch.randint(-32768, 32768, shape, dtype=torch.int32, device="cuda", generator=g).to(torch.int16).view(
+        torch.bfloat16)
+
+
+class Case:
+    def __init__(self, T, L, Hq=32, Hkv=8, D=128, cap=None, extra=0, tail_seed=1):
+        self.T, self.L = np.array(T, np.int32), np.array(L, np.int32)
+        B = len(T)
+        self.cap = cap or int(max(L)) + 40
+        self.q_start = np.concatenate([[0], np.cumsum(self.T)]).astype(np.int32)
+        total = max(int(self.q_start[-1]), 1)
+        self.qb = inputs.normal_bf16(inputs.W_ATTN, inputs.T_Q, (total, Hq, D), 1.0, extra)
+        _, self.kb, self.vb = inputs.attention_prefix(inputs.W_ATTN, B, 1, Hkv, D, int(max(L)), extra=extra)
+        self.kc = _garbage((B, Hkv, self.cap, D), tail_seed)
+        self.vc = _garbage((B, Hkv, self.cap, D), tail_seed + 1)
+        kd, vd = to_dev_bf16(self.kb), to_dev_bf16(self.vb)
+        for b in range(B):
+            self.kc[b, :, :L[b]] = kd[b, :, :L[b]]
+            self.vc[b, :, :L[b]] = vd[b, :, :L[b]]
+        self.hint = max(int(self.T.max()), 1)
+        torch.cuda.synchronize()
+
+    def run(self, err=None, L=None):
+        kv = torch.from_numpy(self.L if L is None else L).cuda()
+        out = ops.extend_attn(to_dev_bf16(self.qb), torch.from_numpy(self.q_start).cuda(), self.kc, self.vc, kv,
+                              self.hint, err=err)
+        torch.cuda.synchronize()
+        return out
+
+    def oracle(self):
+        return oattn.extend_attention(f32(self.qb), f32(self.kb), f32(self.vb), self.q_start, self.L)
+
+
+@pytest.mark.parametrize("T,L", [([100, 37], [100, 37]),          # prefill
+                                 ([20, 64, 1], [300, 513, 77]),    # extend
+                                 ([16, 17, 33], [16, 40, 33])])    # tile edges
+def test_matches_oracle(T, L):
+    need_gpu()
+    c = Case(T, L, extra=400 + sum(T))
+    err = torch.zeros(1, dtype=torch.int32, device="cuda")
+    out = c.run(err)
+    e = max_rel_err(from_dev_bf16(out), c.oracle())
+    log(f"extend T={T} L={L}: max rel err {e:.2e}")
+    assert int(err.item()) == 0
+    assert e <= TOL_BF16_ATTN
+
+
+def test_one_new_token_matches_decode_kernel():
+    need_gpu()
+    L = [234, 400, 1, 57]
+    c = Case([1, 1, 1, 1], L, extra=410)
+    out = from_dev_bf16(c.run())
+    ref = oattn.gqa_decode_attention(f32(c.qb), f32(c.kb), f32(c.vb), np.array(L))
+    assert max_rel_err(out, ref) <= TOL_BF16_ATTN
+    dec = ops.gqa_decode_attn(to_dev_bf16(c.qb), c.kc, c.vc, torch.from_numpy(np.array(L, np.int32)).cuda(), max(L))
+    torch.cuda.synchronize()
+    assert max_rel_err(out, from_dev_bf16(dec)) <= TOL_BF16_ATTN
+
+
+def test_long_prefill_sampled_rows():
+    """A 2048-token prefill: 40 sampled rows, each the oracle's one-token
+    attention over positions 0 .. p."""
+    need_gpu()
+    T = 2048
+    c = Case([T], [T], extra=420)
+    out = from_dev_bf16(c.run())
+    rows = np.unique(np.concatenate([[0, 1, 15, 16, T - 1], np.random.default_rng(7).integers(0, T, 35)]))
+    for t in rows:
+        ref = oattn.gqa_decode_attention(f32(c.qb[t:t + 1]), f32(c.kb), f32(c.vb), np.array([t + 1]))
+        assert max_rel_err(out[t:t + 1], ref) <= TOL_BF16_ATTN, t
+
+
+@pytest.mark.parametrize("Hq,Hkv", [(8, 8), (16, 8), (64, 8)])
+def test_group_sizes(Hq, Hkv):
+    need_gpu()
+    c = Case([40, 9], [90, 9], Hq=Hq, Hkv=Hkv, extra=430 + Hq)
+    assert max_rel_err(from_dev_bf16(c.run()), c.oracle()) <= TOL_BF16_ATTN
+
+
+def test_empty_sequence_and_tail_invariance():
+    need_gpu()
+    c = Case([30, 0, 18], [50, 20, 18], extra=440)
+    base = c.run()
+    assert max_rel_err(from_dev_bf16(base), c.oracle()) <= TOL_BF16_ATTN
+    c2 = Case([30, 0, 18], [50, 20, 18], extra=440, tail_seed=9)
+    assert torch.equal(base.view(torch.int16), c2.run().view(torch.int16))
+
+
+def test_invalid_lengths_zero_their_rows():
+    need_gpu()
+    c = Case([10, 12, 8], [40, 30, 20], extra=450)
+    good = c.run()
+    bad = np.array([40, 5, 20], np.int32)                        # T = 12 > kv_len = 5
+    err = torch.zeros(1, dtype=torch.int32, device="cuda")
+    out = c.run(err, L=bad)
+    assert int(err.item()) == ops.DEV_KVLEN_RANGE
+    assert not out[10:22].float().abs().sum().item()
+    keep = list(range(10)) + list(range(22, 30))
+    assert torch.equal(out[keep].view(torch.int16), good[keep].view(torch.int16))
