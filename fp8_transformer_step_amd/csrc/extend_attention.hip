@@ -11,10 +11,13 @@
 // its kv_len positions; new token t sits at p = kv_len - T + t and attends to
 // positions 0 .. p.
 //
-// MI355X design (D = 128): one workgroup per (sequence, KV head, block of 16
-// new tokens).  Blocks of 32 cache positions are staged once in LDS for all
-// G query heads of the KV head (K row-major, V transposed), and each wave
-// takes query heads wave, wave + 4:
+// MI355X design (D = 128): one workgroup of 16 waves per (sequence, KV head,
+// block of 64 new tokens).  Blocks of 32 cache positions are staged once in
+// LDS for all G query heads and 64 tokens (K row-major, V transposed; the
+// next block is loaded into registers while the current one is multiplied),
+// and wave w takes the 16 tokens 16 (w / 4) .. and query heads w % 4,
+// w % 4 + 4:
+//   (fewer token rows for G = 8 and for short extends)
 //   * S^T = K Q^T with bf16 MFMA 16x16x32 (positions as A rows, the 16
 //     queries as B columns, Q held in registers), so that a lane ends up
 //     with 8 scores of one query -- exactly the A operand that P V needs;
@@ -31,7 +34,12 @@
 namespace fp8s {
 
 constexpr int kExD = 128;
-constexpr int kExQ = 16;                  // new tokens per workgroup
+// QS rows of 4 waves, 16 new tokens each: 4 rows (64 tokens) for prefill-
+// sized work, 2 when every wave carries two query heads (G = 8, which needs
+// more than the 128 registers a 16-wave workgroup leaves a thread), 1 when
+// at most 16 tokens are new (more rows would idle).
+template <int QS>
+constexpr int ex_threads() { return 256 * QS; }
 constexpr int kExKV = 32;                 // cache positions per staged block
 constexpr int kExKRow = kExD * 2 + 16;    // bytes per staged K row (padded)
 constexpr int kExVRow = kExKV * 2 + 8;    // bytes per staged V^T row (padded)
@@ -50,13 +58,14 @@ struct ExtendArgs {
     int32_t* err;
 };
 
-template <int G>
-__global__ __launch_bounds__(256) void extend_attn_kernel(ExtendArgs a) {
+template <int G, int QS>
+__global__ __launch_bounds__(ex_threads<QS>()) void extend_attn_kernel(ExtendArgs a) {
     constexpr int HPW = (G + 3) / 4;      // query heads per wave
+    constexpr int kThreads = ex_threads<QS>(), kTokens = 16 * QS;
     __shared__ __attribute__((aligned(16))) uint8_t s_k[kExKV * kExKRow];
     __shared__ __attribute__((aligned(16))) uint8_t s_vt[kExD * kExVRow];
 
-    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const int lane = threadIdx.x & 63, wave = (threadIdx.x >> 6) & 3, qsub = threadIdx.x >> 8;
     const int g4 = lane >> 4, ql = lane & 15;
     const int b = blockIdx.x / a.n_qblk, qblk = blockIdx.x % a.n_qblk, g = blockIdx.y;
     const int q0 = a.q_start[b], q1 = a.q_start[b + 1];
@@ -65,24 +74,25 @@ __global__ __launch_bounds__(256) void extend_attn_kernel(ExtendArgs a) {
         return;
     }
     const int T = q1 - q0, L = a.kv_len[b];
-    const int t0 = qblk * kExQ;
+    const int t0 = qblk * kTokens;
     if (t0 >= T) return;
     const bool ok = L >= 1 && (int64_t)L <= a.cap && T <= L && (int64_t)T <= a.hint;
     if (!ok) {                            // zero this block's rows of this KV head's query heads
         if (threadIdx.x == 0 && qblk == 0 && g == 0) report_error(a.err, FP8S_DEV_KVLEN_RANGE);
-        for (int e = threadIdx.x; e < kExQ * G * kExD; e += 256) {
+        for (int e = threadIdx.x; e < kTokens * G * kExD; e += kThreads) {
             const int r = e / (G * kExD), c = e % (G * kExD);
             if (t0 + r < T) a.out[((int64_t)(q0 + t0 + r) * a.Hq + g * G) * kExD + c] = 0;
         }
         return;
     }
     const int base_pos = L - T;                                  // position of new token 0
-    const int p_last = base_pos + min(t0 + kExQ, T) - 1;         // last position any row of the block sees
+    const int p_last = base_pos + min(t0 + kTokens, T) - 1;         // last position any row of the block sees
     const int n_blk = (p_last + kExKV) / kExKV;
-    const bool q_live = t0 + ql < T;                              // this lane's query row exists
-    const int pq = base_pos + t0 + ql;                            // its position
+    const int tq = t0 + 16 * qsub + ql;                           // this lane's query row
+    const bool q_live = tq < T;
+    const int pq = base_pos + tq;                                 // its position
 
-    // Q of this lane's query (row t0 + ql) for each head of the wave, as the
+    // Q of this lane's query (row tq) for each head of the wave, as the
     // B operand: d = 32 j + 8 g4 .. +8
     v8bf qb[HPW][4];
 #pragma unroll
@@ -92,7 +102,7 @@ __global__ __launch_bounds__(256) void extend_attn_kernel(ExtendArgs a) {
         for (int j = 0; j < 4; ++j) {
             uint4 w = make_uint4(0, 0, 0, 0);
             if (h < G && q_live)
-                w = *reinterpret_cast<const uint4*>(a.q + ((int64_t)(q0 + t0 + ql) * a.Hq + g * G + h) * kExD +
+                w = *reinterpret_cast<const uint4*>(a.q + ((int64_t)(q0 + tq) * a.Hq + g * G + h) * kExD +
                                                     32 * j + 8 * g4);
             qb[hh][j] = __builtin_bit_cast(v8bf, w);
         }
@@ -109,25 +119,43 @@ __global__ __launch_bounds__(256) void extend_attn_kernel(ExtendArgs a) {
 
     const uint16_t* kbase = a.k + (int64_t)b * a.sb + (int64_t)g * a.sh;
     const uint16_t* vbase = a.v + (int64_t)b * a.sb + (int64_t)g * a.sh;
+    // staging: 512 chunks of 8 K values and the matching 8 V values per
+    // block, CH per thread (chunk c = threadIdx.x + i * kThreads < 512); the
+    // next block's chunks are loaded into registers before the current block
+    // is multiplied
+    constexpr int CH = kThreads >= 512 ? 1 : 512 / kThreads;
+    uint4 kw[CH], vw[CH];
+    auto fetch = [&](int p0) {
+#pragma unroll
+        for (int i = 0; i < CH; ++i) {
+            const int c = threadIdx.x + i * kThreads;
+            const int pr = c / (kExD / 8), d0 = 8 * (c % (kExD / 8));
+            kw[i] = make_uint4(0, 0, 0, 0);
+            vw[i] = make_uint4(0, 0, 0, 0);
+            if (c < kExKV * kExD / 8 && p0 + pr < L) {            // never read past kv_len
+                kw[i] = *reinterpret_cast<const uint4*>(kbase + (int64_t)(p0 + pr) * a.st + d0);
+                vw[i] = *reinterpret_cast<const uint4*>(vbase + (int64_t)(p0 + pr) * a.st + d0);
+            }
+        }
+    };
+    fetch(0);
     for (int blk = 0; blk < n_blk; ++blk) {
         const int p0 = blk * kExKV;
-        // stage K (row-major) and V (transposed): 512 chunks of 8 values each
-        for (int c = threadIdx.x; c < kExKV * kExD / 8; c += 256) {
-            const int pr = c / (kExD / 8), d0 = 8 * (c % (kExD / 8));
-            uint4 kw = make_uint4(0, 0, 0, 0), vw = make_uint4(0, 0, 0, 0);
-            if (p0 + pr < L) {            // never read past kv_len
-                kw = *reinterpret_cast<const uint4*>(kbase + (int64_t)(p0 + pr) * a.st + d0);
-                vw = *reinterpret_cast<const uint4*>(vbase + (int64_t)(p0 + pr) * a.st + d0);
-            }
-            *reinterpret_cast<uint4*>(s_k + pr * kExKRow + 2 * d0) = kw;
-            const uint32_t vv[4] = {vw.x, vw.y, vw.z, vw.w};
 #pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                *reinterpret_cast<uint16_t*>(s_vt + (d0 + 2 * i) * kExVRow + 2 * pr) = (uint16_t)(vv[i] & 0xFFFF);
-                *reinterpret_cast<uint16_t*>(s_vt + (d0 + 2 * i + 1) * kExVRow + 2 * pr) = (uint16_t)(vv[i] >> 16);
+        for (int i = 0; i < CH; ++i) {    // K row-major, V transposed
+            const int c = threadIdx.x + i * kThreads;
+            if (c >= kExKV * kExD / 8) continue;
+            const int pr = c / (kExD / 8), d0 = 8 * (c % (kExD / 8));
+            *reinterpret_cast<uint4*>(s_k + pr * kExKRow + 2 * d0) = kw[i];
+            const uint32_t vv[4] = {vw[i].x, vw[i].y, vw[i].z, vw[i].w};
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                *reinterpret_cast<uint16_t*>(s_vt + (d0 + 2 * e) * kExVRow + 2 * pr) = (uint16_t)(vv[e] & 0xFFFF);
+                *reinterpret_cast<uint16_t*>(s_vt + (d0 + 2 * e + 1) * kExVRow + 2 * pr) = (uint16_t)(vv[e] >> 16);
             }
         }
         __syncthreads();
+        if (blk + 1 < n_blk) fetch(p0 + kExKV);
 
         // K fragments (A operand, rows = positions 16 h2 + ql, d = 32 j + 8 g4 ..)
         v8bf kf[2][4];
@@ -215,7 +243,7 @@ __global__ __launch_bounds__(256) void extend_attn_kernel(ExtendArgs a) {
         for (int r = 0; r < 4; ++r) lr[r] = __shfl(l_run[hh], 4 * g4 + r, kWave);
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
-            const int t = t0 + 4 * g4 + r;
+            const int t = t0 + 16 * qsub + 4 * g4 + r;
             if (t >= T) continue;
             uint16_t* dst = a.out + ((int64_t)(q0 + t) * a.Hq + g * G + h) * kExD + ql;
 #pragma unroll
@@ -247,7 +275,8 @@ extern "C" int extend_attn(const uint16_t* q, const int32_t* q_start, int64_t to
                  "extend_attn: q, caches and out must be 16-byte aligned");
     FP8S_REQUIRE(total_tokens < (1ll << 31) && cap < (1ll << 31), FP8S_EUNSUPPORTED, "extend_attn: too large");
     if (max_new_hint > cap) max_new_hint = cap;
-    const int64_t n_qblk = (max_new_hint + kExQ - 1) / kExQ;
+    const int QS = max_new_hint <= 16 ? 1 : (G == 8 ? 2 : 4);
+    const int64_t n_qblk = (max_new_hint + 16 * QS - 1) / (16 * QS);
     FP8S_REQUIRE(B * n_qblk < (1ll << 31) && Hkv < 65536, FP8S_EUNSUPPORTED, "extend_attn: grid too large");
     ExtendArgs a;
     a.q = q; a.q_start = q_start; a.k = k_cache; a.v = v_cache;
@@ -258,11 +287,11 @@ extern "C" int extend_attn(const uint16_t* q, const int32_t* q_start, int64_t to
     a.scale_log2 = softmax_scale * 1.4426950408889634f;
     a.out = out; a.err = err_flag;
     const dim3 grid((unsigned)(B * n_qblk), (unsigned)Hkv);
-    switch (G) {
-    case 1: FP8S_LAUNCH("extend_attn", extend_attn_kernel<1>, grid, dim3(256), 0, as_stream(stream), a); break;
-    case 2: FP8S_LAUNCH("extend_attn", extend_attn_kernel<2>, grid, dim3(256), 0, as_stream(stream), a); break;
-    case 4: FP8S_LAUNCH("extend_attn", extend_attn_kernel<4>, grid, dim3(256), 0, as_stream(stream), a); break;
-    default: FP8S_LAUNCH("extend_attn", extend_attn_kernel<8>, grid, dim3(256), 0, as_stream(stream), a); break;
-    }
+    const hipStream_t st = as_stream(stream);
+#define FP8S_EX_CASE(GG, QQ)                                                                             \
+    if (G == GG && QS == QQ) FP8S_LAUNCH("extend_attn", (extend_attn_kernel<GG, QQ>), grid, dim3(ex_threads<QQ>()), 0, st, a);
+    FP8S_EX_CASE(1, 1) FP8S_EX_CASE(1, 4) FP8S_EX_CASE(2, 1) FP8S_EX_CASE(2, 4)
+    FP8S_EX_CASE(4, 1) FP8S_EX_CASE(4, 4) FP8S_EX_CASE(8, 1) FP8S_EX_CASE(8, 2)
+#undef FP8S_EX_CASE
     return check_launch("extend_attn");
 }

@@ -91,10 +91,13 @@ def test_long_prefill_sampled_rows():
         assert max_rel_err(out[t:t + 1], ref) <= TOL_BF16_ATTN, t
 
 
-@pytest.mark.parametrize("Hq,Hkv", [(8, 8), (16, 8), (64, 8)])
-def test_group_sizes(Hq, Hkv):
+@pytest.mark.parametrize("Hq,Hkv", [(8, 8), (16, 8), (64, 8), (32, 8)])
+@pytest.mark.parametrize("T,L", [([40, 9], [90, 9]), ([12, 5], [70, 5])])
+def test_group_sizes(Hq, Hkv, T, L):
+    """Every group size, with more than 16 new tokens (several token rows per
+    workgroup) and with at most 16 (one row)."""
     need_gpu()
-    c = Case([40, 9], [90, 9], Hq=Hq, Hkv=Hkv, extra=430 + Hq)
+    c = Case(T, L, Hq=Hq, Hkv=Hkv, extra=430 + Hq + T[0])
     assert max_rel_err(from_dev_bf16(c.run()), c.oracle()) <= TOL_BF16_ATTN
 
 
