@@ -40,12 +40,25 @@ KERNELS = [
     (r"\bdown_kernel", "mlp_down"),
     (r"act_quant_kernel", "act_quant"),
     (r"hq_kernel", "mlp_hq"),
-    (r"attn_split_kernel<[^>]*true", "attn_single"),
+    # split kernels: <D, G, SINGLE, PAGED>; balanced: <D, G, PAGED>
+    (r"attn_split_kernel<\d+, \d+, true, true>", "attn_single_paged"),
+    (r"attn_split_kernel<\d+, \d+, true, false>", "attn_single"),
+    (r"attn_split_kernel<\d+, \d+, false, true>", "attn_split_paged"),
     (r"attn_split_kernel", "attn_split"),
+    (r"attn_bal_kernel<\d+, \d+, true>", "attn_split_paged"),
     (r"attn_bal_kernel", "attn_split"),
-    (r"attn_split_mx_kernel<[^>]*true", "attn_single_mx"),
+    (r"attn_split_mx_kernel<\d+, \d+, true, true>", "attn_single_mx_paged"),
+    (r"attn_split_mx_kernel<\d+, \d+, true, false>", "attn_single_mx"),
+    (r"attn_split_mx_kernel<\d+, \d+, false, true>", "attn_split_mx_paged"),
     (r"attn_split_mx_kernel", "attn_split_mx"),
+    (r"attn_bal_mx_kernel<\d+, \d+, true>", "attn_split_mx_paged"),
     (r"attn_bal_mx_kernel", "attn_split_mx"),
+    (r"gemm_large_mx_kernel<true>", "gemm_large_mx_packed"),
+    (r"gemm_large_mx_kernel", "gemm_large_mx"),
+    (r"pack_mx_kernel", "pack_mx"),
+    (r"extend_attn_kernel", "extend_attn"),
+    (r"sample_kernel", "sample"),
+    (r"window_shift_kernel", "window_shift"),
     (r"attn_merge_kernel", "attn_merge"),
     (r"qlinear_kernel", "qlinear"),
     (r"embed_kernel", "embed_sum"),
@@ -98,6 +111,32 @@ def stats(csv_path, out_md, command):
         short = r["Name"].split("(")[0].replace("void ", "")
         lines.append(f"| {lib} | `{short}` | {r['Calls']} | {float(r['AverageNs']) / 1e3:.1f} | "
                      f"{float(r['MinNs']) / 1e3:.1f} | {float(r['MaxNs']) / 1e3:.1f} |")
+    open(out_md, "w").write("\n".join(lines) + "\n")
+
+
+def by_launch_shape(trace_csv, out_md, command, kernels):
+    """Per (library kernel, grid) durations from a rocprofv3 kernel trace,
+    for the kernels named in `kernels`: one row per launch shape (the grid
+    identifies the problem size of a sweep), calls, average, min and max."""
+    rows = list(csv.DictReader(open(_csv(trace_csv, "kernel_trace.csv"))))
+    groups = {}
+    for r in rows:
+        lib = lib_kernel(r["Kernel_Name"])
+        if lib not in kernels:
+            continue
+        wg = int(r["Workgroup_Size_X"])
+        grid = (int(r["Grid_Size_X"]) // max(wg, 1), int(r["Grid_Size_Y"]), int(r["Grid_Size_Z"]))
+        short = r["Kernel_Name"].split("(")[0].replace("void ", "")
+        us = (int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) / 1e3
+        groups.setdefault((lib, short, grid, wg), []).append(us)
+    lines = ["# rocprofv3 kernel durations by launch shape\n", f"Command:\n\n```\n{command}\n```\n",
+             "One row per (kernel instance, grid); problem sizes that launch the same grid share a row "
+             "(their average mixes them; min and max bound each).\n",
+             "| library kernel | rocprof name | workgroups (x, y, z) | threads | calls | avg us | min us | max us |",
+             "|---|---|---|---|---|---|---|---|"]
+    for (lib, short, grid, wg), v in sorted(groups.items()):
+        lines.append(f"| {lib} | `{short}` | {grid[0]}, {grid[1]}, {grid[2]} | {wg} | {len(v)} | "
+                     f"{statistics.mean(v):.1f} | {min(v):.1f} | {max(v):.1f} |")
     open(out_md, "w").write("\n".join(lines) + "\n")
 
 
@@ -193,6 +232,11 @@ def main():
     b.add_argument("write_dir")
     b.add_argument("out")
     b.add_argument("--command", required=True)
+    s = sub.add_parser("shapes")
+    s.add_argument("trace")
+    s.add_argument("out")
+    s.add_argument("--kernels", required=True, help="comma-separated library kernel names")
+    s.add_argument("--command", required=True)
     c = sub.add_parser("counters")
     c.add_argument("stats")
     c.add_argument("dirs", nargs="+", help="counter pass directories, then the output .md")
@@ -200,6 +244,8 @@ def main():
     args = ap.parse_args()
     if args.cmd == "stats":
         stats(args.csv, args.out, args.command)
+    elif args.cmd == "shapes":
+        by_launch_shape(args.trace, args.out, args.command, set(args.kernels.split(",")))
     elif args.cmd == "pmc":
         pmc(args.fetch_dir, args.write_dir, args.out, args.command)
     else:
