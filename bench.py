@@ -350,8 +350,9 @@ PEAK_FP8_TFLOPS = 5000.0                # dense FP8 MFMA peak of the chip
 
 
 def prefill_gemm_sweep(torch, ops):
-    """fp8_gemm_mx_packed (and the row-major fp8_gemm_mx) on the pages'
-    square shapes and on the MLP's prefill shapes at M = 4096, operands
+    """fp8_gemm_mx_packed (and the row-major fp8_gemm_mx, and the bsgemm
+    fp8_gemm_bs_packed) on the pages' square shapes and on the MLP's prefill
+    shapes at M = 4096, operands
     quantised from seeded bf16 and packed outside the timed loop (packing
     the activation is timed on its own): TFLOP/s and fraction of the dense
     FP8 peak."""
@@ -364,13 +365,17 @@ def prefill_gemm_sweep(torch, ops):
         b = (torch.randn((N, K), generator=g, device="cuda") * 0.02).to(torch.bfloat16)
         qa, ea = ops.qlinear_quantize(a, ops.Q_MX_1x32)
         qb, eb = ops.qlinear_quantize(b, ops.Q_MX_1x32)
+        qa_bs, sa_bs = ops.qlinear_quantize(a, ops.Q_ACT_1x128)
+        qb_bs, sb_bs = ops.qlinear_quantize(b, ops.Q_WGT_128x128)
         del a, b
         pa, pb = ops.fp8_pack_mx(qa, ea), ops.fp8_pack_mx(qb, eb)
+        pa_bs, pb_bs = ops.fp8_pack_bs(qa_bs, sa_bs, 1), ops.fp8_pack_bs(qb_bs, sb_bs, 128)
         c = torch.empty((M, N), dtype=torch.bfloat16, device="cuda")
         n = max(3, min(30, int(2e12 / (2 * M * N * K))))
         res = {}
         for name, fn in (("packed", lambda: ops.fp8_gemm_mx_packed(pa, pb, c)),
                          ("row_major", lambda: ops.fp8_gemm_mx(qa, ea, qb, eb, c)),
+                         ("bsgemm_packed", lambda: ops.fp8_gemm_bs_packed(pa_bs, pb_bs, c)),
                          ("pack_activation", lambda: ops.fp8_pack_mx(qa, ea))):
             for _ in range(2):
                 fn()
@@ -388,8 +393,9 @@ def prefill_gemm_sweep(torch, ops):
                 res[name].update({"TFLOP/s": tf, "frac": tf / PEAK_FP8_TFLOPS})
         out[f"{M}x{N}x{K}"] = res
         log(f"gemm mx {M}x{N}x{K}: packed {res['packed']['us']:.1f} us {res['packed']['TFLOP/s']:.0f} TFLOP/s, "
-            f"row-major {res['row_major']['TFLOP/s']:.0f}, pack A {res['pack_activation']['us']:.1f} us")
-        del qa, ea, qb, eb, pa, pb, c
+            f"row-major {res['row_major']['TFLOP/s']:.0f}, bsgemm packed {res['bsgemm_packed']['TFLOP/s']:.0f}, "
+            f"pack A {res['pack_activation']['us']:.1f} us")
+        del qa, ea, qb, eb, pa, pb, qa_bs, sa_bs, qb_bs, sb_bs, pa_bs, pb_bs, c
         torch.cuda.empty_cache()
     return out
 

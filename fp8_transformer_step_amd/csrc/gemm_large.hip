@@ -26,6 +26,7 @@
 //     walked in groups of 8 tile rows, so each XCD's L2 holds the A rows and
 //     B columns its tiles share.
 #include <algorithm>
+#include <type_traits>
 
 #include "common.h"
 #include "gemm_tiles.h"
@@ -69,8 +70,19 @@ __device__ __forceinline__ void st_frag(uint8_t* frag, const v8i& r, int lane) {
 // PACKED: A and B come in the packed operand layout of fp8_pack_mx
 // (fragments and exponents in MFMA lane order, so every load is one
 // contiguous KiB and each lane's four exponents of an operand are one dword).
-template <bool PACKED>
+// BS (bsgemm, packed only): fp32 scales instead of UE8M0 exponents -- 1x128
+// per activation row and 128x128 per weight block, stored per row by
+// fp8_pack_bs; each 128-K MFMA runs with unit scales and its result is
+// added to the accumulator times (row scale x block scale).
+struct BsScales {
+    float4 a[4];      // scales of this lane's rows 16 i + 4 (lane / 16) + r of its 4 A tiles
+    float b;          // the block scale of the wave's 64 B rows
+};
+
+template <bool PACKED, bool BS>
 __global__ __launch_bounds__(256, 2) void gemm_large_mx_kernel(GemmLargeArgs a) {
+    static_assert(PACKED || !BS, "bsgemm operands come packed");
+    using Sc = typename std::conditional<BS, BsScales, v8i>::type;
     __shared__ __attribute__((aligned(1024))) uint8_t smem[2 * kGlStage];
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
     const int wm = wave >> 1, wn = wave & 1;
@@ -132,7 +144,17 @@ __global__ __launch_bounds__(256, 2) void gemm_large_mx_kernel(GemmLargeArgs a) 
     // ((group * KB + kb) * 64 + lane) * 4
     const uint32_t* pea = reinterpret_cast<const uint32_t*>(a.ae) + (uint32_t)((m0 / 64 + wm) * a.KB) * 64 + lane;
     const uint32_t* peb = reinterpret_cast<const uint32_t*>(a.be) + (uint32_t)((n0 / 64 + wn) * a.KB) * 64 + lane;
-    auto exps = [&](int kb) {
+    // bsgemm packed scales: 64 fp32 per (64-row group, K block), row order
+    const float* psa = reinterpret_cast<const float*>(a.ae) + (uint32_t)((m0 / 64 + wm) * a.KB) * 64 + 4 * g4;
+    const float* psb = reinterpret_cast<const float*>(a.be) + (uint32_t)((n0 / 64 + wn) * a.KB) * 64;
+    auto exps = [&](int kb) -> Sc {
+        if constexpr (BS) {
+            BsScales sc;
+#pragma unroll
+            for (int i = 0; i < 4; ++i) sc.a[i] = *reinterpret_cast<const float4*>(psa + kb * 64 + 16 * i);
+            sc.b = psb[kb * 64];
+            return sc;
+        } else {
         v8i e;
         if (PACKED) {
             const uint32_t wa = pea[kb * 64], wb = peb[kb * 64];
@@ -151,21 +173,42 @@ __global__ __launch_bounds__(256, 2) void gemm_large_mx_kernel(GemmLargeArgs a) 
             e[4 + i] = a.be[offb[i] + gb];
         }
         return e;
+        }
     };
     v4f acc[4][4];
 #pragma unroll
     for (int i = 0; i < 4; ++i)
 #pragma unroll
         for (int j = 0; j < 4; ++j) acc[i][j] = v4f{0, 0, 0, 0};
-    auto compute = [&](const uint8_t* s, const v8i& e) {
+    auto compute = [&](const uint8_t* s, const Sc& e) {
         v8i af[4];
 #pragma unroll
         for (int i = 0; i < 4; ++i) af[i] = lds_frag(s, (4 * wm + i) * kFrag, lane);
+        if constexpr (BS) {
+            float4 sc[4];
 #pragma unroll
-        for (int j = 0; j < 4; ++j) {
-            const v8i bf = lds_frag(s, (8 + 4 * wn + j) * kFrag, lane);
+            for (int i = 0; i < 4; ++i)
+                sc[i] = make_float4(e.a[i].x * e.b, e.a[i].y * e.b, e.a[i].z * e.b, e.a[i].w * e.b);
+            const v4f z = {0, 0, 0, 0};
 #pragma unroll
-            for (int i = 0; i < 4; ++i) acc[i][j] = mfma_fp8(af[i], bf, acc[i][j], e[i], e[4 + j]);
+            for (int j = 0; j < 4; ++j) {
+                const v8i bf = lds_frag(s, (8 + 4 * wn + j) * kFrag, lane);
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                    const v4f t = mfma_fp8(af[i], bf, z, kUnitScale, kUnitScale);
+                    acc[i][j][0] = fmaf(t[0], sc[i].x, acc[i][j][0]);
+                    acc[i][j][1] = fmaf(t[1], sc[i].y, acc[i][j][1]);
+                    acc[i][j][2] = fmaf(t[2], sc[i].z, acc[i][j][2]);
+                    acc[i][j][3] = fmaf(t[3], sc[i].w, acc[i][j][3]);
+                }
+            }
+        } else {
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                const v8i bf = lds_frag(s, (8 + 4 * wn + j) * kFrag, lane);
+#pragma unroll
+                for (int i = 0; i < 4; ++i) acc[i][j] = mfma_fp8(af[i], bf, acc[i][j], e[i], e[4 + j]);
+            }
         }
     };
     // LDS writes of this wave complete, then every wave meets: the stage just
@@ -182,7 +225,7 @@ __global__ __launch_bounds__(256, 2) void gemm_large_mx_kernel(GemmLargeArgs a) 
 
     const int KB = a.KB;
     gload(0);
-    v8i e_cur = exps(0), e_next = e_cur;
+    Sc e_cur = exps(0), e_next = e_cur;
     swrite(smem);
     if (KB > 1) {
         gload(1);
@@ -228,11 +271,15 @@ __global__ __launch_bounds__(256, 2) void gemm_large_mx_kernel(GemmLargeArgs a) 
 // exponents.
 struct PackArgs {
     const uint8_t* q; int64_t ldq;
-    const uint8_t* e; int64_t er, eg;
-    int R, KB, Rp;
+    const uint8_t* e; int64_t er, eg;         // MX exponents, or (BS) the fp32 scale matrix
+    int R, KB, Rp, rows_per_scale;            // BS: scale row of data row r = r / rows_per_scale
     uint8_t* out;
 };
 
+// BS: the scale region holds, per (64-row group G, kb), 64 fp32 at
+// R_pad * K + (G * KB + kb) * 256: row 64 G + r's scale of K block kb
+// (0 for padding rows).
+template <bool BS>
 __global__ __launch_bounds__(256) void pack_mx_kernel(PackArgs a) {
     const int64_t n_chunks = (int64_t)(a.Rp / 16) * a.KB * 128;   // 16-byte chunks: 128 per 2 KiB fragment
     const int64_t n_words = (int64_t)(a.Rp / 64) * a.KB * 64;
@@ -251,6 +298,14 @@ __global__ __launch_bounds__(256) void pack_mx_kernel(PackArgs a) {
         const int l = (int)(w % 64);
         const int64_t gk = w / 64;
         const int G = (int)(gk / a.KB), kb = (int)(gk % a.KB);
+        if (BS) {
+            const int row = 64 * G + l;
+            float v = 0.0f;
+            if (row < a.R)
+                v = reinterpret_cast<const float*>(a.e)[(int64_t)(row / a.rows_per_scale) * a.er + (int64_t)kb * a.eg];
+            reinterpret_cast<float*>(a.out + (int64_t)a.Rp * a.KB * 128)[w] = v;
+            return;
+        }
         uint32_t word = 0;
         for (int i = 0; i < 4; ++i) {
             const int row = 64 * G + 16 * i + (l & 15);
@@ -286,9 +341,10 @@ extern "C" int fp8_pack_mx(const uint8_t* q, int64_t ldq, const uint8_t* e, int6
     p.q = q; p.ldq = ldq; p.e = e; p.er = e_row; p.eg = e_grp;
     p.R = (int)R; p.KB = (int)(K / 128); p.Rp = (int)((R + 127) / 128 * 128);
     p.out = static_cast<uint8_t*>(packed);
+    p.rows_per_scale = 1;
     const int64_t n = (int64_t)(p.Rp / 16) * p.KB * 128 + (int64_t)(p.Rp / 64) * p.KB * 64;
     FP8S_REQUIRE((n + 255) / 256 < (1ll << 31), FP8S_EUNSUPPORTED, "fp8_pack_mx: too large");
-    FP8S_LAUNCH("pack_mx", pack_mx_kernel, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, as_stream(stream), p);
+    FP8S_LAUNCH("pack_mx", pack_mx_kernel<false>, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, as_stream(stream), p);
     return check_launch("fp8_pack_mx");
 }
 
@@ -311,7 +367,7 @@ extern "C" int fp8_gemm_mx_packed(const void* a_packed, const void* b_packed, in
     g.M = (int)M; g.N = (int)N; g.KB = (int)(K / 128);
     g.tiles_m = (int)tiles_m; g.tiles_n = (int)tiles_n;
     g.c = c; g.ldc = ldc;
-    FP8S_LAUNCH("gemm_large_mx", gemm_large_mx_kernel<true>, dim3((unsigned)(tiles_m * tiles_n)), dim3(256), 0,
+    FP8S_LAUNCH("gemm_large_mx", (gemm_large_mx_kernel<true, false>), dim3((unsigned)(tiles_m * tiles_n)), dim3(256), 0,
                 as_stream(stream), g);
     return check_launch("fp8_gemm_mx_packed");
 }
@@ -340,7 +396,62 @@ extern "C" int fp8_gemm_mx(const uint8_t* a, int64_t lda, const uint8_t* a_e, in
     g.M = (int)M; g.N = (int)N; g.KB = (int)(K / 128);
     g.tiles_m = (int)tiles_m; g.tiles_n = (int)tiles_n;
     g.c = c; g.ldc = ldc;
-    FP8S_LAUNCH("gemm_large_mx", gemm_large_mx_kernel<false>, dim3((unsigned)(tiles_m * tiles_n)), dim3(256), 0,
-                as_stream(stream), g);
+    FP8S_LAUNCH("gemm_large_mx", (gemm_large_mx_kernel<false, false>), dim3((unsigned)(tiles_m * tiles_n)), dim3(256),
+                0, as_stream(stream), g);
     return check_launch("fp8_gemm_mx");
+}
+
+extern "C" size_t fp8_bs_packed_bytes(int64_t R, int64_t K) {
+    if (R < 1 || K < 128 || K % 128 || R >= (1ll << 30) || K >= (1ll << 30)) return 0;
+    const int64_t Rp = (R + 127) / 128 * 128;
+    return (size_t)(Rp * K + Rp * (K / 128) * 4);
+}
+
+extern "C" int fp8_pack_bs(const uint8_t* q, int64_t ldq, const float* s, int64_t s_row, int64_t s_col,
+                           int32_t rows_per_scale, int64_t R, int64_t K, void* packed, size_t packed_bytes,
+                           void* stream) {
+    clear_error();
+    FP8S_REQUIRE(q && s && packed, FP8S_EINVAL, "fp8_pack_bs: null pointer");
+    FP8S_REQUIRE(R >= 1 && K >= 128 && K % 128 == 0 && R < (1ll << 30) && K < (1ll << 30), FP8S_EINVAL,
+                 "fp8_pack_bs: need R >= 1 and K a positive multiple of 128");
+    FP8S_REQUIRE(rows_per_scale == 1 || rows_per_scale == 128, FP8S_EINVAL,
+                 "fp8_pack_bs: rows_per_scale must be 1 (1x128 activation groups) or 128 (128x128 weight blocks)");
+    FP8S_REQUIRE(ldq >= K && ldq % 16 == 0 && aligned16(q) && aligned16(packed) &&
+                     (reinterpret_cast<uintptr_t>(s) & 3u) == 0,
+                 FP8S_EINVAL, "fp8_pack_bs: codes and output 16-byte aligned (ldq >= K, ldq % 16 == 0), scales 4-byte");
+    FP8S_REQUIRE(s_row >= 0 && s_col >= 0, FP8S_EINVAL, "fp8_pack_bs: scale strides must be non-negative");
+    FP8S_REQUIRE(packed_bytes >= fp8_bs_packed_bytes(R, K), FP8S_EWORKSPACE, "fp8_pack_bs: output %zu < %zu bytes",
+                 packed_bytes, fp8_bs_packed_bytes(R, K));
+    PackArgs p;
+    p.q = q; p.ldq = ldq; p.e = reinterpret_cast<const uint8_t*>(s); p.er = s_row; p.eg = s_col;
+    p.R = (int)R; p.KB = (int)(K / 128); p.Rp = (int)((R + 127) / 128 * 128); p.rows_per_scale = rows_per_scale;
+    p.out = static_cast<uint8_t*>(packed);
+    const int64_t n = (int64_t)(p.Rp / 16) * p.KB * 128 + (int64_t)(p.Rp / 64) * p.KB * 64;
+    FP8S_REQUIRE((n + 255) / 256 < (1ll << 31), FP8S_EUNSUPPORTED, "fp8_pack_bs: too large");
+    FP8S_LAUNCH("pack_bs", pack_mx_kernel<true>, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, as_stream(stream), p);
+    return check_launch("fp8_pack_bs");
+}
+
+extern "C" int fp8_gemm_bs_packed(const void* a_packed, const void* b_packed, int64_t M, int64_t N, int64_t K,
+                                  uint16_t* c, int64_t ldc, void* stream) {
+    clear_error();
+    FP8S_REQUIRE(a_packed && b_packed && c, FP8S_EINVAL, "fp8_gemm_bs_packed: null pointer");
+    FP8S_REQUIRE(M >= 1 && N >= 1 && K >= 128, FP8S_EINVAL, "fp8_gemm_bs_packed: sizes must be positive");
+    FP8S_REQUIRE(N % 128 == 0 && K % 128 == 0 && M < (1ll << 30) && N < (1ll << 30) && K < (1ll << 30),
+                 FP8S_EUNSUPPORTED, "fp8_gemm_bs_packed: N and K must be multiples of 128");
+    FP8S_REQUIRE(ldc >= N && ldc % 8 == 0 && aligned16(a_packed) && aligned16(b_packed) && aligned16(c), FP8S_EINVAL,
+                 "fp8_gemm_bs_packed: C must be 16-byte aligned with ldc >= N, ldc % 8 == 0; packed operands 16-byte aligned");
+    const int64_t Mp = (M + 127) / 128 * 128, tiles_m = Mp / kGlBM, tiles_n = N / kGlBN;
+    FP8S_REQUIRE(tiles_m * tiles_n < (1ll << 31), FP8S_EUNSUPPORTED, "fp8_gemm_bs_packed: too many tiles");
+    GemmLargeArgs g;
+    g.a = static_cast<const uint8_t*>(a_packed); g.lda = 0;
+    g.ae = g.a + Mp * K; g.ae_r = g.ae_g = 0;
+    g.b = static_cast<const uint8_t*>(b_packed); g.ldb = 0;
+    g.be = g.b + N * K; g.be_r = g.be_g = 0;
+    g.M = (int)M; g.N = (int)N; g.KB = (int)(K / 128);
+    g.tiles_m = (int)tiles_m; g.tiles_n = (int)tiles_n;
+    g.c = c; g.ldc = ldc;
+    FP8S_LAUNCH("gemm_large_bs", (gemm_large_mx_kernel<true, true>), dim3((unsigned)(tiles_m * tiles_n)), dim3(256), 0,
+                as_stream(stream), g);
+    return check_launch("fp8_gemm_bs_packed");
 }

@@ -358,6 +358,37 @@ def fp8_gemm_mx_packed(pa, pb, c=None):
     return c
 
 
+def fp8_pack_bs(q, s, rows_per_scale):
+    """Pack bsgemm codes q uint8 [R, K] with fp32 scales s (activation:
+    [R, K/128], rows_per_scale 1; weight: [R/128, K/128], rows_per_scale
+    128; any strides) for fp8_gemm_bs_packed."""
+    _require_cuda(q, s)
+    R, K = q.shape
+    if q.dtype != torch.uint8 or s.dtype != torch.float32 or q.stride(1) != 1:
+        raise ValueError("need q uint8 [R, K] with contiguous rows and fp32 scales")
+    if tuple(s.shape) != ((R + rows_per_scale - 1) // rows_per_scale, K // 128):
+        raise ValueError("scale shape does not match rows_per_scale")
+    n = int(_lib.load().fp8_bs_packed_bytes(R, K))
+    if n == 0:
+        raise ValueError("K must be a positive multiple of 128")
+    out = torch.empty(n, dtype=torch.uint8, device=q.device)
+    _lib.check(_lib.load().fp8_pack_bs(q.data_ptr(), q.stride(0), s.data_ptr(), s.stride(0), s.stride(1),
+                                       int(rows_per_scale), R, K, out.data_ptr(), n, _stream()))
+    return PackedMx(out, R, K)
+
+
+def fp8_gemm_bs_packed(pa, pb, c=None):
+    """C bf16 [M, N] from bsgemm operands packed by fp8_pack_bs."""
+    if pa.K != pb.K:
+        raise ValueError("operands must share K")
+    M, N, K = pa.rows, pb.rows, pa.K
+    if c is None:
+        c = torch.empty((M, N), dtype=torch.bfloat16, device=pa.data.device)
+    _lib.check(_lib.load().fp8_gemm_bs_packed(pa.data.data_ptr(), pb.data.data_ptr(), M, N, K, _bits(c),
+                                              c.stride(0), _stream()))
+    return c
+
+
 def sample_top_k_top_p(logits, uniforms, temperature=0.8, top_k=30, top_p=0.8, codes=None):
     """One token per row of fp32 logits [B, V] (unit stride along V) with
     the caller's uniforms [B] fp32 in [0, 1); returns int32 codes [B]."""

@@ -428,6 +428,31 @@ FP8S_API int fp8_gemm_mx_packed(const void* a_packed, const void* b_packed, int6
                     uint16_t* c, int64_t ldc, void* stream);
 
 /*
+ * fp8_pack_bs / fp8_gemm_bs_packed -- the prefill GEMM for bsgemm operands
+ * ([TTS] "FP8 Quantization Strategy": 128x128 block-scaled FP8, the config
+ * of the decode step's weights): C[m, n] = bf16( sum_kb s_a[m, kb] s_b[n/128,
+ * kb] sum_{k in kb} qa[m,k] qb[n,k] ), fp32 accumulation.
+ *   fp8_bs_packed_bytes(R, K): bytes of a packed [R, K] operand.
+ *   fp8_pack_bs: q e4m3 [R, K] (row stride ldq) and fp32 scales s, scale of
+ *   (row r, K block kb) at (r / rows_per_scale) * s_row + kb * s_col:
+ *   rows_per_scale = 1 for 1x128 activation groups (qlinear_quantize mode
+ *   0), 128 for 128x128 weight blocks (mode 1).  Packed: the fragments of
+ *   fp8_pack_mx, then 64 fp32 per (64-row group G, kb) at R_pad * K +
+ *   (G * K/128 + kb) * 256, the scales of rows 64 G .. 64 G + 63 in order
+ *   (0 for padding rows).
+ *   fp8_gemm_bs_packed: C [M, N] bf16 from packed A (R = M, activation
+ *   scales) and packed B (R = N, a multiple of 128, weight scales).
+ *   Accuracy: max|C - oracle| <= 2e-2 * max|oracle| (exact when every
+ *   partial sum is).
+ */
+FP8S_API size_t fp8_bs_packed_bytes(int64_t R, int64_t K);
+FP8S_API int fp8_pack_bs(const uint8_t* q, int64_t ldq, const float* s, int64_t s_row, int64_t s_col,
+                    int32_t rows_per_scale, int64_t R, int64_t K, void* packed, size_t packed_bytes,
+                    void* stream);
+FP8S_API int fp8_gemm_bs_packed(const void* a_packed, const void* b_packed, int64_t M, int64_t N, int64_t K,
+                    uint16_t* c, int64_t ldc, void* stream);
+
+/*
  * sample_top_k_top_p -- one token per row drawn from fp32 logits with
  * temperature, top-k and top-p ([KV] section 6: the benchmark generation
  * samples with temperature 0.8, top_p 0.8, top_k 30 under a fixed seed;

@@ -184,3 +184,65 @@ def test_packed_full_size_sampled_rows():
     oqa, oea = ofp8.quant_mx_1x32(f32(a[rows]))
     ref = ofp8.dequant_mx_1x32(oqa, oea) @ ofp8.dequant_mx_1x32(oqb, oeb).T
     assert max_rel_err(from_dev_bf16(c[torch.from_numpy(rows).cuda()]), ref) <= TOL_FP8_PATH
+
+
+# ---- bsgemm (128x128 weight blocks, 1x128 activation groups), packed ----
+
+def _bs_run(a_bits, b_bits):
+    qa, sa = ops.qlinear_quantize(to_dev_bf16(a_bits), ops.Q_ACT_1x128)
+    qb, sb = ops.qlinear_quantize(to_dev_bf16(b_bits), ops.Q_WGT_128x128)
+    c = ops.fp8_gemm_bs_packed(ops.fp8_pack_bs(qa, sa, 1), ops.fp8_pack_bs(qb, sb, 128))
+    torch.cuda.synchronize()
+    return qa, sa, qb, sb, c
+
+
+@pytest.mark.parametrize("M,N,K", [(128, 128, 128), (1000, 256, 384), (1, 128, 256), (77, 640, 1280)])
+def test_bs_packed_matches_oracle(M, N, K):
+    need_gpu()
+    a, b = _operands(M, N, K, extra=500 + M + N + K)
+    qa, sa, qb, sb, c = _bs_run(a, b)
+    oqa, osa = ofp8.quant_act_1x128(f32(a))
+    oqb, osb = ofp8.quant_weight_128x128(f32(b))
+    assert np.array_equal(qa.cpu().numpy(), oqa) and np.array_equal(sa.cpu().numpy(), osa)
+    assert np.array_equal(qb.cpu().numpy(), oqb) and np.array_equal(sb.cpu().numpy(), osb)
+    ref = ofp8.dequant_block_fp32(oqa, osa, 1, 128) @ ofp8.dequant_block_fp32(oqb, osb, 128, 128).T
+    e = max_rel_err(from_dev_bf16(c), ref)
+    log(f"gemm bs {M}x{N}x{K}: max rel err {e:.2e}")
+    assert e <= TOL_FP8_PATH
+
+
+def test_bs_packed_full_size_sampled_rows():
+    need_gpu()
+    M = N = K = 4096
+    a, b = _operands(M, N, K, extra=4098)
+    c = _bs_run(a, b)[4]
+    rows = np.unique(np.concatenate([[0, M - 1], np.random.default_rng(8).integers(0, M, 46)]))
+    oqb, osb = ofp8.quant_weight_128x128(f32(b))
+    oqa, osa = ofp8.quant_act_1x128(f32(a[rows]))
+    ref = ofp8.dequant_block_fp32(oqa, osa, 1, 128) @ ofp8.dequant_block_fp32(oqb, osb, 128, 128).T
+    assert max_rel_err(from_dev_bf16(c[torch.from_numpy(rows).cuda()]), ref) <= TOL_FP8_PATH
+
+
+def test_bs_exact_small_codes_bit_for_bit():
+    """Codes of +-{0, 0.5, 1, 1.5, 2} with a power-of-two scale in [2^-2, 2^2]
+    per activation (row, K block) and per weight block: every product is a
+    multiple of 2^-6 at most 64 in magnitude, partial sums over K = 512 stay
+    below 2^15, so C must be the bf16 rounding of the exact product; a
+    wrong row, block or K-block scale index breaks it."""
+    need_gpu()
+    g = np.random.default_rng(12)
+    M, N, K = 160, 256, 512
+    codes = np.array([0x00, 0x30, 0x38, 0x3C, 0x40, 0xB0, 0xB8, 0xBC, 0xC0], np.uint8)
+    qa = codes[g.integers(0, len(codes), (M, K))]
+    qb = codes[g.integers(0, len(codes), (N, K))]
+    sa = np.ldexp(1.0, g.integers(-2, 3, (M, K // 128))).astype(np.float32)
+    sb = np.ldexp(1.0, g.integers(-2, 3, (N // 128, K // 128))).astype(np.float32)
+    ref = round_bf16(ofp8.dequant_block_fp32(qa, sa, 1, 128) @ ofp8.dequant_block_fp32(qb, sb, 128, 128).T)
+    d = lambda x: torch.from_numpy(np.ascontiguousarray(x)).cuda()
+    sa_km = torch.from_numpy(np.ascontiguousarray(sa.T)).cuda().t()          # K-major activation scales
+    c = ops.fp8_gemm_bs_packed(ops.fp8_pack_bs(d(qa), sa_km, 1), ops.fp8_pack_bs(d(qb), d(sb), 128))
+    torch.cuda.synchronize()
+    assert np.array_equal(from_dev_bf16(c), ref)
+    c2 = ops.fp8_gemm_bs_packed(ops.fp8_pack_bs(d(qa), d(sa[::-1].copy()), 1), ops.fp8_pack_bs(d(qb), d(sb), 128))
+    torch.cuda.synchronize()
+    assert not np.array_equal(from_dev_bf16(c2), ref)
