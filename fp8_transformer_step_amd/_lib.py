@@ -69,6 +69,9 @@ SIGNATURES = {
                                    c_i64, c_vp, c_i64, c_vp]),
     "extend_attn": (ctypes.c_int, [c_vp, c_vp, c_i64, c_vp, c_vp, c_i64, c_i64, c_i64, c_vp, c_i64, c_i32, c_i32,
                                    c_i32, c_i64, c_i64, ctypes.c_float, c_vp, c_vp, c_vp]),
+    "extend_attn_paged": (ctypes.c_int, [c_vp, c_vp, c_i64, c_vp, c_vp, c_i64, c_i64, c_i64, c_i64, c_i32, c_vp,
+                                         c_i64, c_i64, c_vp, c_i64, c_i32, c_i32, c_i32, c_i64, ctypes.c_float, c_vp,
+                                         c_vp, c_vp]),
     "fp8_mx_packed_bytes": (c_sz, [c_i64, c_i64]),
     "fp8_pack_mx": (ctypes.c_int, [c_vp, c_i64, c_vp, c_i64, c_i64, c_i64, c_i64, c_vp, c_sz, c_vp]),
     "fp8_gemm_mx_packed": (ctypes.c_int, [c_vp, c_vp, c_i64, c_i64, c_i64, c_vp, c_i64, c_vp]),

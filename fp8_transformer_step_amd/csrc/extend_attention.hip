@@ -56,9 +56,17 @@ struct ExtendArgs {
     float scale_log2;
     uint16_t* out;
     int32_t* err;
+    // paged pools (bt non-null): sb is the page stride; the pages of sequence
+    // b are bt[b * bt_stride + i], valid ids 0 .. n_pages - 1
+    const int32_t* bt;
+    int64_t bt_stride, n_pages;
+    int page_log2;
 };
 
-template <int G, int QS>
+// PAGED: position p of sequence b is slot p % P of page bt[b][p / P]; a page
+// id outside the pool makes the workgroup read nothing from it, write zeros
+// for its rows and report FP8S_DEV_PAGE_RANGE.
+template <int G, int QS, bool PAGED>
 __global__ __launch_bounds__(ex_threads<QS>()) void extend_attn_kernel(ExtendArgs a) {
     constexpr int HPW = (G + 3) / 4;      // query heads per wave
     constexpr int kThreads = ex_threads<QS>(), kTokens = 16 * QS;
@@ -117,8 +125,26 @@ __global__ __launch_bounds__(ex_threads<QS>()) void extend_attn_kernel(ExtendArg
         for (int dt = 0; dt < 8; ++dt) o[hh][dt] = v4f{0, 0, 0, 0};
     }
 
-    const uint16_t* kbase = a.k + (int64_t)b * a.sb + (int64_t)g * a.sh;
-    const uint16_t* vbase = a.v + (int64_t)b * a.sb + (int64_t)g * a.sh;
+    const uint16_t* kbase = a.k + (PAGED ? 0 : (int64_t)b * a.sb) + (int64_t)g * a.sh;
+    const uint16_t* vbase = a.v + (PAGED ? 0 : (int64_t)b * a.sb) + (int64_t)g * a.sh;
+    __shared__ int s_bad;
+    if (PAGED) {
+        if (threadIdx.x == 0) s_bad = 0;
+        __syncthreads();
+    }
+    // element offset of cache row p (a valid position of sequence b)
+    auto row_of = [&](int p, bool& bad) -> int64_t {
+        if constexpr (PAGED) {
+            const int pg = a.bt[(int64_t)b * a.bt_stride + (p >> a.page_log2)];
+            if (pg < 0 || (int64_t)pg >= a.n_pages) {
+                bad = true;
+                return -1;
+            }
+            return (int64_t)pg * a.sb + (int64_t)(p & ((1 << a.page_log2) - 1)) * a.st;
+        } else {
+            return (int64_t)p * a.st;
+        }
+    };
     // staging: 512 chunks of 8 K values and the matching 8 V values per
     // block, CH per thread (chunk c = threadIdx.x + i * kThreads < 512); the
     // next block's chunks are loaded into registers before the current block
@@ -133,8 +159,14 @@ __global__ __launch_bounds__(ex_threads<QS>()) void extend_attn_kernel(ExtendArg
             kw[i] = make_uint4(0, 0, 0, 0);
             vw[i] = make_uint4(0, 0, 0, 0);
             if (c < kExKV * kExD / 8 && p0 + pr < L) {            // never read past kv_len
-                kw[i] = *reinterpret_cast<const uint4*>(kbase + (int64_t)(p0 + pr) * a.st + d0);
-                vw[i] = *reinterpret_cast<const uint4*>(vbase + (int64_t)(p0 + pr) * a.st + d0);
+                bool bad = false;
+                const int64_t ro = row_of(p0 + pr, bad);
+                if (bad) {
+                    s_bad = 1;                                    // read nothing from a bad page
+                } else {
+                    kw[i] = *reinterpret_cast<const uint4*>(kbase + ro + d0);
+                    vw[i] = *reinterpret_cast<const uint4*>(vbase + ro + d0);
+                }
             }
         }
     };
@@ -233,6 +265,17 @@ __global__ __launch_bounds__(ex_threads<QS>()) void extend_attn_kernel(ExtendArg
         __syncthreads();                  // the stage is rewritten next
     }
 
+    if (PAGED) {
+        __syncthreads();                  // every fetch has recorded its page check
+        if (s_bad) {
+            if (threadIdx.x == 0) report_error(a.err, FP8S_DEV_PAGE_RANGE);
+            for (int e = threadIdx.x; e < kTokens * G * kExD; e += kThreads) {
+                const int r = e / (G * kExD), c = e % (G * kExD);
+                if (t0 + r < T) a.out[((int64_t)(q0 + t0 + r) * a.Hq + g * G) * kExD + c] = 0;
+            }
+            return;
+        }
+    }
     // normalise and store: lane holds O[query 4 g4 + r][16 dt + ql]
 #pragma unroll
     for (int hh = 0; hh < HPW; ++hh) {
@@ -256,42 +299,103 @@ __global__ __launch_bounds__(ex_threads<QS>()) void extend_attn_kernel(ExtendArg
 
 using namespace fp8s;
 
+static int extend_launch(const ExtendArgs& a, int G, int64_t hint, void* stream) {
+    const int QS = hint <= 16 ? 1 : (G == 8 ? 2 : 4);
+    const int64_t n_qblk = (hint + 16 * QS - 1) / (16 * QS);
+    if (a.B * n_qblk >= (1ll << 31)) return FP8S_EUNSUPPORTED;
+    ExtendArgs b = a;
+    b.n_qblk = (int)n_qblk;
+    const dim3 grid((unsigned)(a.B * n_qblk), (unsigned)a.Hkv);
+    const hipStream_t st = as_stream(stream);
+    const bool paged = a.bt != nullptr;
+#define FP8S_EX_CASE(GG, QQ)                                                                                     \
+    if (G == GG && QS == QQ) {                                                                                   \
+        if (paged)                                                                                               \
+            FP8S_LAUNCH("extend_attn_paged", (extend_attn_kernel<GG, QQ, true>), grid, dim3(ex_threads<QQ>()), 0, \
+                        st, b);                                                                                  \
+        else                                                                                                     \
+            FP8S_LAUNCH("extend_attn", (extend_attn_kernel<GG, QQ, false>), grid, dim3(ex_threads<QQ>()), 0, st, \
+                        b);                                                                                      \
+    }
+    FP8S_EX_CASE(1, 1) FP8S_EX_CASE(1, 4) FP8S_EX_CASE(2, 1) FP8S_EX_CASE(2, 4)
+    FP8S_EX_CASE(4, 1) FP8S_EX_CASE(4, 4) FP8S_EX_CASE(8, 1) FP8S_EX_CASE(8, 2)
+#undef FP8S_EX_CASE
+    return check_launch(paged ? "extend_attn_paged" : "extend_attn");
+}
+
+// The checks shared by both entry points; fills everything but the cache
+// addressing.
+static int extend_common(const char* fn, ExtendArgs& a, const uint16_t* q, const int32_t* q_start,
+                         int64_t total_tokens, const uint16_t* k, const uint16_t* v, int64_t stride_h,
+                         int64_t stride_t, const int32_t* kv_len, int64_t B, int32_t Hq, int32_t Hkv, int32_t D,
+                         int64_t cap, int64_t* hint, float softmax_scale, uint16_t* out, int32_t* err_flag) {
+    FP8S_REQUIRE(q && q_start && k && v && kv_len && out, FP8S_EINVAL, "%s: null pointer", fn);
+    FP8S_REQUIRE(B >= 1 && Hq >= 1 && Hkv >= 1 && cap >= 1 && *hint >= 1 && total_tokens >= 1, FP8S_EINVAL,
+                 "%s: sizes must be positive", fn);
+    FP8S_REQUIRE(Hq % Hkv == 0, FP8S_EINVAL, "%s: Hq=%d is not a multiple of Hkv=%d", fn, Hq, Hkv);
+    const int G = Hq / Hkv;
+    FP8S_REQUIRE(D == kExD, FP8S_EUNSUPPORTED, "%s: head dim %d (128 supported)", fn, D);
+    FP8S_REQUIRE(G == 1 || G == 2 || G == 4 || G == 8, FP8S_EUNSUPPORTED, "%s: group size %d (1, 2, 4 or 8)", fn, G);
+    FP8S_REQUIRE(stride_t >= D && stride_t % 8 == 0 && stride_h % 8 == 0, FP8S_EINVAL,
+                 "%s: strides must keep rows 16-byte aligned (multiples of 8) and stride_t >= D", fn);
+    FP8S_REQUIRE(aligned16(q) && aligned16(k) && aligned16(v) && aligned16(out), FP8S_EINVAL,
+                 "%s: q, caches and out must be 16-byte aligned", fn);
+    FP8S_REQUIRE(total_tokens < (1ll << 31) && cap < (1ll << 31) && Hkv < 65536, FP8S_EUNSUPPORTED, "%s: too large",
+                 fn);
+    if (*hint > cap) *hint = cap;
+    a.q = q; a.q_start = q_start; a.k = k; a.v = v;
+    a.sh = stride_h; a.st = stride_t;
+    a.kv_len = kv_len;
+    a.B = (int)B; a.Hq = Hq; a.Hkv = Hkv; a.G = G; a.n_qblk = 0;
+    a.total = total_tokens; a.cap = cap; a.hint = *hint;
+    a.scale_log2 = softmax_scale * 1.4426950408889634f;
+    a.out = out; a.err = err_flag;
+    a.bt = nullptr; a.bt_stride = 0; a.n_pages = 0; a.page_log2 = 0;
+    return FP8S_OK;
+}
+
 extern "C" int extend_attn(const uint16_t* q, const int32_t* q_start, int64_t total_tokens, const uint16_t* k_cache,
                            const uint16_t* v_cache, int64_t stride_b, int64_t stride_h, int64_t stride_t,
                            const int32_t* kv_len, int64_t B, int32_t Hq, int32_t Hkv, int32_t D, int64_t cap,
                            int64_t max_new_hint, float softmax_scale, uint16_t* out, int32_t* err_flag, void* stream) {
     clear_error();
-    FP8S_REQUIRE(q && q_start && k_cache && v_cache && kv_len && out, FP8S_EINVAL, "extend_attn: null pointer");
-    FP8S_REQUIRE(B >= 1 && Hq >= 1 && Hkv >= 1 && cap >= 1 && max_new_hint >= 1 && total_tokens >= 1, FP8S_EINVAL,
-                 "extend_attn: sizes must be positive");
-    FP8S_REQUIRE(Hq % Hkv == 0, FP8S_EINVAL, "extend_attn: Hq=%d is not a multiple of Hkv=%d", Hq, Hkv);
-    const int G = Hq / Hkv;
-    FP8S_REQUIRE(D == kExD, FP8S_EUNSUPPORTED, "extend_attn: head dim %d (128 supported)", D);
-    FP8S_REQUIRE(G == 1 || G == 2 || G == 4 || G == 8, FP8S_EUNSUPPORTED,
-                 "extend_attn: group size %d (1, 2, 4 or 8 supported)", G);
-    FP8S_REQUIRE(stride_t >= D && stride_t % 8 == 0 && stride_h % 8 == 0 && stride_b % 8 == 0, FP8S_EINVAL,
-                 "extend_attn: strides must keep rows 16-byte aligned (multiples of 8) and stride_t >= D");
-    FP8S_REQUIRE(aligned16(q) && aligned16(k_cache) && aligned16(v_cache) && aligned16(out), FP8S_EINVAL,
-                 "extend_attn: q, caches and out must be 16-byte aligned");
-    FP8S_REQUIRE(total_tokens < (1ll << 31) && cap < (1ll << 31), FP8S_EUNSUPPORTED, "extend_attn: too large");
-    if (max_new_hint > cap) max_new_hint = cap;
-    const int QS = max_new_hint <= 16 ? 1 : (G == 8 ? 2 : 4);
-    const int64_t n_qblk = (max_new_hint + 16 * QS - 1) / (16 * QS);
-    FP8S_REQUIRE(B * n_qblk < (1ll << 31) && Hkv < 65536, FP8S_EUNSUPPORTED, "extend_attn: grid too large");
     ExtendArgs a;
-    a.q = q; a.q_start = q_start; a.k = k_cache; a.v = v_cache;
-    a.sb = stride_b; a.sh = stride_h; a.st = stride_t;
-    a.kv_len = kv_len;
-    a.B = (int)B; a.Hq = Hq; a.Hkv = Hkv; a.G = G; a.n_qblk = (int)n_qblk;
-    a.total = total_tokens; a.cap = cap; a.hint = max_new_hint;
-    a.scale_log2 = softmax_scale * 1.4426950408889634f;
-    a.out = out; a.err = err_flag;
-    const dim3 grid((unsigned)(B * n_qblk), (unsigned)Hkv);
-    const hipStream_t st = as_stream(stream);
-#define FP8S_EX_CASE(GG, QQ)                                                                             \
-    if (G == GG && QS == QQ) FP8S_LAUNCH("extend_attn", (extend_attn_kernel<GG, QQ>), grid, dim3(ex_threads<QQ>()), 0, st, a);
-    FP8S_EX_CASE(1, 1) FP8S_EX_CASE(1, 4) FP8S_EX_CASE(2, 1) FP8S_EX_CASE(2, 4)
-    FP8S_EX_CASE(4, 1) FP8S_EX_CASE(4, 4) FP8S_EX_CASE(8, 1) FP8S_EX_CASE(8, 2)
-#undef FP8S_EX_CASE
-    return check_launch("extend_attn");
+    int rc = extend_common("extend_attn", a, q, q_start, total_tokens, k_cache, v_cache, stride_h, stride_t, kv_len,
+                           B, Hq, Hkv, D, cap, &max_new_hint, softmax_scale, out, err_flag);
+    if (rc) return rc;
+    FP8S_REQUIRE(stride_b % 8 == 0, FP8S_EINVAL, "extend_attn: stride_b must be a multiple of 8");
+    a.sb = stride_b;
+    rc = extend_launch(a, a.G, max_new_hint, stream);
+    FP8S_REQUIRE(rc != FP8S_EUNSUPPORTED, FP8S_EUNSUPPORTED, "extend_attn: grid too large");
+    return rc;
+}
+
+extern "C" int extend_attn_paged(const uint16_t* q, const int32_t* q_start, int64_t total_tokens,
+                                 const uint16_t* k_pool, const uint16_t* v_pool, int64_t stride_page,
+                                 int64_t stride_h, int64_t stride_t, int64_t num_pages, int32_t page_size,
+                                 const int32_t* block_table, int64_t bt_stride, int64_t max_pages_per_seq,
+                                 const int32_t* kv_len, int64_t B, int32_t Hq, int32_t Hkv, int32_t D,
+                                 int64_t max_new_hint, float softmax_scale, uint16_t* out, int32_t* err_flag,
+                                 void* stream) {
+    clear_error();
+    FP8S_REQUIRE(block_table, FP8S_EINVAL, "extend_attn_paged: null block table");
+    FP8S_REQUIRE(page_size >= 16 && page_size <= (1 << 20) && (page_size & (page_size - 1)) == 0, FP8S_EUNSUPPORTED,
+                 "extend_attn_paged: page size %d (a power of two from 16 to 2^20)", page_size);
+    FP8S_REQUIRE(num_pages >= 1 && num_pages < (1ll << 31) && max_pages_per_seq >= 1 &&
+                     bt_stride >= max_pages_per_seq && max_pages_per_seq <= (1ll << 31) / page_size,
+                 FP8S_EINVAL, "extend_attn_paged: need 1 <= max_pages_per_seq <= bt_stride, 1 <= num_pages < 2^31");
+    FP8S_REQUIRE(stride_page % 8 == 0 && stride_page >= 0, FP8S_EINVAL,
+                 "extend_attn_paged: page stride must be a non-negative multiple of 8");
+    ExtendArgs a;
+    const int64_t cap = max_pages_per_seq * page_size;
+    int rc = extend_common("extend_attn_paged", a, q, q_start, total_tokens, k_pool, v_pool, stride_h, stride_t,
+                           kv_len, B, Hq, Hkv, D, cap, &max_new_hint, softmax_scale, out, err_flag);
+    if (rc) return rc;
+    int lg = 0;
+    while ((1 << lg) < page_size) ++lg;
+    a.sb = stride_page;
+    a.bt = block_table; a.bt_stride = bt_stride; a.n_pages = num_pages; a.page_log2 = lg;
+    rc = extend_launch(a, a.G, max_new_hint, stream);
+    FP8S_REQUIRE(rc != FP8S_EUNSUPPORTED, FP8S_EUNSUPPORTED, "extend_attn_paged: grid too large");
+    return rc;
 }

@@ -322,6 +322,33 @@ def extend_attn(q, q_start, k_cache, v_cache, kv_len, max_new_hint, softmax_scal
     return out
 
 
+def extend_attn_paged(q, q_start, k_pool, v_pool, block_table, kv_len, max_new_hint, softmax_scale=None, out=None,
+                      err=None):
+    """extend_attn over paged caches: k_pool, v_pool indexed (page, kv
+    head, slot, d) as in gqa_decode_attn_paged."""
+    _require_cuda(q, q_start, k_pool, v_pool, block_table, kv_len)
+    if q_start.dtype != torch.int32 or kv_len.dtype != torch.int32:
+        raise TypeError("q_start and kv_len must be int32")
+    if k_pool.stride() != v_pool.stride() or k_pool.shape != v_pool.shape or k_pool.stride(3) != 1:
+        raise ValueError("k_pool and v_pool must share shape and strides, D contiguous")
+    total, Hq, D = q.shape
+    n_pages, Hkv, P, _ = k_pool.shape
+    B = kv_len.shape[0]
+    _check_block_table(block_table, B)
+    if q_start.shape != (B + 1,):
+        raise ValueError("q_start must be [B + 1]")
+    if softmax_scale is None:
+        softmax_scale = 1.0 / math.sqrt(D)
+    if out is None:
+        out = torch.empty_like(q)
+    _lib.check(_lib.load().extend_attn_paged(
+        _bits(q.contiguous()), q_start.data_ptr(), total, _bits(k_pool), _bits(v_pool), k_pool.stride(0),
+        k_pool.stride(1), k_pool.stride(2), n_pages, P, block_table.data_ptr(), block_table.stride(0),
+        block_table.shape[1], kv_len.data_ptr(), B, Hq, Hkv, D, int(max_new_hint), float(softmax_scale), _bits(out),
+        err.data_ptr() if err is not None else None, _stream()))
+    return out
+
+
 @dataclass
 class PackedMx:
     """An MXFP8 operand [rows, K] in the packed layout of fp8_pack_mx."""

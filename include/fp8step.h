@@ -307,6 +307,25 @@ FP8S_API int extend_attn(const uint16_t* q, const int32_t* q_start, int64_t tota
                     uint16_t* out, int32_t* err_flag, void* stream);
 
 /*
+ * extend_attn_paged -- extend_attn over paged caches (the pages' paged-prefill
+ * "extend"): position p of sequence b is slot p % page_size of page
+ * block_table[b * bt_stride + p / page_size]; pools, page sizes and the
+ * table as gqa_decode_attn_paged (cap = max_pages_per_seq * page_size).
+ * The output equals extend_attn on the contiguous caches the pages
+ * describe, bit for bit.  A read page id outside [0, num_pages) writes
+ * zeros for the rows of the workgroup that met it (all rows that attend to
+ * that page) and sets FP8S_DEV_PAGE_RANGE.
+ */
+FP8S_API int extend_attn_paged(const uint16_t* q, const int32_t* q_start, int64_t total_tokens,
+                    const uint16_t* k_pool, const uint16_t* v_pool,
+                    int64_t stride_page, int64_t stride_h, int64_t stride_t,
+                    int64_t num_pages, int32_t page_size,
+                    const int32_t* block_table, int64_t bt_stride, int64_t max_pages_per_seq,
+                    const int32_t* kv_len, int64_t B, int32_t Hq, int32_t Hkv, int32_t D,
+                    int64_t max_new_hint, float softmax_scale,
+                    uint16_t* out, int32_t* err_flag, void* stream);
+
+/*
  * qlinear_fp8 -- y = [residual +] dequant(quant(norm(x))) . dequant(W)^T, the
  * FP8 projections of a decode block other than the MLP ([TTS] "FP8
  * Quantization Strategy", "Kernel Benchmark Results").

@@ -121,3 +121,52 @@ def test_invalid_lengths_zero_their_rows():
     assert not out[10:22].float().abs().sum().item()
     keep = list(range(10)) + list(range(22, 30))
     assert torch.equal(out[keep].view(torch.int16), good[keep].view(torch.int16))
+
+
+def _paged(c, P, seed):
+    """Pools [pages, Hkv, P, D] holding c's caches on shuffled pages (garbage
+    elsewhere) and the block table [B, cap / P]."""
+    B, Hkv, cap, D = c.kc.shape
+    mp = (cap + P - 1) // P
+    n_pages = B * mp + 3
+    table = inputs.page_table(inputs.W_ATTN, B, mp, n_pages, extra=seed)
+    kp, vp = _garbage((n_pages, Hkv, P, D), seed + 1), _garbage((n_pages, Hkv, P, D), seed + 2)
+    for b in range(B):
+        n = (int(c.L[b]) + P - 1) // P
+        idx = torch.from_numpy(table[b, :n].astype(np.int64)).cuda()
+        kp[idx] = c.kc[b, :, :n * P].reshape(Hkv, n, P, D).transpose(0, 1)
+        vp[idx] = c.vc[b, :, :n * P].reshape(Hkv, n, P, D).transpose(0, 1)
+        table[b, n:] = -1                                       # never read
+    torch.cuda.synchronize()
+    return kp, vp, table
+
+
+@pytest.mark.parametrize("T,L,P", [([100, 37], [100, 37], 16), ([20, 64, 1], [300, 513, 77], 64),
+                                   ([9, 3], [40, 130], 32)])
+def test_paged_equals_contiguous(T, L, P):
+    need_gpu()
+    c = Case(T, L, cap=(max(L) + 127) // 128 * 128, extra=460 + P)
+    base = c.run()
+    kp, vp, table = _paged(c, P, 470 + P)
+    err = torch.zeros(1, dtype=torch.int32, device="cuda")
+    out = ops.extend_attn_paged(to_dev_bf16(c.qb), torch.from_numpy(c.q_start).cuda(), kp, vp,
+                                torch.from_numpy(table).cuda(), torch.from_numpy(c.L).cuda(), c.hint, err=err)
+    torch.cuda.synchronize()
+    assert int(err.item()) == 0
+    assert torch.equal(out.view(torch.int16), base.view(torch.int16))
+    assert max_rel_err(from_dev_bf16(out), c.oracle()) <= TOL_BF16_ATTN
+
+
+def test_paged_bad_page_zeroes_rows():
+    need_gpu()
+    c = Case([20, 10], [60, 40], cap=64, extra=480)
+    base = c.run()
+    kp, vp, table = _paged(c, 16, 490)
+    table[1, 1] = kp.shape[0]                                   # sequence 1 reads pages 0..2
+    err = torch.zeros(1, dtype=torch.int32, device="cuda")
+    out = ops.extend_attn_paged(to_dev_bf16(c.qb), torch.from_numpy(c.q_start).cuda(), kp, vp,
+                                torch.from_numpy(table).cuda(), torch.from_numpy(c.L).cuda(), c.hint, err=err)
+    torch.cuda.synchronize()
+    assert int(err.item()) == ops.DEV_PAGE_RANGE
+    assert not out[20:30].float().abs().sum().item()
+    assert torch.equal(out[:20].view(torch.int16), base[:20].view(torch.int16))
