@@ -400,6 +400,60 @@ def prefill_gemm_sweep(torch, ops):
     return out
 
 
+def mlp_large_sweep(torch, ops):
+    """swiglu_mlp_fp8_large at the Qwen3-4B MLP shape (hidden 2560, inter
+    9728) for M from 128 to 4096, bsgemm and MXFP8, weights packed outside
+    the timed loop: whole-call time (four kernels: quantise x, gate/up GEMM,
+    SwiGLU + quantise h, down GEMM), TFLOP/s over 6 M hidden inter flop, and
+    the decode kernel swiglu_mlp_fp8 at M = 128 beside it."""
+    g = torch.Generator(device="cuda")
+    g.manual_seed(17)
+    H, I = 2560, 9728
+    out = {}
+    for mode, name in ((ops.MLP_BSGEMM, "bsgemm"), (ops.MLP_MXFP8, "mxfp8")):
+        ws = [(torch.randn(shape, generator=g, device="cuda") * 0.02).to(torch.bfloat16)
+              for shape in ((I, H), (I, H), (H, I))]
+        qw = [ops.quantize_weight(w, mode) for w in ws]
+        qgu, sgu = torch.cat([qw[0].w, qw[1].w]), torch.cat([qw[0].scale, qw[1].scale])
+        if mode == ops.MLP_BSGEMM:
+            pgu, pd = ops.fp8_pack_bs(qgu, sgu, 128), ops.fp8_pack_bs(qw[2].w, qw[2].scale, 128)
+        else:
+            pgu, pd = ops.fp8_pack_mx(qgu, sgu), ops.fp8_pack_mx(qw[2].w, qw[2].scale)
+        del ws, qgu, sgu
+        res = {}
+        for M in (128, 512, 1024, 2048, 4096):
+            x = torch.randn((M, H), generator=g, device="cuda").to(torch.bfloat16)
+            y = torch.empty((M, H), dtype=torch.bfloat16, device="cuda")
+            wsp = torch.empty(int(ops._lib.load().swiglu_mlp_fp8_large_workspace_size(M, H, I, mode)),
+                              dtype=torch.uint8, device="cuda")
+            fns = [("large", lambda: ops.swiglu_mlp_fp8_large(x, pgu, pd, mode, y=y, workspace=wsp))]
+            if M == 128:
+                dws = torch.zeros(int(ops._lib.load().swiglu_mlp_fp8_workspace_size(M, H, I, mode)),
+                                  dtype=torch.uint8, device="cuda")
+                fns.append(("decode_kernel", lambda: ops.swiglu_mlp_fp8(x, *qw, mode, y=y, workspace=dws)))
+            for kind, fn in fns:
+                for _ in range(3):
+                    fn()
+                torch.cuda.synchronize()
+                n = 20
+                t0, t1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+                t0.record()
+                for _ in range(n):
+                    fn()
+                t1.record()
+                torch.cuda.synchronize()
+                us = t0.elapsed_time(t1) / n * 1e3
+                tf = 6 * M * H * I / (us * 1e-6) / 1e12
+                res[f"M={M}" + ("" if kind == "large" else ",decode_kernel")] = {
+                    "us": us, "TFLOP/s": tf, "frac": tf / PEAK_FP8_TFLOPS}
+                log(f"mlp large {name} M={M} {kind}: {us:.1f} us {tf:.0f} TFLOP/s")
+            del x, y, wsp
+        out[name] = res
+        del qw, pgu, pd
+        torch.cuda.empty_cache()
+    return out
+
+
 def extend_attn_sweep(torch, ops):
     """extend_attn (prefill / extend) at 32/8/128: a 4096-token prefill, 16
     sequences extending by 256 tokens after 1792 cached, 64 sequences by 16
@@ -714,6 +768,7 @@ def main():
         sweep["sampling"] = token_selection_timing(torch, ops)
         sweep["gemm_mx_prefill"] = prefill_gemm_sweep(torch, ops)
         sweep["extend_attn"] = extend_attn_sweep(torch, ops)
+        sweep["mlp_large"] = mlp_large_sweep(torch, ops)
         result["sweep"] = sweep
 
     if args.copy_calibration:

@@ -78,6 +78,9 @@ SIGNATURES = {
     "fp8_bs_packed_bytes": (c_sz, [c_i64, c_i64]),
     "fp8_pack_bs": (ctypes.c_int, [c_vp, c_i64, c_vp, c_i64, c_i64, c_i32, c_i64, c_i64, c_vp, c_sz, c_vp]),
     "fp8_gemm_bs_packed": (ctypes.c_int, [c_vp, c_vp, c_i64, c_i64, c_i64, c_vp, c_i64, c_vp]),
+    "swiglu_mlp_fp8_large_workspace_size": (c_sz, [c_i64, c_i64, c_i64, c_i32]),
+    "swiglu_mlp_fp8_large": (ctypes.c_int, [c_vp, c_i64, c_i64, c_i64, c_i64, c_i32, c_vp, c_vp, c_vp, c_i64, c_vp,
+                                            c_sz, c_vp]),
     "sample_top_k_top_p": (ctypes.c_int, [c_vp, c_i64, c_i64, c_i64, ctypes.c_float, c_i32, ctypes.c_float, c_vp,
                                           c_vp, c_i64, c_vp]),
     "prev_tokens_shift_inplace": (ctypes.c_int, [c_vp, c_vp, c_i64, c_i64, c_i64, c_vp]),

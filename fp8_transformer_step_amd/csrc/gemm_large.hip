@@ -47,7 +47,8 @@ struct GemmLargeArgs {
     const uint8_t* be; int64_t be_r, be_g;
     int M, N, KB;                             // KB = K / 128
     int tiles_m, tiles_n;
-    uint16_t* c; int64_t ldc;
+    uint16_t* c; int64_t ldc;                 // ldc in elements of C
+    int c_f32;                                // C is fp32 (not bf16)
 };
 
 // One lane's 32 operand bytes: 16 at p and 16 at p + hi (a row-major row:
@@ -256,7 +257,9 @@ __global__ __launch_bounds__(256, 2) void gemm_large_mx_kernel(GemmLargeArgs a) 
             for (int q = 0; q < 4; ++q) {
                 const int row = m0 + 64 * wm + 16 * i + 4 * g4 + q;
                 const int col = n0 + 64 * wn + 16 * j + (lane & 15);
-                if (row < a.M) a.c[(int64_t)row * a.ldc + col] = (uint16_t)f32_to_bf16(acc[i][j][q]);
+                if (row >= a.M) continue;
+                if (a.c_f32) reinterpret_cast<float*>(a.c)[(int64_t)row * a.ldc + col] = acc[i][j][q];
+                else a.c[(int64_t)row * a.ldc + col] = (uint16_t)f32_to_bf16(acc[i][j][q]);
             }
 }
 
@@ -316,9 +319,171 @@ __global__ __launch_bounds__(256) void pack_mx_kernel(PackArgs a) {
     }
 }
 
+// quant_pack: rows of x (bf16 [M, K]) or h = silu(g) u (SWIGLU: g, u fp32,
+// g at column c and u at column c + K of a [M, 2K] matrix) quantised in the
+// groups the GEMM reads (MX: 1x32 UE8M0; BS: 1x128 fp32) straight into the
+// packed operand layout (fp8_pack_mx / fp8_pack_bs).  One wave per (16-row
+// block, K block): lane r + 16 g holds the fragment's 32 values of row r
+// (K = 16 g .. and 64 + 16 g ..), which the fragment quantisers turn into
+// its 32 operand bytes and its scale.  Rows past M are zero.
+struct QuantPackArgs {
+    const void* src; int64_t ld;              // x (bf16) or gu (fp32), row stride in elements
+    int M, KB, Rp;
+    uint8_t* out;
+};
+
+template <bool BS, bool SWIGLU>
+__global__ __launch_bounds__(256) void quant_pack_kernel(QuantPackArgs a) {
+    const int lane = threadIdx.x & 63;
+    const int item = blockIdx.x * 4 + (threadIdx.x >> 6);
+    if (item >= (a.Rp / 16) * a.KB) return;
+    const int rb = item / a.KB, kb = item % a.KB;
+    const int row = 16 * rb + (lane & 15), g = lane >> 4;
+    const int K = a.KB * 128;
+    float v[32];
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+        const int k0 = kb * 128 + 64 * h + 16 * g;
+        if (row >= a.M) {
+#pragma unroll
+            for (int j = 0; j < 16; ++j) v[16 * h + j] = 0.0f;
+        } else if (SWIGLU) {
+            const float* gp = reinterpret_cast<const float*>(a.src) + (int64_t)row * a.ld + k0;
+            const float* up = gp + K;
+#pragma unroll
+            for (int j = 0; j < 16; j += 4) {
+                const float4 gg = *reinterpret_cast<const float4*>(gp + j);
+                const float4 uu = *reinterpret_cast<const float4*>(up + j);
+                const float gv[4] = {gg.x, gg.y, gg.z, gg.w}, uv[4] = {uu.x, uu.y, uu.z, uu.w};
+#pragma unroll
+                for (int t = 0; t < 4; ++t)
+                    v[16 * h + j + t] = gv[t] * __builtin_amdgcn_rcpf(1.0f + __expf(-gv[t])) * uv[t];
+            }
+        } else {
+            const uint16_t* xp = reinterpret_cast<const uint16_t*>(a.src) + (int64_t)row * a.ld + k0;
+#pragma unroll
+            for (int j = 0; j < 16; j += 8) {
+                const uint4 w = *reinterpret_cast<const uint4*>(xp + j);
+                const uint32_t ww[4] = {w.x, w.y, w.z, w.w};
+#pragma unroll
+                for (int t = 0; t < 4; ++t) {
+                    v[16 * h + j + 2 * t] = bf16_to_f32(ww[t] & 0xFFFFu);
+                    v[16 * h + j + 2 * t + 1] = bf16_to_f32(ww[t] >> 16);
+                }
+            }
+        }
+    }
+    v8i q;
+    uint8_t* frag = a.out + (int64_t)item * kFrag;
+    uint8_t* sreg = a.out + (int64_t)a.Rp * K + ((int64_t)(rb / 4) * a.KB + kb) * 256;
+    if (BS) {
+        float4 srow;
+        const float s = quant_frag_bs(v, q, srow, lane);
+        // every lane of row 16 rb + r holds its scale; lanes 0 .. 15 store it
+        if (lane < 16) reinterpret_cast<float*>(sreg)[16 * (rb % 4) + lane] = s;
+    } else {
+        int e;
+        quant_frag_mx(v, q, e, lane);
+        sreg[lane * 4 + (rb % 4)] = (uint8_t)e;
+    }
+    *reinterpret_cast<uint4*>(frag + lane * 16) = make_uint4(q[0], q[1], q[2], q[3]);
+    *reinterpret_cast<uint4*>(frag + 1024 + lane * 16) = make_uint4(q[4], q[5], q[6], q[7]);
+}
+
+static size_t packed_bytes(int64_t R, int64_t K, bool bs) {
+    const int64_t Rp = (R + 127) / 128 * 128;
+    return (size_t)(Rp * K + (bs ? Rp * (K / 128) * 4 : Rp * (K / 32)));
+}
+
+struct MlpLargePlan { size_t off_x, off_gu, off_h, total; };
+static MlpLargePlan plan_mlp_large(int64_t M, int64_t H, int64_t I, bool bs) {
+    MlpLargePlan p;
+    auto al = [](size_t v) { return (v + 255) / 256 * 256; };
+    p.off_x = 0;
+    p.off_gu = al(packed_bytes(M, H, bs));
+    p.off_h = p.off_gu + al((size_t)M * 2 * I * 4);
+    p.total = p.off_h + al(packed_bytes(M, I, bs));
+    return p;
+}
+
 }  // namespace fp8s
 
 using namespace fp8s;
+
+extern "C" size_t swiglu_mlp_fp8_large_workspace_size(int64_t M, int64_t hidden, int64_t inter, int mode) {
+    if (M < 1 || M >= (1ll << 24) || hidden < 128 || hidden % 128 || inter < 128 || inter % 128 ||
+        hidden >= (1ll << 20) || inter >= (1ll << 20))
+        return 0;
+    if (mode != FP8S_MLP_BSGEMM && mode != FP8S_MLP_MXFP8) return 0;
+    return plan_mlp_large(M, hidden, inter, mode == FP8S_MLP_BSGEMM).total;
+}
+
+extern "C" int swiglu_mlp_fp8_large(const uint16_t* x, int64_t ld_x, int64_t M, int64_t hidden, int64_t inter,
+                                    int mode, const void* gate_up_packed, const void* down_packed, uint16_t* y,
+                                    int64_t ld_y, void* workspace, size_t workspace_bytes, void* stream) {
+    clear_error();
+    FP8S_REQUIRE(x && gate_up_packed && down_packed && y, FP8S_EINVAL, "swiglu_mlp_fp8_large: null pointer");
+    FP8S_REQUIRE(mode == FP8S_MLP_BSGEMM || mode == FP8S_MLP_MXFP8, FP8S_EINVAL,
+                 "swiglu_mlp_fp8_large: unknown mode %d", mode);
+    const size_t need = swiglu_mlp_fp8_large_workspace_size(M, hidden, inter, mode);
+    FP8S_REQUIRE(need > 0, FP8S_EINVAL, "swiglu_mlp_fp8_large: need M >= 1 and hidden, inter multiples of 128");
+    FP8S_REQUIRE(ld_x >= hidden && ld_x % 8 == 0 && ld_y >= hidden && ld_y % 8 == 0 && aligned16(x) && aligned16(y),
+                 FP8S_EINVAL, "swiglu_mlp_fp8_large: x and y 16-byte aligned, row strides >= hidden and multiples of 8");
+    FP8S_REQUIRE(aligned16(gate_up_packed) && aligned16(down_packed), FP8S_EINVAL,
+                 "swiglu_mlp_fp8_large: packed weights must be 16-byte aligned");
+    FP8S_REQUIRE(workspace && aligned16(workspace) && workspace_bytes >= need, FP8S_EWORKSPACE,
+                 "swiglu_mlp_fp8_large: workspace %zu < required %zu bytes", workspace_bytes, need);
+    const bool bs = mode == FP8S_MLP_BSGEMM;
+    const MlpLargePlan p = plan_mlp_large(M, hidden, inter, bs);
+    uint8_t* ws = static_cast<uint8_t*>(workspace);
+    const hipStream_t st = as_stream(stream);
+    const int64_t Mp = (M + 127) / 128 * 128;
+    // 1. x -> packed operand
+    QuantPackArgs qa;
+    qa.src = x; qa.ld = ld_x; qa.M = (int)M; qa.KB = (int)(hidden / 128); qa.Rp = (int)Mp; qa.out = ws + p.off_x;
+    const int64_t items_x = Mp / 16 * qa.KB;
+    if (bs)
+        FP8S_LAUNCH("mlpl_xq", (quant_pack_kernel<true, false>), dim3((unsigned)((items_x + 3) / 4)), dim3(256), 0, st, qa);
+    else
+        FP8S_LAUNCH("mlpl_xq", (quant_pack_kernel<false, false>), dim3((unsigned)((items_x + 3) / 4)), dim3(256), 0, st, qa);
+    int rc = check_launch("swiglu_mlp_fp8_large (x quantisation)");
+    if (rc) return rc;
+    // 2. [g | u] = x . [W_gate; W_up]^T, fp32
+    GemmLargeArgs g;
+    g.a = ws + p.off_x; g.lda = 0; g.ae = g.a + Mp * hidden; g.ae_r = g.ae_g = 0;
+    g.b = static_cast<const uint8_t*>(gate_up_packed); g.ldb = 0; g.be = g.b + 2 * inter * hidden; g.be_r = g.be_g = 0;
+    g.M = (int)M; g.N = (int)(2 * inter); g.KB = (int)(hidden / 128);
+    g.tiles_m = (int)(Mp / kGlBM); g.tiles_n = (int)(2 * inter / kGlBN);
+    g.c = reinterpret_cast<uint16_t*>(ws + p.off_gu); g.ldc = 2 * inter; g.c_f32 = 1;
+    FP8S_REQUIRE((2 * inter) % 128 == 0 && inter % 128 == 0, FP8S_EINVAL, "swiglu_mlp_fp8_large: inter % 128");
+    if (bs)
+        FP8S_LAUNCH("mlpl_gu", (gemm_large_mx_kernel<true, true>), dim3((unsigned)(g.tiles_m * g.tiles_n)), dim3(256), 0, st, g);
+    else
+        FP8S_LAUNCH("mlpl_gu", (gemm_large_mx_kernel<true, false>), dim3((unsigned)(g.tiles_m * g.tiles_n)), dim3(256), 0, st, g);
+    if ((rc = check_launch("swiglu_mlp_fp8_large (gate/up)"))) return rc;
+    // 3. h = silu(g) u -> packed operand
+    QuantPackArgs qh;
+    qh.src = ws + p.off_gu; qh.ld = 2 * inter; qh.M = (int)M; qh.KB = (int)(inter / 128); qh.Rp = (int)Mp;
+    qh.out = ws + p.off_h;
+    const int64_t items_h = Mp / 16 * qh.KB;
+    if (bs)
+        FP8S_LAUNCH("mlpl_hq", (quant_pack_kernel<true, true>), dim3((unsigned)((items_h + 3) / 4)), dim3(256), 0, st, qh);
+    else
+        FP8S_LAUNCH("mlpl_hq", (quant_pack_kernel<false, true>), dim3((unsigned)((items_h + 3) / 4)), dim3(256), 0, st, qh);
+    if ((rc = check_launch("swiglu_mlp_fp8_large (h quantisation)"))) return rc;
+    // 4. y = h . W_down^T
+    GemmLargeArgs d;
+    d.a = ws + p.off_h; d.lda = 0; d.ae = d.a + Mp * inter; d.ae_r = d.ae_g = 0;
+    d.b = static_cast<const uint8_t*>(down_packed); d.ldb = 0; d.be = d.b + hidden * inter; d.be_r = d.be_g = 0;
+    d.M = (int)M; d.N = (int)hidden; d.KB = (int)(inter / 128);
+    d.tiles_m = (int)(Mp / kGlBM); d.tiles_n = (int)(hidden / kGlBN);
+    d.c = y; d.ldc = ld_y; d.c_f32 = 0;
+    if (bs)
+        FP8S_LAUNCH("mlpl_down", (gemm_large_mx_kernel<true, true>), dim3((unsigned)(d.tiles_m * d.tiles_n)), dim3(256), 0, st, d);
+    else
+        FP8S_LAUNCH("mlpl_down", (gemm_large_mx_kernel<true, false>), dim3((unsigned)(d.tiles_m * d.tiles_n)), dim3(256), 0, st, d);
+    return check_launch("swiglu_mlp_fp8_large (down)");
+}
 
 extern "C" size_t fp8_mx_packed_bytes(int64_t R, int64_t K) {
     if (R < 1 || K < 128 || K % 128 || R >= (1ll << 30) || K >= (1ll << 30)) return 0;
@@ -366,7 +531,7 @@ extern "C" int fp8_gemm_mx_packed(const void* a_packed, const void* b_packed, in
     g.be = g.b + N * K; g.be_r = g.be_g = 0;
     g.M = (int)M; g.N = (int)N; g.KB = (int)(K / 128);
     g.tiles_m = (int)tiles_m; g.tiles_n = (int)tiles_n;
-    g.c = c; g.ldc = ldc;
+    g.c = c; g.ldc = ldc; g.c_f32 = 0;
     FP8S_LAUNCH("gemm_large_mx", (gemm_large_mx_kernel<true, false>), dim3((unsigned)(tiles_m * tiles_n)), dim3(256), 0,
                 as_stream(stream), g);
     return check_launch("fp8_gemm_mx_packed");
@@ -395,7 +560,7 @@ extern "C" int fp8_gemm_mx(const uint8_t* a, int64_t lda, const uint8_t* a_e, in
     g.b = b; g.ldb = ldb; g.be = b_e; g.be_r = be_row; g.be_g = be_grp;
     g.M = (int)M; g.N = (int)N; g.KB = (int)(K / 128);
     g.tiles_m = (int)tiles_m; g.tiles_n = (int)tiles_n;
-    g.c = c; g.ldc = ldc;
+    g.c = c; g.ldc = ldc; g.c_f32 = 0;
     FP8S_LAUNCH("gemm_large_mx", (gemm_large_mx_kernel<false, false>), dim3((unsigned)(tiles_m * tiles_n)), dim3(256),
                 0, as_stream(stream), g);
     return check_launch("fp8_gemm_mx");
@@ -450,7 +615,7 @@ extern "C" int fp8_gemm_bs_packed(const void* a_packed, const void* b_packed, in
     g.be = g.b + N * K; g.be_r = g.be_g = 0;
     g.M = (int)M; g.N = (int)N; g.KB = (int)(K / 128);
     g.tiles_m = (int)tiles_m; g.tiles_n = (int)tiles_n;
-    g.c = c; g.ldc = ldc;
+    g.c = c; g.ldc = ldc; g.c_f32 = 0;
     FP8S_LAUNCH("gemm_large_bs", (gemm_large_mx_kernel<true, true>), dim3((unsigned)(tiles_m * tiles_n)), dim3(256), 0,
                 as_stream(stream), g);
     return check_launch("fp8_gemm_bs_packed");

@@ -227,8 +227,9 @@ __device__ __forceinline__ void reduce_wk(v4f (&acc)[NB][MTS], uint8_t* lds, int
 
 
 // bsgemm 1x128: the group is the whole 128-block of the row, spread over the
-// four lanes with the same row (lane bits 4 and 5).
-__device__ __forceinline__ void quant_frag_bs(const float (&v)[32], v8i& q, float4& srow, int lane) {
+// four lanes with the same row (lane bits 4 and 5).  Returns the scale of the
+// lane's own row (lane % 16).
+__device__ __forceinline__ float quant_frag_bs(const float (&v)[32], v8i& q, float4& srow, int lane) {
     float am = 0.0f;
 #pragma unroll
     for (int i = 0; i < 32; ++i) am = fmaxf(am, fabsf(v[i]));
@@ -243,6 +244,7 @@ __device__ __forceinline__ void quant_frag_bs(const float (&v)[32], v8i& q, floa
     srow.y = __shfl(s, r0 + 1, kWave);
     srow.z = __shfl(s, r0 + 2, kWave);
     srow.w = __shfl(s, r0 + 3, kWave);
+    return s;
 }
 
 // MX 1x32: the low half of lane g belongs to group g/2, the high half to

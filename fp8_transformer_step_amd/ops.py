@@ -416,6 +416,31 @@ def fp8_gemm_bs_packed(pa, pb, c=None):
     return c
 
 
+def swiglu_mlp_fp8_large(x, gate_up, down, mode, y=None, workspace=None):
+    """y bf16 [M, hidden] = SwiGLU MLP of x bf16 [M, hidden] (any M) with
+    packed weights: gate_up = PackedMx of [Wg; Wu] ([2 inter, hidden]), down
+    = PackedMx of Wd ([hidden, inter]), both from fp8_pack_bs (mode
+    MLP_BSGEMM) or fp8_pack_mx (MLP_MXFP8)."""
+    _require_cuda(x)
+    if x.dim() != 2 or x.stride(1) != 1 or x.dtype != torch.bfloat16:
+        raise ValueError("x must be bf16 [M, hidden] with unit column stride")
+    M, H = x.shape
+    I = gate_up.rows // 2
+    if gate_up.K != H or down.rows != H or down.K != I or gate_up.rows != 2 * I:
+        raise ValueError("weights do not match x: gate_up [2 inter, hidden], down [hidden, inter]")
+    n = int(_lib.load().swiglu_mlp_fp8_large_workspace_size(M, H, I, mode))
+    if n == 0:
+        raise ValueError("need M >= 1, hidden and inter multiples of 128, a known mode")
+    if workspace is None or workspace.numel() < n:
+        workspace = torch.empty(n, dtype=torch.uint8, device=x.device)
+    if y is None:
+        y = torch.empty((M, H), dtype=torch.bfloat16, device=x.device)
+    _lib.check(_lib.load().swiglu_mlp_fp8_large(_bits(x), x.stride(0), M, H, I, mode, gate_up.data.data_ptr(),
+                                                down.data.data_ptr(), _bits(y), y.stride(0), workspace.data_ptr(),
+                                                workspace.numel(), _stream()))
+    return y
+
+
 def sample_top_k_top_p(logits, uniforms, temperature=0.8, top_k=30, top_p=0.8, codes=None):
     """One token per row of fp32 logits [B, V] (unit stride along V) with
     the caller's uniforms [B] fp32 in [0, 1); returns int32 codes [B]."""

@@ -472,6 +472,31 @@ FP8S_API int fp8_gemm_bs_packed(const void* a_packed, const void* b_packed, int6
                     uint16_t* c, int64_t ldc, void* stream);
 
 /*
+ * swiglu_mlp_fp8_large -- the MLP of swiglu_mlp_fp8 at prefill sizes ([TTS]
+ * "Kernel Benchmark Results": the SwiGLU MLP is measured at batch sizes from
+ * 1 to 4096), built on the prefill GEMMs: x is quantised per row (mode 0 /
+ * 2 groups) straight into the packed operand layout, one GEMM computes
+ * [g | u] = x [Wg; Wu]^T in fp32, h = silu(g) * u is quantised the same way
+ * into the packed layout, and a second GEMM gives y = h Wd^T in bf16.  Four
+ * kernels on `stream`.
+ *   x     [M, hidden] bf16, row stride ld_x (>= hidden, multiple of 8).
+ *   gate_up_packed  the weight [2 inter, hidden] (rows 0 .. inter-1 = Wg,
+ *         inter .. 2 inter-1 = Wu) packed by fp8_pack_bs (rows_per_scale
+ *         128) for FP8S_MLP_BSGEMM, by fp8_pack_mx for FP8S_MLP_MXFP8.
+ *   down_packed     Wd [hidden, inter], packed the same way.
+ *   y     [M, hidden] bf16 out, row stride ld_y (>= hidden, multiple of 8).
+ *   M >= 1; hidden, inter multiples of 128 (below 2^20).
+ *   workspace  >= swiglu_mlp_fp8_large_workspace_size(M, hidden, inter, mode)
+ *         bytes (0 = invalid sizes), 16-byte aligned; needs no clearing;
+ *         calls that share it must not overlap in time.
+ *   Accuracy: max|y - y_oracle| <= 2e-2 * max|y_oracle|.
+ */
+FP8S_API size_t swiglu_mlp_fp8_large_workspace_size(int64_t M, int64_t hidden, int64_t inter, int mode);
+FP8S_API int swiglu_mlp_fp8_large(const uint16_t* x, int64_t ld_x, int64_t M, int64_t hidden, int64_t inter,
+                    int mode, const void* gate_up_packed, const void* down_packed, uint16_t* y, int64_t ld_y,
+                    void* workspace, size_t workspace_bytes, void* stream);
+
+/*
  * sample_top_k_top_p -- one token per row drawn from fp32 logits with
  * temperature, top-k and top-p ([KV] section 6: the benchmark generation
  * samples with temperature 0.8, top_p 0.8, top_k 30 under a fixed seed;
