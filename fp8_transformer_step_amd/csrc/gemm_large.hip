@@ -80,9 +80,17 @@ struct BsScales {
     float b;          // the block scale of the wave's 64 B rows
 };
 
-template <bool PACKED, bool BS>
+// SWI (packed only): the gate/up GEMM of the SwiGLU MLP.  B is [Wg; Wu]
+// ([2 N, K], N = inter); tile tn takes gate rows 64 tn .. + 63 (waves wn = 0)
+// and the up rows of the same columns, N + 64 tn .. (wn = 1).  The epilogue
+// hands u to the gate waves through LDS and forms h = silu(g) u in fp32:
+// bsgemm writes h fp32 [M, N] (row stride ldc) to c, whose 1x128 groups
+// span two tiles; MXFP8 quantises h in 1x32 groups straight into the packed
+// operand layout (R = tiles_m * 128 rows, K = N) at c.
+template <bool PACKED, bool BS, bool SWI = false>
 __global__ __launch_bounds__(256, 2) void gemm_large_mx_kernel(GemmLargeArgs a) {
     static_assert(PACKED || !BS, "bsgemm operands come packed");
+    static_assert(PACKED || !SWI, "the SwiGLU epilogue takes packed operands");
     using Sc = typename std::conditional<BS, BsScales, v8i>::type;
     __shared__ __attribute__((aligned(1024))) uint8_t smem[2 * kGlStage];
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
@@ -108,8 +116,10 @@ __global__ __launch_bounds__(256, 2) void gemm_large_mx_kernel(GemmLargeArgs a) 
     if (PACKED) {                              // fragment (16-row block, kb) at (block * KB + kb) * 2 KiB
         pa0 = a.a + (int64_t)((m0 / 16 + wave) * a.KB) * kFrag + lane * 16;
         pa1 = a.a + (int64_t)((m0 / 16 + wave + 4) * a.KB) * kFrag + lane * 16;
-        pb0 = a.b + (int64_t)((n0 / 16 + wave) * a.KB) * kFrag + lane * 16;
-        pb1 = a.b + (int64_t)((n0 / 16 + wave + 4) * a.KB) * kFrag + lane * 16;
+        const int nb0 = SWI ? 4 * tn + wave : n0 / 16 + wave;
+        const int nb1 = SWI ? a.N / 16 + 4 * tn + wave : n0 / 16 + wave + 4;
+        pb0 = a.b + (int64_t)(nb0 * a.KB) * kFrag + lane * 16;
+        pb1 = a.b + (int64_t)(nb1 * a.KB) * kFrag + lane * 16;
     } else {
         pa0 = a.a + (int64_t)min(m0 + 16 * wave + rl, a.M - 1) * a.lda + 16 * g4;
         pa1 = a.a + (int64_t)min(m0 + 16 * (wave + 4) + rl, a.M - 1) * a.lda + 16 * g4;
@@ -144,10 +154,11 @@ __global__ __launch_bounds__(256, 2) void gemm_large_mx_kernel(GemmLargeArgs a) 
     // packed: the four exponents of a 64-row group are one dword per lane at
     // ((group * KB + kb) * 64 + lane) * 4
     const uint32_t* pea = reinterpret_cast<const uint32_t*>(a.ae) + (uint32_t)((m0 / 64 + wm) * a.KB) * 64 + lane;
-    const uint32_t* peb = reinterpret_cast<const uint32_t*>(a.be) + (uint32_t)((n0 / 64 + wn) * a.KB) * 64 + lane;
+    const int bgrp = SWI ? (wn ? a.N / 64 + tn : tn) : n0 / 64 + wn;   // 64-row group of the wave's B rows
+    const uint32_t* peb = reinterpret_cast<const uint32_t*>(a.be) + (uint32_t)(bgrp * a.KB) * 64 + lane;
     // bsgemm packed scales: 64 fp32 per (64-row group, K block), row order
     const float* psa = reinterpret_cast<const float*>(a.ae) + (uint32_t)((m0 / 64 + wm) * a.KB) * 64 + 4 * g4;
-    const float* psb = reinterpret_cast<const float*>(a.be) + (uint32_t)((n0 / 64 + wn) * a.KB) * 64;
+    const float* psb = reinterpret_cast<const float*>(a.be) + (uint32_t)(bgrp * a.KB) * 64;
     auto exps = [&](int kb) -> Sc {
         if constexpr (BS) {
             BsScales sc;
@@ -248,6 +259,82 @@ __global__ __launch_bounds__(256, 2) void gemm_large_mx_kernel(GemmLargeArgs a) 
         lds_sync();
     }
 
+    if constexpr (SWI) {
+        // the loop ended on a barrier: every wave is done with the stages
+        float* ex = reinterpret_cast<float*>(smem) + wm * 4096;       // 16 KiB per row half
+        if (wn == 1) {
+#pragma unroll
+            for (int i = 0; i < 4; ++i)
+#pragma unroll
+                for (int j = 0; j < 4; ++j)
+#pragma unroll
+                    for (int q = 0; q < 4; ++q) ex[((i * 4 + j) * 4 + q) * 64 + lane] = acc[i][j][q];
+        }
+        __syncthreads();
+        if (wn == 1) return;
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+#pragma unroll
+            for (int j = 0; j < 4; ++j)
+#pragma unroll
+                for (int q = 0; q < 4; ++q) {
+                    const float g = acc[i][j][q], u = ex[((i * 4 + j) * 4 + q) * 64 + lane];
+                    acc[i][j][q] = g * __builtin_amdgcn_rcpf(1.0f + __expf(-g)) * u;
+                }
+        const int c0 = 64 * tn;
+        if constexpr (BS) {
+            float* h = reinterpret_cast<float*>(a.c);
+#pragma unroll
+            for (int i = 0; i < 4; ++i)
+#pragma unroll
+                for (int j = 0; j < 4; ++j)
+#pragma unroll
+                    for (int q = 0; q < 4; ++q) {
+                        const int row = m0 + 64 * wm + 16 * i + 4 * g4 + q;
+                        if (row < a.M) h[(int64_t)row * a.ldc + c0 + 16 * j + (lane & 15)] = acc[i][j][q];
+                    }
+        } else {
+            // h [64 rows][64 columns] row-major in the wave's own LDS region
+            // (one wave's LDS accesses complete in order: the u reads above
+            // are done before these writes land)
+#pragma unroll
+            for (int i = 0; i < 4; ++i)
+#pragma unroll
+                for (int j = 0; j < 4; ++j)
+#pragma unroll
+                    for (int q = 0; q < 4; ++q) ex[(16 * i + 4 * g4 + q) * 64 + 16 * j + (lane & 15)] = acc[i][j][q];
+            // lane (r, g) of 16-row block i quantises h[16 i + r][16 g .. 16 g + 15]:
+            // the low (tn even) or high (tn odd) half of the K = 128 fragment
+            // of K block tn / 2; 1x32 groups 2 (tn % 2) + g / 2 pair lanes g, g ^ 1
+            const int KBh = a.N / 128, kbh = tn >> 1, half = tn & 1;
+            uint8_t* out = reinterpret_cast<uint8_t*>(a.c);
+            uint8_t* sreg = out + (int64_t)a.tiles_m * kGlBM * a.N + ((int64_t)((m0 + 64 * wm) / 64) * KBh + kbh) * 256;
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                float v[16];
+                const float* src = ex + (16 * i + rl) * 64 + 16 * g4;
+#pragma unroll
+                for (int k = 0; k < 4; ++k) {
+                    const float4 f = *reinterpret_cast<const float4*>(src + 4 * k);
+                    v[4 * k] = f.x; v[4 * k + 1] = f.y; v[4 * k + 2] = f.z; v[4 * k + 3] = f.w;
+                }
+                float am = 0.0f;
+#pragma unroll
+                for (int k = 0; k < 16; ++k) am = fmaxf(am, fabsf(v[k]));
+                am = fmaxf(am, __shfl_xor(am, 16, kWave));
+                const int e = mx_exponent(__float_as_uint(am));
+                const float m = mx_inv_scale(e);
+                const uint4 qv = make_uint4(e4m3x4(v[0] * m, v[1] * m, v[2] * m, v[3] * m),
+                                            e4m3x4(v[4] * m, v[5] * m, v[6] * m, v[7] * m),
+                                            e4m3x4(v[8] * m, v[9] * m, v[10] * m, v[11] * m),
+                                            e4m3x4(v[12] * m, v[13] * m, v[14] * m, v[15] * m));
+                const int rb16 = (m0 + 64 * wm) / 16 + i;
+                *reinterpret_cast<uint4*>(out + ((int64_t)rb16 * KBh + kbh) * kFrag + half * 1024 + lane * 16) = qv;
+                if (!(g4 & 1)) sreg[(rl + 16 * (2 * half + (g4 >> 1))) * 4 + i] = (uint8_t)e;
+            }
+        }
+        return;
+    }
     // lane holds D[4 * (lane / 16) + r][lane % 16] of every 16 x 16 tile
 #pragma unroll
     for (int i = 0; i < 4; ++i)
@@ -319,8 +406,7 @@ __global__ __launch_bounds__(256) void pack_mx_kernel(PackArgs a) {
     }
 }
 
-// quant_pack: rows of x (bf16 [M, K]) or h = silu(g) u (SWIGLU: g, u fp32,
-// g at column c and u at column c + K of a [M, 2K] matrix) quantised in the
+// quant_pack: rows of x (bf16 [M, K]) or of h (F32: fp32 [M, K]) quantised in the
 // groups the GEMM reads (MX: 1x32 UE8M0; BS: 1x128 fp32) straight into the
 // packed operand layout (fp8_pack_mx / fp8_pack_bs).  One wave per (16-row
 // block, K block): lane r + 16 g holds the fragment's 32 values of row r
@@ -332,7 +418,7 @@ struct QuantPackArgs {
     uint8_t* out;
 };
 
-template <bool BS, bool SWIGLU>
+template <bool BS, bool F32>
 __global__ __launch_bounds__(256) void quant_pack_kernel(QuantPackArgs a) {
     const int lane = threadIdx.x & 63;
     const int item = blockIdx.x * 4 + (threadIdx.x >> 6);
@@ -347,17 +433,12 @@ __global__ __launch_bounds__(256) void quant_pack_kernel(QuantPackArgs a) {
         if (row >= a.M) {
 #pragma unroll
             for (int j = 0; j < 16; ++j) v[16 * h + j] = 0.0f;
-        } else if (SWIGLU) {
-            const float* gp = reinterpret_cast<const float*>(a.src) + (int64_t)row * a.ld + k0;
-            const float* up = gp + K;
+        } else if (F32) {
+            const float* hp = reinterpret_cast<const float*>(a.src) + (int64_t)row * a.ld + k0;
 #pragma unroll
             for (int j = 0; j < 16; j += 4) {
-                const float4 gg = *reinterpret_cast<const float4*>(gp + j);
-                const float4 uu = *reinterpret_cast<const float4*>(up + j);
-                const float gv[4] = {gg.x, gg.y, gg.z, gg.w}, uv[4] = {uu.x, uu.y, uu.z, uu.w};
-#pragma unroll
-                for (int t = 0; t < 4; ++t)
-                    v[16 * h + j + t] = gv[t] * __builtin_amdgcn_rcpf(1.0f + __expf(-gv[t])) * uv[t];
+                const float4 f = *reinterpret_cast<const float4*>(hp + j);
+                v[16 * h + j] = f.x; v[16 * h + j + 1] = f.y; v[16 * h + j + 2] = f.z; v[16 * h + j + 3] = f.w;
             }
         } else {
             const uint16_t* xp = reinterpret_cast<const uint16_t*>(a.src) + (int64_t)row * a.ld + k0;
@@ -401,7 +482,7 @@ static MlpLargePlan plan_mlp_large(int64_t M, int64_t H, int64_t I, bool bs) {
     auto al = [](size_t v) { return (v + 255) / 256 * 256; };
     p.off_x = 0;
     p.off_gu = al(packed_bytes(M, H, bs));
-    p.off_h = p.off_gu + al((size_t)M * 2 * I * 4);
+    p.off_h = p.off_gu + (bs ? al((size_t)M * I * 4) : 0);        // fp32 h (bsgemm only)
     p.total = p.off_h + al(packed_bytes(M, I, bs));
     return p;
 }
@@ -448,29 +529,28 @@ extern "C" int swiglu_mlp_fp8_large(const uint16_t* x, int64_t ld_x, int64_t M, 
         FP8S_LAUNCH("mlpl_xq", (quant_pack_kernel<false, false>), dim3((unsigned)((items_x + 3) / 4)), dim3(256), 0, st, qa);
     int rc = check_launch("swiglu_mlp_fp8_large (x quantisation)");
     if (rc) return rc;
-    // 2. [g | u] = x . [W_gate; W_up]^T, fp32
+    // 2. h = silu(x Wg^T) (x Wu^T): bsgemm writes it fp32, MXFP8 packed
     GemmLargeArgs g;
     g.a = ws + p.off_x; g.lda = 0; g.ae = g.a + Mp * hidden; g.ae_r = g.ae_g = 0;
     g.b = static_cast<const uint8_t*>(gate_up_packed); g.ldb = 0; g.be = g.b + 2 * inter * hidden; g.be_r = g.be_g = 0;
-    g.M = (int)M; g.N = (int)(2 * inter); g.KB = (int)(hidden / 128);
-    g.tiles_m = (int)(Mp / kGlBM); g.tiles_n = (int)(2 * inter / kGlBN);
-    g.c = reinterpret_cast<uint16_t*>(ws + p.off_gu); g.ldc = 2 * inter; g.c_f32 = 1;
-    FP8S_REQUIRE((2 * inter) % 128 == 0 && inter % 128 == 0, FP8S_EINVAL, "swiglu_mlp_fp8_large: inter % 128");
+    g.M = (int)M; g.N = (int)inter; g.KB = (int)(hidden / 128);
+    g.tiles_m = (int)(Mp / kGlBM); g.tiles_n = (int)(inter / 64);
+    g.ldc = inter; g.c_f32 = 1;
+    g.c = reinterpret_cast<uint16_t*>(ws + (bs ? p.off_gu : p.off_h));
     if (bs)
-        FP8S_LAUNCH("mlpl_gu", (gemm_large_mx_kernel<true, true>), dim3((unsigned)(g.tiles_m * g.tiles_n)), dim3(256), 0, st, g);
+        FP8S_LAUNCH("mlpl_gu", (gemm_large_mx_kernel<true, true, true>), dim3((unsigned)(g.tiles_m * g.tiles_n)), dim3(256), 0, st, g);
     else
-        FP8S_LAUNCH("mlpl_gu", (gemm_large_mx_kernel<true, false>), dim3((unsigned)(g.tiles_m * g.tiles_n)), dim3(256), 0, st, g);
+        FP8S_LAUNCH("mlpl_gu", (gemm_large_mx_kernel<true, false, true>), dim3((unsigned)(g.tiles_m * g.tiles_n)), dim3(256), 0, st, g);
     if ((rc = check_launch("swiglu_mlp_fp8_large (gate/up)"))) return rc;
-    // 3. h = silu(g) u -> packed operand
-    QuantPackArgs qh;
-    qh.src = ws + p.off_gu; qh.ld = 2 * inter; qh.M = (int)M; qh.KB = (int)(inter / 128); qh.Rp = (int)Mp;
-    qh.out = ws + p.off_h;
-    const int64_t items_h = Mp / 16 * qh.KB;
-    if (bs)
+    // 3. bsgemm: h -> packed operand (1x128 groups span two gate/up tiles)
+    if (bs) {
+        QuantPackArgs qh;
+        qh.src = ws + p.off_gu; qh.ld = inter; qh.M = (int)M; qh.KB = (int)(inter / 128); qh.Rp = (int)Mp;
+        qh.out = ws + p.off_h;
+        const int64_t items_h = Mp / 16 * qh.KB;
         FP8S_LAUNCH("mlpl_hq", (quant_pack_kernel<true, true>), dim3((unsigned)((items_h + 3) / 4)), dim3(256), 0, st, qh);
-    else
-        FP8S_LAUNCH("mlpl_hq", (quant_pack_kernel<false, true>), dim3((unsigned)((items_h + 3) / 4)), dim3(256), 0, st, qh);
-    if ((rc = check_launch("swiglu_mlp_fp8_large (h quantisation)"))) return rc;
+        if ((rc = check_launch("swiglu_mlp_fp8_large (h quantisation)"))) return rc;
+    }
     // 4. y = h . W_down^T
     GemmLargeArgs d;
     d.a = ws + p.off_h; d.lda = 0; d.ae = d.a + Mp * inter; d.ae_r = d.ae_g = 0;

@@ -475,10 +475,12 @@ FP8S_API int fp8_gemm_bs_packed(const void* a_packed, const void* b_packed, int6
  * swiglu_mlp_fp8_large -- the MLP of swiglu_mlp_fp8 at prefill sizes ([TTS]
  * "Kernel Benchmark Results": the SwiGLU MLP is measured at batch sizes from
  * 1 to 4096), built on the prefill GEMMs: x is quantised per row (mode 0 /
- * 2 groups) straight into the packed operand layout, one GEMM computes
- * [g | u] = x [Wg; Wu]^T in fp32, h = silu(g) * u is quantised the same way
- * into the packed layout, and a second GEMM gives y = h Wd^T in bf16.  Four
- * kernels on `stream`.
+ * 2 groups) straight into the packed operand layout; one GEMM computes
+ * g = x Wg^T and u = x Wu^T side by side in fp32 and forms h = silu(g) * u
+ * in its epilogue (MXFP8: quantised there into the packed layout; bsgemm:
+ * written in fp32 and quantised by one more kernel, its 1x128 groups
+ * spanning two GEMM tiles); a second GEMM gives y = h Wd^T in bf16.  Three
+ * (MXFP8) or four (bsgemm) kernels on `stream`.
  *   x     [M, hidden] bf16, row stride ld_x (>= hidden, multiple of 8).
  *   gate_up_packed  the weight [2 inter, hidden] (rows 0 .. inter-1 = Wg,
  *         inter .. 2 inter-1 = Wu) packed by fp8_pack_bs (rows_per_scale
