@@ -53,8 +53,14 @@ KERNELS = [
     (r"attn_split_mx_kernel", "attn_split_mx"),
     (r"attn_bal_mx_kernel<\d+, \d+, true>", "attn_split_mx_paged"),
     (r"attn_bal_mx_kernel", "attn_split_mx"),
-    (r"gemm_large_mx_kernel<true>", "gemm_large_mx_packed"),
+    # gemm_large_mx_kernel<PACKED, BS, SWI>; SWI = the large-M MLP's gate/up GEMM
+    (r"gemm_large_mx_kernel<true, true, true>", "mlp_large_gu_bs"),
+    (r"gemm_large_mx_kernel<true, false, true>", "mlp_large_gu_mx"),
+    (r"gemm_large_mx_kernel<true, true", "gemm_large_bs_packed"),
+    (r"gemm_large_mx_kernel<true", "gemm_large_mx_packed"),
     (r"gemm_large_mx_kernel", "gemm_large_mx"),
+    (r"quant_pack_kernel<\w+, true>", "mlp_large_hq"),
+    (r"quant_pack_kernel", "mlp_large_xq"),
     (r"pack_mx_kernel", "pack_mx"),
     (r"extend_attn_kernel", "extend_attn"),
     (r"sample_kernel", "sample"),
