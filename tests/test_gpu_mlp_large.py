@@ -2,8 +2,9 @@
 prefill GEMMs) on the GPU against the oracle: the Qwen3-4B-shaped bsgemm and
 MXFP8 workloads at M that are one row, ragged, one tile and several tiles
 (whole outputs), M = 4096 on sampled rows (the MLP acts on each row alone,
-so a sampled row is the oracle's M = 1 case), strided x / y, and agreement
-with the decode kernel where both apply."""
+so a sampled row is the oracle's M = 1 case), the tiny workload's shape,
+strided x / y, agreement with the decode kernel where both apply, and
+bit-identical repeats on a reused workspace."""
 
 import numpy as np
 import pytest
@@ -124,3 +125,33 @@ def test_invalid_sizes_rejected():
         ops.swiglu_mlp_fp8_large(x, pd, pgu, mode)              # operands swapped
     assert ops._lib.load().swiglu_mlp_fp8_large_workspace_size(4, 2560, 100, mode) == 0
     assert ops._lib.load().swiglu_mlp_fp8_large_workspace_size(0, 2560, 9728, mode) == 0
+
+
+@pytest.mark.parametrize("M", [5, 200])
+def test_tiny_workload_shape(M):
+    """hidden 256, inter 1024: two K blocks for the gate/up GEMM, 16 gate/up
+    tiles per row block, one or two row tiles."""
+    need_gpu()
+    mode, _, pgu, pd, deq = _setup(inputs.W_TINY, 256, 1024)
+    xb = inputs.mlp_activations(inputs.W_TINY, M, 256, extra=980 + M)
+    y = ops.swiglu_mlp_fp8_large(to_dev_bf16(xb), pgu, pd, mode)
+    torch.cuda.synchronize()
+    assert max_rel_err(from_dev_bf16(y), omlp.swiglu_mlp(f32(xb), *deq, mode)["y"]) <= TOL_FP8_PATH
+
+
+@pytest.mark.parametrize("workload", [inputs.W_BSGEMM, inputs.W_MXFP8])
+def test_deterministic_with_reused_workspace(workload):
+    """Two calls on one workspace, the second after a larger call, give the
+    same bits (no state carried between calls)."""
+    need_gpu()
+    H, I = _shape(workload)
+    mode, _, pgu, pd, _ = _setup(workload, H, I)
+    x = to_dev_bf16(inputs.mlp_activations(workload, 150, H, extra=990))
+    big = to_dev_bf16(inputs.mlp_activations(workload, 600, H, extra=991))
+    ws = torch.empty(int(ops._lib.load().swiglu_mlp_fp8_large_workspace_size(600, H, I, mode)), dtype=torch.uint8,
+                     device="cuda")
+    a = ops.swiglu_mlp_fp8_large(x, pgu, pd, mode, workspace=ws).clone()
+    ops.swiglu_mlp_fp8_large(big, pgu, pd, mode, workspace=ws)
+    b = ops.swiglu_mlp_fp8_large(x, pgu, pd, mode, workspace=ws)
+    torch.cuda.synchronize()
+    assert torch.equal(a.view(torch.int16), b.view(torch.int16))
