@@ -49,7 +49,21 @@ struct GemmLargeArgs {
     int tiles_m, tiles_n;
     uint16_t* c; int64_t ldc;                 // ldc in elements of C
     int c_f32;                                // C is fp32 (not bf16)
+    // K split of the last tiles: tiles n_full .. run as `split` workgroups
+    // each (K blocks s KB / split .. (s + 1) KB / split), which write fp32
+    // partial tiles [piece][128][128] to `part` for split_reduce_kernel
+    int n_full = 1 << 30, split = 1;
+    float* part = nullptr;
 };
+
+// Tile t of the walk: groups of kGlGroupM tile rows, column by column.
+__device__ __forceinline__ void tile_coords(int t, int tiles_m, int tiles_n, int& tm, int& tn) {
+    const int per_group = kGlGroupM * tiles_n;
+    const int grp = t / per_group, first_m = grp * kGlGroupM;
+    const int gm = min(tiles_m - first_m, kGlGroupM);
+    tm = first_m + (t % per_group) % gm;
+    tn = (t % per_group) / gm;
+}
 
 // One lane's 32 operand bytes: 16 at p and 16 at p + hi (a row-major row:
 // p = row start + K block + 16 * lane group, hi = 64; a packed fragment:
@@ -98,12 +112,19 @@ __global__ __launch_bounds__(256, 2) void gemm_large_mx_kernel(GemmLargeArgs a) 
 
     // tile order: contiguous runs per XCD, grouped rows inside a run
     const int n_tiles = a.tiles_m * a.tiles_n;
-    int t = blockIdx.x;
-    if (n_tiles % 8 == 0) t = (t % 8) * (n_tiles / 8) + t / 8;
-    const int per_group = kGlGroupM * a.tiles_n;
-    const int grp = t / per_group, first_m = grp * kGlGroupM;
-    const int gm = min(a.tiles_m - first_m, kGlGroupM);
-    const int tm = first_m + (t % per_group) % gm, tn = (t % per_group) / gm;
+    const int n_full = min(a.n_full, n_tiles);
+    int t = blockIdx.x, kb0 = 0, kb1 = a.KB, piece = -1;
+    if (t >= n_full) {                         // one K piece of a last tile
+        piece = t - n_full;
+        const int sp = piece % a.split;
+        t = n_full + piece / a.split;
+        kb0 = sp * a.KB / a.split;
+        kb1 = (sp + 1) * a.KB / a.split;
+    } else if (n_full % 8 == 0) {
+        t = (t % 8) * (n_full / 8) + t / 8;
+    }
+    int tm, tn;
+    tile_coords(t, a.tiles_m, a.tiles_n, tm, tn);
     const int m0 = tm * kGlBM, n0 = tn * kGlBN;
     const int g4 = lane >> 4;
 
@@ -130,7 +151,7 @@ __global__ __launch_bounds__(256, 2) void gemm_large_mx_kernel(GemmLargeArgs a) 
     constexpr int kHi = PACKED ? 1024 : 64;           // offset of the lane's second 16 bytes
     v8i ga0, ga1, gb0, gb1;
     auto gload = [&](int kb) {
-        const int ko = kb * kStep;
+        const int ko = (kb0 + kb) * kStep;
         ga0 = ld_row32(pa0 + ko, kHi); ga1 = ld_row32(pa1 + ko, kHi);
         gb0 = ld_row32(pb0 + ko, kHi); gb1 = ld_row32(pb1 + ko, kHi);
     };
@@ -163,13 +184,13 @@ __global__ __launch_bounds__(256, 2) void gemm_large_mx_kernel(GemmLargeArgs a) 
         if constexpr (BS) {
             BsScales sc;
 #pragma unroll
-            for (int i = 0; i < 4; ++i) sc.a[i] = *reinterpret_cast<const float4*>(psa + kb * 64 + 16 * i);
-            sc.b = psb[kb * 64];
+            for (int i = 0; i < 4; ++i) sc.a[i] = *reinterpret_cast<const float4*>(psa + (kb0 + kb) * 64 + 16 * i);
+            sc.b = psb[(kb0 + kb) * 64];
             return sc;
         } else {
         v8i e;
         if (PACKED) {
-            const uint32_t wa = pea[kb * 64], wb = peb[kb * 64];
+            const uint32_t wa = pea[(kb0 + kb) * 64], wb = peb[(kb0 + kb) * 64];
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
                 e[i] = (wa >> (8 * i)) & 0xFF;
@@ -177,7 +198,7 @@ __global__ __launch_bounds__(256, 2) void gemm_large_mx_kernel(GemmLargeArgs a) 
             }
             return e;
         }
-        const uint32_t g = (uint32_t)(kb * 4 + g4);
+        const uint32_t g = (uint32_t)((kb0 + kb) * 4 + g4);
         const uint32_t ga = g * aeg, gb = g * beg;
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
@@ -235,7 +256,7 @@ __global__ __launch_bounds__(256, 2) void gemm_large_mx_kernel(GemmLargeArgs a) 
         asm volatile("" ::: "memory");
     };
 
-    const int KB = a.KB;
+    const int KB = kb1 - kb0;
     gload(0);
     Sc e_cur = exps(0), e_next = e_cur;
     swrite(smem);
@@ -259,6 +280,17 @@ __global__ __launch_bounds__(256, 2) void gemm_large_mx_kernel(GemmLargeArgs a) 
         lds_sync();
     }
 
+    if (piece >= 0) {
+        float* pp = a.part + (int64_t)piece * (kGlBM * kGlBN);
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+#pragma unroll
+            for (int j = 0; j < 4; ++j)
+#pragma unroll
+                for (int q = 0; q < 4; ++q)
+                    pp[(64 * wm + 16 * i + 4 * g4 + q) * kGlBN + 64 * wn + 16 * j + (lane & 15)] = acc[i][j][q];
+        return;
+    }
     if constexpr (SWI) {
         // the loop ended on a barrier: every wave is done with the stages
         float* ex = reinterpret_cast<float*>(smem) + wm * 4096;       // 16 KiB per row half
@@ -406,6 +438,48 @@ __global__ __launch_bounds__(256) void pack_mx_kernel(PackArgs a) {
     }
 }
 
+// Sums the K pieces of each split tile u (tile n_full + u) into bf16 C.
+struct SplitReduceArgs {
+    const float* part;
+    int split, n_full, tiles_m, tiles_n, M;
+    uint16_t* c; int64_t ldc;
+};
+
+__global__ __launch_bounds__(256) void split_reduce_kernel(SplitReduceArgs a) {
+    const int u = blockIdx.x;
+    int tm, tn;
+    tile_coords(a.n_full + u, a.tiles_m, a.tiles_n, tm, tn);
+    const float* p = a.part + (int64_t)u * a.split * (kGlBM * kGlBN);
+#pragma unroll 4
+    for (int i = 0; i < kGlBM * kGlBN / 1024; ++i) {
+        const int idx = (i * 256 + (int)threadIdx.x) * 4;
+        const int row = tm * kGlBM + idx / kGlBN, col = tn * kGlBN + idx % kGlBN;
+        float4 v = *reinterpret_cast<const float4*>(p + idx);
+        for (int sp = 1; sp < a.split; ++sp) {
+            const float4 w = *reinterpret_cast<const float4*>(p + (int64_t)sp * (kGlBM * kGlBN) + idx);
+            v.x += w.x; v.y += w.y; v.z += w.z; v.w += w.w;
+        }
+        if (row >= a.M) continue;
+        const uint32_t lo = (uint32_t)(uint16_t)f32_to_bf16(v.x) | ((uint32_t)(uint16_t)f32_to_bf16(v.y) << 16);
+        const uint32_t hi = (uint32_t)(uint16_t)f32_to_bf16(v.z) | ((uint32_t)(uint16_t)f32_to_bf16(v.w) << 16);
+        *reinterpret_cast<uint2*>(a.c + (int64_t)row * a.ldc + col) = make_uint2(lo, hi);
+    }
+}
+
+// When the last round of tiles would fill at most half of the chip's
+// workgroup slots (256 CUs x 2 resident workgroups), split those tiles over
+// K so that they finish in a fraction of a tile's time.
+constexpr int64_t kGlSlots = 512;
+static void split_policy(int64_t n_tiles, int KB, int64_t& n_full, int& split) {
+    const int64_t rem = n_tiles % kGlSlots;
+    n_full = n_tiles;
+    split = 1;
+    if (n_tiles > kGlSlots && rem > 0 && rem <= kGlSlots / 2 && KB >= 16) {
+        n_full = n_tiles - rem;
+        split = (int)std::min<int64_t>(4, kGlSlots / rem);
+    }
+}
+
 // quant_pack: rows of x (bf16 [M, K]) or of h (F32: fp32 [M, K]) quantised in the
 // groups the GEMM reads (MX: 1x32 UE8M0; BS: 1x128 fp32) straight into the
 // packed operand layout (fp8_pack_mx / fp8_pack_bs).  One wave per (16-row
@@ -476,14 +550,17 @@ static size_t packed_bytes(int64_t R, int64_t K, bool bs) {
     return (size_t)(Rp * K + (bs ? Rp * (K / 128) * 4 : Rp * (K / 32)));
 }
 
-struct MlpLargePlan { size_t off_x, off_gu, off_h, total; };
+struct MlpLargePlan { size_t off_x, off_gu, off_h, off_part, total; int64_t n_full; int split; };
 static MlpLargePlan plan_mlp_large(int64_t M, int64_t H, int64_t I, bool bs) {
     MlpLargePlan p;
     auto al = [](size_t v) { return (v + 255) / 256 * 256; };
     p.off_x = 0;
     p.off_gu = al(packed_bytes(M, H, bs));
     p.off_h = p.off_gu + (bs ? al((size_t)M * I * 4) : 0);        // fp32 h (bsgemm only)
-    p.total = p.off_h + al(packed_bytes(M, I, bs));
+    p.off_part = p.off_h + al(packed_bytes(M, I, bs));
+    const int64_t nt = (M + 127) / 128 * (H / kGlBN);             // down GEMM tiles
+    split_policy(nt, (int)(I / 128), p.n_full, p.split);
+    p.total = p.off_part + (p.split > 1 ? (size_t)(nt - p.n_full) * p.split * kGlBM * kGlBN * 4 : 0);
     return p;
 }
 
@@ -558,11 +635,23 @@ extern "C" int swiglu_mlp_fp8_large(const uint16_t* x, int64_t ld_x, int64_t M, 
     d.M = (int)M; d.N = (int)hidden; d.KB = (int)(inter / 128);
     d.tiles_m = (int)(Mp / kGlBM); d.tiles_n = (int)(hidden / kGlBN);
     d.c = y; d.ldc = ld_y; d.c_f32 = 0;
+    const int64_t nt = (int64_t)d.tiles_m * d.tiles_n;
+    d.n_full = (int)p.n_full; d.split = p.split;
+    d.part = reinterpret_cast<float*>(ws + p.off_part);
+    const unsigned blocks = (unsigned)(p.n_full + (nt - p.n_full) * p.split);
     if (bs)
-        FP8S_LAUNCH("mlpl_down", (gemm_large_mx_kernel<true, true>), dim3((unsigned)(d.tiles_m * d.tiles_n)), dim3(256), 0, st, d);
+        FP8S_LAUNCH("mlpl_down", (gemm_large_mx_kernel<true, true>), dim3(blocks), dim3(256), 0, st, d);
     else
-        FP8S_LAUNCH("mlpl_down", (gemm_large_mx_kernel<true, false>), dim3((unsigned)(d.tiles_m * d.tiles_n)), dim3(256), 0, st, d);
-    return check_launch("swiglu_mlp_fp8_large (down)");
+        FP8S_LAUNCH("mlpl_down", (gemm_large_mx_kernel<true, false>), dim3(blocks), dim3(256), 0, st, d);
+    if ((rc = check_launch("swiglu_mlp_fp8_large (down)"))) return rc;
+    if (p.split > 1) {
+        SplitReduceArgs r;
+        r.part = d.part; r.split = p.split; r.n_full = (int)p.n_full; r.tiles_m = d.tiles_m; r.tiles_n = d.tiles_n;
+        r.M = (int)M; r.c = y; r.ldc = ld_y;
+        FP8S_LAUNCH("mlpl_down_reduce", split_reduce_kernel, dim3((unsigned)(nt - p.n_full)), dim3(256), 0, st, r);
+        rc = check_launch("swiglu_mlp_fp8_large (down reduce)");
+    }
+    return rc;
 }
 
 extern "C" size_t fp8_mx_packed_bytes(int64_t R, int64_t K) {

@@ -59,6 +59,7 @@ KERNELS = [
     (r"gemm_large_mx_kernel<true, true", "gemm_large_bs_packed"),
     (r"gemm_large_mx_kernel<true", "gemm_large_mx_packed"),
     (r"gemm_large_mx_kernel", "gemm_large_mx"),
+    (r"split_reduce_kernel", "mlp_large_down_reduce"),
     (r"quant_pack_kernel<\w+, true>", "mlp_large_hq"),
     (r"quant_pack_kernel", "mlp_large_xq"),
     (r"pack_mx_kernel", "pack_mx"),

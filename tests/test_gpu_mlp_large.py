@@ -71,14 +71,18 @@ def test_matches_oracle(workload, M):
 
 
 @pytest.mark.parametrize("workload", [inputs.W_BSGEMM, inputs.W_MXFP8])
-def test_m4096_sampled_rows(workload):
+@pytest.mark.parametrize("M", [4096, 3300])
+def test_large_m_sampled_rows(workload, M):
+    """M = 4096 (640 down-GEMM tiles) and 3300 (520): the tiles past the
+    last full round of 512 run split over K, and they hold the last row
+    tiles, so rows near M are sampled on purpose."""
     need_gpu()
     H, I = _shape(workload)
     mode, _, pgu, pd, deq = _setup(workload, H, I)
-    M = 4096
-    xb = inputs.mlp_activations(workload, M, H, extra=950)
+    xb = inputs.mlp_activations(workload, M, H, extra=950 + M)
     y = from_dev_bf16(ops.swiglu_mlp_fp8_large(to_dev_bf16(xb), pgu, pd, mode))
-    rows = np.unique(np.concatenate([[0, 127, 128, M - 1], np.random.default_rng(11).integers(0, M, 20)]))
+    rng = np.random.default_rng(11)
+    rows = np.unique(np.concatenate([[0, 127, 128, M - 1], rng.integers(0, M, 12), rng.integers(M - 200, M, 12)]))
     for r in rows:
         ref = omlp.swiglu_mlp(f32(xb[r:r + 1]), *deq, mode)["y"]
         assert max_rel_err(y[r:r + 1], ref) <= TOL_FP8_PATH, r
