@@ -359,9 +359,9 @@ __device__ __forceinline__ void attn_split_body(const AttnArgs& a) {
 }
 
 // Balanced split: the valid prefixes of all sequences, concatenated in
-// sequence order (T positions per KV head), are cut into W = S * K equal
-// ranges of at most kMaxChunk positions, S the workgroups the CUs hold per KV
-// head and K = ceil(T / (S * kMaxChunk)); workgroup (w, g) takes ranges
+// sequence order (T positions per KV head), are cut into W = min(S * K, T)
+// equal ranges of at most kMaxChunk positions (none empty), S the workgroups
+// the CUs hold per KV head and K = ceil(T / (S * kMaxChunk)); workgroup (w, g) takes ranges
 // w*K .. w*K + K - 1 and attends each in pieces, one per sequence it
 // touches.  Piece (v, b) of range v writes record v + b (distinct: along the
 // concatenation one of v and b grows at every cut), so the records of
@@ -399,7 +399,10 @@ __device__ __forceinline__ void attn_bal_body(const AttnArgs& a) {
     const int64_t T = s_pre[a.B];
     const int64_t per_wg = (int64_t)a.bal_slots * kMaxChunk;
     const int K = (int)max((int64_t)1, (T + per_wg - 1) / per_wg);
-    const int W = a.bal_slots * K;
+    // At most T ranges, so that none is empty (each then holds >= T / W >= 1
+    // positions): the ranges a sequence spans are then exactly the records
+    // its pieces write.  W < S * K only when K == 1.
+    const int W = (int)min((int64_t)a.bal_slots * K, T);
     if (blockIdx.x == 0) {
         for (int b = threadIdx.x; b < a.B; b += 256) {
             const int64_t p0 = s_pre[b], Lb = s_pre[b + 1] - p0;
@@ -413,7 +416,7 @@ __device__ __forceinline__ void attn_bal_body(const AttnArgs& a) {
     }
     const int wg = blockIdx.x / a.Hkv, g = blockIdx.x % a.Hkv;
     if (wg >= a.bal_slots || T == 0) return;
-    for (int v = wg * K; v < wg * K + K; ++v) {
+    for (int v = wg * K; v < wg * K + K && v < W; ++v) {
         const int64_t R0 = (int64_t)v * T / W, R1 = (int64_t)(v + 1) * T / W;
         int lo = 0, hi = a.B;                  // first sequence with s_pre[b + 1] > R0
         while (lo < hi) {

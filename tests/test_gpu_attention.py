@@ -181,17 +181,64 @@ def test_balanced_split_mixed_and_invalid_lengths():
     assert max_rel_err(from_dev_bf16(out[keep]), ref) <= TOL_BF16_ATTN
 
 
-@pytest.mark.parametrize("case", ["short_many", "one_long"])
+def _balanced_taken(ws, kv):
+    """The balanced split leaves a table of (first record, record count) int32
+    pairs at the start of its workspace; a chunked split stores fp32 records
+    there instead.  Every valid prefix has at least one record and at most
+    as many as it has positions."""
+    t = ws[: 8 * len(kv)].view(torch.int32).view(-1, 2).cpu().numpy()
+    return bool(np.all(t[:, 1] >= 1) and np.all(t[:, 1] <= kv) and np.all(t[:, 0] >= 0))
+
+
+@pytest.mark.parametrize("case", ["short_many", "one_long", "more_ranges_than_positions"])
 def test_balanced_split_pieces_across_many_sequences(case):
-    """Ranges that span many sequences (tiny prefixes) and more ranges than
-    positions (every prefix one position)."""
+    """Ranges that span many sequences (tiny prefixes), and batches whose
+    prefixes total fewer positions than the balanced split has workgroups
+    (every prefix one position, or a few), so that there are more workgroup
+    slots than positions."""
     need_gpu()
-    B, cap = (64, 64) if case == "short_many" else (20, 2048)
     if case == "short_many":
+        B, cap = 64, 1024
         kv = np.ones(B, np.int32)
-    else:
+    elif case == "one_long":
+        B, cap = 20, 2048
         kv = (np.arange(B) % 3 + 1).astype(np.int32)
         kv[13] = cap
+    else:
+        B, cap = 16, 1024
+        kv = (np.arange(B) % 4 + 2).astype(np.int32)
     qb, kb, vb, kc, vc = _make(inputs.W_ATTN, B, 32, 8, 128, cap, kv, extra=202)
-    out = _run(qb, kc, vc, kv, cap)
+    ws = torch.full((ops.attn_workspace_bytes(B, 32, 128, cap),), 0xFF, dtype=torch.uint8, device="cuda")
+    out = ops.gqa_decode_attn(to_dev_bf16(qb), kc, vc, torch.from_numpy(kv).cuda(), cap, workspace=ws)
+    torch.cuda.synchronize()
+    assert _balanced_taken(ws, kv), "the balanced split did not run"
     assert max_rel_err(from_dev_bf16(out), _oracle(qb, kb, vb, kv)) <= TOL_BF16_ATTN
+
+
+@pytest.mark.parametrize("shape", [(16, 32, 8, 128, 5), (16, 4, 1, 64, 37)])
+def test_balanced_split_reused_workspace_few_positions(shape):
+    """A workspace reused across calls keeps what earlier calls (or garbage)
+    left there: here it is first filled with 0xFF bytes (NaN records), then a
+    call at long prefixes leaves its own records, and a call whose prefixes
+    total fewer positions than the balanced split has workgroups must still
+    give the oracle's output, bit-identical to the same call on a fresh
+    workspace."""
+    need_gpu()
+    B, Hq, Hkv, D, L = shape
+    cap = 1024
+    kv = np.full(B, L, np.int32)
+    qb, kb, vb, kc, vc = _make(inputs.W_ATTN, B, Hq, Hkv, D, cap, kv, extra=300 + L)
+    ws = torch.full((ops.attn_workspace_bytes(B, Hq, D, cap),), 0xFF, dtype=torch.uint8, device="cuda")
+    kvd = torch.from_numpy(kv).cuda()
+    out = ops.gqa_decode_attn(to_dev_bf16(qb), kc, vc, kvd, cap, workspace=ws)
+    torch.cuda.synchronize()
+    assert _balanced_taken(ws, kv), "the balanced split did not run"
+    ref = _oracle(qb, kb, vb, kv)
+    assert max_rel_err(from_dev_bf16(out), ref) <= TOL_BF16_ATTN
+    # records of a long-prefix call, then the short call again on that workspace
+    long_kv = torch.full((B,), cap, dtype=torch.int32, device="cuda")
+    ops.gqa_decode_attn(to_dev_bf16(qb), kc, vc, long_kv, cap, workspace=ws)
+    out2 = ops.gqa_decode_attn(to_dev_bf16(qb), kc, vc, kvd, cap, workspace=ws)
+    fresh = ops.gqa_decode_attn(to_dev_bf16(qb), kc, vc, kvd, cap)
+    torch.cuda.synchronize()
+    assert torch.equal(out, out2) and torch.equal(out, fresh)

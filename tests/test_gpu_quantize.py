@@ -96,3 +96,35 @@ def test_mx_scale_strides_honoured():
     _, s_k = _run(bits, ops.Q_MX_1x32, k_major=True)
     _, s_r = _run(bits, ops.Q_MX_1x32, k_major=False)
     assert np.array_equal(s_k, s_r)
+
+
+def test_division_and_lower_clamp_cases_bit_exact():
+    """The inputs that pin the oracle's fp32 division (an exact quotient just
+    above an e4m3 midpoint whose fp32 rounding lands on it) and the UE8M0
+    lower clamp (groups with amax in [2^-133, 2^-119)), through the
+    standalone quantiser in all three modes: bytes and scales bit-exact."""
+    need_gpu()
+    from test_oracle_fp8 import _DIV_CASES
+    rows = []
+    for amax, x in _DIV_CASES:
+        r = np.zeros(256, np.float32)
+        r[3], r[77], r[130], r[200] = amax, x, -amax, -x
+        rows.append(r)
+        rows.append(r * np.float32(2.0 ** -60))
+        rows.append(r * np.float32(2.0 ** 40))
+    for vals in ([2.0 ** -120], [2.0 ** -133], [1.5 * 2.0 ** -129, -2.0 ** -128], [1.75 * 2.0 ** -120],
+                 [2.0 ** -119], [2.0 ** -118, 2.0 ** -133]):
+        r = np.zeros(256, np.float32)
+        r[:len(vals)] = vals
+        r[100:100 + len(vals)] = vals
+        rows.append(r)
+    while len(rows) % 128:
+        rows.append(rows[len(rows) % 12])
+    x = np.stack(rows)
+    xb = inputs.f32_to_bf16_bits(x)
+    assert np.array_equal(f32(xb), x), "the cases must be exact bf16 values"
+    for mode in (ops.Q_ACT_1x128, ops.Q_WGT_128x128, ops.Q_MX_1x32):
+        q, s = _run(xb, mode)
+        qo, so = _oracle(xb, mode)
+        assert np.array_equal(q, qo), f"mode {mode}: {np.count_nonzero(q != qo)} bytes differ"
+        assert np.array_equal(s, so), f"mode {mode}: scales differ"

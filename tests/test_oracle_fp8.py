@@ -182,3 +182,111 @@ def test_negative_underflow_keeps_sign():
 def test_group_must_divide_shape(gr, gc):
     with pytest.raises(ValueError):
         fp8.quant_block_fp32(np.zeros((128, 256), np.float32), gr, gc)
+
+
+# ---- exact-arithmetic pins of the bsgemm division and the UE8M0 lower clamp ----
+# These rebuild each rounding step with fractions.Fraction (exact rationals),
+# so they do not rely on NumPy's float32 arithmetic.
+
+from fractions import Fraction  # noqa: E402
+
+
+def _round_binary(q, mant_bits, min_exp):
+    """Round the exact rational q to the nearest value with mant_bits stored
+    mantissa bits and exponent >= min_exp (subnormals below), ties to even."""
+    if q == 0:
+        return Fraction(0)
+    sign = -1 if q < 0 else 1
+    a = abs(q)
+    e = a.numerator.bit_length() - a.denominator.bit_length()
+    if Fraction(2) ** e > a:
+        e -= 1                                  # now 2^e <= a < 2^(e+1)
+    e = max(e, min_exp)
+    quantum = Fraction(2) ** (e - mant_bits)
+    n, r = divmod(a, quantum)
+    n = int(n)
+    if r * 2 > quantum or (r * 2 == quantum and n % 2 == 1):
+        n += 1
+    return sign * n * quantum
+
+
+def _fp32(q):
+    return _round_binary(q, 23, -126)
+
+
+def _e4m3(q):
+    v = _round_binary(q, 3, -6)
+    return max(min(v, Fraction(448)), Fraction(-448))
+
+
+# (amax, x): bf16 values for which e4m3(fp32(x / s)), s = fp32(amax / 448),
+# differs from both e4m3 of the exact quotient and e4m3(fp32(x * fp32(1 / s))).
+# Found by a search over bf16 pairs; each is checked below with exact rationals.
+_DIV_CASES = [(1.078125, 0.10107421875), (1.59375, 0.07470703125), (1.625, 0.3046875),
+              (1.296875, 0.97265625)]
+
+
+def _division_readings(amax, x):
+    s = _fp32(Fraction(amax) / 448)
+    fp32_div = _e4m3(_fp32(Fraction(x) / s))
+    exact = _e4m3(Fraction(x) / s)
+    recip = _e4m3(_fp32(Fraction(x) * _fp32(1 / s)))
+    return s, fp32_div, exact, recip
+
+
+def test_bsgemm_division_is_fp32_correctly_rounded():
+    """The bsgemm rule divides in fp32 (correctly rounded) before the e4m3
+    rounding.  Each case is built so that the exact quotient lies just above
+    an e4m3 rounding midpoint and its fp32 rounding lands on it (a tie that
+    goes to the even code), so dividing exactly, in fp64, or multiplying by
+    an fp32 reciprocal each give a different code: all three readings are
+    computed here in exact arithmetic and the oracle must give the first."""
+    for amax, x in _DIV_CASES:
+        s, want, exact, recip = _division_readings(amax, x)
+        assert want != exact and want != recip, "the case does not tell the readings apart"
+        for shape, fn, slot in (((1, 128), fp8.quant_act_1x128, (0, 77)),
+                                ((128, 128), fp8.quant_weight_128x128, (93, 5))):
+            blk = np.zeros(shape, np.float32)
+            blk[0, 0] = amax
+            blk[slot] = x
+            blk[slot[0], (slot[1] + 1) % 128] = -x
+            q, sc = fn(blk)
+            assert Fraction(float(sc.reshape(-1)[0])) == s
+            got = Fraction(float(fp8.e4m3_decode(q[slot])))
+            assert got == want
+            assert Fraction(float(fp8.e4m3_decode(q[slot[0], (slot[1] + 1) % 128]))) == -want
+            assert Fraction(float(fp8.e4m3_decode(q[0, 0]))) == _e4m3(_fp32(Fraction(amax) / s))
+
+
+def test_bsgemm_division_cases_reach_the_fp64_path():
+    """The fp64 quotient also rounds to the exact reading's code here, so an
+    oracle that divided in float64 would fail the pin above."""
+    for amax, x in _DIV_CASES:
+        s, want, exact, _ = _division_readings(amax, x)
+        q64 = fp8.e4m3_encode(np.float64(x) / np.float64(float(s)))
+        assert Fraction(float(fp8.e4m3_decode(q64))) == exact != want
+
+
+def test_ue8m0_lower_clamp():
+    """Blocks whose largest magnitude lies in [2^-133, 2^-119) (bf16
+    subnormals included) have floor(log2 amax) - 8 + 127 < 0: the shared
+    exponent clamps to 0, X = 2^-127, and the codes are e4m3(x * 2^127),
+    written out here by hand."""
+    # (values of one 32-group, expected exponent byte, expected codes)
+    cases = [
+        ([2.0 ** -120], 0, [0x70]),                          # 2^7 = 128: exp 14, mant 0
+        ([2.0 ** -133], 0, [0x08]),                          # 2^-6, smallest normal e4m3
+        ([1.5 * 2.0 ** -129, -2.0 ** -128], 0, [0x2C, 0xB0]),  # 0.375, -0.5
+        ([1.75 * 2.0 ** -120], 0, [0x76]),                   # 224: exp 14, mant 6
+        ([1.0 * 2.0 ** -119], 0, [0x78]),                    # amax = 2^-119 -> E = 0, 256 (exp 15, mant 0)
+        ([2.0 ** -118], 1, [0x78]),                          # first exponent above the clamp: 2^-118 / 2^-126
+    ]
+    for vals, e_want, codes in cases:
+        blk = np.zeros((1, 32), np.float32)
+        blk[0, :len(vals)] = vals
+        q, E = fp8.quant_mx_1x32(blk)
+        assert int(E[0, 0]) == e_want
+        assert list(q[0, :len(vals)]) == codes
+        assert not q[0, len(vals):].any()
+    assert int(fp8.ue8m0_exponent(np.float64(2.0 ** -133))) == 0
+    assert int(fp8.ue8m0_exponent(np.float64(2.0 ** -119 * 1.99))) == 0
