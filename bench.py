@@ -89,7 +89,7 @@ class Workload:
     """Rotating sets of GPU-resident weights, activations and KV caches."""
 
     def __init__(self, torch, ops, B, M, mode, n_sets, kv_len, with_attn=True, with_mlp=True, mx_kv=False,
-                 page=0):
+                 page=0, packed=False):
         self.torch, self.ops = torch, ops
         self.mx_kv = mx_kv
         self.page = page
@@ -103,8 +103,9 @@ class Workload:
                 ws = []
                 for shape in ((I, H), (I, H), (H, I)):
                     wb = (torch.randn(shape, generator=g, device="cuda") * 0.02).to(torch.bfloat16)
-                    ws.append(ops.quantize_weight(wb, mode))
-                    del wb
+                    qw = ops.quantize_weight(wb, mode)
+                    ws.append(ops.pack_weight(qw) if packed else qw)
+                    del wb, qw
                 st["w"] = ws
                 x = torch.randn((M, H), generator=g, device="cuda")
                 if mode == ops.MLP_MXFP8:
@@ -529,13 +530,15 @@ def percentiles(v):
 
 
 def mlp_sweep(torch, ops, inputs, n_sets):
-    """The MLP alone at M in {1, 8, 32, 64, 128}, bsgemm and MXFP8, on
-    rotating weight sets."""
+    """The MLP alone at M in {1, 8, 32, 64, 128}, bsgemm and MXFP8, with
+    row-major and fragment-packed weights, on rotating weight sets."""
     kv_len = inputs.kv_lengths(inputs.W_ATTN, 64, 234, 400)
-    sweep = {"mlp_bsgemm": {}, "mlp_mxfp8": {}}
-    for mode, key in ((ops.MLP_BSGEMM, "mlp_bsgemm"), (ops.MLP_MXFP8, "mlp_mxfp8")):
+    sweep = {}
+    for mode, key, packed in ((ops.MLP_BSGEMM, "mlp_bsgemm", False), (ops.MLP_MXFP8, "mlp_mxfp8", False),
+                              (ops.MLP_BSGEMM, "mlp_bsgemm_packed", True), (ops.MLP_MXFP8, "mlp_mxfp8_packed", True)):
+        sweep[key] = {}
         for M in (1, 8, 32, 64, 128):
-            w = Workload(torch, ops, 1, M, mode, n_sets, kv_len, with_attn=False)
+            w = Workload(torch, ops, 1, M, mode, n_sets, kv_len, with_attn=False, packed=packed)
             t, _, per = time_parts(torch, ops, w, [w.mlp], 20, 5)
             gb = mlp_bytes(M, mode) / (t * 1e-3) / 1e9
             sweep[key][M] = {"us": t * 1e3, "tokens/s": M / (t * 1e-3), "GB/s": gb, "frac": gb / PEAK_HBM_GBS,

@@ -31,14 +31,26 @@ __device__ __forceinline__ v8i load_frag(const uint8_t* base, int lane) {
 
 typedef __attribute__((address_space(3))) void lds_void;
 
-// Stream weight fragment (rows n0..n0+15, K block kb) of W [N, K] into LDS at
+// A weight W [N, K] e4m3 is row-major (row stride ld > 0) or, for ld == 0,
+// fragment-packed: the MFMA operand fragment of rows 16 nb .. 16 nb + 15 and
+// K block kb is 2 KiB at (nb * KB + kb) * 2048 (KB = K / 128), lane l's
+// operand bytes 0..15 at 16 l and 16..31 at 1024 + 16 l -- every wave load
+// of a fragment reads two contiguous KiB.  wfrag_off: where lane's bytes
+// 0..15 of fragment (n0 / 16, kb) are; its bytes 16..31 follow wfrag_hi later.
+__device__ __forceinline__ int64_t wfrag_off(int64_t ld, int KB, int n0, int kb, int lane) {
+    return ld ? (int64_t)(n0 + (lane & 15)) * ld + kb * 128 + 16 * (lane >> 4)
+              : ((int64_t)(n0 >> 4) * KB + kb) * kFrag + 16 * lane;
+}
+__device__ __forceinline__ int wfrag_hi(int64_t ld) { return ld ? 64 : 1024; }
+
+// Stream weight fragment (rows n0..n0+15, K block kb) of W into LDS at
 // byte offset `dst`: the first 1 KiB holds every lane's operand bytes 0..15
 // (K = kb*128 + 16g ..), the second its bytes 16..31 (K = kb*128 + 64 + 16g ..).
-__device__ __forceinline__ void stage_w(const uint8_t* w, int64_t ld, int n0, int kb, uint8_t* lds, int dst,
+__device__ __forceinline__ void stage_w(const uint8_t* w, int64_t ld, int KB, int n0, int kb, uint8_t* lds, int dst,
                                         int lane) {
-    const uint8_t* src = w + (int64_t)(n0 + (lane & 15)) * ld + kb * 128 + 16 * (lane >> 4);
+    const uint8_t* src = w + wfrag_off(ld, KB, n0, kb, lane);
     __builtin_amdgcn_global_load_lds(src, (lds_void*)(lds + dst), 16, 0, 0);
-    __builtin_amdgcn_global_load_lds(src + 64, (lds_void*)(lds + dst + 1024), 16, 0, 0);
+    __builtin_amdgcn_global_load_lds(src + wfrag_hi(ld), (lds_void*)(lds + dst + 1024), 16, 0, 0);
 }
 
 __device__ __forceinline__ v8i lds_frag(const uint8_t* lds, int off, int lane) {
@@ -272,10 +284,10 @@ __device__ __forceinline__ void quant_frag_mx(const float (&v)[32], v8i& q, int&
 
 // Weight operand straight into registers: row n0 + lane%16, K bytes
 // kb*128 + [16g, +16) and kb*128 + [64+16g, +16), g = lane/16.
-__device__ __forceinline__ v8i load_w(const uint8_t* w, int64_t ld, int n0, int kb, int lane) {
-    const uint8_t* row = w + (int64_t)(n0 + (lane & 15)) * ld + kb * 128 + 16 * (lane >> 4);
-    const uint4 lo = *reinterpret_cast<const uint4*>(row);
-    const uint4 hi = *reinterpret_cast<const uint4*>(row + 64);
+__device__ __forceinline__ v8i load_w(const uint8_t* w, int64_t ld, int KB, int n0, int kb, int lane) {
+    const uint8_t* p = w + wfrag_off(ld, KB, n0, kb, lane);
+    const uint4 lo = *reinterpret_cast<const uint4*>(p);
+    const uint4 hi = *reinterpret_cast<const uint4*>(p + wfrag_hi(ld));
     v8i r;
     r[0] = lo.x; r[1] = lo.y; r[2] = lo.z; r[3] = lo.w;
     r[4] = hi.x; r[5] = hi.y; r[6] = hi.z; r[7] = hi.w;

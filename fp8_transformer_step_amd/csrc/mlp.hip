@@ -157,8 +157,8 @@ __global__ __launch_bounds__(256) void gu_small_kernel(MlpArgs a) {
 #pragma unroll
     for (int i = 0; i < kWaveKb; ++i)
         if (lo + i < hi) {
-            bg[i] = load_w(a.wg, a.ldg, n0, lo + i, lane);
-            bu[i] = load_w(a.wu, a.ldu, n0, lo + i, lane);
+            bg[i] = load_w(a.wg, a.ldg, a.KBH, n0, lo + i, lane);
+            bu[i] = load_w(a.wu, a.ldu, a.KBH, n0, lo + i, lane);
         }
     if (MODE == FP8S_MLP_MXFP8) {
 #pragma unroll
@@ -259,7 +259,7 @@ __global__ __launch_bounds__(256, 2) void gu_kernel(MlpArgs a) {
     for (int f = wave; f < 2 * nkb; f += 4) {
         const bool up = f >= nkb;
         const int kb = klo + (up ? f - nkb : f);
-        stage_w(up ? a.wu : a.wg, up ? a.ldu : a.ldg, n0, kb, lds, f * kFrag, lane);
+        stage_w(up ? a.wu : a.wg, up ? a.ldu : a.ldg, a.KBH, n0, kb, lds, f * kFrag, lane);
     }
 
     v4f acc[2][MTS];
@@ -362,7 +362,7 @@ __global__ __launch_bounds__(256) void down_small_kernel(MlpArgs a) {
     v8i b[NB];
     if (live) {
 #pragma unroll
-        for (int t = 0; t < NB; ++t) b[t] = load_w(a.wd, a.ldd, n0 + 16 * t, kb, lane);
+        for (int t = 0; t < NB; ++t) b[t] = load_w(a.wd, a.ldd, a.KBI, n0 + 16 * t, kb, lane);
     }
     v8i av;
     float4 sh = make_float4(0, 0, 0, 0);
@@ -446,7 +446,7 @@ __global__ __launch_bounds__(256, 2) void down_kernel(MlpArgs a) {
 
     for (int f = wave; f < NB * nkb; f += 4) {
         const int j = f / nkb, kb = klo + f % nkb;
-        stage_w(a.wd, a.ldd, n0 + 16 * j, kb, lds, f * kFrag, lane);
+        stage_w(a.wd, a.ldd, a.KBI, n0 + 16 * j, kb, lds, f * kFrag, lane);
     }
 
     v4f acc[NB][MTS];
@@ -567,8 +567,9 @@ static void launch_mlp(const MlpPlan& p, hipStream_t st, const MlpArgs& a, bool 
 
 static int check_qweight(const fp8s_qweight& w, int64_t K, int mode, const char* name) {
     FP8S_REQUIRE(w.w && w.scale, FP8S_EINVAL, "swiglu_mlp_fp8: %s weight or scale is null", name);
-    FP8S_REQUIRE(w.ld_w >= K && w.ld_w % 16 == 0 && aligned16(w.w), FP8S_EINVAL,
-                 "swiglu_mlp_fp8: %s weight must be 16-byte aligned with ld_w >= K and ld_w %% 16 == 0", name);
+    FP8S_REQUIRE((w.ld_w == 0 || (w.ld_w >= K && w.ld_w % 16 == 0)) && aligned16(w.w), FP8S_EINVAL,
+                 "swiglu_mlp_fp8: %s weight must be 16-byte aligned with ld_w >= K and ld_w %% 16 == 0 (or 0: "
+                 "fragment-packed)", name);
     FP8S_REQUIRE(mode == FP8S_MLP_MXFP8 || (reinterpret_cast<uintptr_t>(w.scale) & 3u) == 0, FP8S_EINVAL,
                  "swiglu_mlp_fp8: %s fp32 scale must be 4-byte aligned", name);
     return FP8S_OK;

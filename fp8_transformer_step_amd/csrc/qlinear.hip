@@ -92,7 +92,7 @@ __global__ __launch_bounds__(256, 2) void qlinear_kernel(QlArgs a) {
 
     for (int f = wave; f < NB * nkb; f += 4) {
         const int j = f / nkb, kb = klo + f % nkb;
-        stage_w(a.w, a.ldw, n0 + 16 * j, kb, lds, f * kFrag, lane);
+        stage_w(a.w, a.ldw, a.KB, n0 + 16 * j, kb, lds, f * kFrag, lane);
     }
 
     v4f acc[NB][MTS];
@@ -211,8 +211,9 @@ static int ql_check_common(const char* fn, const uint16_t* x, int64_t M, int64_t
     FP8S_REQUIRE(!norm_w || (aligned16(norm_w) && eps >= 0.0f && isfinite(eps)), FP8S_EINVAL,
                  "%s: norm weight must be 16-byte aligned and eps finite and >= 0", fn);
     FP8S_REQUIRE(w.w && w.scale, FP8S_EINVAL, "%s: null weight or scale", fn);
-    FP8S_REQUIRE(w.ld_w >= K && w.ld_w % 16 == 0 && aligned16(w.w), FP8S_EINVAL,
-                 "%s: weight must be 16-byte aligned with ld_w >= K and ld_w %% 16 == 0", fn);
+    FP8S_REQUIRE((w.ld_w == 0 || (w.ld_w >= K && w.ld_w % 16 == 0)) && aligned16(w.w), FP8S_EINVAL,
+                 "%s: weight must be 16-byte aligned with ld_w >= K and ld_w %% 16 == 0 (or 0: fragment-packed)",
+                 fn);
     FP8S_REQUIRE((reinterpret_cast<uintptr_t>(w.scale) & 3u) == 0, FP8S_EINVAL,
                  "%s: weight scale must be 4-byte aligned", fn);
     *plan = plan_ql(M, N, K);

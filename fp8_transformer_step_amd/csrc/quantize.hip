@@ -129,9 +129,40 @@ __global__ __launch_bounds__(256) void quant_block128_kernel(
     if (threadIdx.x == 0) scale[rb * ssr + cb * ssc] = s;
 }
 
+// W [N, K] e4m3 (row stride ld) -> the fragment-packed layout: one thread
+// per 16-byte piece; piece p of fragment f = (nb, kb) is lane p % 64's bytes
+// 0..15 (p < 64) or 16..31 (p >= 64).
+__global__ __launch_bounds__(256) void pack_weight_kernel(const uint8_t* w, int64_t ld, int64_t KB, int64_t pieces,
+                                                          uint8_t* out) {
+    const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
+    if (i >= pieces) return;
+    const int64_t f = i >> 7, nb = f / KB, kb = f % KB;
+    const int piece = (int)(i & 127), half = piece >> 6, l = piece & 63;
+    const uint8_t* src = w + (nb * 16 + (l & 15)) * ld + kb * 128 + 64 * half + 16 * (l >> 4);
+    *reinterpret_cast<uint4*>(out + f * 2048 + half * 1024 + 16 * l) = *reinterpret_cast<const uint4*>(src);
+}
+
 }  // namespace fp8s
 
 using namespace fp8s;
+
+extern "C" size_t fp8s_packed_weight_bytes(int64_t N, int64_t K) {
+    if (N < 16 || K < 128 || N % 16 || K % 128 || N > (1ll << 24) || K > (1ll << 20)) return 0;
+    return (size_t)N * (size_t)K;
+}
+
+extern "C" int fp8s_pack_weight(const uint8_t* q, int64_t ldq, int64_t N, int64_t K, uint8_t* out, void* stream) {
+    clear_error();
+    FP8S_REQUIRE(fp8s_packed_weight_bytes(N, K) != 0, FP8S_EINVAL,
+                 "fp8s_pack_weight: N=%lld must be a positive multiple of 16 and K=%lld of 128", (long long)N,
+                 (long long)K);
+    FP8S_REQUIRE(q && out && aligned16(q) && aligned16(out) && ldq >= K && ldq % 16 == 0, FP8S_EINVAL,
+                 "fp8s_pack_weight: q and out must be 16-byte aligned, ldq >= K and ldq %% 16 == 0");
+    const int64_t pieces = N * K / 16;
+    FP8S_LAUNCH("pack_weight", pack_weight_kernel, dim3((unsigned)((pieces + 255) / 256)), dim3(256), 0,
+                as_stream(stream), q, ldq, K / 128, pieces, out);
+    return check_launch("fp8s_pack_weight");
+}
 
 extern "C" int qlinear_quantize(const uint16_t* x, int64_t rows, int64_t cols, int64_t ld_x,
                                 int mode, uint8_t* q, int64_t ld_q, void* scale,

@@ -81,21 +81,24 @@ def _bf16(bits, device):
     return torch.from_numpy(np.ascontiguousarray(bits).view(np.int16)).to(device).view(torch.bfloat16)
 
 
-def _qweight(bits, device):
-    return ops.quantize_weight(_bf16(bits, device), ops.MLP_BSGEMM)
+def _qweight(bits, device, packed):
+    qw = ops.quantize_weight(_bf16(bits, device), ops.MLP_BSGEMM)
+    return ops.pack_weight(qw) if packed else qw
 
 
-def device_model(host, device="cuda"):
-    """Upload and quantise every weight; returns an ops.DualArModel."""
+def device_model(host, device="cuda", packed=True):
+    """Upload and quantise every weight; returns an ops.DualArModel.
+    packed: store the e4m3 matrices fragment-packed (fp8s_pack_weight), the
+    layout the decode GEMMs stream fastest; results are identical."""
     c = host.cfg
 
     def block(d):
-        return {k: _qweight(d[k], device) for k in ("qkv", "o", "gate", "up", "down")} | \
+        return {k: _qweight(d[k], device, packed) for k in ("qkv", "o", "gate", "up", "down")} | \
                {"norm_attn": _bf16(d["norm_attn"], device), "norm_mlp": _bf16(d["norm_mlp"], device)}
     slow = [block(d) for d in host.slow]
     fast = [block(d) for d in host.fast]
     embed = [_bf16(t, device) for t in host.embed]
-    heads = [_qweight(t, device) for t in host.heads]
+    heads = [_qweight(t, device, packed) for t in host.heads]
     return ops.DualArModel(slow, fast, _bf16(host.slow_norm, device), _bf16(host.fast_norm, device), embed, heads,
                            c.n_heads, c.n_kv_heads, c.head_dim, c.inter, c.rms_eps)
 

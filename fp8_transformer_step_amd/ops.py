@@ -72,13 +72,29 @@ def qlinear_quantize(x, mode, q=None, scale=None, k_major=None):
 
 @dataclass
 class QWeight:
-    """An e4m3 weight [N, K] with its block scales (see fp8s_qweight)."""
+    """An e4m3 weight [N, K] with its block scales (see fp8s_qweight).
+    packed: w holds the bytes in the fragment-packed layout of
+    fp8s_pack_weight (passed with ld_w = 0)."""
     w: torch.Tensor
     scale: torch.Tensor
+    packed: bool = False
 
     def as_c(self):
-        return _lib.QWeightC(self.w.data_ptr(), self.w.stride(0), self.scale.data_ptr(),
+        return _lib.QWeightC(self.w.data_ptr(), 0 if self.packed else self.w.stride(0), self.scale.data_ptr(),
                              self.scale.stride(0), self.scale.stride(1))
+
+
+def pack_weight(qw):
+    """Load-time copy of a QWeight into the fragment-packed layout (same
+    scales, same results from every consumer)."""
+    if qw.packed:
+        return qw
+    N, K = qw.w.shape
+    if int(_lib.load().fp8s_packed_weight_bytes(N, K)) == 0:
+        raise ValueError(f"cannot pack a [{N}, {K}] weight (N % 16, K % 128)")
+    out = torch.empty((N, K), dtype=torch.uint8, device=qw.w.device)
+    _lib.check(_lib.load().fp8s_pack_weight(qw.w.data_ptr(), qw.w.stride(0), N, K, out.data_ptr(), _stream()))
+    return QWeight(out, qw.scale, True)
 
 
 def quantize_weight(w_bf16, mlp_mode):

@@ -116,7 +116,10 @@ FP8S_API int qlinear_quantize(const uint16_t* x, int64_t rows, int64_t cols, int
 
 /* A quantised weight W[N, K] (row n, column k at w[n * ld_w + k]) and its
  * scales: bsgemm fp32 s[nb, kb] (128x128 blocks), MX uint8 E[n, kg] (1x32
- * groups along K), at scale[i * scale_stride_row + j * scale_stride_colblk]. */
+ * groups along K), at scale[i * scale_stride_row + j * scale_stride_colblk].
+ * ld_w == 0: w holds W in the fragment-packed layout of fp8s_pack_weight
+ * (N a multiple of 16, K of 128); every function that takes an fp8s_qweight
+ * accepts it and gives the same result, bit for bit. */
 typedef struct fp8s_qweight {
     const uint8_t* w;
     int64_t ld_w;
@@ -124,6 +127,23 @@ typedef struct fp8s_qweight {
     int64_t scale_stride_row;
     int64_t scale_stride_colblk;
 } fp8s_qweight;
+
+/*
+ * fp8s_pack_weight -- load-time re-layout of a quantised weight's e4m3
+ * matrix for the decode GEMMs (a data layout of this library; the pages fix
+ * none).  W [N, K] (row stride ldq) -> out, N * K bytes: the MFMA operand
+ * fragment of rows 16 nb .. 16 nb + 15 and K block kb (128 columns) is
+ * 2 KiB at (nb * K/128 + kb) * 2048; in it lane l = r + 16 g holds
+ * W[16 nb + r][128 kb + 16 g .. +16] at 16 l and W[16 nb + r][128 kb + 64 +
+ * 16 g .. +16] at 1024 + 16 l.  A wave then reads each fragment as two
+ * contiguous KiB.  Use it with ld_w = 0 and the unchanged scales.
+ *   fp8s_packed_weight_bytes(N, K): N * K, or 0 unless N is a positive
+ *   multiple of 16 and K of 128.
+ *   q, out 16-byte aligned; ldq >= K, a multiple of 16.  One kernel on
+ *   `stream`; out must not overlap q.
+ */
+FP8S_API size_t fp8s_packed_weight_bytes(int64_t N, int64_t K);
+FP8S_API int fp8s_pack_weight(const uint8_t* q, int64_t ldq, int64_t N, int64_t K, uint8_t* out, void* stream);
 
 /*
  * swiglu_mlp_fp8 -- y = down( quant( silu(x Wg^T) * (x Wu^T) ) ) at decode

@@ -181,3 +181,23 @@ def test_full_model_sampled_layers_teacher_forced():
         e = max_rel_err(g["logits"][p + 1][rows], lg)
         log(f"  micro-step {p}: head {p + 1} {e:.3e}")
         assert e <= TOL_FP8_PATH
+
+
+def test_packed_weights_give_the_same_step():
+    """Fragment-packed weights (the layout device_model uses by default) and
+    row-major ones give the same logits and codes, bit for bit, on the
+    4-head batch-24 model."""
+    need_gpu()
+    host = model.HostModel(model.scaled(model.TINY, batch=24, n_heads=4))
+    out = []
+    for packed in (False, True):
+        dm = model.device_model(host, packed=packed)
+        kv, _, _ = model.device_kv(host)
+        logits = torch.empty((host.cfg.n_codebooks, host.cfg.batch, host.cfg.codebook_size), dtype=torch.float32,
+                             device="cuda")
+        log(f"dual-AR step packed={packed}")
+        codes = ops.dual_ar_decode_step(dm, kv, torch.from_numpy(host.prev_codes).cuda(), logits_tap=logits)
+        torch.cuda.synchronize()
+        out.append((codes.cpu().numpy(), logits.cpu().numpy()))
+    np.testing.assert_array_equal(out[0][0], out[1][0])
+    np.testing.assert_array_equal(out[0][1], out[1][1])

@@ -119,3 +119,40 @@ def test_wrong_scale_strides_fail_loudly():
     bad = from_dev_bf16(ops.swiglu_mlp_fp8(to_dev_bf16(xb), *bad_w, mode))
     torch.cuda.synchronize()
     assert max_rel_err(bad, ref) > 0.2
+
+
+def _pack_reference(q):
+    """The fragment-packed layout written out with NumPy index arithmetic:
+    fragment (nb, kb) at (nb * KB + kb) * 2048, lane l = r + 16 g holding row
+    16 nb + r, columns 128 kb + 16 g .. at 16 l and 128 kb + 64 + 16 g .. at
+    1024 + 16 l."""
+    N, K = q.shape
+    KB = K // 128
+    t = q.reshape(N // 16, 16, KB, 2, 4, 16)            # nb, r, kb, half, g, byte
+    t = t.transpose(0, 2, 3, 4, 1, 5)                   # nb, kb, half, g, r, byte
+    return np.ascontiguousarray(t).reshape(N, K)
+
+
+def test_pack_weight_layout():
+    need_gpu()
+    _, w, _ = _setup(inputs.W_BSGEMM, 2560, 9728)
+    for qw in w:
+        p = ops.pack_weight(qw)
+        torch.cuda.synchronize()
+        assert np.array_equal(p.w.cpu().numpy(), _pack_reference(qw.w.cpu().numpy()))
+
+
+@pytest.mark.parametrize("workload", [inputs.W_BSGEMM, inputs.W_MXFP8])
+@pytest.mark.parametrize("M", [1, 4, 8, 16, 37, 64, 128])
+def test_packed_weights_bit_identical(workload, M):
+    """The MLP reads fragment-packed weights (ld_w = 0) to the same result,
+    bit for bit, at every launch shape (M <= 4, <= 16, each M tile count)."""
+    need_gpu()
+    mode, w, _ = _setup(workload, 2560, 9728)
+    packed = [ops.pack_weight(q) for q in w]
+    xb = to_dev_bf16(inputs.mlp_activations(workload, M, 2560, extra=100 + M))
+    log(f"mlp packed workload={workload} M={M}")
+    y0 = ops.swiglu_mlp_fp8(xb, *w, mode)
+    y1 = ops.swiglu_mlp_fp8(xb, *packed, mode)
+    torch.cuda.synchronize()
+    assert torch.equal(y0, y1)

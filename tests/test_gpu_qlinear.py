@@ -200,3 +200,16 @@ def test_argmax_is_exact_with_ties_nan_and_inf():
     codes = ops.argmax_rows(torch.from_numpy(lg).cuda())
     torch.cuda.synchronize()
     np.testing.assert_array_equal(codes[:, 0].cpu().numpy(), want)
+
+
+@pytest.mark.parametrize("M,N,K", [(1, 6144, 2560), (64, 2560, 4096), (37, 384, 640)])
+def test_qlinear_packed_weight_bit_identical(M, N, K):
+    """A fragment-packed weight (ld_w = 0) gives the row-major result bit for bit."""
+    need_gpu()
+    e = 11 * M + N + K
+    xb = to_dev_bf16(inputs.normal_bf16(W, inputs.T_X, (M, K), 1.0, extra=e))
+    qw, _ = _weight(inputs.normal_bf16(W, inputs.T_WO, (N, K), 0.02, extra=e))
+    y0 = ops.qlinear_fp8(xb, qw)
+    y1 = ops.qlinear_fp8(xb, ops.pack_weight(qw))
+    torch.cuda.synchronize()
+    assert torch.equal(y0, y1)
