@@ -55,6 +55,9 @@ SIGNATURES = {
     "fp8s_pack_weight": (ctypes.c_int, [c_vp, c_i64, c_i64, c_i64, c_vp, c_vp]),
     "swiglu_mlp_fp8": (ctypes.c_int, [c_vp, c_i64, c_i64, c_i64, ctypes.c_int, QWeightC, QWeightC, QWeightC,
                                       c_vp, c_vp, c_sz, c_vp, c_vp]),
+    "swiglu_mlp_fp8_noalloc_max_bytes": (c_sz, []),
+    "swiglu_mlp_fp8_noalloc": (ctypes.c_int, [c_vp, c_i64, c_i64, c_i64, ctypes.c_int, QWeightC, QWeightC,
+                                              QWeightC, c_vp, c_vp, c_vp]),
     "gqa_decode_attn_workspace_size": (c_sz, [c_i64, c_i32, c_i32, c_i64]),
     "gqa_decode_attn": (ctypes.c_int, [c_vp, c_vp, c_vp, c_i64, c_i64, c_i64, c_vp, c_i64, c_i32, c_i32, c_i32,
                                        c_i64, c_i64, ctypes.c_float, c_vp, c_vp, c_sz, c_vp, c_vp]),

@@ -41,6 +41,8 @@
 #include "internal.h"
 #include "profile.h"
 
+#include <mutex>
+
 namespace fp8s {
 
 constexpr int kGuCols = 16;        // I columns per gate/up item (16 gate + 16 up rows)
@@ -669,4 +671,71 @@ extern "C" int swiglu_mlp_fp8(const uint16_t* x, int64_t M, int64_t H, int64_t I
     FP8S_REQUIRE(x, FP8S_EINVAL, "swiglu_mlp_fp8: null x or y");
     return swiglu_mlp_fp8_ex(x, M, H, I, mode, gate, up, down, nullptr, 0.0f, nullptr, y, workspace,
                              workspace_bytes, stream, nullptr);
+}
+
+// ---- swiglu_mlp_fp8_noalloc: the same MLP on a library-owned scratch array --------
+// For callers that cannot allocate (code under graph capture, tight serving
+// loops).  The workspace lives in `scratch`, one copy per GPU for the life of
+// the process; its device address comes from hipGetSymbolAddress once per
+// device (the array's name in host code is only a host-side stand-in).
+namespace fp8s {
+
+constexpr size_t kNoAllocScratchBytes = size_t(32) << 20;
+constexpr int kNoAllocMaxDevices = 64;
+static __device__ __align__(256) uint8_t scratch[kNoAllocScratchBytes];
+
+__global__ __launch_bounds__(256) void zero_words_kernel(int* p, int n) {
+    const int i = blockIdx.x * 256 + threadIdx.x;
+    if (i < n) p[i] = 0;
+}
+
+static std::mutex g_scratch_mu;
+static void* g_scratch[kNoAllocMaxDevices];
+
+// The current device's scratch address; on the first call for a device the
+// control words at its start are cleared on `st` (a fill kernel, so the call
+// may be captured into a graph).
+static int noalloc_scratch(hipStream_t st, void** out) {
+    int dev = -1;
+    FP8S_REQUIRE(hipGetDevice(&dev) == hipSuccess && dev >= 0, FP8S_EHIP, "swiglu_mlp_fp8_noalloc: hipGetDevice failed");
+    FP8S_REQUIRE(dev < kNoAllocMaxDevices, FP8S_EUNSUPPORTED, "swiglu_mlp_fp8_noalloc: device %d >= %d", dev,
+                 kNoAllocMaxDevices);
+    std::lock_guard<std::mutex> lock(g_scratch_mu);
+    if (!g_scratch[dev]) {
+        void* p = nullptr;
+        const hipError_t e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+        FP8S_REQUIRE(e == hipSuccess && p, FP8S_EHIP, "swiglu_mlp_fp8_noalloc: hipGetSymbolAddress: %s",
+                     hipGetErrorString(e));
+        FP8S_LAUNCH("noalloc_clear", zero_words_kernel, dim3((kCtrlWords + 255) / 256), dim3(256), 0, st,
+                    static_cast<int*>(p), kCtrlWords);
+        const int rc = check_launch("swiglu_mlp_fp8_noalloc");
+        if (rc) return rc;
+        g_scratch[dev] = p;
+    }
+    *out = g_scratch[dev];
+    return FP8S_OK;
+}
+
+}  // namespace fp8s
+
+extern "C" size_t swiglu_mlp_fp8_noalloc_max_bytes(void) { return kNoAllocScratchBytes; }
+
+extern "C" int swiglu_mlp_fp8_noalloc(const uint16_t* x, int64_t M, int64_t H, int64_t I, int mode,
+                                      fp8s_qweight gate, fp8s_qweight up, fp8s_qweight down, uint16_t* y,
+                                      int32_t* err_flag, void* stream) {
+    clear_error();
+    (void)err_flag;
+    FP8S_REQUIRE(x, FP8S_EINVAL, "swiglu_mlp_fp8_noalloc: null x or y");
+    const size_t need = swiglu_mlp_fp8_workspace_size(M, H, I, mode);
+    FP8S_REQUIRE(need != 0, FP8S_EINVAL, "swiglu_mlp_fp8_noalloc: unsupported shape or mode");
+    FP8S_REQUIRE(need <= kNoAllocScratchBytes, FP8S_EUNSUPPORTED,
+                 "swiglu_mlp_fp8_noalloc: M=%lld hidden=%lld inter=%lld needs %zu bytes of scratch, more than the "
+                 "%zu this entry point holds (use swiglu_mlp_fp8 with a workspace)",
+                 (long long)M, (long long)H, (long long)I, need, kNoAllocScratchBytes);
+    hipStream_t st = as_stream(stream);
+    void* ws = nullptr;
+    int rc = noalloc_scratch(st, &ws);
+    if (rc) return rc;
+    return swiglu_mlp_fp8_ex(x, M, H, I, mode, gate, up, down, nullptr, 0.0f, nullptr, y, ws, kNoAllocScratchBytes,
+                             stream, nullptr);
 }

@@ -176,6 +176,24 @@ FP8S_API int swiglu_mlp_fp8(const uint16_t* x, int64_t M, int64_t hidden, int64_
                    int32_t* err_flag, void* stream);
 
 /*
+ * swiglu_mlp_fp8_noalloc -- swiglu_mlp_fp8 for callers that cannot allocate
+ * device memory (code under HIP graph capture, tight serving loops,
+ * harnesses that forbid hipMalloc).  Same arguments but no workspace; same
+ * kernels and result, bit for bit.  The workspace is a scratch array the
+ * library holds on every GPU it runs on, swiglu_mlp_fp8_noalloc_max_bytes()
+ * = 32 MiB, kept until the process ends; the call itself allocates nothing.
+ * A shape whose swiglu_mlp_fp8_workspace_size exceeds it fails with
+ * FP8S_EUNSUPPORTED (hidden 2560 / inter 9728 fit up to M = 128).  All calls
+ * on one GPU share that GPU's array, which keeps the last call's contents:
+ * calls that overlap in time on one GPU (other streams, other host threads)
+ * race and must not be made.
+ */
+FP8S_API size_t swiglu_mlp_fp8_noalloc_max_bytes(void);
+FP8S_API int swiglu_mlp_fp8_noalloc(const uint16_t* x, int64_t M, int64_t hidden, int64_t inter, int mode,
+                   fp8s_qweight gate, fp8s_qweight up, fp8s_qweight down, uint16_t* y,
+                   int32_t* err_flag, void* stream);
+
+/*
  * gqa_decode_attn -- grouped-query decode attention over the active prefix
  * of a pre-allocated KV cache ([KV] sections 4-5): for sequence b and query
  * head h, with g = h / (Hq / Hkv),
