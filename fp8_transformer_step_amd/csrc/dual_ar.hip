@@ -337,6 +337,31 @@ static int ql_operand(const StepCtx& c, uint8_t** qx, float** sx) {
 // when not null, the normalised rows).  The output and down projections
 // leave split partials that the row finisher reduces together with the
 // residual and the next RMSNorm.
+// Bytes of one slow layer's part of the FP8S_TAP_STEP_SLOW debug tap: ao, its operand, the MLP
+// input and its operand (operand = T * KB fragments of 2 KiB + T * KB scale
+// slots of 64 bytes, T = ceil(B / 16)).
+struct TapLayout {
+    size_t ao, ofrag, osc, xn, mfrag, msc, total;
+};
+static TapLayout tap_layout(const fp8s_dual_ar_model* m, int64_t B) {
+    const int64_t A = (int64_t)m->n_heads * m->head_dim, T = (B + 15) / 16;
+    TapLayout t;
+    t.ao = 0;
+    t.ofrag = t.ao + (size_t)B * A * 2;
+    t.osc = t.ofrag + (size_t)T * (A / 128) * kFrag;
+    t.xn = t.osc + (size_t)T * (A / 128) * 64;
+    t.mfrag = t.xn + (size_t)B * m->hidden * 2;
+    t.msc = t.mfrag + (size_t)T * (m->hidden / 128) * kFrag;
+    t.total = t.msc + (size_t)T * (m->hidden / 128) * 64;
+    return t;
+}
+
+static int tap_copy(void* dst, const void* src, size_t n, void* stream) {
+    FP8S_REQUIRE(hipMemcpyAsync(dst, src, n, hipMemcpyDeviceToDevice, as_stream(stream)) == hipSuccess, FP8S_EHIP,
+                 "dual_ar_decode_step: debug tap copy failed");
+    return FP8S_OK;
+}
+
 static int run_block(const StepCtx& c, const fp8s_block_weights& L, const uint16_t* xin, uint16_t* xmid,
                      uint16_t* xout, const uint16_t* next_norm, uint16_t* xn, uint16_t* kc, uint16_t* vc, int64_t sb,
                      int64_t sh, int64_t stt, int64_t cap, const int32_t* kv_len, int64_t hint) {
@@ -363,13 +388,35 @@ static int run_block(const StepCtx& c, const fp8s_block_weights& L, const uint16
     if (!fuse) {                               // quantise ao into the same operand buffer
         if ((rc = qlinear_quantize_operand(ao, c.B, A, qo, so, c.stream))) return step_error(rc, "attention");
     }
+    // debug tap (tests): every slow layer's fused operands, layer l at l *
+    // tl.total (the size was checked before the step enqueued anything)
+    size_t tap_bytes = 0;
+    const TapLayout tl = tap_layout(m, c.B);
+    uint8_t* tap = nullptr;
+    if (&L >= m->slow && &L < m->slow + m->n_slow_layers) {
+        tap = static_cast<uint8_t*>(debug_tap(FP8S_TAP_STEP_SLOW, &tap_bytes));
+        if (tap) tap += (size_t)(&L - m->slow) * tl.total;
+    }
+    if (tap) {
+        if ((rc = tap_copy(tap + tl.ao, ao, tl.ofrag - tl.ao, c.stream)) ||
+            (rc = tap_copy(tap + tl.ofrag, qo, tl.osc - tl.ofrag, c.stream)) ||
+            (rc = tap_copy(tap + tl.osc, so, tl.xn - tl.osc, c.stream)))
+            return rc;
+    }
     SplitPartials po;
     if ((rc = qlinear_fp8_partials(c.B, A, L.o, H, qlw, c.p->ql_bytes, c.stream, &po)))
         return step_error(rc, "output projection");
     uint8_t* mq;
     void* ms;
     if ((rc = mlp_operand(c.B, H, m->inter, FP8S_MLP_BSGEMM, mlpw, c.p->mlp_bytes, &mq, &ms))) return step_error(rc, "mlp");
-    if ((rc = finish_rows(c, &po, xin, xmid, L.norm_mlp, nullptr, mq, ms, "output projection"))) return rc;
+    if ((rc = finish_rows(c, &po, xin, xmid, L.norm_mlp, tap ? reinterpret_cast<uint16_t*>(tap + tl.xn) : nullptr, mq,
+                          ms, "output projection")))
+        return rc;
+    if (tap) {
+        if ((rc = tap_copy(tap + tl.mfrag, mq, tl.msc - tl.mfrag, c.stream)) ||
+            (rc = tap_copy(tap + tl.msc, ms, tl.total - tl.msc, c.stream)))
+            return rc;
+    }
     SplitPartials pd;
     rc = swiglu_mlp_fp8_ex(nullptr, c.B, H, m->inter, FP8S_MLP_BSGEMM, L.gate, L.up, L.down, nullptr, 0.0f, nullptr,
                            nullptr, mlpw, c.p->mlp_bytes, c.stream, &pd);
@@ -450,6 +497,11 @@ extern "C" int dual_ar_decode_step(const fp8s_dual_ar_model* m, int64_t B, const
     FP8S_REQUIRE(!slow_taps || aligned16(slow_taps), FP8S_EINVAL, "dual_ar_decode_step: slow_taps unaligned");
     FP8S_REQUIRE(!fast_taps || aligned16(fast_taps), FP8S_EINVAL, "dual_ar_decode_step: fast_taps unaligned");
     const StepPlan p = plan_step(m, B, kv->max_kv_len_hint);
+    size_t tap_bytes = 0;
+    const size_t tap_need = tap_layout(m, B).total * (size_t)m->n_slow_layers;
+    if (debug_tap(FP8S_TAP_STEP_SLOW, &tap_bytes))
+        FP8S_REQUIRE(tap_bytes >= tap_need, FP8S_EINVAL, "dual_ar_decode_step: debug tap of %zu bytes < %zu", tap_bytes,
+                     tap_need);
     FP8S_REQUIRE(workspace && aligned16(workspace), FP8S_EWORKSPACE, "dual_ar_decode_step: workspace missing or unaligned");
     FP8S_REQUIRE(workspace_bytes >= p.total, FP8S_EWORKSPACE, "dual_ar_decode_step: workspace %zu < required %zu bytes",
                  workspace_bytes, p.total);

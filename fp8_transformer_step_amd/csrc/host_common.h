@@ -14,6 +14,9 @@ namespace fp8s {
 int set_error(int code, const char* fmt, ...);
 void clear_error();
 
+// The buffer set by fp8s_set_debug_tap for `kind` (null when none) and its size.
+void* debug_tap(int kind, size_t* bytes);
+
 inline bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
 
 inline hipStream_t as_stream(void* s) { return reinterpret_cast<hipStream_t>(s); }

@@ -81,6 +81,8 @@ struct MlpArgs {
     float eps;
     const uint16_t* res;           // optional residual [M, H] added to y
     bool defer;                    // leave the down projection's split partials for the next kernel
+    uint8_t* xtap;                 // debug tap: gu_small's x operand (fragments, then scales at xtap_s)
+    uint8_t* xtap_s;
 };
 
 __device__ __forceinline__ void load8(const float* p, float (&v)[8]) {
@@ -189,6 +191,16 @@ __global__ __launch_bounds__(256) void gu_small_kernel(MlpArgs a) {
                           row, j, valid);
     }
     __syncthreads();
+    if (a.xtap && blockIdx.x == 0) {           // debug tap: this wave's operand blocks as the MFMAs read them
+        for (int kl = 0; kl < nkb; ++kl) {
+            const uint4* src = reinterpret_cast<const uint4*>(s_a[wk] + kl * kFrag) + 2 * lane;
+            uint4* dst = reinterpret_cast<uint4*>(a.xtap + frag_off(0, lo + kl, a.KBH)) + 2 * lane;
+            dst[0] = src[0];
+            dst[1] = src[1];
+            const uint8_t* s = MODE == FP8S_MLP_BSGEMM ? reinterpret_cast<const uint8_t*>(s_sx[wk][kl]) : s_ex[wk][kl];
+            a.xtap_s[(int64_t)(lo + kl) * 64 + lane] = s[lane];
+        }
+    }
 
     v4f acc_g = {0, 0, 0, 0}, acc_u = {0, 0, 0, 0};
 #pragma unroll
@@ -650,6 +662,15 @@ int swiglu_mlp_fp8_ex(const uint16_t* x, int64_t M, int64_t H, int64_t I, int mo
     a.norm_w = norm_w; a.eps = eps; a.res = residual;
     a.defer = partials != nullptr;
     hipStream_t st = as_stream(stream);
+    // debug tap of the x operand (tests)
+    size_t tap_bytes = 0;
+    uint8_t* tap = static_cast<uint8_t*>(debug_tap(FP8S_TAP_MLP_X, &tap_bytes));
+    const size_t tap_frag = (size_t)((M + 15) / 16) * p.KBH * kFrag, tap_sc = (size_t)((M + 15) / 16) * p.KBH * 64;
+    FP8S_REQUIRE(!tap || tap_bytes >= tap_frag + tap_sc, FP8S_EINVAL,
+                 "swiglu_mlp_fp8: debug tap of %zu bytes < %zu", tap_bytes, tap_frag + tap_sc);
+    const bool in_gu = M <= kTinyM && !norm_w && !prequant;
+    a.xtap = tap && in_gu ? tap : nullptr;
+    a.xtap_s = tap && in_gu ? tap + tap_frag : nullptr;
     if (mode == FP8S_MLP_BSGEMM)
         launch_mlp<FP8S_MLP_BSGEMM>(p, st, a, prequant);
     else
@@ -658,6 +679,11 @@ int swiglu_mlp_fp8_ex(const uint16_t* x, int64_t M, int64_t H, int64_t I, int mo
         partials->part = a.ypart;
         partials->S = p.S;
         partials->cols = p.MT == 1 ? kSmallDownCols : 16 * kDownNb;
+    }
+    if (tap && !in_gu) {
+        FP8S_REQUIRE(hipMemcpyAsync(tap, a.qx, tap_frag, hipMemcpyDeviceToDevice, st) == hipSuccess &&
+                         hipMemcpyAsync(tap + tap_frag, a.sx, tap_sc, hipMemcpyDeviceToDevice, st) == hipSuccess,
+                     FP8S_EHIP, "swiglu_mlp_fp8: debug tap copy failed");
     }
     return check_launch("swiglu_mlp_fp8");
 }

@@ -16,7 +16,8 @@ from . import _lib
 # Quantisation and MLP modes (include/fp8step.h).
 Q_ACT_1x128, Q_WGT_128x128, Q_MX_1x32 = 0, 1, 2
 MLP_BSGEMM, MLP_MXFP8 = 0, 1
-DEV_KVLEN_RANGE, DEV_WAIT_TIMEOUT, DEV_CODE_RANGE, DEV_PAGE_RANGE = 1, 2, 3, 4
+DEV_KVLEN_RANGE, DEV_CODE_RANGE, DEV_PAGE_RANGE = 1, 3, 4
+TAP_MLP_X, TAP_STEP_SLOW = 1, 2
 OUT_BF16, OUT_F32 = 0, 1
 
 
@@ -661,3 +662,13 @@ def profile_stop():
         _lib.check(lib.fp8s_profile_record(i, buf, 64, ctypes.byref(ms)))
         out.append((buf.value.decode(), float(ms.value)))
     return out
+
+
+def set_debug_tap(kind, buf):
+    """Point debug tap `kind` (TAP_MLP_X, TAP_STEP_SLOW) at a uint8 device
+    tensor, or switch it off with None (see fp8s_set_debug_tap)."""
+    if buf is None:
+        _lib.check(_lib.load().fp8s_set_debug_tap(int(kind), None, 0))
+    else:
+        _require_cuda(buf)
+        _lib.check(_lib.load().fp8s_set_debug_tap(int(kind), buf.data_ptr(), buf.numel() * buf.element_size()))

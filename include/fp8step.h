@@ -60,10 +60,40 @@ enum fp8s_status {
 /* Device error codes written to err_flag. */
 enum fp8s_device_error {
     FP8S_DEV_KVLEN_RANGE = 1, /* kv_len[b] outside [1, min(cap, hint)]         */
-    FP8S_DEV_WAIT_TIMEOUT = 2,/* a cross-workgroup wait in a fused kernel gave up */
+                              /* 2 is not used                                 */
     FP8S_DEV_CODE_RANGE = 3,  /* a codebook index outside [0, codebook_size)   */
     FP8S_DEV_PAGE_RANGE = 4   /* a block-table page id outside [0, num_pages)  */
 };
+
+/*
+ * Debug taps (for tests): fp8s_set_debug_tap(kind, buf, bytes) makes the
+ * calls named below also copy an internal fused operand into the device
+ * buffer buf (16-byte aligned; null or bytes 0 switches the tap off).  The
+ * setting is process-wide and not thread-safe.  A call whose tap is smaller
+ * than what it would copy fails with FP8S_EINVAL before it enqueues work.
+ * Operand layout ("operand of X [M, K]", T = ceil(M / 16), KB = K / 128):
+ * T * KB fragments of 2 KiB, [t][kb], in which lane l = r + 16 g holds the
+ * codes of row 16 t + r at columns 128 kb + 16 g .. +16 (bytes 32 l ..) and
+ * 128 kb + 64 + 16 g .. +16 (bytes 32 l + 16 ..); then T * KB scale slots,
+ * [t][kb]: bsgemm 16 fp32 (rows 16 t ..), MX 64 bytes (byte l = exponent of
+ * row 16 t + l % 16, group 4 kb + l / 16).  Rows >= M are unspecified.
+ *   FP8S_TAP_MLP_X          swiglu_mlp_fp8: the operand of x [M, hidden] the
+ *                           gate/up GEMM consumes (quantised inside that
+ *                           GEMM for M <= 4, by the x kernel otherwise).
+ *   FP8S_TAP_STEP_SLOW      dual_ar_decode_step, for each slow layer l in
+ *                           turn (n_slow_layers equal parts), back to back:
+ *                           the attention output ao bf16 [B, Hq*D]; the
+ *                           output projection's operand of ao as the
+ *                           attention kernel quantised it; the MLP input
+ *                           RMSNorm_mlp(x) bf16 [B, hidden] as the row
+ *                           finisher computed it; the MLP's operand of that
+ *                           input as the finisher quantised it (bsgemm).
+ */
+enum fp8s_debug_tap {
+    FP8S_TAP_MLP_X = 1,
+    FP8S_TAP_STEP_SLOW = 2
+};
+FP8S_API int fp8s_set_debug_tap(int kind, void* buf, size_t bytes);
 
 /* Output types of qlinear_fp8. */
 enum fp8s_out_dtype {
@@ -147,12 +177,18 @@ FP8S_API int fp8s_pack_weight(const uint8_t* q, int64_t ldq, int64_t N, int64_t 
 
 /*
  * swiglu_mlp_fp8 -- y = down( quant( silu(x Wg^T) * (x Wu^T) ) ) at decode
- * shape, with the activation quantisation of x fused into the gate/up GEMM
- * and the SwiGLU fused into the down projection's activation quantisation
- * ([TTS] "Why cuBLAS Wasn't Enough", "Kernel Benchmark Results").  A chain
- * of two (M <= 4) to four streaming kernels on `stream`; the gate and up
- * projections cross memory once in fp32, h = silu(g) * u is never written
- * in bf16 (only as the e4m3 operand of the down GEMM when M > 4).
+ * shape ([TTS] "Why cuBLAS Wasn't Enough", "Kernel Benchmark Results").  A
+ * chain of streaming kernels on `stream`; h = silu(g) * u is never written
+ * in bf16:
+ *   M <= 4   two kernels.  The gate/up GEMM quantises x itself (the
+ *            activation quantisation fused into the GEMM launch) and writes
+ *            g and u in fp32; the down GEMM forms h and quantises it as its
+ *            own operand (the SwiGLU fused into its activation quantisation).
+ *   M > 4    four kernels: x quantised once; the gate/up GEMM; h formed and
+ *            quantised once into the down GEMM's e4m3 operand; the down
+ *            GEMM.  Fusing either quantisation here would make every GEMM
+ *            workgroup re-quantise all M rows of its K range (the down
+ *            projection's 80 column groups would each redo h).
  *
  *   x     [M, hidden] bf16, contiguous.  1 <= M <= 128.
  *   gate, up  : W [inter, hidden];  down : W [hidden, inter].
@@ -166,7 +202,8 @@ FP8S_API int fp8s_pack_weight(const uint8_t* q, int64_t ldq, int64_t N, int64_t 
  *         again, so the buffer can then be reused for any M, hidden and inter
  *         it is large enough for (also under graph replay).  Calls that
  *         share a workspace must not overlap in time.
- *   err_flag  optional device int (see conventions).
+ *   err_flag  optional device int (see conventions); no condition of this
+ *         function writes it.
  *   Accuracy: fp32 accumulation; max|y - y_oracle| <= 2e-2 * max|y_oracle|.
  */
 FP8S_API size_t swiglu_mlp_fp8_workspace_size(int64_t M, int64_t hidden, int64_t inter, int mode);
