@@ -43,7 +43,7 @@ class KvStateC(ctypes.Structure):
     """Mirror of fp8s_kv_state (cache arrays are host pointers)."""
     _fields_ = [("k_cache", ctypes.POINTER(c_vp)), ("v_cache", ctypes.POINTER(c_vp)),
                 ("stride_b", c_i64), ("stride_h", c_i64), ("stride_t", c_i64), ("cap", c_i64),
-                ("kv_len", c_vp), ("max_kv_len_hint", c_i64)]
+                ("kv_len", c_vp), ("max_kv_len_hint", c_i64), ("live_rows", c_vp)]
 
 
 # name -> (restype, argtypes)

@@ -304,6 +304,7 @@ struct StepCtx {
     const StepPlan* p;
     int32_t* err;
     void* stream;
+    const int32_t* live;       // optional: rows >= *live are padding (no K/V append)
 };
 
 // The operand of the next projection from the row stream: x = base (+ the
@@ -371,8 +372,10 @@ static int run_block(const StepCtx& c, const fp8s_block_weights& L, const uint16
     uint16_t* ao = reinterpret_cast<uint16_t*>(c.ws + c.p->off_ao);
     void* qlw = c.ws + c.p->off_ql;
     void* mlpw = c.ws + c.p->off_mlp;
+    const bool slow_layer = &L >= m->slow && &L < m->slow + m->n_slow_layers;
     int rc = qkv_proj_kv_append_ex(nullptr, c.B, H, H, nullptr, 0.0f, L.qkv, m->n_heads, m->n_kv_heads, m->head_dim,
-                                   q, kc, vc, sb, sh, stt, kv_len, cap, qlw, c.p->ql_bytes, c.err, c.stream);
+                                   q, kc, vc, sb, sh, stt, kv_len, cap, qlw, c.p->ql_bytes, c.err, c.stream,
+                                   slow_layer ? c.live : nullptr);
     if (rc) return step_error(rc, "qkv projection");
     // The attention quantises its own output straight into the output
     // projection's operand when every KV head's query group covers whole
@@ -506,7 +509,7 @@ extern "C" int dual_ar_decode_step(const fp8s_dual_ar_model* m, int64_t B, const
     FP8S_REQUIRE(workspace_bytes >= p.total, FP8S_EWORKSPACE, "dual_ar_decode_step: workspace %zu < required %zu bytes",
                  workspace_bytes, p.total);
     uint8_t* ws = static_cast<uint8_t*>(workspace);
-    const StepCtx c{m, B, ws, &p, err_flag, stream};
+    const StepCtx c{m, B, ws, &p, err_flag, stream, kv->live_rows};
     const int64_t H = m->hidden, BH = B * H, V = m->codebook_size;
     const int C = m->n_codebooks, L = m->n_slow_layers, F = m->n_fast_layers;
     uint16_t* xbuf[2] = {reinterpret_cast<uint16_t*>(ws + p.off_x[0]), reinterpret_cast<uint16_t*>(ws + p.off_x[1])};

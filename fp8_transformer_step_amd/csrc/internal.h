@@ -63,7 +63,8 @@ int qkv_proj_kv_append_ex(const uint16_t* x, int64_t M, int64_t K, int64_t ld_x,
                           fp8s_qweight w_qkv, int32_t Hq, int32_t Hkv, int32_t D, uint16_t* q_out,
                           uint16_t* k_cache, uint16_t* v_cache, int64_t stride_b, int64_t stride_h,
                           int64_t stride_t, const int32_t* kv_len, int64_t cap, void* workspace,
-                          size_t workspace_bytes, int32_t* err_flag, void* stream);
+                          size_t workspace_bytes, int32_t* err_flag, void* stream,
+                          const int32_t* live_rows = nullptr);
 
 // x [M, K] bf16 (contiguous rows) quantised in 1x128 groups into the operand
 // layout of qlinear_operand.

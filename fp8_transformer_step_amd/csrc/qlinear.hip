@@ -47,6 +47,7 @@ struct QlArgs {
     uint16_t* q; int nq, nkv, D;              // EPI_QKV: q [M, nq]; K/V columns nkv each
     uint16_t* kc; uint16_t* vc; int64_t sb, sh, st;
     const int32_t* kv_len; int64_t cap;
+    const int32_t* live;                      // optional: rows >= *live append nothing
     int32_t* err;
 };
 
@@ -65,6 +66,7 @@ __device__ __forceinline__ void ql_epilogue(const QlArgs& a, int m, int n, float
         a.q[(int64_t)m * a.nq + n] = b;
         return;
     }
+    if (a.live && m >= *a.live) return;       // a padding row: its cache slot is not ours
     const int64_t t = (int64_t)a.kv_len[m] - 1;
     if (t < 0 || t >= a.cap) {                // nothing is written outside the cache
         report_error(a.err, FP8S_DEV_KVLEN_RANGE);
@@ -321,7 +323,7 @@ int qkv_proj_kv_append_ex(const uint16_t* x, int64_t M, int64_t K, int64_t ld_x,
                           fp8s_qweight w_qkv, int32_t Hq, int32_t Hkv, int32_t D, uint16_t* q_out,
                           uint16_t* k_cache, uint16_t* v_cache, int64_t stride_b, int64_t stride_h,
                           int64_t stride_t, const int32_t* kv_len, int64_t cap, void* workspace,
-                          size_t workspace_bytes, int32_t* err_flag, void* stream) {
+                          size_t workspace_bytes, int32_t* err_flag, void* stream, const int32_t* live_rows) {
     FP8S_REQUIRE(Hq >= 1 && Hkv >= 1 && Hq % Hkv == 0, FP8S_EINVAL, "qkv_proj_kv_append: Hq must be a multiple of Hkv");
     FP8S_REQUIRE(D == 64 || D == 128, FP8S_EUNSUPPORTED, "qkv_proj_kv_append: head_dim %d (64 or 128)", D);
     const int64_t N = (int64_t)(Hq + 2 * Hkv) * D;
@@ -338,7 +340,7 @@ int qkv_proj_kv_append_ex(const uint16_t* x, int64_t M, int64_t K, int64_t ld_x,
     a.epi = EPI_QKV;
     a.q = q_out; a.nq = Hq * D; a.nkv = Hkv * D; a.D = D;
     a.kc = k_cache; a.vc = v_cache; a.sb = stride_b; a.sh = stride_h; a.st = stride_t;
-    a.kv_len = kv_len; a.cap = cap; a.err = err_flag;
+    a.kv_len = kv_len; a.cap = cap; a.err = err_flag; a.live = live_rows;
     ql_launch(p, a, x, ld_x, K, norm_w, eps, workspace, as_stream(stream));
     return check_launch("qkv_proj_kv_append");
 }

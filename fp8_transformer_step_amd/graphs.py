@@ -10,10 +10,12 @@ min(max running requests, 64) restored the throughput curve.  So buckets
 here go up to 64 by default.
 
 A batch of b rows runs on the smallest bucket >= b: the caller's rows are
-copied into the bucket's static input, rows b and above keep whatever they
-held (they are computed and ignored; their KV rows must be valid, which
-they are when the state was built for the largest bucket), and the first b
-rows of the bucket's output are returned.  Every bucket has its own
+copied into the bucket's static input and the live row count b into a
+device word the captured step reads; rows b and above are computed and
+ignored, and append nothing to the KV caches (their kv_len must still be
+valid, which it is when the state was built for the largest bucket), so
+sequences parked in those rows keep their cache; the first b rows of the
+bucket's output are returned.  Every bucket has its own
 workspace, input and output buffers, so replays of different buckets never
 share scratch memory.  The library makes no allocation, synchronisation or
 memset inside the step, so capture needs nothing else.
@@ -37,11 +39,14 @@ class StepGraphs:
         self.buckets = sorted(set(int(b) for b in buckets if 1 <= b <= n_rows))
         if not self.buckets:
             raise ValueError("no bucket fits the KV state")
-        self.model, self.kv = model, kv
+        self.model = model
+        self.live = torch.zeros(1, dtype=torch.int32, device=device)
+        self.kv = kv = kv.with_live_rows(self.live)
         C = len(model.embed)
         self.err = torch.zeros(1, dtype=torch.int32, device=device)
         self.graphs = {}
         for B in self.buckets:
+            self.live.fill_(B)
             st = {"prev": torch.zeros((B, C), dtype=torch.int32, device=device),
                   "codes": torch.zeros((B, C), dtype=torch.int32, device=device),
                   "ws": model.new_workspace(B, kv.c.max_kv_len_hint, device)}
@@ -72,10 +77,12 @@ class StepGraphs:
         b = prev_codes.shape[0]
         st = self.graphs[self.bucket_for(b)]
         st["prev"][:b].copy_(prev_codes)
+        self.live.fill_(b)
         st["graph"].replay()
         return st["codes"][:b]
 
     def replay(self, B):
-        """Replay bucket B as captured (its static input unchanged)."""
+        """Replay bucket B as captured (its static input unchanged, all rows live)."""
+        self.live.fill_(B)
         self.graphs[B]["graph"].replay()
         return self.graphs[B]["codes"]

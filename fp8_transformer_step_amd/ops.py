@@ -611,7 +611,9 @@ class DualArModel:
 class KvState:
     """Per-slow-layer K/V caches (each [B, Hkv, cap, D], shared strides) and kv_len."""
 
-    def __init__(self, k_caches, v_caches, kv_len, max_kv_len_hint):
+    def __init__(self, k_caches, v_caches, kv_len, max_kv_len_hint, live_rows=None):
+        """live_rows: optional device int32 [1]; rows b >= live_rows[0] of a
+        step are padding and append no K/V (see fp8s_kv_state)."""
         import ctypes
         k0 = k_caches[0]
         for t in list(k_caches) + list(v_caches):
@@ -619,11 +621,19 @@ class KvState:
                 raise ValueError("all caches must share shape and strides, D contiguous")
         if kv_len.dtype != torch.int32:
             raise TypeError("kv_len must be int32")
-        self.k_caches, self.v_caches, self.kv_len = k_caches, v_caches, kv_len
+        if live_rows is not None and (live_rows.dtype != torch.int32 or not live_rows.is_cuda):
+            raise TypeError("live_rows must be an int32 device tensor")
+        self.k_caches, self.v_caches, self.kv_len, self.live_rows = k_caches, v_caches, kv_len, live_rows
+        self.max_kv_len_hint = int(max_kv_len_hint)
         self._k = (ctypes.c_void_p * len(k_caches))(*[t.data_ptr() for t in k_caches])
         self._v = (ctypes.c_void_p * len(v_caches))(*[t.data_ptr() for t in v_caches])
         self.c = _lib.KvStateC(self._k, self._v, k0.stride(0), k0.stride(1), k0.stride(2), k0.shape[2],
-                               kv_len.data_ptr(), int(max_kv_len_hint))
+                               kv_len.data_ptr(), int(max_kv_len_hint),
+                               live_rows.data_ptr() if live_rows is not None else None)
+
+    def with_live_rows(self, live_rows):
+        """The same caches and kv_len with a padding-row count (device int32 [1])."""
+        return KvState(self.k_caches, self.v_caches, self.kv_len, self.max_kv_len_hint, live_rows)
 
 
 def dual_ar_decode_step(model, kv, prev_codes, codes=None, slow_taps=None, fast_taps=None, logits_tap=None,

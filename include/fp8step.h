@@ -652,6 +652,10 @@ typedef struct fp8s_kv_state {
     int64_t stride_b, stride_h, stride_t, cap;
     const int32_t* kv_len;               /* device [B], counts this token    */
     int64_t max_kv_len_hint;             /* host bound of kv_len             */
+    const int32_t* live_rows;            /* optional device int32: rows b >= *live_rows are
+                                            padding (a graph captured for a larger batch):
+                                            their K/V is not appended to the caches and
+                                            their codes must be ignored; null = all live */
 } fp8s_kv_state;
 
 /*

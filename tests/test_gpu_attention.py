@@ -242,3 +242,23 @@ def test_balanced_split_reused_workspace_few_positions(shape):
     fresh = ops.gqa_decode_attn(to_dev_bf16(qb), kc, vc, kvd, cap)
     torch.cuda.synchronize()
     assert torch.equal(out, out2) and torch.equal(out, fresh)
+
+
+@pytest.mark.timeout(600)
+def test_b64_long_context_sampled_rows():
+    """B = 64, kv U[234, 8192], the full head configuration: every sequence
+    runs in one launch; the oracle checks sampled sequences (first, last,
+    longest, shortest and a spread)."""
+    need_gpu()
+    B, hi = 64, 8192
+    kv = inputs.kv_lengths(inputs.W_ATTN, B, 234, hi, extra=900)
+    log(f"attn B=64 kv range {kv.min()}..{kv.max()}")
+    qb, kb, vb, kc, vc = _make(inputs.W_ATTN, B, 32, 8, 128, hi, kv, extra=900)
+    err = torch.zeros(1, dtype=torch.int32, device="cuda")
+    out = from_dev_bf16(_run(qb, kc, vc, kv, hi, err))
+    rows = sorted({0, 13, 29, 47, B - 1, int(np.argmax(kv)), int(np.argmin(kv))})
+    ref = _oracle(qb[rows], kb[rows], vb[rows], kv[rows])
+    e = max_rel_err(out[rows], ref)
+    log(f"  rows {rows} kv {[int(kv[b]) for b in rows]}: max rel err {e:.3e}")
+    assert int(err.item()) == 0
+    assert e <= TOL_BF16_ATTN

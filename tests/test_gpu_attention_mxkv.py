@@ -142,3 +142,23 @@ def test_balanced_split_mixed_lengths():
     qb, kb, vb, kc, vc = _make(inputs.W_ATTN, B, 32, 8, 128, cap, kv, extra=203)
     out = _run(qb, kc, vc, kv, cap)
     assert max_rel_err(from_dev_bf16(out), _oracle(qb, kb, vb, kv)) <= TOL_BF16_ATTN
+
+
+@pytest.mark.timeout(600)
+@pytest.mark.parametrize("hi", [4096, 8192])
+def test_b64_sampled_rows(hi):
+    """B = 64, kv U[234, hi] over MXFP8 caches in one launch; the oracle
+    checks sampled sequences (first, last, longest, shortest and a spread)."""
+    need_gpu()
+    B = 64
+    kv = inputs.kv_lengths(inputs.W_ATTN, B, 234, hi, extra=910 + hi)
+    log(f"attn mxkv B=64 kv range {kv.min()}..{kv.max()}")
+    qb, kb, vb, kc, vc = _make(inputs.W_ATTN, B, 32, 8, 128, hi, kv, extra=910 + hi)
+    err = torch.zeros(1, dtype=torch.int32, device="cuda")
+    out = from_dev_bf16(_run(qb, kc, vc, kv, hi, err))
+    rows = sorted({0, 13, 29, 47, B - 1, int(np.argmax(kv)), int(np.argmin(kv))})
+    ref = _oracle(qb[rows], kb[rows], vb[rows], kv[rows])
+    e = max_rel_err(out[rows], ref)
+    log(f"  rows {rows} kv {[int(kv[b]) for b in rows]}: max rel err {e:.3e}")
+    assert int(err.item()) == 0
+    assert e <= TOL_BF16_ATTN
