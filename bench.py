@@ -32,6 +32,7 @@ if ROOT not in sys.path:
 
 METRIC = "decode-step tokens/s + achieved HBM GB/s (% of peak) for MLP & attn, M=1..128"
 PEAK_HBM_GBS = 8000.0            # MI355X HBM3E, published
+ROTATE_BYTES = 512 << 20         # sweeps rotate at least this many touched bytes (> the 256 MB last-level cache)
 H, I = 2560, 9728                # Qwen3-4B MLP
 HQ, HKV, D, CAP = 32, 8, 128, 32768
 
@@ -89,7 +90,7 @@ class Workload:
     """Rotating sets of GPU-resident weights, activations and KV caches."""
 
     def __init__(self, torch, ops, B, M, mode, n_sets, kv_len, with_attn=True, with_mlp=True, mx_kv=False,
-                 page=0, packed=False):
+                 page=0, packed=False, cap=CAP):
         self.torch, self.ops = torch, ops
         self.mx_kv = mx_kv
         self.page = page
@@ -116,8 +117,8 @@ class Workload:
                 st["ws"] = ops.new_mlp_workspace(M, H, I, mode)
             if with_attn:
                 Lmax = int(kv_len.max())
-                kc = torch.empty((B, HKV, CAP, D), dtype=torch.bfloat16, device="cuda")
-                vc = torch.empty((B, HKV, CAP, D), dtype=torch.bfloat16, device="cuda")
+                kc = torch.empty((B, HKV, cap, D), dtype=torch.bfloat16, device="cuda")
+                vc = torch.empty((B, HKV, cap, D), dtype=torch.bfloat16, device="cuda")
                 kc[:, :, :Lmax] = torch.randn((B, HKV, Lmax, D), generator=g, device="cuda").to(torch.bfloat16)
                 vc[:, :, :Lmax] = torch.randn((B, HKV, Lmax, D), generator=g, device="cuda").to(torch.bfloat16)
                 if page:                                # the prefixes on shuffled pages of a pool
@@ -542,7 +543,7 @@ def mlp_sweep(torch, ops, inputs, n_sets):
             t, _, per = time_parts(torch, ops, w, [w.mlp], 20, 5)
             gb = mlp_bytes(M, mode) / (t * 1e-3) / 1e9
             sweep[key][M] = {"us": t * 1e3, "tokens/s": M / (t * 1e-3), "GB/s": gb, "frac": gb / PEAK_HBM_GBS,
-                             "kernels": kernel_table(per, 20, M, mode)}
+                             "rotated_bytes": n_sets * mlp_bytes(M, mode), "kernels": kernel_table(per, 20, M, mode)}
             log(f"{key} M={M}: {t * 1e3:.1f} us {gb:.0f} GB/s  " +
                 " ".join(f"{k}={v['us']:.1f}" for k, v in sweep[key][M]["kernels"].items()))
             del w
@@ -605,19 +606,23 @@ def step_kernel_table(recs, plan, steps):
     return out
 
 
+def _blas_threads():
+    try:
+        import threadpoolctl
+        return max((p.get("num_threads", 1) for p in threadpoolctl.threadpool_info()), default=1)
+    except Exception:
+        return 1
+
+
 def cpu_baseline(host):
     """The oracle as it stands, on the host cores, on a bounded sample of the
     step: one slow layer (full batch, the first cache set's prefixes), one
-    fast-AR layer at its first micro-step and one codebook head, timed once
-    each with their weights dequantised outside the timing, and scaled to a
-    full step (36 slow + 9 x 4 fast layer evaluations + 10 heads)."""
+    fast-AR layer at its first micro-step and one codebook head, with their
+    weights dequantised outside the timing, scaled to a full step (36 slow
+    + 9 x 4 fast layer evaluations + 10 heads); the median of 3 samples."""
     import oracle
     f32 = __import__("fp8_transformer_step_amd.inputs", fromlist=["x"]).bf16_bits_to_f32
-    try:
-        import threadpoolctl
-        blas = max((p.get("num_threads", 1) for p in threadpoolctl.threadpool_info()), default=1)
-    except Exception:
-        blas = 1
+    blas = _blas_threads()
     c = host.cfg
 
     def block(d):
@@ -632,25 +637,80 @@ def cpu_baseline(host):
     for b in range(c.batch):
         kp, vp = host.kv_prefix(0, b)
         k[b, :, :kp.shape[1]], v[b, :, :vp.shape[1]] = f32(kp), f32(vp)
-    fk = np.zeros((c.batch, c.n_kv_heads, c.n_codebooks - 1, c.head_dim))
-    fv = np.zeros_like(fk)
-    t0 = time.perf_counter()
-    x = oracle.embed_sum([f32(t) for t in host.embed], host.prev_codes)
-    t1 = time.perf_counter()
-    x1, _ = oracle.decoder_layer(x, ps, k, v, host.kv_len, c.n_heads, c.n_kv_heads, c.head_dim, c.rms_eps)
-    t2 = time.perf_counter()
-    z, _ = oracle.decoder_layer(x1, pf, fk, fv, np.ones(c.batch, np.int32), c.n_heads, c.n_kv_heads,
-                                c.head_dim, c.rms_eps)
-    t3 = time.perf_counter()
-    oracle.greedy_code(oracle.rmsnorm(z, f32(host.fast_norm)), head)
-    t4 = time.perf_counter()
     L, F, C = c.n_slow_layers, c.n_fast_layers, c.n_codebooks
-    est = (t1 - t0) + L * (t2 - t1) + (C - 1) * F * (t3 - t2) + C * (t4 - t3)
+    samples = []
+    for _ in range(3):
+        fk = np.zeros((c.batch, c.n_kv_heads, c.n_codebooks - 1, c.head_dim))
+        fv = np.zeros_like(fk)
+        t0 = time.perf_counter()
+        x = oracle.embed_sum([f32(t) for t in host.embed], host.prev_codes)
+        t1 = time.perf_counter()
+        x1, _ = oracle.decoder_layer(x, ps, k.copy(), v.copy(), host.kv_len, c.n_heads, c.n_kv_heads, c.head_dim,
+                                     c.rms_eps)
+        t2 = time.perf_counter()
+        z, _ = oracle.decoder_layer(x1, pf, fk, fv, np.ones(c.batch, np.int32), c.n_heads, c.n_kv_heads,
+                                    c.head_dim, c.rms_eps)
+        t3 = time.perf_counter()
+        oracle.greedy_code(oracle.rmsnorm(z, f32(host.fast_norm)), head)
+        t4 = time.perf_counter()
+        est = (t1 - t0) + L * (t2 - t1) + (C - 1) * F * (t3 - t2) + C * (t4 - t3)
+        samples.append((est, t2 - t1, t3 - t2, t4 - t3))
+    est, ts, tf, th = sorted(samples)[1]
     return {"value": c.batch / est, "unit": "tokens/s", "cores": int(blas), "kind": "oracle",
-            "sample": f"one slow layer ({t2 - t1:.2f} s), one fast layer ({t3 - t2:.2f} s) and one head "
-                      f"({t4 - t3:.2f} s) at batch {c.batch}, float64 NumPy, weights dequantised outside the "
+            "sample": f"median of 3: one slow layer ({ts:.2f} s), one fast layer ({tf:.2f} s) and one head "
+                      f"({th:.2f} s) at batch {c.batch}, float64 NumPy, weights dequantised outside the "
                       f"timing, scaled to a full step of {L} + {(C - 1) * F} layer evaluations and {C} heads "
-                      f"= {est:.1f} s; host affinity {len(os.sched_getaffinity(0))} cores"}
+                      f"= {est:.1f} s (samples {', '.join(f'{s[0]:.1f}' for s in samples)} s); host affinity "
+                      f"{len(os.sched_getaffinity(0))} cores, {blas} BLAS threads"}
+
+
+def config_cpu_baselines():
+    """The oracle on the other headline configurations, median of 3 timed
+    calls each (inputs and dequantised weights prepared outside the timing):
+    the Qwen3-4B-shaped MLP at M = 64 on the bsgemm and MXFP8 paths, and
+    decode attention at B = 64, kv U[234, 400] and U[234, 4096]."""
+    import oracle
+    from oracle import attention as oattn, fp8 as ofp8, mlp as omlp
+    from fp8_transformer_step_amd import inputs
+    f32 = inputs.bf16_bits_to_f32
+    blas, cores = _blas_threads(), len(os.sched_getaffinity(0))
+    out = {}
+
+    def med3(fn):
+        ts = []
+        for _ in range(3):
+            t0 = time.perf_counter()
+            fn()
+            ts.append(time.perf_counter() - t0)
+        return sorted(ts)[1], ts
+
+    H, I, M = 2560, 9728, 64
+    for wl, mode, key in ((inputs.W_BSGEMM, omlp.MODE_BSGEMM, "C2_mlp_bsgemm_M64"),
+                          (inputs.W_MXFP8, omlp.MODE_MXFP8, "C3_mlp_mxfp8_M64")):
+        deq = []
+        for wb in inputs.mlp_weights(wl, H, I):
+            w32 = f32(wb)
+            if mode == omlp.MODE_BSGEMM:
+                q, s = ofp8.quant_weight_128x128(w32)
+                deq.append(ofp8.dequant_block_fp32(q, s, 128, 128))
+            else:
+                q, s = ofp8.quant_mx_1x32(w32)
+                deq.append(ofp8.dequant_mx_1x32(q, s))
+        x = f32(inputs.mlp_activations(wl, M, H))
+        t, ts = med3(lambda: omlp.swiglu_mlp(x, *deq, mode))
+        out[key] = {"value": M / t, "unit": "tokens/s", "us_per_call": t * 1e6, "cores": cores,
+                    "blas_threads": int(blas), "kind": "oracle", "samples_s": ts}
+        del deq
+    for hi in (400, 4096):
+        B = 64
+        kv = inputs.kv_lengths(inputs.W_ATTN, B, 234, hi, extra=B + hi)
+        qb, kb, vb = inputs.attention_prefix(inputs.W_ATTN, B, HQ, HKV, D, int(kv.max()), extra=B + hi)
+        q, k, v = f32(qb), f32(kb), f32(vb)
+        t, ts = med3(lambda: oattn.gqa_decode_attention(q, k, v, kv))
+        out[f"C4_attn_B64_kv_U[234,{hi}]"] = {"value": B / t, "unit": "tokens/s", "us_per_call": t * 1e6,
+                                              "cores": cores, "blas_threads": int(blas), "kind": "oracle",
+                                              "samples_s": ts}
+    return out
 
 
 def main():
@@ -658,7 +718,9 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=3)
-    ap.add_argument("--sets", type=int, default=4, help="rotating weight/cache sets of the sweeps")
+    ap.add_argument("--sets", type=int, default=8,
+                    help="rotating weight sets of the MLP sweep (8 x 74.7 MB); the attention sweeps rotate "
+                         "at least 512 MB of touched cache bytes on their own")
     ap.add_argument("--no-sweep", action="store_true")
     ap.add_argument("--mlp-only", action="store_true",
                     help="only the MLP at M in {1, 8, 32, 64, 128} (both paths), for counter runs; prints that "
@@ -711,6 +773,9 @@ def main():
         gbs = nb / (us * 1e-6) / 1e9
         parts[gname] = {"us_per_step": us, "bytes_per_step": nb, "GB/s": gbs, "frac": gbs / PEAK_HBM_GBS}
     traffic = pmc_traffic(dom_name)
+    step_bytes = int(sum(v["bytes_per_step"] for v in ktab.values()))
+    log(f"step algorithmic bytes {step_bytes / 1e9:.2f} GB: {step_bytes / (ms_step * 1e-3) / 1e9:.0f} GB/s "
+        f"({100 * step_bytes / (ms_step * 1e-3) / 1e9 / PEAK_HBM_GBS:.1f}% of HBM peak over the whole step)")
     result = {
         "metric": METRIC,
         "value": B / (ms_step * 1e-3),
@@ -738,6 +803,9 @@ def main():
                      "algorithmic_bytes": dom["bytes_per_launch"], "launch_us": dom["us_per_launch"],
                      "launches_per_step": dom["per_step"]},
         "parts": parts,
+        "launches_per_step": len(plan),
+        "step_hbm": {"bytes_per_step": step_bytes, "GB/s": step_bytes / (ms_step * 1e-3) / 1e9,
+                     "frac": step_bytes / (ms_step * 1e-3) / 1e9 / PEAK_HBM_GBS},
         "kernels": ktab,
         "wall_ms_per_step": wall,
         "ms_per_step_eager": ms_step,
@@ -756,13 +824,18 @@ def main():
                                      (64, 234, 4096, True, 0), (64, 234, 8192, True, 0),
                                      (64, 234, 4096, False, 16), (64, 234, 4096, True, 16)):
             kv = inputs.kv_lengths(inputs.W_ATTN, Bs, lo, hi, extra=Bs + hi)
-            w = Workload(torch, ops, Bs, 1, 0, 2 if hi > 400 else args.sets, kv, with_mlp=False, mx_kv=mx,
-                         page=page)
+            # rotate >= 512 MB of the bytes a call touches (more than the 256 MB
+            # last-level cache); short prefixes get 512-slot caches so that
+            # many sets fit
+            n_sets = max(2, min(1024, -(-ROTATE_BYTES // attn_bytes(kv, Bs, mx))))
+            w = Workload(torch, ops, Bs, 1, 0, n_sets, kv, with_mlp=False, mx_kv=mx, page=page,
+                         cap=CAP if hi > 400 else 512)
             t, _, per = time_parts(torch, ops, w, [w.attn], 20, 5)
             gb = attn_bytes(kv, Bs, mx) / (t * 1e-3) / 1e9
             key = f"B={Bs},kv=U[{lo},{hi}]" + (f",page={page},{'mxfp8' if mx else 'bf16'}" if page else "")
             sweep["attn_paged" if page else "attn_mxkv" if mx else "attn"][key] = {
                 "us": t * 1e3, "tokens/s": Bs / (t * 1e-3), "GB/s": gb, "frac": gb / PEAK_HBM_GBS,
+                "rotated_bytes": n_sets * attn_bytes(kv, Bs, mx),
                 "kernels": kernel_table(per, 20, 1, 0, kv, Bs)}
             log(f"attn{' mxkv' if mx else ''}{f' paged {page}' if page else ''} B={Bs} kv {lo}..{hi}: "
                 f"{t * 1e3:.1f} us {gb:.0f} GB/s")
@@ -787,6 +860,8 @@ def main():
     if not args.no_cpu_baseline:
         log("bench: timing the CPU oracle")
         result["cpu_baseline"] = cpu_baseline(host)
+        if not args.no_sweep:
+            result["cpu_baselines_other_configs"] = config_cpu_baselines()
     print(json.dumps(result), flush=True)
 
 
