@@ -606,6 +606,44 @@ def step_kernel_table(recs, plan, steps):
     return out
 
 
+def stream_ceiling(torch, ops):
+    """What one launch can stream: fp8s_stream_read over the byte counts of
+    the MLP (all weights, gate/up, down), the QKV projection and one attention
+    call at B = 64, kv U[234, 4096], each on buffers rotating >= 512 MB."""
+    lib = ops._lib.load()
+    sink = torch.zeros(4, dtype=torch.int32, device="cuda")
+    H, I = 2560, 9728
+    sizes = {"mlp_weights": 3 * H * I, "mlp_gate_up": 2 * H * I, "mlp_down": H * I, "qkv_proj": 6144 * H,
+             "attn_b64_kv4096": 533291008}
+    out = {}
+    for name, nb in sizes.items():
+        nb = nb // 2048 * 2048
+        n_bufs = max(2, -(-ROTATE_BYTES // nb))
+        bufs = [torch.ones(nb, dtype=torch.uint8, device="cuda") for _ in range(n_bufs)]
+        st = torch.cuda.current_stream().cuda_stream
+
+        def run(i):
+            ops._lib.check(lib.fp8s_stream_read(bufs[i % n_bufs].data_ptr(), nb, sink.data_ptr(), st))
+        for i in range(2 * n_bufs):
+            run(i)
+        torch.cuda.synchronize()
+        n = max(40, 2 * n_bufs)
+        t0, t1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        t0.record()
+        for i in range(n):
+            run(i)
+        t1.record()
+        torch.cuda.synchronize()
+        us = t0.elapsed_time(t1) / n * 1e3
+        gbs = nb / (us * 1e-6) / 1e9
+        out[name] = {"bytes": nb, "us": us, "GB/s": gbs, "frac": gbs / PEAK_HBM_GBS, "rotated_bytes": n_bufs * nb}
+        log(f"stream_read {name}: {nb / 1e6:.1f} MB in {us:.2f} us = {gbs:.0f} GB/s "
+            f"({100 * gbs / PEAK_HBM_GBS:.1f}% of peak)")
+        del bufs
+        torch.cuda.empty_cache()
+    return out
+
+
 def _blas_threads():
     try:
         import threadpoolctl
@@ -726,6 +764,9 @@ def main():
                     help="only the MLP at M in {1, 8, 32, 64, 128} (both paths), for counter runs; prints that "
                          "sweep as JSON")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--stream-ceiling", action="store_true",
+                    help="only time fp8s_stream_read over the byte counts of the decode kernels (>= 512 MB "
+                         "rotation); prints that table as JSON")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="also run a plain 512 MiB device copy (3x) so that profiler byte counters can be "
                          "scaled against a kernel of known traffic")
@@ -739,6 +780,9 @@ def main():
     from fp8_transformer_step_amd import inputs, model, ops
 
     torch.cuda.set_device(0)
+    if args.stream_ceiling:
+        print(json.dumps({"stream_ceiling": stream_ceiling(torch, ops)}), flush=True)
+        return
     if args.mlp_only:
         print(json.dumps({"mlp_sweep": mlp_sweep(torch, ops, inputs, args.sets)}), flush=True)
         return

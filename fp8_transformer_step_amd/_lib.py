@@ -53,6 +53,7 @@ SIGNATURES = {
     "swiglu_mlp_fp8_workspace_size": (c_sz, [c_i64, c_i64, c_i64, ctypes.c_int]),
     "fp8s_packed_weight_bytes": (c_sz, [c_i64, c_i64]),
     "fp8s_set_debug_tap": (ctypes.c_int, [ctypes.c_int, c_vp, c_sz]),
+    "fp8s_stream_read": (ctypes.c_int, [c_vp, c_sz, c_vp, c_vp]),
     "fp8s_pack_weight": (ctypes.c_int, [c_vp, c_i64, c_i64, c_i64, c_vp, c_vp]),
     "swiglu_mlp_fp8": (ctypes.c_int, [c_vp, c_i64, c_i64, c_i64, ctypes.c_int, QWeightC, QWeightC, QWeightC,
                                       c_vp, c_vp, c_sz, c_vp, c_vp]),

@@ -24,7 +24,7 @@ DEVICE = ["-x", "hip", "--offload-arch=" + ARCH,
           "-fno-gpu-rdc"]
 
 SOURCES = ["status.cpp", "profile.cpp", "quantize.hip", "mlp.hip", "attention.hip", "qlinear.hip", "dual_ar.hip",
-           "sampling.hip", "gemm_large.hip", "extend_attention.hip"]
+           "sampling.hip", "gemm_large.hip", "extend_attention.hip", "stream.hip"]
 
 
 def _compile(src, verbose):

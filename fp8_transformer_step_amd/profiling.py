@@ -39,6 +39,8 @@ KERNELS = [
     (r"\bgu_kernel", "mlp_gu"),
     (r"\bdown_kernel", "mlp_down"),
     (r"act_quant_kernel", "act_quant"),
+    (r"stream_read_kernel", "stream_read"),
+    (r"pack_weight_kernel", "pack_weight"),
     (r"hq_kernel", "mlp_hq"),
     # split kernels: <D, G, SINGLE, PAGED>; balanced: <D, G, PAGED>
     (r"attn_split_kernel<\d+, \d+, true, true>", "attn_single_paged"),
@@ -121,7 +123,7 @@ def stats(csv_path, out_md, command):
     open(out_md, "w").write("\n".join(lines) + "\n")
 
 
-def by_launch_shape(trace_csv, out_md, command, kernels):
+def by_launch_shape(trace_csv, out_md, command, kernels, note=""):
     """Per (library kernel, grid) durations from a rocprofv3 kernel trace,
     for the kernels named in `kernels`: one row per launch shape (the grid
     identifies the problem size of a sweep), calls, average, min and max."""
@@ -138,12 +140,13 @@ def by_launch_shape(trace_csv, out_md, command, kernels):
         groups.setdefault((lib, short, grid, wg), []).append(us)
     lines = ["# rocprofv3 kernel durations by launch shape\n", f"Command:\n\n```\n{command}\n```\n",
              "One row per (kernel instance, grid); problem sizes that launch the same grid share a row "
-             "(their average mixes them; min and max bound each).\n",
-             "| library kernel | rocprof name | workgroups (x, y, z) | threads | calls | avg us | min us | max us |",
-             "|---|---|---|---|---|---|---|---|"]
+             "(their average mixes them; min and max bound each).\n" + (f"\n{note}\n" if note else ""),
+             "| library kernel | rocprof name | workgroups (x, y, z) | threads | calls | avg us | median us | "
+             "min us | max us |",
+             "|---|---|---|---|---|---|---|---|---|"]
     for (lib, short, grid, wg), v in sorted(groups.items()):
         lines.append(f"| {lib} | `{short}` | {grid[0]}, {grid[1]}, {grid[2]} | {wg} | {len(v)} | "
-                     f"{statistics.mean(v):.1f} | {min(v):.1f} | {max(v):.1f} |")
+                     f"{statistics.mean(v):.1f} | {statistics.median(v):.1f} | {min(v):.1f} | {max(v):.1f} |")
     open(out_md, "w").write("\n".join(lines) + "\n")
 
 
@@ -244,6 +247,7 @@ def main():
     s.add_argument("out")
     s.add_argument("--kernels", required=True, help="comma-separated library kernel names")
     s.add_argument("--command", required=True)
+    s.add_argument("--note", default="", help="a line of explanation printed above the table")
     c = sub.add_parser("counters")
     c.add_argument("stats")
     c.add_argument("dirs", nargs="+", help="counter pass directories, then the output .md")
@@ -252,7 +256,7 @@ def main():
     if args.cmd == "stats":
         stats(args.csv, args.out, args.command)
     elif args.cmd == "shapes":
-        by_launch_shape(args.trace, args.out, args.command, set(args.kernels.split(",")))
+        by_launch_shape(args.trace, args.out, args.command, set(args.kernels.split(",")), args.note)
     elif args.cmd == "pmc":
         pmc(args.fetch_dir, args.write_dir, args.out, args.command)
     else:

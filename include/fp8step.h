@@ -173,6 +173,15 @@ typedef struct fp8s_qweight {
  *   `stream`; out must not overlap q.
  */
 FP8S_API size_t fp8s_packed_weight_bytes(int64_t N, int64_t K);
+/*
+ * fp8s_stream_read -- a measurement kernel, not part of the decode path: reads
+ * `bytes` (a positive multiple of 2048) of buf once, each workgroup staging
+ * one 20 KiB item into LDS by direct-to-LDS loads as the GEMM kernels stage
+ * weights, and writes nothing (sink, a device word, is written only in a
+ * case that practically never occurs).  Timing it gives the rate one launch
+ * of that size can stream, the ceiling the decode kernels are set against.
+ */
+FP8S_API int fp8s_stream_read(const void* buf, size_t bytes, uint32_t* sink, void* stream);
 FP8S_API int fp8s_pack_weight(const uint8_t* q, int64_t ldq, int64_t N, int64_t K, uint8_t* out, void* stream);
 
 /*
