@@ -73,13 +73,13 @@ struct AttnArgs {
 
 // UE8M0 byte -> 2^(E - 127) (E = 0 is the subnormal 2^-127).
 __device__ __forceinline__ float ue8m0_f32(uint32_t E) { return __uint_as_float(E ? E << 23 : 0x00400000u); }
-// Two OCP e4m3 bytes (bytes 0-1 or 2-3 of dw) times X, as a bf16 pair.  An
-// e4m3 value times a power of two has at most four significant bits, so the
-// product and its bf16 truncation are exact.
+// Two OCP e4m3 bytes (bytes 0-1 or 2-3 of dw) times X, as a bf16 pair, in one
+// gfx950 scaled conversion (it applies the exponent of X, which for X =
+// 2^(E - 127) is X itself; an e4m3 value times a power of two is exact in
+// bf16 and f32).
 template <bool HI>
 __device__ __forceinline__ uint32_t fp8x2_bf16x2(uint32_t dw, float X) {
-    const auto f = __builtin_amdgcn_cvt_pk_f32_fp8((int)dw, HI);
-    return (__float_as_uint(f[0] * X) >> 16) | (__float_as_uint(f[1] * X) & 0xFFFF0000u);
+    return __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8((int)dw, X, HI));
 }
 
 // Quantise one 128-column group kb of output row b (held by one wave: column
@@ -277,9 +277,9 @@ __device__ __forceinline__ void attn_piece(const AttnArgs& a, int b, int g, int 
             const uint32_t ww[2] = {w.x, w.y};
 #pragma unroll
             for (int i = 0; i < 2; ++i) {
-                const auto lo = __builtin_amdgcn_cvt_pk_f32_fp8((int)ww[i], false);
-                const auto hi = __builtin_amdgcn_cvt_pk_f32_fp8((int)ww[i], true);
-                vf[4 * i] = lo[0] * X; vf[4 * i + 1] = lo[1] * X; vf[4 * i + 2] = hi[0] * X; vf[4 * i + 3] = hi[1] * X;
+                const auto lo = __builtin_amdgcn_cvt_scalef32_pk_f32_fp8((int)ww[i], X, false);
+                const auto hi = __builtin_amdgcn_cvt_scalef32_pk_f32_fp8((int)ww[i], X, true);
+                vf[4 * i] = lo[0]; vf[4 * i + 1] = lo[1]; vf[4 * i + 2] = hi[0]; vf[4 * i + 3] = hi[1];
             }
         } else {
             const uint4 w = *reinterpret_cast<const uint4*>(vbase + row(t_begin + t) + dl);
