@@ -268,23 +268,26 @@ def step_launch_plan(cfg, kv_len):
                 finish(True)]
 
     def head():
-        return [("qlinear", V * H + ws(V, H) + B * H + asc(H) + B * V * 4),
-                ("argmax", B * V * 4 + 4 * B)]
+        return [("qlinear", V * H + ws(V, H) + B * H + asc(H) + B * V * 4)]
 
-    out = [("embed_sum", B * C * H * 2 + B * H * 2 + 4 * B * C), finish(False)]
+    # embedding rows straight into the finisher: rows gathered (+ the added
+    # row), x written, norm weight, operand; the slow input reads the codes
+    # and fills the fast AR's kv_len table, a fast micro-step takes its code
+    # as the argmax of the previous head's logits
+    operand = B * H * 2 + H * 2 + B * H + asc(H)
+    out = [("embed_finish", B * C * H * 2 + 4 * B * C + (C - 1) * B * 4 + operand)]
     slow_kv = int(np.sum(kv_len, dtype=np.int64)) * KVD * 2 * 2
     # the slow AR's prefixes are split over chunks and merged; the fast AR's
     # few-slot caches are one chunk, written by the split kernel itself
     for _ in range(c.n_slow_layers):
         out += block(slow_kv, False)
     out += head()
-    out.append(("fill_steps", (C - 1) * B * 4))
     for p in range(C - 1):
-        out.append(("embed_sum", B * H * 2 * (3 if p == 0 else 2) + 4 * B))
-        out.append(finish(False))
+        out.append(("embed_finish", B * V * 4 + 4 * B + B * H * 2 * (2 if p == 0 else 1) + operand))
         for _ in range(c.n_fast_layers):
             out += block((p + 1) * B * KVD * 2 * 2, True)
         out += head()
+    out.append(("argmax", B * V * 4 + 4 * B))
     return out
 
 

@@ -84,16 +84,18 @@ __device__ __forceinline__ bool better(float v, int i, float bv, int bi) {
     return v > bv || (v == bv && i < bi);
 }
 
-// One workgroup per row.
-__global__ __launch_bounds__(256) void argmax_kernel(const float* logits, int64_t N, int64_t ld, int32_t* codes,
-                                                     int64_t ldc) {
-    __shared__ float s_v[4];
-    __shared__ int s_i[4];
-    const int64_t b = blockIdx.x;
-    const float* r = logits + b * ld;
+// Greedy code of one row of N logits, by a workgroup of NT threads: each
+// thread scans n = t, t + NT, ... keeping its first maximum, then the waves
+// and the workgroup reduce with `better`.  An all-NaN row gives 0.  The
+// result is returned to every thread.
+template <int NT>
+__device__ __forceinline__ int argmax_row(const float* r, int64_t N) {
+    __shared__ float s_v[NT / 64];
+    __shared__ int s_i[NT / 64];
+    __shared__ int s_best;
     float bv = -INFINITY;
     int bi = 0x7FFFFFFF;
-    for (int64_t n = threadIdx.x; n < N; n += 256) {
+    for (int64_t n = threadIdx.x; n < N; n += NT) {
         const float v = r[n];
         if (v > bv) { bv = v; bi = (int)n; }      // increasing n: the first maximum stays
     }
@@ -107,10 +109,20 @@ __global__ __launch_bounds__(256) void argmax_kernel(const float* logits, int64_
     if ((threadIdx.x & 63) == 0) { s_v[wave] = bv; s_i[wave] = bi; }
     __syncthreads();
     if (threadIdx.x == 0) {
-        for (int w = 1; w < 4; ++w)
+        for (int w = 1; w < NT / 64; ++w)
             if (better(s_v[w], s_i[w], bv, bi)) { bv = s_v[w]; bi = s_i[w]; }
-        codes[b * ldc] = bi == 0x7FFFFFFF ? 0 : bi;
+        s_best = bi == 0x7FFFFFFF ? 0 : bi;
     }
+    __syncthreads();
+    return s_best;
+}
+
+// One workgroup per row.
+__global__ __launch_bounds__(256) void argmax_kernel(const float* logits, int64_t N, int64_t ld, int32_t* codes,
+                                                     int64_t ldc) {
+    const int64_t b = blockIdx.x;
+    const int code = argmax_row<256>(logits + b * ld, N);
+    if (threadIdx.x == 0) codes[b * ldc] = code;
 }
 
 // ---- row finisher -------------------------------------------------------------
@@ -139,9 +151,40 @@ struct FinishArgs {
     int M, H, KB;
 };
 
-__global__ __launch_bounds__(kFinishThreads) void finish_kernel(FinishArgs a) {
+// The row's sum of squares ss (this thread's part) -> RMSNorm with norm_w ->
+// bf16 -> 1x128 quantisation into the operand (and xn when asked).
+__device__ __forceinline__ void finish_tail(const FinishArgs& a, int m, const float (&x)[kFinishChunks][8],
+                                            const uint4 (&wn)[kFinishChunks], float ss) {
     constexpr int NW = kFinishThreads / 64;
     __shared__ float s_ss[NW];
+    const int t = threadIdx.x, nch = a.H / 8;
+    ss = fsum_xor<kWave>(ss);
+    if ((t & 63) == 0) s_ss[t >> 6] = ss;
+    __syncthreads();
+    float tot = 0.0f;
+#pragma unroll
+    for (int w = 0; w < NW; ++w) tot += s_ss[w];
+    const float inv = 1.0f / sqrtf(tot / (float)a.H + a.eps);
+#pragma unroll
+    for (int p = 0; p < kFinishChunks; ++p) {
+        const int c = t + kFinishThreads * p;
+        if (c >= nch) continue;
+        float w[8], f[8];
+        unpack_bf16x8(wn[p], w);
+#pragma unroll
+        for (int i = 0; i < 8; ++i) f[i] = bf16_to_f32(f32_to_bf16(x[p][i] * inv * w[i]));
+        if (a.xn) {
+            uint32_t o[4];
+#pragma unroll
+            for (int i = 0; i < 4; ++i) o[i] = f32_to_bf16(f[2 * i]) | (f32_to_bf16(f[2 * i + 1]) << 16);
+            *reinterpret_cast<uint4*>(a.xn + (int64_t)m * a.H + 8 * c) = make_uint4(o[0], o[1], o[2], o[3]);
+        }
+        quant_chunk<FP8S_MLP_BSGEMM>(f, a.qx + frag_off(m >> 4, c >> 4, a.KB),
+                                     scale_slot<FP8S_MLP_BSGEMM>(a.sx, m >> 4, c >> 4, a.KB), m & 15, c & 15);
+    }
+}
+
+__global__ __launch_bounds__(kFinishThreads) void finish_kernel(FinishArgs a) {
     const int m = blockIdx.x, t = threadIdx.x;
     const int nch = a.H / 8;
     float x[kFinishChunks][8];
@@ -191,36 +234,81 @@ __global__ __launch_bounds__(kFinishThreads) void finish_kernel(FinishArgs a) {
             x[p][i] = v[i];
         }
     }
-    ss = fsum_xor<kWave>(ss);
-    if ((t & 63) == 0) s_ss[t >> 6] = ss;
-    __syncthreads();
-    float tot = 0.0f;
+    finish_tail(a, m, x, wn, ss);
+}
+
+// Embedding rows fused with the finisher: one workgroup per row m builds x =
+// bf16(add + sum_t table_t[code_t]) in fp32 (as embed_kernel), writes it to
+// f.xout (the residual stream) and finishes it (RMSNorm, operand).  The codes
+// are codes_in[m][0 .. nt) (checked: an out-of-range code reports
+// FP8S_DEV_CODE_RANGE and adds nothing), or, with logits, the one code is the
+// argmax of the row's logits (as argmax_kernel), also stored to codes_out.
+// With steps, the row also fills steps[p * M + m] = p + 1 for p < n_steps
+// (the fast AR's kv_len table).
+struct EmbedFinishArgs {
+    FinishArgs f;
+    const uint16_t* t[kMaxTables];
+    int nt;
+    int64_t V;
+    const int32_t* codes_in; int64_t ldc_in;
+    const float* logits; int64_t ld_logits;
+    int32_t* codes_out; int64_t ldc_out;
+    const uint16_t* add;
+    int32_t* steps; int n_steps;
+    int32_t* err;
+};
+
+__global__ __launch_bounds__(kFinishThreads) void embed_finish_kernel(EmbedFinishArgs a) {
+    __shared__ int s_code[kMaxTables];
+    const int m = blockIdx.x, t = threadIdx.x;
+    const int H = a.f.H, nch = H / 8;
+    if (a.steps)
+        for (int p = t; p < a.n_steps; p += kFinishThreads) a.steps[(int64_t)p * a.f.M + m] = p + 1;
+    uint4 wn[kFinishChunks];                  // the norm weights, requested first
 #pragma unroll
-    for (int w = 0; w < NW; ++w) tot += s_ss[w];
-    const float inv = 1.0f / sqrtf(tot / (float)a.H + a.eps);
+    for (int p = 0; p < kFinishChunks; ++p)
+        wn[p] = *reinterpret_cast<const uint4*>(a.f.norm_w + 8 * min(t + kFinishThreads * p, nch - 1));
+    if (a.logits) {
+        const int code = argmax_row<kFinishThreads>(a.logits + (int64_t)m * a.ld_logits, a.V);
+        if (t == 0) {
+            a.codes_out[(int64_t)m * a.ldc_out] = code;
+            s_code[0] = code;
+        }
+    } else if (t < a.nt) {
+        int c = a.codes_in[(int64_t)m * a.ldc_in + t];
+        if (c < 0 || c >= a.V) {
+            report_error(a.err, FP8S_DEV_CODE_RANGE);
+            c = -1;
+        }
+        s_code[t] = c;
+    }
+    __syncthreads();
+    float x[kFinishChunks][8];
+    float ss = 0.0f;
 #pragma unroll
     for (int p = 0; p < kFinishChunks; ++p) {
         const int c = t + kFinishThreads * p;
         if (c >= nch) continue;
-        float w[8], f[8];
-        unpack_bf16x8(wn[p], w);
+        float f[8] = {0, 0, 0, 0, 0, 0, 0, 0};
+        if (a.add) unpack_bf16x8(*reinterpret_cast<const uint4*>(a.add + (int64_t)m * H + 8 * c), f);
+        for (int tt = 0; tt < a.nt; ++tt) {
+            const int code = s_code[tt];
+            if (code < 0) continue;
+            float e[8];
+            unpack_bf16x8(*reinterpret_cast<const uint4*>(a.t[tt] + (int64_t)code * H + 8 * c), e);
 #pragma unroll
-        for (int i = 0; i < 8; ++i) f[i] = bf16_to_f32(f32_to_bf16(x[p][i] * inv * w[i]));
-        if (a.xn) {
-            uint32_t o[4];
-#pragma unroll
-            for (int i = 0; i < 4; ++i) o[i] = f32_to_bf16(f[2 * i]) | (f32_to_bf16(f[2 * i + 1]) << 16);
-            *reinterpret_cast<uint4*>(a.xn + (int64_t)m * a.H + 8 * c) = make_uint4(o[0], o[1], o[2], o[3]);
+            for (int i = 0; i < 8; ++i) f[i] += e[i];
         }
-        quant_chunk<FP8S_MLP_BSGEMM>(f, a.qx + frag_off(m >> 4, c >> 4, a.KB),
-                                     scale_slot<FP8S_MLP_BSGEMM>(a.sx, m >> 4, c >> 4, a.KB), m & 15, c & 15);
+        uint32_t o[4];
+#pragma unroll
+        for (int i = 0; i < 8; ++i) x[p][i] = bf16_to_f32(f32_to_bf16(f[i]));
+#pragma unroll
+        for (int i = 0; i < 4; ++i) o[i] = f32_to_bf16(x[p][2 * i]) | (f32_to_bf16(x[p][2 * i + 1]) << 16);
+        *reinterpret_cast<uint4*>(a.f.xout + (int64_t)m * H + 8 * c) = make_uint4(o[0], o[1], o[2], o[3]);
+#pragma unroll
+        for (int i = 0; i < 8; ++i) ss = fmaf(x[p][i], x[p][i], ss);
     }
-}
-
-// kv_len table of the fast AR: table[p * B + b] = p + 1.
-__global__ __launch_bounds__(256) void fill_steps_kernel(int32_t* table, int P, int B) {
-    const int i = blockIdx.x * 256 + threadIdx.x;
-    if (i < P * B) table[i] = i / B + 1;
+    finish_tail(a.f, m, x, wn, ss);
 }
 
 // ---- host side ---------------------------------------------------------------
@@ -321,6 +409,44 @@ static int finish_rows(const StepCtx& c, const SplitPartials* part, const uint16
     a.M = (int)c.B; a.H = (int)c.m->hidden; a.KB = (int)(c.m->hidden / 128);
     FP8S_LAUNCH("row_finish", finish_kernel, dim3((unsigned)c.B), dim3(kFinishThreads), 0, as_stream(c.stream), a);
     const int rc = check_launch("row finish");
+    return rc ? step_error(rc, where) : FP8S_OK;
+}
+
+// Embedding rows straight into the finisher (embed_finish_kernel): the codes
+// are codes_in (nt tables) or, with logits, the argmax of each logits row
+// (one table), stored to codes_out.
+struct EmbedSpec {
+    const uint16_t* const* tables;
+    int nt;
+    const int32_t* codes_in;
+    int64_t ldc_in;
+    const float* logits;
+    int32_t* codes_out;
+    int64_t ldc_out;
+    const uint16_t* add;
+    int32_t* steps;
+    int n_steps;
+};
+
+static int embed_finish(const StepCtx& c, const EmbedSpec& e, uint16_t* xout, const uint16_t* norm_w, uint16_t* xn,
+                        uint8_t* qx, void* sx, const char* where) {
+    EmbedFinishArgs a{};
+    a.f.part = nullptr; a.f.S = 0; a.f.cols = 8;
+    a.f.base = nullptr; a.f.xout = xout; a.f.norm_w = norm_w; a.f.eps = c.m->rms_eps; a.f.xn = xn;
+    a.f.qx = qx; a.f.sx = static_cast<float*>(sx);
+    a.f.M = (int)c.B; a.f.H = (int)c.m->hidden; a.f.KB = (int)(c.m->hidden / 128);
+    for (int t = 0; t < e.nt; ++t) a.t[t] = e.tables[t];
+    a.nt = e.nt;
+    a.V = c.m->codebook_size;
+    a.codes_in = e.codes_in; a.ldc_in = e.ldc_in;
+    a.logits = e.logits; a.ld_logits = c.m->codebook_size;
+    a.codes_out = e.codes_out; a.ldc_out = e.ldc_out;
+    a.add = e.add;
+    a.steps = e.steps; a.n_steps = e.n_steps;
+    a.err = c.err;
+    FP8S_LAUNCH("embed_finish", embed_finish_kernel, dim3((unsigned)c.B), dim3(kFinishThreads), 0,
+                as_stream(c.stream), a);
+    const int rc = check_launch("embedding and row finish");
     return rc ? step_error(rc, where) : FP8S_OK;
 }
 
@@ -430,16 +556,14 @@ static int run_block(const StepCtx& c, const fp8s_block_weights& L, const uint16
     return finish_rows(c, &pd, xmid, xout, next_norm, xn, nq, ns, "mlp");
 }
 
-// logits = head . z with z already quantised in the qlinear workspace;
-// codes[:, col] = argmax.
-static int run_head(const StepCtx& c, const fp8s_qweight& head, float* logits, int32_t* codes, int col) {
+// logits = head . z with z already quantised in the qlinear workspace (the
+// greedy code is taken by the next embed_finish launch, or by argmax_kernel
+// for the last head).
+static int run_head(const StepCtx& c, const fp8s_qweight& head, float* logits) {
     const fp8s_dual_ar_model* m = c.m;
     int rc = qlinear_fp8_ex(nullptr, c.B, m->hidden, m->hidden, nullptr, 0.0f, head, m->codebook_size, nullptr, 0,
                             FP8S_OUT_F32, logits, m->codebook_size, c.ws + c.p->off_ql, c.p->ql_bytes, c.stream);
-    if (rc) return step_error(rc, "codebook head");
-    rc = argmax_rows_f32(logits, c.B, m->codebook_size, m->codebook_size, codes + col, m->n_codebooks, c.stream);
-    if (rc) return step_error(rc, "argmax");
-    return FP8S_OK;
+    return rc ? step_error(rc, "codebook head") : FP8S_OK;
 }
 
 }  // namespace fp8s
@@ -529,17 +653,16 @@ extern "C" int dual_ar_decode_step(const fp8s_dual_ar_model* m, int64_t B, const
     auto logits = [&](int cb) {
         return logits_tap ? logits_tap + (int64_t)cb * B * V : reinterpret_cast<float*>(ws + p.off_logits);
     };
-    hipStream_t st = as_stream(stream);
     uint8_t* oq;
     float* os;
     if ((rc = ql_operand(c, &oq, &os))) return step_error(rc, "workspace");
 
-    // ---- slow AR
-    rc = embed_sum_bf16(m->embed, C, V, H, prev_codes, C, B, nullptr, slow_x(0), err_flag, stream);
-    if (rc) return step_error(rc, "slow input embedding");
-    // operand of layer 0's QKV projection (or, with no layers, of the head)
-    rc = finish_rows(c, nullptr, slow_x(0), nullptr, L > 0 ? m->slow[0].norm_attn : m->slow_norm, L > 0 ? nullptr : h,
-                     oq, os, "slow input norm");
+    // ---- slow AR: the summed embeddings of the previous frame's codes, the
+    // operand of layer 0's QKV projection (or, with no layers, of the head),
+    // and the fast AR's kv_len table
+    int32_t* steps = reinterpret_cast<int32_t*>(ws + p.off_fsteps);
+    rc = embed_finish(c, EmbedSpec{m->embed, C, prev_codes, C, nullptr, nullptr, 0, nullptr, steps, p.FS}, slow_x(0),
+                      L > 0 ? m->slow[0].norm_attn : m->slow_norm, L > 0 ? nullptr : h, oq, os, "slow input");
     if (rc) return rc;
     for (int l = 0; l < L; ++l) {
         const bool last = l == L - 1;
@@ -548,20 +671,15 @@ extern "C" int dual_ar_decode_step(const fp8s_dual_ar_model* m, int64_t B, const
                        kv->cap, kv->kv_len, kv->max_kv_len_hint);
         if (rc) return rc;
     }
-    if ((rc = run_head(c, m->heads[0], logits(0), codes, 0))) return rc;
+    if ((rc = run_head(c, m->heads[0], logits(0)))) return rc;
 
-    // ---- fast AR over the remaining codebooks
-    int32_t* steps = reinterpret_cast<int32_t*>(ws + p.off_fsteps);
-    FP8S_LAUNCH("fill_steps", fill_steps_kernel, dim3((unsigned)((p.FS * B + 255) / 256)), dim3(256), 0, st, steps,
-                p.FS, (int)B);
-    if ((rc = check_launch("dual_ar_decode_step: fast steps"))) return rc;
+    // ---- fast AR over the remaining codebooks: micro-step s takes code s
+    // (the argmax of head s) and its embedding
     const int64_t fsh = (int64_t)p.FS * m->head_dim, fsb = (int64_t)m->n_kv_heads * fsh;
     for (int s = 0; s < C - 1; ++s) {
-        rc = embed_sum_bf16(&m->embed[s], 1, V, H, codes + s, C, B, s == 0 ? h : nullptr, fast_x(s, 0), err_flag,
-                            stream);
-        if (rc) return step_error(rc, "fast input embedding");
-        rc = finish_rows(c, nullptr, fast_x(s, 0), nullptr, F > 0 ? m->fast[0].norm_attn : m->fast_norm, nullptr, oq, os,
-                         "fast input norm");
+        rc = embed_finish(c, EmbedSpec{&m->embed[s], 1, nullptr, 0, logits(s), codes + s, C, s == 0 ? h : nullptr,
+                                       nullptr, 0},
+                          fast_x(s, 0), F > 0 ? m->fast[0].norm_attn : m->fast_norm, nullptr, oq, os, "fast input");
         if (rc) return rc;
         for (int f = 0; f < F; ++f) {
             uint16_t* fk = reinterpret_cast<uint16_t*>(ws + p.off_fk) + (int64_t)f * B * fsb;
@@ -571,7 +689,8 @@ extern "C" int dual_ar_decode_step(const fp8s_dual_ar_model* m, int64_t B, const
                            p.FS, steps + (int64_t)s * B, s + 1);
             if (rc) return rc;
         }
-        if ((rc = run_head(c, m->heads[s + 1], logits(s + 1), codes, s + 1))) return rc;
+        if ((rc = run_head(c, m->heads[s + 1], logits(s + 1)))) return rc;
     }
-    return FP8S_OK;
+    rc = argmax_rows_f32(logits(C - 1), B, V, V, codes + (C - 1), C, stream);
+    return rc ? step_error(rc, "argmax") : FP8S_OK;
 }

@@ -44,7 +44,7 @@ struct QlArgs {
     int epi;
     void* y; int64_t ldy;                     // EPI_BF16 / EPI_F32 output
     const uint16_t* res; int64_t ld_res;      // optional residual (EPI_BF16)
-    uint16_t* q; int nq, nkv, D;              // EPI_QKV: q [M, nq]; K/V columns nkv each
+    uint16_t* q; int nq, nkv, D, dlog;        // EPI_QKV: q [M, nq]; K/V columns nkv each; D = 1 << dlog
     uint16_t* kc; uint16_t* vc; int64_t sb, sh, st;
     const int32_t* kv_len; int64_t cap;
     const int32_t* live;                      // optional: rows >= *live append nothing
@@ -78,7 +78,7 @@ __device__ __forceinline__ void ql_epilogue(const QlArgs& a, int m, int n, float
         j -= a.nkv;
         c = a.vc;
     }
-    c[(int64_t)m * a.sb + (int64_t)(j / a.D) * a.sh + t * a.st + (j % a.D)] = b;
+    c[(int64_t)m * a.sb + (int64_t)(j >> a.dlog) * a.sh + t * a.st + (j & (a.D - 1))] = b;
 }
 
 template <int MT>
@@ -338,7 +338,7 @@ int qkv_proj_kv_append_ex(const uint16_t* x, int64_t M, int64_t K, int64_t ld_x,
     a.M = (int)M; a.N = (int)N;
     ql_weight(a, w_qkv);
     a.epi = EPI_QKV;
-    a.q = q_out; a.nq = Hq * D; a.nkv = Hkv * D; a.D = D;
+    a.q = q_out; a.nq = Hq * D; a.nkv = Hkv * D; a.D = D; a.dlog = D == 128 ? 7 : 6;
     a.kc = k_cache; a.vc = v_cache; a.sb = stride_b; a.sh = stride_h; a.st = stride_t;
     a.kv_len = kv_len; a.cap = cap; a.err = err_flag; a.live = live_rows;
     ql_launch(p, a, x, ld_x, K, norm_w, eps, workspace, as_stream(stream));

@@ -72,8 +72,8 @@ KERNELS = [
     (r"qlinear_kernel", "qlinear"),
     (r"embed_kernel", "embed_sum"),
     (r"argmax_kernel", "argmax"),
+    (r"embed_finish_kernel", "embed_finish"),
     (r"finish_kernel", "row_finish"),
-    (r"fill_steps_kernel", "fill_steps"),
     (r"quant_block128_kernel", "quantize_block128"),
     (r"quant_rows_kernel<128>", "quantize_1x128"),
     (r"quant_rows_kernel<32>", "quantize_1x32"),
