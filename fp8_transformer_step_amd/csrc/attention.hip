@@ -196,49 +196,67 @@ __device__ __forceinline__ void attn_piece(const AttnArgs& a, int b, int g, int 
         }
     }
 
-    // ---- scores: 16 positions per MFMA group, groups round-robin over waves
+    // ---- scores: 16 positions per MFMA group, groups round-robin over waves.
+    // A wave takes SG of its groups per iteration and issues all their K
+    // loads before the first MFMA (the compiler does not unroll a loop that
+    // holds MFMAs, so the batching is written out); a group past the piece
+    // loads nothing and writes nothing.
+    constexpr int SG = MX ? 4 : 2;
+    constexpr int QB = D / 4;                  // MX: bytes of a row per lane group, NJ pieces of 8
     const int n_grp = (n_tok + 15) / 16;
-#pragma unroll 2
-    for (int grp = wave; grp < n_grp; grp += 4) {
-        const int tl = grp * 16 + (lane & 15);             // position within the chunk
-        const bool live = tl < n_tok;
-        v4f acc = {0, 0, 0, 0};
-        uint4 kw[NJ];
-        if constexpr (MX) {
-            constexpr int QB = D / 4;            // bytes of the row per lane group: NJ pieces of 8
-            uint4 raw[QB / 16];
-            float X = 0.0f;
+    for (int grp0 = wave; grp0 < n_grp; grp0 += 4 * SG) {
+        uint4 kw[MX ? 1 : SG][NJ];             // bf16 K operands
+        uint4 raw[MX ? SG : 1][QB / 16];       // MX: e4m3 bytes
+        float X[MX ? SG : 1];                  //   and their scale
 #pragma unroll
-            for (int i = 0; i < QB / 16; ++i) raw[i] = make_uint4(0, 0, 0, 0);
-            if (live) {
-                const int64_t t = t_begin + tl;
-                const uint8_t* src = kqbase + row(t) + (lane >> 4) * QB;
+        for (int u = 0; u < SG; ++u) {
+            const int tl = (grp0 + 4 * u) * 16 + (lane & 15);     // position within the piece
+            const bool live = tl < n_tok;
+            if constexpr (MX) {
 #pragma unroll
-                for (int i = 0; i < QB / 16; ++i) raw[i] = reinterpret_cast<const uint4*>(src)[i];
-                X = ue8m0_f32(kebase[erow(t) + (lane >> 4) * QB / 32]);
-            }
+                for (int i = 0; i < QB / 16; ++i) raw[u][i] = make_uint4(0, 0, 0, 0);
+                X[u] = 0.0f;
+                if (live) {
+                    const int64_t t = t_begin + tl;
+                    const uint8_t* src = kqbase + row(t) + (lane >> 4) * QB;
 #pragma unroll
-            for (int j = 0; j < NJ; ++j) {
-                const uint32_t w0 = j & 1 ? raw[j / 2].z : raw[j / 2].x, w1 = j & 1 ? raw[j / 2].w : raw[j / 2].y;
-                kw[j] = make_uint4(fp8x2_bf16x2<false>(w0, X), fp8x2_bf16x2<true>(w0, X),
-                                   fp8x2_bf16x2<false>(w1, X), fp8x2_bf16x2<true>(w1, X));
-            }
-        } else {
+                    for (int i = 0; i < QB / 16; ++i) raw[u][i] = reinterpret_cast<const uint4*>(src)[i];
+                    X[u] = ue8m0_f32(kebase[erow(t) + (lane >> 4) * QB / 32]);
+                }
+            } else {
 #pragma unroll
-            for (int j = 0; j < NJ; ++j) {
-                kw[j] = make_uint4(0, 0, 0, 0);
-                if (live)
-                    kw[j] = *reinterpret_cast<const uint4*>(kbase + row(t_begin + tl) + 32 * j + 8 * (lane >> 4));
+                for (int j = 0; j < NJ; ++j) {
+                    kw[u][j] = make_uint4(0, 0, 0, 0);
+                    if (live)
+                        kw[u][j] = *reinterpret_cast<const uint4*>(kbase + row(t_begin + tl) + 32 * j + 8 * (lane >> 4));
+                }
             }
         }
+        __builtin_amdgcn_sched_barrier(0);     // all of the batch's K loads before its first MFMA
 #pragma unroll
-        for (int j = 0; j < NJ; ++j)
-            acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(qa[j], __builtin_bit_cast(v8bf, kw[j]), acc, 0, 0, 0);
-        // lane holds S[head 4*(lane/16)+r][position tl]
+        for (int u = 0; u < SG; ++u) {
+            const int tl = (grp0 + 4 * u) * 16 + (lane & 15);
+            const bool live = tl < n_tok;
+            v4f acc = {0, 0, 0, 0};
 #pragma unroll
-        for (int r = 0; r < 4; ++r) {
-            const int h = 4 * (lane >> 4) + r;
-            if (h < G && live) s_p[h][tl] = acc[r] * a.scale_log2;
+            for (int j = 0; j < NJ; ++j) {
+                uint4 k;
+                if constexpr (MX) {
+                    const uint32_t w0 = j & 1 ? raw[u][j / 2].z : raw[u][j / 2].x;
+                    const uint32_t w1 = j & 1 ? raw[u][j / 2].w : raw[u][j / 2].y;
+                    k = make_uint4(fp8x2_bf16x2<false>(w0, X[u]), fp8x2_bf16x2<true>(w0, X[u]),
+                                   fp8x2_bf16x2<false>(w1, X[u]), fp8x2_bf16x2<true>(w1, X[u]));
+                } else {
+                    k = kw[u][j];
+                }
+                acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(qa[j], __builtin_bit_cast(v8bf, k), acc, 0, 0, 0);
+            }
+            // lane holds S[head 4*(lane/16)+r][position tl]
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+                const int h = 4 * (lane >> 4) + r;
+                if (h < G && live) s_p[h][tl] = acc[r] * a.scale_log2;
+            }
         }
     }
     __syncthreads();
@@ -267,31 +285,52 @@ __device__ __forceinline__ void attn_piece(const AttnArgs& a, int b, int g, int 
         for (int i = 0; i < 8; ++i) o[h][i] = 0.0f;
     const int dl = 8 * (lane % LPR);
     const int slot = lane / LPR;
-#pragma unroll 4
-    for (int t = wave * TPL + slot; t < n_tok; t += 4 * TPL) {
-        float vf[8];
-        if constexpr (MX) {
-            const int64_t tt = (int64_t)(t_begin + t);
-            const uint2 w = *reinterpret_cast<const uint2*>(vqbase + row(tt) + dl);
-            const float X = ue8m0_f32(vebase[erow(tt) + dl / 32]);
-            const uint32_t ww[2] = {w.x, w.y};
+    // PB row slots per lane and iteration, all loaded before any is used (so
+    // that PB rows per lane are in flight; MXFP8 rows are half as wide and
+    // take twice as many).  A slot past the piece loads the piece's last row
+    // and is skipped; rows are added in ascending order.
+    constexpr int PB = MX ? 8 : 4;
+    for (int t0 = wave * TPL + slot; t0 < n_tok; t0 += PB * 4 * TPL) {
+        uint4 vb[MX ? 1 : PB];
+        uint2 vm[MX ? PB : 1];
+        float vx[MX ? PB : 1];
 #pragma unroll
-            for (int i = 0; i < 2; ++i) {
-                const auto lo = __builtin_amdgcn_cvt_scalef32_pk_f32_fp8((int)ww[i], X, false);
-                const auto hi = __builtin_amdgcn_cvt_scalef32_pk_f32_fp8((int)ww[i], X, true);
-                vf[4 * i] = lo[0]; vf[4 * i + 1] = lo[1]; vf[4 * i + 2] = hi[0]; vf[4 * i + 3] = hi[1];
+        for (int u = 0; u < PB; ++u) {
+            const int64_t tt = t_begin + min(t0 + u * 4 * TPL, n_tok - 1);
+            if constexpr (MX) {
+                vm[u] = *reinterpret_cast<const uint2*>(vqbase + row(tt) + dl);
+                vx[u] = ue8m0_f32(vebase[erow(tt) + dl / 32]);
+            } else {
+                vb[u] = *reinterpret_cast<const uint4*>(vbase + row(tt) + dl);
             }
-        } else {
-            const uint4 w = *reinterpret_cast<const uint4*>(vbase + row(t_begin + t) + dl);
-            const uint32_t ww[4] = {w.x, w.y, w.z, w.w};
-#pragma unroll
-            for (int i = 0; i < 4; ++i) { vf[2 * i] = bf16_to_f32(ww[i] & 0xFFFFu); vf[2 * i + 1] = bf16_to_f32(ww[i] >> 16); }
         }
+        // keep the batch's loads ahead of its math: left alone, the scheduler
+        // sinks each load to its first use and the rows go one at a time
+        __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-        for (int h = 0; h < G; ++h) {
-            const float p = s_p[h][t];
+        for (int u = 0; u < PB; ++u) {
+            const int t = t0 + u * 4 * TPL;
+            if (t >= n_tok) break;
+            float vf[8];
+            if constexpr (MX) {
+                const uint32_t ww[2] = {vm[u].x, vm[u].y};
 #pragma unroll
-            for (int i = 0; i < 8; ++i) o[h][i] += p * vf[i];
+                for (int i = 0; i < 2; ++i) {
+                    const auto lo = __builtin_amdgcn_cvt_scalef32_pk_f32_fp8((int)ww[i], vx[u], false);
+                    const auto hi = __builtin_amdgcn_cvt_scalef32_pk_f32_fp8((int)ww[i], vx[u], true);
+                    vf[4 * i] = lo[0]; vf[4 * i + 1] = lo[1]; vf[4 * i + 2] = hi[0]; vf[4 * i + 3] = hi[1];
+                }
+            } else {
+                const uint32_t ww[4] = {vb[u].x, vb[u].y, vb[u].z, vb[u].w};
+#pragma unroll
+                for (int i = 0; i < 4; ++i) { vf[2 * i] = bf16_to_f32(ww[i] & 0xFFFFu); vf[2 * i + 1] = bf16_to_f32(ww[i] >> 16); }
+            }
+#pragma unroll
+            for (int h = 0; h < G; ++h) {
+                const float p = s_p[h][t];
+#pragma unroll
+                for (int i = 0; i < 8; ++i) o[h][i] += p * vf[i];
+            }
         }
     }
     // reduce the TPL row slots of the wave, then the 4 waves
@@ -444,18 +483,18 @@ __global__ __launch_bounds__(256) void attn_bal_kernel(AttnArgs a) {
     attn_bal_body<D, G, false, PAGED>(a);
 }
 
-// The MXFP8-cache kernel holds five workgroups per CU only when capped at
-// 102 registers (measured faster: 85 against 90 us at B = 64, kv up to
-// 4096); the bf16 kernel is faster uncapped.  The paged balanced MXFP8
-// kernel spills under that cap and is capped at 128 registers instead
-// (97.5 against 105.8 us with 16-position pages).
+// The balanced MXFP8-cache kernel is capped at 128 registers (four
+// workgroups per CU), which holds its batch of eight V rows per lane without
+// spilling (77.8 against 99.5 us at B = 64, kv U[234, 4096], for five
+// workgroups per CU with the rows loaded one at a time); the chunked MXFP8
+// kernel holds five per CU at 102 registers; the bf16 kernel runs uncapped.
 template <int D, int G, bool SINGLE, bool PAGED>
 __global__ __launch_bounds__(256, 5) void attn_split_mx_kernel(AttnArgs a) {
     attn_split_body<D, G, SINGLE, true, PAGED>(a);
 }
 
 template <int D, int G, bool PAGED>
-__global__ __launch_bounds__(256, PAGED ? 4 : 5) void attn_bal_mx_kernel(AttnArgs a) {
+__global__ __launch_bounds__(256, 4) void attn_bal_mx_kernel(AttnArgs a) {
     attn_bal_body<D, G, true, PAGED>(a);
 }
 
