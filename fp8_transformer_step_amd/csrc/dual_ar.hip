@@ -93,11 +93,19 @@ __device__ __forceinline__ int argmax_row(const float* r, int64_t N) {
     __shared__ float s_v[NT / 64];
     __shared__ int s_i[NT / 64];
     __shared__ int s_best;
+    constexpr int U = 8;                       // values per thread loaded together
     float bv = -INFINITY;
     int bi = 0x7FFFFFFF;
-    for (int64_t n = threadIdx.x; n < N; n += NT) {
-        const float v = r[n];
-        if (v > bv) { bv = v; bi = (int)n; }      // increasing n: the first maximum stays
+    for (int64_t n0 = threadIdx.x; n0 < N; n0 += U * NT) {
+        float v[U];
+#pragma unroll
+        for (int u = 0; u < U; ++u) v[u] = r[min(n0 + (int64_t)u * NT, N - 1)];
+        __builtin_amdgcn_sched_barrier(0);     // all U loads in flight before the first compare
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+            const int64_t n = n0 + (int64_t)u * NT;
+            if (n < N && v[u] > bv) { bv = v[u]; bi = (int)n; }   // increasing n: the first maximum stays
+        }
     }
 #pragma unroll
     for (int o = 1; o < kWave; o <<= 1) {
@@ -198,12 +206,12 @@ __global__ __launch_bounds__(kFinishThreads) void finish_kernel(FinishArgs a) {
         const int c = t + kFinishThreads * p;
         if (c >= nch) continue;
         float v[8];
-        unpack_bf16x8(*reinterpret_cast<const uint4*>(a.base + (int64_t)m * a.H + 8 * c), v);
+        const uint4 braw = *reinterpret_cast<const uint4*>(a.base + (int64_t)m * a.H + 8 * c);
         if (a.part) {
             const int n = 8 * c;
             const float* ps = a.part + ((int64_t)(n / a.cols) * a.S * a.M + m) * a.cols + n % a.cols;
-            // the loads of kFinishBatch splits are issued together, then
-            // added in split order
+            // the loads of kFinishBatch splits are issued together (with the
+            // row), then added in split order
             float acc[8] = {0, 0, 0, 0, 0, 0, 0, 0};
             const int64_t ss_ = (int64_t)a.M * a.cols;
             for (int s0 = 0; s0 < a.S; s0 += kFinishBatch) {
@@ -214,6 +222,9 @@ __global__ __launch_bounds__(kFinishThreads) void finish_kernel(FinishArgs a) {
                     pv[u][0] = *reinterpret_cast<const float4*>(q);
                     pv[u][1] = *reinterpret_cast<const float4*>(q + 4);
                 }
+                // left alone, the scheduler sinks each load to its use and
+                // the splits arrive one round trip after another
+                __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
                 for (int u = 0; u < kFinishBatch; ++u) {
                     if (s0 + u >= a.S) break;
@@ -222,11 +233,14 @@ __global__ __launch_bounds__(kFinishThreads) void finish_kernel(FinishArgs a) {
                 }
             }
             uint32_t o[4];
+            unpack_bf16x8(braw, v);
 #pragma unroll
             for (int i = 0; i < 8; ++i) v[i] = bf16_to_f32(f32_to_bf16(acc[i] + v[i]));
 #pragma unroll
             for (int i = 0; i < 4; ++i) o[i] = f32_to_bf16(v[2 * i]) | (f32_to_bf16(v[2 * i + 1]) << 16);
             if (a.xout) *reinterpret_cast<uint4*>(a.xout + (int64_t)m * a.H + n) = make_uint4(o[0], o[1], o[2], o[3]);
+        } else {
+            unpack_bf16x8(braw, v);
         }
 #pragma unroll
         for (int i = 0; i < 8; ++i) {
