@@ -202,3 +202,29 @@ def test_packed_weights_give_the_same_step():
         out.append((codes.cpu().numpy(), logits.cpu().numpy()))
     np.testing.assert_array_equal(out[0][0], out[1][0])
     np.testing.assert_array_equal(out[0][1], out[1][1])
+
+
+def test_out_of_range_previous_code_is_reported_and_skipped():
+    """A previous-frame code outside [0, codebook_size) sets
+    FP8S_DEV_CODE_RANGE and adds nothing to its row's input embedding; the
+    other rows and codes are untouched."""
+    need_gpu()
+    host = model.HostModel(model.scaled(model.TINY, batch=5, n_heads=4))
+    c = host.cfg
+    B, H, C, V = c.batch, c.hidden, c.n_codebooks, c.codebook_size
+    dm = model.device_model(host)
+    kv, _, _ = model.device_kv(host)
+    prev = host.prev_codes.copy()
+    prev[2, 3] = V
+    prev[4, 0] = -1
+    slow_taps = torch.empty((2 * c.n_slow_layers + 1, B, H), dtype=torch.bfloat16, device="cuda")
+    err = torch.zeros(1, dtype=torch.int32, device="cuda")
+    ops.dual_ar_decode_step(dm, kv, torch.from_numpy(prev).cuda(), slow_taps=slow_taps, err=err)
+    torch.cuda.synchronize()
+    assert int(err.item()) == ops.DEV_CODE_RANGE
+    got = _np(slow_taps[0])
+    tables = [f32(t) for t in host.embed]
+    for b in range(B):
+        keep = [t for t in range(C) if 0 <= prev[b, t] < V]
+        want = oracle.embed_sum([tables[t] for t in keep], prev[b:b + 1, keep])[0]
+        assert _ulp_close(got[b], want), b
