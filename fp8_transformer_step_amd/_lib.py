@@ -43,7 +43,11 @@ class KvStateC(ctypes.Structure):
     """Mirror of fp8s_kv_state (cache arrays are host pointers)."""
     _fields_ = [("k_cache", ctypes.POINTER(c_vp)), ("v_cache", ctypes.POINTER(c_vp)),
                 ("stride_b", c_i64), ("stride_h", c_i64), ("stride_t", c_i64), ("cap", c_i64),
-                ("kv_len", c_vp), ("max_kv_len_hint", c_i64), ("live_rows", c_vp)]
+                ("kv_len", c_vp), ("max_kv_len_hint", c_i64), ("live_rows", c_vp),
+                ("kv_format", c_i32),
+                ("k_q", ctypes.POINTER(c_vp)), ("k_e", ctypes.POINTER(c_vp)),
+                ("v_q", ctypes.POINTER(c_vp)), ("v_e", ctypes.POINTER(c_vp)),
+                ("sstride_b", c_i64), ("sstride_h", c_i64), ("sstride_t", c_i64)]
 
 
 # name -> (restype, argtypes)
@@ -97,6 +101,9 @@ SIGNATURES = {
     "qkv_proj_kv_append": (ctypes.c_int, [c_vp, c_i64, c_i64, c_i64, c_vp, ctypes.c_float, QWeightC, c_i32, c_i32,
                                           c_i32, c_vp, c_vp, c_vp, c_i64, c_i64, c_i64, c_vp, c_i64, c_vp, c_sz,
                                           c_vp, c_vp]),
+    "qkv_proj_kv_append_mxkv": (ctypes.c_int, [c_vp, c_i64, c_i64, c_i64, c_vp, ctypes.c_float, QWeightC, c_i32,
+                                               c_i32, c_i32, c_vp, c_vp, c_vp, c_vp, c_vp, c_i64, c_i64, c_i64,
+                                               c_i64, c_i64, c_i64, c_vp, c_i64, c_vp, c_sz, c_vp, c_vp]),
     "embed_sum_bf16": (ctypes.c_int, [ctypes.POINTER(c_vp), c_i32, c_i64, c_i64, c_vp, c_i64, c_i64, c_vp, c_vp,
                                       c_vp, c_vp]),
     "argmax_rows_f32": (ctypes.c_int, [c_vp, c_i64, c_i64, c_i64, c_vp, c_i64, c_vp]),

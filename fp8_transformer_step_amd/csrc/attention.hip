@@ -823,13 +823,14 @@ int gqa_decode_attn_ex(const uint16_t* q, const uint16_t* k_cache, const uint16_
 }
 
 // MXFP8 caches (kq/ke, vq/ve): the checks and layout rules of the bf16 path,
-// with byte strides; the query, output and workspace are as there.
-static int gqa_decode_attn_mxkv_ex(const uint16_t* q, const uint8_t* kq, const uint8_t* ke, const uint8_t* vq,
+// with byte strides; the query, output, quantised output and workspace are
+// as there.
+int gqa_decode_attn_mxkv_ex(const uint16_t* q, const uint8_t* kq, const uint8_t* ke, const uint8_t* vq,
                             const uint8_t* ve, int64_t stride_b, int64_t stride_h, int64_t stride_t, int64_t sstride_b,
                             int64_t sstride_h, int64_t sstride_t, const int32_t* kv_len, int64_t B, int32_t Hq,
                             int32_t Hkv, int32_t D, int64_t cap, int64_t hint, float softmax_scale, uint16_t* out,
-                            void* workspace, size_t workspace_bytes, int32_t* err_flag, void* stream,
-                            const PagedSpec* paged = nullptr) {
+                            uint8_t* qo, float* so, void* workspace, size_t workspace_bytes, int32_t* err_flag,
+                            void* stream, const PagedSpec* paged) {
     FP8S_REQUIRE(q && kq && ke && vq && ve && kv_len && out, FP8S_EINVAL, "gqa_decode_attn_mxkv: null pointer");
     FP8S_REQUIRE(B >= 1 && Hq >= 1 && Hkv >= 1 && cap >= 1 && hint >= 1, FP8S_EINVAL,
                  "gqa_decode_attn_mxkv: sizes must be positive");
@@ -846,6 +847,8 @@ static int gqa_decode_attn_mxkv_ex(const uint16_t* q, const uint8_t* kq, const u
     FP8S_REQUIRE(aligned16(q) && aligned16(kq) && aligned16(vq) && aligned16(out), FP8S_EINVAL,
                  "gqa_decode_attn_mxkv: q, caches and out must be 16-byte aligned");
     FP8S_REQUIRE(B * Hkv <= (1ll << 24), FP8S_EUNSUPPORTED, "gqa_decode_attn_mxkv: batch too large");
+    FP8S_REQUIRE(!qo || (so && (G * D) % 128 == 0), FP8S_EUNSUPPORTED,
+                 "gqa_decode_attn_mxkv: a quantised output needs whole 128-column groups per KV head");
     if (hint > cap) hint = cap;
     const AttnPlan p = plan_attn(B, Hq, Hkv, D, hint);
     const size_t need = p.need;
@@ -865,7 +868,7 @@ static int gqa_decode_attn_mxkv_ex(const uint16_t* q, const uint8_t* kq, const u
     set_split_layout(a, p, workspace);
     a.out = out;
     a.err = err_flag;
-    a.qo = nullptr; a.so = nullptr; a.qo_KB = Hq * D / 128;
+    a.qo = qo; a.so = so; a.qo_KB = Hq * D / 128;
     set_paged(a, paged);
     return attn_launch<true>(a, D, G, as_stream(stream));
 }
@@ -894,8 +897,8 @@ extern "C" int gqa_decode_attn_mxkv(const uint16_t* q, const uint8_t* k_q, const
                                     int32_t* err_flag, void* stream) {
     clear_error();
     return gqa_decode_attn_mxkv_ex(q, k_q, k_e, v_q, v_e, stride_b, stride_h, stride_t, sstride_b, sstride_h,
-                                   sstride_t, kv_len, B, Hq, Hkv, D, cap, hint, softmax_scale, out, workspace,
-                                   workspace_bytes, err_flag, stream);
+                                   sstride_t, kv_len, B, Hq, Hkv, D, cap, hint, softmax_scale, out, nullptr, nullptr,
+                                   workspace, workspace_bytes, err_flag, stream);
 }
 
 extern "C" int gqa_decode_attn(const uint16_t* q, const uint16_t* k_cache, const uint16_t* v_cache,
@@ -942,6 +945,6 @@ extern "C" int gqa_decode_attn_paged_mxkv(const uint16_t* q, const uint8_t* k_q,
                                max_pages_per_seq, B, &spec, &cap);
     if (rc) return rc;
     return gqa_decode_attn_mxkv_ex(q, k_q, k_e, v_q, v_e, stride_page, stride_h, stride_t, sstride_page, sstride_h,
-                                   sstride_t, kv_len, B, Hq, Hkv, D, cap, hint, softmax_scale, out, workspace,
-                                   workspace_bytes, err_flag, stream, &spec);
+                                   sstride_t, kv_len, B, Hq, Hkv, D, cap, hint, softmax_scale, out, nullptr, nullptr,
+                                   workspace, workspace_bytes, err_flag, stream, &spec);
 }

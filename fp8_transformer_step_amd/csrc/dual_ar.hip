@@ -504,8 +504,8 @@ static int tap_copy(void* dst, const void* src, size_t n, void* stream) {
 }
 
 static int run_block(const StepCtx& c, const fp8s_block_weights& L, const uint16_t* xin, uint16_t* xmid,
-                     uint16_t* xout, const uint16_t* next_norm, uint16_t* xn, uint16_t* kc, uint16_t* vc, int64_t sb,
-                     int64_t sh, int64_t stt, int64_t cap, const int32_t* kv_len, int64_t hint) {
+                     uint16_t* xout, const uint16_t* next_norm, uint16_t* xn, const KvDest& kvd,
+                     const int32_t* kv_len, int64_t hint) {
     const fp8s_dual_ar_model* m = c.m;
     const int64_t H = m->hidden, A = (int64_t)m->n_heads * m->head_dim;
     uint16_t* q = reinterpret_cast<uint16_t*>(c.ws + c.p->off_q);
@@ -514,8 +514,7 @@ static int run_block(const StepCtx& c, const fp8s_block_weights& L, const uint16
     void* mlpw = c.ws + c.p->off_mlp;
     const bool slow_layer = &L >= m->slow && &L < m->slow + m->n_slow_layers;
     int rc = qkv_proj_kv_append_ex(nullptr, c.B, H, H, nullptr, 0.0f, L.qkv, m->n_heads, m->n_kv_heads, m->head_dim,
-                                   q, kc, vc, sb, sh, stt, kv_len, cap, qlw, c.p->ql_bytes, c.err, c.stream,
-                                   slow_layer ? c.live : nullptr);
+                                   q, kvd, kv_len, qlw, c.p->ql_bytes, c.err, c.stream, slow_layer ? c.live : nullptr);
     if (rc) return step_error(rc, "qkv projection");
     // The attention quantises its own output straight into the output
     // projection's operand when every KV head's query group covers whole
@@ -524,9 +523,16 @@ static int run_block(const StepCtx& c, const fp8s_block_weights& L, const uint16
     uint8_t* qo = nullptr;
     float* so = nullptr;
     if ((rc = qlinear_operand(c.B, H, A, qlw, c.p->ql_bytes, &qo, &so))) return step_error(rc, "attention");
-    rc = gqa_decode_attn_ex(q, kc, vc, sb, sh, stt, kv_len, c.B, m->n_heads, m->n_kv_heads, m->head_dim, cap, hint,
-                            1.0f / sqrtf((float)m->head_dim), ao, fuse ? qo : nullptr, fuse ? so : nullptr,
-                            c.ws + c.p->off_attn, c.p->attn_bytes, c.err, c.stream);
+    const float scale = 1.0f / sqrtf((float)m->head_dim);
+    if (kvd.mx)
+        rc = gqa_decode_attn_mxkv_ex(q, kvd.kq, kvd.ke, kvd.vq, kvd.ve, kvd.sb, kvd.sh, kvd.st, kvd.esb, kvd.esh,
+                                     kvd.est, kv_len, c.B, m->n_heads, m->n_kv_heads, m->head_dim, kvd.cap, hint, scale,
+                                     ao, fuse ? qo : nullptr, fuse ? so : nullptr, c.ws + c.p->off_attn,
+                                     c.p->attn_bytes, c.err, c.stream);
+    else
+        rc = gqa_decode_attn_ex(q, kvd.k, kvd.v, kvd.sb, kvd.sh, kvd.st, kv_len, c.B, m->n_heads, m->n_kv_heads,
+                                m->head_dim, kvd.cap, hint, scale, ao, fuse ? qo : nullptr, fuse ? so : nullptr,
+                                c.ws + c.p->off_attn, c.p->attn_bytes, c.err, c.stream);
     if (rc) return step_error(rc, "attention");
     if (!fuse) {                               // quantise ao into the same operand buffer
         if ((rc = qlinear_quantize_operand(ao, c.B, A, qo, so, c.stream))) return step_error(rc, "attention");
@@ -631,10 +637,15 @@ extern "C" int dual_ar_decode_step(const fp8s_dual_ar_model* m, int64_t B, const
     int rc = check_model(m, B, kv->max_kv_len_hint);
     if (rc) return rc;
     FP8S_REQUIRE(prev_codes && codes, FP8S_EINVAL, "dual_ar_decode_step: null codes");
-    FP8S_REQUIRE(m->n_slow_layers == 0 || (kv->k_cache && kv->v_cache && kv->kv_len), FP8S_EINVAL,
-                 "dual_ar_decode_step: null cache array or kv_len");
+    FP8S_REQUIRE(kv->kv_format == FP8S_KV_BF16 || kv->kv_format == FP8S_KV_MXFP8, FP8S_EINVAL,
+                 "dual_ar_decode_step: unknown kv_format %d", kv->kv_format);
+    const bool mx = kv->kv_format == FP8S_KV_MXFP8;
+    FP8S_REQUIRE(m->n_slow_layers == 0 || (kv->kv_len && (mx ? kv->k_q && kv->k_e && kv->v_q && kv->v_e
+                                                             : kv->k_cache && kv->v_cache)),
+                 FP8S_EINVAL, "dual_ar_decode_step: null cache array or kv_len");
     for (int l = 0; l < m->n_slow_layers; ++l)
-        FP8S_REQUIRE(kv->k_cache[l] && kv->v_cache[l], FP8S_EINVAL, "dual_ar_decode_step: null cache of layer %d", l);
+        FP8S_REQUIRE(mx ? kv->k_q[l] && kv->k_e[l] && kv->v_q[l] && kv->v_e[l] : kv->k_cache[l] && kv->v_cache[l],
+                     FP8S_EINVAL, "dual_ar_decode_step: null cache of layer %d", l);
     FP8S_REQUIRE(!slow_taps || aligned16(slow_taps), FP8S_EINVAL, "dual_ar_decode_step: slow_taps unaligned");
     FP8S_REQUIRE(!fast_taps || aligned16(fast_taps), FP8S_EINVAL, "dual_ar_decode_step: fast_taps unaligned");
     const StepPlan p = plan_step(m, B, kv->max_kv_len_hint);
@@ -680,9 +691,17 @@ extern "C" int dual_ar_decode_step(const fp8s_dual_ar_model* m, int64_t B, const
     if (rc) return rc;
     for (int l = 0; l < L; ++l) {
         const bool last = l == L - 1;
+        KvDest kvd{};
+        kvd.mx = mx;
+        if (mx) {
+            kvd.kq = kv->k_q[l]; kvd.ke = kv->k_e[l]; kvd.vq = kv->v_q[l]; kvd.ve = kv->v_e[l];
+            kvd.esb = kv->sstride_b; kvd.esh = kv->sstride_h; kvd.est = kv->sstride_t;
+        } else {
+            kvd.k = kv->k_cache[l]; kvd.v = kv->v_cache[l];
+        }
+        kvd.sb = kv->stride_b; kvd.sh = kv->stride_h; kvd.st = kv->stride_t; kvd.cap = kv->cap;
         rc = run_block(c, m->slow[l], slow_x(l), slow_mid(l), slow_x(l + 1), last ? m->slow_norm : m->slow[l + 1].norm_attn,
-                       last ? h : nullptr, kv->k_cache[l], kv->v_cache[l], kv->stride_b, kv->stride_h, kv->stride_t,
-                       kv->cap, kv->kv_len, kv->max_kv_len_hint);
+                       last ? h : nullptr, kvd, kv->kv_len, kv->max_kv_len_hint);
         if (rc) return rc;
     }
     if ((rc = run_head(c, m->heads[0], logits(0)))) return rc;
@@ -698,9 +717,11 @@ extern "C" int dual_ar_decode_step(const fp8s_dual_ar_model* m, int64_t B, const
         for (int f = 0; f < F; ++f) {
             uint16_t* fk = reinterpret_cast<uint16_t*>(ws + p.off_fk) + (int64_t)f * B * fsb;
             uint16_t* fv = reinterpret_cast<uint16_t*>(ws + p.off_fv) + (int64_t)f * B * fsb;
+            KvDest kvd{};
+            kvd.k = fk; kvd.v = fv; kvd.sb = fsb; kvd.sh = fsh; kvd.st = m->head_dim; kvd.cap = p.FS;
             rc = run_block(c, m->fast[f], fast_x(s, f), fast_mid(s, f), fast_x(s, f + 1),
-                           f + 1 < F ? m->fast[f + 1].norm_attn : m->fast_norm, nullptr, fk, fv, fsb, fsh, m->head_dim,
-                           p.FS, steps + (int64_t)s * B, s + 1);
+                           f + 1 < F ? m->fast[f + 1].norm_attn : m->fast_norm, nullptr, kvd, steps + (int64_t)s * B,
+                           s + 1);
             if (rc) return rc;
         }
         if ((rc = run_head(c, m->heads[s + 1], logits(s + 1)))) return rc;

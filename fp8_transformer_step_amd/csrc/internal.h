@@ -59,12 +59,29 @@ int qlinear_operand(int64_t M, int64_t N, int64_t K, void* workspace, size_t wor
 int qlinear_fp8_ex(const uint16_t* x, int64_t M, int64_t K, int64_t ld_x, const uint16_t* norm_w, float eps,
                    fp8s_qweight w, int64_t N, const uint16_t* residual, int64_t ld_res, int out_dtype, void* y,
                    int64_t ld_y, void* workspace, size_t workspace_bytes, void* stream);
+// Where qkv_proj_kv_append puts the new K/V rows: bf16 caches (k, v with
+// element strides) or MXFP8 caches (e4m3 bytes kq, vq with byte strides and
+// UE8M0 exponents ke, ve with their own strides).
+struct KvDest {
+    bool mx;
+    uint16_t* k; uint16_t* v;
+    uint8_t* kq; uint8_t* vq; uint8_t* ke; uint8_t* ve;
+    int64_t sb, sh, st;                       // cache strides (elements, or bytes for MX)
+    int64_t esb, esh, est;                    // exponent strides (MX)
+    int64_t cap;
+};
 int qkv_proj_kv_append_ex(const uint16_t* x, int64_t M, int64_t K, int64_t ld_x, const uint16_t* norm_w, float eps,
                           fp8s_qweight w_qkv, int32_t Hq, int32_t Hkv, int32_t D, uint16_t* q_out,
-                          uint16_t* k_cache, uint16_t* v_cache, int64_t stride_b, int64_t stride_h,
-                          int64_t stride_t, const int32_t* kv_len, int64_t cap, void* workspace,
-                          size_t workspace_bytes, int32_t* err_flag, void* stream,
-                          const int32_t* live_rows = nullptr);
+                          const KvDest& dst, const int32_t* kv_len, void* workspace, size_t workspace_bytes,
+                          int32_t* err_flag, void* stream, const int32_t* live_rows = nullptr);
+
+// gqa_decode_attn_mxkv with the quantised output of gqa_decode_attn_ex.
+int gqa_decode_attn_mxkv_ex(const uint16_t* q, const uint8_t* kq, const uint8_t* ke, const uint8_t* vq,
+                            const uint8_t* ve, int64_t stride_b, int64_t stride_h, int64_t stride_t, int64_t sstride_b,
+                            int64_t sstride_h, int64_t sstride_t, const int32_t* kv_len, int64_t B, int32_t Hq,
+                            int32_t Hkv, int32_t D, int64_t cap, int64_t hint, float softmax_scale, uint16_t* out,
+                            uint8_t* qo, float* so, void* workspace, size_t workspace_bytes, int32_t* err_flag,
+                            void* stream, const PagedSpec* paged = nullptr);
 
 // x [M, K] bf16 (contiguous rows) quantised in 1x128 groups into the operand
 // layout of qlinear_operand.

@@ -46,6 +46,9 @@ struct QlArgs {
     const uint16_t* res; int64_t ld_res;      // optional residual (EPI_BF16)
     uint16_t* q; int nq, nkv, D, dlog;        // EPI_QKV: q [M, nq]; K/V columns nkv each; D = 1 << dlog
     uint16_t* kc; uint16_t* vc; int64_t sb, sh, st;
+    int kv_mx;                                // MXFP8 caches: e4m3 kq, vq (byte strides sb, sh, st) and
+    uint8_t* kq; uint8_t* vq;                 // UE8M0 exponents ke, ve (strides esb, esh, est)
+    uint8_t* ke; uint8_t* ve; int64_t esb, esh, est;
     const int32_t* kv_len; int64_t cap;
     const int32_t* live;                      // optional: rows >= *live append nothing
     int32_t* err;
@@ -79,6 +82,51 @@ __device__ __forceinline__ void ql_epilogue(const QlArgs& a, int m, int n, float
         c = a.vc;
     }
     c[(int64_t)m * a.sb + (int64_t)(j >> a.dlog) * a.sh + t * a.st + (j & (a.D - 1))] = b;
+}
+
+// The MXFP8 K/V append of one row's 32-column group (one group of 32 d:
+// kQlCols is 32 and K/V columns start on a multiple of 32).  `width` lanes
+// hold the group, `per` values each (v[0..per)), value i of lane l being
+// column col(l, i) of the group; the group's lanes are an aligned run of
+// `width` within the wave, and all of them must call this (the amax is a
+// lane reduction) with the same m.  The values are rounded to bf16 (what
+// the bf16 append stores), then quantised as qlinear_quantize mode 2 does:
+// amax over the bf16 magnitudes, E = mx_exponent(amax), byte =
+// e4m3(value * 2^(127 - E)).
+template <int WIDTH, int PER, typename Col>
+__device__ __forceinline__ void kv_append_mx(const QlArgs& a, int m, int n0, const float (&v)[PER], int lane,
+                                             Col col) {
+    uint16_t b[PER];
+    uint32_t am = 0;
+#pragma unroll
+    for (int i = 0; i < PER; ++i) {
+        b[i] = (uint16_t)f32_to_bf16(v[i]);
+        const uint32_t mag = b[i] & 0x7FFFu;
+        am = am > mag ? am : mag;
+    }
+    am = umax_xor<WIDTH>(am);
+    if (m >= a.M) return;
+    if (a.live && m >= *a.live) return;       // a padding row: its cache slot is not ours
+    const int64_t t = (int64_t)a.kv_len[m] - 1;
+    if (t < 0 || t >= a.cap) {                // nothing is written outside the cache
+        report_error(a.err, FP8S_DEV_KVLEN_RANGE);
+        return;
+    }
+    const int E = mx_exponent(am << 16);
+    const float mul = mx_inv_scale(E);
+    int j = n0 - a.nq;
+    uint8_t* cq = a.kq;
+    uint8_t* ce = a.ke;
+    if (j >= a.nkv) {
+        j -= a.nkv;
+        cq = a.vq;
+        ce = a.ve;
+    }
+    const int64_t g = j >> a.dlog, d0 = j & (a.D - 1);
+    uint8_t* row = cq + m * a.sb + g * a.sh + t * a.st + d0;
+#pragma unroll
+    for (int i = 0; i < PER; ++i) row[col(lane, i)] = (uint8_t)e4m3x2(bf16_to_f32(b[i]) * mul, 0.0f);
+    if ((lane & (WIDTH - 1)) == 0) ce[m * a.esb + g * a.esh + t * a.est + (d0 >> 5)] = (uint8_t)E;
 }
 
 template <int MT>
@@ -115,7 +163,19 @@ __global__ __launch_bounds__(256, 2) void qlinear_kernel(QlArgs a) {
     reduce_wk<MTS, NB, WK>(acc, lds, wm, wk, lane);
 
     if (a.S == 1 && a.epi != EPI_PARTIAL) {   // the whole K range: the epilogue straight from registers
-        if (wk == 0) {
+        if (wk == 0 && a.epi == EPI_QKV && a.kv_mx && n0 >= a.nq) {
+            // lane l holds columns l % 16 (tile 0) and 16 + l % 16 (tile 1) of
+            // rows 4 (l / 16) + r: a row's group is the 16 lanes of l / 16
+            static_assert(NB == 2, "one 32-column MX group per item");
+#pragma unroll
+            for (int i = 0; i < MTS; ++i)
+#pragma unroll
+                for (int r = 0; r < 4; ++r) {
+                    const int m = (wm * MTS + i) * 16 + 4 * (lane >> 4) + r;
+                    const float v[2] = {acc[0][i][r], acc[1][i][r]};
+                    kv_append_mx<16, 2>(a, m, n0, v, lane, [](int l, int k) { return 16 * k + (l & 15); });
+                }
+        } else if (wk == 0) {
 #pragma unroll
             for (int j = 0; j < NB; ++j)
 #pragma unroll
@@ -152,10 +212,21 @@ __global__ __launch_bounds__(256, 2) void qlinear_kernel(QlArgs a) {
     constexpr int kItems = MT * 16 * kQlCols / 256;
     float sum[kItems];
     sum_partials<kItems>(a.part + (int64_t)nt * a.S * a.M * kQlCols, (int64_t)a.M * kQlCols, a.S, a.M * kQlCols, sum);
+    if (a.epi == EPI_QKV && a.kv_mx && n0 >= a.nq) {
+        // element e = (row e / 32, column e % 32): a row's group is an aligned
+        // run of 32 threads, all of which take part (rows >= M too)
 #pragma unroll
-    for (int i = 0; i < kItems; ++i) {
-        const int e = threadIdx.x + 256 * i;
-        if (e < a.M * kQlCols) ql_epilogue(a, e / kQlCols, n0 + e % kQlCols, sum[i]);
+        for (int i = 0; i < kItems; ++i) {
+            const int e = threadIdx.x + 256 * i;
+            const float v[1] = {sum[i]};
+            kv_append_mx<32, 1>(a, e / kQlCols, n0, v, threadIdx.x & 63, [](int l, int) { return l & 31; });
+        }
+    } else {
+#pragma unroll
+        for (int i = 0; i < kItems; ++i) {
+            const int e = threadIdx.x + 256 * i;
+            if (e < a.M * kQlCols) ql_epilogue(a, e / kQlCols, n0 + e % kQlCols, sum[i]);
+        }
     }
     if (threadIdx.x == 0) store_relaxed_agent(a.cnt + nt, 0);
 }
@@ -321,9 +392,8 @@ int qlinear_quantize_operand(const uint16_t* x, int64_t M, int64_t K, uint8_t* q
 
 int qkv_proj_kv_append_ex(const uint16_t* x, int64_t M, int64_t K, int64_t ld_x, const uint16_t* norm_w, float eps,
                           fp8s_qweight w_qkv, int32_t Hq, int32_t Hkv, int32_t D, uint16_t* q_out,
-                          uint16_t* k_cache, uint16_t* v_cache, int64_t stride_b, int64_t stride_h,
-                          int64_t stride_t, const int32_t* kv_len, int64_t cap, void* workspace,
-                          size_t workspace_bytes, int32_t* err_flag, void* stream, const int32_t* live_rows) {
+                          const KvDest& dst, const int32_t* kv_len, void* workspace, size_t workspace_bytes,
+                          int32_t* err_flag, void* stream, const int32_t* live_rows) {
     FP8S_REQUIRE(Hq >= 1 && Hkv >= 1 && Hq % Hkv == 0, FP8S_EINVAL, "qkv_proj_kv_append: Hq must be a multiple of Hkv");
     FP8S_REQUIRE(D == 64 || D == 128, FP8S_EUNSUPPORTED, "qkv_proj_kv_append: head_dim %d (64 or 128)", D);
     const int64_t N = (int64_t)(Hq + 2 * Hkv) * D;
@@ -331,16 +401,21 @@ int qkv_proj_kv_append_ex(const uint16_t* x, int64_t M, int64_t K, int64_t ld_x,
     int rc = ql_check_common("qkv_proj_kv_append", x ? x : kNoX, M, K, x ? ld_x : K, norm_w, eps, w_qkv, N,
                              workspace, workspace_bytes, &p);
     if (rc) return rc;
-    FP8S_REQUIRE(q_out && k_cache && v_cache && kv_len, FP8S_EINVAL, "qkv_proj_kv_append: null output or kv_len");
-    FP8S_REQUIRE(cap >= 1 && stride_t >= D && stride_h >= 1 && stride_b >= 1, FP8S_EINVAL,
+    FP8S_REQUIRE(q_out && kv_len && (dst.mx ? dst.kq && dst.vq && dst.ke && dst.ve : dst.k && dst.v), FP8S_EINVAL,
+                 "qkv_proj_kv_append: null output or kv_len");
+    FP8S_REQUIRE(dst.cap >= 1 && dst.st >= D && dst.sh >= 1 && dst.sb >= 1, FP8S_EINVAL,
                  "qkv_proj_kv_append: bad cache capacity or strides");
+    FP8S_REQUIRE(!dst.mx || (dst.est >= D / 32 && dst.esh >= 0 && dst.esb >= 0), FP8S_EINVAL,
+                 "qkv_proj_kv_append_mxkv: exponent strides must be non-negative with sstride_t >= D/32");
     QlArgs a{};
     a.M = (int)M; a.N = (int)N;
     ql_weight(a, w_qkv);
     a.epi = EPI_QKV;
     a.q = q_out; a.nq = Hq * D; a.nkv = Hkv * D; a.D = D; a.dlog = D == 128 ? 7 : 6;
-    a.kc = k_cache; a.vc = v_cache; a.sb = stride_b; a.sh = stride_h; a.st = stride_t;
-    a.kv_len = kv_len; a.cap = cap; a.err = err_flag; a.live = live_rows;
+    a.kc = dst.k; a.vc = dst.v; a.sb = dst.sb; a.sh = dst.sh; a.st = dst.st;
+    a.kv_mx = dst.mx;
+    a.kq = dst.kq; a.vq = dst.vq; a.ke = dst.ke; a.ve = dst.ve; a.esb = dst.esb; a.esh = dst.esh; a.est = dst.est;
+    a.kv_len = kv_len; a.cap = dst.cap; a.err = err_flag; a.live = live_rows;
     ql_launch(p, a, x, ld_x, K, norm_w, eps, workspace, as_stream(stream));
     return check_launch("qkv_proj_kv_append");
 }
@@ -370,6 +445,26 @@ extern "C" int qkv_proj_kv_append(const uint16_t* x, int64_t M, int64_t K, int64
                                   void* workspace, size_t workspace_bytes, int32_t* err_flag, void* stream) {
     clear_error();
     FP8S_REQUIRE(x, FP8S_EINVAL, "qkv_proj_kv_append: null x");
-    return qkv_proj_kv_append_ex(x, M, K, ld_x, norm_w, eps, w_qkv, Hq, Hkv, D, q_out, k_cache, v_cache, stride_b,
-                                 stride_h, stride_t, kv_len, cap, workspace, workspace_bytes, err_flag, stream);
+    KvDest dst{};
+    dst.k = k_cache; dst.v = v_cache;
+    dst.sb = stride_b; dst.sh = stride_h; dst.st = stride_t; dst.cap = cap;
+    return qkv_proj_kv_append_ex(x, M, K, ld_x, norm_w, eps, w_qkv, Hq, Hkv, D, q_out, dst, kv_len, workspace,
+                                 workspace_bytes, err_flag, stream);
+}
+
+extern "C" int qkv_proj_kv_append_mxkv(const uint16_t* x, int64_t M, int64_t K, int64_t ld_x, const uint16_t* norm_w,
+                                       float eps, fp8s_qweight w_qkv, int32_t Hq, int32_t Hkv, int32_t D,
+                                       uint16_t* q_out, uint8_t* k_q, uint8_t* k_e, uint8_t* v_q, uint8_t* v_e,
+                                       int64_t stride_b, int64_t stride_h, int64_t stride_t, int64_t sstride_b,
+                                       int64_t sstride_h, int64_t sstride_t, const int32_t* kv_len, int64_t cap,
+                                       void* workspace, size_t workspace_bytes, int32_t* err_flag, void* stream) {
+    clear_error();
+    FP8S_REQUIRE(x, FP8S_EINVAL, "qkv_proj_kv_append_mxkv: null x");
+    KvDest dst{};
+    dst.mx = true;
+    dst.kq = k_q; dst.ke = k_e; dst.vq = v_q; dst.ve = v_e;
+    dst.sb = stride_b; dst.sh = stride_h; dst.st = stride_t; dst.cap = cap;
+    dst.esb = sstride_b; dst.esh = sstride_h; dst.est = sstride_t;
+    return qkv_proj_kv_append_ex(x, M, K, ld_x, norm_w, eps, w_qkv, Hq, Hkv, D, q_out, dst, kv_len, workspace,
+                                 workspace_bytes, err_flag, stream);
 }

@@ -103,9 +103,12 @@ def device_model(host, device="cuda", packed=True):
                            c.n_heads, c.n_kv_heads, c.head_dim, c.inter, c.rms_eps)
 
 
-def device_kv(host, device="cuda", garbage_seed=1234):
+def device_kv(host, device="cuda", garbage_seed=1234, mx=False):
     """Physical K/V sets [B, Hkv, cap, D] with the seeded prefixes and random
-    bytes (NaN and Inf patterns included) in every unfilled slot."""
+    bytes (NaN and Inf patterns included) in every unfilled slot.
+    mx: MXFP8 caches (ops.MxKvCache) instead, each set the library's 1x32
+    quantisation of the bf16 set, garbage slots included (they stay garbage:
+    NaN codes and arbitrary exponents)."""
     c = host.cfg
     g = torch.Generator(device=device)
     g.manual_seed(garbage_seed)
@@ -122,6 +125,10 @@ def device_kv(host, device="cuda", garbage_seed=1234):
         ks.append(kc.view(torch.bfloat16))
         vs.append(vc.view(torch.bfloat16))
     kv_len = torch.from_numpy(host.kv_len).to(device)
+    if mx:
+        ks = [ops.quantize_kv_mx(k) for k in ks]
+        vs = [ops.quantize_kv_mx(v) for v in vs]
+        torch.cuda.synchronize()
     layers_k = [ks[l % c.kv_sets] for l in range(c.n_slow_layers)]
     layers_v = [vs[l % c.kv_sets] for l in range(c.n_slow_layers)]
     return ops.KvState(layers_k, layers_v, kv_len, int(host.kv_len.max())), ks, vs

@@ -546,6 +546,29 @@ def qkv_proj_kv_append(x, w_qkv, Hq, Hkv, D, k_cache, v_cache, kv_len, norm_w=No
     return q_out
 
 
+def qkv_proj_kv_append_mxkv(x, w_qkv, Hq, Hkv, D, k, v, kv_len, norm_w=None, eps=1e-6,
+                            q_out=None, workspace=None, err=None):
+    """qkv_proj_kv_append into MXFP8 caches k, v (MxKvCache): the new rows'
+    e4m3 bytes and UE8M0 exponents are written at kv_len - 1."""
+    _require_cuda(x, k.q, k.e, v.q, v.e, kv_len)
+    if k.q.stride() != v.q.stride() or k.e.stride() != v.e.stride() or k.q.shape != v.q.shape:
+        raise ValueError("k and v must share shapes and strides")
+    if k.q.stride(3) != 1 or k.e.stride(3) != 1:
+        raise ValueError("the head dimension must be contiguous")
+    M, K = x.shape
+    N = (Hq + 2 * Hkv) * D
+    if q_out is None:
+        q_out = torch.empty((M, Hq * D), dtype=torch.bfloat16, device=x.device)
+    if workspace is None:
+        workspace = new_qlinear_workspace(M, N, K, x.device)
+    _lib.check(_lib.load().qkv_proj_kv_append_mxkv(
+        _bits(x), M, K, x.stride(0), _opt_ptr(norm_w), float(eps), w_qkv.as_c(), Hq, Hkv, D, _bits(q_out),
+        k.q.data_ptr(), k.e.data_ptr(), v.q.data_ptr(), v.e.data_ptr(),
+        k.q.stride(0), k.q.stride(1), k.q.stride(2), k.e.stride(0), k.e.stride(1), k.e.stride(2),
+        kv_len.data_ptr(), k.q.shape[2], workspace.data_ptr(), workspace.numel(), _opt_ptr(err), _stream()))
+    return q_out
+
+
 def embed_sum(tables, codes, add=None, out=None, err=None):
     """out[b] = bf16(add[b] + sum_c tables[c][codes[b, c]]); codes int32 [B, >= len(tables)]."""
     import ctypes
@@ -608,28 +631,48 @@ class DualArModel:
         return torch.zeros(n, dtype=torch.uint8, device=device)
 
 
+KV_BF16, KV_MXFP8 = 0, 1
+
+
 class KvState:
-    """Per-slow-layer K/V caches (each [B, Hkv, cap, D], shared strides) and kv_len."""
+    """Per-slow-layer K/V caches and kv_len: bf16 tensors [B, Hkv, cap, D],
+    or MxKvCache objects (MXFP8), all with shared shapes and strides."""
 
     def __init__(self, k_caches, v_caches, kv_len, max_kv_len_hint, live_rows=None):
         """live_rows: optional device int32 [1]; rows b >= live_rows[0] of a
         step are padding and append no K/V (see fp8s_kv_state)."""
         import ctypes
-        k0 = k_caches[0]
+        mx = isinstance(k_caches[0], MxKvCache)
+        if any(isinstance(t, MxKvCache) != mx for t in list(k_caches) + list(v_caches)):
+            raise TypeError("the caches must be all bf16 tensors or all MxKvCache")
+        k0 = k_caches[0].q if mx else k_caches[0]
+        e0 = k_caches[0].e if mx else None
         for t in list(k_caches) + list(v_caches):
-            if t.stride() != k0.stride() or t.shape != k0.shape or t.stride(3) != 1:
+            tq = t.q if mx else t
+            if tq.stride() != k0.stride() or tq.shape != k0.shape or tq.stride(3) != 1:
                 raise ValueError("all caches must share shape and strides, D contiguous")
+            if mx and (t.e.stride() != e0.stride() or t.e.stride(3) != 1):
+                raise ValueError("all exponent caches must share strides, D/32 contiguous")
         if kv_len.dtype != torch.int32:
             raise TypeError("kv_len must be int32")
         if live_rows is not None and (live_rows.dtype != torch.int32 or not live_rows.is_cuda):
             raise TypeError("live_rows must be an int32 device tensor")
         self.k_caches, self.v_caches, self.kv_len, self.live_rows = k_caches, v_caches, kv_len, live_rows
         self.max_kv_len_hint = int(max_kv_len_hint)
-        self._k = (ctypes.c_void_p * len(k_caches))(*[t.data_ptr() for t in k_caches])
-        self._v = (ctypes.c_void_p * len(v_caches))(*[t.data_ptr() for t in v_caches])
-        self.c = _lib.KvStateC(self._k, self._v, k0.stride(0), k0.stride(1), k0.stride(2), k0.shape[2],
-                               kv_len.data_ptr(), int(max_kv_len_hint),
-                               live_rows.data_ptr() if live_rows is not None else None)
+        self.mx = mx
+        ptrs = lambda ts: (ctypes.c_void_p * len(ts))(*[t.data_ptr() for t in ts])
+        if mx:
+            self._kq, self._ke = ptrs([t.q for t in k_caches]), ptrs([t.e for t in k_caches])
+            self._vq, self._ve = ptrs([t.q for t in v_caches]), ptrs([t.e for t in v_caches])
+            self.c = _lib.KvStateC(None, None, k0.stride(0), k0.stride(1), k0.stride(2), k0.shape[2],
+                                   kv_len.data_ptr(), int(max_kv_len_hint),
+                                   live_rows.data_ptr() if live_rows is not None else None, KV_MXFP8,
+                                   self._kq, self._ke, self._vq, self._ve, e0.stride(0), e0.stride(1), e0.stride(2))
+        else:
+            self._k, self._v = ptrs(k_caches), ptrs(v_caches)
+            self.c = _lib.KvStateC(self._k, self._v, k0.stride(0), k0.stride(1), k0.stride(2), k0.shape[2],
+                                   kv_len.data_ptr(), int(max_kv_len_hint),
+                                   live_rows.data_ptr() if live_rows is not None else None, KV_BF16)
 
     def with_live_rows(self, live_rows):
         """The same caches and kv_len with a padding-row count (device int32 [1])."""

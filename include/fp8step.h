@@ -461,6 +461,33 @@ FP8S_API int qkv_proj_kv_append(const uint16_t* x, int64_t M, int64_t K, int64_t
                        int32_t* err_flag, void* stream);
 
 /*
+ * qkv_proj_kv_append_mxkv -- qkv_proj_kv_append into MXFP8 KV caches (the
+ * pages' FP8/MX decode-attention variant, [TTS] "What's Open Source" and
+ * "FP8 Quantization Strategy"; the cache layout read by
+ * gqa_decode_attn_mxkv).  The new K and V rows are first rounded to bf16,
+ * exactly the values qkv_proj_kv_append would store, then quantised in
+ * 1x32 groups as qlinear_quantize mode 2 quantises a bf16 row: for each 32
+ * consecutive d, E = UE8M0 exponent of the group's largest magnitude and
+ * byte = e4m3(value * 2^(127 - E)).  So the bytes and exponents written
+ * equal those of qlinear_quantize mode 2 applied to the bf16 row, bit for
+ * bit.  Writes
+ *   k_q[m*stride_b + g*stride_h + t*stride_t + d]      <- e4m3 byte of key d
+ *   k_e[m*sstride_b + g*sstride_h + t*sstride_t + d/32] <- its group's exponent
+ *   v_q, v_e the same for the value columns;  q_out as qkv_proj_kv_append.
+ * Byte strides; stride_t >= D, sstride_t >= D/32.  Everything else (t,
+ * the kv_len range check, D, Hq, the workspace) as qkv_proj_kv_append.
+ */
+FP8S_API int qkv_proj_kv_append_mxkv(const uint16_t* x, int64_t M, int64_t K, int64_t ld_x,
+                       const uint16_t* norm_w, float eps, fp8s_qweight w_qkv,
+                       int32_t Hq, int32_t Hkv, int32_t D, uint16_t* q_out,
+                       uint8_t* k_q, uint8_t* k_e, uint8_t* v_q, uint8_t* v_e,
+                       int64_t stride_b, int64_t stride_h, int64_t stride_t,
+                       int64_t sstride_b, int64_t sstride_h, int64_t sstride_t,
+                       const int32_t* kv_len, int64_t cap,
+                       void* workspace, size_t workspace_bytes,
+                       int32_t* err_flag, void* stream);
+
+/*
  * embed_sum_bf16 -- out[b, :] = bf16( add[b, :] + sum_{c < n_tables}
  * tables[c][codes[b * ld_codes + c], :] ), summed in fp32 in table order: the
  * input of a Dual-AR step is the embedding of the previous frame's codes
@@ -630,7 +657,10 @@ FP8S_API int prev_tokens_shift_inplace(int32_t* prev, const int32_t* next_tokens
  * kv_len = p + 1, and sets code p+1 = argmax(head_{p+1} . RMSNorm_fast(z)).
  * No rotary embedding; softmax scale 1/sqrt(D); all activations bf16, every
  * projection an FP8 bsgemm GEMM (128x128 weight blocks, 1x128 activation
- * groups).
+ * groups).  With kv->kv_format == FP8S_KV_MXFP8 the slow layers append and
+ * attend as qkv_proj_kv_append_mxkv and gqa_decode_attn_mxkv do (the
+ * attention reads the dequantised MXFP8 caches); the fast AR's own small
+ * cache stays bf16.
  */
 typedef struct fp8s_block_weights {
     fp8s_qweight qkv;             /* [(Hq + 2*Hkv)*D, hidden]              */
@@ -655,6 +685,13 @@ typedef struct fp8s_dual_ar_model {
     const fp8s_qweight* heads;           /* HOST array [C] of [V, hidden]    */
 } fp8s_dual_ar_model;
 
+/* Formats of the slow AR's KV caches. */
+enum {
+    FP8S_KV_BF16 = 0,   /* bf16 elements                                        */
+    FP8S_KV_MXFP8 = 1   /* e4m3 bytes + one UE8M0 exponent per 32 d (the layout of
+                           gqa_decode_attn_mxkv; appended as qkv_proj_kv_append_mxkv) */
+};
+
 typedef struct fp8s_kv_state {
     uint16_t* const* k_cache;            /* HOST array [n_slow_layers] of   */
     uint16_t* const* v_cache;            /*   device bf16 caches (strides)  */
@@ -665,6 +702,16 @@ typedef struct fp8s_kv_state {
                                             padding (a graph captured for a larger batch):
                                             their K/V is not appended to the caches and
                                             their codes must be ignored; null = all live */
+    int32_t kv_format;                   /* FP8S_KV_BF16 or FP8S_KV_MXFP8 */
+    /* FP8S_KV_MXFP8 only (k_cache and v_cache are then unused): HOST arrays
+       [n_slow_layers] of device e4m3 byte caches and UE8M0 exponent caches;
+       byte (b, g, t, d) at b*stride_b + g*stride_h + t*stride_t + d and its
+       exponent at b*sstride_b + g*sstride_h + t*sstride_t + d/32. */
+    uint8_t* const* k_q;
+    uint8_t* const* k_e;
+    uint8_t* const* v_q;
+    uint8_t* const* v_e;
+    int64_t sstride_b, sstride_h, sstride_t;
 } fp8s_kv_state;
 
 /*

@@ -37,7 +37,7 @@ from .fp8 import (  # noqa: F401
     dequant_mx_1x32,
 )
 from .mlp import linear_dequant, swiglu, swiglu_mlp  # noqa: F401
-from .attention import gqa_decode_attention, kv_len_schedule  # noqa: F401
+from .attention import gqa_decode_attention, kv_len_schedule, mx_kv_store  # noqa: F401
 from .dual_ar import (  # noqa: F401
     RMS_EPS,
     round_bf16,

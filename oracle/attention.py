@@ -111,6 +111,18 @@ def dequant_mx_rows(codes, exps):
     return flat.reshape(codes.shape)
 
 
+def mx_kv_store(rows):
+    """The values an MXFP8 KV cache holds for bf16 rows [..., D]: each row
+    quantised in 1x32 groups with UE8M0 shared exponents (OCP MX, the MXFP8
+    attention variant of "How We Made Our Text-to-Speech API Free", "What's
+    Open Source", and its "FP8 Quantization Strategy" groups), then
+    dequantised exactly."""
+    rows = np.asarray(rows, np.float64)
+    D = rows.shape[-1]
+    q, e = fp8.quant_mx_1x32(rows.reshape(-1, D))
+    return fp8.dequant_mx_1x32(q, e).reshape(rows.shape)
+
+
 def gqa_decode_attention_mxkv(q, k_codes, k_exps, v_codes, v_exps, kv_len, scale=None):
     """gqa_decode_attention over MXFP8 caches: k_codes, v_codes [B, Hkv, T, D]
     e4m3 bytes, k_exps, v_exps [B, Hkv, T, D/32] UE8M0 bytes.  Only rows

@@ -98,15 +98,19 @@ def dequant_weight(w_bf16_values):
     return q, s, dequant_block_fp32(q, s, 128, 128)
 
 
-def attention_block(x, p, k_cache, v_cache, kv_len, n_heads, n_kv_heads, head_dim, eps=RMS_EPS):
+def attention_block(x, p, k_cache, v_cache, kv_len, n_heads, n_kv_heads, head_dim, eps=RMS_EPS, kv_store=None):
     """First half of a pre-norm block: x + O(attn(qkv(RMSNorm(x)))).
 
     x        : [B, H] bf16 values
     p        : dict with dequantised 'qkv' [(Hq+2Hkv)D, H], 'o' [H, Hq D] and
                the bf16 RMSNorm weight 'norm_attn' [H]
-    k_cache, v_cache : [B, Hkv, slots, D] arrays, written at kv_len[b] - 1
-               (the new token) and read over [0, kv_len[b])
-    Returns (x_mid, dict of the intermediates).
+    k_cache, v_cache : [B, Hkv, slots, D] arrays (the values the cache
+               holds), written at kv_len[b] - 1 (the new token) and read over
+               [0, kv_len[b])
+    kv_store : the values a cache holds for the new bf16 K/V rows [Hkv, D]
+               (None: the rows themselves, a bf16 cache; attention.mx_kv_store
+               for an MXFP8 cache)
+    Returns (x_mid, dict of the intermediates; 'k', 'v' are the bf16 rows).
     """
     x = np.asarray(x, np.float64)
     B = x.shape[0]
@@ -120,8 +124,8 @@ def attention_block(x, p, k_cache, v_cache, kv_len, n_heads, n_kv_heads, head_di
         t = int(kv_len[b]) - 1
         if not 0 <= t < k_cache.shape[2]:
             raise ValueError(f"kv_len[{b}] = {t + 1} outside [1, {k_cache.shape[2]}]")
-        k_cache[b, :, t, :] = k[b]
-        v_cache[b, :, t, :] = v[b]
+        k_cache[b, :, t, :] = k[b] if kv_store is None else kv_store(k[b])
+        v_cache[b, :, t, :] = v[b] if kv_store is None else kv_store(v[b])
     attn = round_bf16(gqa_decode_attention(q, k_cache, v_cache, kv_len)).reshape(B, Hq * D)
     x_mid = round_bf16(x + fp8_linear(attn, p["o"]))
     return x_mid, {"xn": xn, "q": q, "k": k, "v": v, "attn": attn}
@@ -160,7 +164,7 @@ def greedy_code(z_normed, head_deq):
     return logits, np.argmax(logits, axis=1).astype(np.int32)
 
 
-def dual_ar_step(model, prev_codes, slow_k, slow_v, kv_len, force=None):
+def dual_ar_step(model, prev_codes, slow_k, slow_v, kv_len, force=None, slow_kv_store=None):
     """One batched Dual-AR decode step.
 
     model : dict with
@@ -183,6 +187,9 @@ def dual_ar_step(model, prev_codes, slow_k, slow_v, kv_len, force=None):
       Each half-block then starts from the forced input instead of the
       oracle's own previous output, and each micro-step embeds the forced code
       (FP8 re-quantisation flips and argmax near-ties cannot compound).
+    slow_kv_store : the kv_store of the slow layers' caches (see
+      attention_block; slow_k, slow_v then hold the values those caches
+      hold); the fast AR's own cache is bf16.
     Returns a dict with slow_x [2L+1], h, logits [C], codes [B, C], fast_x
     [C-1][2F+1] (each entry the oracle's output given its (forced) input), and
     the K/V rows written per layer ('slow_kv', 'fast_kv').
@@ -196,9 +203,9 @@ def dual_ar_step(model, prev_codes, slow_k, slow_v, kv_len, force=None):
     def stream_in(own, forced, i):
         return own[i] if forced is None else np.asarray(forced[i], np.float64)
 
-    def run_layers(xs, forced, layers, ks, vs, lens, kv_out):
+    def run_layers(xs, forced, layers, ks, vs, lens, kv_out, store=None):
         for l, p in enumerate(layers):
-            x_mid, it = attention_block(stream_in(xs, forced, 2 * l), p, ks[l], vs[l], lens, Hq, Hkv, D, eps)
+            x_mid, it = attention_block(stream_in(xs, forced, 2 * l), p, ks[l], vs[l], lens, Hq, Hkv, D, eps, store)
             xs.append(x_mid)
             out, _ = mlp_block(stream_in(xs, forced, 2 * l + 1), p, eps)
             xs.append(out)
@@ -206,7 +213,8 @@ def dual_ar_step(model, prev_codes, slow_k, slow_v, kv_len, force=None):
 
     slow_x = [embed_sum(model["embed"], prev_codes)]
     slow_kv = []
-    run_layers(slow_x, None if force is None else force["slow_x"], model["slow"], slow_k, slow_v, kv_len, slow_kv)
+    run_layers(slow_x, None if force is None else force["slow_x"], model["slow"], slow_k, slow_v, kv_len, slow_kv,
+               slow_kv_store)
     h = rmsnorm(stream_in(slow_x, None if force is None else force["slow_x"], 2 * L), model["slow_norm"], eps)
     logits = [None] * C
     codes = np.zeros((B, C), np.int32)

@@ -18,6 +18,10 @@ from fp8_transformer_step_amd import model, ops
 from _helpers import TOL_FP8_PATH, f32, log, max_rel_err, need_gpu
 
 pytestmark = pytest.mark.gpu
+# An MXFP8 cache row against the bf16 row it stores: up to 1/8 of a group's
+# largest magnitude (saturation at 448 of a group scaled into [256, 512)),
+# plus the bf16 path's own tolerance for the row itself.
+MX_KV_TOL = 1 / 8 + TOL_FP8_PATH
 
 
 def _np(t):
@@ -44,17 +48,34 @@ def _prefix_cache(host, s, rows):
     return k, v
 
 
+def _prefix_cache_mx(host, s, rows):
+    """_prefix_cache as an MXFP8 cache holds it (the oracle's MX store of
+    every prefix row)."""
+    k, v = _prefix_cache(host, s, rows)
+    return oracle.mx_kv_store(k), oracle.mx_kv_store(v)
+
+
+def _dequant_mx(cache, b, t):
+    """The values of an MxKvCache at sequence b, slot t: [Hkv, D] float64."""
+    from oracle import attention as oattn
+    return oattn.dequant_mx_rows(cache.q[b, :, t].cpu().numpy(), cache.e[b, :, t].cpu().numpy())
+
+
 def _ulp_close(got, want):
     ulp = np.ldexp(1.0, np.frexp(np.maximum(np.abs(want), 1e-30))[1] - 8)
     return bool(np.all(np.abs(got - want) <= ulp))
 
 
-def _run_step(host):
+def _clone(c):
+    return ops.MxKvCache(c.q.clone(), c.e.clone()) if isinstance(c, ops.MxKvCache) else c.clone()
+
+
+def _run_step(host, mx=False):
     c = host.cfg
     dm = model.device_model(host)
-    kv, ks, vs = model.device_kv(host)
-    k0 = [k.clone() for k in ks]
-    v0 = [v.clone() for v in vs]
+    kv, ks, vs = model.device_kv(host, mx=mx)
+    k0 = [_clone(k) for k in ks]
+    v0 = [_clone(v) for v in vs]
     B, H, C, V = c.batch, c.hidden, c.n_codebooks, c.codebook_size
     slow_taps = torch.empty((2 * c.n_slow_layers + 1, B, H), dtype=torch.bfloat16, device="cuda")
     fast_taps = torch.empty((C - 1, 2 * c.n_fast_layers + 1, B, H), dtype=torch.bfloat16, device="cuda")
@@ -131,21 +152,67 @@ def test_small_model_every_layer_teacher_forced(batch, n_heads):
             assert torch.equal(vg[b][:, keep].view(torch.int16), g["v0"][s][b][:, keep].view(torch.int16))
 
 
+def test_small_model_mxfp8_kv_teacher_forced():
+    """The step with MXFP8 slow-layer caches: every half-block against the
+    oracle whose slow caches hold the MX store of their rows (prefix and
+    appended row); the appended rows dequantise to the oracle's bf16 K/V
+    within the MX rounding: the OCP rule scales a group's largest magnitude
+    into [256, 512) and e4m3 saturates at 448, so an element can lose up to
+    1/8 of the group's largest magnitude (half an e4m3 step, 1/16, below
+    that); no other cache byte changes."""
+    need_gpu()
+    host = model.HostModel(model.scaled(model.TINY, batch=24, n_heads=8))
+    c = host.cfg
+    g = _run_step(host, mx=True)
+    C, F, L = c.n_codebooks, c.n_fast_layers, c.n_slow_layers
+    om = {"slow": [_oracle_block(d) for d in host.slow], "fast": [_oracle_block(d) for d in host.fast],
+          "slow_norm": f32(host.slow_norm).astype(np.float64), "fast_norm": f32(host.fast_norm).astype(np.float64),
+          "embed": [f32(t) for t in host.embed], "heads": [oracle.dequant_weight(f32(h))[2] for h in host.heads],
+          "n_heads": c.n_heads, "n_kv_heads": c.n_kv_heads, "head_dim": c.head_dim, "eps": c.rms_eps}
+    rows = list(range(c.batch))
+    caches = [_prefix_cache_mx(host, l % c.kv_sets, rows) for l in range(L)]
+    force = {"slow_x": list(g["slow"]), "codes": g["codes"], "fast_x": [list(g["fast"][p]) for p in range(C - 1)]}
+    r = oracle.dual_ar_step(om, host.prev_codes, [k for k, _ in caches], [v for _, v in caches], host.kv_len,
+                            force=force, slow_kv_store=oracle.mx_kv_store)
+    for i in range(1, 2 * L + 1):
+        e = max_rel_err(g["slow"][i], r["slow_x"][i])
+        log(f"  slow layer {(i - 1) // 2} {'attention' if i % 2 else 'mlp'} half: {e:.3e}")
+        assert e <= TOL_FP8_PATH
+    for cb in range(C):
+        assert max_rel_err(g["logits"][cb], r["logits"][cb]) <= TOL_FP8_PATH
+    for p in range(C - 1):
+        for i in range(1, 2 * F + 1):
+            assert max_rel_err(g["fast"][p][i], r["fast_x"][p][i]) <= TOL_FP8_PATH, (p, i)
+    for s in range(c.kv_sets):
+        last = max(l for l in range(L) if l % c.kv_sets == s)
+        kk, vv = r["slow_kv"][last]
+        kg, vg, k0, v0 = g["ks"][s], g["vs"][s], g["k0"][s], g["v0"][s]
+        for b in rows:
+            t = int(host.kv_len[b]) - 1
+            for got, want in ((_dequant_mx(kg, b, t), kk[b]), (_dequant_mx(vg, b, t), vv[b])):
+                assert max_rel_err(got, want) <= MX_KV_TOL
+            keep = torch.arange(c.cap, device="cuda") != t
+            for now, before in ((kg, k0), (vg, v0)):
+                assert torch.equal(now.q[b][:, keep], before.q[b][:, keep])
+                assert torch.equal(now.e[b][:, keep], before.e[b][:, keep])
+
+
 @pytest.mark.timeout(900)
-def test_full_model_sampled_layers_teacher_forced():
+@pytest.mark.parametrize("mx", [False, True], ids=["bf16_kv", "mxfp8_kv"])
+def test_full_model_sampled_layers_teacher_forced(mx):
     need_gpu()
     host = model.HostModel(model.FULL)
     c = host.cfg
-    g = _run_step(host)
+    g = _run_step(host, mx=mx)
     C, F, L = c.n_codebooks, c.n_fast_layers, c.n_slow_layers
     rows = sorted({0, 13, 29, 47, c.batch - 1, int(np.argmax(host.kv_len)), int(np.argmin(host.kv_len))})
     log(f"  sampled rows {rows}, kv_len {[int(host.kv_len[b]) for b in rows]}")
     D = c.head_dim
     for l in (0, 17, L - 1):
         p = _oracle_block(host.slow[l])
-        k, v = _prefix_cache(host, l % c.kv_sets, rows)
+        k, v = (_prefix_cache_mx if mx else _prefix_cache)(host, l % c.kv_sets, rows)
         mid, it = oracle.attention_block(g["slow"][2 * l][rows], p, k, v, host.kv_len[rows], c.n_heads,
-                                         c.n_kv_heads, D, c.rms_eps)
+                                         c.n_kv_heads, D, c.rms_eps, oracle.mx_kv_store if mx else None)
         out, _ = oracle.mlp_block(g["slow"][2 * l + 1][rows], p, c.rms_eps)
         e1 = max_rel_err(g["slow"][2 * l + 1][rows], mid)
         e2 = max_rel_err(g["slow"][2 * l + 2][rows], out)
@@ -155,8 +222,12 @@ def test_full_model_sampled_layers_teacher_forced():
             s = l % c.kv_sets
             for i, b in enumerate(rows):
                 t = int(host.kv_len[b]) - 1
-                assert max_rel_err(_np(g["ks"][s][b, :, t]), it["k"][i]) <= TOL_FP8_PATH
-                assert max_rel_err(_np(g["vs"][s][b, :, t]), it["v"][i]) <= TOL_FP8_PATH
+                if mx:
+                    assert max_rel_err(_dequant_mx(g["ks"][s], b, t), it["k"][i]) <= MX_KV_TOL
+                    assert max_rel_err(_dequant_mx(g["vs"][s], b, t), it["v"][i]) <= MX_KV_TOL
+                else:
+                    assert max_rel_err(_np(g["ks"][s][b, :, t]), it["k"][i]) <= TOL_FP8_PATH
+                    assert max_rel_err(_np(g["vs"][s][b, :, t]), it["v"][i]) <= TOL_FP8_PATH
     heads = [oracle.dequant_weight(f32(h))[2] for h in host.heads]
     h = oracle.rmsnorm(g["slow"][2 * L][rows], f32(host.slow_norm))
     lg, _ = oracle.greedy_code(h, heads[0])

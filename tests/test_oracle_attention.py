@@ -142,6 +142,32 @@ def test_mxkv_kv_len_one_returns_dequantised_first_value():
         assert np.array_equal(out[:, h], vval[:, 0, 0])
 
 
+def test_mx_kv_store_is_identity_on_representable_rows():
+    """A row whose 32-groups are MX-representable is stored as it is."""
+    g = np.random.default_rng(13)
+    vals, _, _ = _mx_representable(g, (3, 2, 128))
+    assert np.array_equal(attention.mx_kv_store(vals), vals)
+    assert np.array_equal(attention.mx_kv_store(np.zeros((2, 64))), np.zeros((2, 64)))
+
+
+def test_mx_kv_store_brute_force_nearest_grid_point():
+    """Each stored value is the e4m3 grid point (times the group's power of
+    two 2^(floor(log2 amax) - 8)) nearest to the input, found by a search
+    over all 254 finite codes; inputs are drawn off the rounding midpoints."""
+    g = np.random.default_rng(14)
+    rows = g.standard_normal((4, 64)) * np.ldexp(1.0, g.integers(-6, 7, size=(4, 1)))
+    got = attention.mx_kv_store(rows)
+    grid = fp8.e4m3_decode(np.array([c for c in range(256) if (c & 0x7F) != 0x7F], np.uint8))
+    for r in range(rows.shape[0]):
+        for k in range(0, 64, 32):
+            grp = rows[r, k:k + 32]
+            X = np.ldexp(1.0, int(np.floor(np.log2(np.abs(grp).max()))) - 8)
+            for i, x in enumerate(grp):
+                d = np.abs(grid * X - x)
+                assert np.sort(d)[1] - d.min() > 1e-12 * abs(x)   # not a tie
+                assert got[r, k + i] == grid[np.argmin(d)] * X
+
+
 def _scatter_pages(g, cache, P, spare=3):
     """A pool [pages, Hkv, P, D] holding a contiguous cache [B, Hkv, cap, D]
     (cap a multiple of P) on shuffled pages, plus `spare` NaN pages no
