@@ -224,12 +224,14 @@ def kernel_table(per, steps, M, mode, kv_len=None, B=None):
     return out
 
 
-def step_launch_plan(cfg, kv_len):
+def step_launch_plan(cfg, kv_len, mx=False):
     """(library kernel name, algorithmic bytes) of every launch of one
     dual_ar_decode_step, in launch order.  Algorithmic bytes are what the
     operation must move: weights and their scales, the activations it reads
     and writes, the K/V prefix; workspace traffic of split partials and the
-    L2-resident re-reads of a row for its RMS are not counted."""
+    L2-resident re-reads of a row for its RMS are not counted.
+    mx: the slow layers' caches are MXFP8 (D e4m3 bytes and D/32 exponents
+    per position and KV head, read by attn_split_mx and appended as such)."""
     c = cfg
     B, H, I, V, C = c.batch, c.hidden, c.inter, c.codebook_size, c.n_codebooks
     A, NQKV, KVD = c.n_heads * c.head_dim, (c.n_heads + 2 * c.n_kv_heads) * c.head_dim, c.n_kv_heads * c.head_dim
@@ -255,10 +257,15 @@ def step_launch_plan(cfg, kv_len):
     def finish(with_residual):
         return ("row_finish", B * H * 2 + (B * H * 2 if with_residual else 0) + H * 2 + B * H + asc(H))
 
-    def block(kv_bytes, single):
+    # bytes a K/V row of one KV head takes in a cache: bf16, or e4m3 + UE8M0
+    row_mx = c.head_dim + c.head_dim // 32
+
+    def block(kv_bytes, single, mx_kv=False):
         attn = ([("attn_single", kv_bytes + 2 * B * A * 2 + 4 * B + oq)] if single else
-                [("attn_split", kv_bytes + B * A * 2 + 4 * B), ("attn_merge", B * A * 2 + 4 * B + oq)])
-        return [("qlinear", NQKV * H + ws(NQKV, H) + B * H + asc(H) + B * NQKV * 2)] + attn + (
+                [("attn_split_mx" if mx_kv else "attn_split", kv_bytes + B * A * 2 + 4 * B),
+                 ("attn_merge", B * A * 2 + 4 * B + oq)])
+        qkv_out = B * A * 2 + (B * 2 * c.n_kv_heads * row_mx if mx_kv else B * 2 * KVD * 2)
+        return [("qlinear", NQKV * H + ws(NQKV, H) + B * H + asc(H) + qkv_out)] + attn + (
                 [] if fused else [act_quant("ql_act_quant", A, False)]) + [
                 ("qlinear", H * A + ws(H, A) + B * A + asc(A)),
                 finish(True),
@@ -276,11 +283,12 @@ def step_launch_plan(cfg, kv_len):
     # as the argmax of the previous head's logits
     operand = B * H * 2 + H * 2 + B * H + asc(H)
     out = [("embed_finish", B * C * H * 2 + 4 * B * C + (C - 1) * B * 4 + operand)]
-    slow_kv = int(np.sum(kv_len, dtype=np.int64)) * KVD * 2 * 2
+    slow_kv = int(np.sum(kv_len, dtype=np.int64)) * (c.n_kv_heads * row_mx * 2 if mx else KVD * 2 * 2)
     # the slow AR's prefixes are split over chunks and merged; the fast AR's
-    # few-slot caches are one chunk, written by the split kernel itself
+    # few-slot caches (bf16 either way) are one chunk, written by the split
+    # kernel itself
     for _ in range(c.n_slow_layers):
-        out += block(slow_kv, False)
+        out += block(slow_kv, False, mx)
     out += head()
     for p in range(C - 1):
         out.append(("embed_finish", B * V * 4 + 4 * B + B * H * 2 * (2 if p == 0 else 1) + operand))
@@ -609,6 +617,33 @@ def step_kernel_table(recs, plan, steps):
     return out
 
 
+def mxfp8_kv_step(torch, model, host, dm, prev, workspace, args):
+    """The same step with the slow layers' caches in MXFP8 (the pages'
+    MXFP8 decode attention; the K/V append quantises the new rows): ms per
+    step, tokens/s and the per-kernel table.  A second configuration, not
+    the headline: the caches hold the same prefixes quantised in 1x32 groups."""
+    from fp8_transformer_step_amd import ops
+    cfg = host.cfg
+    log("bench: the step over MXFP8 KV caches")
+    kv, _, _ = model.device_kv(host, mx=True)
+    err = torch.zeros(1, dtype=torch.int32, device="cuda")
+    ms, wall, recs, per_step = time_step(torch, ops, dm, kv, prev, args.steps, args.warmup, workspace, err)
+    if int(err.item()) != 0:
+        raise SystemExit(f"device error flag {int(err.item())} (MXFP8 KV step)")
+    plan = step_launch_plan(cfg, host.kv_len, mx=True)
+    ktab = step_kernel_table(recs, plan, args.steps)
+    step_bytes = int(sum(v["bytes_per_step"] for v in ktab.values()))
+    log(f"step (MXFP8 KV) {ms:.3f} ms ({cfg.batch / (ms * 1e-3):.0f} tokens/s); attn_split_mx "
+        f"{ktab['attn_split_mx']['us_per_launch']:.1f} us per layer")
+    del kv
+    torch.cuda.empty_cache()
+    return {"ms_per_step": ms, "tokens/s": cfg.batch / (ms * 1e-3), "wall_ms_per_step": wall,
+            "ms_per_step_dist": percentiles(per_step), "launches_per_step": len(plan),
+            "step_hbm": {"bytes_per_step": step_bytes, "GB/s": step_bytes / (ms * 1e-3) / 1e9,
+                         "frac": step_bytes / (ms * 1e-3) / 1e9 / PEAK_HBM_GBS},
+            "kernels": ktab}
+
+
 def stream_ceiling(torch, ops):
     """What one launch can stream: fp8s_stream_read over the byte counts of
     the MLP (all weights, gate/up, down), the QKV projection and one attention
@@ -861,7 +896,10 @@ def main():
     }
     if not args.no_sweep:
         result["step_buckets"] = bucket_curve(torch, dm, kv, B)
-    del dm, kv, workspace, prev
+    del kv
+    torch.cuda.empty_cache()
+    result["step_mxfp8_kv"] = mxfp8_kv_step(torch, model, host, dm, prev, workspace, args)
+    del dm, workspace, prev
     torch.cuda.empty_cache()
 
     if not args.no_sweep:
