@@ -117,18 +117,19 @@ def test_projection_output_and_workspace(out_dtype, M, N, K):
         assert _bits_equal(y, ref)
 
 
-def test_decode_step_outputs_and_workspace():
+@pytest.mark.parametrize("mx", [False, True], ids=["bf16_kv", "mxfp8_kv"])
+def test_decode_step_outputs_and_workspace(mx):
     """The step's codes, its taps and its workspace, on the small model at
-    batch 24 (two 16-row tiles)."""
+    batch 24 (two 16-row tiles), with bf16 and MXFP8 slow-layer caches."""
     need_gpu()
     host = model.HostModel(model.scaled(model.TINY, batch=24, n_heads=8))
     c = host.cfg
     B, H, C, V = c.batch, c.hidden, c.n_codebooks, c.codebook_size
     dm = model.device_model(host)
     prev = torch.from_numpy(host.prev_codes).cuda()
-    kv, _, _ = model.device_kv(host)
+    kv, _, _ = model.device_kv(host, mx=mx)
     ref = ops.dual_ar_decode_step(dm, kv, prev)
-    kv, _, _ = model.device_kv(host)           # fresh caches: the step appends K/V
+    kv, _, _ = model.device_kv(host, mx=mx)    # fresh caches: the step appends K/V
     cbuf, codes = _guarded((B, C), torch.int32)
     sbuf, slow = _guarded((2 * c.n_slow_layers + 1, B, H), torch.bfloat16)
     fbuf, fast = _guarded((C - 1, 2 * c.n_fast_layers + 1, B, H), torch.bfloat16)
