@@ -13,21 +13,33 @@
 // workgroup hand-off on the critical path (a hand-off queues behind the
 // weight stream for microseconds).  So the MLP is a short chain of plain
 // streaming kernels on one stream:
-//   M <= 16: gu_small  -> hq -> down_small
-//   M >  16: xq -> gu  -> hq -> down
-//   xq        quantise x once (1x128 fp32 or 1x32 UE8M0 groups) into a buffer
-//             laid out in MFMA operand order;
+//   M <= 4 : gu_small -> down_small<fused>
+//   M <= 16: xq -> gu<1>  -> hq -> down_small
+//   M >  16: xq -> gu<MT> -> hq -> down
+//   (xq is skipped when the caller hands over x already quantised, and the
+//   M <= 16 chain runs at M <= 4 when an RMSNorm sits in front)
+//   xq        quantise x once (1x128 fp32 or 1x32 UE8M0 groups; codes and
+//             scales in one launch) into a buffer in MFMA operand order;
 //   gu_small  one workgroup per 16 columns of gate AND up (608 items for
 //             Qwen3-4B, all resident at once): each wave quantises its quarter
 //             of x in registers (activation quantisation fused into this
 //             launch), streams its 10 weight fragments straight into MFMA
 //             operand registers and accumulates; writes g and u in fp32;
-//   gu        the same with the weight slice staged in LDS by direct-to-LDS
-//             loads and shared by waves that split the M tiles; activations
-//             through a register ring from the xq buffer;
+//   down_small<fused>  forms h = silu(g) * u, its group amax and e4m3
+//             operand in its prologue (SwiGLU fused into the down GEMM's
+//             activation quantisation, inside the down GEMM launch);
+//   gu        the weight slice staged in LDS by direct-to-LDS loads and shared
+//             by waves that split the M tiles; activations through a register
+//             ring from the xq buffer; writes g and u in fp32;
 //   hq        h = silu(g) * u and its quantisation for the down projection
-//             (the SwiGLU "prologue" of the down GEMM's activation
-//             quantisation): e4m3 + scales in MFMA operand order;
+//             in one launch (the SwiGLU prologue of the down GEMM's activation
+//             quantisation; h never exists in bf16): e4m3 + scales in MFMA
+//             operand order.  Each down item needs all M rows of a long K
+//             range, so quantising h inside the down GEMM would re-read g and
+//             u (8 bytes per element) once per column tile, and forming the
+//             operand in the gate/up epilogue needs a hand-off between the
+//             tiles of each quantisation group that costs more than this
+//             launch (both measured);
 //   down_*    split-K tiles of the down projection (registers for M <= 16,
 //             LDS-staged otherwise); each split writes an fp32 partial and the
 //             last split of a tile to finish sums the partials in split order
@@ -82,6 +94,7 @@ struct MlpArgs {
     const uint16_t* res;           // optional residual [M, H] added to y
     bool defer;                    // leave the down projection's split partials for the next kernel
     uint8_t* xtap;                 // debug tap: gu_small's x operand (fragments, then scales at xtap_s)
+    float* htap;                   // debug tap: h = silu(g) * u as hq forms it, fp32 [M][I]
     uint8_t* xtap_s;
 };
 
@@ -122,6 +135,11 @@ __global__ __launch_bounds__(256) void hq_kernel(MlpArgs a) {
         }
 #pragma unroll
         for (int i = 0; i < 8; ++i) f[i] = g[i] * __builtin_amdgcn_rcpf(1.0f + __expf(-g[i])) * u[i];
+        if (a.htap) {
+            float4* t = reinterpret_cast<float4*>(a.htap + (int64_t)m * a.I + kb * 128 + 8 * j);
+            t[0] = make_float4(f[0], f[1], f[2], f[3]);
+            t[1] = make_float4(f[4], f[5], f[6], f[7]);
+        }
     }
     quant_chunk<MODE>(f, a.qh + frag_off(mt, kb, a.KBI), scale_slot<MODE>(a.sh, mt, kb, a.KBI), row, j);
 }
@@ -669,6 +687,14 @@ int swiglu_mlp_fp8_ex(const uint16_t* x, int64_t M, int64_t H, int64_t I, int mo
     FP8S_REQUIRE(!tap || tap_bytes >= tap_frag + tap_sc, FP8S_EINVAL,
                  "swiglu_mlp_fp8: debug tap of %zu bytes < %zu", tap_bytes, tap_frag + tap_sc);
     const bool in_gu = M <= kTinyM && !norm_w && !prequant;
+    // debug tap of h (tests): h in fp32 as hq forms it, then hq's operand of h
+    size_t htap_bytes = 0;
+    uint8_t* htap = in_gu ? nullptr : static_cast<uint8_t*>(debug_tap(FP8S_TAP_MLP_H, &htap_bytes));
+    const size_t htap_h = (size_t)M * I * 4, htap_frag = (size_t)((M + 15) / 16) * p.KBI * kFrag,
+                 htap_sc = (size_t)((M + 15) / 16) * p.KBI * 64;
+    FP8S_REQUIRE(!htap || htap_bytes >= htap_h + htap_frag + htap_sc, FP8S_EINVAL,
+                 "swiglu_mlp_fp8: debug tap of %zu bytes < %zu", htap_bytes, htap_h + htap_frag + htap_sc);
+    a.htap = reinterpret_cast<float*>(htap);
     a.xtap = tap && in_gu ? tap : nullptr;
     a.xtap_s = tap && in_gu ? tap + tap_frag : nullptr;
     if (mode == FP8S_MLP_BSGEMM)
@@ -683,6 +709,12 @@ int swiglu_mlp_fp8_ex(const uint16_t* x, int64_t M, int64_t H, int64_t I, int mo
     if (tap && !in_gu) {
         FP8S_REQUIRE(hipMemcpyAsync(tap, a.qx, tap_frag, hipMemcpyDeviceToDevice, st) == hipSuccess &&
                          hipMemcpyAsync(tap + tap_frag, a.sx, tap_sc, hipMemcpyDeviceToDevice, st) == hipSuccess,
+                     FP8S_EHIP, "swiglu_mlp_fp8: debug tap copy failed");
+    }
+    if (htap) {
+        FP8S_REQUIRE(hipMemcpyAsync(htap + htap_h, a.qh, htap_frag, hipMemcpyDeviceToDevice, st) == hipSuccess &&
+                         hipMemcpyAsync(htap + htap_h + htap_frag, a.sh, htap_sc, hipMemcpyDeviceToDevice, st) ==
+                             hipSuccess,
                      FP8S_EHIP, "swiglu_mlp_fp8: debug tap copy failed");
     }
     return check_launch("swiglu_mlp_fp8");

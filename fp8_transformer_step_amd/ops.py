@@ -17,7 +17,7 @@ from . import _lib
 Q_ACT_1x128, Q_WGT_128x128, Q_MX_1x32 = 0, 1, 2
 MLP_BSGEMM, MLP_MXFP8 = 0, 1
 DEV_KVLEN_RANGE, DEV_CODE_RANGE, DEV_PAGE_RANGE = 1, 3, 4
-TAP_MLP_X, TAP_STEP_SLOW = 1, 2
+TAP_MLP_X, TAP_STEP_SLOW, TAP_MLP_H = 1, 2, 3
 OUT_BF16, OUT_F32 = 0, 1
 
 
@@ -718,7 +718,7 @@ def profile_stop():
 
 
 def set_debug_tap(kind, buf):
-    """Point debug tap `kind` (TAP_MLP_X, TAP_STEP_SLOW) at a uint8 device
+    """Point debug tap `kind` (TAP_MLP_X, TAP_STEP_SLOW, TAP_MLP_H) at a uint8 device
     tensor, or switch it off with None (see fp8s_set_debug_tap)."""
     if buf is None:
         _lib.check(_lib.load().fp8s_set_debug_tap(int(kind), None, 0))

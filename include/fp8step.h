@@ -80,6 +80,13 @@ enum fp8s_device_error {
  *   FP8S_TAP_MLP_X          swiglu_mlp_fp8: the operand of x [M, hidden] the
  *                           gate/up GEMM consumes (quantised inside that
  *                           GEMM for M <= 4, by the x kernel otherwise).
+ *   FP8S_TAP_MLP_H          swiglu_mlp_fp8 at M > 4: h = silu(g) u fp32
+ *                           [M, inter] row-major as the SwiGLU-quantise
+ *                           kernel formed it from the gate/up GEMM's g and
+ *                           u, then the down GEMM's operand of h [M, inter]
+ *                           as that kernel quantised it.  Not written at
+ *                           M <= 4, where the down GEMM forms h in its own
+ *                           prologue.
  *   FP8S_TAP_STEP_SLOW      dual_ar_decode_step, for each slow layer l in
  *                           turn (n_slow_layers equal parts), back to back:
  *                           the attention output ao bf16 [B, Hq*D]; the
@@ -91,7 +98,8 @@ enum fp8s_device_error {
  */
 enum fp8s_debug_tap {
     FP8S_TAP_MLP_X = 1,
-    FP8S_TAP_STEP_SLOW = 2
+    FP8S_TAP_STEP_SLOW = 2,
+    FP8S_TAP_MLP_H = 3
 };
 FP8S_API int fp8s_set_debug_tap(int kind, void* buf, size_t bytes);
 

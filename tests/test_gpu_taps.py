@@ -4,6 +4,8 @@ quantisation of the GPU's own bf16 input of that step, bit for bit.
 
   * swiglu_mlp_fp8's x operand: quantised inside the gate/up GEMM (M <= 4)
     or by the x kernel (M > 4), bsgemm and MXFP8;
+  * swiglu_mlp_fp8's h operand at M > 4: h = silu(g) u and its quantisation,
+    formed in one launch from the gate/up GEMM's g and u;
   * the decode step, every slow layer: the attention kernel's quantised
     output (operand of the output projection) against its bf16 output, and
     the row finisher's quantised MLP input against its RMSNorm rows.  With
@@ -78,6 +80,45 @@ def test_mlp_x_operand_tap(mode, M):
     finally:
         ops.set_debug_tap(ops.TAP_MLP_X, None)
     _check_operand(tap.cpu().numpy(), f32(xb), mode, "x operand")
+
+
+@pytest.mark.parametrize("mode", [ops.MLP_BSGEMM, ops.MLP_MXFP8])
+@pytest.mark.parametrize("M", [5, 16, 29, 37, 64, 128])
+def test_mlp_h_operand_tap(mode, M):
+    """The SwiGLU-quantise launch: h = silu(g) u as it formed it (against the
+    oracle's h from the same x operand), and the down GEMM's operand of h
+    bit-exact with the oracle's activation quantisation of that h.  M = 5
+    and 16 run the one-tile gate/up GEMM, 29 two tiles, 37 and 64 four, 128
+    eight; the 96 gate/up tiles past the first 512 are split over K and their
+    quarters summed in that launch."""
+    need_gpu()
+    H, I = 2560, 9728
+    wl = inputs.W_MXFP8 if mode == ops.MLP_MXFP8 else inputs.W_BSGEMM
+    wbits = inputs.mlp_weights(wl, H, I)
+    w = [ops.quantize_weight(to_dev_bf16(wb), mode) for wb in wbits]
+    xb = inputs.mlp_activations(wl, M, H, extra=700 + M)
+    nh = M * I * 4
+    tap = torch.zeros(nh + _operand_bytes(M, I), dtype=torch.uint8, device="cuda")
+    log(f"h operand tap mode={mode} M={M}")
+    ops.set_debug_tap(ops.TAP_MLP_H, tap)
+    try:
+        ops.swiglu_mlp_fp8(to_dev_bf16(xb), *w, mode)
+        torch.cuda.synchronize()
+    finally:
+        ops.set_debug_tap(ops.TAP_MLP_H, None)
+    t = tap.cpu().numpy()
+    h = np.ascontiguousarray(t[:nh]).view(np.float32).reshape(M, I)
+    assert np.all(np.isfinite(h))
+    _check_operand(t[nh:], h, mode, "h operand")
+    if mode == ops.MLP_MXFP8:
+        deq = [fp8.dequant_mx_1x32(*fp8.quant_mx_1x32(f32(b))) for b in wbits]
+    else:
+        deq = [fp8.dequant_block_fp32(*fp8.quant_weight_128x128(f32(b)), 128, 128) for b in wbits]
+    ref = omlp.swiglu_mlp(f32(xb), *deq, mode)["h"].astype(np.float64)
+    # fp32 accumulation of 2560 products and the fp32 exp / reciprocal against
+    # float64: 1e-3 of max |h| (measured up to 1.4e-4 with the MX outliers),
+    # far below the 2^-4 relative step of an e4m3 code
+    assert max_rel_err(h.astype(np.float64), ref) <= 1e-3
 
 
 def test_tap_too_small_is_refused():
