@@ -686,14 +686,16 @@ static int attn_launch(const AttnArgs& a, int D, int G, hipStream_t st) {
 
 // Workgroups of a balanced-split kernel that all CUs hold at once, per KV
 // head (queried once per device; at most kBalSlotsMax in all).
-template <typename K>
-static int bal_slots(K kernel, int Hkv) {
+// (One cache per kernel: the kernels share a function type, so the cache is
+// keyed by the kernel itself as a template argument.)
+template <auto KERNEL>
+static int bal_slots(int Hkv) {
     static int slots[64];
     int dev = 0;
     if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return std::max(1, 1024 / Hkv);
     if (!slots[dev]) {
         int per_cu = 0, cus = 0;
-        if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, kernel, 256, 0) != hipSuccess ||
+        if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, KERNEL, 256, 0) != hipSuccess ||
             hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || per_cu < 1 ||
             cus < 1)
             return std::max(1, 1024 / Hkv);
@@ -713,11 +715,11 @@ static void launch_split_t(dim3 grid, hipStream_t st, const AttnArgs& a) {
     if (a.bal) {
         AttnArgs b = a;
         if (MX) {
-            b.bal_slots = bal_slots(attn_bal_mx_kernel<D, G, PAGED>, a.Hkv);
+            b.bal_slots = bal_slots<attn_bal_mx_kernel<D, G, PAGED>>(a.Hkv);
             FP8S_LAUNCH(names[0], (attn_bal_mx_kernel<D, G, PAGED>), dim3((unsigned)(b.bal_slots * a.Hkv)),
                         dim3(256), 0, st, b);
         } else {
-            b.bal_slots = bal_slots(attn_bal_kernel<D, G, PAGED>, a.Hkv);
+            b.bal_slots = bal_slots<attn_bal_kernel<D, G, PAGED>>(a.Hkv);
             FP8S_LAUNCH(names[0], (attn_bal_kernel<D, G, PAGED>), dim3((unsigned)(b.bal_slots * a.Hkv)),
                         dim3(256), 0, st, b);
         }
