@@ -161,14 +161,19 @@ class Workload:
         fn(st["q"], st["k"], st["v"], st["kv"], st["hint"], out=st["o"], workspace=st["aws"], err=self.err)
 
 
-def time_parts(torch, ops, wl, parts, steps, warmup):
+def time_parts(torch, ops, wl, parts, steps, warmup, graph=False):
     """Two timed regions of `steps` steps each (every step calls every part
     once on a rotating set), bracketed by synchronisation and HIP events:
       1. clean: gives ms per step (the headline);
       2. per kernel: the library records a HIP event pair around every kernel
          it launches, on the launch stream (the events add small gaps between
          launches, so this pass is not used for the headline).
-    Returns (ms per step, wall ms per step, {kernel: [ms, ...]})."""
+    graph: a third region replays the `steps` steps captured once into a HIP
+    graph (the same kernels on the same sets, without the host's launch gaps:
+    a call of a few tens of microseconds can otherwise wait for the host to
+    enqueue it).
+    Returns (ms per step, wall ms per step, {kernel: [ms, ...]}[, graph ms
+    per step])."""
     n = len(wl.sets)
     for i in range(warmup):
         for p in parts:
@@ -194,7 +199,28 @@ def time_parts(torch, ops, wl, parts, steps, warmup):
     per = {}
     for name, ms in recs:
         per.setdefault(name, []).append(ms)
-    return ms_step, wall, per
+    if not graph:
+        return ms_step, wall, per
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        for p in parts:
+            p(0)
+    torch.cuda.current_stream().wait_stream(side)
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        for i in range(steps):
+            for p in parts:
+                p(i % n)
+    g.replay()
+    torch.cuda.synchronize()
+    t0.record()
+    g.replay()
+    t1.record()
+    torch.cuda.synchronize()
+    ms_graph = t0.elapsed_time(t1) / steps
+    del g
+    return ms_step, wall, per, ms_graph
 
 
 def pmc_traffic(kernel):
@@ -245,7 +271,10 @@ def step_launch_plan(cfg, kv_len, mx=False):
     def act_quant(name, K, norm):
         return (name, B * K * 2 + (K * 2 if norm else 0) + B * K + asc(K))
 
-    down = "mlp_down_small" if B <= 16 else "mlp_down"
+    # the MLP: M <= 16 forms h in the down GEMM's prologue from g and u,
+    # M > 16 quantises it in a launch of its own
+    mlp_tail = ([("mlp_down_small_fused", H * I + ws(H, I) + 2 * B * I * 4)] if B <= 16 else
+                [("mlp_hq", 2 * B * I * 4 + B * I + asc(I)), ("mlp_down", H * I + ws(H, I) + B * I + asc(I))])
 
     # the attention quantises its output into the output projection's operand
     # itself when each KV head's query group spans whole 128-column groups
@@ -269,9 +298,7 @@ def step_launch_plan(cfg, kv_len, mx=False):
                 [] if fused else [act_quant("ql_act_quant", A, False)]) + [
                 ("qlinear", H * A + ws(H, A) + B * A + asc(A)),
                 finish(True),
-                ("mlp_gu", 2 * I * H + 2 * ws(I, H) + B * H + asc(H) + 2 * B * I * 4),
-                ("mlp_hq", 2 * B * I * 4 + B * I + asc(I)),
-                (down, H * I + ws(H, I) + B * I + asc(I)),
+                ("mlp_gu", 2 * I * H + 2 * ws(I, H) + B * H + asc(H) + 2 * B * I * 4)] + mlp_tail + [
                 finish(True)]
 
     def head():
@@ -551,9 +578,10 @@ def mlp_sweep(torch, ops, inputs, n_sets):
         sweep[key] = {}
         for M in (1, 8, 32, 64, 128):
             w = Workload(torch, ops, 1, M, mode, n_sets, kv_len, with_attn=False, packed=packed)
-            t, _, per = time_parts(torch, ops, w, [w.mlp], 20, 5)
+            te, _, per, t = time_parts(torch, ops, w, [w.mlp], 20, 5, graph=True)
             gb = mlp_bytes(M, mode) / (t * 1e-3) / 1e9
-            sweep[key][M] = {"us": t * 1e3, "tokens/s": M / (t * 1e-3), "GB/s": gb, "frac": gb / PEAK_HBM_GBS,
+            sweep[key][M] = {"us": t * 1e3, "us_eager": te * 1e3, "tokens/s": M / (t * 1e-3), "GB/s": gb,
+                             "frac": gb / PEAK_HBM_GBS,
                              "rotated_bytes": n_sets * mlp_bytes(M, mode), "kernels": kernel_table(per, 20, M, mode)}
             log(f"{key} M={M}: {t * 1e3:.1f} us {gb:.0f} GB/s  " +
                 " ".join(f"{k}={v['us']:.1f}" for k, v in sweep[key][M]["kernels"].items()))
@@ -915,12 +943,12 @@ def main():
             n_sets = max(2, min(1024, -(-ROTATE_BYTES // attn_bytes(kv, Bs, mx))))
             w = Workload(torch, ops, Bs, 1, 0, n_sets, kv, with_mlp=False, mx_kv=mx, page=page,
                          cap=CAP if hi > 400 else 512)
-            t, _, per = time_parts(torch, ops, w, [w.attn], 20, 5)
+            te, _, per, t = time_parts(torch, ops, w, [w.attn], 20, 5, graph=True)
             gb = attn_bytes(kv, Bs, mx) / (t * 1e-3) / 1e9
             key = f"B={Bs},kv=U[{lo},{hi}]" + (f",page={page},{'mxfp8' if mx else 'bf16'}" if page else "")
             sweep["attn_paged" if page else "attn_mxkv" if mx else "attn"][key] = {
-                "us": t * 1e3, "tokens/s": Bs / (t * 1e-3), "GB/s": gb, "frac": gb / PEAK_HBM_GBS,
-                "rotated_bytes": n_sets * attn_bytes(kv, Bs, mx),
+                "us": t * 1e3, "us_eager": te * 1e3, "tokens/s": Bs / (t * 1e-3), "GB/s": gb,
+                "frac": gb / PEAK_HBM_GBS, "rotated_bytes": n_sets * attn_bytes(kv, Bs, mx),
                 "kernels": kernel_table(per, 20, 1, 0, kv, Bs)}
             log(f"attn{' mxkv' if mx else ''}{f' paged {page}' if page else ''} B={Bs} kv {lo}..{hi}: "
                 f"{t * 1e3:.1f} us {gb:.0f} GB/s")

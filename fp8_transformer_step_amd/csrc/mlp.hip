@@ -13,8 +13,8 @@
 // workgroup hand-off on the critical path (a hand-off queues behind the
 // weight stream for microseconds).  So the MLP is a short chain of plain
 // streaming kernels on one stream:
-//   M <= 4 : gu_small -> down_small<fused>
-//   M <= 16: xq -> gu<1>  -> hq -> down_small
+//   M <= 4 : gu_small -> down_small
+//   M <= 16: xq -> gu<1>  -> down_small
 //   M >  16: xq -> gu<MT> -> hq -> down
 //   (xq is skipped when the caller hands over x already quantised, and the
 //   M <= 16 chain runs at M <= 4 when an RMSNorm sits in front)
@@ -25,21 +25,21 @@
 //             of x in registers (activation quantisation fused into this
 //             launch), streams its 10 weight fragments straight into MFMA
 //             operand registers and accumulates; writes g and u in fp32;
-//   down_small<fused>  forms h = silu(g) * u, its group amax and e4m3
-//             operand in its prologue (SwiGLU fused into the down GEMM's
+//   down_small forms h = silu(g) * u, its group amax and e4m3 operand in
+//             its prologue, up to 16 rows (SwiGLU fused into the down GEMM's
 //             activation quantisation, inside the down GEMM launch);
 //   gu        the weight slice staged in LDS by direct-to-LDS loads and shared
 //             by waves that split the M tiles; activations through a register
 //             ring from the xq buffer; writes g and u in fp32;
-//   hq        h = silu(g) * u and its quantisation for the down projection
-//             in one launch (the SwiGLU prologue of the down GEMM's activation
-//             quantisation; h never exists in bf16): e4m3 + scales in MFMA
-//             operand order.  Each down item needs all M rows of a long K
-//             range, so quantising h inside the down GEMM would re-read g and
-//             u (8 bytes per element) once per column tile, and forming the
-//             operand in the gate/up epilogue needs a hand-off between the
-//             tiles of each quantisation group that costs more than this
-//             launch (both measured);
+//   hq        (M > 16) h = silu(g) * u and its quantisation for the down
+//             projection in one launch (the SwiGLU prologue of the down GEMM's
+//             activation quantisation; h never exists in bf16): e4m3 + scales
+//             in MFMA operand order.  Each down item needs all M rows of a
+//             long K range, so at M > 16 quantising h inside the down GEMM
+//             would re-read g and u (8 bytes per element) once per column
+//             tile, and forming the operand in the gate/up epilogue needs a
+//             hand-off between the tiles of each quantisation group that costs
+//             more than this launch (both measured);
 //   down_*    split-K tiles of the down projection (registers for M <= 16,
 //             LDS-staged otherwise); each split writes an fp32 partial and the
 //             last split of a tile to finish sums the partials in split order
@@ -94,7 +94,8 @@ struct MlpArgs {
     const uint16_t* res;           // optional residual [M, H] added to y
     bool defer;                    // leave the down projection's split partials for the next kernel
     uint8_t* xtap;                 // debug tap: gu_small's x operand (fragments, then scales at xtap_s)
-    float* htap;                   // debug tap: h = silu(g) * u as hq forms it, fp32 [M][I]
+    float* htap;                   // debug tap: h = silu(g) * u as hq / down_small form it, fp32 [M][I]
+    uint8_t* htap_op;              //   and down_small's operand of h (M <= 16), after it
     uint8_t* xtap_s;
 };
 
@@ -362,15 +363,17 @@ __device__ __forceinline__ void finish_split(const MlpArgs& a, int nt, int s, in
 }
 
 // ---- down_small (M <= 16): 64 columns x 4 K blocks, one K block per wave -------
-// FUSED (M <= 4): the wave builds its operand from g and u itself: h =
-// silu(g) * u over the whole 128-column block, the block's 1x128 / 1x32 group
-// amax, e4m3 quantisation into LDS (the SwiGLU prologue of the down GEMM's
-// activation quantisation).  Otherwise it reads the operand made by hq.
-template <int MODE, bool FUSED>
+// The wave builds its operand from g and u itself: h = silu(g) * u over the
+// whole 128-column block, the block's 1x128 / 1x32 group amax, e4m3
+// quantisation into LDS (the SwiGLU prologue of the down GEMM's activation
+// quantisation, inside this launch).  Four rows per pass, up to four passes;
+// the g and u loads of every pass are issued before the weight fragments.
+constexpr int kSmallPasses = 4;
+template <int MODE>
 __global__ __launch_bounds__(256) void down_small_kernel(MlpArgs a) {
     constexpr int NB = kSmallDownCols / 16;
     __shared__ float red[3][NB][4][64];
-    __shared__ __attribute__((aligned(16))) uint8_t s_a[FUSED ? 4 : 1][kFrag];
+    __shared__ __attribute__((aligned(16))) uint8_t s_a[4][kFrag];
     __shared__ float s_sh[4][16];
     __shared__ uint8_t s_eh[4][64];
     __shared__ int s_prev;
@@ -380,16 +383,20 @@ __global__ __launch_bounds__(256) void down_small_kernel(MlpArgs a) {
     const bool live = kb < a.KBI;
     const int n0 = nt * kSmallDownCols;
 
-    // g and u of this wave's block (FUSED), then the weight fragments.
-    const int row = lane >> 4, j = lane & 15;  // chunk = (row, 8 columns); rows < M <= 4
-    const bool valid = FUSED && live && row < a.M;
-    float4 g0 = make_float4(0, 0, 0, 0), g1 = g0, u0 = g0, u1 = g0;
-    if (valid) {
-        const int64_t o = (int64_t)row * a.I + kb * 128 + 8 * j;
-        g0 = *reinterpret_cast<const float4*>(a.gbuf + o);
-        g1 = *reinterpret_cast<const float4*>(a.gbuf + o + 4);
-        u0 = *reinterpret_cast<const float4*>(a.ubuf + o);
-        u1 = *reinterpret_cast<const float4*>(a.ubuf + o + 4);
+    // g and u of this wave's block, then the weight fragments.
+    const int row0 = lane >> 4, j = lane & 15;  // chunk = (row row0 + 4 p, 8 columns); rows < M <= 16
+    float4 gv[kSmallPasses][2], uv[kSmallPasses][2];
+#pragma unroll
+    for (int p = 0; p < kSmallPasses; ++p) {
+        const int row = row0 + 4 * p;
+        gv[p][0] = gv[p][1] = uv[p][0] = uv[p][1] = make_float4(0, 0, 0, 0);
+        if (live && row < a.M) {
+            const int64_t o = (int64_t)row * a.I + kb * 128 + 8 * j;
+            gv[p][0] = *reinterpret_cast<const float4*>(a.gbuf + o);
+            gv[p][1] = *reinterpret_cast<const float4*>(a.gbuf + o + 4);
+            uv[p][0] = *reinterpret_cast<const float4*>(a.ubuf + o);
+            uv[p][1] = *reinterpret_cast<const float4*>(a.ubuf + o + 4);
+        }
     }
     v8i b[NB];
     if (live) {
@@ -399,29 +406,42 @@ __global__ __launch_bounds__(256) void down_small_kernel(MlpArgs a) {
     v8i av;
     float4 sh = make_float4(0, 0, 0, 0);
     int eh = 0;
-    if (FUSED) {
-        uint4* za = reinterpret_cast<uint4*>(s_a[FUSED ? wk : 0]);
+    {
+        uint4* za = reinterpret_cast<uint4*>(s_a[wk]);
         for (int i = lane; i < kFrag / 16; i += 64) za[i] = make_uint4(0, 0, 0, 0);
         if (lane < 16) s_sh[wk][lane] = 1.0f;
         s_eh[wk][lane] = 0;
         __syncthreads();
-        const float g[8] = {g0.x, g0.y, g0.z, g0.w, g1.x, g1.y, g1.z, g1.w};
-        const float u[8] = {u0.x, u0.y, u0.z, u0.w, u1.x, u1.y, u1.z, u1.w};
-        float f[8];
 #pragma unroll
-        for (int i = 0; i < 8; ++i) f[i] = g[i] * __builtin_amdgcn_rcpf(1.0f + __expf(-g[i])) * u[i];
-        quant_chunk<MODE>(f, s_a[FUSED ? wk : 0], MODE == FP8S_MLP_BSGEMM ? (void*)s_sh[wk] : (void*)s_eh[wk], row, j,
-                          valid);
+        for (int p = 0; p < kSmallPasses; ++p) {
+            const int row = row0 + 4 * p;
+            const float g[8] = {gv[p][0].x, gv[p][0].y, gv[p][0].z, gv[p][0].w,
+                                gv[p][1].x, gv[p][1].y, gv[p][1].z, gv[p][1].w};
+            const float u[8] = {uv[p][0].x, uv[p][0].y, uv[p][0].z, uv[p][0].w,
+                                uv[p][1].x, uv[p][1].y, uv[p][1].z, uv[p][1].w};
+            float f[8];
+#pragma unroll
+            for (int i = 0; i < 8; ++i) f[i] = g[i] * __builtin_amdgcn_rcpf(1.0f + __expf(-g[i])) * u[i];
+            if (a.htap && live && nt == 0 && row < a.M) {
+                float4* t = reinterpret_cast<float4*>(a.htap + (int64_t)row * a.I + kb * 128 + 8 * j);
+                t[0] = make_float4(f[0], f[1], f[2], f[3]);
+                t[1] = make_float4(f[4], f[5], f[6], f[7]);
+            }
+            quant_chunk<MODE>(f, s_a[wk], MODE == FP8S_MLP_BSGEMM ? (void*)s_sh[wk] : (void*)s_eh[wk], row, j,
+                              live && row < a.M);
+        }
         __syncthreads();
-        av = lds_frag32(s_a[FUSED ? wk : 0], lane);
+        av = lds_frag32(s_a[wk], lane);
         if (MODE == FP8S_MLP_BSGEMM) sh = *reinterpret_cast<const float4*>(&s_sh[wk][4 * (lane >> 4)]);
         else eh = s_eh[wk][lane];
-    } else if (live) {
-        av = load_frag(a.qh + frag_off(0, kb, a.KBI), lane);
-        if (MODE == FP8S_MLP_BSGEMM)
-            sh = *reinterpret_cast<const float4*>(reinterpret_cast<const float*>(a.sh) + (int64_t)kb * 16 + 4 * (lane >> 4));
-        else
-            eh = reinterpret_cast<const uint8_t*>(a.sh)[(int64_t)kb * 64 + lane];
+        if (a.htap && live && nt == 0) {       // debug tap: the operand block this wave built
+            const uint4* src = reinterpret_cast<const uint4*>(s_a[wk]) + 2 * lane;
+            uint4* dst = reinterpret_cast<uint4*>(a.htap_op + frag_off(0, kb, a.KBI)) + 2 * lane;
+            dst[0] = src[0];
+            dst[1] = src[1];
+            const uint8_t* sc = MODE == FP8S_MLP_BSGEMM ? reinterpret_cast<const uint8_t*>(s_sh[wk]) : s_eh[wk];
+            a.htap_op[(int64_t)a.KBI * kFrag + (int64_t)kb * 64 + lane] = sc[lane];
+        }
     }
     v4f acc[NB];
 #pragma unroll
@@ -541,8 +561,10 @@ static MlpPlan plan_mlp(int64_t M, int64_t H, int64_t I, int mode) {
     // gu: two whole-hidden items per CU (256 CUs) in the first round, the
     // rest as K quarters (a multiple of 8 tiles, so no 128-column group of h
     // mixes the two).
+    // (M <= 16: every tile runs over the whole hidden dimension, so that g
+    // and u are complete for the down kernel's SwiGLU prologue.)
     const int tiles = (int)(I / kGuCols);
-    p.GF = tiles <= kGuFullItems ? tiles : kGuFullItems;
+    p.GF = tiles <= kGuFullItems || p.MT == 1 ? tiles : kGuFullItems;
     p.GQ = tiles - p.GF;
     const size_t rows = 16 * (size_t)p.MT;
     const size_t cols = p.MT == 1 ? kSmallDownCols : 16 * kDownNb;
@@ -563,9 +585,9 @@ static MlpPlan plan_mlp(int64_t M, int64_t H, int64_t I, int mode) {
     return p;
 }
 
-// M <= 4  : gu_small (x quantised in-kernel) -> down_small<fused SwiGLU+quant>
+// M <= 4  : gu_small (x quantised in-kernel) -> down_small (SwiGLU + h quantised in-kernel)
 //           (with an RMSNorm in front, the M <= 16 chain instead)
-// M <= 16 : xq -> gu<1> -> hq -> down_small
+// M <= 16 : xq -> gu<1> -> down_small
 // M >  16 : xq -> gu<MT> -> hq -> down<MT>
 // prequant: the quantised x is already in the workspace (no xq launch).
 template <int MODE>
@@ -573,7 +595,7 @@ static void launch_mlp(const MlpPlan& p, hipStream_t st, const MlpArgs& a, bool 
     const dim3 blk(256), g_gu(a.I / kGuCols), g_gul(a.GF + 4 * a.GQ), g_xq(p.MT * p.KBH), g_hq(p.MT * p.KBI), g_dn(p.NT * p.S);
     if (a.M <= kTinyM && !a.norm_w && !prequant) {
         FP8S_LAUNCH("mlp_gu_small", gu_small_kernel<MODE>, g_gu, blk, 0, st, a);
-        FP8S_LAUNCH("mlp_down_small_fused", (down_small_kernel<MODE, true>), g_dn, blk, 0, st, a);
+        FP8S_LAUNCH("mlp_down_small_fused", down_small_kernel<MODE>, g_dn, blk, 0, st, a);
         return;
     }
     if (!prequant) {
@@ -583,8 +605,7 @@ static void launch_mlp(const MlpPlan& p, hipStream_t st, const MlpArgs& a, bool 
     switch (p.MT) {
     case 1:
         FP8S_LAUNCH("mlp_gu", (gu_kernel<1, MODE>), g_gul, blk, kLdsBytes, st, a);
-        FP8S_LAUNCH("mlp_hq", hq_kernel<MODE>, g_hq, blk, 0, st, a);
-        FP8S_LAUNCH("mlp_down_small", (down_small_kernel<MODE, false>), g_dn, blk, 0, st, a);
+        FP8S_LAUNCH("mlp_down_small_fused", down_small_kernel<MODE>, g_dn, blk, 0, st, a);
         break;
 #define FP8S_MT_CASE(N)                                                                \
     case N:                                                                            \
@@ -689,12 +710,13 @@ int swiglu_mlp_fp8_ex(const uint16_t* x, int64_t M, int64_t H, int64_t I, int mo
     const bool in_gu = M <= kTinyM && !norm_w && !prequant;
     // debug tap of h (tests): h in fp32 as hq forms it, then hq's operand of h
     size_t htap_bytes = 0;
-    uint8_t* htap = in_gu ? nullptr : static_cast<uint8_t*>(debug_tap(FP8S_TAP_MLP_H, &htap_bytes));
+    uint8_t* htap = static_cast<uint8_t*>(debug_tap(FP8S_TAP_MLP_H, &htap_bytes));
     const size_t htap_h = (size_t)M * I * 4, htap_frag = (size_t)((M + 15) / 16) * p.KBI * kFrag,
                  htap_sc = (size_t)((M + 15) / 16) * p.KBI * 64;
     FP8S_REQUIRE(!htap || htap_bytes >= htap_h + htap_frag + htap_sc, FP8S_EINVAL,
                  "swiglu_mlp_fp8: debug tap of %zu bytes < %zu", htap_bytes, htap_h + htap_frag + htap_sc);
     a.htap = reinterpret_cast<float*>(htap);
+    a.htap_op = htap ? htap + htap_h : nullptr;
     a.xtap = tap && in_gu ? tap : nullptr;
     a.xtap_s = tap && in_gu ? tap + tap_frag : nullptr;
     if (mode == FP8S_MLP_BSGEMM)
@@ -711,7 +733,7 @@ int swiglu_mlp_fp8_ex(const uint16_t* x, int64_t M, int64_t H, int64_t I, int mo
                          hipMemcpyAsync(tap + tap_frag, a.sx, tap_sc, hipMemcpyDeviceToDevice, st) == hipSuccess,
                      FP8S_EHIP, "swiglu_mlp_fp8: debug tap copy failed");
     }
-    if (htap) {
+    if (htap && p.MT > 1) {                    // hq's operand (down_small writes its own)
         FP8S_REQUIRE(hipMemcpyAsync(htap + htap_h, a.qh, htap_frag, hipMemcpyDeviceToDevice, st) == hipSuccess &&
                          hipMemcpyAsync(htap + htap_h + htap_frag, a.sh, htap_sc, hipMemcpyDeviceToDevice, st) ==
                              hipSuccess,

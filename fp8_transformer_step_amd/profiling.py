@@ -34,8 +34,7 @@ ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 # (ql_act_quant); the profiler cannot tell the two apart.
 KERNELS = [
     (r"gu_small_kernel", "mlp_gu_small"),
-    (r"down_small_kernel<[^>]*true", "mlp_down_small_fused"),
-    (r"down_small_kernel", "mlp_down_small"),
+    (r"down_small_kernel", "mlp_down_small_fused"),
     (r"\bgu_kernel", "mlp_gu"),
     (r"\bdown_kernel", "mlp_down"),
     (r"act_quant_kernel", "act_quant"),

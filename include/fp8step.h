@@ -80,13 +80,12 @@ enum fp8s_device_error {
  *   FP8S_TAP_MLP_X          swiglu_mlp_fp8: the operand of x [M, hidden] the
  *                           gate/up GEMM consumes (quantised inside that
  *                           GEMM for M <= 4, by the x kernel otherwise).
- *   FP8S_TAP_MLP_H          swiglu_mlp_fp8 at M > 4: h = silu(g) u fp32
- *                           [M, inter] row-major as the SwiGLU-quantise
- *                           kernel formed it from the gate/up GEMM's g and
- *                           u, then the down GEMM's operand of h [M, inter]
- *                           as that kernel quantised it.  Not written at
- *                           M <= 4, where the down GEMM forms h in its own
- *                           prologue.
+ *   FP8S_TAP_MLP_H          swiglu_mlp_fp8: h = silu(g) u fp32 [M, inter]
+ *                           row-major as the kernel that quantises it formed
+ *                           it from the gate/up GEMM's g and u (the down
+ *                           GEMM's prologue at M <= 16, the SwiGLU-quantise
+ *                           launch at M > 16), then the down GEMM's operand
+ *                           of h [M, inter] as that kernel quantised it.
  *   FP8S_TAP_STEP_SLOW      dual_ar_decode_step, for each slow layer l in
  *                           turn (n_slow_layers equal parts), back to back:
  *                           the attention output ao bf16 [B, Hq*D]; the
@@ -201,7 +200,10 @@ FP8S_API int fp8s_pack_weight(const uint8_t* q, int64_t ldq, int64_t N, int64_t 
  *            activation quantisation fused into the GEMM launch) and writes
  *            g and u in fp32; the down GEMM forms h and quantises it as its
  *            own operand (the SwiGLU fused into its activation quantisation).
- *   M > 4    four kernels: x quantised once; the gate/up GEMM; h formed and
+ *   M <= 16  three kernels: x quantised once (codes and scales in one
+ *            launch); the gate/up GEMM; the down GEMM, which forms and
+ *            quantises h in its prologue as at M <= 4.
+ *   M > 16   four kernels: x quantised once; the gate/up GEMM; h formed and
  *            quantised once into the down GEMM's e4m3 operand; the down
  *            GEMM.  Fusing either quantisation here would make every GEMM
  *            workgroup re-quantise all M rows of its K range (the down

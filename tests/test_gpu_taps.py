@@ -4,8 +4,9 @@ quantisation of the GPU's own bf16 input of that step, bit for bit.
 
   * swiglu_mlp_fp8's x operand: quantised inside the gate/up GEMM (M <= 4)
     or by the x kernel (M > 4), bsgemm and MXFP8;
-  * swiglu_mlp_fp8's h operand at M > 4: h = silu(g) u and its quantisation,
-    formed in one launch from the gate/up GEMM's g and u;
+  * swiglu_mlp_fp8's h operand: h = silu(g) u and its quantisation, formed
+    from the gate/up GEMM's g and u in the down GEMM's prologue (M <= 16) or
+    in one launch of its own (M > 16);
   * the decode step, every slow layer: the attention kernel's quantised
     output (operand of the output projection) against its bf16 output, and
     the row finisher's quantised MLP input against its RMSNorm rows.  With
@@ -83,14 +84,15 @@ def test_mlp_x_operand_tap(mode, M):
 
 
 @pytest.mark.parametrize("mode", [ops.MLP_BSGEMM, ops.MLP_MXFP8])
-@pytest.mark.parametrize("M", [5, 16, 29, 37, 64, 128])
+@pytest.mark.parametrize("M", [1, 4, 5, 16, 29, 37, 64, 128])
 def test_mlp_h_operand_tap(mode, M):
-    """The SwiGLU-quantise launch: h = silu(g) u as it formed it (against the
-    oracle's h from the same x operand), and the down GEMM's operand of h
-    bit-exact with the oracle's activation quantisation of that h.  M = 5
-    and 16 run the one-tile gate/up GEMM, 29 two tiles, 37 and 64 four, 128
-    eight; the 96 gate/up tiles past the first 512 are split over K and their
-    quarters summed in that launch."""
+    """The kernel that quantises h: h = silu(g) u as it formed it (against
+    the oracle's h from the same x operand), and the down GEMM's operand of h
+    bit-exact with the oracle's activation quantisation of that h.  M <= 16:
+    the down GEMM's own prologue (after the register gate/up kernel at M <= 4,
+    the one-tile LDS kernel at 5 and 16); M > 16: the SwiGLU-quantise launch
+    (29 two tiles, 37 and 64 four, 128 eight), where the 96 gate/up tiles past
+    the first 512 are split over K and their quarters summed."""
     need_gpu()
     H, I = 2560, 9728
     wl = inputs.W_MXFP8 if mode == ops.MLP_MXFP8 else inputs.W_BSGEMM
