@@ -362,6 +362,69 @@ __device__ __forceinline__ void finish_split(const MlpArgs& a, int nt, int s, in
     if (threadIdx.x == 0) store_relaxed_agent(a.cnt + nt, 0);
 }
 
+// The same for down_small's tiles (COLS = 64, M <= 16, so the tile is at most
+// 256 float4 groups): the loads of all S partials are spread over the 256
+// threads, G = 256 / (float4 groups) threads per group taking every G-th
+// split, up to eight float4 loads in flight per thread, so the tail costs one
+// or two memory round trips instead of one per four splits.  Each thread adds
+// its splits in increasing order and the G sums are added in thread order
+// through LDS (`red`, 256 float4): a fixed association, so the result does
+// not depend on which split finished last.  The partials of other
+// workgroups are read after one agent-scope acquire (their stores were
+// device-coherent and complete before their counter bumps).
+template <int COLS>
+__device__ __forceinline__ void finish_split_small(const MlpArgs& a, int nt, int n0, int* s_prev, float4* red) {
+    static_assert(COLS == 64, "sized for 16 rows x 64 columns");
+    if (a.defer) return;                       // the next kernel reduces the partials
+    __builtin_amdgcn_s_waitcnt(0);             // this thread's partial stores are complete
+    __syncthreads();
+    if (threadIdx.x == 0) *s_prev = atomic_add_relaxed(a.cnt + nt, 1);
+    __syncthreads();
+    if (*s_prev != a.S - 1) return;
+    acquire_fence_agent();
+    const int t = threadIdx.x;
+    const int n4 = a.M * COLS / 4;             // float4 groups of the tile, <= 256
+    const int G = 256 / n4;                    // threads per group
+    const int e4 = t % n4, j = t / n4;
+    float4 acc = make_float4(0, 0, 0, 0);
+    if (j < G) {
+        const int64_t per = (int64_t)a.M * COLS / 4;   // float4s per split
+        const float4* base = reinterpret_cast<const float4*>(a.ypart + (int64_t)nt * a.S * a.M * COLS) + e4;
+        for (int s0 = j; s0 < a.S; s0 += 8 * G) {
+            float4 v[8];
+#pragma unroll
+            for (int u = 0; u < 8; ++u) {
+                const int sp = s0 + u * G;
+                v[u] = sp < a.S ? base[sp * per] : make_float4(0, 0, 0, 0);
+            }
+            __builtin_amdgcn_sched_barrier(0); // the eight loads issued before any is added
+#pragma unroll
+            for (int u = 0; u < 8; ++u) {
+                acc.x += v[u].x; acc.y += v[u].y; acc.z += v[u].z; acc.w += v[u].w;
+            }
+        }
+    }
+    red[t] = acc;
+    __syncthreads();
+    if (t < n4) {
+        float4 sum = red[t];
+        for (int jj = 1; jj < G; ++jj) {
+            const float4 r = red[jj * n4 + t];
+            sum.x += r.x; sum.y += r.y; sum.z += r.z; sum.w += r.w;
+        }
+        const int e = 4 * t, m = e / COLS, col = n0 + e % COLS;
+        float v[4] = {sum.x, sum.y, sum.z, sum.w};
+        if (a.res) {
+            const uint2 rr = *reinterpret_cast<const uint2*>(a.res + (int64_t)m * a.H + col);
+            v[0] += bf16_to_f32(rr.x & 0xFFFFu); v[1] += bf16_to_f32(rr.x >> 16);
+            v[2] += bf16_to_f32(rr.y & 0xFFFFu); v[3] += bf16_to_f32(rr.y >> 16);
+        }
+        *reinterpret_cast<uint2*>(a.y + (int64_t)m * a.H + col) =
+            make_uint2(f32_to_bf16(v[0]) | (f32_to_bf16(v[1]) << 16), f32_to_bf16(v[2]) | (f32_to_bf16(v[3]) << 16));
+    }
+    if (threadIdx.x == 0) store_relaxed_agent(a.cnt + nt, 0);
+}
+
 // ---- down_small (M <= 16): 64 columns x 4 K blocks, one K block per wave -------
 // The wave builds its operand from g and u itself: h = silu(g) * u over the
 // whole 128-column block, the block's 1x128 / 1x32 group amax, e4m3
@@ -372,7 +435,7 @@ constexpr int kSmallPasses = 4;
 template <int MODE>
 __global__ __launch_bounds__(256) void down_small_kernel(MlpArgs a) {
     constexpr int NB = kSmallDownCols / 16;
-    __shared__ float red[3][NB][4][64];
+    __shared__ __attribute__((aligned(16))) float red[3][NB][4][64];
     __shared__ __attribute__((aligned(16))) uint8_t s_a[4][kFrag];
     __shared__ float s_sh[4][16];
     __shared__ uint8_t s_eh[4][64];
@@ -481,7 +544,7 @@ __global__ __launch_bounds__(256) void down_small_kernel(MlpArgs a) {
                                   acc[t][r] + red[0][t][r][lane] + red[1][t][r][lane] + red[2][t][r][lane]);
             }
     }
-    finish_split<kSmallDownCols, 16>(a, nt, s, n0, &s_prev);
+    finish_split_small<kSmallDownCols>(a, nt, n0, &s_prev, reinterpret_cast<float4*>(&red[0][0][0][0]));
 }
 
 // ---- down (M > 16): 32 columns x one K split staged in LDS ---------------------
