@@ -576,7 +576,8 @@ def mlp_sweep(torch, ops, inputs, n_sets):
     for mode, key, packed in ((ops.MLP_BSGEMM, "mlp_bsgemm", False), (ops.MLP_MXFP8, "mlp_mxfp8", False),
                               (ops.MLP_BSGEMM, "mlp_bsgemm_packed", True), (ops.MLP_MXFP8, "mlp_mxfp8_packed", True)):
         sweep[key] = {}
-        for M in (1, 8, 32, 64, 128):
+        # the bsgemm workload's M list, and the MXFP8 workload's "1..128"
+        for M in ((1, 8, 32, 64, 128) if mode == ops.MLP_BSGEMM else (1, 2, 4, 8, 16, 32, 64, 96, 128)):
             w = Workload(torch, ops, 1, M, mode, n_sets, kv_len, with_attn=False, packed=packed)
             te, _, per, t = time_parts(torch, ops, w, [w.mlp], 20, 5, graph=True)
             gb = mlp_bytes(M, mode) / (t * 1e-3) / 1e9
@@ -934,6 +935,8 @@ def main():
         sweep = mlp_sweep(torch, ops, inputs, args.sets) | {"attn": {}, "attn_mxkv": {}, "attn_paged": {}}
         for Bs, lo, hi, mx, page in ((1, 234, 400, False, 0), (16, 234, 400, False, 0), (64, 234, 400, False, 0),
                                      (64, 234, 4096, False, 0), (64, 234, 8192, False, 0),
+                                     (64, 1024, 1024, False, 0), (64, 2048, 2048, False, 0),
+                                     (64, 4096, 4096, False, 0), (64, 8192, 8192, False, 0),
                                      (64, 234, 4096, True, 0), (64, 234, 8192, True, 0),
                                      (64, 234, 4096, False, 16), (64, 234, 4096, True, 16)):
             kv = inputs.kv_lengths(inputs.W_ATTN, Bs, lo, hi, extra=Bs + hi)
@@ -945,7 +948,8 @@ def main():
                          cap=CAP if hi > 400 else 512)
             te, _, per, t = time_parts(torch, ops, w, [w.attn], 20, 5, graph=True)
             gb = attn_bytes(kv, Bs, mx) / (t * 1e-3) / 1e9
-            key = f"B={Bs},kv=U[{lo},{hi}]" + (f",page={page},{'mxfp8' if mx else 'bf16'}" if page else "")
+            key = f"B={Bs},kv=" + (f"{lo}" if lo == hi else f"U[{lo},{hi}]") + (
+                f",page={page},{'mxfp8' if mx else 'bf16'}" if page else "")
             sweep["attn_paged" if page else "attn_mxkv" if mx else "attn"][key] = {
                 "us": t * 1e3, "us_eager": te * 1e3, "tokens/s": Bs / (t * 1e-3), "GB/s": gb,
                 "frac": gb / PEAK_HBM_GBS, "rotated_bytes": n_sets * attn_bytes(kv, Bs, mx),
