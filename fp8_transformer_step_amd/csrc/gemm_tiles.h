@@ -62,15 +62,17 @@ __device__ __forceinline__ v8i lds_frag(const uint8_t* lds, int off, int lane) {
     return r;
 }
 
-// An operand fragment stored lane-contiguous (64 lanes x 32 bytes) in LDS.
-__device__ __forceinline__ v8i lds_frag32(const uint8_t* frag, int lane) {
-    const uint4 lo = *reinterpret_cast<const uint4*>(frag + lane * 32);
-    const uint4 hi = *reinterpret_cast<const uint4*>(frag + lane * 32 + 16);
-    v8i r;
-    r[0] = lo.x; r[1] = lo.y; r[2] = lo.z; r[3] = lo.w;
-    r[4] = hi.x; r[5] = hi.y; r[6] = hi.z; r[7] = hi.w;
-    return r;
-}
+// An operand fragment that quant_chunk<.., true> builds in LDS has the layout
+// of the staged weight fragments (read with lds_frag): the first KiB holds
+// every lane's bytes 0..15, the second its bytes 16..31, so each read is 16
+// consecutive bytes per lane.  Lane l's bytes sit at slot lds_lane(l, rot) =
+// l ^ ((l / 16 + rot) % 4): the 16 lanes of one quantisation row write to
+// operand lanes row + 16 g (g = 0..3), whose slots would otherwise repeat
+// the same banks (the bank pattern repeats every 128 bytes); XOR-ing g into
+// the low bits of the row spreads them, and `rot` (the fragment's index when
+// one store covers several fragments) turns the pattern per fragment.
+__device__ __forceinline__ int lds_lane(int l, int rot = 0) { return l ^ (((l >> 4) + rot) & 3); }
+
 
 // bsgemm weight scale of the 128x128 block holding (row n0, K block kb).  The
 // per-block step kb * sc stays 32-bit: a scale matrix never nears 2^31 entries.
@@ -300,9 +302,10 @@ __device__ __forceinline__ v8i load_w(const uint8_t* w, int64_t ld, int KB, int 
 // e4m3(v / s).  MX: 1x32 groups (4 lanes), E = floor(log2 amax) - 8 + 127,
 // q = e4m3(v * 2^(127 - E)).  frag: the (mt, kb) fragment; sc: its 16 fp32
 // scales (bsgemm) or 64 exponent bytes (MX, scale lane order).
-template <int MODE>
+// SWZ: frag is an LDS fragment in the rotated lane order of lds_lane.
+template <int MODE, bool SWZ = false>
 __device__ __forceinline__ void quant_chunk(const float (&f)[8], uint8_t* frag, void* sc, int row, int j,
-                                            bool valid = true) {
+                                            bool valid = true, int rot = 0) {
     float am = 0.0f;
 #pragma unroll
     for (int i = 0; i < 8; ++i) am = fmaxf(am, fabsf(f[i]));
@@ -322,7 +325,12 @@ __device__ __forceinline__ void quant_chunk(const float (&f)[8], uint8_t* frag, 
         if (valid && (j & 3) == 0) reinterpret_cast<uint8_t*>(sc)[row + 16 * (j >> 2)] = (uint8_t)E;
     }
     const int lane = row + 16 * frag_lane_group(8 * j);
-    if (valid) *reinterpret_cast<uint2*>(frag + lane * 32 + frag_byte(8 * j)) = make_uint2(q0, q1);
+    if (SWZ) {
+        if (valid)
+            *reinterpret_cast<uint2*>(frag + (j >> 3) * 1024 + lds_lane(lane, rot) * 16 + (j & 1) * 8) = make_uint2(q0, q1);
+    } else if (valid) {
+        *reinterpret_cast<uint2*>(frag + lane * 32 + frag_byte(8 * j)) = make_uint2(q0, q1);
+    }
 }
 
 template <int MODE>

@@ -171,7 +171,7 @@ __global__ __launch_bounds__(256) void gu_small_kernel(MlpArgs a) {
         const int c = lane + 64 * t;
         xv[t] = make_uint4(0, 0, 0, 0);
         if (c < nch) {
-            const int row = c / (nkb * 16), kl = (c >> 4) % nkb, j = c & 15;
+            const int row = (c >> 4) % a.M, kl = (c >> 4) / a.M, j = c & 15;
             xv[t] = *reinterpret_cast<const uint4*>(a.x + (int64_t)row * a.H + (lo + kl) * 128 + 8 * j);
         }
     }
@@ -201,21 +201,23 @@ __global__ __launch_bounds__(256) void gu_small_kernel(MlpArgs a) {
     for (int t = 0; t < kTinyChunks; ++t) {
         const int c = lane + 64 * t;
         const bool valid = c < nch;             // a group of 16 chunks is all valid or all not
-        const int row = valid ? c / (nkb * 16) : 0, kl = valid ? (c >> 4) % nkb : 0, j = c & 15;
+        // chunk c: 8 columns j of row (c / 16) % M in block (c / 16) / M, so that
+        // the four 16-lane groups of a store take different rows
+        const int row = valid ? (c >> 4) % a.M : 0, kl = valid ? (c >> 4) / a.M : 0, j = c & 15;
         float f[8];
         const uint32_t w4[4] = {xv[t].x, xv[t].y, xv[t].z, xv[t].w};
 #pragma unroll
         for (int k = 0; k < 4; ++k) { f[2 * k] = bf16_to_f32(w4[k] & 0xFFFFu); f[2 * k + 1] = bf16_to_f32(w4[k] >> 16); }
-        quant_chunk<MODE>(f, s_a[wk] + kl * kFrag, MODE == FP8S_MLP_BSGEMM ? (void*)s_sx[wk][kl] : (void*)s_ex[wk][kl],
-                          row, j, valid);
+        quant_chunk<MODE, true>(f, s_a[wk] + kl * kFrag, MODE == FP8S_MLP_BSGEMM ? (void*)s_sx[wk][kl] : (void*)s_ex[wk][kl],
+                          row, j, valid, kl);
     }
     __syncthreads();
     if (a.xtap && blockIdx.x == 0) {           // debug tap: this wave's operand blocks as the MFMAs read them
         for (int kl = 0; kl < nkb; ++kl) {
-            const uint4* src = reinterpret_cast<const uint4*>(s_a[wk] + kl * kFrag) + 2 * lane;
+            const uint4* src = reinterpret_cast<const uint4*>(s_a[wk] + kl * kFrag) + lds_lane(lane, kl);
             uint4* dst = reinterpret_cast<uint4*>(a.xtap + frag_off(0, lo + kl, a.KBH)) + 2 * lane;
             dst[0] = src[0];
-            dst[1] = src[1];
+            dst[1] = src[64];
             const uint8_t* s = MODE == FP8S_MLP_BSGEMM ? reinterpret_cast<const uint8_t*>(s_sx[wk][kl]) : s_ex[wk][kl];
             a.xtap_s[(int64_t)(lo + kl) * 64 + lane] = s[lane];
         }
@@ -226,7 +228,7 @@ __global__ __launch_bounds__(256) void gu_small_kernel(MlpArgs a) {
     for (int i = 0; i < kWaveKb; ++i) {
         const int kb = lo + i;
         if (kb < hi) {
-            const v8i av = lds_frag32(s_a[wk] + i * kFrag, lane);
+            const v8i av = lds_frag(s_a[wk] + i * kFrag, 0, lds_lane(lane, i));
             if (MODE == FP8S_MLP_BSGEMM) {
                 const float4 sx = *reinterpret_cast<const float4*>(&s_sx[wk][i][4 * (lane >> 4)]);
                 const float swg = wscale_bs(a.sg, a.sg_r, a.sg_c, n0, kb);
@@ -490,18 +492,18 @@ __global__ __launch_bounds__(256) void down_small_kernel(MlpArgs a) {
                 t[0] = make_float4(f[0], f[1], f[2], f[3]);
                 t[1] = make_float4(f[4], f[5], f[6], f[7]);
             }
-            quant_chunk<MODE>(f, s_a[wk], MODE == FP8S_MLP_BSGEMM ? (void*)s_sh[wk] : (void*)s_eh[wk], row, j,
+            quant_chunk<MODE, true>(f, s_a[wk], MODE == FP8S_MLP_BSGEMM ? (void*)s_sh[wk] : (void*)s_eh[wk], row, j,
                               live && row < a.M);
         }
         __syncthreads();
-        av = lds_frag32(s_a[wk], lane);
+        av = lds_frag(s_a[wk], 0, lds_lane(lane));
         if (MODE == FP8S_MLP_BSGEMM) sh = *reinterpret_cast<const float4*>(&s_sh[wk][4 * (lane >> 4)]);
         else eh = s_eh[wk][lane];
         if (a.htap && live && nt == 0) {       // debug tap: the operand block this wave built
-            const uint4* src = reinterpret_cast<const uint4*>(s_a[wk]) + 2 * lane;
+            const uint4* src = reinterpret_cast<const uint4*>(s_a[wk]) + lds_lane(lane);
             uint4* dst = reinterpret_cast<uint4*>(a.htap_op + frag_off(0, kb, a.KBI)) + 2 * lane;
             dst[0] = src[0];
-            dst[1] = src[1];
+            dst[1] = src[64];
             const uint8_t* sc = MODE == FP8S_MLP_BSGEMM ? reinterpret_cast<const uint8_t*>(s_sh[wk]) : s_eh[wk];
             a.htap_op[(int64_t)a.KBI * kFrag + (int64_t)kb * 64 + lane] = sc[lane];
         }
